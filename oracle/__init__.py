@@ -1,0 +1,241 @@
+"""CPU oracle for the MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+ctypes wrapper around ``moe_oracle.cpp`` (plain C++17, fp64, per-expert masked
+loop). Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the GPU library never calls it and it
+never calls the GPU library.
+
+Inputs come from the ``gen`` package (host numpy buffers); no input and no
+expected value here is ever produced by the GPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC = os.path.join(_HERE, "moe_oracle.cpp")
+
+
+class OrcShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("gating", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("capacity", ctypes.c_int64), ("aux_alpha", ctypes.c_double)]
+
+
+class OrcWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2",
+                 "sw_scale")]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile liboracle.so with g++ (OpenMP). sanitize=True adds ASan/UBSan."""
+    cmd = ["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", LIB_PATH, SRC]
+    if sanitize:
+        cmd[3:3] = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        sp, wp = ctypes.POINTER(OrcShape), ctypes.POINTER(OrcWeights)
+        L.orc_router_logits.argtypes = [sp, vp, wp, vp, vp]
+        L.orc_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_dispatch.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.orc_expert_rows.argtypes = [sp, wp, i32, i32, vp, i64, vp]
+        L.orc_moe_output.argtypes = [sp, vp, wp, vp, vp, vp, vp, i64, vp]
+        L.orc_combine.argtypes = [sp, vp, vp, vp, vp, vp]
+        for name in ("orc_router_logits", "orc_route", "orc_dispatch", "orc_expert_rows",
+                     "orc_moe_output", "orc_combine", "orc_abi_version"):
+            getattr(L, name).restype = ctypes.c_int
+        for name in ("orc_bf16_value", "orc_gelu", "orc_silu"):
+            getattr(L, name).restype = ctypes.c_double
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_gelu.argtypes = [ctypes.c_double]
+        L.orc_silu.argtypes = [ctypes.c_double]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def shape_of(wl, T: int | None = None, capacity: int | None = None) -> OrcShape:
+    """OrcShape for a gen.Workload (T and capacity may be overridden)."""
+    return OrcShape(T=wl.T if T is None else T, d=wl.d, d_ff=wl.d_ff, n_experts=wl.n_experts,
+                    top_k=wl.top_k, n_shared=wl.n_shared, act=wl.act, gating=wl.gating,
+                    act_dtype=wl.act_dtype, w_dtype=wl.w_dtype,
+                    capacity=wl.capacity() if capacity is None else capacity, aux_alpha=wl.aux_alpha)
+
+
+def weights_of(inp) -> tuple[OrcWeights, list]:
+    keep = [inp.w_router, inp.b_router, inp.w1, inp.w3, inp.w2, inp.b1, inp.b2, inp.w_scale,
+            inp.sw1, inp.sw3, inp.sw2, inp.sw_scale]
+    w = OrcWeights(*[_p(a) for a in keep])
+    return w, keep
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: arguments outside the contract")
+
+
+def router_logits(shape: OrcShape, x, inp):
+    w, _keep = weights_of(inp)
+    l64 = np.empty((shape.T, shape.n_experts), np.float64)
+    l32 = np.empty((shape.T, shape.n_experts), np.float32)
+    _check(lib().orc_router_logits(ctypes.byref(shape), _p(x), ctypes.byref(w), _p(l64), _p(l32)),
+           "router_logits")
+    return l64, l32
+
+
+@dataclass
+class Routing:
+    topk_idx: np.ndarray   # [T,k] int32
+    topk_w: np.ndarray     # [T,k] fp64
+    probs: np.ndarray      # [T,N] fp64
+    lse: np.ndarray        # [T]
+    margin_set: np.ndarray
+    margin_order: np.ndarray
+    counts: np.ndarray     # [N] int64, before drops
+    f: np.ndarray
+    P: np.ndarray
+    l_aux: float
+    z: float
+    lse_sq_mean: float
+
+
+def route(shape: OrcShape, logits32: np.ndarray) -> Routing:
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    logits32 = np.ascontiguousarray(logits32, np.float32)
+    assert logits32.shape == (T, N)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    probs = np.empty((T, N), np.float64)
+    lse = np.empty(T, np.float64)
+    ms, mo = np.empty(T, np.float64), np.empty(T, np.float64)
+    counts = np.empty(N, np.int64)
+    f, P = np.empty(N, np.float64), np.empty(N, np.float64)
+    la, z, lsq = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().orc_route(ctypes.byref(shape), _p(logits32), _p(idx), _p(w), _p(probs), _p(lse), _p(ms),
+                           _p(mo), _p(counts), _p(f), _p(P), ctypes.addressof(la), ctypes.addressof(z),
+                           ctypes.addressof(lsq)), "route")
+    return Routing(idx, w, probs, lse, ms, mo, counts, f, P, la.value, z.value, lsq.value)
+
+
+@dataclass
+class Dispatch:
+    kept: np.ndarray        # [N] int32
+    offsets: np.ndarray     # [N+1] int32
+    perm_token: np.ndarray  # [T*k] int32 (rows >= M are -1)
+    inv_map: np.ndarray     # [T,k] int32 (-1 = dropped)
+    n_dropped: int
+
+
+def dispatch(shape: OrcShape, topk_idx: np.ndarray) -> Dispatch:
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    topk_idx = np.ascontiguousarray(topk_idx, np.int32)
+    kept = np.empty(N, np.int32)
+    off = np.empty(N + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    inv = np.empty((T, k), np.int32)
+    nd = ctypes.c_int64()
+    _check(lib().orc_dispatch(ctypes.byref(shape), _p(topk_idx), _p(kept), _p(off), _p(perm), _p(inv),
+                              ctypes.addressof(nd)), "dispatch")
+    return Dispatch(kept, off, perm, inv, nd.value)
+
+
+def expert_rows(shape: OrcShape, inp, e: int, X: np.ndarray, shared: bool = False) -> np.ndarray:
+    w, _keep = weights_of(inp)
+    X = np.ascontiguousarray(X)
+    n = X.shape[0]
+    Y = np.empty((n, shape.d), np.float64)
+    _check(lib().orc_expert_rows(ctypes.byref(shape), ctypes.byref(w), int(shared), e, _p(X), n, _p(Y)),
+           "expert_rows")
+    return Y
+
+
+def moe_output(shape: OrcShape, x, inp, routing: Routing, disp: Dispatch | None,
+               tokens: np.ndarray) -> np.ndarray:
+    w, _keep = weights_of(inp)
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    y = np.empty((len(tokens), shape.d), np.float64)
+    inv = None if disp is None else disp.inv_map
+    _check(lib().orc_moe_output(ctypes.byref(shape), _p(x), ctypes.byref(w), _p(routing.topk_idx),
+                                _p(np.ascontiguousarray(routing.topk_w)), _p(inv), _p(tokens), len(tokens),
+                                _p(y)), "moe_output")
+    return y
+
+
+def combine(shape: OrcShape, y_perm, inv_map, topk_w32, y_shared=None) -> np.ndarray:
+    y = np.empty((shape.T, shape.d), np.float64)
+    _check(lib().orc_combine(ctypes.byref(shape), _p(y_perm), _p(np.ascontiguousarray(inv_map, np.int32)),
+                             _p(np.ascontiguousarray(topk_w32, np.float32)), _p(y_shared), _p(y)), "combine")
+    return y
+
+
+@dataclass
+class Forward:
+    logits64: np.ndarray
+    logits32: np.ndarray
+    routing: Routing
+    disp: Dispatch
+    tokens: np.ndarray
+    y: np.ndarray            # [len(tokens), d] fp64
+
+
+def forward(inp, tokens: np.ndarray | None = None, logits32: np.ndarray | None = None) -> Forward:
+    """Whole layer: logits -> routing/stats -> dispatch -> outputs of `tokens`
+    (all tokens when None). `logits32` replaces the router GEMM when given."""
+    wl = inp.wl
+    shape = shape_of(wl)
+    if logits32 is None:
+        l64, l32 = router_logits(shape, inp.x, inp)
+    else:
+        l64, l32 = logits32.astype(np.float64), np.ascontiguousarray(logits32, np.float32)
+    r = route(shape, l32)
+    dsp = dispatch(shape, r.topk_idx)
+    if tokens is None:
+        tokens = np.arange(wl.T, dtype=np.int64)
+    y = moe_output(shape, inp.x, inp, r, dsp, tokens)
+    return Forward(l64, l32, r, dsp, np.asarray(tokens, np.int64), y)
+
+
+def bf16_value(b: int) -> float:
+    return lib().orc_bf16_value(b)
+
+
+def e4m3_value(q: int) -> float:
+    return lib().orc_e4m3_value(q)
+
+
+def gelu(u: float) -> float:
+    return lib().orc_gelu(u)
+
+
+def silu(u: float) -> float:
+    return lib().orc_silu(u)

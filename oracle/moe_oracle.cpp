@@ -1,0 +1,445 @@
+// MoE layer forward -- CPU ORACLE. TEST INFRASTRUCTURE ONLY.
+//
+// Plain, slow, fp64 reference of what the GPU library computes. Only the test
+// suite, the smoke check and the benchmark's CPU-baseline leg may load it. It
+// shares no code, header or table with the GPU library (it has its own copies
+// of the argument structs below and decodes bf16 / e4m3 itself).
+//
+// Sources (the pages this follows, cited by title and section):
+//  [AIG]  aigrafen.se, "Mixture of Experts": the y = sum g_i E_i(x) and
+//         g = softmax(W_r x) equation, the L_aux = alpha*N*sum f_i P_i equation,
+//         the capacity equation C = tokens/N * cf, and the `MoE` module (router
+//         softmax -> top-k -> renormalise, capacity int(cf*T*k/N), the
+//         per-expert loop with `nonzero` order and truncation to C, f and P).
+//  [MOEA] vanos001 placement notes, "MoE Architecture": section "Expert Network
+//         Design" (SwiGLUExpert w2(silu(w1 x) * w3 x); StandardExpert
+//         Linear-GELU-Linear), "Router Design / Token-Choice Router" (top-k on
+//         logits, then softmax over the k), "Capacity and Token Dropping".
+//  [SPX]  learn.starphix.com, "Mixture of Experts (MoE)": sections "Key
+//         Equations", "Top-k Gating", "Load Balancing (Critical)"
+//         (load_balancing_loss, z_loss), "Shared + Specialized".
+//  [WIKI] wiki.ai-engineering.at, "Mixture of Experts (MoE)": the router /
+//         softmax / top-k / weighted-combination figure and the `MoELayer`
+//         snippet (top-k of the gate scores, softmax over the k).
+//
+// Readings where the pages are silent or disagree (all listed in the design
+// notes of the repository):
+//  - Router output is an fp32 tensor (the pages' modules run in PyTorch's
+//    default float32). Logits are accumulated in fp64 and rounded once to fp32;
+//    selection and everything after it use those fp32 values widened exactly.
+//  - Top-k order: descending logit, exact ties go to the lower expert index.
+//    Selection on logits equals selection on softmax probabilities because
+//    softmax is strictly increasing.
+//  - f_e = counts_e / (T*k) counted before drops; P_e = mean over tokens of the
+//    full softmax; alpha multiplies the loss; z = (mean_t logsumexp_t)^2.
+//  - Capacity: pairs of expert e in ascending token order, the first C kept;
+//    a dropped pair adds 0 to the layer output (the residual is outside).
+//  - GELU is the exact erf form; SiLU(u) = u / (1 + e^-u).
+//  - e4m3 weights: W = s * q, q an OCP e4m3fn code, one fp32 scale per
+//    (expert, matrix).
+//
+// Every function returns 0 on success and -1 when the arguments fall outside
+// the contract (k > N, N < 1, ...). Parallelism (OpenMP) only splits
+// independent rows; every sum is accumulated sequentially in fp64.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+extern "C" {
+
+struct OrcShape {
+  int64_t T, d, d_ff;
+  int32_t n_experts, top_k, n_shared;
+  int32_t act;        // 0 GELU expert (Linear+bias, GELU, Linear+bias), 1 SwiGLU
+  int32_t gating;     // 0 softmax->top-k, 1 softmax->top-k->renormalise, 2 top-k->softmax
+  int32_t act_dtype;  // 0 fp32, 1 bf16 (x, router weight, layer output)
+  int32_t w_dtype;    // 0 fp32, 1 bf16, 2 e4m3fn + per-(expert, matrix) fp32 scale
+  int64_t capacity;   // < 0: no capacity limit
+  double aux_alpha;
+};
+
+struct OrcWeights {
+  const void* w_router;        // [N][d], act dtype
+  const float* b_router;       // [N] or null
+  const void* w1;              // [N][d_ff][d]
+  const void* w3;              // [N][d_ff][d] (SwiGLU) or null
+  const void* w2;              // [N][d][d_ff]
+  const float* b1;             // [N][d_ff] or null (GELU only)
+  const float* b2;             // [N][d] or null (GELU only)
+  const float* w_scale;        // [N][3] scales of (W1, W3, W2) for e4m3
+  const void* sw1;             // shared experts [S][d_ff][d]
+  const void* sw3;             // [S][d_ff][d]
+  const void* sw2;             // [S][d][d_ff]
+  const float* sw_scale;       // [S][3]
+};
+
+}  // extern "C"
+
+namespace {
+
+double bf16_value(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return static_cast<double>(f);
+}
+
+// OCP e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+// is subnormal (m * 2^-9); no infinities; S.1111.111 is NaN (never produced).
+double e4m3_value(uint8_t q) {
+  const int e = (q >> 3) & 15, m = q & 7;
+  double v = (e == 0) ? std::ldexp(static_cast<double>(m), -9)
+                      : std::ldexp(1.0 + m / 8.0, e - 7);
+  return (q & 0x80) ? -v : v;
+}
+
+// Element i of a tensor stored in `dtype`, times `scale` (e4m3 only).
+double elem(const void* p, int dtype, int64_t i, double scale) {
+  switch (dtype) {
+    case 0: return static_cast<double>(static_cast<const float*>(p)[i]);
+    case 1: return bf16_value(static_cast<const uint16_t*>(p)[i]);
+    default: return scale * e4m3_value(static_cast<const uint8_t*>(p)[i]);
+  }
+}
+
+bool shape_ok(const OrcShape* s) {
+  return s && s->T >= 0 && s->d > 0 && s->d_ff > 0 && s->n_experts >= 1 && s->top_k >= 1 &&
+         s->top_k <= s->n_experts && s->n_shared >= 0 && (s->act == 0 || s->act == 1) &&
+         s->gating >= 0 && s->gating <= 2 && (s->act_dtype == 0 || s->act_dtype == 1) &&
+         s->w_dtype >= 0 && s->w_dtype <= 2;
+}
+
+double gelu(double u) { return 0.5 * u * (1.0 + std::erf(u / std::sqrt(2.0))); }
+double silu(double u) { return u / (1.0 + std::exp(-u)); }
+
+// One expert applied to n rows X [n][d] -> Y [n][d] (fp64).
+// GELU expert [AIG `MoE` module; MOEA "Expert Network Design", StandardExpert]:
+//   y = W2 gelu(W1 x + b1) + b2.
+// SwiGLU expert [MOEA "Expert Network Design", SwiGLUExpert]:
+//   y = W2 (silu(W1 x) * (W3 x)).
+void expert_rows(const OrcShape* s, const OrcWeights* w, bool shared, int e, const double* X,
+                 int64_t n, double* Y) {
+  const int64_t d = s->d, f = s->d_ff;
+  const void* W1 = shared ? w->sw1 : w->w1;
+  const void* W3 = shared ? w->sw3 : w->w3;
+  const void* W2 = shared ? w->sw2 : w->w2;
+  const float* sc = shared ? w->sw_scale : w->w_scale;
+  const float* b1 = shared ? nullptr : w->b1;
+  const float* b2 = shared ? nullptr : w->b2;
+  const double s1 = (s->w_dtype == 2) ? sc[3 * e + 0] : 1.0;
+  const double s3 = (s->w_dtype == 2) ? sc[3 * e + 1] : 1.0;
+  const double s2 = (s->w_dtype == 2) ? sc[3 * e + 2] : 1.0;
+  const int64_t base1 = static_cast<int64_t>(e) * f * d;  // expert e in [N][d_ff][d]
+  const int64_t base2 = static_cast<int64_t>(e) * d * f;  // expert e in [N][d][d_ff]
+  std::vector<double> H(static_cast<size_t>(n * f));
+
+#pragma omp parallel
+  {
+    std::vector<double> a(d), g(d);
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < f; ++i) {
+      for (int64_t j = 0; j < d; ++j) a[j] = elem(W1, s->w_dtype, base1 + i * d + j, s1);
+      if (s->act == 1)
+        for (int64_t j = 0; j < d; ++j) g[j] = elem(W3, s->w_dtype, base1 + i * d + j, s3);
+      for (int64_t r = 0; r < n; ++r) {
+        const double* x = X + r * d;
+        double u = 0.0;
+        for (int64_t j = 0; j < d; ++j) u += a[j] * x[j];
+        if (s->act == 0) {
+          if (b1) u += static_cast<double>(b1[static_cast<int64_t>(e) * f + i]);
+          H[r * f + i] = gelu(u);
+        } else {
+          double v = 0.0;
+          for (int64_t j = 0; j < d; ++j) v += g[j] * x[j];
+          H[r * f + i] = silu(u) * v;
+        }
+      }
+    }
+  }
+
+#pragma omp parallel
+  {
+    std::vector<double> a(f);
+#pragma omp for schedule(static)
+    for (int64_t o = 0; o < d; ++o) {
+      for (int64_t i = 0; i < f; ++i) a[i] = elem(W2, s->w_dtype, base2 + o * f + i, s2);
+      for (int64_t r = 0; r < n; ++r) {
+        const double* h = H.data() + r * f;
+        double u = 0.0;
+        for (int64_t i = 0; i < f; ++i) u += a[i] * h[i];
+        if (s->act == 0 && b2) u += static_cast<double>(b2[static_cast<int64_t>(e) * d + o]);
+        Y[r * d + o] = u;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int orc_abi_version(void) { return 1; }
+
+// Router logits [AIG, g = softmax(W_r x); SPX "Key Equations", router_logits =
+// x W_router^T; WIKI `MoELayer`/`CapacityMoE` use a biased gate]:
+//   l[t][e] = sum_i x[t][i] * W_r[e][i] (+ b_r[e]), accumulated in fp64.
+// Outputs the fp64 value and the fp32 router output (one rounding).
+int orc_router_logits(const OrcShape* s, const void* x, const OrcWeights* w, double* logits64,
+                      float* logits32) {
+  if (!shape_ok(s) || !x || !w || !w->w_router) return -1;
+  const int64_t T = s->T, d = s->d, N = s->n_experts;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < N; ++e) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < d; ++i)
+        acc += elem(x, s->act_dtype, t * d + i, 1.0) * elem(w->w_router, s->act_dtype, e * d + i, 1.0);
+      if (w->b_router) acc += static_cast<double>(w->b_router[e]);
+      if (logits64) logits64[t * N + e] = acc;
+      if (logits32) logits32[t * N + e] = static_cast<float>(acc);
+    }
+  }
+  return 0;
+}
+
+// Routing and statistics from fp32 router outputs `logits` [T][N].
+//  softmax  p[t][e] = exp(l - m) / sum exp(l - m), m = max_e l;  lse = m + ln sum exp(l - m)
+//  select   S_t = the k largest logits, descending, ties -> lower expert index
+//  gates    mode 0 [AIG equation; WIKI figure]: g_j = p[t][S_j]
+//           mode 1 [AIG `MoE` module]:          g_j = p[t][S_j] / sum_j' p[t][S_j']
+//           mode 2 [MOEA Token-Choice Router; SPX "Top-k Gating"; WIKI `MoELayer`]:
+//                                               g = softmax over l[t][S_t]
+//  stats    [AIG L_aux equation and `MoE` module; SPX "Load Balancing"]:
+//           counts_e = #{t : e in S_t} (before any capacity drop)
+//           f_e = counts_e / (T k),  P_e = (1/T) sum_t p[t][e]
+//           L_aux = alpha * N * sum_e f_e P_e
+//           z = ((1/T) sum_t lse_t)^2  [SPX z_loss];  lse_sq_mean = (1/T) sum_t lse_t^2
+//  margins  margin_set[t]   = l_(k) - l_(k+1) of the sorted logits (+inf when k = N)
+//           margin_order[t] = min_j l_(j) - l_(j+1), j < k (+inf when k = 1)
+// Any output pointer except topk_idx may be null.
+int orc_route(const OrcShape* s, const float* logits, int32_t* topk_idx, double* topk_w,
+              double* probs, double* lse_out, double* margin_set, double* margin_order,
+              int64_t* counts, double* f, double* P, double* l_aux, double* z,
+              double* lse_sq_mean) {
+  if (!shape_ok(s) || !logits || !topk_idx) return -1;
+  const int64_t T = s->T, N = s->n_experts, k = s->top_k;
+  std::vector<double> p_all(static_cast<size_t>(T * N));
+  std::vector<double> lse(static_cast<size_t>(T));
+
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * N;
+    double m = -std::numeric_limits<double>::infinity();
+    for (int64_t e = 0; e < N; ++e) m = std::max(m, static_cast<double>(l[e]));
+    double sum = 0.0;
+    for (int64_t e = 0; e < N; ++e) sum += std::exp(static_cast<double>(l[e]) - m);
+    for (int64_t e = 0; e < N; ++e) p_all[t * N + e] = std::exp(static_cast<double>(l[e]) - m) / sum;
+    lse[t] = m + std::log(sum);
+
+    // selection: k rounds, each taking the largest remaining logit; scanning e
+    // upward with a strict '>' keeps the lower index on exact ties.
+    std::vector<char> taken(static_cast<size_t>(N), 0);
+    int32_t* S = topk_idx + t * k;
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < N; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+      taken[best] = 1;
+      S[j] = static_cast<int32_t>(best);
+    }
+    if (margin_set) {
+      double next = -std::numeric_limits<double>::infinity();
+      for (int64_t e = 0; e < N; ++e)
+        if (!taken[e]) next = std::max(next, static_cast<double>(l[e]));
+      margin_set[t] = (k == N) ? std::numeric_limits<double>::infinity()
+                               : static_cast<double>(l[S[k - 1]]) - next;
+    }
+    if (margin_order) {
+      double mo = std::numeric_limits<double>::infinity();
+      for (int64_t j = 0; j + 1 < k; ++j)
+        mo = std::min(mo, static_cast<double>(l[S[j]]) - static_cast<double>(l[S[j + 1]]));
+      margin_order[t] = mo;
+    }
+    if (topk_w) {
+      double* g = topk_w + t * k;
+      if (s->gating == 0) {
+        for (int64_t j = 0; j < k; ++j) g[j] = p_all[t * N + S[j]];
+      } else if (s->gating == 1) {
+        double den = 0.0;
+        for (int64_t j = 0; j < k; ++j) den += p_all[t * N + S[j]];
+        for (int64_t j = 0; j < k; ++j) g[j] = p_all[t * N + S[j]] / den;
+      } else {
+        const double m0 = static_cast<double>(l[S[0]]);  // largest selected logit
+        double den = 0.0;
+        for (int64_t j = 0; j < k; ++j) den += std::exp(static_cast<double>(l[S[j]]) - m0);
+        for (int64_t j = 0; j < k; ++j) g[j] = std::exp(static_cast<double>(l[S[j]]) - m0) / den;
+      }
+    }
+  }
+
+  if (probs) std::memcpy(probs, p_all.data(), sizeof(double) * static_cast<size_t>(T * N));
+  if (lse_out) std::memcpy(lse_out, lse.data(), sizeof(double) * static_cast<size_t>(T));
+
+  std::vector<int64_t> cnt(static_cast<size_t>(N), 0);
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < k; ++j) cnt[topk_idx[t * k + j]] += 1;
+  std::vector<double> Pv(static_cast<size_t>(N), 0.0), fv(static_cast<size_t>(N), 0.0);
+  for (int64_t e = 0; e < N; ++e) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) acc += p_all[t * N + e];
+    Pv[e] = (T > 0) ? acc / static_cast<double>(T) : 0.0;
+    fv[e] = (T > 0) ? static_cast<double>(cnt[e]) / static_cast<double>(T * k) : 0.0;
+  }
+  double dot = 0.0;
+  for (int64_t e = 0; e < N; ++e) dot += fv[e] * Pv[e];
+  double lse_sum = 0.0, lse_sq = 0.0;
+  for (int64_t t = 0; t < T; ++t) { lse_sum += lse[t]; lse_sq += lse[t] * lse[t]; }
+  const double lse_mean = (T > 0) ? lse_sum / static_cast<double>(T) : 0.0;
+
+  if (counts) std::memcpy(counts, cnt.data(), sizeof(int64_t) * static_cast<size_t>(N));
+  if (f) std::memcpy(f, fv.data(), sizeof(double) * static_cast<size_t>(N));
+  if (P) std::memcpy(P, Pv.data(), sizeof(double) * static_cast<size_t>(N));
+  if (l_aux) *l_aux = s->aux_alpha * static_cast<double>(N) * dot;
+  if (z) *z = lse_mean * lse_mean;
+  if (lse_sq_mean) *lse_sq_mean = (T > 0) ? lse_sq / static_cast<double>(T) : 0.0;
+  return 0;
+}
+
+// Dispatch with capacity [AIG capacity equation and `MoE` module;
+// MOEA "Capacity and Token Dropping"]. For every expert e (ascending), the
+// tokens that selected e in ascending token order; the first min(count, C)
+// are kept. The kept pairs, experts ascending and tokens ascending within an
+// expert, define the permuted row order:
+//   kept[e], offsets[e] = sum_{e' < e} kept[e'] (offsets[N] = M),
+//   perm_token[row] = token of that row (rows >= M are -1),
+//   inv_map[t*k + j] = row of pair (t, S_t[j]), or -1 if dropped.
+int orc_dispatch(const OrcShape* s, const int32_t* topk_idx, int32_t* kept, int32_t* offsets,
+                 int32_t* perm_token, int32_t* inv_map, int64_t* n_dropped) {
+  if (!shape_ok(s) || !topk_idx) return -1;
+  const int64_t T = s->T, N = s->n_experts, k = s->top_k;
+  const int64_t C = s->capacity;
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> lists(static_cast<size_t>(N));
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = topk_idx[t * k + j];
+      if (e < 0 || e >= N) return -1;
+      lists[e].push_back({t, j});
+    }
+  int64_t row = 0, dropped = 0;
+  for (int64_t i = 0; i < T * k; ++i) {
+    if (inv_map) inv_map[i] = -1;
+    if (perm_token) perm_token[i] = -1;
+  }
+  for (int64_t e = 0; e < N; ++e) {
+    const int64_t cnt = static_cast<int64_t>(lists[e].size());
+    const int64_t keep = (C < 0) ? cnt : std::min(cnt, C);
+    if (offsets) offsets[e] = static_cast<int32_t>(row);
+    if (kept) kept[e] = static_cast<int32_t>(keep);
+    for (int64_t r = 0; r < keep; ++r) {
+      const auto& pr = lists[e][r];
+      if (perm_token) perm_token[row] = static_cast<int32_t>(pr.first);
+      if (inv_map) inv_map[pr.first * k + pr.second] = static_cast<int32_t>(row);
+      ++row;
+    }
+    dropped += cnt - keep;
+  }
+  if (offsets) offsets[N] = static_cast<int32_t>(row);
+  if (n_dropped) *n_dropped = dropped;
+  return 0;
+}
+
+// Expert e (or shared expert e when `shared` != 0) applied to n rows given in
+// the activation dtype: Y[r] = E_e(X[r]), fp64 output.
+int orc_expert_rows(const OrcShape* s, const OrcWeights* w, int shared, int e, const void* X,
+                    int64_t n, double* Y) {
+  if (!shape_ok(s) || !w || !X || !Y) return -1;
+  if (shared ? (e < 0 || e >= s->n_shared) : (e < 0 || e >= s->n_experts)) return -1;
+  std::vector<double> Xd(static_cast<size_t>(n * s->d));
+  for (int64_t i = 0; i < n * s->d; ++i) Xd[i] = elem(X, s->act_dtype, i, 1.0);
+  expert_rows(s, w, shared != 0, e, Xd.data(), n, Y);
+  return 0;
+}
+
+// Layer output for the tokens listed in `tokens` (n_tok of them), following
+// the per-expert masked loop of [AIG `MoE` module] and the weighted sum
+// y = sum_{i in top-k} g_i E_i(x) [AIG equation; SPX "Key Equations"], plus
+// the always-on shared experts [SPX "Shared + Specialized"; MOEA "Shared vs
+// Specialized Experts"]:
+//   y_t = sum_{j : inv_map[t][j] >= 0} g[t][j] * E_{S_t[j]}(x_t) + sum_s E^sh_s(x_t)
+// Dropped pairs (inv_map < 0) add nothing; the gates are not renormalised
+// after drops. topk_idx, topk_w and inv_map cover all T tokens.
+int orc_moe_output(const OrcShape* s, const void* x, const OrcWeights* w, const int32_t* topk_idx,
+                   const double* topk_w, const int32_t* inv_map, const int64_t* tokens,
+                   int64_t n_tok, double* y) {
+  if (!shape_ok(s) || !x || !w || !topk_idx || !topk_w || !tokens || !y) return -1;
+  const int64_t d = s->d, k = s->top_k, N = s->n_experts;
+  for (int64_t i = 0; i < n_tok * d; ++i) y[i] = 0.0;
+  for (int64_t e = 0; e < N; ++e) {
+    // mask: the listed tokens whose kept selection includes e
+    std::vector<int64_t> which;   // position in `tokens`
+    std::vector<double> gate;
+    for (int64_t i = 0; i < n_tok; ++i) {
+      const int64_t t = tokens[i];
+      for (int64_t j = 0; j < k; ++j)
+        if (topk_idx[t * k + j] == e && (!inv_map || inv_map[t * k + j] >= 0)) {
+          which.push_back(i);
+          gate.push_back(topk_w[t * k + j]);
+        }
+    }
+    if (which.empty()) continue;
+    const int64_t n = static_cast<int64_t>(which.size());
+    std::vector<double> X(static_cast<size_t>(n * d)), Y(static_cast<size_t>(n * d));
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) X[r * d + c] = elem(x, s->act_dtype, tokens[which[r]] * d + c, 1.0);
+    expert_rows(s, w, false, static_cast<int>(e), X.data(), n, Y.data());
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) y[which[r] * d + c] += gate[r] * Y[r * d + c];
+  }
+  if (s->n_shared > 0) {
+    std::vector<double> X(static_cast<size_t>(n_tok * d)), Y(static_cast<size_t>(n_tok * d));
+    for (int64_t r = 0; r < n_tok; ++r)
+      for (int64_t c = 0; c < d; ++c) X[r * d + c] = elem(x, s->act_dtype, tokens[r] * d + c, 1.0);
+    for (int sh = 0; sh < s->n_shared; ++sh) {
+      expert_rows(s, w, true, sh, X.data(), n_tok, Y.data());
+      for (int64_t i = 0; i < n_tok * d; ++i) y[i] += Y[i];
+    }
+  }
+  return 0;
+}
+
+// Combine alone [AIG `MoE` module, out[index] += w * expert(x[index])]: given
+// permuted expert outputs y_perm [M][d] (activation dtype), the pair -> row map
+// and the gates, y_t = sum_{j : inv_map >= 0} g[t][j] * y_perm[inv_map[t][j]]
+// (+ sum_s y_shared[s][t] when y_shared is given, [S][T][d] activation dtype).
+int orc_combine(const OrcShape* s, const void* y_perm, const int32_t* inv_map, const float* topk_w,
+                const void* y_shared, double* y) {
+  if (!shape_ok(s) || !y_perm || !inv_map || !topk_w || !y) return -1;
+  const int64_t T = s->T, d = s->d, k = s->top_k;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        const int64_t row = inv_map[t * k + j];
+        if (row >= 0) acc += static_cast<double>(topk_w[t * k + j]) * elem(y_perm, s->act_dtype, row * d + c, 1.0);
+      }
+      if (y_shared)
+        for (int64_t sh = 0; sh < s->n_shared; ++sh)
+          acc += elem(y_shared, s->act_dtype, (sh * T + t) * d + c, 1.0);
+      y[t * d + c] = acc;
+    }
+  }
+  return 0;
+}
+
+// Exact decoders, exported so that tests can pin them to library conversions.
+double orc_bf16_value(uint16_t b) { return bf16_value(b); }
+double orc_e4m3_value(uint8_t q) { return e4m3_value(q); }
+double orc_gelu(double u) { return gelu(u); }
+double orc_silu(double u) { return silu(u); }
+
+}  // extern "C"
