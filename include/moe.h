@@ -1,0 +1,239 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) top-k token-choice Mixture-of-Experts
+ * layer forward.
+ *
+ * The layer (pages, cited by title and section or equation):
+ *   aigrafen.se "Mixture of Experts": y = sum_{i in top-k} g_i E_i(x) with
+ *     g = softmax(W_r x); L_aux = alpha N sum_i f_i P_i; capacity
+ *     C = tokens / experts * capacity factor; the `MoE` module (softmax, top-k,
+ *     renormalise, int(cf*T*k/N), per-expert `nonzero` order truncated to C).
+ *   vanos001 "MoE Architecture": "Router Design" (top-k on logits, softmax over
+ *     the k), "Expert Network Design" (SwiGLU and GELU experts), "Capacity and
+ *     Token Dropping", "Shared vs Specialized Experts".
+ *   learn.starphix.com "Mixture of Experts (MoE)": "Key Equations", "Top-k
+ *     Gating", "Load Balancing (Critical)" (load_balancing_loss, z_loss),
+ *     "Shared + Specialized", "Quantization".
+ *
+ * Conventions for every entry point:
+ *  - Memory: every pointer argument is DEVICE memory except the moe_shape /
+ *    moe_weights / moe_stats structs themselves, which are read on the host
+ *    during the call (the pointers inside them are device pointers). The
+ *    caller allocates and owns every buffer; the library never allocates,
+ *    frees or keeps a pointer after returning. Buffers must stay valid until
+ *    the work enqueued on `stream` has finished.
+ *  - Asynchrony: work is enqueued on `stream` (0 = the null stream) and the
+ *    call returns without synchronising. Results are valid after the caller
+ *    synchronises with the stream.
+ *  - Layout: row-major. Tokens are the flattened batch*sequence rows [T][d].
+ *    Weights use the nn.Linear layout [out][in], stacked per expert:
+ *    W_r [N][d], W1 and W3 [N][d_ff][d], W2 [N][d][d_ff].
+ *  - Errors: arguments are validated on the host before anything is launched.
+ *    A negative moe_status means nothing was enqueued, except MOE_ERR_HIP, which
+ *    reports a failed launch (the HIP error code is kept per thread and read
+ *    with moe_last_hip_error()). No C++ exception crosses this interface.
+ *  - Workspace: `ws` is caller-provided device scratch of at least
+ *    moe_workspace_size() bytes for that entry point, 256-byte aligned. Its
+ *    contents on entry do not matter; they are clobbered.
+ *  - Limits: 1 <= N <= 256, 1 <= k <= min(8, N), n_shared <= 4, d and d_ff
+ *    multiples of 128, T <= 2^24, T*k*max(d, d_ff) < 2^31. Otherwise
+ *    MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad shape, k > N, ... */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside the limits above */
+  MOE_ERR_HIP = -3,         /* a launch failed; see moe_last_hip_error() */
+  MOE_ERR_WORKSPACE = -4    /* ws is null, misaligned or smaller than required */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Expert FFN. GELU: y = W2 gelu(W1 x + b1) + b2 with the exact erf GELU
+ * (aigrafen "Mixture of Experts", `MoE` module; vanos001 "Expert Network
+ * Design", StandardExpert). SwiGLU: y = W2 (silu(W1 x) * W3 x), no biases
+ * (vanos001 "Expert Network Design", SwiGLUExpert). */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* Gates of the k selected experts S_t (selection is always the k largest fp32
+ * logits, descending, exact ties to the lower expert index):
+ *  SOFTMAX_TOPK:        g_j = softmax(l_t)[S_j]  (aigrafen, the y/g equation;
+ *                       wiki.ai-engineering.at router/top-k figure)
+ *  SOFTMAX_TOPK_RENORM: the same, divided by their sum (aigrafen `MoE` module)
+ *  TOPK_SOFTMAX:        softmax over the k selected logits (vanos001
+ *                       Token-Choice Router; starphix "Top-k Gating") --
+ *                       equal to SOFTMAX_TOPK_RENORM in exact arithmetic. */
+typedef enum {
+  MOE_GATE_SOFTMAX_TOPK = 0,
+  MOE_GATE_SOFTMAX_TOPK_RENORM = 1,
+  MOE_GATE_TOPK_SOFTMAX = 2
+} moe_gating;
+
+typedef struct {
+  int64_t T;          /* tokens in the call (batch * sequence) */
+  int64_t d;          /* model width */
+  int64_t d_ff;       /* expert hidden width */
+  int32_t n_experts;  /* N routed experts */
+  int32_t top_k;      /* k */
+  int32_t n_shared;   /* always-on shared experts, same shape and act (0..4) */
+  int32_t act;        /* moe_act */
+  int32_t gating;     /* moe_gating */
+  int32_t act_dtype;  /* moe_dtype of x, W_r, the layer output: MOE_F32 or MOE_BF16 */
+  int32_t w_dtype;    /* moe_dtype of expert weights: same as act_dtype, or
+                         MOE_FP8_E4M3 with act_dtype MOE_BF16 */
+  int64_t capacity;   /* C pairs per expert; -1 = no limit (dropless) */
+  float aux_alpha;    /* alpha of L_aux (the pages use about 0.01) */
+} moe_shape;
+
+typedef struct {
+  const void* w_router;   /* [N][d], act_dtype (router stays 16/32-bit) */
+  const float* b_router;  /* [N] fp32 logit bias or NULL */
+  const void* w1;         /* [N][d_ff][d] w_dtype */
+  const void* w3;         /* [N][d_ff][d] w_dtype (SwiGLU only, else NULL) */
+  const void* w2;         /* [N][d][d_ff] w_dtype */
+  const float* b1;        /* [N][d_ff] fp32 or NULL (GELU only) */
+  const float* b2;        /* [N][d] fp32 or NULL (GELU only) */
+  const float* w_scale;   /* [N][3] fp32 per-tensor scales of (W1, W3, W2) for
+                             MOE_FP8_E4M3 (W = scale * code), else NULL */
+  const void* sw1;        /* shared experts: [n_shared][d_ff][d] */
+  const void* sw3;        /* [n_shared][d_ff][d] (SwiGLU) */
+  const void* sw2;        /* [n_shared][d][d_ff] */
+  const float* sw_scale;  /* [n_shared][3] for MOE_FP8_E4M3 */
+} moe_weights;
+
+/* Router statistics (aigrafen L_aux equation and `latest` dict; starphix
+ * load_balancing_loss and z_loss). Every member is a device pointer; any
+ * member may be NULL (not written). Written by moe_route (counts, f, P, l_aux,
+ * z_loss, lse_mean, lse_sq_mean) and moe_permute (kept, n_dropped). */
+typedef struct {
+  int32_t* counts;      /* [N] pairs that selected expert e, before capacity drops */
+  int32_t* kept;        /* [N] pairs kept after the capacity cut */
+  float* f;             /* [N] counts / (T k) */
+  float* P;             /* [N] mean over tokens of the full softmax */
+  float* l_aux;         /* [1] alpha * N * sum_e f_e P_e */
+  float* z_loss;        /* [1] (mean_t logsumexp_t)^2 */
+  float* lse_mean;      /* [1] mean_t logsumexp_t */
+  float* lse_sq_mean;   /* [1] mean_t logsumexp_t^2 */
+  int32_t* n_dropped;   /* [1] pairs dropped by the capacity cut */
+} moe_stats;
+
+/* Entry points whose workspace size can be queried. */
+typedef enum {
+  MOE_ENTRY_ROUTE = 0,
+  MOE_ENTRY_PERMUTE = 1,
+  MOE_ENTRY_GROUPED_FFN = 2,
+  MOE_ENTRY_FORWARD = 3
+} moe_entry;
+
+/* moe_route flag: take the fp32 logits from `logits` instead of computing the
+ * router GEMM (x and w_router are then ignored and may be NULL). */
+#define MOE_ROUTE_LOGITS_GIVEN 1u
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Static text for a moe_status (never NULL). */
+const char* moe_status_string(int status);
+
+/* hipError_t of the last MOE_ERR_HIP returned on this host thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* Expert capacity C = floor(cf * T * k / N), evaluated in fp64 (aigrafen
+ * capacity equation with the module's int(cf*T*k/N)). Returns -1 for cf < 0
+ * (no limit) and for N < 1. Host function. */
+int64_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf);
+
+/* Device workspace bytes that `entry` needs for `shape`. */
+moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* bytes);
+
+/*
+ * Router (aigrafen y/g equation; starphix "Key Equations" router_logits = x W_r^T;
+ * vanos001 Token-Choice Router; starphix load_balancing_loss and z_loss).
+ *   logits[t][e] = sum_i x[t][i] W_r[e][i] (+ b_router[e])   fp32 accumulation
+ *   topk_idx[t][j], topk_w[t][j]: the k largest logits, descending (ties to the
+ *   lower index), gates per shape->gating; statistics into `stats`.
+ * x [T][d] act_dtype; logits [T][N] fp32 (written, or read with
+ * MOE_ROUTE_LOGITS_GIVEN); topk_idx [T][k] int32; topk_w [T][k] fp32.
+ * Deterministic: identical inputs give identical bits.
+ */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router,
+                     const float* b_router, float* logits, uint32_t flags, int32_t* topk_idx,
+                     float* topk_w, const moe_stats* stats, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Dispatch with expert capacity (aigrafen capacity equation and `MoE` module;
+ * vanos001 "Capacity and Token Dropping"). For each expert e the pairs (t, j)
+ * with topk_idx[t][j] == e, in ascending token order; the first
+ * min(count, C) are kept, the rest dropped. Kept pairs are laid out expert by
+ * expert, tokens ascending within an expert:
+ *   expert_offsets [N+1]: offsets[e] = sum_{e'<e} kept[e'], offsets[N] = M
+ *   perm_token [T*k]: token of permuted row r < M (rows >= M not written)
+ *   inv_map [T][k]: permuted row of pair (t, j), or -1 when dropped
+ *   x_perm [T*k][d] (act_dtype): x_perm[r] = x[perm_token[r]] for r < M
+ * topk_idx [T][k] int32 with values in [0, N), distinct within a row.
+ * Writes stats->kept and stats->n_dropped when given. Bit-deterministic.
+ */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
+                       void* x_perm, const moe_stats* stats, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * Grouped expert FFN (vanos001 "Expert Network Design" and "Efficient Batched
+ * MoE"): for every expert e and every row r in [offsets[e], offsets[e+1]),
+ *   y_perm[r] = E_e(x_perm[r]);
+ * and, when shape->n_shared > 0 (starphix "Shared + Specialized"), for every
+ * shared expert s and token t, y_shared[s][t] = E^sh_s(x[t]).
+ * x_perm, y_perm [rows][d] act_dtype; expert_offsets [N+1] (device, as written
+ * by moe_permute, nondecreasing, offsets[0] = 0, offsets[N] <= T*k);
+ * x [T][d] and y_shared [n_shared][T][d] (required iff n_shared > 0).
+ * The hidden activation is kept in act_dtype (bf16 for bf16 layers).
+ */
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
+                           const int32_t* expert_offsets, const void* x,
+                           const moe_weights* weights, void* y_perm, void* y_shared, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Combine (aigrafen y = sum g_i E_i(x) and the module's out[index] += w * ...;
+ * starphix "Shared + Specialized"):
+ *   y[t] = sum_{j : inv_map[t][j] >= 0} topk_w[t][j] * y_perm[inv_map[t][j]]
+ *          + sum_s y_shared[s][t]
+ * A dropped pair adds 0 (the residual connection is outside this layer); the
+ * gates are not renormalised after drops. y_shared may be NULL.
+ * fp32 accumulation in a fixed order (slots ascending, then shared experts).
+ */
+moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_map,
+                       const float* topk_w, const void* y_shared, void* y, hipStream_t stream);
+
+/*
+ * Whole layer: moe_route -> moe_permute -> moe_grouped_ffn (routed + shared)
+ * -> moe_combine, enqueued on one stream with no host synchronisation.
+ * x [T][d], y [T][d] act_dtype. logits [T][N], topk_idx/topk_w/inv_map [T][k],
+ * expert_offsets [N+1], perm_token [T*k] are optional outputs (NULL: kept in
+ * the workspace). stats may be NULL.
+ */
+moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights* weights,
+                       void* y, float* logits, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
+                       const moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

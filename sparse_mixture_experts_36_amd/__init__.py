@@ -1,0 +1,257 @@
+"""MI355X (gfx950) top-k token-choice Mixture-of-Experts layer forward.
+
+Thin Python binding over the C ABI in ``include/moe.h`` (``libmoe.so``, built
+in-tree by ``sparse_mixture_experts_36_amd.build``). The functions here only
+marshal torch tensors (device memory) and the current HIP stream into the C
+entry points of the same names; every step of the layer runs in the library's
+HIP kernels. There is no fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = 0, -1, -2, -3, -4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+GELU, SWIGLU = 0, 1
+SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
+ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_FFN, ENTRY_FORWARD = 0, 1, 2, 3
+ROUTE_LOGITS_GIVEN = 1
+
+
+class Shape(ctypes.Structure):
+    """moe_shape"""
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("gating", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("capacity", ctypes.c_int64), ("aux_alpha", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    """moe_weights (device pointers)"""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2",
+                 "sw_scale")]
+
+
+class Stats(ctypes.Structure):
+    """moe_stats (device pointers)"""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("counts", "kept", "f", "P", "l_aux", "z_loss", "lse_mean", "lse_sq_mean", "n_dropped")]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().moe_status_string(status).decode()
+        if status == MOE_ERR_HIP:
+            msg += f" (hipError {lib().moe_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_mixture_experts_36_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        sp, wp, stp = ctypes.POINTER(Shape), ctypes.POINTER(Weights), ctypes.POINTER(Stats)
+        L.moe_abi_version.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_hip_error.restype = ctypes.c_int
+        L.moe_capacity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
+        L.moe_capacity.restype = ctypes.c_int64
+        L.moe_workspace_size.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(sz)]
+        L.moe_route.argtypes = [sp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, stp, vp, sz, vp]
+        L.moe_permute.argtypes = [sp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
+        L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
+        L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.moe_forward.argtypes = [sp, vp, wp, vp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
+        for f in ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
+                  "moe_forward"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoEError(rc, what)
+
+
+def make_shape(T, d, d_ff, n_experts, top_k, act, gating, act_dtype, w_dtype, capacity=-1, n_shared=0,
+               aux_alpha=0.01) -> Shape:
+    return Shape(T=T, d=d, d_ff=d_ff, n_experts=n_experts, top_k=top_k, n_shared=n_shared, act=act,
+                 gating=gating, act_dtype=act_dtype, w_dtype=w_dtype, capacity=capacity, aux_alpha=aux_alpha)
+
+
+def capacity(T: int, k: int, N: int, cf: float | None) -> int:
+    """floor(cf*T*k/N) (moe_capacity); -1 when cf is None (dropless)."""
+    return -1 if cf is None else lib().moe_capacity(T, k, N, cf)
+
+
+def workspace_size(shape: Shape, entry: int = ENTRY_FORWARD) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(shape), entry, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(shape: Shape, entry: int = ENTRY_FORWARD, device="cuda"):
+    """A device byte tensor big enough for `entry` (torch's allocator aligns to 256 B or more)."""
+    import torch
+    return torch.empty(workspace_size(shape, entry), dtype=torch.uint8, device=device)
+
+
+def stats_struct(st: dict | None) -> Stats | None:
+    if st is None:
+        return None
+    return Stats(**{k: _ptr(v) for k, v in st.items() if v is not None})
+
+
+def alloc_stats(N: int, device="cuda") -> dict:
+    import torch
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return {"counts": torch.zeros(N, **i32), "kept": torch.zeros(N, **i32), "f": torch.zeros(N, **f32),
+            "P": torch.zeros(N, **f32), "l_aux": torch.zeros(1, **f32), "z_loss": torch.zeros(1, **f32),
+            "lse_mean": torch.zeros(1, **f32), "lse_sq_mean": torch.zeros(1, **f32),
+            "n_dropped": torch.zeros(1, **i32)}
+
+
+def route(shape, x, w_router, b_router, logits, topk_idx, topk_w, stats=None, ws=None, flags=0, stream=None):
+    st = stats_struct(stats)
+    ws_ = ws if ws is not None else workspace(shape, ENTRY_ROUTE)
+    rc = lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits), flags,
+                         _ptr(topk_idx), _ptr(topk_w), ctypes.byref(st) if st else None, _ptr(ws_),
+                         ws_.numel(), _stream(stream))
+    _check(rc, "moe_route")
+
+
+def permute(shape, topk_idx, x, expert_offsets, perm_token, inv_map, x_perm, stats=None, ws=None, stream=None):
+    st = stats_struct(stats)
+    ws_ = ws if ws is not None else workspace(shape, ENTRY_PERMUTE)
+    rc = lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(x), _ptr(expert_offsets), _ptr(perm_token),
+                           _ptr(inv_map), _ptr(x_perm), ctypes.byref(st) if st else None, _ptr(ws_), ws_.numel(),
+                           _stream(stream))
+    _check(rc, "moe_permute")
+
+
+def grouped_ffn(shape, x_perm, expert_offsets, x, weights: Weights, y_perm, y_shared=None, ws=None, stream=None):
+    ws_ = ws if ws is not None else workspace(shape, ENTRY_GROUPED_FFN)
+    rc = lib().moe_grouped_ffn(ctypes.byref(shape), _ptr(x_perm), _ptr(expert_offsets), _ptr(x),
+                               ctypes.byref(weights), _ptr(y_perm), _ptr(y_shared), _ptr(ws_), ws_.numel(),
+                               _stream(stream))
+    _check(rc, "moe_grouped_ffn")
+
+
+def combine(shape, y_perm, inv_map, topk_w, y_shared, y, stream=None):
+    rc = lib().moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(inv_map), _ptr(topk_w), _ptr(y_shared),
+                           _ptr(y), _stream(stream))
+    _check(rc, "moe_combine")
+
+
+def forward(shape, x, weights: Weights, y, logits=None, topk_idx=None, topk_w=None, expert_offsets=None,
+            perm_token=None, inv_map=None, stats=None, ws=None, stream=None):
+    st = stats_struct(stats)
+    ws_ = ws if ws is not None else workspace(shape, ENTRY_FORWARD)
+    rc = lib().moe_forward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y), _ptr(logits),
+                           _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_token), _ptr(inv_map),
+                           ctypes.byref(st) if st else None, _ptr(ws_), ws_.numel(), _stream(stream))
+    _check(rc, "moe_forward")
+
+
+def weights_struct(t: dict) -> Weights:
+    """moe_weights from a dict of device tensors (missing keys are NULL)."""
+    return Weights(**{k: _ptr(v) for k, v in t.items() if v is not None})
+
+
+@dataclass
+class LayerOutputs:
+    y: object
+    logits: object
+    topk_idx: object
+    topk_w: object
+    expert_offsets: object
+    perm_token: object
+    inv_map: object
+    stats: dict
+
+
+class MoELayer:
+    """Device-resident weights + workspace for repeated moe_forward calls.
+
+    `tensors` maps moe_weights member names to device tensors (bf16 data may be
+    given as torch.bfloat16 or int16/uint16 bit patterns; e4m3 as uint8)."""
+
+    def __init__(self, shape: Shape, tensors: dict, device="cuda"):
+        import torch
+        self.shape = shape
+        self.tensors = tensors
+        self.weights = weights_struct(tensors)
+        self.ws = workspace(shape, ENTRY_FORWARD, device)
+        T, N, k = shape.T, shape.n_experts, shape.top_k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.out = LayerOutputs(
+            y=torch.empty((T, shape.d), dtype=torch.float32 if shape.act_dtype == F32 else torch.bfloat16,
+                          device=device),
+            logits=torch.empty((T, N), dtype=torch.float32, device=device),
+            topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+            expert_offsets=torch.empty(N + 1, **i32), perm_token=torch.empty(T * k, **i32),
+            inv_map=torch.empty((T, k), **i32), stats=alloc_stats(N, device))
+
+    def __call__(self, x, stream=None) -> LayerOutputs:
+        o = self.out
+        forward(self.shape, x, self.weights, o.y, o.logits, o.topk_idx, o.topk_w, o.expert_offsets, o.perm_token,
+                o.inv_map, o.stats, self.ws, stream)
+        return o
+
+    def latest(self) -> dict:
+        """Host copy of the router statistics (synchronises): aux loss, z-loss,
+        dropped share and the per-expert token shares."""
+        st = {k: v.cpu() for k, v in self.out.stats.items()}
+        tk = self.shape.T * self.shape.top_k
+        return {"aux_loss": float(st["l_aux"][0]), "z_loss": float(st["z_loss"][0]),
+                "dropped_share": int(st["n_dropped"][0]) / max(tk, 1),
+                "distribution": [float(v) for v in st["f"]], "counts": [int(v) for v in st["counts"]],
+                "kept": [int(v) for v in st["kept"]],
+                "entropy": routing_entropy([float(v) for v in st["f"]])}
+
+
+# ---------------------------------------------------------------- host-side helpers
+
+def routing_entropy(f) -> float:
+    """Entropy of the per-expert token shares f (natural log). A collapse
+    detector: far below ln(N) means only a few experts are used (aigrafen.se
+    "Mixture of Experts", the collapsed/balanced routing example)."""
+    return -sum(p * math.log(p) for p in f if p > 0)
+
+
+def expert_params(d: int, d_ff: int, act: int) -> int:
+    """Weights of one expert: SwiGLU has three d x d_ff matrices, GELU two
+    (aigrafen.se "Mixture of Experts", the total/active parameter example)."""
+    return (3 if act == SWIGLU else 2) * d * d_ff

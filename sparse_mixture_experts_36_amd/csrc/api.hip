@@ -1,0 +1,412 @@
+// C ABI of the MoE layer forward: argument checks, workspace layout, and the
+// launch sequence of every entry point. All validation happens on the host
+// before anything is enqueued; nothing here allocates or synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxShared = 4;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rows reserved for routed experts: every kept pair has one row.
+int64_t routed_row_cap(const moe_shape& s) {
+  const int64_t tk = s.T * s.top_k;
+  if (s.capacity < 0) return tk;
+  const int64_t nc = static_cast<int64_t>(s.n_experts) * s.capacity;
+  return nc < tk ? nc : tk;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->d <= 0 || s->d_ff <= 0 || s->n_experts < 1 || s->top_k < 1 || s->top_k > s->n_experts ||
+      s->n_shared < 0 || s->capacity < -1)
+    return MOE_ERR_INVALID_ARG;
+  if (s->act != MOE_ACT_GELU && s->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (s->gating < MOE_GATE_SOFTMAX_TOPK || s->gating > MOE_GATE_TOPK_SOFTMAX) return MOE_ERR_INVALID_ARG;
+  if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (s->n_experts > kMaxExperts || s->top_k > kMaxTopK || s->n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
+  if (s->d % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->w_dtype != s->act_dtype && !(s->w_dtype == MOE_FP8_E4M3 && s->act_dtype == MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
+  if (s->T > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = s->T * s->top_k + static_cast<int64_t>(s->n_shared) * s->T;
+  const int64_t wmax = s->d > s->d_ff ? s->d : s->d_ff;
+  if (rows * wmax >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Workspace carving; the same walk serves the size query and the launch.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + sizeof(T) * count);
+    return p;
+  }
+};
+
+struct RouteWs {
+  float* part_P;
+  int32_t* part_cnt;
+  float* part_lse;
+};
+RouteWs carve_route(Carver& c, const moe_shape& s) {
+  const size_t nb = static_cast<size_t>(moe::ceil_div(s.T, moe::kRouteTokens));
+  RouteWs w;
+  w.part_P = c.take<float>(nb * s.n_experts);
+  w.part_cnt = c.take<int32_t>(nb * s.n_experts);
+  w.part_lse = c.take<float>(2 * nb);
+  return w;
+}
+
+struct PermWs {
+  int32_t *block_cnt, *block_base, *local_rank, *kept, *n_dropped;
+};
+PermWs carve_perm(Carver& c, const moe_shape& s) {
+  const size_t nb = static_cast<size_t>(moe::ceil_div(s.T, moe::kPermTokens));
+  PermWs w;
+  w.block_cnt = c.take<int32_t>(nb * s.n_experts);
+  w.block_base = c.take<int32_t>(nb * s.n_experts);
+  w.local_rank = c.take<int32_t>(static_cast<size_t>(s.T) * s.top_k);
+  w.kept = c.take<int32_t>(s.n_experts);
+  w.n_dropped = c.take<int32_t>(1);
+  return w;
+}
+
+struct FfnWs {
+  void* h;
+  moe::GroupDesc* groups;
+  int32_t* tile_start;
+};
+FfnWs carve_ffn(Carver& c, const moe_shape& s) {
+  const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
+  const size_t hrows = static_cast<size_t>(routed_row_cap(s) + static_cast<int64_t>(s.n_shared) * s.T);
+  FfnWs w;
+  w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff) * act_bytes(s.act_dtype));
+  w.groups = c.take<moe::GroupDesc>(2 * G);
+  w.tile_start = c.take<int32_t>(G + 1);
+  return w;
+}
+
+struct FwdWs {
+  float* logits;
+  int32_t *topk_idx, *inv_map, *offsets, *perm_token;
+  float* topk_w;
+  void *x_perm, *y_perm, *y_shared;
+};
+FwdWs carve_fwd(Carver& c, const moe_shape& s) {
+  const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(s.top_k);
+  const size_t cap = static_cast<size_t>(routed_row_cap(s));
+  const size_t rowb = static_cast<size_t>(s.d) * act_bytes(s.act_dtype);
+  FwdWs w;
+  w.logits = c.take<float>(T * s.n_experts);
+  w.topk_idx = c.take<int32_t>(T * k);
+  w.topk_w = c.take<float>(T * k);
+  w.inv_map = c.take<int32_t>(T * k);
+  w.offsets = c.take<int32_t>(s.n_experts + 1);
+  w.perm_token = c.take<int32_t>(T * k);
+  w.x_perm = c.take<char>(cap * rowb);
+  w.y_perm = c.take<char>(cap * rowb);
+  w.y_shared = c.take<char>(static_cast<size_t>(s.n_shared) * T * rowb);
+  return w;
+}
+
+size_t ws_bytes_for(const moe_shape& s, int32_t entry) {
+  Carver c{nullptr};
+  switch (entry) {
+    case MOE_ENTRY_ROUTE: carve_route(c, s); break;
+    case MOE_ENTRY_PERMUTE: carve_perm(c, s); break;
+    case MOE_ENTRY_GROUPED_FFN: carve_ffn(c, s); break;
+    default:
+      carve_route(c, s);
+      carve_perm(c, s);
+      carve_ffn(c, s);
+      carve_fwd(c, s);
+      break;
+  }
+  return c.off + kAlign;
+}
+
+moe_status check_ws(const moe_shape& s, int32_t entry, void* ws, size_t ws_bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_bytes_for(s, entry)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MOE_ERR_HIP;
+}
+
+moe::RouteArgs route_args(const moe_shape& s, const void* x, const void* w_router, const float* b_router,
+                          float* logits, bool given, int32_t* topk_idx, float* topk_w, const moe_stats* st,
+                          const RouteWs& w) {
+  moe::RouteArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.N = s.n_experts;
+  a.k = s.top_k;
+  a.gating = s.gating;
+  a.act_dtype = s.act_dtype;
+  a.logits_given = given;
+  a.x = x;
+  a.w_router = w_router;
+  a.b_router = b_router;
+  a.logits = logits;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.part_P = w.part_P;
+  a.part_cnt = w.part_cnt;
+  a.part_lse = w.part_lse;
+  if (st) {
+    a.counts = st->counts;
+    a.f = st->f;
+    a.P = st->P;
+    a.l_aux = st->l_aux;
+    a.z_loss = st->z_loss;
+    a.lse_mean = st->lse_mean;
+    a.lse_sq_mean = st->lse_sq_mean;
+  }
+  a.aux_alpha = s.aux_alpha;
+  return a;
+}
+
+moe::PermuteArgs perm_args(const moe_shape& s, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                           int32_t* perm_token, int32_t* inv_map, void* x_perm, const moe_stats* st,
+                           const PermWs& w) {
+  moe::PermuteArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.N = s.n_experts;
+  a.k = s.top_k;
+  a.act_bytes = act_bytes(s.act_dtype);
+  a.capacity = s.capacity;
+  a.topk_idx = topk_idx;
+  a.x = x;
+  a.offsets = offsets;
+  a.perm_token = perm_token;
+  a.inv_map = inv_map;
+  a.x_perm = x_perm;
+  a.kept = (st && st->kept) ? st->kept : w.kept;
+  a.n_dropped = (st && st->n_dropped) ? st->n_dropped : w.n_dropped;
+  a.block_cnt = w.block_cnt;
+  a.block_base = w.block_base;
+  a.local_rank = w.local_rank;
+  return a;
+}
+
+moe_status check_weights(const moe_shape& s, const moe_weights* w, bool need_router) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (need_router && !w->w_router) return MOE_ERR_INVALID_ARG;
+  if (!w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (s.act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARG;
+  if (s.w_dtype == MOE_FP8_E4M3 && !w->w_scale) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0) {
+    if (!w->sw1 || !w->sw2 || (s.act == MOE_ACT_SWIGLU && !w->sw3)) return MOE_ERR_INVALID_ARG;
+    if (s.w_dtype == MOE_FP8_E4M3 && !w->sw_scale) return MOE_ERR_INVALID_ARG;
+  }
+  const void* ptrs[] = {w->w_router, w->w1, w->w3, w->w2, w->sw1, w->sw3, w->sw2};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* offsets, const void* x,
+                      const moe_weights* w, void* y_perm, void* y_shared, const FfnWs& fw) {
+  moe::FfnArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.d_ff = s.d_ff;
+  a.n_routed = s.n_experts;
+  a.n_shared = s.n_shared;
+  a.act = s.act;
+  a.act_dtype = s.act_dtype;
+  a.w_dtype = s.w_dtype;
+  a.routed_row_cap = static_cast<int32_t>(routed_row_cap(s));
+  a.offsets = offsets;
+  a.x_perm = x_perm;
+  a.x = x;
+  a.w1 = w->w1;
+  a.w3 = w->w3;
+  a.w2 = w->w2;
+  a.b1 = w->b1;
+  a.b2 = w->b2;
+  a.w_scale = w->w_scale;
+  a.sw1 = w->sw1;
+  a.sw3 = w->sw3;
+  a.sw2 = w->sw2;
+  a.sw_scale = w->sw_scale;
+  a.h = fw.h;
+  a.y_perm = y_perm;
+  a.y_shared = y_shared;
+  a.groups = fw.groups;
+  a.tile_start = fw.tile_start;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf) {
+  if (cf < 0.0 || N < 1) return -1;
+  const double c = cf * static_cast<double>(T) * static_cast<double>(k) / static_cast<double>(N);
+  return static_cast<int64_t>(c);  // truncation = floor for c >= 0
+}
+
+moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* bytes) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes || entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_FORWARD) return MOE_ERR_INVALID_ARG;
+  *bytes = ws_bytes_for(*shape, entry);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                     float* logits, uint32_t flags, int32_t* topk_idx, float* topk_w, const moe_stats* stats,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
+  if ((flags & ~MOE_ROUTE_LOGITS_GIVEN) != 0) return MOE_ERR_INVALID_ARG;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!given && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(*shape, MOE_ENTRY_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  const RouteWs w = carve_route(c, *shape);
+  return hip_status(moe::launch_route(
+      route_args(*shape, x, w_router, b_router, logits, given, topk_idx, topk_w, stats, w), stream));
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
+                       int32_t* perm_token, int32_t* inv_map, void* x_perm, const moe_stats* stats, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !expert_offsets || !perm_token || !inv_map) return MOE_ERR_INVALID_ARG;
+  if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(*shape, MOE_ENTRY_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  const PermWs w = carve_perm(c, *shape);
+  return hip_status(moe::launch_permute(
+      perm_args(*shape, topk_idx, x, expert_offsets, perm_token, inv_map, x_perm, stats, w), stream));
+}
+
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* expert_offsets,
+                           const void* x, const moe_weights* weights, void* y_perm, void* y_shared, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !x_perm || !y_perm || !aligned16(x_perm) || !aligned16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (shape->n_shared > 0 && (!x || !y_shared || !aligned16(x) || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weights(*shape, weights, false)) != MOE_OK) return st;
+  if ((st = check_ws(*shape, MOE_ENTRY_GROUPED_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  Carver c{static_cast<char*>(ws)};
+  const FfnWs fw = carve_ffn(c, *shape);
+  return hip_status(
+      moe::launch_grouped_ffn(ffn_args(*shape, x_perm, expert_offsets, x, weights, y_perm, y_shared, fw), stream));
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_map, const float* topk_w,
+                       const void* y_shared, void* y, hipStream_t stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !inv_map || !topk_w || !y || !aligned16(y_perm) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (y_shared && !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
+  moe::CombineArgs a{};
+  a.T = shape->T;
+  a.d = shape->d;
+  a.k = shape->top_k;
+  a.n_shared = shape->n_shared;
+  a.act_dtype = shape->act_dtype;
+  a.y_perm = y_perm;
+  a.inv_map = inv_map;
+  a.topk_w = topk_w;
+  a.y_shared = y_shared;
+  a.y = y;
+  return hip_status(moe::launch_combine(a, stream));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights* weights, void* y, float* logits,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* perm_token,
+                       int32_t* inv_map, const moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weights(*shape, weights, true)) != MOE_OK) return st;
+  if ((st = check_ws(*shape, MOE_ENTRY_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  const moe_shape& s = *shape;
+  Carver c{static_cast<char*>(ws)};
+  const RouteWs rw = carve_route(c, s);
+  const PermWs pw = carve_perm(c, s);
+  const FfnWs fw = carve_ffn(c, s);
+  const FwdWs w = carve_fwd(c, s);
+  if (!logits) logits = w.logits;
+  if (!topk_idx) topk_idx = w.topk_idx;
+  if (!topk_w) topk_w = w.topk_w;
+  if (!inv_map) inv_map = w.inv_map;
+  if (!expert_offsets) expert_offsets = w.offsets;
+  if (!perm_token) perm_token = w.perm_token;
+
+  hipError_t e = moe::launch_route(
+      route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
+  if (e == hipSuccess)
+    e = moe::launch_permute(perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, w.x_perm, stats, pw),
+                            stream);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_ffn(ffn_args(s, w.x_perm, expert_offsets, x, weights, w.y_perm, w.y_shared, fw), stream);
+  if (e == hipSuccess) {
+    moe::CombineArgs a{};
+    a.T = s.T;
+    a.d = s.d;
+    a.k = s.top_k;
+    a.n_shared = s.n_shared;
+    a.act_dtype = s.act_dtype;
+    a.y_perm = w.y_perm;
+    a.inv_map = inv_map;
+    a.topk_w = topk_w;
+    a.y_shared = s.n_shared > 0 ? w.y_shared : nullptr;
+    a.y = y;
+    e = moe::launch_combine(a, stream);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Combine: gate-weighted gather of the expert outputs back to token order.
+//
+// Pages: aigrafen.se "Mixture of Experts" (y = sum_{i in top-k} g_i E_i(x);
+// the `MoE` module adds w * expert(x[index]) into out[index], so a token
+// dropped by the capacity cut gets nothing from that expert),
+// learn.starphix.com "Mixture of Experts (MoE)" / "Shared + Specialized"
+// (shared outputs are added to the routed sum).
+//
+// Gather form instead of a scatter-add: each token reads its own k rows, so no
+// atomics are needed and the sum order (slots ascending, then shared experts)
+// is fixed -- the output is bit-for-bit reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 8;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  const int64_t t = blockIdx.x;
+  const int k = a.k;
+  int64_t row[kMaxK];
+  float g[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    row[j] = -1;
+    g[j] = 0.f;
+    if (j < k) {
+      row[j] = a.inv_map[t * k + j];
+      g[j] = a.topk_w[t * k + j];
+    }
+  }
+  constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int64_t nch = a.d / E;
+  for (int64_t c = threadIdx.x; c < nch; c += kThreads) {
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    auto add = [&](const void* base, int64_t r, float w) {
+      const uint4 v = reinterpret_cast<const uint4*>(base)[r * nch + c];
+      if constexpr (BF16) {
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(u[e] & 0xFFFFu)), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(u[e] >> 16)), acc[2 * e + 1]);
+        }
+      } else {
+        acc[0] = fmaf(w, __uint_as_float(v.x), acc[0]);
+        acc[1] = fmaf(w, __uint_as_float(v.y), acc[1]);
+        acc[2] = fmaf(w, __uint_as_float(v.z), acc[2]);
+        acc[3] = fmaf(w, __uint_as_float(v.w), acc[3]);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && row[j] >= 0) add(a.y_perm, row[j], g[j]);
+    if (a.y_shared)
+      for (int s = 0; s < a.n_shared; ++s) add(a.y_shared, static_cast<int64_t>(s) * a.T + t, 1.0f);
+    uint4 o;
+    if constexpr (BF16) {
+      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                     pack_bf16x2(acc[6], acc[7]));
+    } else {
+      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                     __float_as_uint(acc[3]));
+    }
+    reinterpret_cast<uint4*>(a.y)[t * nch + c] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.act_dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,483 @@
+// Grouped expert FFN: up GEMM with fused activation, then down GEMM.
+//
+// Pages: vanos001 "MoE Architecture" / "Expert Network Design" (SwiGLUExpert:
+// w2(silu(w1 x) * w3 x); StandardExpert: Linear -> GELU -> Linear) and
+// "Efficient Batched MoE" (all experts' weights stacked and run as grouped
+// operations instead of a per-expert loop); aigrafen.se "Mixture of Experts"
+// (`MoE` module experts: Linear(d, hidden) -> GELU -> Linear(hidden, d));
+// learn.starphix.com "Mixture of Experts (MoE)" / "Shared + Specialized"
+// (always-on shared experts) and "Quantization" (low-precision expert
+// weights; here OCP e4m3 with one fp32 scale per expert matrix).
+//
+// Both GEMMs are "NT": C[m][n] = sum_k A[m][k] * B[n][k], A rows and weight
+// rows both contiguous in k (the nn.Linear layout). A group is one weight set
+// over a contiguous block of rows: the routed experts over their slices of the
+// permuted rows, then the shared experts over all T tokens, all in one launch.
+//
+// Tile schedule: the plan kernel turns the device-resident expert offsets into
+// per-group row-tile counts and their prefix (no host round trip). Tile L runs
+// group g's n-tile (L - base_g) / mt_g and m-tile (L - base_g) % mt_g, so the
+// row tiles that share one weight tile are consecutive; consecutive L are
+// mapped onto one XCD (workgroup ids reach the 8 XCDs round-robin), so they
+// run together and share that weight tile in the XCD's L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+struct GemmParams {
+  const void* A_r;        // routed A rows
+  const void* A_s;        // shared A rows
+  int64_t lda;            // = K
+  const void* B_r;        // routed weights [n_routed][Nout][K] (W1 or W2)
+  const void* B3_r;       // routed W3 (SwiGLU up GEMM) or null
+  const void* B_s;        // shared weights
+  const void* B3_s;
+  int64_t b_stride;       // elements per expert matrix = Nout * K
+  const float* bias;      // [n_routed][Nout] or null (routed GELU experts only)
+  const float* scale_r;   // [n_routed][3] (e4m3) or null
+  const float* scale_s;   // [n_shared][3]
+  int scale_col;          // 0 for the up GEMM (W1, W3 at +1), 2 for the down GEMM
+  void* C_r;
+  void* C_s;
+  int64_t ldc;            // = Nout
+  int32_t K, Nout;
+  int32_t n_routed, n_groups;
+  const GroupDesc* groups;
+  const int32_t* tile_start;  // [n_groups+1] row-tile prefix
+};
+
+enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_PLAIN = 2 };
+
+// Largest g < n with ts[g] <= m (ts nondecreasing, ts[0] = 0 <= m).
+__device__ __forceinline__ int find_group(const int32_t* ts, int n, int m) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ts[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct TileInfo {
+  int g, m_tile, n_tile, rows;
+  GroupDesc gd;
+};
+
+// Maps this workgroup to a tile; false when it has none.
+template <int BM, int BNO>
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
+  const int nt = p.Nout / BNO;
+  const int total = p.tile_start[p.n_groups] * nt;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int bid = blockIdx.x;
+  const int slot = bid / kXcds;
+  if (slot >= per_xcd) return false;
+  const int L = (bid % kXcds) * per_xcd + slot;
+  if (L >= total) return false;
+  const int g = find_group(p.tile_start, p.n_groups, L / nt);
+  const int base = p.tile_start[g] * nt;
+  const int mt = p.tile_start[g + 1] - p.tile_start[g];
+  const int local = L - base;
+  ti.g = g;
+  ti.n_tile = local / mt;
+  ti.m_tile = local % mt;
+  ti.gd = p.groups[g];
+  ti.rows = min(BM, ti.gd.rows - ti.m_tile * BM);
+  return true;
+}
+
+// ------------------------------------------------------------------ bf16 MFMA
+// 4 waves as 2 x 2; a wave owns BM/2 rows and BNO/2 output columns (for SwiGLU
+// the matching W1 and W3 columns, so silu(a) * b is formed in registers).
+template <int BM, int BNO, int EPI, bool FP8>
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int BNB = SWI ? 2 * BNO : BNO;  // weight rows per tile
+  constexpr int BK = 64;
+  constexpr int S = BK + 8;                 // padded LDS row (bf16 elements)
+  constexpr int WM = BM / 2, WNO = BNO / 2;
+  constexpr int FM = WM / 16;
+  constexpr int FNO = WNO / 16;
+  constexpr int FN = SWI ? 2 * FNO : FNO;
+  constexpr int A_CH = BM * (BK / 8) / kThreads;   // 16-byte chunks per thread
+  constexpr int B_CH = FP8 ? BNB * (BK / 16) / kThreads : BNB * (BK / 8) / kThreads;
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for 256 threads");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * S];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNB * S];
+
+  TileInfo ti;
+  if (!decode_tile<BM, BNO>(p, ti)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, c16 = lane & 15;
+  const bool shared = ti.g >= p.n_routed;
+  const int widx = ti.gd.widx;
+  const int ew = shared ? widx - p.n_routed : widx;
+  const int n0 = ti.n_tile * BNO;
+  const int K = p.K;
+
+  const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
+                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
+  const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r);
+  const char* B3w = static_cast<const char*>(shared ? p.B3_s : p.B3_r);
+  constexpr int WB = FP8 ? 1 : 2;  // weight bytes
+  const int64_t eoff = static_cast<int64_t>(ew) * p.b_stride * WB;
+
+  // per-thread global chunk sources
+  const uint16_t* a_src[A_CH];
+  int a_dst[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + i * kThreads;
+    int r = c >> 3;
+    const int kc = c & 7;
+    a_dst[i] = r * S + kc * 8;
+    if (r > ti.rows - 1) r = ti.rows - 1;  // rows past the group compute garbage, never stored
+    a_src[i] = A + static_cast<int64_t>(r) * p.lda + kc * 8;
+  }
+  const char* b_src[B_CH];
+  int b_dst[B_CH];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + i * kThreads;
+    constexpr int CPR = FP8 ? BK / 16 : BK / 8;  // chunks per row
+    const int r = c / CPR, kc = c % CPR;
+    b_dst[i] = r * S + kc * (FP8 ? 16 : 8);
+    const char* base = Bw;
+    int wr = n0 + r;
+    if (SWI && r >= BNO) {
+      base = B3w;
+      wr = n0 + r - BNO;
+    }
+    b_src[i] = base + eoff + (static_cast<int64_t>(wr) * K + kc * (FP8 ? 16 : 8)) * WB;
+  }
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[A_CH], rb[B_CH];
+#define MOE_GLOAD(kb)                                                                               \
+  do {                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                                        \
+        *reinterpret_cast<const uint4*>(a_src[i] + (kb));                                           \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                                        \
+        *reinterpret_cast<const uint4*>(b_src[i] + static_cast<int64_t>(kb) * WB);                  \
+  } while (0)
+#define MOE_LSTORE(buf)                                                                             \
+  do {                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                \
+        *reinterpret_cast<uint4*>(&sA[buf][a_dst[i]]) = ra[i];                                      \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                              \
+      if constexpr (FP8) {                                                                          \
+        const uint2 x0 = e4m3x4_to_bf16x4(rb[i].x), x1 = e4m3x4_to_bf16x4(rb[i].y);                 \
+        const uint2 x2 = e4m3x4_to_bf16x4(rb[i].z), x3 = e4m3x4_to_bf16x4(rb[i].w);                 \
+        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i]]) = make_uint4(x0.x, x0.y, x1.x, x1.y);         \
+        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i] + 8]) = make_uint4(x2.x, x2.y, x3.x, x3.y);     \
+      } else {                                                                                      \
+        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i]]) = rb[i];                                      \
+      }                                                                                             \
+    }                                                                                               \
+  } while (0)
+
+  const int KT = K / BK;
+  MOE_GLOAD(0);
+  MOE_LSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    // prefetch the next k-step (the last iteration re-reads its own step; the
+    // copy lands in the idle buffer and is never read)
+    const int kn = (kt + 1 < KT) ? (kt + 1) * BK : kt * BK;
+    MOE_GLOAD(kn);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      uint4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(&sA[buf][(wm * WM + i * 16 + c16) * S + kk * 32 + q * 8]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int brow = SWI ? ((j < FNO) ? wn * WNO + j * 16 : BNO + wn * WNO + (j - FNO) * 16)
+                             : wn * WNO + j * 16;
+        bf[j] = *reinterpret_cast<const uint4*>(&sB[buf][(brow + c16) * S + kk * 32 + q * 8]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+    }
+    MOE_LSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+
+  // ---- epilogue
+  const float* sc = shared ? p.scale_s : p.scale_r;
+  float s_a = 1.f, s_b = 1.f;
+  if (FP8 && sc) {
+    s_a = sc[ew * 3 + p.scale_col];
+    if (SWI) s_b = sc[ew * 3 + p.scale_col + 1];
+  }
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout : nullptr;
+  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
+                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FNO; ++j) {
+      const int col = wn * WNO + j * 16 + c16;
+      const float bv = bias ? bias[n0 + col] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * WM + i * 16 + q * 4 + r;
+        if (row >= ti.rows) continue;
+        float v;
+        if constexpr (EPI == EPI_SWIGLU) {
+          v = silu(acc[i][j][r] * s_a) * (acc[i][j + FNO][r] * s_b);
+        } else if constexpr (EPI == EPI_GELU) {
+          v = gelu_erf(acc[i][j][r] * s_a + bv);
+        } else {
+          v = acc[i][j][r] * s_a + bv;
+        }
+        C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+// Plain FMA tiles (64 x 64 outputs, 4 x 4 per thread) for fp32 layers.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int BM = 64, BNO = 64, BK = 16;
+  constexpr int BNB = SWI ? 2 * BNO : BNO;
+  __shared__ float sA[BK][BM + 4];
+  __shared__ float sB[BK][BNB + 4];
+
+  TileInfo ti;
+  if (!decode_tile<BM, BNO>(p, ti)) return;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const bool shared = ti.g >= p.n_routed;
+  const int widx = ti.gd.widx;
+  const int ew = shared ? widx - p.n_routed : widx;
+  const int n0 = ti.n_tile * BNO;
+  const int K = p.K;
+  const float* A = static_cast<const float*>(shared ? p.A_s : p.A_r) +
+                   (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
+  const float* Bw = static_cast<const float*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride;
+  const float* B3w = SWI ? static_cast<const float*>(shared ? p.B3_s : p.B3_r) + static_cast<int64_t>(ew) * p.b_stride
+                         : nullptr;
+
+  float acc[4][4] = {}, acc3[4][4] = {};
+  for (int kb = 0; kb < K; kb += BK) {
+    {
+      int r = tid >> 2;
+      const int k4 = (tid & 3) * 4;
+      const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;
+      const float4 v = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(rr) * p.lda + kb + k4);
+      sA[k4 + 0][r] = v.x;
+      sA[k4 + 1][r] = v.y;
+      sA[k4 + 2][r] = v.z;
+      sA[k4 + 3][r] = v.w;
+    }
+    for (int c = tid; c < BNB * 4; c += kThreads) {
+      const int r = c >> 2, k4 = (c & 3) * 4;
+      const float* src = (SWI && r >= BNO) ? B3w + static_cast<int64_t>(n0 + r - BNO) * K
+                                           : Bw + static_cast<int64_t>(n0 + r) * K;
+      const float4 v = *reinterpret_cast<const float4*>(src + kb + k4);
+      sB[k4 + 0][r] = v.x;
+      sB[k4 + 1][r] = v.y;
+      sB[k4 + 2][r] = v.z;
+      sB[k4 + 3][r] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], bv[4], b3[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = sA[kk][ty * 4 + i];
+        bv[i] = sB[kk][tx * 4 + i];
+        if (SWI) b3[i] = sB[kk][BNO + tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+          if (SWI) acc3[i][j] = fmaf(av[i], b3[j], acc3[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout : nullptr;
+  float* C = static_cast<float*>(shared ? p.C_s : p.C_r) +
+             (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = ty * 4 + i;
+    if (row >= ti.rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = tx * 4 + j;
+      float v;
+      if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j]) * acc3[i][j];
+      else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j] + (bias ? bias[n0 + col] : 0.f));
+      else v = acc[i][j] + (bias ? bias[n0 + col] : 0.f);
+      C[static_cast<int64_t>(row) * p.ldc + col] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ plan
+// Group descriptors of both GEMMs and the row-tile prefix for tile height bm.
+// Routed expert e: rows [offsets[e], offsets[e+1]) of x_perm / h / y_perm,
+// clamped to the reserved routed rows. Shared expert s: the T token rows; its
+// hidden rows sit after the routed ones in h, its outputs in y_shared[s].
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, int32_t n_routed, int32_t n_shared,
+                                                        int32_t T, int32_t cap, int32_t bm, GroupDesc* up,
+                                                        GroupDesc* down, int32_t* tile_start) {
+  __shared__ int32_t s_mt[kThreads + 8];
+  const int tid = threadIdx.x;
+  const int G = n_routed + n_shared;
+  for (int g = tid; g < G; g += kThreads) {
+    GroupDesc u, dn;
+    if (g < n_routed) {
+      int r0 = offsets[g], r1 = offsets[g + 1];
+      r0 = max(0, min(r0, cap));
+      r1 = max(r0, min(r1, cap));
+      u.a_row0 = u.c_row0 = dn.a_row0 = dn.c_row0 = r0;
+      u.rows = dn.rows = r1 - r0;
+    } else {
+      const int s = g - n_routed;
+      u.a_row0 = 0;
+      u.c_row0 = cap + s * T;
+      dn.a_row0 = cap + s * T;
+      dn.c_row0 = s * T;
+      u.rows = dn.rows = T;
+    }
+    u.widx = dn.widx = g;
+    up[g] = u;
+    down[g] = dn;
+    s_mt[g] = (u.rows + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int g = 0; g < G; ++g) {
+      tile_start[g] = acc;
+      acc += s_mt[g];
+    }
+    tile_start[G] = acc;
+  }
+}
+
+template <int BM, int BNO, int EPI, bool FP8>
+hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  int64_t grid = max_mtiles * (p.Nout / BNO);
+  grid = ceil_div(grid, kXcds) * kXcds;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNO, EPI, FP8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  int64_t grid = max_mtiles * (p.Nout / 64);
+  grid = ceil_div(grid, kXcds) * kXcds;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
+  const int G = a.n_routed + a.n_shared;
+  const bool f32 = (a.act_dtype == 0);
+  const int bm = f32 ? 64 : 128;
+  GroupDesc* up = a.groups;
+  GroupDesc* down = a.groups + G;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a.offsets, a.n_routed, a.n_shared,
+                     static_cast<int32_t>(a.T), a.routed_row_cap, bm, up, down, a.tile_start);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // upper bound on row tiles: every group may end in a partial tile
+  const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
+  const bool fp8 = (a.w_dtype == 2);
+  const bool swi = (a.act == 1);
+
+  GemmParams p{};
+  p.n_routed = a.n_routed;
+  p.n_groups = G;
+  p.tile_start = a.tile_start;
+  // up GEMM: [rows][d] x [d_ff][d]^T -> h [rows][d_ff]
+  p.A_r = a.x_perm;
+  p.A_s = a.x;
+  p.lda = a.d;
+  p.B_r = a.w1;
+  p.B3_r = a.w3;
+  p.B_s = a.sw1;
+  p.B3_s = a.sw3;
+  p.b_stride = a.d_ff * a.d;
+  p.bias = swi ? nullptr : a.b1;
+  p.scale_r = a.w_scale;
+  p.scale_s = a.sw_scale;
+  p.scale_col = 0;
+  p.C_r = a.h;
+  p.C_s = a.h;
+  p.ldc = a.d_ff;
+  p.K = static_cast<int32_t>(a.d);
+  p.Nout = static_cast<int32_t>(a.d_ff);
+  p.groups = up;
+  if (f32) {
+    err = swi ? run_f32<EPI_SWIGLU>(p, max_mtiles, s) : run_f32<EPI_GELU>(p, max_mtiles, s);
+  } else if (swi) {
+    err = fp8 ? run_bf16<128, 64, EPI_SWIGLU, true>(p, max_mtiles, s)
+              : run_bf16<128, 64, EPI_SWIGLU, false>(p, max_mtiles, s);
+  } else {
+    err = fp8 ? run_bf16<128, 128, EPI_GELU, true>(p, max_mtiles, s)
+              : run_bf16<128, 128, EPI_GELU, false>(p, max_mtiles, s);
+  }
+  if (err != hipSuccess) return err;
+
+  // down GEMM: h [rows][d_ff] x [d][d_ff]^T -> y [rows][d]
+  p.A_r = a.h;
+  p.A_s = a.h;
+  p.lda = a.d_ff;
+  p.B_r = a.w2;
+  p.B3_r = nullptr;
+  p.B_s = a.sw2;
+  p.B3_s = nullptr;
+  p.b_stride = a.d * a.d_ff;
+  p.bias = swi ? nullptr : a.b2;
+  p.scale_col = 2;
+  p.C_r = a.y_perm;
+  p.C_s = a.y_shared;
+  p.ldc = a.d;
+  p.K = static_cast<int32_t>(a.d_ff);
+  p.Nout = static_cast<int32_t>(a.d);
+  p.groups = down;
+  if (f32) {
+    err = run_f32<EPI_PLAIN>(p, max_mtiles, s);
+  } else {
+    err = fp8 ? run_bf16<128, 128, EPI_PLAIN, true>(p, max_mtiles, s)
+              : run_bf16<128, 128, EPI_PLAIN, false>(p, max_mtiles, s);
+  }
+  return err;
+}
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+struct RouteArgs {
+  int64_t T, d;
+  int32_t N, k, gating, act_dtype;
+  bool logits_given;
+  const void* x;
+  const void* w_router;
+  const float* b_router;
+  float* logits;            // [T][N]
+  int32_t* topk_idx;        // [T][k]
+  float* topk_w;            // [T][k]
+  // per-block partials (workspace), nb = ceil(T / kRouteTokens)
+  float* part_P;            // [nb][N]
+  int32_t* part_cnt;        // [nb][N]
+  float* part_lse;          // [nb][2]
+  // statistics outputs (any may be null)
+  int32_t* counts;
+  float *f, *P, *l_aux, *z_loss, *lse_mean, *lse_sq_mean;
+  float aux_alpha;
+};
+constexpr int kRouteTokens = 64;  // tokens per route workgroup
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- permute
+struct PermuteArgs {
+  int64_t T, d;
+  int32_t N, k, act_bytes;
+  int64_t capacity;          // < 0: none
+  const int32_t* topk_idx;
+  const void* x;
+  int32_t* offsets;          // [N+1]
+  int32_t* perm_token;       // [T*k]
+  int32_t* inv_map;          // [T*k]
+  void* x_perm;              // [T*k][d] (may be null: no gather)
+  int32_t* kept;             // [N] (workspace if the caller gave none)
+  int32_t* n_dropped;        // [1] (workspace if the caller gave none)
+  // workspace
+  int32_t* block_cnt;        // [nb][N]
+  int32_t* block_base;       // [nb][N]
+  int32_t* local_rank;       // [T*k]
+};
+constexpr int kPermTokens = 256;  // tokens per permute workgroup
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- grouped FFN
+// One group = one weight set applied to a contiguous block of rows.
+struct GroupDesc {
+  int32_t a_row0;   // first row in the A source (routed: x_perm / h, shared: x / h)
+  int32_t c_row0;   // first row in the output
+  int32_t rows;
+  int32_t widx;     // expert index; shared experts are n_routed + s
+};
+
+struct FfnArgs {
+  int64_t T, d, d_ff;
+  int32_t n_routed, n_shared, act, act_dtype, w_dtype;
+  int32_t routed_row_cap;     // rows reserved for routed experts in h (T*k or N*C)
+  const int32_t* offsets;     // [n_routed+1] device
+  const void* x_perm;         // routed A of the up GEMM
+  const void* x;              // shared A of the up GEMM
+  const void *w1, *w3, *w2;
+  const float *b1, *b2, *w_scale;
+  const void *sw1, *sw3, *sw2;
+  const float* sw_scale;
+  void* h;                    // [routed_row_cap + n_shared*T][d_ff] act dtype (workspace)
+  void* y_perm;               // [*][d]
+  void* y_shared;             // [n_shared][T][d]
+  GroupDesc* groups;          // [n_routed + n_shared] (workspace)
+  int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
+};
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+struct CombineArgs {
+  int64_t T, d;
+  int32_t k, n_shared, act_dtype;
+  const void* y_perm;
+  const int32_t* inv_map;
+  const float* topk_w;
+  const void* y_shared;
+  void* y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,192 @@
+// Dispatch with expert capacity: histogram -> scan -> rank/drop -> gather.
+//
+// Pages: aigrafen.se "Mixture of Experts" (the capacity equation; the `MoE`
+// module takes, per expert, the selecting tokens in `nonzero` (ascending
+// token) order and truncates the list to the capacity), vanos001 "MoE
+// Architecture" / "Capacity and Token Dropping".
+//
+// The rank of pair (t, j) with expert e is the number of tokens t' < t that
+// also selected e. It is built without any order-dependent atomics:
+//  1. rank kernel: per 256-token block, each wave ranks its 64 tokens with
+//     ballots (one pass per distinct expert in the wave), waves are combined in
+//     wave order, and the block's per-expert counts are written;
+//  2. scan kernel (one workgroup): per expert, an exclusive scan of the block
+//     counts in block order, the capacity cut, and the expert offsets;
+//  3. scatter kernel: one wave per token writes inv_map / perm_token and copies
+//     the token's row once into each of its kept slots (x read once).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxN = 256;
+constexpr int kMaxK = 8;
+
+__global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
+  __shared__ int32_t s_wcnt[4][kMaxN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N, k = a.k;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermTokens + wave * 64 + lane;
+  const bool live = t < a.T;
+
+  for (int i = tid; i < 4 * kMaxN; i += kThreads) (&s_wcnt[0][0])[i] = 0;
+
+  int ex[kMaxK], rank[kMaxK];
+  uint64_t rem[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    ex[j] = -1;
+    rank[j] = 0;
+    if (j < k && live) {
+      const int e = a.topk_idx[t * k + j];
+      ex[j] = (e >= 0 && e < N) ? e : -1;  // out-of-range ids are treated as dropped
+    }
+    rem[j] = (j < k) ? __ballot(ex[j] >= 0) : 0ull;
+  }
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (;;) {
+    int j0 = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j0 < 0 && rem[j] != 0ull) j0 = j;
+    if (j0 < 0) break;
+    uint64_t r0 = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j == j0) r0 = rem[j];
+    const int src = __builtin_ctzll(r0);
+    int v = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j == j0) v = __shfl(ex[j], src);
+    uint64_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const uint64_t bj = __ballot(ex[j] == v) & rem[j];
+      m |= bj;
+      rem[j] &= ~bj;
+    }
+    const int pos = __popcll(m & below);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (ex[j] == v) rank[j] = pos;
+    if (lane == 0) s_wcnt[wave][v] = __popcll(m);
+  }
+  __syncthreads();
+
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      int r = -1;
+      if (ex[j] >= 0) {
+        r = rank[j];
+        for (int w = 0; w < wave; ++w) r += s_wcnt[w][ex[j]];
+      }
+      a.local_rank[t * k + j] = r;  // -1: out-of-range expert id
+    }
+  }
+  const int64_t b = blockIdx.x;
+  for (int e = tid; e < N; e += kThreads)
+    a.block_cnt[b * N + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+}
+
+__global__ __launch_bounds__(kThreads) void perm_scan_kernel(PermuteArgs a, int nb) {
+  __shared__ int32_t s_kept[kMaxN];
+  __shared__ int32_t s_drop[kMaxN];
+  const int tid = threadIdx.x, N = a.N;
+  for (int e = tid; e < N; e += kThreads) {
+    int32_t run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i = static_cast<int64_t>(b) * N + e;
+      a.block_base[i] = run;
+      run += a.block_cnt[i];
+    }
+    int32_t kept = run;
+    if (a.capacity >= 0 && kept > a.capacity) kept = static_cast<int32_t>(a.capacity);
+    s_kept[e] = kept;
+    s_drop[e] = run - kept;
+    a.kept[e] = kept;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t off = 0, drop = 0;
+    for (int e = 0; e < N; ++e) {
+      a.offsets[e] = off;
+      off += s_kept[e];
+      drop += s_drop[e];
+    }
+    a.offsets[N] = off;
+    *a.n_dropped = drop;
+  }
+}
+
+// One wave per token. Copies move 16-byte chunks; x is read once per token.
+__global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= a.T) return;
+  const int N = a.N, k = a.k;
+  const int64_t blk = t / kPermTokens;
+  int64_t row[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    row[j] = -1;
+    if (j < k) {
+      const int e = a.topk_idx[t * k + j];
+      const int r = a.local_rank[t * k + j];
+      if (r >= 0 && e >= 0 && e < N) {
+        const int64_t rank = static_cast<int64_t>(a.block_base[blk * N + e]) + r;
+        if (a.capacity < 0 || rank < a.capacity) row[j] = a.offsets[e] + rank;
+      }
+      if (lane == 0) {
+        a.inv_map[t * k + j] = static_cast<int32_t>(row[j]);
+        if (row[j] >= 0) a.perm_token[row[j]] = static_cast<int32_t>(t);
+      }
+    }
+  }
+  if (!a.x_perm) return;
+  const int64_t nchunk = a.d * a.act_bytes / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(a.x_perm);
+  constexpr int U = 8;
+  for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 64 + lane;
+      if (c < nchunk) v[u] = src[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k || row[j] < 0) continue;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nchunk) dst[row[j] * nchunk + c] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.T <= 0) {
+    // no tokens: the scan over zero blocks writes the empty layout
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, 0);
+    return hipGetLastError();
+  }
+  const int nb = static_cast<int>(ceil_div(a.T, kPermTokens));
+  hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(a.T, 4))), dim3(kThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

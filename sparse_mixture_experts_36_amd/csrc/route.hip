@@ -1,0 +1,320 @@
+// Router: logits GEMM fused with softmax / top-k / gates and per-block
+// statistics partials, then a one-workgroup finalize of f, P, L_aux and z.
+//
+// Pages: aigrafen.se "Mixture of Experts" (g = softmax(W_r x); L_aux =
+// alpha N sum f_i P_i; the `MoE` module's softmax -> top-k -> renormalise),
+// vanos001 "MoE Architecture" / "Router Design" (top-k of the logits, softmax
+// over the k), learn.starphix.com "Mixture of Experts (MoE)" / "Load Balancing
+// (Critical)" (load_balancing_loss, z_loss).
+//
+// Layout on the GPU: a workgroup owns 64 consecutive tokens; each of its four
+// waves owns 16 of them. The router GEMM leaves a wave's 16 x N logits in MFMA
+// accumulator layout: quarter-wave q (lanes 16q..16q+15) holds tokens 4q+i
+// (i < 4) with lane l%16 holding experts 16*nt + l%16. Every per-token step
+// (max, sum, top-k) is then a 16-lane reduction inside one quarter, with no LDS
+// round trip. Reductions run in a fixed order, so the result is bit-for-bit
+// reproducible.
+#include <float.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRK = 64;            // k-step of the router GEMM
+constexpr int kWStride = kRK + 8;  // padded LDS row (bf16 elements): 144 B spreads the banks
+constexpr int kMaxN = 256;
+
+struct Sel {
+  float v;
+  int e;
+};
+
+// (v, e) total order: larger value first, lower expert index on exact ties.
+__device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
+  return v > v2 || (v == v2 && e < e2);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[kMaxN * kWStride];
+  __shared__ int32_t s_cnt[kMaxN];
+  __shared__ float s_P[4][kMaxN];
+  __shared__ float s_lse[4][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int N = a.N, k = a.k;
+  const int64_t T = a.T, d = a.d;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 16;
+
+  for (int e = tid; e < kMaxN; e += kThreads) s_cnt[e] = 0;
+
+  // ---- logits in accumulator layout: acc[nt][i] = l[t0 + 4q + i][16 nt + c16]
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (a.logits_given) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 4 * q + i;
+        const int e = 16 * nt + c16;
+        acc[nt][i] = (t < T && e < N) ? a.logits[t * N + e] : 0.f;
+      }
+  } else if (a.act_dtype == 1) {
+    // bf16 x and W_r on MFMA. Lane (row c16, k-group q) takes 16 consecutive k
+    // of its row per step; the weight tile for all experts sits in LDS.
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x);
+    const uint16_t* wr = static_cast<const uint16_t*>(a.w_router);
+    int64_t trow = t0 + c16;
+    if (trow > T - 1) trow = T - 1;  // rows past T compute garbage that is never stored
+    const uint16_t* xrow = xr + trow * d + q * 16;
+    for (int64_t kb = 0; kb < d; kb += kRK) {
+      __syncthreads();
+      for (int c = tid; c < NT * 16 * (kRK / 8); c += kThreads) {
+        const int e = c >> 3, kc = c & 7;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (e < N) v = *reinterpret_cast<const uint4*>(wr + e * d + kb + kc * 8);
+        *reinterpret_cast<uint4*>(&wtile[e * kWStride + kc * 8]) = v;
+      }
+      const uint4 a0 = *reinterpret_cast<const uint4*>(xrow + kb);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(xrow + kb + 8);
+      __syncthreads();
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* wp = &wtile[(16 * nt + c16) * kWStride + q * 16];
+        const uint4 b0 = *reinterpret_cast<const uint4*>(wp);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(wp + 8);
+        acc[nt] = mfma16x16x32(a0, b0, acc[nt]);
+        acc[nt] = mfma16x16x32(a1, b1, acc[nt]);
+      }
+    }
+  } else {
+    // fp32: plain dot products straight into the same layout.
+    const float* xr = static_cast<const float*>(a.x);
+    const float* wr = static_cast<const float*>(a.w_router);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = 16 * nt + c16;
+      if (e >= N) continue;
+      const float4* w4 = reinterpret_cast<const float4*>(wr + e * d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t t = t0 + 4 * q + i;
+        if (t > T - 1) t = T - 1;
+        const float4* x4 = reinterpret_cast<const float4*>(xr + t * d);
+        float s = 0.f;
+        for (int64_t j = 0; j < d / 4; ++j) {
+          const float4 u = x4[j], w = w4[j];
+          s = fmaf(u.x, w.x, s);
+          s = fmaf(u.y, w.y, s);
+          s = fmaf(u.z, w.z, s);
+          s = fmaf(u.w, w.w, s);
+        }
+        acc[nt][i] = s;
+      }
+    }
+  }
+
+  // bias, logits store
+  if (!a.logits_given) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = 16 * nt + c16;
+      const float b = (a.b_router && e < N) ? a.b_router[e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[nt][i] += b;
+        const int64_t t = t0 + 4 * q + i;
+        if (t < T && e < N) a.logits[t * N + e] = acc[nt][i];
+      }
+    }
+  }
+  __syncthreads();  // s_cnt cleared before any count below
+
+  // ---- per token: softmax, top-k, gates, statistics
+  float pacc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) pacc[nt] = 0.f;
+  float lse_s = 0.f, lse_sq = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 4 * q + i;
+    const bool live = t < T;  // uniform within the quarter
+    // selection: k rounds of a 16-lane arg-max under `better`
+    uint32_t taken = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (16 * nt + c16 >= N) taken |= 1u << nt;
+    float selv[8];
+    int sele[8];
+    for (int j = 0; j < k; ++j) {
+      Sel b{-FLT_MAX, 0x7fffffff};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = 16 * nt + c16;
+        if (!(taken >> nt & 1u) && (b.e == 0x7fffffff || better(acc[nt][i], e, b.v, b.e))) {
+          b.v = acc[nt][i];
+          b.e = e;
+        }
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(b.v, o, 16);
+        const int e2 = __shfl_xor(b.e, o, 16);
+        if (e2 != 0x7fffffff && (b.e == 0x7fffffff || better(v2, e2, b.v, b.e))) {
+          b.v = v2;
+          b.e = e2;
+        }
+      }
+      selv[j] = b.v;
+      sele[j] = b.e;
+      if ((b.e & 15) == c16) taken |= 1u << (b.e >> 4);
+    }
+    // softmax over all N: the largest logit is the first selected one
+    const float m = selv[0];
+    float s = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (16 * nt + c16 < N) s += expf(acc[nt][i] - m);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+    const float inv_s = 1.0f / s;
+    const float lse = m + logf(s);
+    if (live) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (16 * nt + c16 < N) pacc[nt] += expf(acc[nt][i] - m) * inv_s;
+      lse_s += lse;
+      lse_sq += lse * lse;
+      // gates
+      float g[8];
+      if (a.gating == 0) {
+        for (int j = 0; j < k; ++j) g[j] = expf(selv[j] - m) * inv_s;
+      } else if (a.gating == 1) {
+        float den = 0.f;
+        for (int j = 0; j < k; ++j) {
+          g[j] = expf(selv[j] - m) * inv_s;
+          den += g[j];
+        }
+        for (int j = 0; j < k; ++j) g[j] = g[j] / den;
+      } else {
+        float den = 0.f;
+        for (int j = 0; j < k; ++j) {
+          g[j] = expf(selv[j] - m);
+          den += g[j];
+        }
+        for (int j = 0; j < k; ++j) g[j] = g[j] / den;
+      }
+      for (int j = 0; j < k; ++j)
+        if (c16 == j) {
+          a.topk_idx[t * k + j] = sele[j];
+          a.topk_w[t * k + j] = g[j];
+          atomicAdd(&s_cnt[sele[j]], 1);
+        }
+    }
+  }
+
+  // ---- block partials, fixed reduction order: quarters (xor 16, 32), then waves
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float v = pacc[nt];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (q == 0) s_P[wave][16 * nt + c16] = v;
+  }
+  // lse sums live in every lane of a quarter; take lane 16q's
+  {
+    float a1 = __shfl(lse_s, 0) + __shfl(lse_s, 16) + __shfl(lse_s, 32) + __shfl(lse_s, 48);
+    float a2 = __shfl(lse_sq, 0) + __shfl(lse_sq, 16) + __shfl(lse_sq, 32) + __shfl(lse_sq, 48);
+    if (lane == 0) {
+      s_lse[wave][0] = a1;
+      s_lse[wave][1] = a2;
+    }
+  }
+  __syncthreads();
+  const int b = blockIdx.x;
+  for (int e = tid; e < N; e += kThreads) {
+    a.part_P[static_cast<int64_t>(b) * N + e] = ((s_P[0][e] + s_P[1][e]) + s_P[2][e]) + s_P[3][e];
+    a.part_cnt[static_cast<int64_t>(b) * N + e] = s_cnt[e];
+  }
+  if (tid == 0) {
+    a.part_lse[2 * b] = ((s_lse[0][0] + s_lse[1][0]) + s_lse[2][0]) + s_lse[3][0];
+    a.part_lse[2 * b + 1] = ((s_lse[0][1] + s_lse[1][1]) + s_lse[2][1]) + s_lse[3][1];
+  }
+}
+
+// One workgroup: sums the block partials in block order (fp64) and writes
+// counts, f = counts/(T k), P = sum/T, L_aux = alpha N sum f P, z = mean(lse)^2.
+__global__ __launch_bounds__(kThreads) void route_finalize_kernel(RouteArgs a, int nb) {
+  __shared__ double s_fp[kMaxN];
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const double T = static_cast<double>(a.T);
+  for (int e = tid; e < kMaxN; e += kThreads) s_fp[e] = 0.0;
+  __syncthreads();
+  for (int e = tid; e < N; e += kThreads) {
+    double p = 0.0;
+    int64_t c = 0;
+    for (int b = 0; b < nb; ++b) {
+      p += static_cast<double>(a.part_P[static_cast<int64_t>(b) * N + e]);
+      c += a.part_cnt[static_cast<int64_t>(b) * N + e];
+    }
+    const double P = p / T;
+    const double f = static_cast<double>(c) / (T * a.k);
+    if (a.counts) a.counts[e] = static_cast<int32_t>(c);
+    if (a.f) a.f[e] = static_cast<float>(f);
+    if (a.P) a.P[e] = static_cast<float>(P);
+    s_fp[e] = f * P;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double dot = 0.0, ls = 0.0, lq = 0.0;
+    for (int e = 0; e < N; ++e) dot += s_fp[e];
+    for (int b = 0; b < nb; ++b) {
+      ls += static_cast<double>(a.part_lse[2 * b]);
+      lq += static_cast<double>(a.part_lse[2 * b + 1]);
+    }
+    const double lm = ls / T;
+    if (a.l_aux) *a.l_aux = static_cast<float>(static_cast<double>(a.aux_alpha) * N * dot);
+    if (a.z_loss) *a.z_loss = static_cast<float>(lm * lm);
+    if (a.lse_mean) *a.lse_mean = static_cast<float>(lm);
+    if (a.lse_sq_mean) *a.lse_sq_mean = static_cast<float>(lq / T);
+  }
+}
+
+template <int NT>
+hipError_t launch_nt(const RouteArgs& a, int nb, hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int nb = static_cast<int>(ceil_div(a.T, kRouteTokens));
+  const int nt = static_cast<int>(ceil_div(a.N, 16));
+  hipError_t err;
+  switch (nt) {
+#define MOE_ROUTE_CASE(n) \
+  case n: err = launch_nt<n>(a, nb, s); break;
+    MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6) MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8)
+    MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11) MOE_ROUTE_CASE(12)
+    MOE_ROUTE_CASE(13) MOE_ROUTE_CASE(14) MOE_ROUTE_CASE(15) MOE_ROUTE_CASE(16)
+#undef MOE_ROUTE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  return hipGetLastError();
+}
+
+}  // namespace moe

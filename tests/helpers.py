@@ -1,0 +1,63 @@
+"""Host <-> device marshalling and comparison helpers for the GPU tests."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import gen
+import sparse_mixture_experts_36_amd as moe
+
+
+def say(*a):
+    """Progress line that reaches the log even if the process dies next."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray | None, bf16: bool = False):
+    """numpy -> cuda tensor. uint16 arrays are bf16 bit patterns."""
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t) -> np.ndarray:
+    """cuda tensor -> numpy (bf16 comes back as uint16 bits)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return gen.bf16_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def shape_of(wl, T=None, capacity=None) -> moe.Shape:
+    return moe.make_shape(T=wl.T if T is None else T, d=wl.d, d_ff=wl.d_ff, n_experts=wl.n_experts,
+                          top_k=wl.top_k, act=wl.act, gating=wl.gating, act_dtype=wl.act_dtype,
+                          w_dtype=wl.w_dtype, capacity=wl.capacity() if capacity is None else capacity,
+                          n_shared=wl.n_shared, aux_alpha=wl.aux_alpha)
+
+
+def device_weights(inp) -> dict:
+    names = ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2", "sw_scale")
+    return {n: dev(getattr(inp, n)) for n in names}
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref|"""
+    den = float(np.abs(ref).max())
+    return float(np.abs(got - ref).max()) / (den if den > 0 else 1.0)
+
+
+def tol_for(wl) -> float:
+    return 1e-4 if wl.act_dtype == gen.F32 and wl.w_dtype == gen.F32 else 2e-2

@@ -1,0 +1,175 @@
+"""End-to-end moe_forward against the CPU oracle, for every workload: reduced
+sizes (every token compared) and the full sizes in the launch configuration the
+benchmark times (sampled tokens, which the oracle computes one by one).
+
+Routing: the GPU's fp32 logits are compared with the oracle's fp64 logits;
+tokens whose top-k margin exceeds the logit error must route identically
+(bit-exact). Tokens closer to a tie are reported, must still pick a valid top-k
+set, and are left out of the output comparison together with every token whose
+capacity slot they could have moved. The router_grid inputs make every logit an
+exact fp32 number, so there the whole routing, permutation and drop set must
+match bit for bit."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import sparse_mixture_experts_36_amd as moe
+from helpers import as_f64, dev, device_weights, host, rel_err, say, shape_of, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_check(inp, sample=None, exact_routing=False, label=""):
+    import torch
+    wl = inp.wl
+    say(f"forward {label or wl.name}: T={wl.T} d={wl.d} d_ff={wl.d_ff} N={wl.n_experts} k={wl.top_k} "
+        f"C={wl.capacity()} shared={wl.n_shared} w_dtype={wl.w_dtype}")
+    layer = moe.MoELayer(shape_of(wl), device_weights(inp))
+    out = layer(dev(inp.x))
+    torch.cuda.synchronize()
+    so = oracle.shape_of(wl)
+    l64, l32 = oracle.router_logits(so, inp.x, inp)
+    r = oracle.route(so, l32)
+    dsp = oracle.dispatch(so, r.topk_idx)
+    lg = host(out.logits)
+    gi = host(out.topk_idx)
+    err = float(np.abs(lg.astype(np.float64) - l64).max())
+    lmax = float(np.abs(l64).max())
+    assert err <= 1e-5 * lmax, f"logit error {err} vs max {lmax}"
+    if exact_routing:
+        assert np.array_equal(lg, l32)
+        diff = np.zeros(wl.T, bool)
+    else:
+        thr = 4 * err + 1e-6 * lmax
+        amb = ~((r.margin_set > thr) & (r.margin_order > thr))
+        assert np.array_equal(gi[~amb], r.topk_idx[~amb])
+        for t in np.nonzero(amb)[0]:
+            kth = np.sort(l64[t])[::-1][wl.top_k - 1]
+            assert (l64[t, gi[t]] >= kth - thr).all()
+        diff = (gi != r.topk_idx).any(1)
+        say(f"  logit err {err:.2e}; near-tie tokens {int(amb.sum())}; routed differently {int(diff.sum())}")
+    assert np.allclose(host(out.topk_w)[~diff], r.topk_w[~diff], rtol=1e-4, atol=1e-6)
+
+    # tokens whose result the comparison can trust
+    ok = ~diff
+    if diff.any() and wl.capacity() >= 0:
+        t0 = int(np.nonzero(diff)[0].min())
+        moved = set(gi[diff].ravel()) | set(r.topk_idx[diff].ravel())
+        for t in range(t0, wl.T):
+            if set(r.topk_idx[t]) & moved:
+                ok[t] = False
+    if not diff.any():
+        assert np.array_equal(host(out.inv_map), dsp.inv_map)
+        assert np.array_equal(host(out.expert_offsets), dsp.offsets)
+        M = int(dsp.offsets[-1])
+        assert np.array_equal(host(out.perm_token)[:M], dsp.perm_token[:M])
+        st = {k: host(v) for k, v in out.stats.items()}
+        assert np.array_equal(st["counts"].astype(np.int64), r.counts)
+        assert np.array_equal(st["kept"], dsp.kept) and int(st["n_dropped"][0]) == dsp.n_dropped
+        assert np.allclose(st["P"], r.P, rtol=1e-4, atol=1e-7)
+        assert abs(float(st["l_aux"][0]) - r.l_aux) <= 1e-4 * abs(r.l_aux)
+        assert abs(float(st["z_loss"][0]) - r.z) <= 1e-4 * abs(r.z) + 1e-6
+        say(f"  rows {M}, dropped {dsp.n_dropped}, L_aux {float(st['l_aux'][0]):.6f}, z {float(st['z_loss'][0]):.4f}")
+
+    tokens = np.arange(wl.T) if sample is None else np.asarray(sample)
+    tokens = tokens[ok[tokens]]
+    assert len(tokens) > 0
+    y_ref = oracle.moe_output(so, inp.x, inp, r, dsp, tokens)
+    y_gpu = as_f64(host(out.y))[tokens]
+    e = rel_err(y_gpu, y_ref)
+    tol = tol_for(wl)
+    say(f"  compared {len(tokens)} tokens: max|d|/max|ref| = {e:.3e} (tol {tol})")
+    assert e <= tol
+    return out
+
+
+def _sample(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    s = set([0, T - 1]) | set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    return np.array(sorted(s)[:max(n, 2)], np.int64)
+
+
+# ---------------------------------------------------------------- reduced sizes, every token
+
+REDUCED = {
+    "tiny-gelu-fp32": gen.TINY_GELU,
+    "tiny-gelu-fp32-tight-capacity": gen.TINY_GELU.with_(capacity_factor=0.5),
+    "mixtral-like": gen.MIXTRAL_PREFILL.with_(T=512, d=1024, d_ff=1536),
+    "mixtral-like-renorm": gen.MIXTRAL_PREFILL.with_(T=300, d=512, d_ff=768, gating=gen.SOFTMAX_TOPK_RENORM),
+    "fine-grained-like": gen.FINE_GRAINED.with_(T=512, d=512, d_ff=256),
+    "switch-like": gen.SWITCH_TOP1.with_(T=2048, d=512, d_ff=1024),
+    "switch-like-fp8": gen.SWITCH_TOP1_FP8.with_(T=2048, d=512, d_ff=1024),
+    "switch-like-renorm": gen.SWITCH_TOP1.with_(T=1024, d=256, d_ff=512, gating=gen.SOFTMAX_TOPK_RENORM),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_forward_reduced(name):
+    run_and_check(gen.make_inputs(REDUCED[name]), label=name)
+
+
+def test_forward_capacity_zero_gives_shared_only():
+    wl = gen.FINE_GRAINED.with_(T=128, d=256, d_ff=256, capacity_factor=0.0)
+    run_and_check(gen.make_inputs(wl), label="capacity 0")
+
+
+def test_forward_is_deterministic():
+    import torch
+    wl = gen.SWITCH_TOP1.with_(T=4096, d=512, d_ff=1024)
+    inp = gen.make_inputs(wl)
+    layer = moe.MoELayer(shape_of(wl), device_weights(inp))
+    x = dev(inp.x)
+    a = layer(x)
+    ya, la = a.y.clone(), a.logits.clone()
+    sa = {k: v.clone() for k, v in a.stats.items()}
+    b = layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), b.y.view(torch.int16))
+    assert torch.equal(la, b.logits)
+    for k in sa:
+        assert torch.equal(sa[k], b.stats[k]), k
+
+
+# ---------------------------------------------------------------- full sizes, sampled tokens
+
+def test_full_tiny_gelu_fp32():
+    run_and_check(gen.make_inputs(gen.TINY_GELU), label="tiny-gelu-fp32 (full)")
+
+
+def test_full_mixtral_prefill():
+    inp = gen.make_inputs(gen.MIXTRAL_PREFILL)
+    run_and_check(inp, sample=_sample(4096, 12), label="mixtral-prefill (full)")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_full_mixtral_decode(T):
+    inp = gen.make_inputs(gen.MIXTRAL_DECODE[T])
+    run_and_check(inp, sample=None if T <= 16 else _sample(T, 12), label=f"mixtral-decode T={T}")
+
+
+def test_full_fine_grained():
+    inp = gen.make_inputs(gen.FINE_GRAINED)
+    run_and_check(inp, sample=_sample(8192, 6), label="fine-grained (full)")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_full_switch(fp8):
+    wl = gen.SWITCH_TOP1_FP8 if fp8 else gen.SWITCH_TOP1
+    run_and_check(gen.make_inputs(wl), sample=_sample(16384, 48), label=wl.name + " (full)")
+
+
+def test_full_switch_exact_routing_grid():
+    """Every logit exact in fp32: routing, the 16384-token permutation, the drop
+    set and the counts must match the oracle bit for bit."""
+    inp = gen.make_inputs(gen.SWITCH_TOP1, router_grid=True)
+    run_and_check(inp, sample=_sample(16384, 32), exact_routing=True, label="switch exact-grid (full)")
