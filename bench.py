@@ -1,0 +1,255 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one moe_forward (router GEMM + softmax/top-k/gates + statistics,
+permutation with capacity, grouped up GEMM with the fused activation, grouped
+down GEMM, combine) over one batch of seeded synthetic input that is already
+resident in HBM when the timed region starts. Prints ONE JSON line.
+
+Default workload: the Mixtral-shape prefill layer (T=4096, d=4096,
+d_ff=14336, 8 experts, top-2, top-k-then-softmax, dropless, bf16 with fp32
+accumulation). `value` is layer tokens/s. `roofline` describes the dominant
+kernel (the grouped up GEMM with the fused SwiGLU): algorithmic flops per
+launch = 4 * d * d_ff per kept (token, expert) pair, divided by that kernel's
+mean launch time, measured with hipEvents on the stream it runs on over the
+timed region. `decode` reports the Mixtral-shape decode layer (T = 1, 16, 64)
+in HBM GB/s of algorithmic bytes (every touched expert's three matrices once,
+the router weight, x and y). `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def shape_for(wl):
+    import sparse_mixture_experts_36_amd as moe
+    return moe.make_shape(wl.T, wl.d, wl.d_ff, wl.n_experts, wl.top_k, wl.act, wl.gating, wl.act_dtype,
+                          wl.w_dtype, wl.capacity(), wl.n_shared, wl.aux_alpha)
+
+
+def weight_bytes_per_expert(wl) -> int:
+    import gen
+    import sparse_mixture_experts_36_amd as moe
+    wb = {gen.F32: 4, gen.BF16: 2, gen.E4M3: 1}[wl.w_dtype]
+    return moe.expert_params(wl.d, wl.d_ff, wl.act) * wb
+
+
+def up_flops_per_pair(wl) -> float:
+    """Up GEMM: d x d_ff per matrix, two matrices (W1, W3) for SwiGLU."""
+    return 2.0 * wl.d * wl.d_ff * (2 if wl.act == 1 else 1)
+
+
+def ffn_flops_per_pair(wl) -> float:
+    return up_flops_per_pair(wl) + 2.0 * wl.d * wl.d_ff
+
+
+def run_gpu(wl, inp, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_36_amd as moe
+
+    names = ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2", "sw_scale")
+    tensors = {n: to_dev(getattr(inp, n)) for n in names}
+    layer = moe.MoELayer(shape_for(wl), tensors)
+    x = to_dev(inp.x)
+    for _ in range(warmup):
+        layer(x)
+    torch.cuda.synchronize()
+    moe.timing_start(8 * steps + 8)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer(x)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = moe.timing_stop()
+    latest = layer.latest()
+    kept = int(sum(latest["kept"]))
+    shared_rows = wl.n_shared * wl.T
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "stages": stages, "latest": latest, "kept": kept,
+            "rows": kept + shared_rows, "layer": layer, "tensors": tensors}
+
+
+def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
+    """Decode shapes on the prefill weights. Each timed step takes a different
+    slice of the prefill tokens, so consecutive steps touch different experts'
+    weights where routing allows; the bytes of each step are counted from its
+    own routing (read once before the timed loop)."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_36_amd as moe
+
+    out = {}
+    per_expert = weight_bytes_per_expert(wl_prefill)
+    x_all = to_dev(inp.x)
+    names = ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale")
+    tensors = {n: to_dev(getattr(inp, n)) for n in names}
+    for T in Ts:
+        wl = wl_prefill.with_(T=T)
+        layer = moe.MoELayer(shape_for(wl), tensors)
+        nslices = min(steps, wl_prefill.T // T)
+        xs = [x_all[i * T:(i + 1) * T].contiguous() for i in range(nslices)]
+        touched = []
+        for xi in xs:
+            o = layer(xi)
+            touched.append(len(set(o.topk_idx.cpu().numpy().ravel().tolist())))
+        act_b = 2
+        fixed = wl.n_experts * wl.d * act_b + 2 * T * wl.d * act_b  # router weight, x, y
+        for _ in range(warmup):
+            layer(xs[0])
+        torch.cuda.synchronize()
+        moe.timing_start(8 * nslices + 8)
+        t0 = time.perf_counter()
+        for xi in xs:
+            layer(xi)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st = moe.timing_stop()
+        us = (t1 - t0) * 1e6 / nslices
+        nbytes = sum(n * per_expert + fixed for n in touched) / nslices
+        ffn_us = (st["ffn_up"][0] + st["ffn_down"][0]) * 1e3 / max(st["ffn_up"][1], 1)
+        out[f"T{T}"] = {"us_per_step": round(us, 2), "touched_experts": round(sum(touched) / nslices, 2),
+                        "GB": round(nbytes / 1e9, 4), "GB_per_s": round(nbytes / us / 1e3, 1),
+                        "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                        "ffn_us": round(ffn_us, 2),
+                        "ffn_GB_per_s": round((nbytes - fixed) / ffn_us / 1e3, 1),
+                        "steps": nslices}
+        log(f"decode T={T}: {out[f'T{T}']}")
+    return out
+
+
+def cpu_baseline(wl, inp, target_s=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample: the first S tokens as
+    their own batch (S grown from 8 until one run takes a few seconds, then the
+    sample is fixed so the timed run lasts about target_s)."""
+    import numpy as np
+
+    import gen
+    import oracle
+
+    def run(S):
+        sub = gen.Inputs(wl.with_(T=S), inp.x[:S], inp.w_router, inp.b_router, inp.w1, inp.w3, inp.w2, inp.b1,
+                         inp.b2, inp.w_scale, inp.sw1, inp.sw3, inp.sw2, inp.sw_scale)
+        t = time.perf_counter()
+        oracle.forward(sub)
+        return time.perf_counter() - t
+
+    run(4)  # first touch of the weight pages and the oracle library load
+    S, dt = 8, run(8)
+    while dt < 2.0 and S < wl.T:
+        S = min(wl.T, S * 4)
+        dt = run(S)
+    S2 = int(min(wl.T, max(S, S * target_s / max(dt, 1e-3))))
+    if S2 != S:
+        S, dt = S2, run(S2)
+    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {S} tokens of the {wl.name} input as one batch (all {wl.n_experts} experts' "
+                      f"weights), fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral-prefill-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import gen
+    import sparse_mixture_experts_36_amd as moe
+
+    moe.lib()  # raises when the HIP library is missing: there is no fallback
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = gen.WORKLOADS[args.workload]
+    log(f"workload {wl}")
+    t = time.perf_counter()
+    inp = gen.make_inputs(wl)
+    log(f"inputs generated in {time.perf_counter() - t:.1f} s")
+
+    r = run_gpu(wl, inp, args.steps, args.warmup)
+    ms = r["ms_per_step"]
+    st = r["stages"]
+    log(f"ms/step {ms:.3f}; stages " + ", ".join(f"{k} {v[0] / max(v[1], 1):.3f} ms" for k, v in st.items()))
+    up_ms = st["ffn_up"][0] / max(st["ffn_up"][1], 1)
+    down_ms = st["ffn_down"][0] / max(st["ffn_down"][1], 1)
+    up_flops = r["rows"] * up_flops_per_pair(wl)
+    ffn_flops = r["rows"] * ffn_flops_per_pair(wl)
+    router_flops = 2.0 * wl.T * wl.d * wl.n_experts
+    bf16 = wl.act_dtype == gen.BF16
+    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    result = {
+        "metric": "MoE-layer tokens/s (Mixtral-shape prefill) + % bf16 MFMA peak; decode HBM GB/s",
+        "value": round(wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "d_ff": wl.d_ff, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "act": "swiglu" if wl.act == gen.SWIGLU else "gelu",
+                   "gating": ["softmax_topk", "softmax_topk_renorm", "topk_softmax"][wl.gating],
+                   "capacity": wl.capacity(), "n_shared": wl.n_shared,
+                   "w_dtype": {0: "f32", 1: "bf16", 2: "e4m3"}[wl.w_dtype], "parallelism": "single-gpu"},
+        "roofline": {"kernel": "grouped up GEMM + fused activation", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4)},
+        "layer": {"mfma_frac": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "ffn_mfma_frac": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in st.items()},
+                  "rows": r["rows"], "dropped": int(r["latest"]["dropped_share"] * wl.T * wl.top_k + 0.5),
+                  "l_aux": round(r["latest"]["aux_loss"], 6), "z_loss": round(r["latest"]["z_loss"], 5)},
+    }
+    if not args.no_decode and wl.name == "mixtral-prefill-bf16":
+        del r
+        result["decode"] = run_decode(wl, inp, max(args.steps, 16), args.warmup)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -232,6 +232,31 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
                        int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
                        const moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Stage timing, for profiling. Between moe_timing_start and moe_timing_stop
+ * every entry point records a pair of hipEvents on its stream around each
+ * stage below (ROUTE: router kernel + statistics finalize; PERMUTE: rank, scan
+ * and scatter kernels; FFN_PLAN: the tile-plan kernel; FFN_UP / FFN_DOWN: the
+ * up and down grouped GEMM kernels, one launch each; COMBINE: the combine
+ * kernel). The events are host-side HIP objects created on the first start
+ * (2 * max_launches of them) and kept until the process ends; no device memory
+ * is allocated. moe_timing_stop waits for the recorded events and returns the
+ * summed milliseconds and the number of recorded launches per stage; records
+ * beyond max_launches are not taken. Process-wide state, serialised by a lock.
+ */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_PERMUTE = 1,
+  MOE_STAGE_FFN_PLAN = 2,
+  MOE_STAGE_FFN_UP = 3,
+  MOE_STAGE_FFN_DOWN = 4,
+  MOE_STAGE_COMBINE = 5,
+  MOE_N_STAGES = 6
+} moe_stage;
+
+moe_status moe_timing_start(int32_t max_launches);
+moe_status moe_timing_stop(double* total_ms /* [MOE_N_STAGES] */, int32_t* launches /* [MOE_N_STAGES] */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,7 +64,7 @@ def lib():
         L.orc_moe_output.argtypes = [sp, vp, wp, vp, vp, vp, vp, i64, vp]
         L.orc_combine.argtypes = [sp, vp, vp, vp, vp, vp]
         for name in ("orc_router_logits", "orc_route", "orc_dispatch", "orc_expert_rows",
-                     "orc_moe_output", "orc_combine", "orc_abi_version"):
+                     "orc_moe_output", "orc_combine", "orc_abi_version", "orc_threads"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("orc_bf16_value", "orc_gelu", "orc_silu"):
             getattr(L, name).restype = ctypes.c_double
@@ -223,6 +223,11 @@ def forward(inp, tokens: np.ndarray | None = None, logits32: np.ndarray | None =
         tokens = np.arange(wl.T, dtype=np.int64)
     y = moe_output(shape, inp.x, inp, r, dsp, tokens)
     return Forward(l64, l32, r, dsp, np.asarray(tokens, np.int64), y)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return lib().orc_threads()
 
 
 def bf16_value(b: int) -> float:

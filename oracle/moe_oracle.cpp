@@ -49,6 +49,8 @@
 #include <limits>
 #include <vector>
 
+#include <omp.h>
+
 extern "C" {
 
 struct OrcShape {
@@ -183,6 +185,17 @@ void expert_rows(const OrcShape* s, const OrcWeights* w, bool shared, int e, con
 extern "C" {
 
 int orc_abi_version(void) { return 1; }
+
+// Threads the oracle's parallel loops use (OpenMP default team size).
+int orc_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}
 
 // Router logits [AIG, g = softmax(W_r x); SPX "Key Equations", router_logits =
 // x W_router^T; WIKI `MoELayer`/`CapacityMoE` use a biased gate]:

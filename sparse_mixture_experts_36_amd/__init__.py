@@ -80,8 +80,10 @@ def lib():
         L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [sp, vp, wp, vp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
+        L.moe_timing_start.argtypes = [ctypes.c_int32]
+        L.moe_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         for f in ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                  "moe_forward"):
+                  "moe_forward", "moe_timing_start", "moe_timing_stop"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,6 +185,22 @@ def forward(shape, x, weights: Weights, y, logits=None, topk_idx=None, topk_w=No
                            _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_token), _ptr(inv_map),
                            ctypes.byref(st) if st else None, _ptr(ws_), ws_.numel(), _stream(stream))
     _check(rc, "moe_forward")
+
+
+STAGES = ("route", "permute", "ffn_plan", "ffn_up", "ffn_down", "combine")
+
+
+def timing_start(max_launches: int = 4096):
+    """Start per-stage hipEvent timing (moe_timing_start)."""
+    _check(lib().moe_timing_start(max_launches), "moe_timing_start")
+
+
+def timing_stop() -> dict:
+    """Stop stage timing; {stage: (total_ms, launches)} (waits for the events)."""
+    ms = (ctypes.c_double * len(STAGES))()
+    n = (ctypes.c_int32 * len(STAGES))()
+    _check(lib().moe_timing_stop(ms, n), "moe_timing_stop")
+    return {s: (ms[i], n[i]) for i, s in enumerate(STAGES)}
 
 
 def weights_struct(t: dict) -> Weights:

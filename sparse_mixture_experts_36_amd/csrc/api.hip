@@ -4,6 +4,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "../../include/moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -263,9 +267,87 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* off
   return a;
 }
 
+// ---------------------------------------------------------------- stage timing
+struct Timing {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> ev;  // pairs: 2i start, 2i+1 end
+  std::vector<int> stage_of;
+  int cap = 0, used = 0;
+  int open[moe::kNumStages];
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
 }  // namespace
 
+namespace moe {
+void stage_mark(int stage, bool end, hipStream_t s) {
+  Timing& t = timing();
+  if (!t.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  if (!end) {
+    if (t.used >= t.cap) {
+      t.open[stage] = -1;
+      return;
+    }
+    const int i = t.used++;
+    t.stage_of[i] = stage;
+    t.open[stage] = i;
+    (void)hipEventRecord(t.ev[2 * i], s);
+  } else {
+    const int i = t.open[stage];
+    if (i < 0) return;
+    t.open[stage] = -1;
+    (void)hipEventRecord(t.ev[2 * i + 1], s);
+  }
+}
+}  // namespace moe
+
 extern "C" {
+
+moe_status moe_timing_start(int32_t max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  while (static_cast<int>(t.ev.size()) < 2 * max_launches) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_status(err);
+    t.ev.push_back(e);
+  }
+  t.stage_of.assign(max_launches, 0);
+  t.cap = max_launches;
+  t.used = 0;
+  for (int& o : t.open) o = -1;
+  t.on = true;
+  return MOE_OK;
+}
+
+moe_status moe_timing_stop(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return MOE_ERR_INVALID_ARG;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.on = false;
+  for (int s = 0; s < moe::kNumStages; ++s) {
+    total_ms[s] = 0.0;
+    launches[s] = 0;
+  }
+  for (int i = 0; i < t.used; ++i) {
+    hipError_t err = hipEventSynchronize(t.ev[2 * i + 1]);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+    if (err != hipSuccess) return hip_status(err);
+    total_ms[t.stage_of[i]] += ms;
+    launches[t.stage_of[i]] += 1;
+  }
+  t.used = 0;
+  return MOE_OK;
+}
+
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 

@@ -76,10 +76,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  stage_mark(kStageCombine, false, s);
   if (a.act_dtype == 1)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+  stage_mark(kStageCombine, true, s);
   return hipGetLastError();
 }
 

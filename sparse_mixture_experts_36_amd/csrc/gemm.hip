@@ -411,8 +411,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   const int bm = f32 ? 64 : 128;
   GroupDesc* up = a.groups;
   GroupDesc* down = a.groups + G;
+  stage_mark(kStageFfnPlan, false, s);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a.offsets, a.n_routed, a.n_shared,
                      static_cast<int32_t>(a.T), a.routed_row_cap, bm, up, down, a.tile_start);
+  stage_mark(kStageFfnPlan, true, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // upper bound on row tiles: every group may end in a partial tile
@@ -443,6 +445,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   p.K = static_cast<int32_t>(a.d);
   p.Nout = static_cast<int32_t>(a.d_ff);
   p.groups = up;
+  stage_mark(kStageFfnUp, false, s);
   if (f32) {
     err = swi ? run_f32<EPI_SWIGLU>(p, max_mtiles, s) : run_f32<EPI_GELU>(p, max_mtiles, s);
   } else if (swi) {
@@ -452,6 +455,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
     err = fp8 ? run_bf16<128, 128, EPI_GELU, true>(p, max_mtiles, s)
               : run_bf16<128, 128, EPI_GELU, false>(p, max_mtiles, s);
   }
+  stage_mark(kStageFfnUp, true, s);
   if (err != hipSuccess) return err;
 
   // down GEMM: h [rows][d_ff] x [d][d_ff]^T -> y [rows][d]
@@ -471,12 +475,14 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   p.K = static_cast<int32_t>(a.d_ff);
   p.Nout = static_cast<int32_t>(a.d);
   p.groups = down;
+  stage_mark(kStageFfnDown, false, s);
   if (f32) {
     err = run_f32<EPI_PLAIN>(p, max_mtiles, s);
   } else {
     err = fp8 ? run_bf16<128, 128, EPI_PLAIN, true>(p, max_mtiles, s)
               : run_bf16<128, 128, EPI_PLAIN, false>(p, max_mtiles, s);
   }
+  stage_mark(kStageFfnDown, true, s);
   return err;
 }
 

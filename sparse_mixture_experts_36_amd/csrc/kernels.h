@@ -6,6 +6,11 @@
 
 namespace moe {
 
+// Stage timing hook (moe_timing_start / moe_timing_stop): records a hipEvent
+// on `s` at the start (end = false) or end of a stage; no-op when disabled.
+enum Stage { kStageRoute = 0, kStagePermute, kStageFfnPlan, kStageFfnUp, kStageFfnDown, kStageCombine, kNumStages };
+void stage_mark(int stage, bool end, hipStream_t s);
+
 // ---------------------------------------------------------------- router
 struct RouteArgs {
   int64_t T, d;

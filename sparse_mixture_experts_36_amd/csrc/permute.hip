@@ -182,10 +182,12 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int nb = static_cast<int>(ceil_div(a.T, kPermTokens));
+  stage_mark(kStagePermute, false, s);
   hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(a.T, 4))), dim3(kThreads), 0, s,
                      a);
+  stage_mark(kStagePermute, true, s);
   return hipGetLastError();
 }
 

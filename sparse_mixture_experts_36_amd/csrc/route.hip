@@ -302,6 +302,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nb = static_cast<int>(ceil_div(a.T, kRouteTokens));
   const int nt = static_cast<int>(ceil_div(a.N, 16));
   hipError_t err;
+  stage_mark(kStageRoute, false, s);
   switch (nt) {
 #define MOE_ROUTE_CASE(n) \
   case n: err = launch_nt<n>(a, nb, s); break;
@@ -314,6 +315,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  stage_mark(kStageRoute, true, s);
   return hipGetLastError();
 }
 
