@@ -29,6 +29,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
+// k-steps of global loads in flight in the bf16 GEMM (1 or 2)
+#ifndef MOE_GEMM_PF
+#define MOE_GEMM_PF 1
+#endif
+
 struct GemmParams {
   const void* A_r;        // routed A rows
   const void* A_s;        // shared A rows
@@ -92,30 +97,43 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
 }
 
 // ------------------------------------------------------------------ bf16 MFMA
-// 4 waves as 2 x 2; a wave owns BM/2 rows and BNO/2 output columns (for SwiGLU
-// the matching W1 and W3 columns, so silu(a) * b is formed in registers).
-template <int BM, int BNO, int EPI, bool FP8>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
+// WGM x WGN waves; a wave owns BM/WGM rows and BNB/WGN weight rows of the tile
+// (for SwiGLU the matching halves of W1 and W3, so silu(a) * b is formed in
+// registers). Weight tile rows: [0, BNO) from W1 (or W), [BNO, 2 BNO) from W3.
+// Main loop: k-steps of 64 through two LDS buffers; the next step's global
+// loads are in flight while the current one computes. LDS rows are 128 B (8
+// chunks of 16 B) stored with chunk c of row r at position c ^ (r & 7): the 16
+// rows of an MFMA operand read then hit distinct banks, so ds_read_b128 runs at
+// the full 256 B/clk of a gfx950 CU (a 16-byte row pad only reaches half of
+// it). The epilogue stages the bf16 output tile through LDS for 16-byte stores.
+template <int BM, int BNB, int WGM, int WGN, int EPI, bool FP8, int PF>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NTH = 64 * WGM * WGN;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int BNB = SWI ? 2 * BNO : BNO;  // weight rows per tile
+  constexpr int BNO = SWI ? BNB / 2 : BNB;   // output columns per tile
   constexpr int BK = 64;
-  constexpr int S = BK + 8;                 // padded LDS row (bf16 elements)
-  constexpr int WM = BM / 2, WNO = BNO / 2;
-  constexpr int FM = WM / 16;
-  constexpr int FNO = WNO / 16;
-  constexpr int FN = SWI ? 2 * FNO : FNO;
-  constexpr int A_CH = BM * (BK / 8) / kThreads;   // 16-byte chunks per thread
-  constexpr int B_CH = FP8 ? BNB * (BK / 16) / kThreads : BNB * (BK / 8) / kThreads;
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for 256 threads");
+  constexpr int S = BK;                      // LDS row (bf16 elements), swizzled chunks
+  constexpr int WTM = BM / WGM;              // rows per wave
+  constexpr int WTB = BNB / WGN;             // weight rows per wave
+  constexpr int WTO = SWI ? WTB / 2 : WTB;   // output columns per wave
+  constexpr int FM = WTM / 16;
+  constexpr int FN = WTB / 16;
+  constexpr int FNO = WTO / 16;
+  constexpr int A_CH = BM * (BK / 8) / NTH;  // 16-byte chunks per thread
+  constexpr int CPR = FP8 ? BK / 16 : BK / 8;  // weight chunks per row
+  constexpr int B_CH = BNB * CPR / NTH;
+  constexpr int STAGE = (BM + BNB) * S;      // elements per LDS buffer
+  constexpr int SO = BNO + 8;                // output staging row (elements)
+  static_assert(A_CH >= 1 && B_CH >= 1 && BM * (BK / 8) % NTH == 0 && BNB * CPR % NTH == 0, "tile/threads");
+  constexpr int SMEM = (2 * STAGE > BM * SO) ? 2 * STAGE : BM * SO;  // operands, then the output tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * S];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNB * S];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
   TileInfo ti;
   if (!decode_tile<BM, BNO>(p, ti)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
   const bool shared = ti.g >= p.n_routed;
   const int widx = ti.gd.widx;
@@ -125,38 +143,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 
   const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
                       (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
-  const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r);
-  const char* B3w = static_cast<const char*>(shared ? p.B3_s : p.B3_r);
   constexpr int WB = FP8 ? 1 : 2;  // weight bytes
-  const int64_t eoff = static_cast<int64_t>(ew) * p.b_stride * WB;
+  const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride * WB;
+  const char* B3w = SWI ? static_cast<const char*>(shared ? p.B3_s : p.B3_r) +
+                              static_cast<int64_t>(ew) * p.b_stride * WB
+                        : Bw;
 
-  // per-thread global chunk sources
-  const uint16_t* a_src[A_CH];
+  // per-thread chunk offsets (elements from A / bytes from the weight bases)
+  uint32_t a_off[A_CH];
   int a_dst[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * kThreads;
+    const int c = tid + i * NTH;
     int r = c >> 3;
     const int kc = c & 7;
-    a_dst[i] = r * S + kc * 8;
+    a_dst[i] = r * S + ((kc ^ (r & 7)) * 8);
     if (r > ti.rows - 1) r = ti.rows - 1;  // rows past the group compute garbage, never stored
-    a_src[i] = A + static_cast<int64_t>(r) * p.lda + kc * 8;
+    a_off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.lda) + kc * 8;
   }
-  const char* b_src[B_CH];
+  // For SwiGLU the W3 rows are [BNO, 2 BNO). When that split falls on a chunk
+  // boundary of every thread (chunks i >= B_CH / 2), the base choice is static.
+  constexpr bool SPLIT = (B_CH % 2 == 0 && BNO * CPR == NTH * (B_CH / 2));
+  uint32_t b_off[B_CH];
   int b_dst[B_CH];
+  bool b_w3[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * kThreads;
-    constexpr int CPR = FP8 ? BK / 16 : BK / 8;  // chunks per row
+    const int c = tid + i * NTH;
     const int r = c / CPR, kc = c % CPR;
-    b_dst[i] = r * S + kc * (FP8 ? 16 : 8);
-    const char* base = Bw;
-    int wr = n0 + r;
-    if (SWI && r >= BNO) {
-      base = B3w;
-      wr = n0 + r - BNO;
-    }
-    b_src[i] = base + eoff + (static_cast<int64_t>(wr) * K + kc * (FP8 ? 16 : 8)) * WB;
+    // bf16: one chunk; e4m3: 16 codes become the two bf16 chunks 2 kc, 2 kc + 1
+    b_dst[i] = BM * S + r * S + (FP8 ? 0 : ((kc ^ (r & 7)) * 8));
+    b_w3[i] = SWI && (SPLIT ? (i >= B_CH / 2) : (r >= BNO));
+    const int wr = n0 + (b_w3[i] ? r - BNO : r);
+    b_off[i] = (static_cast<uint32_t>(wr) * static_cast<uint32_t>(K) + kc * (FP8 ? 16 : 8)) * WB;
   }
 
   floatx4_t acc[FM][FN];
@@ -165,94 +184,134 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[A_CH], rb[B_CH];
-#define MOE_GLOAD(kb)                                                                               \
+#define MOE_GLOAD(RA, RB, kb)                                                                       \
   do {                                                                                              \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                                        \
-        *reinterpret_cast<const uint4*>(a_src[i] + (kb));                                           \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                                        \
-        *reinterpret_cast<const uint4*>(b_src[i] + static_cast<int64_t>(kb) * WB);                  \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) RA[i] =                                        \
+        *reinterpret_cast<const uint4*>(A + a_off[i] + (kb));                                       \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) RB[i] = *reinterpret_cast<const uint4*>(       \
+        ((SPLIT ? (SWI && i >= B_CH / 2) : b_w3[i]) ? B3w : Bw) + b_off[i] +                        \
+        static_cast<uint32_t>(kb) * WB);                                                            \
   } while (0)
-#define MOE_LSTORE(buf)                                                                             \
+#define MOE_LSTORE(RA, RB, buf)                                                                     \
   do {                                                                                              \
+    uint16_t* st_ = smem + (buf) * STAGE;                                                           \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                \
-        *reinterpret_cast<uint4*>(&sA[buf][a_dst[i]]) = ra[i];                                      \
+        *reinterpret_cast<uint4*>(st_ + a_dst[i]) = RA[i];                                          \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                              \
       if constexpr (FP8) {                                                                          \
-        const uint2 x0 = e4m3x4_to_bf16x4(rb[i].x), x1 = e4m3x4_to_bf16x4(rb[i].y);                 \
-        const uint2 x2 = e4m3x4_to_bf16x4(rb[i].z), x3 = e4m3x4_to_bf16x4(rb[i].w);                 \
-        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i]]) = make_uint4(x0.x, x0.y, x1.x, x1.y);         \
-        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i] + 8]) = make_uint4(x2.x, x2.y, x3.x, x3.y);     \
+        const int r_ = (tid + i * NTH) / CPR, k2_ = 2 * ((tid + i * NTH) % CPR);                    \
+        const uint2 x0 = e4m3x4_to_bf16x4(RB[i].x), x1 = e4m3x4_to_bf16x4(RB[i].y);                 \
+        const uint2 x2 = e4m3x4_to_bf16x4(RB[i].z), x3 = e4m3x4_to_bf16x4(RB[i].w);                 \
+        *reinterpret_cast<uint4*>(st_ + b_dst[i] + ((k2_ ^ (r_ & 7)) * 8)) =                        \
+            make_uint4(x0.x, x0.y, x1.x, x1.y);                                                     \
+        *reinterpret_cast<uint4*>(st_ + b_dst[i] + (((k2_ + 1) ^ (r_ & 7)) * 8)) =                  \
+            make_uint4(x2.x, x2.y, x3.x, x3.y);                                                     \
       } else {                                                                                      \
-        *reinterpret_cast<uint4*>(&sB[buf][b_dst[i]]) = rb[i];                                      \
+        *reinterpret_cast<uint4*>(st_ + b_dst[i]) = RB[i];                                          \
       }                                                                                             \
     }                                                                                               \
   } while (0)
 
+#define MOE_COMPUTE(SA)                                                                             \
+  do {                                                                                              \
+    const uint16_t* sA_ = (SA);                                                                     \
+    const uint16_t* sB_ = sA_ + BM * S;                                                             \
+    _Pragma("unroll") for (int kk = 0; kk < BK / 32; ++kk) {                                        \
+      uint4 af[FM], bf[FN];                                                                         \
+      /* operand rows start at multiples of 16, so row & 7 == c16 & 7 */                            \
+      const int ch = ((kk * 4 + q) ^ (c16 & 7)) * 8;                                                \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                        \
+          *reinterpret_cast<const uint4*>(sA_ + (wm * WTM + i * 16 + c16) * S + ch);                \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                              \
+        const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                              \
+                                             : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)            \
+                             : wn * WTB + j * 16;                                                   \
+        bf[j] = *reinterpret_cast<const uint4*>(sB_ + (brow + c16) * S + ch);                       \
+      }                                                                                             \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                \
+              mfma16x16x32(af[i], bf[j], acc[i][j]);                                                \
+    }                                                                                               \
+  } while (0)
+
   const int KT = K / BK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    // prefetch the next k-step (the last iteration re-reads its own step; the
-    // copy lands in the idle buffer and is never read)
-    const int kn = (kt + 1 < KT) ? (kt + 1) * BK : kt * BK;
-    MOE_GLOAD(kn);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      uint4 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(&sA[buf][(wm * WM + i * 16 + c16) * S + kk * 32 + q * 8]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int brow = SWI ? ((j < FNO) ? wn * WNO + j * 16 : BNO + wn * WNO + (j - FNO) * 16)
-                             : wn * WNO + j * 16;
-        bf[j] = *reinterpret_cast<const uint4*>(&sB[buf][(brow + c16) * S + kk * 32 + q * 8]);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
-    }
-    MOE_LSTORE(buf ^ 1);
+  if constexpr (PF == 1) {
+    uint4 ra[A_CH], rb[B_CH];
+    MOE_GLOAD(ra, rb, 0);
+    MOE_LSTORE(ra, rb, 0);
     __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      // prefetch the next k-step (the last iteration re-reads its own step;
+      // the copy lands in the idle buffer and is never read)
+      const int kn = (kt + 1 < KT) ? (kt + 1) * BK : kt * BK;
+      MOE_GLOAD(ra, rb, kn);
+      MOE_COMPUTE(smem + (kt & 1) * STAGE);
+      MOE_LSTORE(ra, rb, (kt + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // two k-steps in flight: registers hold step kt+1 while step kt+2 loads.
+    // K is a multiple of 128, so the number of 64-wide k-steps is even; steps
+    // past the end re-read the last one into buffers that are never read.
+    uint4 ra0[A_CH], rb0[B_CH], ra1[A_CH], rb1[B_CH];
+    MOE_GLOAD(ra0, rb0, 0);
+    MOE_GLOAD(ra1, rb1, BK);
+    MOE_LSTORE(ra0, rb0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      MOE_GLOAD(ra0, rb0, min(kt + 2, KT - 1) * BK);
+      MOE_COMPUTE(smem);
+      MOE_LSTORE(ra1, rb1, 1);
+      __syncthreads();
+      MOE_GLOAD(ra1, rb1, min(kt + 3, KT - 1) * BK);
+      MOE_COMPUTE(smem + STAGE);
+      MOE_LSTORE(ra0, rb0, 0);
+      __syncthreads();
+    }
   }
 #undef MOE_GLOAD
 #undef MOE_LSTORE
+#undef MOE_COMPUTE
 
-  // ---- epilogue
+  // ---- epilogue: activation in registers, bf16 tile staged in LDS, 16-byte stores
   const float* sc = shared ? p.scale_s : p.scale_r;
   float s_a = 1.f, s_b = 1.f;
   if (FP8 && sc) {
     s_a = sc[ew * 3 + p.scale_col];
     if (SWI) s_b = sc[ew * 3 + p.scale_col + 1];
   }
-  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout : nullptr;
-  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
-                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+  uint16_t* so = smem;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int j = 0; j < FNO; ++j) {
+    const int col = wn * WTO + j * 16 + c16;
+    const float bv = bias ? bias[col] : 0.f;
 #pragma unroll
-    for (int j = 0; j < FNO; ++j) {
-      const int col = wn * WNO + j * 16 + c16;
-      const float bv = bias ? bias[n0 + col] : 0.f;
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * WM + i * 16 + q * 4 + r;
-        if (row >= ti.rows) continue;
+        const int row = wm * WTM + i * 16 + q * 4 + r;
         float v;
         if constexpr (EPI == EPI_SWIGLU) {
-          v = silu(acc[i][j][r] * s_a) * (acc[i][j + FNO][r] * s_b);
+          v = silu(acc[i][j][r] * s_a) * (acc[i][j + FN / 2][r] * s_b);
         } else if constexpr (EPI == EPI_GELU) {
           v = gelu_erf(acc[i][j][r] * s_a + bv);
         } else {
           v = acc[i][j][r] * s_a + bv;
         }
-        C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v);
+        so[row * SO + col] = f32_to_bf16(v);
       }
     }
+  }
+  __syncthreads();
+  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
+                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+  constexpr int OCH = BNO / 8;  // 16-byte chunks per output row
+  for (int c = tid; c < BM * OCH; c += NTH) {
+    const int row = c / OCH, cc = c % OCH;
+    if (row < ti.rows)
+      *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
+          *reinterpret_cast<const uint4*>(so + row * SO + cc * 8);
   }
 }
 
@@ -384,15 +443,30 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, 
   }
 }
 
-template <int BM, int BNO, int EPI, bool FP8>
+template <int BM, int BNB, int WGM, int WGN, int EPI, bool FP8, int PF = MOE_GEMM_PF>
 hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;
+  if (p.Nout % BNO != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
   grid = ceil_div(grid, kXcds) * kXcds;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNO, EPI, FP8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB, WGM, WGN, EPI, FP8, PF>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
 }
+
+// Tile configurations: rows x weight rows, wave grid.
+enum TileCfg { kTile128x128w4 = 0, kTile256x256w4 = 1, kTile256x256w8 = 2, kTile128x256w4 = 3, kTile256x128w4 = 4,
+               kTile128x128w8 = 5 };
+constexpr int tile_rows(int cfg) { return (cfg == kTile256x256w4 || cfg == kTile256x256w8 || cfg == kTile256x128w4) ? 256 : 128; }
+
+// Configuration of the prefill path (many rows) and of the small-row path.
+#ifndef MOE_GEMM_BIG_CFG
+#define MOE_GEMM_BIG_CFG kTile256x256w8
+#endif
+#ifndef MOE_GEMM_SMALL_CFG
+#define MOE_GEMM_SMALL_CFG kTile128x128w4
+#endif
 
 template <int EPI>
 hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
@@ -403,12 +477,25 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int EPI, bool FP8>
+hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  switch (cfg) {
+    case kTile256x256w4: return run_bf16<256, 256, 2, 2, EPI, FP8>(p, max_mtiles, s);
+    case kTile256x256w8: return run_bf16<256, 256, 2, 4, EPI, FP8>(p, max_mtiles, s);
+    case kTile128x256w4: return run_bf16<128, 256, 2, 2, EPI, FP8>(p, max_mtiles, s);
+    case kTile256x128w4: return run_bf16<256, 128, 2, 2, EPI, FP8>(p, max_mtiles, s);
+    case kTile128x128w8: return run_bf16<128, 128, 2, 4, EPI, FP8>(p, max_mtiles, s);
+    default: return run_bf16<128, 128, 2, 2, EPI, FP8>(p, max_mtiles, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
   const bool f32 = (a.act_dtype == 0);
-  const int bm = f32 ? 64 : 128;
+  const int cfg = (a.routed_row_cap + a.n_shared * a.T >= 2048) ? MOE_GEMM_BIG_CFG : MOE_GEMM_SMALL_CFG;
+  const int bm = f32 ? 64 : tile_rows(cfg);
   GroupDesc* up = a.groups;
   GroupDesc* down = a.groups + G;
   stage_mark(kStageFfnPlan, false, s);
@@ -449,11 +536,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   if (f32) {
     err = swi ? run_f32<EPI_SWIGLU>(p, max_mtiles, s) : run_f32<EPI_GELU>(p, max_mtiles, s);
   } else if (swi) {
-    err = fp8 ? run_bf16<128, 64, EPI_SWIGLU, true>(p, max_mtiles, s)
-              : run_bf16<128, 64, EPI_SWIGLU, false>(p, max_mtiles, s);
+    err = fp8 ? run_cfg<EPI_SWIGLU, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_SWIGLU, false>(cfg, p, max_mtiles, s);
   } else {
-    err = fp8 ? run_bf16<128, 128, EPI_GELU, true>(p, max_mtiles, s)
-              : run_bf16<128, 128, EPI_GELU, false>(p, max_mtiles, s);
+    err = fp8 ? run_cfg<EPI_GELU, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_GELU, false>(cfg, p, max_mtiles, s);
   }
   stage_mark(kStageFfnUp, true, s);
   if (err != hipSuccess) return err;
@@ -479,8 +564,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   if (f32) {
     err = run_f32<EPI_PLAIN>(p, max_mtiles, s);
   } else {
-    err = fp8 ? run_bf16<128, 128, EPI_PLAIN, true>(p, max_mtiles, s)
-              : run_bf16<128, 128, EPI_PLAIN, false>(p, max_mtiles, s);
+    err = fp8 ? run_cfg<EPI_PLAIN, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_PLAIN, false>(cfg, p, max_mtiles, s);
   }
   stage_mark(kStageFfnDown, true, s);
   return err;
