@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--workload", default="mixtral-prefill-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode shapes (T = 1, 16, 64) on the prefill weights; prints their JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -203,6 +205,9 @@ def main():
     t = time.perf_counter()
     inp = gen.make_inputs(wl)
     log(f"inputs generated in {time.perf_counter() - t:.1f} s")
+    if args.decode_only:
+        print(json.dumps({"decode": run_decode(wl, inp, max(args.steps, 16), args.warmup)}), flush=True)
+        return
 
     r = run_gpu(wl, inp, args.steps, args.warmup)
     ms = r["ms_per_step"]

@@ -71,6 +71,7 @@ struct RouteWs {
   float* part_P;
   int32_t* part_cnt;
   float* part_lse;
+  float* part_logits;
 };
 RouteWs carve_route(Carver& c, const moe_shape& s) {
   const size_t nb = static_cast<size_t>(moe::ceil_div(s.T, moe::kRouteTokens));
@@ -78,6 +79,7 @@ RouteWs carve_route(Carver& c, const moe_shape& s) {
   w.part_P = c.take<float>(nb * s.n_experts);
   w.part_cnt = c.take<int32_t>(nb * s.n_experts);
   w.part_lse = c.take<float>(2 * nb);
+  w.part_logits = c.take<float>(static_cast<size_t>(moe::route_splits(s.T, s.d)) * s.T * s.n_experts);
   return w;
 }
 
@@ -99,6 +101,7 @@ struct FfnWs {
   void* h;
   moe::GroupDesc* groups;
   int32_t* tile_start;
+  float* part;
 };
 FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
@@ -107,6 +110,10 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff) * act_bytes(s.act_dtype));
   w.groups = c.take<moe::GroupDesc>(2 * G);
   w.tile_start = c.take<int32_t>(G + 1);
+  w.part = nullptr;
+  if (moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T))
+    w.part = c.take<float>(
+        moe::skinny_part_floats(s.T, s.d, s.d_ff, s.n_experts, s.n_shared, s.act, routed_row_cap(s)));
   return w;
 }
 
@@ -181,6 +188,7 @@ moe::RouteArgs route_args(const moe_shape& s, const void* x, const void* w_route
   a.part_P = w.part_P;
   a.part_cnt = w.part_cnt;
   a.part_lse = w.part_lse;
+  a.part_logits = w.part_logits;
   if (st) {
     a.counts = st->counts;
     a.f = st->f;
@@ -264,6 +272,7 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* off
   a.y_shared = y_shared;
   a.groups = fw.groups;
   a.tile_start = fw.tile_start;
+  a.part = fw.part;
   return a;
 }
 

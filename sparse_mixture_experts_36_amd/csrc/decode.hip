@@ -1,0 +1,392 @@
+// Grouped expert FFN for decode-sized row counts: expert-weight streaming.
+//
+// Pages: vanos001 "MoE Architecture" / "Expert Network Design" (SwiGLU and
+// GELU experts), aigrafen.se "Mixture of Experts" (every expert must sit in
+// memory while only the selected ones are used per token), learn.starphix.com
+// "Mixture of Experts (MoE)" / "Shared + Specialized" and "Quantization".
+//
+// With a few rows per expert the layer is bound by reading each touched
+// expert's weights once from HBM, so the design maximises bytes in flight:
+//  - a wave owns 32 weight rows of one expert (SwiGLU up: the same 16 rows of
+//    W1 and W3; otherwise 32 rows of W1 or W2) and a k range, and streams them
+//    from memory straight into MFMA operand registers (no LDS): lane (c, q)
+//    takes 64 contiguous bytes of row c per 128-wide k-step, the four lanes of
+//    a row covering its 256 bytes;
+//  - every load of two k-steps is issued before the first MFMA that needs them
+//    (a scheduling barrier keeps the compiler from interleaving and draining);
+//  - the token rows (16, 32 or 64 per pass, the MFMA's M) come from L2;
+//  - when few experts are touched, k is split across waves; fp32 partials are
+//    then summed in split order by a second kernel that also applies the
+//    activation or the bias (bit-for-bit reproducible).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;  // 4 independent waves per workgroup
+constexpr int KC = 128;        // k per step
+constexpr int KU = 2;          // steps whose loads are issued together
+
+struct StreamParams {
+  const uint16_t* A_r;       // routed A rows (x_perm or h)
+  const uint16_t* A_s;       // shared A rows (x or h)
+  int64_t lda;
+  const char* B_r;           // weights of routed experts (bytes)
+  const char* B3_r;          // W3 (SwiGLU up) or null
+  const char* B_s;
+  const char* B3_s;
+  int64_t b_stride;          // elements per expert matrix
+  const float* bias;         // [n_routed][Nout] (routed GELU experts) or null
+  const float* scale_r;      // e4m3 scales [n_routed][3]
+  const float* scale_s;
+  int scale_col;
+  uint16_t* C_r;             // outputs (h / y_perm) for routed groups
+  uint16_t* C_s;             //              (h / y_shared) for shared groups
+  int64_t ldc;
+  int32_t c_shared_base;     // partial-row base of shared groups (down: cap, up: 0)
+  float* part;               // [splits][rows_total][width] or null (direct epilogue)
+  int32_t rows_total, width; // partial buffer shape
+  int32_t K, Nout, splits;
+  int32_t n_routed, n_groups;
+  int32_t epi;               // 0 GELU (+b1), 1 SwiGLU, 2 plain (+b2)
+  const GroupDesc* groups;
+};
+
+// 8 bf16 weights per uint4; e4m3 codes are decoded to bf16 in registers.
+template <bool FP8>
+__device__ __forceinline__ void load_w(const char* base, int64_t elem, uint4 (&w)[4]) {
+  if constexpr (FP8) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(base + elem);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(base + elem + 16);
+    w[0] = make_uint4(q0.x, q0.y, 0, 0);
+    w[1] = make_uint4(q0.z, q0.w, 0, 0);
+    w[2] = make_uint4(q1.x, q1.y, 0, 0);
+    w[3] = make_uint4(q1.z, q1.w, 0, 0);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(base + elem * 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t] = p[t];
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ uint4 as_bf16(const uint4& w) {
+  if constexpr (FP8) {
+    const uint2 a = e4m3x4_to_bf16x4(w.x), b = e4m3x4_to_bf16x4(w.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  } else {
+    return w;
+  }
+}
+
+__device__ __forceinline__ float epilogue(int epi, float a, float b, float bias) {
+  if (epi == 1) return silu(a) * b;
+  if (epi == 0) return gelu_erf(a + bias);
+  return a + bias;
+}
+
+// Wave -> (group g, block nb of 32 weight rows, k split sp).
+template <int RB, bool FP8>
+__global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
+  constexpr int FN = 2;  // 16-row weight tiles per wave
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, c16 = lane & 15;
+  const bool swi = (p.epi == 1);
+  const int nblk = swi ? p.Nout / 16 : p.Nout / 32;  // blocks per expert
+  const int w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int per_g = nblk * p.splits;
+  const int g = w / per_g;
+  if (g >= p.n_groups) return;
+  const GroupDesc gd = p.groups[g];
+  if (gd.rows <= 0) return;
+  const int nb = (w % per_g) / p.splits, sp = w % p.splits;
+  const bool shared = g >= p.n_routed;
+  const int ew = shared ? g - p.n_routed : g;
+  constexpr int WB = FP8 ? 1 : 2;
+  const int64_t eoff = static_cast<int64_t>(ew) * p.b_stride * WB;
+  const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
+  const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
+  const uint16_t* A = (shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * p.lda;
+  const int K = p.K, ks = K / p.splits;
+  const int kbeg = sp * ks, nsteps = ks / KC;
+  // weight rows of the two tiles, and the output / partial columns they feed
+  const int n0 = swi ? nb * 16 : nb * 32;
+  int64_t woff[FN];
+  const char* wbase[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = swi ? n0 + c16 : n0 + j * 16 + c16;
+    wbase[j] = (swi && j == 1) ? B3w : Bw;
+    woff[j] = static_cast<int64_t>(n) * K + kbeg + q * 32;
+  }
+  float s_a = 1.f, s_b = 1.f;
+  if (FP8) {
+    const float* sc = shared ? p.scale_s : p.scale_r;
+    s_a = sc[ew * 3 + p.scale_col];
+    s_b = swi ? sc[ew * 3 + p.scale_col + 1] : s_a;
+  }
+
+  for (int r0 = 0; r0 < gd.rows; r0 += 16 * RB) {
+    const uint16_t* ap[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int arow = min(r0 + rb * 16 + c16, gd.rows - 1);  // rows past the group compute garbage
+      ap[rb] = A + static_cast<int64_t>(arow) * p.lda + kbeg + q * 32;
+    }
+    floatx4_t acc[RB][FN];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[rb][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int st = 0; st < nsteps; st += KU) {
+      uint4 bw[KU][FN][4], a[KU][RB][4];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int kk = min(st + u, nsteps - 1) * KC;  // a step past the end re-reads the last one
+#pragma unroll
+        for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk, bw[u][j]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[u][rb][t] = *reinterpret_cast<const uint4*>(ap[rb] + kk + t * 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        if (st + u >= nsteps) break;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const uint4 b = as_bf16<FP8>(bw[u][j][t]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(a[u][rb][t], b, acc[rb][j]);
+          }
+      }
+    }
+
+    // tile j, lane (q, c16): rows r0 + rb*16 + 4q + i, weight row n of tile j
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + rb * 16 + q * 4 + i;
+        if (row >= gd.rows) continue;
+        if (p.part) {
+          const int prow = (shared ? p.c_shared_base : 0) + gd.c_row0 + row;
+          float* dst = p.part + (static_cast<int64_t>(sp) * p.rows_total + prow) * p.width;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            // partial columns: SwiGLU [W1 results | W3 results], otherwise the output columns
+            const int col = swi ? (j == 0 ? n0 + c16 : p.Nout + n0 + c16) : n0 + j * 16 + c16;
+            dst[col] = acc[rb][j][i] * (j == 1 ? s_b : s_a);
+          }
+        } else {
+          uint16_t* C = (shared ? p.C_s : p.C_r) + (static_cast<int64_t>(gd.c_row0) + row) * p.ldc;
+          const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout : nullptr;
+          if (swi) {
+            C[n0 + c16] = f32_to_bf16(epilogue(1, acc[rb][0][i] * s_a, acc[rb][1][i] * s_b, 0.f));
+          } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int col = n0 + j * 16 + c16;
+              C[col] = f32_to_bf16(epilogue(p.epi, acc[rb][j][i] * s_a, 0.f, bias ? bias[col] : 0.f));
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Sums the split partials in split order, applies the activation / bias and
+// writes bf16. Block (x, R): partial row R, columns [x*1024, x*1024 + 1024), four
+// per thread; all split loads are issued before the fixed-order sum. Rows never
+// written (past the routed rows) are skipped.
+constexpr int kRedCols = 4 * kThreads;
+
+__global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p, const int32_t* offsets,
+                                                                  int32_t cap) {
+  const int R = blockIdx.y;
+  const int c = blockIdx.x * kRedCols + threadIdx.x * 4;
+  if (c >= p.Nout) return;
+  // the group that owns partial row R: routed rows first, then T rows per shared expert
+  int g = -1, row = 0;
+  if (R < cap) {
+    const int routed_rows = min(offsets[p.n_routed], cap);
+    if (R >= routed_rows) return;
+    int lo = 0, hi = p.n_routed - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= R) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    row = R - offsets[g];
+  } else {
+    const int T = (p.rows_total - cap) / (p.n_groups - p.n_routed);
+    g = p.n_routed + (R - cap) / T;
+    row = (R - cap) % T;
+  }
+  const GroupDesc gd = p.groups[g];
+  const bool shared = g >= p.n_routed;
+  uint16_t* C = (shared ? p.C_s : p.C_r) + (static_cast<int64_t>(gd.c_row0) + row) * p.ldc + c;
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(g) * p.Nout + c : nullptr;
+  const int64_t plane = static_cast<int64_t>(p.rows_total) * p.width;
+  const float* src = p.part + static_cast<int64_t>(R) * p.width + c;
+  constexpr int kMaxSplits = 16;
+  float4 va[kMaxSplits], vb[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < p.splits) {
+      va[sp] = *reinterpret_cast<const float4*>(src + sp * plane);
+      if (p.epi == 1) vb[sp] = *reinterpret_cast<const float4*>(src + sp * plane + p.Nout);
+    }
+  float4 a = va[0], b = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.epi == 1) b = vb[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxSplits; ++sp)
+    if (sp < p.splits) {
+      a.x += va[sp].x; a.y += va[sp].y; a.z += va[sp].z; a.w += va[sp].w;
+      if (p.epi == 1) { b.x += vb[sp].x; b.y += vb[sp].y; b.z += vb[sp].z; b.w += vb[sp].w; }
+    }
+  const float4 bv = bias ? *reinterpret_cast<const float4*>(bias) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float o0 = epilogue(p.epi, a.x, b.x, bv.x), o1 = epilogue(p.epi, a.y, b.y, bv.y);
+  const float o2 = epilogue(p.epi, a.z, b.z, bv.z), o3 = epilogue(p.epi, a.w, b.w, bv.w);
+  *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+}
+
+// k splits for one GEMM: double while the touched experts' blocks give fewer
+// than 4096 waves and every split keeps at least two 128-wide k-steps.
+int pick_splits(int64_t K, int64_t blocks_touched) {
+  const int64_t steps = K / KC;
+  int s = 1;
+  while (blocks_touched * s < 4096 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
+  return s;
+}
+
+hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, hipStream_t s) {
+  const int64_t waves = blocks * p.splits;
+  const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
+#define MOE_STREAM_CASE(R)                                                                          \
+  if (rb == R) {                                                                                    \
+    if (fp8) hipLaunchKernelGGL((stream_kernel<R, true>), grid, dim3(kThreads), 0, s, p);           \
+    else hipLaunchKernelGGL((stream_kernel<R, false>), grid, dim3(kThreads), 0, s, p);              \
+  }
+  MOE_STREAM_CASE(1) MOE_STREAM_CASE(2) MOE_STREAM_CASE(4)
+#undef MOE_STREAM_CASE
+  return hipGetLastError();
+}
+
+struct SplitPlan {
+  int rb, up_splits, down_splits;
+};
+
+SplitPlan plan_splits(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
+                      int64_t cap) {
+  SplitPlan sp;
+  const int64_t rows = cap + n_shared * T;
+  sp.rb = rows <= 32 ? 1 : (rows <= 128 ? 2 : 4);
+  // experts that can have rows: at most one per routed row, plus the shared ones
+  const int64_t touched = (cap < n_routed ? cap : n_routed) + n_shared;
+  const int64_t up_blocks = (act == 1 ? d_ff / 16 : d_ff / 32);
+  sp.up_splits = pick_splits(d, touched * up_blocks);
+  sp.down_splits = pick_splits(d_ff, touched * (d / 32));
+  return sp;
+}
+
+}  // namespace
+
+size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
+                          int64_t cap) {
+  const SplitPlan sp = plan_splits(T, d, d_ff, n_routed, n_shared, act, cap);
+  const int64_t rows = cap + n_shared * T;
+  const int64_t up = sp.up_splits > 1 ? sp.up_splits * rows * (act == 1 ? 2 * d_ff : d_ff) : 0;
+  const int64_t down = sp.down_splits > 1 ? sp.down_splits * rows * d : 0;
+  return static_cast<size_t>(up > down ? up : down);
+}
+
+hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
+                             hipStream_t s) {
+  const int G = a.n_routed + a.n_shared;
+  const bool fp8 = (a.w_dtype == 2);
+  const bool swi = (a.act == 1);
+  const SplitPlan sp = plan_splits(a.T, a.d, a.d_ff, a.n_routed, a.n_shared, a.act, a.routed_row_cap);
+  StreamParams p{};
+  p.n_routed = a.n_routed;
+  p.n_groups = G;
+  p.rows_total = a.routed_row_cap + a.n_shared * static_cast<int32_t>(a.T);
+  constexpr int WB2 = 1;  // byte pointers below
+  (void)WB2;
+
+  // ---- up: [rows][d] x W1 (W3)^T -> h [rows][d_ff]
+  p.A_r = static_cast<const uint16_t*>(a.x_perm);
+  p.A_s = static_cast<const uint16_t*>(a.x);
+  p.lda = a.d;
+  p.B_r = static_cast<const char*>(a.w1);
+  p.B3_r = static_cast<const char*>(a.w3);
+  p.B_s = static_cast<const char*>(a.sw1);
+  p.B3_s = static_cast<const char*>(a.sw3);
+  p.b_stride = a.d_ff * a.d;
+  p.bias = swi ? nullptr : a.b1;
+  p.scale_r = a.w_scale;
+  p.scale_s = a.sw_scale;
+  p.scale_col = 0;
+  p.C_r = static_cast<uint16_t*>(a.h);
+  p.C_s = static_cast<uint16_t*>(a.h);
+  p.ldc = a.d_ff;
+  p.c_shared_base = 0;  // up group descriptors already place shared rows after cap
+  p.K = static_cast<int32_t>(a.d);
+  p.Nout = static_cast<int32_t>(a.d_ff);
+  p.epi = swi ? 1 : 0;
+  p.splits = sp.up_splits;
+  p.width = swi ? 2 * p.Nout : p.Nout;
+  p.part = sp.up_splits > 1 ? part : nullptr;
+  p.groups = up;
+  const int64_t up_blocks = static_cast<int64_t>(G) * (swi ? a.d_ff / 16 : a.d_ff / 32);
+  stage_mark(kStageFfnUp, false, s);
+  hipError_t e = run_stream(p, sp.rb, fp8, up_blocks, s);
+  if (e == hipSuccess && p.part) {
+    const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
+    hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);
+    e = hipGetLastError();
+  }
+  stage_mark(kStageFfnUp, true, s);
+  if (e != hipSuccess) return e;
+
+  // ---- down: h [rows][d_ff] x W2^T -> y [rows][d]
+  p.A_r = static_cast<const uint16_t*>(a.h);
+  p.A_s = static_cast<const uint16_t*>(a.h);
+  p.lda = a.d_ff;
+  p.B_r = static_cast<const char*>(a.w2);
+  p.B3_r = nullptr;
+  p.B_s = static_cast<const char*>(a.sw2);
+  p.B3_s = nullptr;
+  p.b_stride = a.d * a.d_ff;
+  p.bias = swi ? nullptr : a.b2;
+  p.scale_col = 2;
+  p.C_r = static_cast<uint16_t*>(a.y_perm);
+  p.C_s = static_cast<uint16_t*>(a.y_shared);
+  p.ldc = a.d;
+  p.c_shared_base = a.routed_row_cap;  // down descriptors index y_shared; partial rows follow the routed ones
+  p.K = static_cast<int32_t>(a.d_ff);
+  p.Nout = static_cast<int32_t>(a.d);
+  p.epi = 2;
+  p.splits = sp.down_splits;
+  p.width = p.Nout;
+  p.part = sp.down_splits > 1 ? part : nullptr;
+  p.groups = down;
+  const int64_t down_blocks = static_cast<int64_t>(G) * (a.d / 32);
+  stage_mark(kStageFfnDown, false, s);
+  e = run_stream(p, sp.rb, fp8, down_blocks, s);
+  if (e == hipSuccess && p.part) {
+    const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
+    hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);
+    e = hipGetLastError();
+  }
+  stage_mark(kStageFfnDown, true, s);
+  return e;
+}
+
+}  // namespace moe

@@ -26,12 +26,14 @@ struct RouteArgs {
   float* part_P;            // [nb][N]
   int32_t* part_cnt;        // [nb][N]
   float* part_lse;          // [nb][2]
+  float* part_logits;       // [splits][T][N] k-split partial logits (workspace)
   // statistics outputs (any may be null)
   int32_t* counts;
   float *f, *P, *l_aux, *z_loss, *lse_mean, *lse_sq_mean;
   float aux_alpha;
 };
 constexpr int kRouteTokens = 64;  // tokens per route workgroup
+int route_splits(int64_t T, int64_t d);  // k splits of the router GEMM
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- permute
@@ -78,10 +80,23 @@ struct FfnArgs {
   void* h;                    // [routed_row_cap + n_shared*T][d_ff] act dtype (workspace)
   void* y_perm;               // [*][d]
   void* y_shared;             // [n_shared][T][d]
-  GroupDesc* groups;          // [n_routed + n_shared] (workspace)
+  GroupDesc* groups;          // [2][n_routed + n_shared] (workspace)
   int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
+  float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
 };
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+// Decode-sized layers (few rows per expert) stream expert weights instead of
+// tiling rows: taken when all expert rows of the call fit in kSkinnyMaxRows.
+constexpr int64_t kSkinnyMaxRows = 256;
+inline bool use_skinny(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shared, int64_t T) {
+  return act_dtype == 1 && routed_row_cap + n_shared * T <= kSkinnyMaxRows;
+}
+// fp32 partial-sum floats the decode path needs (0 when no GEMM is split)
+size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
+                          int64_t cap);
+hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
+                             hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 struct CombineArgs {

@@ -37,62 +37,74 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
   return v > v2 || (v == v2 && e < e2);
 }
 
+// Router GEMM over one k range: partial logits of 64 tokens (4 waves x 16) for
+// all experts. Grid (token blocks, k splits). bf16 runs on MFMA with the
+// router-weight tile for all experts in LDS (double buffered); the next
+// k-step's tile and token fragments are loaded while the current one computes.
 template <int NT>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wtile[kMaxN * kWStride];
-  __shared__ int32_t s_cnt[kMaxN];
-  __shared__ float s_P[4][kMaxN];
-  __shared__ float s_lse[4][2];
-
+__global__ __launch_bounds__(kThreads) void router_gemm_kernel(RouteArgs a, float* part, int k_len) {
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[2][NT * 16 * kWStride];
+  constexpr int WCH = (NT * 16 * (kRK / 8) + kThreads - 1) / kThreads;  // 16-byte weight chunks per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c16 = lane & 15;
-  const int N = a.N, k = a.k;
+  const int N = a.N;
   const int64_t T = a.T, d = a.d;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 16;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * k_len;
+  float* out = part + static_cast<int64_t>(blockIdx.y) * T * N;
 
-  for (int e = tid; e < kMaxN; e += kThreads) s_cnt[e] = 0;
-
-  // ---- logits in accumulator layout: acc[nt][i] = l[t0 + 4q + i][16 nt + c16]
   floatx4_t acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (a.logits_given) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * q + i;
-        const int e = 16 * nt + c16;
-        acc[nt][i] = (t < T && e < N) ? a.logits[t * N + e] : 0.f;
-      }
-  } else if (a.act_dtype == 1) {
-    // bf16 x and W_r on MFMA. Lane (row c16, k-group q) takes 16 consecutive k
-    // of its row per step; the weight tile for all experts sits in LDS.
+  if (a.act_dtype == 1) {
+    // Lane (row c16, k-group q) takes 16 consecutive k of its token row per step.
     const uint16_t* xr = static_cast<const uint16_t*>(a.x);
     const uint16_t* wr = static_cast<const uint16_t*>(a.w_router);
     int64_t trow = t0 + c16;
     if (trow > T - 1) trow = T - 1;  // rows past T compute garbage that is never stored
-    const uint16_t* xrow = xr + trow * d + q * 16;
-    for (int64_t kb = 0; kb < d; kb += kRK) {
-      __syncthreads();
-      for (int c = tid; c < NT * 16 * (kRK / 8); c += kThreads) {
+    const uint16_t* xrow = xr + trow * d + k0 + q * 16;
+    const int nsteps = k_len / kRK;
+    uint4 wv[WCH];
+    auto wload = [&](int step) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) {
+        const int c = tid + i * kThreads;
         const int e = c >> 3, kc = c & 7;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e < N) v = *reinterpret_cast<const uint4*>(wr + e * d + kb + kc * 8);
-        *reinterpret_cast<uint4*>(&wtile[e * kWStride + kc * 8]) = v;
+        wv[i] = make_uint4(0, 0, 0, 0);
+        if (c < NT * 16 * 8 && e < N) wv[i] = *reinterpret_cast<const uint4*>(wr + e * d + k0 + step * kRK + kc * 8);
       }
-      const uint4 a0 = *reinterpret_cast<const uint4*>(xrow + kb);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(xrow + kb + 8);
-      __syncthreads();
+    };
+    auto wstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) {
+        const int c = tid + i * kThreads;
+        const int e = c >> 3, kc = c & 7;
+        if (c < NT * 16 * 8) *reinterpret_cast<uint4*>(&wtile[buf][e * kWStride + kc * 8]) = wv[i];
+      }
+    };
+    wload(0);
+    uint4 x0 = *reinterpret_cast<const uint4*>(xrow);
+    uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 8);
+    wstore(0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+      const int nx = (st + 1 < nsteps) ? st + 1 : st;  // the last step re-reads itself into the idle buffer
+      wload(nx);
+      const uint4 y0 = *reinterpret_cast<const uint4*>(xrow + nx * kRK);
+      const uint4 y1 = *reinterpret_cast<const uint4*>(xrow + nx * kRK + 8);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const uint16_t* wp = &wtile[(16 * nt + c16) * kWStride + q * 16];
+        const uint16_t* wp = &wtile[st & 1][(16 * nt + c16) * kWStride + q * 16];
         const uint4 b0 = *reinterpret_cast<const uint4*>(wp);
         const uint4 b1 = *reinterpret_cast<const uint4*>(wp + 8);
-        acc[nt] = mfma16x16x32(a0, b0, acc[nt]);
-        acc[nt] = mfma16x16x32(a1, b1, acc[nt]);
+        acc[nt] = mfma16x16x32(x0, b0, acc[nt]);
+        acc[nt] = mfma16x16x32(x1, b1, acc[nt]);
       }
+      wstore((st + 1) & 1);
+      x0 = y0;
+      x1 = y1;
+      __syncthreads();
     }
   } else {
     // fp32: plain dot products straight into the same layout.
@@ -102,14 +114,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
       const int e = 16 * nt + c16;
       if (e >= N) continue;
-      const float4* w4 = reinterpret_cast<const float4*>(wr + e * d);
+      const float4* w4 = reinterpret_cast<const float4*>(wr + e * d + k0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int64_t t = t0 + 4 * q + i;
         if (t > T - 1) t = T - 1;
-        const float4* x4 = reinterpret_cast<const float4*>(xr + t * d);
+        const float4* x4 = reinterpret_cast<const float4*>(xr + t * d + k0);
         float s = 0.f;
-        for (int64_t j = 0; j < d / 4; ++j) {
+        for (int64_t j = 0; j < k_len / 4; ++j) {
           const float4 u = x4[j], w = w4[j];
           s = fmaf(u.x, w.x, s);
           s = fmaf(u.y, w.y, s);
@@ -120,21 +132,55 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
       }
     }
   }
-
-  // bias, logits store
-  if (!a.logits_given) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int e = 16 * nt + c16;
-      const float b = (a.b_router && e < N) ? a.b_router[e] : 0.f;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = 16 * nt + c16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[nt][i] += b;
-        const int64_t t = t0 + 4 * q + i;
-        if (t < T && e < N) a.logits[t * N + e] = acc[nt][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * q + i;
+      if (t < T && e < N) out[t * N + e] = acc[nt][i];
     }
   }
+}
+
+// Softmax / top-k / gates / block statistics over 64 tokens. Logits are the
+// given ones, or the sum of the k-split partial logits (in split order) plus
+// the router bias, which is then also stored as the router output.
+template <int NT>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, const float* part, int splits) {
+  __shared__ int32_t s_cnt[kMaxN];
+  __shared__ float s_P[4][kMaxN];
+  __shared__ float s_lse[4][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int N = a.N, k = a.k;
+  const int64_t T = a.T;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 16;
+
+  for (int e = tid; e < kMaxN; e += kThreads) s_cnt[e] = 0;
+
+  // logits in accumulator layout: acc[nt][i] = l[t0 + 4q + i][16 nt + c16]
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * q + i;
+      const int e = 16 * nt + c16;
+      float v = 0.f;
+      if (t < T && e < N) {
+        if (a.logits_given) {
+          v = a.logits[t * N + e];
+        } else {
+          v = part[t * N + e];
+          for (int sp = 1; sp < splits; ++sp) v += part[(static_cast<int64_t>(sp) * T + t) * N + e];
+          if (a.b_router) v += a.b_router[e];
+          a.logits[t * N + e] = v;
+        }
+      }
+      acc[nt][i] = v;
+    }
   __syncthreads();  // s_cnt cleared before any count below
 
   // ---- per token: softmax, top-k, gates, statistics
@@ -290,22 +336,36 @@ __global__ __launch_bounds__(kThreads) void route_finalize_kernel(RouteArgs a, i
 }
 
 template <int NT>
-hipError_t launch_nt(const RouteArgs& a, int nb, hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kThreads), 0, s, a);
+hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
+  if (!a.logits_given) {
+    hipLaunchKernelGGL(router_gemm_kernel<NT>, dim3(nb, splits), dim3(kThreads), 0, s, a, a.part_logits,
+                       static_cast<int>(a.d / splits));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kThreads), 0, s, a, a.part_logits, splits);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int route_splits(int64_t T, int64_t d) {
+  const int64_t nb = ceil_div(T, kRouteTokens), steps = d / kRK;
+  int s = 1;
+  while (nb * s < 256 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const int nb = static_cast<int>(ceil_div(a.T, kRouteTokens));
   const int nt = static_cast<int>(ceil_div(a.N, 16));
+  const int splits = a.logits_given ? 1 : route_splits(a.T, a.d);
   hipError_t err;
   stage_mark(kStageRoute, false, s);
   switch (nt) {
 #define MOE_ROUTE_CASE(n) \
-  case n: err = launch_nt<n>(a, nb, s); break;
+  case n: err = launch_nt<n>(a, nb, splits, s); break;
     MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4)
     MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6) MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8)
     MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11) MOE_ROUTE_CASE(12)

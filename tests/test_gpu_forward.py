@@ -110,6 +110,11 @@ REDUCED = {
     "switch-like": gen.SWITCH_TOP1.with_(T=2048, d=512, d_ff=1024),
     "switch-like-fp8": gen.SWITCH_TOP1_FP8.with_(T=2048, d=512, d_ff=1024),
     "switch-like-renorm": gen.SWITCH_TOP1.with_(T=1024, d=256, d_ff=512, gating=gen.SOFTMAX_TOPK_RENORM),
+    # decode-sized: the weight-streaming path
+    "mixtral-like-decode-T1": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
+    "mixtral-like-decode-T64": gen.MIXTRAL_PREFILL.with_(T=64, d=1024, d_ff=1536),
+    "fine-grained-like-decode": gen.FINE_GRAINED.with_(T=24, d=512, d_ff=256),
+    "switch-like-decode-fp8": gen.SWITCH_TOP1_FP8.with_(T=128, d=512, d_ff=1024),
 }
 
 

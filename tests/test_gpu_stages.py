@@ -152,6 +152,14 @@ FFN_CASES = [
     dict(T=200, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
     dict(T=256, N=8, k=2, act=gen.GELU, d=512, d_ff=2048, dt=gen.F32, biases=True),
     dict(T=130, N=8, k=2, act=gen.SWIGLU, d=128, d_ff=256, dt=gen.F32, n_shared=1),
+    # decode-sized calls (<= 256 expert rows): the weight-streaming path
+    dict(T=1, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=1024),
+    dict(T=100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=512),
+    dict(T=128, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=384),
+    dict(T=64, N=16, k=1, act=gen.GELU, d=256, d_ff=512, wdt=gen.E4M3, biases=True),
+    dict(T=64, N=16, k=1, act=gen.GELU, d=256, d_ff=512, biases=True),
+    dict(T=40, N=32, k=4, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
+    dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=1536, wdt=gen.E4M3),
 ]
 
 
