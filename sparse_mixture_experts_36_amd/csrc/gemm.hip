@@ -315,6 +315,190 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA, LDS DMA pipeline
+// 256 x 256 tile, 8 waves (2 x 4, each 128 rows x 64 weight rows), k-steps of
+// 32 through four LDS stage buffers with three steps in flight. Operands move
+// from memory to LDS with global_load_lds (no VGPR staging, no ds_write): each
+// wave instruction writes 1 KB = 16 rows x 64 B of one stage, and the source
+// address each lane fetches puts 16-byte chunk c of row r at position
+// c ^ ((r >> 1) & 3): measured on gfx950, this is the placement of 64-byte rows
+// at which the MFMA operand reads (16 rows, one chunk each) run at the full
+// 256 B/clk of the LDS; (r >> 2) & 3 or no swizzle reach only half of it.
+// The stage buffers are separate LDS objects so that the compiler's wait for a
+// DMA store only blocks reads of that buffer. Before every barrier a wave waits
+// for its own LDS reads, so no DMA can overwrite data still being read.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
+  constexpr int BM = 256, BNB = 256, NTH = 512, WGN = 4;
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int BNO = SWI ? BNB / 2 : BNB;
+  constexpr int BK = 32;                 // k per stage: one MFMA step, 64 B per row
+  constexpr int WTM = 128, WTB = 64;     // rows / weight rows per wave
+  constexpr int WTO = SWI ? WTB / 2 : WTB;
+  constexpr int FM = 8, FN = 4, FNO = WTO / 16;
+  constexpr int SBYTES = (BM + BNB) * BK * 2;  // 32 KB per stage
+  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
+  __shared__ __attribute__((aligned(16))) char S1[SBYTES];
+  __shared__ __attribute__((aligned(16))) char S2[SBYTES];
+  __shared__ __attribute__((aligned(16))) char S3[SBYTES];
+
+  TileInfo ti;
+  if (!decode_tile<BM, BNO>(p, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int q = lane >> 4, c16 = lane & 15;
+  const bool shared = ti.g >= p.n_routed;
+  const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
+  const int n0 = ti.n_tile * BNO;
+  const int K = p.K;
+  const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
+                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
+  const uint16_t* Bw = static_cast<const uint16_t*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride;
+  const uint16_t* B3w = SWI ? static_cast<const uint16_t*>(shared ? p.B3_s : p.B3_r) + static_cast<int64_t>(ew) * p.b_stride
+                            : Bw;
+
+  // This wave's four DMA instructions per stage: A rows [32 w, 32 w + 32) and
+  // weight rows [32 w, 32 w + 32), 16 rows each. Lane L of an instruction over
+  // rows [r0, r0 + 16) fills row r0 + L/4, position L%4 with logical chunk
+  // (L%4) ^ ((row >> 1) & 3).
+  const uint16_t* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (i & 1) * 16 + wave * 32 + (lane >> 2);  // row inside the A (i < 2) or weight (i >= 2) tile
+    const int chunk = (lane & 3) ^ ((r >> 1) & 3);
+    if (i < 2) {
+      const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
+      src[i] = A + static_cast<int64_t>(rr) * p.lda + chunk * 8;
+    } else {
+      const bool w3 = SWI && r >= BNO;
+      src[i] = (w3 ? B3w : Bw) + static_cast<int64_t>(n0 + (w3 ? r - BNO : r)) * K + chunk * 8;
+    }
+  }
+  const int dst_a = wave * 2048, dst_b = BM * 64 + wave * 2048;  // byte offsets inside a stage
+#define MOE_LDS(x) ((__attribute__((address_space(3))) void*)(x))
+#define MOE_DMA(S, kt)                                                                               \
+  do {                                                                                               \
+    const int ko_ = (kt) * BK;                                                                       \
+    __builtin_amdgcn_global_load_lds(src[0] + ko_, MOE_LDS(S + dst_a), 16, 0, 0);                    \
+    __builtin_amdgcn_global_load_lds(src[1] + ko_, MOE_LDS(S + dst_a + 1024), 16, 0, 0);             \
+    __builtin_amdgcn_global_load_lds(src[2] + ko_, MOE_LDS(S + dst_b), 16, 0, 0);                    \
+    __builtin_amdgcn_global_load_lds(src[3] + ko_, MOE_LDS(S + dst_b + 1024), 16, 0, 0);             \
+  } while (0)
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // operand read offsets: rows start at multiples of 16, so (row >> 1) & 3 == (c16 >> 1) & 3
+  const int rd = (c16 * 64) + ((q ^ ((c16 >> 1) & 3)) * 16);
+#define MOE_READ(S, AF, BF)                                                                          \
+  do {                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
+        *reinterpret_cast<const uint4*>(S + (wm * WTM + i * 16) * 64 + rd);                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                 \
+      const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
+                                           : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
+                           : wn * WTB + j * 16;                                                      \
+      BF[j] = *reinterpret_cast<const uint4*>(S + BM * 64 + brow * 64 + rd);                         \
+    }                                                                                                \
+  } while (0)
+  // Step kt: wait until step kt+1 has landed (this wave's DMA, then the
+  // barrier for everyone's), refill the buffer of step kt-1 with step kt+3,
+  // read step kt+1's fragments, and run step kt's MFMAs on the fragments read
+  // during the previous step.
+#define MOE_STEP(SNEXT, SFILL, kfill, AC, BC, AN, BN)                                                \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(0x0f74); /* vmcnt(4): only step kt+2's DMA may still fly */           \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of step kt's buffer are done */      \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA(SFILL, min((kfill), KT - 1));                                                            \
+    MOE_READ(SNEXT, AN, BN);                                                                         \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                   \
+            mfma16x16x32(AC[i], BC[j], acc[i][j]);                                                   \
+    MOE_SCHEDULE();                                                                                  \
+  } while (0)
+  // Keep the issue order of a step: the four DMA instructions, then one
+  // fragment read per two MFMAs, then the remaining MFMAs. Left alone, the
+  // scheduler sinks each read down to its first use in the next step and
+  // waits on it there.
+#define MOE_SCHEDULE()                                                                               \
+  do {                                                                                               \
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);                                               \
+    _Pragma("unroll") for (int g_ = 0; g_ < FM + FN; ++g_) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
+    }                                                                                                \
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2 * (FM + FN), 0);                         \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+  } while (0)
+
+  const int KT = K / BK;  // a multiple of 4: K is a multiple of 128
+  uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
+  MOE_DMA(S0, 0);
+  MOE_DMA(S1, 1);
+  MOE_DMA(S2, 2);
+  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): step 0 landed
+  __builtin_amdgcn_s_barrier();
+  MOE_READ(S0, af0, bf0);
+  for (int kt = 0; kt < KT; kt += 4) {
+    MOE_STEP(S1, S3, kt + 3, af0, bf0, af1, bf1);
+    MOE_STEP(S2, S0, kt + 4, af1, bf1, af0, bf0);
+    MOE_STEP(S3, S1, kt + 5, af0, bf0, af1, bf1);
+    MOE_STEP(S0, S2, kt + 6, af1, bf1, af0, bf0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the trailing DMAs have landed
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+#undef MOE_READ
+#undef MOE_STEP
+#undef MOE_SCHEDULE
+#undef MOE_DMA
+#undef MOE_LDS
+
+  // ---- epilogue in four 64-row quarters staged through S0 (16-byte chunk
+  // c of staged row r at position c ^ (r & 7))
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+  uint16_t* so = reinterpret_cast<uint16_t*>(S0);
+  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
+                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+  constexpr int OCH = BNO / 8;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    if (wm == qq / 2) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = (qq % 2) * 4 + ii;
+#pragma unroll
+        for (int j = 0; j < FNO; ++j) {
+          const int col = wn * WTO + j * 16 + c16;
+          const float bv = bias ? bias[col] : 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int srow = ii * 16 + q * 4 + r;  // row inside the quarter
+            float v;
+            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
+            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
+            else v = acc[i][j][r] + bv;
+            so[srow * BNO + (((col >> 3) ^ (srow & 7)) << 3) + (col & 7)] = f32_to_bf16(v);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < 64 * OCH; c += NTH) {
+      const int srow = c / OCH, cc = c % OCH;
+      const int row = qq * 64 + srow;
+      if (row < ti.rows)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
+            *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ fp32
 // Plain FMA tiles (64 x 64 outputs, 4 x 4 per thread) for fp32 layers.
 template <int EPI>
@@ -457,12 +641,25 @@ hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 // Tile configurations: rows x weight rows, wave grid.
 enum TileCfg { kTile128x128w4 = 0, kTile256x256w4 = 1, kTile256x256w8 = 2, kTile128x256w4 = 3, kTile256x128w4 = 4,
-               kTile128x128w8 = 5 };
-constexpr int tile_rows(int cfg) { return (cfg == kTile256x256w4 || cfg == kTile256x256w8 || cfg == kTile256x128w4) ? 256 : 128; }
+               kTile128x128w8 = 5, kTile256x256Dma = 6 };
+constexpr int tile_rows(int cfg) {
+  return (cfg == kTile256x256w4 || cfg == kTile256x256w8 || cfg == kTile256x128w4 || cfg == kTile256x256Dma) ? 256 : 128;
+}
+
+template <int EPI>
+hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? 128 : 256;
+  if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
+  int64_t grid = max_mtiles * (p.Nout / BNO);
+  grid = ceil_div(grid, kXcds) * kXcds;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
 
 // Configuration of the prefill path (many rows) and of the small-row path.
 #ifndef MOE_GEMM_BIG_CFG
-#define MOE_GEMM_BIG_CFG kTile256x256w8
+#define MOE_GEMM_BIG_CFG kTile256x256Dma
 #endif
 #ifndef MOE_GEMM_SMALL_CFG
 #define MOE_GEMM_SMALL_CFG kTile128x128w4
@@ -479,6 +676,10 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 template <int EPI, bool FP8>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  if (cfg == kTile256x256Dma) {
+    if constexpr (FP8) return run_bf16<256, 256, 2, 4, EPI, FP8>(p, max_mtiles, s);  // e4m3 is decoded in registers
+    else return run_dma<EPI>(p, max_mtiles, s);
+  }
   switch (cfg) {
     case kTile256x256w4: return run_bf16<256, 256, 2, 2, EPI, FP8>(p, max_mtiles, s);
     case kTile256x256w8: return run_bf16<256, 256, 2, 4, EPI, FP8>(p, max_mtiles, s);
