@@ -316,14 +316,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 }
 
 // ------------------------------------------------------------------ bf16 MFMA, LDS DMA pipeline
-// 256 x 256 tile, 8 waves (2 x 4, each 128 rows x 64 weight rows), k-steps of
-// 32 through four LDS stage buffers with three steps in flight. Operands move
-// from memory to LDS with global_load_lds (no VGPR staging, no ds_write): each
-// wave instruction writes 1 KB = 16 rows x 64 B of one stage, and the source
-// address each lane fetches puts 16-byte chunk c of row r at position
-// c ^ ((r >> 1) & 3): measured on gfx950, this is the placement of 64-byte rows
-// at which the MFMA operand reads (16 rows, one chunk each) run at the full
-// 256 B/clk of the LDS; (r >> 2) & 3 or no swizzle reach only half of it.
+// 256 x 256 tile, 8 waves (2 x 4, each 128 rows x 64 weight rows), k-stages of
+// 64 through two 64 KB LDS buffers. Operands move from memory to LDS with
+// global_load_lds (no VGPR staging, no ds_write): each wave instruction writes
+// 1 KB = 8 rows x 128 B, so every fetched 128-byte line is used whole, and the
+// source address each lane fetches puts 16-byte chunk c of row r at position
+// c ^ (r & 7), at which the MFMA operand reads (16 rows, one chunk each) run
+// conflict-free. A stage feeds two MFMA k-steps of 32; the fragments of the
+// next k-step are read from LDS while the current one's MFMAs run.
 // The stage buffers are separate LDS objects so that the compiler's wait for a
 // DMA store only blocks reads of that buffer. Before every barrier a wave waits
 // for its own LDS reads, so no DMA can overwrite data still being read.
@@ -332,15 +332,14 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr int BM = 256, BNB = 256, NTH = 512, WGN = 4;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int BNO = SWI ? BNB / 2 : BNB;
-  constexpr int BK = 32;                 // k per stage: one MFMA step, 64 B per row
+  constexpr int BK = 64;                 // k per stage, 128 B per row
+  constexpr int RB = BK * 2;             // row bytes in a stage
   constexpr int WTM = 128, WTB = 64;     // rows / weight rows per wave
   constexpr int WTO = SWI ? WTB / 2 : WTB;
   constexpr int FM = 8, FN = 4, FNO = WTO / 16;
-  constexpr int SBYTES = (BM + BNB) * BK * 2;  // 32 KB per stage
+  constexpr int SBYTES = (BM + BNB) * RB;  // 64 KB per stage
   __shared__ __attribute__((aligned(16))) char S0[SBYTES];
   __shared__ __attribute__((aligned(16))) char S1[SBYTES];
-  __shared__ __attribute__((aligned(16))) char S2[SBYTES];
-  __shared__ __attribute__((aligned(16))) char S3[SBYTES];
 
   TileInfo ti;
   if (!decode_tile<BM, BNO>(p, ti)) return;
@@ -351,38 +350,37 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
   const int K = p.K;
-  const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
-                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
-  const uint16_t* Bw = static_cast<const uint16_t*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride;
-  const uint16_t* B3w = SWI ? static_cast<const uint16_t*>(shared ? p.B3_s : p.B3_r) + static_cast<int64_t>(ew) * p.b_stride
-                            : Bw;
-
-  // This wave's four DMA instructions per stage: A rows [32 w, 32 w + 32) and
-  // weight rows [32 w, 32 w + 32), 16 rows each. Lane L of an instruction over
-  // rows [r0, r0 + 16) fills row r0 + L/4, position L%4 with logical chunk
-  // (L%4) ^ ((row >> 1) & 3).
-  const uint16_t* src[4];
+  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
+                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda * 2;
+  // This wave loads A rows and weight rows [32 w, 32 w + 32): four
+  // instructions of 8 rows each. For SwiGLU the weight rows [0, 128) of the
+  // tile are W1 rows and [128, 256) the matching W3 rows, so one wave's weight
+  // rows come from one matrix.
+  const int wr0 = wave * 32;
+  const bool w3 = SWI && wr0 >= BNO;
+  const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
+                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * K) * 2;
+  // Lane L of an instruction over rows [r0, r0 + 8) fills row r0 + L/8,
+  // position L%8 with logical chunk (L%8) ^ (row & 7); byte offsets are
+  // relative to the tile's first A row and the wave's first weight row.
+  uint32_t offa[4], offb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (i & 1) * 16 + wave * 32 + (lane >> 2);  // row inside the A (i < 2) or weight (i >= 2) tile
-    const int chunk = (lane & 3) ^ ((r >> 1) & 3);
-    if (i < 2) {
-      const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
-      src[i] = A + static_cast<int64_t>(rr) * p.lda + chunk * 8;
-    } else {
-      const bool w3 = SWI && r >= BNO;
-      src[i] = (w3 ? B3w : Bw) + static_cast<int64_t>(n0 + (w3 ? r - BNO : r)) * K + chunk * 8;
-    }
+    const int r = wr0 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
+    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(p.lda) * 2 + chunk * 16);
+    offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * K * 2 + chunk * 16);
   }
-  const int dst_a = wave * 2048, dst_b = BM * 64 + wave * 2048;  // byte offsets inside a stage
+  const int dst_a = wr0 * RB, dst_b = BM * RB + wr0 * RB;  // byte offsets inside a stage
 #define MOE_LDS(x) ((__attribute__((address_space(3))) void*)(x))
-#define MOE_DMA(S, kt)                                                                               \
+#define MOE_DMA(S, ks)                                                                               \
   do {                                                                                               \
-    const int ko_ = (kt) * BK;                                                                       \
-    __builtin_amdgcn_global_load_lds(src[0] + ko_, MOE_LDS(S + dst_a), 16, 0, 0);                    \
-    __builtin_amdgcn_global_load_lds(src[1] + ko_, MOE_LDS(S + dst_a + 1024), 16, 0, 0);             \
-    __builtin_amdgcn_global_load_lds(src[2] + ko_, MOE_LDS(S + dst_b), 16, 0, 0);                    \
-    __builtin_amdgcn_global_load_lds(src[3] + ko_, MOE_LDS(S + dst_b + 1024), 16, 0, 0);             \
+    const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                 \
+        __builtin_amdgcn_global_load_lds(A + offa[i_] + ko_, MOE_LDS(S + dst_a + i_ * 1024), 16, 0, 0); \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                 \
+        __builtin_amdgcn_global_load_lds(Bw + offb[i_] + ko_, MOE_LDS(S + dst_b + i_ * 1024), 16, 0, 0); \
   } while (0)
 
   floatx4_t acc[FM][FN];
@@ -391,42 +389,30 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // operand read offsets: rows start at multiples of 16, so (row >> 1) & 3 == (c16 >> 1) & 3
-  const int rd = (c16 * 64) + ((q ^ ((c16 >> 1) & 3)) * 16);
-#define MOE_READ(S, AF, BF)                                                                          \
+  // operand read offsets of the two k-steps of a stage: logical chunk
+  // u * 4 + q of row c16 (mod 8) sits at position (u * 4 + q) ^ (c16 & 7)
+  const int rd0 = c16 * RB + ((q ^ (c16 & 7)) * 16);
+  const int rd1 = c16 * RB + (((4 + q) ^ (c16 & 7)) * 16);
+#define MOE_READ(S, RD, AF, BF)                                                                      \
   do {                                                                                               \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
-        *reinterpret_cast<const uint4*>(S + (wm * WTM + i * 16) * 64 + rd);                          \
+        *reinterpret_cast<const uint4*>(S + (wm * WTM + i * 16) * RB + RD);                          \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                 \
       const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
                                            : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
                            : wn * WTB + j * 16;                                                      \
-      BF[j] = *reinterpret_cast<const uint4*>(S + BM * 64 + brow * 64 + rd);                         \
+      BF[j] = *reinterpret_cast<const uint4*>(S + BM * RB + brow * RB + RD);                         \
     }                                                                                                \
   } while (0)
-  // Step kt: wait until step kt+1 has landed (this wave's DMA, then the
-  // barrier for everyone's), refill the buffer of step kt-1 with step kt+3,
-  // read step kt+1's fragments, and run step kt's MFMAs on the fragments read
-  // during the previous step.
-#define MOE_STEP(SNEXT, SFILL, kfill, AC, BC, AN, BN)                                                \
+#define MOE_MFMA(AC, BC)                                                                             \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                     \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(AC[i], BC[j], acc[i][j])
+  // Issue order inside a k-step: DMA instructions (if any), then one fragment
+  // read per two MFMAs, then the remaining MFMAs. Left alone, the scheduler
+  // sinks each read down to its first use in the next k-step and waits there.
+#define MOE_SCHEDULE(NDMA)                                                                           \
   do {                                                                                               \
-    __builtin_amdgcn_s_waitcnt(0x0f74); /* vmcnt(4): only step kt+2's DMA may still fly */           \
-    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of step kt's buffer are done */      \
-    __builtin_amdgcn_s_barrier();                                                                    \
-    MOE_DMA(SFILL, min((kfill), KT - 1));                                                            \
-    MOE_READ(SNEXT, AN, BN);                                                                         \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                   \
-            mfma16x16x32(AC[i], BC[j], acc[i][j]);                                                   \
-    MOE_SCHEDULE();                                                                                  \
-  } while (0)
-  // Keep the issue order of a step: the four DMA instructions, then one
-  // fragment read per two MFMAs, then the remaining MFMAs. Left alone, the
-  // scheduler sinks each read down to its first use in the next step and
-  // waits on it there.
-#define MOE_SCHEDULE()                                                                               \
-  do {                                                                                               \
-    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);                                               \
+    if (NDMA) __builtin_amdgcn_sched_group_barrier(0x020, NDMA, 0);                                  \
     _Pragma("unroll") for (int g_ = 0; g_ < FM + FN; ++g_) {                                         \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
@@ -434,50 +420,68 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2 * (FM + FN), 0);                         \
     __builtin_amdgcn_sched_barrier(0);                                                               \
   } while (0)
+  // Stage ks lives in buffer SC; its first k-step's fragments are in af0/bf0.
+  // First half: read the second k-step's fragments, run the first's MFMAs.
+  // Second half: wait for stage ks+1 (this wave's DMA, then the barrier for
+  // everyone's, which also tells that all reads of SC are done), refill SC
+  // with stage ks+2, read stage ks+1's first fragments from SN, run the second
+  // k-step's MFMAs.
+#define MOE_STAGE(SC, SN, ks)                                                                        \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): af0/bf0 have arrived */                       \
+    MOE_READ(SC, rd1, af1, bf1);                                                                     \
+    MOE_MFMA(af0, bf0);                                                                              \
+    MOE_SCHEDULE(0);                                                                                 \
+    __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0): stage ks+1 landed */                            \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of SC are done */                    \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA(SC, min((ks) + 2, KS - 1));                                                              \
+    MOE_READ(SN, rd0, af0, bf0);                                                                     \
+    MOE_MFMA(af1, bf1);                                                                              \
+    MOE_SCHEDULE(8);                                                                                 \
+  } while (0)
 
-  const int KT = K / BK;  // a multiple of 4: K is a multiple of 128
+  const int KS = K / BK;  // even: K is a multiple of 128
   uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
   MOE_DMA(S0, 0);
   MOE_DMA(S1, 1);
-  MOE_DMA(S2, 2);
-  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): step 0 landed
+  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): stage 0 landed
   __builtin_amdgcn_s_barrier();
-  MOE_READ(S0, af0, bf0);
-  for (int kt = 0; kt < KT; kt += 4) {
-    MOE_STEP(S1, S3, kt + 3, af0, bf0, af1, bf1);
-    MOE_STEP(S2, S0, kt + 4, af1, bf1, af0, bf0);
-    MOE_STEP(S3, S1, kt + 5, af0, bf0, af1, bf1);
-    MOE_STEP(S0, S2, kt + 6, af1, bf1, af0, bf0);
+  MOE_READ(S0, rd0, af0, bf0);
+  for (int ks = 0; ks < KS; ks += 2) {
+    MOE_STAGE(S0, S1, ks);
+    MOE_STAGE(S1, S0, ks + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the trailing DMAs have landed
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
-#undef MOE_READ
-#undef MOE_STEP
+#undef MOE_STAGE
 #undef MOE_SCHEDULE
+#undef MOE_MFMA
+#undef MOE_READ
 #undef MOE_DMA
 #undef MOE_LDS
 
-  // ---- epilogue in four 64-row quarters staged through S0 (16-byte chunk
-  // c of staged row r at position c ^ (r & 7))
+  // ---- epilogue in two 128-row halves staged through S0 (16-byte chunk c of
+  // staged row r at position c ^ (r & 7))
   const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
   uint16_t* so = reinterpret_cast<uint16_t*>(S0);
   uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
   constexpr int OCH = BNO / 8;
+  static_assert(WTM * BNO * 2 <= SBYTES, "output staging exceeds a stage buffer");
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    if (wm == qq / 2) {
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = (qq % 2) * 4 + ii;
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FNO; ++j) {
           const int col = wn * WTO + j * 16 + c16;
           const float bv = bias ? bias[col] : 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int srow = ii * 16 + q * 4 + r;  // row inside the quarter
+            const int srow = i * 16 + q * 4 + r;  // row inside the half
             float v;
             if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
             else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
@@ -488,9 +492,9 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
       }
     }
     __syncthreads();
-    for (int c = tid; c < 64 * OCH; c += NTH) {
+    for (int c = tid; c < WTM * OCH; c += NTH) {
       const int srow = c / OCH, cc = c % OCH;
-      const int row = qq * 64 + srow;
+      const int row = h * WTM + srow;
       if (row < ti.rows)
         *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
             *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
