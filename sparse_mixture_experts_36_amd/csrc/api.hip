@@ -102,6 +102,7 @@ struct FfnWs {
   moe::GroupDesc* groups;
   int32_t* tile_start;
   float* part;
+  float* split_part;
 };
 FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
@@ -114,6 +115,9 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   if (moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T))
     w.part = c.take<float>(
         moe::skinny_part_floats(s.T, s.d, s.d_ff, s.n_experts, s.n_shared, s.act, routed_row_cap(s)));
+  w.split_part = nullptr;
+  if (moe::uses_prefill_gemm(s.act_dtype, s.w_dtype, routed_row_cap(s), s.n_shared, s.T))
+    w.split_part = c.take<float>(static_cast<size_t>(moe::kSplitPartFloats));
   return w;
 }
 
@@ -273,6 +277,7 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* off
   a.groups = fw.groups;
   a.tile_start = fw.tile_start;
   a.part = fw.part;
+  a.split_part = fw.split_part;
   return a;
 }
 

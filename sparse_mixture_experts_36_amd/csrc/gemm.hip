@@ -54,6 +54,8 @@ struct GemmParams {
   int32_t n_routed, n_groups;
   const GroupDesc* groups;
   const int32_t* tile_start;  // [n_groups+1] row-tile prefix
+  float* split_part;          // fp32 partial tiles of the k-split tail, or null (no split)
+  int32_t ncu;                // compute units of the device
 };
 
 enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_PLAIN = 2 };
@@ -73,17 +75,11 @@ struct TileInfo {
   GroupDesc gd;
 };
 
-// Maps this workgroup to a tile; false when it has none.
+// Tile L of the launch: tiles run group by group, n-tile by n-tile, with the
+// row tile fastest, so that consecutive tiles share a weight tile.
 template <int BM, int BNO>
-__device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
+__device__ __forceinline__ void tile_from_linear(const GemmParams& p, int L, TileInfo& ti) {
   const int nt = p.Nout / BNO;
-  const int total = p.tile_start[p.n_groups] * nt;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int bid = blockIdx.x;
-  const int slot = bid / kXcds;
-  if (slot >= per_xcd) return false;
-  const int L = (bid % kXcds) * per_xcd + slot;
-  if (L >= total) return false;
   const int g = find_group(p.tile_start, p.n_groups, L / nt);
   const int base = p.tile_start[g] * nt;
   const int mt = p.tile_start[g + 1] - p.tile_start[g];
@@ -93,7 +89,45 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   ti.m_tile = local % mt;
   ti.gd = p.groups[g];
   ti.rows = min(BM, ti.gd.rows - ti.m_tile * BM);
+}
+
+// Maps this workgroup to a tile; false when it has none. Consecutive tiles go
+// to one XCD (workgroups are dealt to the 8 XCDs round-robin), so the tiles
+// sharing a weight tile also share that XCD's L2.
+template <int BM, int BNO>
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
+  const int total = p.tile_start[p.n_groups] * (p.Nout / BNO);
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int bid = blockIdx.x;
+  const int slot = bid / kXcds;
+  if (slot >= per_xcd) return false;
+  const int L = (bid % kXcds) * per_xcd + slot;
+  if (L >= total) return false;
+  tile_from_linear<BM, BNO>(p, L, ti);
   return true;
+}
+
+// k-split of the last, partial round of tiles. With r = total mod ncu tiles
+// left after the full rounds, and r <= ncu / 2, each of those r tiles is cut
+// into s k-chunks (s * r <= ncu), run as s * r workgroups that write fp32
+// partial tiles; a fix-up pass sums each tile's chunks in chunk order and
+// applies the epilogue. The result then does not depend on timing.
+constexpr int kSplitUnits = 256;  // partial tiles the workspace holds
+constexpr int kMaxSplit = 8;
+struct SplitPlan {
+  int total, full, r, s;
+};
+template <int BNO>
+__device__ __forceinline__ SplitPlan split_plan(const GemmParams& p, int ks_pairs) {
+  SplitPlan sp;
+  sp.total = p.tile_start[p.n_groups] * (p.Nout / BNO);
+  sp.r = sp.total % p.ncu;
+  sp.s = 1;
+  if (p.split_part && sp.r > 0 && 2 * sp.r <= p.ncu)
+    sp.s = min(min(p.ncu / sp.r, kMaxSplit), min(kSplitUnits / sp.r, ks_pairs));
+  if (sp.s < 2) sp.s = 1;
+  sp.full = sp.s > 1 ? sp.total - sp.r : sp.total;
+  return sp;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA
@@ -327,29 +361,114 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 // The stage buffers are separate LDS objects so that the compiler's wait for a
 // DMA store only blocks reads of that buffer. Before every barrier a wave waits
 // for its own LDS reads, so no DMA can overwrite data still being read.
-template <int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
-  constexpr int BM = 256, BNB = 256, NTH = 512, WGN = 4;
-  constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int BNO = SWI ? BNB / 2 : BNB;
-  constexpr int BK = 64;                 // k per stage, 128 B per row
-  constexpr int RB = BK * 2;             // row bytes in a stage
-  constexpr int WTM = 128, WTB = 64;     // rows / weight rows per wave
-  constexpr int WTO = SWI ? WTB / 2 : WTB;
-  constexpr int FM = 8, FN = 4, FNO = WTO / 16;
-  constexpr int SBYTES = (BM + BNB) * RB;  // 64 KB per stage
-  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
-  __shared__ __attribute__((aligned(16))) char S1[SBYTES];
+namespace dma {
+constexpr int BM = 256, BNB = 256, NTH = 512, WGN = 4;
+constexpr int BK = 64;              // k per stage, 128 B per row
+constexpr int RB = BK * 2;          // row bytes in a stage
+constexpr int WTM = 128, WTB = 64;  // rows / weight rows per wave
+constexpr int FM = 8, FN = 4;
+constexpr int SBYTES = (BM + BNB) * RB;  // 64 KB per stage
+constexpr int bno(int epi) { return epi == EPI_SWIGLU ? BNB / 2 : BNB; }
+}  // namespace dma
 
-  TileInfo ti;
-  if (!decode_tile<BM, BNO>(p, ti)) return;
+// Epilogue of a 256 x 256 DMA tile held as per-wave MFMA fragments: bias and
+// activation (or the SwiGLU product of the W1 and W3 halves), bf16, and
+// 16-byte stores through an LDS staging buffer of 64 KB, in two 128-row
+// halves (16-byte chunk c of staged row r at position c ^ (r & 7)).
+template <int EPI>
+__device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
+                                               floatx4_t (&acc)[dma::FM][dma::FN], char* stage) {
+  using namespace dma;
+  constexpr int BNO = bno(EPI);
+  constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
+  constexpr int FNO = WTO / 16;
+  static_assert(WTM * BNO * 2 <= SBYTES, "output staging exceeds a stage buffer");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
   const bool shared = ti.g >= p.n_routed;
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+  uint16_t* so = reinterpret_cast<uint16_t*>(stage);
+  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
+                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
+  constexpr int OCH = BNO / 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FNO; ++j) {
+          const int col = wn * WTO + j * 16 + c16;
+          const float bv = bias ? bias[col] : 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int srow = i * 16 + q * 4 + r;  // row inside the half
+            float v;
+            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
+            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
+            else v = acc[i][j][r] + bv;
+            so[srow * BNO + (((col >> 3) ^ (srow & 7)) << 3) + (col & 7)] = f32_to_bf16(v);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < WTM * OCH; c += NTH) {
+      const int srow = c / OCH, cc = c % OCH;
+      const int row = h * WTM + srow;
+      if (row < ti.rows)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
+            *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 partial tile of a k-chunk, in fragment order: fragment (wave, i, j) is
+// 64 lanes x 4 floats, 1 KB contiguous.
+__device__ __forceinline__ float* dma_part_frag(float* part, int unit, int wave, int i, int j) {
+  using namespace dma;
+  return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * FM + i) * FN + j) * 256;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
+  using namespace dma;
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int BNO = bno(EPI);
+  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
+  __shared__ __attribute__((aligned(16))) char S1[SBYTES];
+
   const int K = p.K;
+  const int KS = K / BK;  // even: K is a multiple of 128
+  TileInfo ti;
+  int ks_begin = 0, ks_end = KS, unit = -1;
+  {
+    const SplitPlan sp = split_plan<BNO>(p, KS / 2);
+    const int bid = blockIdx.x;
+    if (sp.s == 1) {
+      if (!decode_tile<BM, BNO>(p, ti)) return;
+    } else if (bid < sp.full) {  // full rounds; sp.full is a multiple of the XCD count
+      const int per_xcd = sp.full / kXcds;
+      tile_from_linear<BM, BNO>(p, (bid % kXcds) * per_xcd + bid / kXcds, ti);
+    } else {
+      unit = bid - sp.full;
+      if (unit >= sp.r * sp.s) return;
+      const int c = unit % sp.s;
+      tile_from_linear<BM, BNO>(p, sp.full + unit / sp.s, ti);
+      ks_begin = 2 * ((c * (KS / 2)) / sp.s);  // chunks of whole stage pairs
+      ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
+    }
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int q = lane >> 4, c16 = lane & 15;
+  const bool shared = ti.g >= p.n_routed;
+  const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
+  const int n0 = ti.n_tile * BNO;
   const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
                   (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda * 2;
   // This wave loads A rows and weight rows [32 w, 32 w + 32): four
@@ -435,20 +554,19 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0): stage ks+1 landed */                            \
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of SC are done */                    \
     __builtin_amdgcn_s_barrier();                                                                    \
-    MOE_DMA(SC, min((ks) + 2, KS - 1));                                                              \
+    MOE_DMA(SC, min((ks) + 2, ks_end - 1));                                                          \
     MOE_READ(SN, rd0, af0, bf0);                                                                     \
     MOE_MFMA(af1, bf1);                                                                              \
     MOE_SCHEDULE(8);                                                                                 \
   } while (0)
 
-  const int KS = K / BK;  // even: K is a multiple of 128
   uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
-  MOE_DMA(S0, 0);
-  MOE_DMA(S1, 1);
-  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): stage 0 landed
+  MOE_DMA(S0, ks_begin);
+  MOE_DMA(S1, ks_begin + 1);
+  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): the first stage landed
   __builtin_amdgcn_s_barrier();
   MOE_READ(S0, rd0, af0, bf0);
-  for (int ks = 0; ks < KS; ks += 2) {
+  for (int ks = ks_begin; ks < ks_end; ks += 2) {
     MOE_STAGE(S0, S1, ks);
     MOE_STAGE(S1, S0, ks + 1);
   }
@@ -462,45 +580,45 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
 #undef MOE_DMA
 #undef MOE_LDS
 
-  // ---- epilogue in two 128-row halves staged through S0 (16-byte chunk c of
-  // staged row r at position c ^ (r & 7))
-  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
-  uint16_t* so = reinterpret_cast<uint16_t*>(S0);
-  uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
-                (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
-  constexpr int OCH = BNO / 8;
-  static_assert(WTM * BNO * 2 <= SBYTES, "output staging exceeds a stage buffer");
+  if (unit >= 0) {  // a k-chunk: raw fp32 partial sums, summed by the fix-up pass
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FNO; ++j) {
-          const int col = wn * WTO + j * 16 + c16;
-          const float bv = bias ? bias[col] : 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int srow = i * 16 + q * 4 + r;  // row inside the half
-            float v;
-            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
-            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
-            else v = acc[i][j][r] + bv;
-            so[srow * BNO + (((col >> 3) ^ (srow & 7)) << 3) + (col & 7)] = f32_to_bf16(v);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    for (int c = tid; c < WTM * OCH; c += NTH) {
-      const int srow = c / OCH, cc = c % OCH;
-      const int row = h * WTM + srow;
-      if (row < ti.rows)
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
-            *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
-    }
-    __syncthreads();
+      for (int j = 0; j < FN; ++j)
+        *reinterpret_cast<floatx4_t*>(dma_part_frag(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
+    return;
   }
+  dma_store_tile<EPI>(p, ti, acc, S0);
+}
+
+// Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
+// partial tiles in chunk order and runs the tile epilogue.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_split_fixup_kernel(GemmParams p) {
+  using namespace dma;
+  constexpr int BNO = bno(EPI);
+  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
+  const SplitPlan sp = split_plan<BNO>(p, p.K / BK / 2);
+  const int b = blockIdx.x;
+  if (sp.s == 1 || b >= sp.r) return;
+  TileInfo ti;
+  tile_from_linear<BM, BNO>(p, sp.full + b, ti);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag(p.split_part, b * sp.s, wave, i, j) + lane * 4);
+  for (int c = 1; c < sp.s; ++c) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag(p.split_part, b * sp.s + c, wave, i, j) +
+                                                         lane * 4);
+  }
+  dma_store_tile<EPI>(p, ti, acc, S0);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -652,12 +770,20 @@ constexpr int tile_rows(int cfg) {
 
 template <int EPI>
 hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? 128 : 256;
+  constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
   grid = ceil_div(grid, kXcds) * kXcds;
   if (grid <= 0) return hipSuccess;
+  // a k-split tail runs at most total - r + kSplitUnits workgroups
+  if (p.split_part) grid += kSplitUnits;
   hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
+  if (p.split_part) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // split tiles: r <= kSplitUnits / 2 (each is cut at least in two)
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -694,6 +820,19 @@ hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t
   }
 }
 
+// Compute units of the current device, cached per device.
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
@@ -716,6 +855,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   const bool swi = (a.act == 1);
 
   GemmParams p{};
+  p.split_part = a.split_part;
+  p.ncu = device_cus();
   p.n_routed = a.n_routed;
   p.n_groups = G;
   p.tile_start = a.tile_start;

@@ -83,7 +83,11 @@ struct FfnArgs {
   GroupDesc* groups;          // [2][n_routed + n_shared] (workspace)
   int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
+  float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null
 };
+// fp32 floats of the prefill path's k-split partial tiles: 256 tiles of 256 x 256
+constexpr int64_t kSplitPartFloats = 256LL * 256 * 256;
+
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 
 // Decode-sized layers (few rows per expert) stream expert weights instead of
@@ -91,6 +95,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 constexpr int64_t kSkinnyMaxRows = 256;
 inline bool use_skinny(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shared, int64_t T) {
   return act_dtype == 1 && routed_row_cap + n_shared * T <= kSkinnyMaxRows;
+}
+// whether a layer's FFN may take the bf16 prefill GEMM, which uses the k-split
+// partial tiles
+inline bool uses_prefill_gemm(int32_t act_dtype, int32_t w_dtype, int64_t routed_row_cap, int32_t n_shared,
+                              int64_t T) {
+  return act_dtype == 1 && w_dtype == 1 && !use_skinny(act_dtype, routed_row_cap, n_shared, T);
 }
 // fp32 partial-sum floats the decode path needs (0 when no GEMM is split)
 size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,

@@ -160,6 +160,14 @@ FFN_CASES = [
     dict(T=64, N=16, k=1, act=gen.GELU, d=256, d_ff=512, biases=True),
     dict(T=40, N=32, k=4, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=1536, wdt=gen.E4M3),
+    # prefill-sized calls (>= 2048 expert rows): the 256 x 256 LDS-DMA tiles.
+    # With 256 CUs, a launch whose last round holds r <= 128 tiles cuts those
+    # tiles along k and sums the chunks in a fix-up pass; the comments give
+    # (tiles, split) of the up and down GEMM.
+    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512),                  # (~64, 4), (~32, 4)
+    dict(T=1100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=4096),                 # (512, none), (16, 8)
+    dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True),  # (~96, 2), (~24, 8)
+    dict(T=1024, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),    # (~96, 2), (~48, 2)
 ]
 
 
