@@ -33,6 +33,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_36_amd", "csrc", "gemm.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm-dma-up-swiglu_mixtral-prefill_hbm-traffic.md")
+COPY_BYTES = 1 << 30        # the calibration kernel reads and writes this many bytes
 
 
 def log(*a):
@@ -70,6 +73,43 @@ def up_flops_per_pair(wl) -> float:
 
 def ffn_flops_per_pair(wl) -> float:
     return up_flops_per_pair(wl) + 2.0 * wl.d * wl.d_ff
+
+
+def measured_traffic():
+    """HBM bytes per launch of the up GEMM kernel from the committed PMC summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when the summary is missing or was taken on another version of the GEMM
+    source than the one built here."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("gemm.hip sha256") != src or "hbm bytes per launch" not in fields:
+        return None
+    return int(float(fields["hbm bytes per launch"]))
+
+
+def copy_calibration():
+    """A plain streaming kernel of known traffic (x * 1 over 1 GiB of fp32:
+    1 GiB read, 1 GiB written), run under rocprofv3 --pmc to scale FETCH_SIZE
+    and WRITE_SIZE to bytes."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "elementwise mul by 1.0, fp32", "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def run_gpu(wl, inp, steps, warmup):
@@ -187,6 +227,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode shapes (T = 1, 16, 64) on the prefill weights; prints their JSON")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the copy kernel that scales the PMC byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -198,8 +240,11 @@ def main():
     import gen
     import sparse_mixture_experts_36_amd as moe
 
-    moe.lib()  # raises when the HIP library is missing: there is no fallback
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    moe.lib()  # raises when the HIP library is missing: there is no fallback
     wl = gen.WORKLOADS[args.workload]
     log(f"workload {wl}")
     t = time.perf_counter()
@@ -240,7 +285,8 @@ def main():
                    "w_dtype": {0: "f32", 1: "bf16", 2: "e4m3"}[wl.w_dtype], "parallelism": "single-gpu"},
         "roofline": {"kernel": "grouped up GEMM + fused activation", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if wl.name == "mixtral-prefill-bf16" else None,
                      "algorithmic_flops_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4)},
         "layer": {"mfma_frac": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "ffn_mfma_frac": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
