@@ -112,6 +112,15 @@ typedef struct {
   const void* sw3;        /* [n_shared][d_ff][d] (SwiGLU) */
   const void* sw2;        /* [n_shared][d][d_ff] */
   const float* sw_scale;  /* [n_shared][3] for MOE_FP8_E4M3 */
+  /* Row pitches of the expert matrices, in elements (0 = contiguous rows).
+   * ld_up applies to w1, w3, sw1, sw3: row j of expert e starts at element
+   * (e * d_ff + j) * ld_up, ld_up >= d. ld_down applies to w2 and sw2:
+   * (e * d + j) * ld_down, ld_down >= d_ff. Nonzero pitches must be multiples
+   * of 16. A pitch of d + 64 (resp. d_ff + 64) keeps the rows of one k-column
+   * from falling into the same few L2 channels when d or d_ff is a multiple
+   * of 4096 and is the layout the prefill GEMM runs fastest on. */
+  int64_t ld_up;
+  int64_t ld_down;
 } moe_weights;
 
 /* Router statistics (aigrafen L_aux equation and `latest` dict; starphix

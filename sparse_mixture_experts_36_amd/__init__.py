@@ -34,10 +34,10 @@ class Shape(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    """moe_weights (device pointers)"""
+    """moe_weights (device pointers, then the row pitches of the expert matrices)"""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2",
-                 "sw_scale")]
+                 "sw_scale")] + [("ld_up", ctypes.c_int64), ("ld_down", ctypes.c_int64)]
 
 
 class Stats(ctypes.Structure):
@@ -203,9 +203,43 @@ def timing_stop() -> dict:
     return {s: (ms[i], n[i]) for i, s in enumerate(STAGES)}
 
 
+def _row_pitch(ts, what):
+    """Row pitch (elements) shared by 3-D expert matrices [E][rows][cols] whose
+    rows may be padded (a view [..., :cols] of a wider allocation); 0 if none."""
+    ld = 0
+    for t in ts:
+        if t is None:
+            continue
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{what}: expert matrices must be [E][rows][cols] with unit column stride and "
+                             f"no gap between experts")
+        if ld and t.stride(1) != ld:
+            raise ValueError(f"{what}: all matrices must share one row pitch")
+        ld = t.stride(1)
+    return ld
+
+
 def weights_struct(t: dict) -> Weights:
-    """moe_weights from a dict of device tensors (missing keys are NULL)."""
-    return Weights(**{k: _ptr(v) for k, v in t.items() if v is not None})
+    """moe_weights from a dict of device tensors (missing keys are NULL). The
+    row pitches come from the strides of w1/w3/sw1/sw3 and of w2/sw2."""
+    w = Weights(**{k: _ptr(v) for k, v in t.items() if v is not None})
+    w.ld_up = _row_pitch([t.get(k) for k in ("w1", "w3", "sw1", "sw3")], "w1/w3/sw1/sw3")
+    w.ld_down = _row_pitch([t.get(k) for k in ("w2", "sw2")], "w2/sw2")
+    return w
+
+
+def padded(t, pad: int = 64):
+    """A copy of expert matrices [E][rows][cols] whose rows are `pad` elements
+    longer than cols (a view of the wider allocation): the layout the prefill
+    GEMM reads fastest when cols is a multiple of 4096."""
+    import torch
+    if t is None:
+        return None
+    E, R, C = t.shape
+    buf = torch.empty((E, R, C + pad), dtype=t.dtype, device=t.device)
+    v = buf[:, :, :C]
+    v.copy_(t)
+    return v
 
 
 @dataclass

@@ -108,7 +108,7 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
   const size_t hrows = static_cast<size_t>(routed_row_cap(s) + static_cast<int64_t>(s.n_shared) * s.T);
   FfnWs w;
-  w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff) * act_bytes(s.act_dtype));
+  w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff + moe::kActPad) * act_bytes(s.act_dtype));
   w.groups = c.take<moe::GroupDesc>(2 * G);
   w.tile_start = c.take<int32_t>(G + 1);
   w.part = nullptr;
@@ -138,7 +138,7 @@ FwdWs carve_fwd(Carver& c, const moe_shape& s) {
   w.inv_map = c.take<int32_t>(T * k);
   w.offsets = c.take<int32_t>(s.n_experts + 1);
   w.perm_token = c.take<int32_t>(T * k);
-  w.x_perm = c.take<char>(cap * rowb);
+  w.x_perm = c.take<char>(cap * static_cast<size_t>(s.d + moe::kActPad) * act_bytes(s.act_dtype));
   w.y_perm = c.take<char>(cap * rowb);
   w.y_shared = c.take<char>(static_cast<size_t>(s.n_shared) * T * rowb);
   return w;
@@ -207,8 +207,8 @@ moe::RouteArgs route_args(const moe_shape& s, const void* x, const void* w_route
 }
 
 moe::PermuteArgs perm_args(const moe_shape& s, const int32_t* topk_idx, const void* x, int32_t* offsets,
-                           int32_t* perm_token, int32_t* inv_map, void* x_perm, const moe_stats* st,
-                           const PermWs& w) {
+                           int32_t* perm_token, int32_t* inv_map, void* x_perm, int64_t ld_x_perm,
+                           const moe_stats* st, const PermWs& w) {
   moe::PermuteArgs a{};
   a.T = s.T;
   a.d = s.d;
@@ -222,6 +222,7 @@ moe::PermuteArgs perm_args(const moe_shape& s, const int32_t* topk_idx, const vo
   a.perm_token = perm_token;
   a.inv_map = inv_map;
   a.x_perm = x_perm;
+  a.ld_out = ld_x_perm;
   a.kept = (st && st->kept) ? st->kept : w.kept;
   a.n_dropped = (st && st->n_dropped) ? st->n_dropped : w.n_dropped;
   a.block_cnt = w.block_cnt;
@@ -243,11 +244,13 @@ moe_status check_weights(const moe_shape& s, const moe_weights* w, bool need_rou
   const void* ptrs[] = {w->w_router, w->w1, w->w3, w->w2, w->sw1, w->sw3, w->sw2};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (w->ld_up != 0 && (w->ld_up < s.d || w->ld_up % 16 != 0)) return MOE_ERR_INVALID_ARG;
+  if (w->ld_down != 0 && (w->ld_down < s.d_ff || w->ld_down % 16 != 0)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
-moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* offsets, const void* x,
-                      const moe_weights* w, void* y_perm, void* y_shared, const FfnWs& fw) {
+moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm, const int32_t* offsets,
+                      const void* x, const moe_weights* w, void* y_perm, void* y_shared, const FfnWs& fw) {
   moe::FfnArgs a{};
   a.T = s.T;
   a.d = s.d;
@@ -260,6 +263,10 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, const int32_t* off
   a.routed_row_cap = static_cast<int32_t>(routed_row_cap(s));
   a.offsets = offsets;
   a.x_perm = x_perm;
+  a.ld_xp = ld_x_perm;
+  a.ld_h = s.d_ff + moe::kActPad;
+  a.ld_up = w->ld_up ? w->ld_up : s.d;
+  a.ld_down = w->ld_down ? w->ld_down : s.d_ff;
   a.x = x;
   a.w1 = w->w1;
   a.w3 = w->w3;
@@ -419,7 +426,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, const vo
   Carver c{static_cast<char*>(ws)};
   const PermWs w = carve_perm(c, *shape);
   return hip_status(moe::launch_permute(
-      perm_args(*shape, topk_idx, x, expert_offsets, perm_token, inv_map, x_perm, stats, w), stream));
+      perm_args(*shape, topk_idx, x, expert_offsets, perm_token, inv_map, x_perm, shape->d, stats, w), stream));
 }
 
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* expert_offsets,
@@ -436,7 +443,8 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int
   Carver c{static_cast<char*>(ws)};
   const FfnWs fw = carve_ffn(c, *shape);
   return hip_status(
-      moe::launch_grouped_ffn(ffn_args(*shape, x_perm, expert_offsets, x, weights, y_perm, y_shared, fw), stream));
+      moe::launch_grouped_ffn(ffn_args(*shape, x_perm, shape->d, expert_offsets, x, weights, y_perm, y_shared, fw),
+                              stream));
 }
 
 moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_map, const float* topk_w,
@@ -474,6 +482,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   const PermWs pw = carve_perm(c, s);
   const FfnWs fw = carve_ffn(c, s);
   const FwdWs w = carve_fwd(c, s);
+  const int64_t ld_xp = s.d + moe::kActPad;  // the internal x_perm has a padded row pitch
   if (!logits) logits = w.logits;
   if (!topk_idx) topk_idx = w.topk_idx;
   if (!topk_w) topk_w = w.topk_w;
@@ -484,10 +493,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   hipError_t e = moe::launch_route(
       route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
   if (e == hipSuccess)
-    e = moe::launch_permute(perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, w.x_perm, stats, pw),
-                            stream);
+    e = moe::launch_permute(
+        perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, w.x_perm, ld_xp, stats, pw), stream);
   if (e == hipSuccess)
-    e = moe::launch_grouped_ffn(ffn_args(s, w.x_perm, expert_offsets, x, weights, w.y_perm, w.y_shared, fw), stream);
+    e = moe::launch_grouped_ffn(
+        ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw), stream);
   if (e == hipSuccess) {
     moe::CombineArgs a{};
     a.T = s.T;

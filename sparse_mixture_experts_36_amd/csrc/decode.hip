@@ -31,7 +31,8 @@ constexpr int KU = 2;          // steps whose loads are issued together
 struct StreamParams {
   const uint16_t* A_r;       // routed A rows (x_perm or h)
   const uint16_t* A_s;       // shared A rows (x or h)
-  int64_t lda;
+  int64_t lda_r, lda_s;      // A row pitches (elements)
+  int64_t ldb;               // weight row pitch (elements)
   const char* B_r;           // weights of routed experts (bytes)
   const char* B3_r;          // W3 (SwiGLU up) or null
   const char* B_s;
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   const int64_t eoff = static_cast<int64_t>(ew) * p.b_stride * WB;
   const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
   const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
-  const uint16_t* A = (shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * p.lda;
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
+  const uint16_t* A = (shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda;
   const int K = p.K, ks = K / p.splits;
   const int kbeg = sp * ks, nsteps = ks / KC;
   // weight rows of the two tiles, and the output / partial columns they feed
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   for (int j = 0; j < FN; ++j) {
     const int n = swi ? n0 + c16 : n0 + j * 16 + c16;
     wbase[j] = (swi && j == 1) ? B3w : Bw;
-    woff[j] = static_cast<int64_t>(n) * K + kbeg + q * 32;
+    woff[j] = static_cast<int64_t>(n) * p.ldb + kbeg + q * 32;
   }
   float s_a = 1.f, s_b = 1.f;
   if (FP8) {
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int arow = min(r0 + rb * 16 + c16, gd.rows - 1);  // rows past the group compute garbage
-      ap[rb] = A + static_cast<int64_t>(arow) * p.lda + kbeg + q * 32;
+      ap[rb] = A + static_cast<int64_t>(arow) * lda + kbeg + q * 32;
     }
     floatx4_t acc[RB][FN];
 #pragma unroll
@@ -317,25 +319,25 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.n_routed = a.n_routed;
   p.n_groups = G;
   p.rows_total = a.routed_row_cap + a.n_shared * static_cast<int32_t>(a.T);
-  constexpr int WB2 = 1;  // byte pointers below
-  (void)WB2;
 
   // ---- up: [rows][d] x W1 (W3)^T -> h [rows][d_ff]
   p.A_r = static_cast<const uint16_t*>(a.x_perm);
   p.A_s = static_cast<const uint16_t*>(a.x);
-  p.lda = a.d;
+  p.lda_r = a.ld_xp;
+  p.lda_s = a.d;
   p.B_r = static_cast<const char*>(a.w1);
   p.B3_r = static_cast<const char*>(a.w3);
   p.B_s = static_cast<const char*>(a.sw1);
   p.B3_s = static_cast<const char*>(a.sw3);
-  p.b_stride = a.d_ff * a.d;
+  p.ldb = a.ld_up;
+  p.b_stride = a.d_ff * a.ld_up;
   p.bias = swi ? nullptr : a.b1;
   p.scale_r = a.w_scale;
   p.scale_s = a.sw_scale;
   p.scale_col = 0;
   p.C_r = static_cast<uint16_t*>(a.h);
   p.C_s = static_cast<uint16_t*>(a.h);
-  p.ldc = a.d_ff;
+  p.ldc = a.ld_h;
   p.c_shared_base = 0;  // up group descriptors already place shared rows after cap
   p.K = static_cast<int32_t>(a.d);
   p.Nout = static_cast<int32_t>(a.d_ff);
@@ -358,12 +360,14 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   // ---- down: h [rows][d_ff] x W2^T -> y [rows][d]
   p.A_r = static_cast<const uint16_t*>(a.h);
   p.A_s = static_cast<const uint16_t*>(a.h);
-  p.lda = a.d_ff;
+  p.lda_r = a.ld_h;
+  p.lda_s = a.ld_h;
   p.B_r = static_cast<const char*>(a.w2);
   p.B3_r = nullptr;
   p.B_s = static_cast<const char*>(a.sw2);
   p.B3_s = nullptr;
-  p.b_stride = a.d * a.d_ff;
+  p.ldb = a.ld_down;
+  p.b_stride = a.d * a.ld_down;
   p.bias = swi ? nullptr : a.b2;
   p.scale_col = 2;
   p.C_r = static_cast<uint16_t*>(a.y_perm);

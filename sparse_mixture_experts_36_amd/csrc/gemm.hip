@@ -37,12 +37,13 @@ constexpr int kXcds = 8;
 struct GemmParams {
   const void* A_r;        // routed A rows
   const void* A_s;        // shared A rows
-  int64_t lda;            // = K
+  int64_t lda_r, lda_s;   // A row pitches (elements, >= K)
   const void* B_r;        // routed weights [n_routed][Nout][K] (W1 or W2)
   const void* B3_r;       // routed W3 (SwiGLU up GEMM) or null
   const void* B_s;        // shared weights
   const void* B3_s;
-  int64_t b_stride;       // elements per expert matrix = Nout * K
+  int64_t ldb;            // weight row pitch (elements, >= K)
+  int64_t b_stride;       // elements per expert matrix = Nout * ldb
   const float* bias;      // [n_routed][Nout] or null (routed GELU experts only)
   const float* scale_r;   // [n_routed][3] (e4m3) or null
   const float* scale_s;   // [n_shared][3]
@@ -175,8 +176,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   const int n0 = ti.n_tile * BNO;
   const int K = p.K;
 
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
   const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
-                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
+                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda;
   constexpr int WB = FP8 ? 1 : 2;  // weight bytes
   const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride * WB;
   const char* B3w = SWI ? static_cast<const char*>(shared ? p.B3_s : p.B3_r) +
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
     const int kc = c & 7;
     a_dst[i] = r * S + ((kc ^ (r & 7)) * 8);
     if (r > ti.rows - 1) r = ti.rows - 1;  // rows past the group compute garbage, never stored
-    a_off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.lda) + kc * 8;
+    a_off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(lda) + kc * 8;
   }
   // For SwiGLU the W3 rows are [BNO, 2 BNO). When that split falls on a chunk
   // boundary of every thread (chunks i >= B_CH / 2), the base choice is static.
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
     b_dst[i] = BM * S + r * S + (FP8 ? 0 : ((kc ^ (r & 7)) * 8));
     b_w3[i] = SWI && (SPLIT ? (i >= B_CH / 2) : (r >= BNO));
     const int wr = n0 + (b_w3[i] ? r - BNO : r);
-    b_off[i] = (static_cast<uint32_t>(wr) * static_cast<uint32_t>(K) + kc * (FP8 ? 16 : 8)) * WB;
+    b_off[i] = (static_cast<uint32_t>(wr) * static_cast<uint32_t>(p.ldb) + kc * (FP8 ? 16 : 8)) * WB;
   }
 
   floatx4_t acc[FM][FN];
@@ -350,39 +352,52 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 }
 
 // ------------------------------------------------------------------ bf16 MFMA, LDS DMA pipeline
-// 256 x 256 tile, 8 waves (2 x 4, each 128 rows x 64 weight rows), k-stages of
-// 64 through two 64 KB LDS buffers. Operands move from memory to LDS with
-// global_load_lds (no VGPR staging, no ds_write): each wave instruction writes
-// 1 KB = 8 rows x 128 B, so every fetched 128-byte line is used whole, and the
-// source address each lane fetches puts 16-byte chunk c of row r at position
-// c ^ (r & 7), at which the MFMA operand reads (16 rows, one chunk each) run
-// conflict-free. A stage feeds two MFMA k-steps of 32; the fragments of the
-// next k-step are read from LDS while the current one's MFMAs run.
-// The stage buffers are separate LDS objects so that the compiler's wait for a
-// DMA store only blocks reads of that buffer. Before every barrier a wave waits
-// for its own LDS reads, so no DMA can overwrite data still being read.
+// BM x 256 tile (BM = 256 or 128), 8 waves (2 x 4, each BM/2 rows x 64 weight
+// rows), k-stages of 64 through LDS stage buffers: two of 64 KB for BM = 256,
+// three of 48 KB for BM = 128 (two stages in flight). Operands move from
+// memory to LDS with global_load_lds (no VGPR staging, no ds_write): each wave
+// instruction writes 1 KB = 8 rows x 128 B, so every fetched 128-byte line is
+// used whole, and the source address each lane fetches puts 16-byte chunk c of
+// row r at position c ^ (r & 7), at which the MFMA operand reads (16 rows, one
+// chunk each) run conflict-free. A stage feeds two MFMA k-steps of 32; the
+// fragments of the next k-step are read from LDS while the current one's
+// MFMAs run. The stage buffers are separate LDS objects so that the
+// compiler's wait for a DMA store only blocks reads of that buffer. Before
+// every barrier a wave waits for its own LDS reads, so no DMA can overwrite
+// data still being read.
 namespace dma {
-constexpr int BM = 256, BNB = 256, NTH = 512, WGN = 4;
-constexpr int BK = 64;              // k per stage, 128 B per row
-constexpr int RB = BK * 2;          // row bytes in a stage
-constexpr int WTM = 128, WTB = 64;  // rows / weight rows per wave
-constexpr int FM = 8, FN = 4;
-constexpr int SBYTES = (BM + BNB) * RB;  // 64 KB per stage
+constexpr int BNB = 256, NTH = 512, WGM = 2, WGN = 4;
+constexpr int BK = 64;      // k per stage
+constexpr int RB = BK * 2;  // row bytes in a stage
+constexpr int WTB = 64, FN = 4;
 constexpr int bno(int epi) { return epi == EPI_SWIGLU ? BNB / 2 : BNB; }
+template <int BM>
+struct Cfg {
+  static_assert(BM == 256 || BM == 128, "DMA tile rows");
+  static constexpr int WTM = BM / WGM;               // rows per wave
+  static constexpr int FM = WTM / 16;
+  static constexpr int NSTAGE = BM == 256 ? 2 : 3;
+  static constexpr int SBYTES = (BM + BNB) * RB;     // one stage buffer
+  static constexpr int ADMA = BM / 64;               // A instructions per wave and stage
+  static constexpr int NDMA = ADMA + 4;              // + 4 weight instructions
+};
+// s_waitcnt immediate: vmcnt(n), no wait on expcnt and lgkmcnt
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 }  // namespace dma
 
-// Epilogue of a 256 x 256 DMA tile held as per-wave MFMA fragments: bias and
-// activation (or the SwiGLU product of the W1 and W3 halves), bf16, and
-// 16-byte stores through an LDS staging buffer of 64 KB, in two 128-row
-// halves (16-byte chunk c of staged row r at position c ^ (r & 7)).
-template <int EPI>
+// Epilogue of a DMA tile held as per-wave MFMA fragments: bias and activation
+// (or the SwiGLU product of the W1 and W3 halves), bf16, and 16-byte stores
+// through an LDS staging buffer, one wave row (BM/2 rows) at a time (16-byte
+// chunk c of staged row r at position c ^ (r & 7)).
+template <int EPI, int BM>
 __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
-                                               floatx4_t (&acc)[dma::FM][dma::FN], char* stage) {
+                                               floatx4_t (&acc)[dma::Cfg<BM>::FM][dma::FN], char* stage) {
   using namespace dma;
+  using C_ = Cfg<BM>;
   constexpr int BNO = bno(EPI);
   constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
   constexpr int FNO = WTO / 16;
-  static_assert(WTM * BNO * 2 <= SBYTES, "output staging exceeds a stage buffer");
+  static_assert(C_::WTM * BNO * 2 <= C_::SBYTES, "output staging exceeds a stage buffer");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
@@ -395,17 +410,18 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
   constexpr int OCH = BNO / 8;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < WGM; ++h) {
+    if (h * C_::WTM >= ti.rows) break;  // the same for the whole workgroup
     if (wm == h) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < C_::FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FNO; ++j) {
           const int col = wn * WTO + j * 16 + c16;
           const float bv = bias ? bias[col] : 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int srow = i * 16 + q * 4 + r;  // row inside the half
+            const int srow = i * 16 + q * 4 + r;  // row inside the staged part
             float v;
             if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
             else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
@@ -416,9 +432,9 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
       }
     }
     __syncthreads();
-    for (int c = tid; c < WTM * OCH; c += NTH) {
+    for (int c = tid; c < C_::WTM * OCH; c += NTH) {
       const int srow = c / OCH, cc = c % OCH;
-      const int row = h * WTM + srow;
+      const int row = h * C_::WTM + srow;
       if (row < ti.rows)
         *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
             *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
@@ -429,18 +445,22 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
 
 // fp32 partial tile of a k-chunk, in fragment order: fragment (wave, i, j) is
 // 64 lanes x 4 floats, 1 KB contiguous.
+template <int BM>
 __device__ __forceinline__ float* dma_part_frag(float* part, int unit, int wave, int i, int j) {
   using namespace dma;
-  return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * FM + i) * FN + j) * 256;
+  return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * Cfg<BM>::FM + i) * FN + j) * 256;
 }
 
-template <int EPI>
+template <int EPI, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
   using namespace dma;
+  using C_ = Cfg<BM>;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int BNO = bno(EPI);
-  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
-  __shared__ __attribute__((aligned(16))) char S1[SBYTES];
+  constexpr int FM = C_::FM, WTM = C_::WTM, ADMA = C_::ADMA, NDMA = C_::NDMA, NSTAGE = C_::NSTAGE;
+  __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
+  __shared__ __attribute__((aligned(16))) char S1[C_::SBYTES];
+  __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? C_::SBYTES : 16];
 
   const int K = p.K;
   const int KS = K / BK;  // even: K is a multiple of 128
@@ -463,43 +483,57 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
       ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
     }
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // stage j of the loops below loads k-column ks_begin + j; all tiles walk k
+  // in the same order, so tiles that share a weight tile or A rows read the
+  // same lines at about the same time and L2 keeps them
+  const int n_st = ks_end - ks_begin;
+#define MOE_COL(j) (ks_begin + (j))
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level pointers stay in SGPRs
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
   const bool shared = ti.g >= p.n_routed;
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
   const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
-                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda * 2;
-  // This wave loads A rows and weight rows [32 w, 32 w + 32): four
-  // instructions of 8 rows each. For SwiGLU the weight rows [0, 128) of the
-  // tile are W1 rows and [128, 256) the matching W3 rows, so one wave's weight
-  // rows come from one matrix.
-  const int wr0 = wave * 32;
+                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda * 2;
+  // This wave loads A rows [BM/8 w, BM/8 (w + 1)) and weight rows
+  // [32 w, 32 w + 32), in instructions of 8 rows each. For SwiGLU the weight
+  // rows [0, 128) of the tile are W1 rows and [128, 256) the matching W3 rows,
+  // so one wave's weight rows come from one matrix.
+  const int ar0 = wave * (BM / 8), wr0 = wave * 32;
   const bool w3 = SWI && wr0 >= BNO;
   const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
-                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * K) * 2;
+                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) * 2;
   // Lane L of an instruction over rows [r0, r0 + 8) fills row r0 + L/8,
   // position L%8 with logical chunk (L%8) ^ (row & 7); byte offsets are
   // relative to the tile's first A row and the wave's first weight row.
-  uint32_t offa[4], offb[4];
+  uint32_t offa[ADMA], offb[4];
+#pragma unroll
+  for (int i = 0; i < ADMA; ++i) {
+    const int r = ar0 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
+    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(lda) * 2 + chunk * 16);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wr0 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (r & 7);
-    const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
-    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(p.lda) * 2 + chunk * 16);
-    offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * K * 2 + chunk * 16);
+    offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * static_cast<int>(p.ldb) * 2 + chunk * 16);
   }
-  const int dst_a = wr0 * RB, dst_b = BM * RB + wr0 * RB;  // byte offsets inside a stage
+  const int dst_a = ar0 * RB, dst_b = BM * RB + wr0 * RB;  // byte offsets inside a stage
+// (the source pointer is passed as const void*: with a char* argument the host
+// compilation pass silently drops the kernel's launch stub)
 #define MOE_LDS(x) ((__attribute__((address_space(3))) void*)(x))
 #define MOE_DMA(S, ks)                                                                               \
   do {                                                                                               \
     const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < ADMA; ++i_)                                              \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(A + (offa[i_] + ko_)), MOE_LDS((S) + dst_a + i_ * 1024), 16, 0, 0); \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                 \
-        __builtin_amdgcn_global_load_lds(A + offa[i_] + ko_, MOE_LDS(S + dst_a + i_ * 1024), 16, 0, 0); \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                 \
-        __builtin_amdgcn_global_load_lds(Bw + offb[i_] + ko_, MOE_LDS(S + dst_b + i_ * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bw + (offb[i_] + ko_)), MOE_LDS((S) + dst_b + i_ * 1024), 16, 0, 0); \
   } while (0)
 
   floatx4_t acc[FM][FN];
@@ -515,69 +549,130 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
 #define MOE_READ(S, RD, AF, BF)                                                                      \
   do {                                                                                               \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
-        *reinterpret_cast<const uint4*>(S + (wm * WTM + i * 16) * RB + RD);                          \
+        *reinterpret_cast<const uint4*>((S) + (wm * WTM + i * 16) * RB + RD);                        \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                 \
       const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
                                            : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
                            : wn * WTB + j * 16;                                                      \
-      BF[j] = *reinterpret_cast<const uint4*>(S + BM * RB + brow * RB + RD);                         \
+      BF[j] = *reinterpret_cast<const uint4*>((S) + BM * RB + brow * RB + RD);                       \
     }                                                                                                \
   } while (0)
 #define MOE_MFMA(AC, BC)                                                                             \
   _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                     \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(AC[i], BC[j], acc[i][j])
-  // Issue order inside a k-step: DMA instructions (if any), then one fragment
-  // read per two MFMAs, then the remaining MFMAs. Left alone, the scheduler
-  // sinks each read down to its first use in the next k-step and waits there.
-#define MOE_SCHEDULE(NDMA)                                                                           \
+  // Issue order inside a k-step: one fragment read per two MFMAs, then the
+  // remaining MFMAs; in the k-step after the barrier the MFMAs come first (the
+  // MFMA unit restarts at once) and the DMA instructions are spread among
+  // them. Left alone, the scheduler sinks each read down to its first use in
+  // the next k-step and waits there.
+  constexpr int REST = FM * FN - 2 * (FM + FN);
+  static_assert(REST >= 0 && NDMA <= FM + FN, "schedule shape");
+#define MOE_SCHEDULE(WITH_DMA)                                                                       \
   do {                                                                                               \
-    if (NDMA) __builtin_amdgcn_sched_group_barrier(0x020, NDMA, 0);                                  \
     _Pragma("unroll") for (int g_ = 0; g_ < FM + FN; ++g_) {                                         \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
+      if constexpr (WITH_DMA) {                                                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                           \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                           \
+        if (g_ < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                            \
+      } else {                                                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                           \
+      }                                                                                              \
     }                                                                                                \
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2 * (FM + FN), 0);                         \
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                    \
     __builtin_amdgcn_sched_barrier(0);                                                               \
   } while (0)
   // Stage ks lives in buffer SC; its first k-step's fragments are in af0/bf0.
   // First half: read the second k-step's fragments, run the first's MFMAs.
   // Second half: wait for stage ks+1 (this wave's DMA, then the barrier for
   // everyone's, which also tells that all reads of SC are done), refill SC
-  // with stage ks+2, read stage ks+1's first fragments from SN, run the second
-  // k-step's MFMAs.
+  // with stage ks+NSTAGE, read stage ks+1's first fragments from SN, run the
+  // second k-step's MFMAs.
 #define MOE_STAGE(SC, SN, ks)                                                                        \
   do {                                                                                               \
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): af0/bf0 have arrived */                       \
     MOE_READ(SC, rd1, af1, bf1);                                                                     \
     MOE_MFMA(af0, bf0);                                                                              \
-    MOE_SCHEDULE(0);                                                                                 \
-    __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0): stage ks+1 landed */                            \
+    MOE_SCHEDULE(false);                                                                             \
+    /* stage ks+1 landed; the DMA of the NSTAGE-2 later stages may still fly */                      \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 2) * NDMA));                                     \
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of SC are done */                    \
     __builtin_amdgcn_s_barrier();                                                                    \
-    MOE_DMA(SC, min((ks) + 2, ks_end - 1));                                                          \
+    MOE_DMA(SC, MOE_COL(min((ks) + NSTAGE, n_st - 1)));                                              \
     MOE_READ(SN, rd0, af0, bf0);                                                                     \
     MOE_MFMA(af1, bf1);                                                                              \
-    MOE_SCHEDULE(8);                                                                                 \
+    MOE_SCHEDULE(true);                                                                              \
   } while (0)
 
+  // A stage of a wave whose rows all lie past the group's end (a tile's
+  // second half when the tile holds at most BM/2 rows): no reads and no MFMAs,
+  // but the same DMA and barriers as the other waves.
+#define MOE_STAGE_IDLE(SC, ks)                                                                       \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 2) * NDMA));                                     \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA(SC, MOE_COL(min((ks) + NSTAGE, n_st - 1)));                                              \
+  } while (0)
+  // Loops over the stages: whole rounds of the stage buffers in the loop (a
+  // conditional exit inside it makes the compiler drain every DMA at the loop
+  // head), then the one or two stages left when NSTAGE is 3 (chunks hold whole
+  // stage pairs).
+#define MOE_STAGES(STAGE0, STAGE1, STAGE2)                                                           \
+  do {                                                                                               \
+    if constexpr (NSTAGE == 2) {                                                                     \
+      for (int ks = 0; ks < n_st; ks += 2) {                                                         \
+        STAGE0(ks);                                                                                  \
+        STAGE1(ks + 1);                                                                              \
+      }                                                                                              \
+    } else {                                                                                         \
+      const int ks_round = n_st / 3 * 3;                                                             \
+      for (int ks = 0; ks < ks_round; ks += 3) {                                                     \
+        STAGE0(ks);                                                                                  \
+        STAGE1(ks + 1);                                                                              \
+        STAGE2(ks + 2);                                                                              \
+      }                                                                                              \
+      if (ks_round < n_st) {                                                                         \
+        STAGE0(ks_round);                                                                            \
+        if (ks_round + 1 < n_st) STAGE1(ks_round + 1);                                               \
+      }                                                                                              \
+    }                                                                                                \
+  } while (0)
+#define MOE_LIVE0(ks) MOE_STAGE(S0, S1, ks)
+#define MOE_LIVE1(ks) MOE_STAGE(S1, (NSTAGE == 2 ? S0 : S2), ks)
+#define MOE_LIVE2(ks) MOE_STAGE(S2, S0, ks)
+#define MOE_IDLE0(ks) MOE_STAGE_IDLE(S0, ks)
+#define MOE_IDLE1(ks) MOE_STAGE_IDLE(S1, ks)
+#define MOE_IDLE2(ks) MOE_STAGE_IDLE(S2, ks)
+
   uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
-  MOE_DMA(S0, ks_begin);
-  MOE_DMA(S1, ks_begin + 1);
-  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): the first stage landed
+  MOE_DMA(S0, MOE_COL(0));
+  MOE_DMA(S1, MOE_COL(1));
+  if constexpr (NSTAGE == 3) MOE_DMA(S2, MOE_COL(min(2, n_st - 1)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 1) * NDMA));  // the first stage landed
   __builtin_amdgcn_s_barrier();
-  MOE_READ(S0, rd0, af0, bf0);
-  for (int ks = ks_begin; ks < ks_end; ks += 2) {
-    MOE_STAGE(S0, S1, ks);
-    MOE_STAGE(S1, S0, ks + 1);
+  if (wm * WTM < ti.rows) {
+    MOE_READ(S0, rd0, af0, bf0);
+    MOE_STAGES(MOE_LIVE0, MOE_LIVE1, MOE_LIVE2);
+  } else {
+    MOE_STAGES(MOE_IDLE0, MOE_IDLE1, MOE_IDLE2);
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the trailing DMAs have landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing DMAs have landed
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
+#undef MOE_LIVE0
+#undef MOE_LIVE1
+#undef MOE_LIVE2
+#undef MOE_IDLE0
+#undef MOE_IDLE1
+#undef MOE_IDLE2
+#undef MOE_STAGES
+#undef MOE_STAGE_IDLE
 #undef MOE_STAGE
 #undef MOE_SCHEDULE
 #undef MOE_MFMA
 #undef MOE_READ
 #undef MOE_DMA
+#undef MOE_COL
 #undef MOE_LDS
 
   if (unit >= 0) {  // a k-chunk: raw fp32 partial sums, summed by the fix-up pass
@@ -585,19 +680,21 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        *reinterpret_cast<floatx4_t*>(dma_part_frag(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
+        *reinterpret_cast<floatx4_t*>(dma_part_frag<BM>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
-  dma_store_tile<EPI>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM>(p, ti, acc, S0);
 }
 
 // Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
 // partial tiles in chunk order and runs the tile epilogue.
-template <int EPI>
+template <int EPI, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_split_fixup_kernel(GemmParams p) {
   using namespace dma;
+  using C_ = Cfg<BM>;
   constexpr int BNO = bno(EPI);
-  __shared__ __attribute__((aligned(16))) char S0[SBYTES];
+  constexpr int FM = C_::FM;
+  __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
   const SplitPlan sp = split_plan<BNO>(p, p.K / BK / 2);
   const int b = blockIdx.x;
   if (sp.s == 1 || b >= sp.r) return;
@@ -609,16 +706,16 @@ __global__ __launch_bounds__(512, 1) void gemm_split_fixup_kernel(GemmParams p) 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag(p.split_part, b * sp.s, wave, i, j) + lane * 4);
+      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM>(p.split_part, b * sp.s, wave, i, j) + lane * 4);
   for (int c = 1; c < sp.s; ++c) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag(p.split_part, b * sp.s + c, wave, i, j) +
+        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM>(p.split_part, b * sp.s + c, wave, i, j) +
                                                          lane * 4);
   }
-  dma_store_tile<EPI>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM>(p, ti, acc, S0);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -639,8 +736,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
   const int ew = shared ? widx - p.n_routed : widx;
   const int n0 = ti.n_tile * BNO;
   const int K = p.K;
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
   const float* A = static_cast<const float*>(shared ? p.A_s : p.A_r) +
-                   (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.lda;
+                   (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda;
   const float* Bw = static_cast<const float*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride;
   const float* B3w = SWI ? static_cast<const float*>(shared ? p.B3_s : p.B3_r) + static_cast<int64_t>(ew) * p.b_stride
                          : nullptr;
@@ -651,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
       int r = tid >> 2;
       const int k4 = (tid & 3) * 4;
       const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;
-      const float4 v = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(rr) * p.lda + kb + k4);
+      const float4 v = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(rr) * lda + kb + k4);
       sA[k4 + 0][r] = v.x;
       sA[k4 + 1][r] = v.y;
       sA[k4 + 2][r] = v.z;
@@ -659,8 +757,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
     }
     for (int c = tid; c < BNB * 4; c += kThreads) {
       const int r = c >> 2, k4 = (c & 3) * 4;
-      const float* src = (SWI && r >= BNO) ? B3w + static_cast<int64_t>(n0 + r - BNO) * K
-                                           : Bw + static_cast<int64_t>(n0 + r) * K;
+      const float* src = (SWI && r >= BNO) ? B3w + static_cast<int64_t>(n0 + r - BNO) * p.ldb
+                                           : Bw + static_cast<int64_t>(n0 + r) * p.ldb;
       const float4 v = *reinterpret_cast<const float4*>(src + kb + k4);
       sB[k4 + 0][r] = v.x;
       sB[k4 + 1][r] = v.y;
@@ -761,14 +859,16 @@ hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile configurations: rows x weight rows, wave grid.
-enum TileCfg { kTile128x128w4 = 0, kTile256x256w4 = 1, kTile256x256w8 = 2, kTile128x256w4 = 3, kTile256x128w4 = 4,
-               kTile128x128w8 = 5, kTile256x256Dma = 6 };
-constexpr int tile_rows(int cfg) {
-  return (cfg == kTile256x256w4 || cfg == kTile256x256w8 || cfg == kTile256x128w4 || cfg == kTile256x256Dma) ? 256 : 128;
-}
+// Tile configurations of the bf16 path.
+enum TileCfg {
+  kReg128 = 0,  // register-staged 128 x 128, 4 waves: fewer than 2048 rows
+  kReg256 = 1,  // register-staged 256 x 256, 8 waves: e4m3 weights (decoded in registers)
+  kDma256 = 2,  // LDS-DMA 256 x 256: bf16, many rows per group
+  kDma128 = 3,  // LDS-DMA 128 x 256: bf16, few rows per group
+};
+constexpr int tile_rows(int cfg) { return (cfg == kReg256 || cfg == kDma256) ? 256 : 128; }
 
-template <int EPI>
+template <int EPI, int BM>
 hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
@@ -777,23 +877,15 @@ hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   // a k-split tail runs at most total - r + kSplitUnits workgroups
   if (p.split_part) grid += kSplitUnits;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, BM>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
   if (p.split_part) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // split tiles: r <= kSplitUnits / 2 (each is cut at least in two)
-    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, BM>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }
-
-// Configuration of the prefill path (many rows) and of the small-row path.
-#ifndef MOE_GEMM_BIG_CFG
-#define MOE_GEMM_BIG_CFG kTile256x256Dma
-#endif
-#ifndef MOE_GEMM_SMALL_CFG
-#define MOE_GEMM_SMALL_CFG kTile128x128w4
-#endif
 
 template <int EPI>
 hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
@@ -806,18 +898,26 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 template <int EPI, bool FP8>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  if (cfg == kTile256x256Dma) {
-    if constexpr (FP8) return run_bf16<256, 256, 2, 4, EPI, FP8>(p, max_mtiles, s);  // e4m3 is decoded in registers
-    else return run_dma<EPI>(p, max_mtiles, s);
+  if constexpr (FP8) {
+    if (cfg == kReg256) return run_bf16<256, 256, 2, 4, EPI, true>(p, max_mtiles, s);
+    return run_bf16<128, 128, 2, 2, EPI, true>(p, max_mtiles, s);
+  } else {
+    switch (cfg) {
+      case kDma256: return run_dma<EPI, 256>(p, max_mtiles, s);
+      case kDma128: return run_dma<EPI, 128>(p, max_mtiles, s);
+      default: return run_bf16<128, 128, 2, 2, EPI, false>(p, max_mtiles, s);
+    }
   }
-  switch (cfg) {
-    case kTile256x256w4: return run_bf16<256, 256, 2, 2, EPI, FP8>(p, max_mtiles, s);
-    case kTile256x256w8: return run_bf16<256, 256, 2, 4, EPI, FP8>(p, max_mtiles, s);
-    case kTile128x256w4: return run_bf16<128, 256, 2, 2, EPI, FP8>(p, max_mtiles, s);
-    case kTile256x128w4: return run_bf16<256, 128, 2, 2, EPI, FP8>(p, max_mtiles, s);
-    case kTile128x128w8: return run_bf16<128, 128, 2, 4, EPI, FP8>(p, max_mtiles, s);
-    default: return run_bf16<128, 128, 2, 2, EPI, FP8>(p, max_mtiles, s);
-  }
+}
+
+// Tile configuration of a bf16 call: register-staged tiles for few rows; for
+// many rows the LDS-DMA tiles, 256 rows when the groups average at least 768
+// rows (little padding in a group's last tile), else 128.
+int pick_cfg(const FfnArgs& a) {
+  const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
+  if (rows < 2048) return kReg128;
+  if (a.w_dtype == 2) return kReg256;
+  return rows >= 768LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
 // Compute units of the current device, cached per device.
@@ -838,7 +938,7 @@ int device_cus() {
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
   const bool f32 = (a.act_dtype == 0);
-  const int cfg = (a.routed_row_cap + a.n_shared * a.T >= 2048) ? MOE_GEMM_BIG_CFG : MOE_GEMM_SMALL_CFG;
+  const int cfg = pick_cfg(a);
   const int bm = f32 ? 64 : tile_rows(cfg);
   GroupDesc* up = a.groups;
   GroupDesc* down = a.groups + G;
@@ -863,19 +963,21 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   // up GEMM: [rows][d] x [d_ff][d]^T -> h [rows][d_ff]
   p.A_r = a.x_perm;
   p.A_s = a.x;
-  p.lda = a.d;
+  p.lda_r = a.ld_xp;
+  p.lda_s = a.d;
   p.B_r = a.w1;
   p.B3_r = a.w3;
   p.B_s = a.sw1;
   p.B3_s = a.sw3;
-  p.b_stride = a.d_ff * a.d;
+  p.ldb = a.ld_up;
+  p.b_stride = a.d_ff * a.ld_up;
   p.bias = swi ? nullptr : a.b1;
   p.scale_r = a.w_scale;
   p.scale_s = a.sw_scale;
   p.scale_col = 0;
   p.C_r = a.h;
   p.C_s = a.h;
-  p.ldc = a.d_ff;
+  p.ldc = a.ld_h;
   p.K = static_cast<int32_t>(a.d);
   p.Nout = static_cast<int32_t>(a.d_ff);
   p.groups = up;
@@ -893,12 +995,14 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   // down GEMM: h [rows][d_ff] x [d][d_ff]^T -> y [rows][d]
   p.A_r = a.h;
   p.A_s = a.h;
-  p.lda = a.d_ff;
+  p.lda_r = a.ld_h;
+  p.lda_s = a.ld_h;
   p.B_r = a.w2;
   p.B3_r = nullptr;
   p.B_s = a.sw2;
   p.B3_s = nullptr;
-  p.b_stride = a.d * a.d_ff;
+  p.ldb = a.ld_down;
+  p.b_stride = a.d * a.ld_down;
   p.bias = swi ? nullptr : a.b2;
   p.scale_col = 2;
   p.C_r = a.y_perm;

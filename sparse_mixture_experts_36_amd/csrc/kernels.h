@@ -46,7 +46,8 @@ struct PermuteArgs {
   int32_t* offsets;          // [N+1]
   int32_t* perm_token;       // [T*k]
   int32_t* inv_map;          // [T*k]
-  void* x_perm;              // [T*k][d] (may be null: no gather)
+  void* x_perm;              // [T*k] rows of pitch ld_out (may be null: no gather)
+  int64_t ld_out;            // x_perm row pitch in elements (>= d)
   int32_t* kept;             // [N] (workspace if the caller gave none)
   int32_t* n_dropped;        // [1] (workspace if the caller gave none)
   // workspace
@@ -71,13 +72,16 @@ struct FfnArgs {
   int32_t n_routed, n_shared, act, act_dtype, w_dtype;
   int32_t routed_row_cap;     // rows reserved for routed experts in h (T*k or N*C)
   const int32_t* offsets;     // [n_routed+1] device
-  const void* x_perm;         // routed A of the up GEMM
+  const void* x_perm;         // routed A of the up GEMM, rows of pitch ld_xp
+  int64_t ld_xp;              // x_perm row pitch (elements)
+  int64_t ld_h;               // h row pitch (elements)
+  int64_t ld_up, ld_down;     // weight row pitches (elements): W1/W3, W2
   const void* x;              // shared A of the up GEMM
   const void *w1, *w3, *w2;
   const float *b1, *b2, *w_scale;
   const void *sw1, *sw3, *sw2;
   const float* sw_scale;
-  void* h;                    // [routed_row_cap + n_shared*T][d_ff] act dtype (workspace)
+  void* h;                    // [routed_row_cap + n_shared*T] rows of pitch ld_h, act dtype (workspace)
   void* y_perm;               // [*][d]
   void* y_shared;             // [n_shared][T][d]
   GroupDesc* groups;          // [2][n_routed + n_shared] (workspace)
@@ -93,6 +97,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 // Decode-sized layers (few rows per expert) stream expert weights instead of
 // tiling rows: taken when all expert rows of the call fit in kSkinnyMaxRows.
 constexpr int64_t kSkinnyMaxRows = 256;
+// Elements added to the row pitch of the activation workspaces the library
+// owns (x_perm inside moe_forward, h): with d or d_ff a multiple of 4096, rows
+// a power of two apart put the lines of one k-column into few L2 channels.
+constexpr int64_t kActPad = 64;
 inline bool use_skinny(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shared, int64_t T) {
   return act_dtype == 1 && routed_row_cap + n_shared * T <= kSkinnyMaxRows;
 }

@@ -151,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
   }
   if (!a.x_perm) return;
   const int64_t nchunk = a.d * a.act_bytes / 16;
+  const int64_t ochunk = a.ld_out * a.act_bytes / 16;  // 16-byte chunks per x_perm row
   const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
   uint4* dst = reinterpret_cast<uint4*>(a.x_perm);
   constexpr int U = 8;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t c = c0 + u * 64 + lane;
-        if (c < nchunk) dst[row[j] * nchunk + c] = v[u];
+        if (c < nchunk) dst[row[j] * ochunk + c] = v[u];
       }
     }
   }

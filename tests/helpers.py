@@ -48,9 +48,16 @@ def shape_of(wl, T=None, capacity=None) -> moe.Shape:
                           n_shared=wl.n_shared, aux_alpha=wl.aux_alpha)
 
 
-def device_weights(inp) -> dict:
+def device_weights(inp, pad: int = 0) -> dict:
+    """Device copies of the layer's weights; with pad > 0 the expert matrices
+    get rows `pad` elements longer than their width (moe_weights ld_up/ld_down)."""
+    import sparse_mixture_experts_36_amd as moe
     names = ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2", "sw_scale")
-    return {n: dev(getattr(inp, n)) for n in names}
+    t = {n: dev(getattr(inp, n)) for n in names}
+    if pad:
+        for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2"):
+            t[n] = moe.padded(t[n], pad)
+    return t
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -118,6 +118,27 @@ def test_null_and_workspace_errors_return_before_launch():
     assert L.moe_forward(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 2), ctypes.byref(w), fake, None, None, None,
                          None, None, None, None, fake, 1 << 34, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(s), None, fake, fake, None, fake, None) == moe.MOE_ERR_INVALID_ARG
+    # weight row pitches: shorter than a row, or not a multiple of 16
+    for ld_up, ld_down in ((s.d - 16, 0), (s.d + 8, 0), (0, s.d_ff - 16), (0, s.d_ff + 4)):
+        w = moe.Weights(w_router=1 << 20, w1=1 << 20, w3=1 << 20, w2=1 << 20, ld_up=ld_up, ld_down=ld_down)
+        assert L.moe_forward(ctypes.byref(s), fake, ctypes.byref(w), fake, None, None, None, None, None, None,
+                             None, fake, 1 << 34, None) == moe.MOE_ERR_INVALID_ARG, (ld_up, ld_down)
+
+
+def test_weight_row_pitches_come_from_tensor_strides():
+    import torch
+    w1 = moe.padded(torch.zeros(3, 8, 32), 16)
+    w3 = moe.padded(torch.ones(3, 8, 32), 16)
+    w2 = moe.padded(torch.zeros(3, 32, 8), 24)
+    assert w1.shape == (3, 8, 32) and w1.stride() == (8 * 48, 48, 1) and float(w3.sum()) == 3 * 8 * 32
+    w = moe.weights_struct({"w1": w1, "w3": w3, "w2": w2})
+    assert (w.ld_up, w.ld_down) == (48, 32)
+    w = moe.weights_struct({"w1": torch.zeros(3, 8, 32), "w2": torch.zeros(3, 32, 8)})
+    assert (w.ld_up, w.ld_down) == (32, 8)
+    with pytest.raises(ValueError):  # W1 and W3 with different pitches
+        moe.weights_struct({"w1": w1, "w3": torch.zeros(3, 8, 32), "w2": w2})
+    with pytest.raises(ValueError):  # a gap between experts
+        moe.weights_struct({"w1": torch.zeros(3, 16, 32)[:, :8], "w2": w2})
 
 
 def test_host_helpers_reproduce_pages_worked_examples():

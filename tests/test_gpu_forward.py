@@ -29,12 +29,12 @@ def _cuda():
     torch.cuda.synchronize()
 
 
-def run_and_check(inp, sample=None, exact_routing=False, label=""):
+def run_and_check(inp, sample=None, exact_routing=False, label="", pad=0):
     import torch
     wl = inp.wl
     say(f"forward {label or wl.name}: T={wl.T} d={wl.d} d_ff={wl.d_ff} N={wl.n_experts} k={wl.top_k} "
-        f"C={wl.capacity()} shared={wl.n_shared} w_dtype={wl.w_dtype}")
-    layer = moe.MoELayer(shape_of(wl), device_weights(inp))
+        f"C={wl.capacity()} shared={wl.n_shared} w_dtype={wl.w_dtype} weight row pad={pad}")
+    layer = moe.MoELayer(shape_of(wl), device_weights(inp, pad))
     out = layer(dev(inp.x))
     torch.cuda.synchronize()
     so = oracle.shape_of(wl)
@@ -151,20 +151,22 @@ def test_full_tiny_gelu_fp32():
     run_and_check(gen.make_inputs(gen.TINY_GELU), label="tiny-gelu-fp32 (full)")
 
 
-def test_full_mixtral_prefill():
+@pytest.mark.parametrize("pad", [0, 64])
+def test_full_mixtral_prefill(pad):
+    """pad=64 is the weight layout the benchmark times."""
     inp = gen.make_inputs(gen.MIXTRAL_PREFILL)
-    run_and_check(inp, sample=_sample(4096, 12), label="mixtral-prefill (full)")
+    run_and_check(inp, sample=_sample(4096, 12), label="mixtral-prefill (full)", pad=pad)
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])
 def test_full_mixtral_decode(T):
     inp = gen.make_inputs(gen.MIXTRAL_DECODE[T])
-    run_and_check(inp, sample=None if T <= 16 else _sample(T, 12), label=f"mixtral-decode T={T}")
+    run_and_check(inp, sample=None if T <= 16 else _sample(T, 12), label=f"mixtral-decode T={T}", pad=64)
 
 
 def test_full_fine_grained():
     inp = gen.make_inputs(gen.FINE_GRAINED)
-    run_and_check(inp, sample=_sample(8192, 6), label="fine-grained (full)")
+    run_and_check(inp, sample=_sample(8192, 6), label="fine-grained (full)", pad=64)
 
 
 @pytest.mark.parametrize("fp8", [False, True])

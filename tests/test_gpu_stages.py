@@ -160,14 +160,24 @@ FFN_CASES = [
     dict(T=64, N=16, k=1, act=gen.GELU, d=256, d_ff=512, biases=True),
     dict(T=40, N=32, k=4, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=1536, wdt=gen.E4M3),
-    # prefill-sized calls (>= 2048 expert rows): the 256 x 256 LDS-DMA tiles.
-    # With 256 CUs, a launch whose last round holds r <= 128 tiles cuts those
-    # tiles along k and sums the chunks in a fix-up pass; the comments give
-    # (tiles, split) of the up and down GEMM.
-    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512),                  # (~64, 4), (~32, 4)
-    dict(T=1100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=4096),                 # (512, none), (16, 8)
-    dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True),  # (~96, 2), (~24, 8)
-    dict(T=1024, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),    # (~96, 2), (~48, 2)
+    dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=512, n_shared=1, pad=64),       # decode path, padded
+    dict(T=400, N=16, k=1, act=gen.GELU, d=256, d_ff=512, wdt=gen.E4M3, biases=True, pad=32),  # fp8, padded
+    dict(T=130, N=8, k=2, act=gen.SWIGLU, d=128, d_ff=256, dt=gen.F32, n_shared=1, pad=16),    # fp32, padded
+    # prefill-sized calls (>= 2048 expert rows): the LDS-DMA tiles, 128 x 256
+    # when the groups average fewer than 768 rows, else 256 x 256. With 256
+    # CUs, a launch whose last round holds r <= 128 tiles cuts those tiles
+    # along k and sums the chunks in a fix-up pass; the comments give (tiles,
+    # split) of the up and down GEMM.
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512),                  # 256 rows: (~68, 2), (~17, 4)
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, pad=64),          # the same, padded weight rows
+    dict(T=4096, N=4, k=2, act=gen.SWIGLU, d=512, d_ff=512),                  # 256 rows: (~144, none), (~72, 3)
+    dict(T=3000, N=4, k=2, act=gen.SWIGLU, d=1024, d_ff=512),                 # 256 rows: (~100, 2), (~100, 2)
+    dict(T=3072, N=4, k=1, act=gen.GELU, d=512, d_ff=1024, biases=True),      # 256 rows: (~52, 4), (~26, 8)
+    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512),                  # 128 rows: (~80, 4), (~40, 4)
+    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, pad=16),  # padded weights + shared
+    dict(T=1100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=4096),                 # 128 rows: (~768, none), (~24, 8)
+    dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True),  # 128 rows: (~128, 2), (~32, 8)
+    dict(T=1024, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),    # 128 rows: (~150, none), (~75, 2)
 ]
 
 
@@ -176,6 +186,7 @@ def test_grouped_ffn_against_oracle(case):
     import torch
     case = dict(case)
     biases = case.pop("biases", False)
+    pad = case.pop("pad", 0)
     say(f"grouped ffn {case}")
     wl = _wl(**case)
     inp = gen.make_inputs(wl, seed=11)
@@ -193,8 +204,7 @@ def test_grouped_ffn_against_oracle(case):
     tdt = torch.float32 if wl.act_dtype == gen.F32 else torch.bfloat16
     yp = torch.zeros((max(M, 1), wl.d), dtype=tdt, device="cuda")
     ysh = torch.zeros((wl.n_shared, wl.T, wl.d), dtype=tdt, device="cuda") if wl.n_shared else None
-    W = moe.weights_struct(device_weights(inp))
-    keep = device_weights(inp)
+    keep = device_weights(inp, pad)
     W = moe.weights_struct(keep)
     moe.grouped_ffn(shape, dev(x_perm) if M else yp, dev(dsp.offsets), dev(inp.x), W, yp, ysh)
     torch.cuda.synchronize()
