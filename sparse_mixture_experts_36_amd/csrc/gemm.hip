@@ -366,20 +366,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 // every barrier a wave waits for its own LDS reads, so no DMA can overwrite
 // data still being read.
 namespace dma {
-constexpr int BNB = 256, NTH = 512, WGM = 2, WGN = 4;
+constexpr int BNB = 256, WGM = 2;
 constexpr int BK = 64;      // k per stage
 constexpr int RB = BK * 2;  // row bytes in a stage
-constexpr int WTB = 64, FN = 4;
 constexpr int bno(int epi) { return epi == EPI_SWIGLU ? BNB / 2 : BNB; }
-template <int BM>
+// BM x 256 tile on W waves (2 x W/2): a wave owns BM/2 rows and 512/W weight
+// rows as FM x FN MFMA fragments, and moves BM/W A rows and 256/W weight rows
+// of each stage from memory to LDS.
+template <int BM, int W>
 struct Cfg {
-  static_assert(BM == 256 || BM == 128, "DMA tile rows");
+  static_assert((BM == 256 || BM == 128) && (W == 8 || W == 4), "DMA tile shape");
+  static constexpr int NTH = 64 * W;
+  static constexpr int WGN = W / WGM;
   static constexpr int WTM = BM / WGM;               // rows per wave
-  static constexpr int FM = WTM / 16;
+  static constexpr int WTB = BNB / WGN;              // weight rows per wave
+  static constexpr int FM = WTM / 16, FN = WTB / 16;
   static constexpr int NSTAGE = BM == 256 ? 2 : 3;
   static constexpr int SBYTES = (BM + BNB) * RB;     // one stage buffer
-  static constexpr int ADMA = BM / 64;               // A instructions per wave and stage
-  static constexpr int NDMA = ADMA + 4;              // + 4 weight instructions
+  static constexpr int AROWS = BM / W, BROWS = BNB / W;
+  static constexpr int ADMA = AROWS / 8, BDMA = BROWS / 8;  // DMA instructions per wave and stage
+  static constexpr int NDMA = ADMA + BDMA;
 };
 // s_waitcnt immediate: vmcnt(n), no wait on expcnt and lgkmcnt
 constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
@@ -389,12 +395,14 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 1
 // (or the SwiGLU product of the W1 and W3 halves), bf16, and 16-byte stores
 // through an LDS staging buffer, one wave row (BM/2 rows) at a time (16-byte
 // chunk c of staged row r at position c ^ (r & 7)).
-template <int EPI, int BM>
+template <int EPI, int BM, int W>
 __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
-                                               floatx4_t (&acc)[dma::Cfg<BM>::FM][dma::FN], char* stage) {
+                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN],
+                                               char* stage) {
   using namespace dma;
-  using C_ = Cfg<BM>;
+  using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
+  constexpr int WTB = C_::WTB, FN = C_::FN, WGN = C_::WGN, NTH = C_::NTH;
   constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
   constexpr int FNO = WTO / 16;
   static_assert(C_::WTM * BNO * 2 <= C_::SBYTES, "output staging exceeds a stage buffer");
@@ -445,19 +453,21 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
 
 // fp32 partial tile of a k-chunk, in fragment order: fragment (wave, i, j) is
 // 64 lanes x 4 floats, 1 KB contiguous.
-template <int BM>
+template <int BM, int W>
 __device__ __forceinline__ float* dma_part_frag(float* part, int unit, int wave, int i, int j) {
   using namespace dma;
-  return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * Cfg<BM>::FM + i) * FN + j) * 256;
+  using C_ = Cfg<BM, W>;
+  return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * C_::FM + i) * C_::FN + j) * 256;
 }
 
-template <int EPI, int BM>
-__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
+template <int EPI, int BM, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   using namespace dma;
-  using C_ = Cfg<BM>;
+  using C_ = Cfg<BM, W>;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int BNO = bno(EPI);
-  constexpr int FM = C_::FM, WTM = C_::WTM, ADMA = C_::ADMA, NDMA = C_::NDMA, NSTAGE = C_::NSTAGE;
+  constexpr int FM = C_::FM, FN = C_::FN, WTM = C_::WTM, WTB = C_::WTB, WGN = C_::WGN;
+  constexpr int ADMA = C_::ADMA, BDMA = C_::BDMA, NDMA = C_::NDMA, NSTAGE = C_::NSTAGE;
   __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
   __shared__ __attribute__((aligned(16))) char S1[C_::SBYTES];
   __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? C_::SBYTES : 16];
@@ -498,18 +508,18 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
   const int64_t lda = shared ? p.lda_s : p.lda_r;
   const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
                   (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda * 2;
-  // This wave loads A rows [BM/8 w, BM/8 (w + 1)) and weight rows
-  // [32 w, 32 w + 32), in instructions of 8 rows each. For SwiGLU the weight
-  // rows [0, 128) of the tile are W1 rows and [128, 256) the matching W3 rows,
-  // so one wave's weight rows come from one matrix.
-  const int ar0 = wave * (BM / 8), wr0 = wave * 32;
+  // This wave loads A rows [AROWS w, AROWS (w + 1)) and weight rows
+  // [BROWS w, BROWS (w + 1)), in instructions of 8 rows each. For SwiGLU the
+  // weight rows [0, 128) of the tile are W1 rows and [128, 256) the matching
+  // W3 rows, so one wave's weight rows come from one matrix.
+  const int ar0 = wave * C_::AROWS, wr0 = wave * C_::BROWS;
   const bool w3 = SWI && wr0 >= BNO;
   const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
                    (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) * 2;
   // Lane L of an instruction over rows [r0, r0 + 8) fills row r0 + L/8,
   // position L%8 with logical chunk (L%8) ^ (row & 7); byte offsets are
   // relative to the tile's first A row and the wave's first weight row.
-  uint32_t offa[ADMA], offb[4];
+  uint32_t offa[ADMA], offb[BDMA];
 #pragma unroll
   for (int i = 0; i < ADMA; ++i) {
     const int r = ar0 + i * 8 + (lane >> 3);
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     offa[i] = static_cast<uint32_t>(rr * static_cast<int>(lda) * 2 + chunk * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < BDMA; ++i) {
     const int r = wr0 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (r & 7);
     offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * static_cast<int>(p.ldb) * 2 + chunk * 16);
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
     _Pragma("unroll") for (int i_ = 0; i_ < ADMA; ++i_)                                              \
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(A + (offa[i_] + ko_)), MOE_LDS((S) + dst_a + i_ * 1024), 16, 0, 0); \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                 \
+    _Pragma("unroll") for (int i_ = 0; i_ < BDMA; ++i_)                                              \
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bw + (offb[i_] + ko_)), MOE_LDS((S) + dst_b + i_ * 1024), 16, 0, 0); \
   } while (0)
 
@@ -680,20 +690,20 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        *reinterpret_cast<floatx4_t*>(dma_part_frag<BM>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
+        *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
-  dma_store_tile<EPI, BM>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
 }
 
 // Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
 // partial tiles in chunk order and runs the tile epilogue.
-template <int EPI, int BM>
-__global__ __launch_bounds__(512, 1) void gemm_split_fixup_kernel(GemmParams p) {
+template <int EPI, int BM, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams p) {
   using namespace dma;
-  using C_ = Cfg<BM>;
+  using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
-  constexpr int FM = C_::FM;
+  constexpr int FM = C_::FM, FN = C_::FN;
   __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
   const SplitPlan sp = split_plan<BNO>(p, p.K / BK / 2);
   const int b = blockIdx.x;
@@ -706,16 +716,17 @@ __global__ __launch_bounds__(512, 1) void gemm_split_fixup_kernel(GemmParams p) 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM>(p.split_part, b * sp.s, wave, i, j) + lane * 4);
+      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM, W>(p.split_part, b * sp.s, wave, i, j) +
+                                                      lane * 4);
   for (int c = 1; c < sp.s; ++c) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM>(p.split_part, b * sp.s + c, wave, i, j) +
+        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM, W>(p.split_part, b * sp.s + c, wave, i, j) +
                                                          lane * 4);
   }
-  dma_store_tile<EPI, BM>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -868,7 +879,7 @@ enum TileCfg {
 };
 constexpr int tile_rows(int cfg) { return (cfg == kReg256 || cfg == kDma256) ? 256 : 128; }
 
-template <int EPI, int BM>
+template <int EPI, int BM, int W>
 hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
@@ -877,12 +888,13 @@ hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   // a k-split tail runs at most total - r + kSplitUnits workgroups
   if (p.split_part) grid += kSplitUnits;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI, BM>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
+  constexpr int NTH = dma::Cfg<BM, W>::NTH;
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, BM, W>), dim3(static_cast<unsigned>(grid)), dim3(NTH), 0, s, p);
   if (p.split_part) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // split tiles: r <= kSplitUnits / 2 (each is cut at least in two)
-    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, BM>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, BM, W>), dim3(kSplitUnits / 2), dim3(NTH), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -903,8 +915,8 @@ hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t
     return run_bf16<128, 128, 2, 2, EPI, true>(p, max_mtiles, s);
   } else {
     switch (cfg) {
-      case kDma256: return run_dma<EPI, 256>(p, max_mtiles, s);
-      case kDma128: return run_dma<EPI, 128>(p, max_mtiles, s);
+      case kDma256: return run_dma<EPI, 256, 8>(p, max_mtiles, s);
+      case kDma128: return run_dma<EPI, 128, 8>(p, max_mtiles, s);
       default: return run_bf16<128, 128, 2, 2, EPI, false>(p, max_mtiles, s);
     }
   }
