@@ -15,8 +15,10 @@ launch = 4 * d * d_ff per kept (token, expert) pair, divided by that kernel's
 mean launch time, measured with hipEvents on the stream it runs on over the
 timed region. `decode` reports the Mixtral-shape decode layer (T = 1, 16, 64)
 in HBM GB/s of algorithmic bytes (every touched expert's three matrices once,
-the router weight, x and y). `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workload.
+the router weight, x and y): whole steps replayed from captured HIP graphs
+(`us_per_step`; eager launches in `us_per_step_eager`) and the expert FFN
+alone (`ffn_us`, from hipEvents on a separate pass). `cpu_baseline` times the
+fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -180,21 +182,37 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
         for _ in range(warmup):
             layer(xs[0])
         torch.cuda.synchronize()
+
+        def timed(run):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e6 / nslices
+
+        # eager launches, stage timing off
+        us_eager = timed(lambda: [layer(xi) for xi in xs])
+        # each step replayed from a captured HIP graph: no host launch gaps
+        graphs = [layer.capture(xi) for xi in xs]
+        for g in graphs[:warmup]:
+            g.replay()
+        us = timed(lambda: [g.replay() for g in graphs])
+        del graphs
+        # stage timing (hipEvents around the FFN launches) on a separate eager pass
         moe.timing_start(8 * nslices + 8)
-        t0 = time.perf_counter()
         for xi in xs:
             layer(xi)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         st = moe.timing_stop()
-        us = (t1 - t0) * 1e6 / nslices
         nbytes = sum(n * per_expert + fixed for n in touched) / nslices
         ffn_us = (st["ffn_up"][0] + st["ffn_down"][0]) * 1e3 / max(st["ffn_up"][1], 1)
-        out[f"T{T}"] = {"us_per_step": round(us, 2), "touched_experts": round(sum(touched) / nslices, 2),
+        out[f"T{T}"] = {"us_per_step": round(us, 2), "us_per_step_eager": round(us_eager, 2),
+                        "touched_experts": round(sum(touched) / nslices, 2),
                         "GB": round(nbytes / 1e9, 4), "GB_per_s": round(nbytes / us / 1e3, 1),
                         "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
                         "ffn_us": round(ffn_us, 2),
                         "ffn_GB_per_s": round((nbytes - fixed) / ffn_us / 1e3, 1),
+                        "ffn_hbm_frac": round((nbytes - fixed) / ffn_us / 1e3 / PEAK_HBM_GBS, 4),
                         "steps": nslices}
         log(f"decode T={T}: {out[f'T{T}']}")
     return out

@@ -282,6 +282,23 @@ class MoELayer:
                 o.inv_map, o.stats, self.ws, stream)
         return o
 
+    def capture(self, x):
+        """Capture one forward on the device tensor x into a HIP graph
+        (torch.cuda.CUDAGraph) and return it: each replay recomputes self.out
+        from x's contents at replay time, with no host launch work. The
+        library's kernels record no memset or copy nodes; stage timing must be
+        off while capturing."""
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self(x)  # one eager call outside the capture (library and device setup)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self(x)
+        return g
+
     def latest(self) -> dict:
         """Host copy of the router statistics (synchronises): aux loss, z-loss,
         dropped share and the per-expert token shares."""

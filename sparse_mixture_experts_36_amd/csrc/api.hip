@@ -101,6 +101,7 @@ struct FfnWs {
   void* h;
   moe::GroupDesc* groups;
   int32_t* tile_start;
+  int32_t* active;
   float* part;
   float* split_part;
 };
@@ -111,6 +112,7 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff + moe::kActPad) * act_bytes(s.act_dtype));
   w.groups = c.take<moe::GroupDesc>(2 * G);
   w.tile_start = c.take<int32_t>(G + 1);
+  w.active = c.take<int32_t>(G + 1);
   w.part = nullptr;
   if (moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T))
     w.part = c.take<float>(
@@ -283,6 +285,7 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.y_shared = y_shared;
   a.groups = fw.groups;
   a.tile_start = fw.tile_start;
+  a.active = fw.active;
   a.part = fw.part;
   a.split_part = fw.split_part;
   return a;

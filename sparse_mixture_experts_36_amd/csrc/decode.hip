@@ -15,9 +15,13 @@
 //  - every load of two k-steps is issued before the first MFMA that needs them
 //    (a scheduling barrier keeps the compiler from interleaving and draining);
 //  - the token rows (16, 32 or 64 per pass, the MFMA's M) come from L2;
+//  - waves run over the groups that have rows only (the plan kernel lists
+//    them), so a token's two experts do not dispatch work for all eight;
 //  - when few experts are touched, k is split across waves; fp32 partials are
 //    then summed in split order by a second kernel that also applies the
 //    activation or the bias (bit-for-bit reproducible).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -52,6 +56,7 @@ struct StreamParams {
   int32_t n_routed, n_groups;
   int32_t epi;               // 0 GELU (+b1), 1 SwiGLU, 2 plain (+b2)
   const GroupDesc* groups;
+  const int32_t* active;     // [0]: groups with rows, [1..]: those groups
 };
 
 // 8 bf16 weights per uint4; e4m3 codes are decoded to bf16 in registers.
@@ -97,7 +102,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   const int nblk = swi ? p.Nout / 16 : p.Nout / 32;  // blocks per expert
   const int w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int per_g = nblk * p.splits;
-  const int g = w / per_g;
+  const int slot = w / per_g;  // waves run over the groups that have rows only
+  if (slot >= p.active[0]) return;
+  const int g = p.active[1 + slot];
   if (g >= p.n_groups) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
@@ -260,11 +267,14 @@ __global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p,
 }
 
 // k splits for one GEMM: double while the touched experts' blocks give fewer
-// than 4096 waves and every split keeps at least two 128-wide k-steps.
+// than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
+// which is more than HBM latency times bandwidth needs) and every split keeps
+// at least two 128-wide k-steps. Fewer splits means less partial traffic and,
+// at one split, no reduction pass.
 int pick_splits(int64_t K, int64_t blocks_touched) {
   const int64_t steps = K / KC;
   int s = 1;
-  while (blocks_touched * s < 4096 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
+  while (blocks_touched * s < 1024 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
   return s;
 }
 
@@ -346,7 +356,10 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.width = swi ? 2 * p.Nout : p.Nout;
   p.part = sp.up_splits > 1 ? part : nullptr;
   p.groups = up;
-  const int64_t up_blocks = static_cast<int64_t>(G) * (swi ? a.d_ff / 16 : a.d_ff / 32);
+  p.active = a.active;
+  // groups that can have rows: at most one routed expert per routed row, plus the shared ones
+  const int64_t slots = std::min<int64_t>(a.routed_row_cap, a.n_routed) + a.n_shared;
+  const int64_t up_blocks = slots * (swi ? a.d_ff / 16 : a.d_ff / 32);
   stage_mark(kStageFfnUp, false, s);
   hipError_t e = run_stream(p, sp.rb, fp8, up_blocks, s);
   if (e == hipSuccess && p.part) {
@@ -381,7 +394,7 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.width = p.Nout;
   p.part = sp.down_splits > 1 ? part : nullptr;
   p.groups = down;
-  const int64_t down_blocks = static_cast<int64_t>(G) * (a.d / 32);
+  const int64_t down_blocks = slots * (a.d / 32);
   stage_mark(kStageFfnDown, false, s);
   e = run_stream(p, sp.rb, fp8, down_blocks, s);
   if (e == hipSuccess && p.part) {

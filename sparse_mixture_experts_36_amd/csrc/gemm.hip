@@ -820,9 +820,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 // Routed expert e: rows [offsets[e], offsets[e+1]) of x_perm / h / y_perm,
 // clamped to the reserved routed rows. Shared expert s: the T token rows; its
 // hidden rows sit after the routed ones in h, its outputs in y_shared[s].
+// active[0] = the number of groups with rows, active[1..] those groups in order.
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, int32_t n_routed, int32_t n_shared,
                                                         int32_t T, int32_t cap, int32_t bm, GroupDesc* up,
-                                                        GroupDesc* down, int32_t* tile_start) {
+                                                        GroupDesc* down, int32_t* tile_start, int32_t* active) {
   __shared__ int32_t s_mt[kThreads + 8];
   const int tid = threadIdx.x;
   const int G = n_routed + n_shared;
@@ -849,12 +850,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, 
   }
   __syncthreads();
   if (tid == 0) {
-    int32_t acc = 0;
+    int32_t acc = 0, n_active = 0;
     for (int g = 0; g < G; ++g) {
       tile_start[g] = acc;
       acc += s_mt[g];
+      if (s_mt[g] > 0) active[1 + n_active++] = g;
     }
     tile_start[G] = acc;
+    active[0] = n_active;
   }
 }
 
@@ -956,7 +959,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   GroupDesc* down = a.groups + G;
   stage_mark(kStageFfnPlan, false, s);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a.offsets, a.n_routed, a.n_shared,
-                     static_cast<int32_t>(a.T), a.routed_row_cap, bm, up, down, a.tile_start);
+                     static_cast<int32_t>(a.T), a.routed_row_cap, bm, up, down, a.tile_start, a.active);
   stage_mark(kStageFfnPlan, true, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -86,6 +86,7 @@ struct FfnArgs {
   void* y_shared;             // [n_shared][T][d]
   GroupDesc* groups;          // [2][n_routed + n_shared] (workspace)
   int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
+  int32_t* active;            // [1 + n_routed + n_shared]: count, then the groups with rows (workspace)
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
   float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null
 };
