@@ -34,41 +34,62 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     }
   }
   constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int U = 2;             // chunks per thread whose loads are in flight together
   const int64_t nch = a.d / E;
-  for (int64_t c = threadIdx.x; c < nch; c += kThreads) {
-    float acc[E];
+  const int nsh = a.y_shared ? a.n_shared : 0;
+  for (int64_t c0 = threadIdx.x; c0 < nch; c0 += U * kThreads) {
+    // every load of the U chunks (k routed rows, then the shared rows) first
+    uint4 v[U][kMaxK + 4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    auto add = [&](const void* base, int64_t r, float w) {
-      const uint4 v = reinterpret_cast<const uint4*>(base)[r * nch + c];
-      if constexpr (BF16) {
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nch) break;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(u[e] & 0xFFFFu)), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(u[e] >> 16)), acc[2 * e + 1]);
-        }
-      } else {
-        acc[0] = fmaf(w, __uint_as_float(v.x), acc[0]);
-        acc[1] = fmaf(w, __uint_as_float(v.y), acc[1]);
-        acc[2] = fmaf(w, __uint_as_float(v.z), acc[2]);
-        acc[3] = fmaf(w, __uint_as_float(v.w), acc[3]);
-      }
-    };
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k && row[j] >= 0) v[u][j] = reinterpret_cast<const uint4*>(a.y_perm)[row[j] * nch + c];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k && row[j] >= 0) add(a.y_perm, row[j], g[j]);
-    if (a.y_shared)
-      for (int s = 0; s < a.n_shared; ++s) add(a.y_shared, static_cast<int64_t>(s) * a.T + t, 1.0f);
-    uint4 o;
-    if constexpr (BF16) {
-      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                     pack_bf16x2(acc[6], acc[7]));
-    } else {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3]));
+      for (int s = 0; s < 4; ++s)
+        if (s < nsh) v[u][kMaxK + s] = reinterpret_cast<const uint4*>(a.y_shared)[(s * a.T + t) * nch + c];
     }
-    reinterpret_cast<uint4*>(a.y)[t * nch + c] = o;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nch) break;
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      auto add = [&](const uint4& x, float w) {
+        if constexpr (BF16) {
+          const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xFFFFu)), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)), acc[2 * e + 1]);
+          }
+        } else {
+          acc[0] = fmaf(w, __uint_as_float(x.x), acc[0]);
+          acc[1] = fmaf(w, __uint_as_float(x.y), acc[1]);
+          acc[2] = fmaf(w, __uint_as_float(x.z), acc[2]);
+          acc[3] = fmaf(w, __uint_as_float(x.w), acc[3]);
+        }
+      };
+      // fixed order: routed slots ascending, then the shared experts
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k && row[j] >= 0) add(v[u][j], g[j]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < nsh) add(v[u][kMaxK + s], 1.0f);
+      uint4 o;
+      if constexpr (BF16) {
+        o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                       pack_bf16x2(acc[6], acc[7]));
+      } else {
+        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                       __float_as_uint(acc[3]));
+      }
+      reinterpret_cast<uint4*>(a.y)[t * nch + c] = o;
+    }
   }
 }
 

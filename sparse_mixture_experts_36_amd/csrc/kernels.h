@@ -33,6 +33,7 @@ struct RouteArgs {
   float aux_alpha;
 };
 constexpr int kRouteTokens = 64;  // tokens per route workgroup
+constexpr int kMaxRouteSplits = 16;  // k splits of the router GEMM (partial logit planes)
 int route_splits(int64_t T, int64_t d);  // k splits of the router GEMM
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 

@@ -132,6 +132,17 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
   if (t >= a.T) return;
   const int N = a.N, k = a.k;
   const int64_t blk = t / kPermTokens;
+  // the token's first 64*U chunks are loaded before the chain of index loads
+  // below, so the two latencies overlap
+  constexpr int U = 8;
+  const int64_t nchunk = a.x_perm ? a.d * a.act_bytes / 16 : 0;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = u * 64 + lane;
+    if (c < nchunk) v[u] = src[c];
+  }
   int64_t row[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
@@ -150,17 +161,15 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
     }
   }
   if (!a.x_perm) return;
-  const int64_t nchunk = a.d * a.act_bytes / 16;
   const int64_t ochunk = a.ld_out * a.act_bytes / 16;  // 16-byte chunks per x_perm row
-  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
   uint4* dst = reinterpret_cast<uint4*>(a.x_perm);
-  constexpr int U = 8;
   for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
-    uint4 v[U];
+    if (c0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * 64 + lane;
-      if (c < nchunk) v[u] = src[c];
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nchunk) v[u] = src[c];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {

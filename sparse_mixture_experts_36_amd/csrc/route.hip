@@ -173,8 +173,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, const floa
         if (a.logits_given) {
           v = a.logits[t * N + e];
         } else {
-          v = part[t * N + e];
-          for (int sp = 1; sp < splits; ++sp) v += part[(static_cast<int64_t>(sp) * T + t) * N + e];
+          // all split partials are loaded before the first add (one round
+          // trip, not one per split), then summed in split order
+          float pv[kMaxRouteSplits];
+#pragma unroll
+          for (int sp = 0; sp < kMaxRouteSplits; ++sp)
+            if (sp < splits) pv[sp] = part[(static_cast<int64_t>(sp) * T + t) * N + e];
+          v = pv[0];
+#pragma unroll
+          for (int sp = 1; sp < kMaxRouteSplits; ++sp)
+            if (sp < splits) v += pv[sp];
           if (a.b_router) v += a.b_router[e];
           a.logits[t * N + e] = v;
         }
@@ -352,7 +360,7 @@ hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
 int route_splits(int64_t T, int64_t d) {
   const int64_t nb = ceil_div(T, kRouteTokens), steps = d / kRK;
   int s = 1;
-  while (nb * s < 256 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 4) s *= 2;
+  while (nb * s < 256 && s < kMaxRouteSplits && steps % (2 * s) == 0 && steps / (2 * s) >= 4) s *= 2;
   return s;
 }
 
