@@ -112,6 +112,33 @@ def measured_traffic():
     return int(float(fields["hbm bytes per launch"]))
 
 
+def vendor_gemm_context(steps=20):
+    """Context for the grouped GEMM: torch.matmul (the ROCm BLAS library) on
+    one expert's GEMMs of the Mixtral prefill layer, at the rows one expert gets
+    (1024 = 4096 tokens x top-2 / 8 experts) and at 8192 rows, bf16. Prints
+    TFLOP/s per shape; nothing here is part of the layer."""
+    import torch
+    d, d_ff = 4096, 14336
+    out = {}
+    for M in (1024, 8192):
+        for name, (K, Nn) in {"up (W1|W3)": (d, 2 * d_ff), "down (W2)": (d_ff, d)}.items():
+            a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(Nn, K, device="cuda", dtype=torch.bfloat16)
+            bt = b.t()  # [K][N] view: the NT product of the layer
+            for _ in range(3):
+                torch.matmul(a, bt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                torch.matmul(a, bt)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            out[f"M={M} {name}"] = {"ms": round(ms, 4), "TFLOP/s": round(2.0 * M * K * Nn / ms / 1e9, 1)}
+    print(json.dumps({"vendor_gemm_bf16": out}), flush=True)
+
+
 def copy_calibration():
     """A plain streaming kernel of known traffic (x * 1 over 1 GiB of fp32:
     1 GiB read, 1 GiB written), run under rocprofv3 --pmc to scale FETCH_SIZE
@@ -259,6 +286,8 @@ def main():
                     help="only the decode shapes (T = 1, 16, 64) on the prefill weights; prints their JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel that scales the PMC byte counters")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time only torch.matmul on one expert's GEMM shapes (context for the grouped GEMM)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -273,6 +302,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.vendor_gemm:
+        vendor_gemm_context()
         return
     moe.lib()  # raises when the HIP library is missing: there is no fallback
     wl = gen.WORKLOADS[args.workload]

@@ -30,7 +30,8 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int KC = 128;        // k per step
-constexpr int KU = 2;          // steps whose loads are issued together
+// KU: k-steps whose loads are issued together (a template argument: 2, or 4
+// when few waves run and each must keep more bytes in flight)
 
 struct StreamParams {
   const uint16_t* A_r;       // routed A rows (x_perm or h)
@@ -93,7 +94,7 @@ __device__ __forceinline__ float epilogue(int epi, float a, float b, float bias)
 }
 
 // Wave -> (group g, block nb of 32 weight rows, k split sp).
-template <int RB, bool FP8>
+template <int RB, bool FP8, int KU>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   constexpr int FN = 2;  // 16-row weight tiles per wave
   const int lane = threadIdx.x & 63;
@@ -281,12 +282,19 @@ int pick_splits(int64_t K, int64_t blocks_touched) {
 hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, hipStream_t s) {
   const int64_t waves = blocks * p.splits;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
+  // at most 8 waves per CU: four k-steps per burst (their registers still fit 2 waves per SIMD)
+  const bool deep = rb == 1 && waves <= 2048;
 #define MOE_STREAM_CASE(R)                                                                          \
   if (rb == R) {                                                                                    \
-    if (fp8) hipLaunchKernelGGL((stream_kernel<R, true>), grid, dim3(kThreads), 0, s, p);           \
-    else hipLaunchKernelGGL((stream_kernel<R, false>), grid, dim3(kThreads), 0, s, p);              \
+    if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, 2>), grid, dim3(kThreads), 0, s, p);        \
+    else hipLaunchKernelGGL((stream_kernel<R, false, 2>), grid, dim3(kThreads), 0, s, p);           \
   }
-  MOE_STREAM_CASE(1) MOE_STREAM_CASE(2) MOE_STREAM_CASE(4)
+  if (deep) {
+    if (fp8) hipLaunchKernelGGL((stream_kernel<1, true, 4>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((stream_kernel<1, false, 4>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    MOE_STREAM_CASE(1) MOE_STREAM_CASE(2) MOE_STREAM_CASE(4)
+  }
 #undef MOE_STREAM_CASE
   return hipGetLastError();
 }
