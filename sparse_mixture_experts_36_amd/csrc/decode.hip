@@ -9,11 +9,13 @@
 // expert's weights once from HBM, so the design maximises bytes in flight:
 //  - a wave owns 32 weight rows of one expert (SwiGLU up: the same 16 rows of
 //    W1 and W3; otherwise 32 rows of W1 or W2) and a k range, and streams them
-//    from memory straight into MFMA operand registers (no LDS): lane (c, q)
-//    takes 64 contiguous bytes of row c per 128-wide k-step, the four lanes of
-//    a row covering its 256 bytes;
-//  - every load of two k-steps is issued before the first MFMA that needs them
-//    (a scheduling barrier keeps the compiler from interleaving and draining);
+//    from memory straight into MFMA operand registers (no LDS): per 128-wide
+//    k-step, each bf16 load instruction reads 64 contiguous bytes of each of
+//    16 rows;
+//  - every load of two (or four) k-steps is issued before the first MFMA that
+//    needs them (a scheduling barrier keeps the compiler from interleaving and
+//    draining): each row is then read in runs of 512 bytes or more, which HBM
+//    serves better than the same bytes requested one step at a time;
 //  - the token rows (16, 32 or 64 per pass, the MFMA's M) come from L2;
 //  - waves run over the groups that have rows only (the plan kernel lists
 //    them), so a token's two experts do not dispatch work for all eight;
@@ -30,8 +32,9 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int KC = 128;        // k per step
-// KU: k-steps whose loads are issued together (a template argument: 2, or 4
-// when few waves run and each must keep more bytes in flight)
+constexpr int kTStride = 64;   // bf16 weight bytes between MFMA t and t + 1 of a step
+// KU: k-steps in flight per wave (a template argument: 1, 2 or 4; 4 when few
+// waves run and each must keep more bytes in flight)
 
 struct StreamParams {
   const uint16_t* A_r;       // routed A rows (x_perm or h)
@@ -61,19 +64,21 @@ struct StreamParams {
 };
 
 // 8 bf16 weights per uint4; e4m3 codes are decoded to bf16 in registers.
+// One k-step of a weight row for lane (row, q): 32 weights from byte offset
+// `off` of a wave-uniform base (8 bf16 weights per uint4; e4m3 codes are
+// decoded to bf16 in registers).
 template <bool FP8>
-__device__ __forceinline__ void load_w(const char* base, int64_t elem, uint4 (&w)[4]) {
+__device__ __forceinline__ void load_w(const char* base, uint32_t off, uint4 (&w)[4]) {
   if constexpr (FP8) {
-    const uint4 q0 = *reinterpret_cast<const uint4*>(base + elem);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(base + elem + 16);
+    const uint4 q0 = *reinterpret_cast<const uint4*>(base + off);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(base + (off + 16));
     w[0] = make_uint4(q0.x, q0.y, 0, 0);
     w[1] = make_uint4(q0.z, q0.w, 0, 0);
     w[2] = make_uint4(q1.x, q1.y, 0, 0);
     w[3] = make_uint4(q1.z, q1.w, 0, 0);
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(base + elem * 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[t] = p[t];
+    for (int t = 0; t < 4; ++t) w[t] = *reinterpret_cast<const uint4*>(base + (off + kTStride * t));
   }
 }
 
@@ -101,7 +106,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   const int q = lane >> 4, c16 = lane & 15;
   const bool swi = (p.epi == 1);
   const int nblk = swi ? p.Nout / 16 : p.Nout / 32;  // blocks per expert
-  const int w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // the wave index is made wave-uniform, so that group, expert and base
+  // pointers live in scalar registers and loads take a 32-bit lane offset
+  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int per_g = nblk * p.splits;
   const int slot = w / per_g;  // waves run over the groups that have rows only
   if (slot >= p.active[0]) return;
@@ -113,23 +120,31 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   const bool shared = g >= p.n_routed;
   const int ew = shared ? g - p.n_routed : g;
   constexpr int WB = FP8 ? 1 : 2;
-  const int64_t eoff = static_cast<int64_t>(ew) * p.b_stride * WB;
-  const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
-  const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
-  const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const uint16_t* A = (shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda;
+  // k order inside a 128-wide step (the same for both operands, so any order
+  // gives the same sums): bf16 MFMA t takes k [32t, 32t + 32), lane group q
+  // its 8 k at 8q, so the four lanes of a row read 64 contiguous bytes per
+  // load; e4m3 lane group q takes k [32q, 32q + 32) in two 16-byte loads, MFMA
+  // t its 8 k at 8t
+  constexpr int QK = FP8 ? 32 : 8;         // k offset of lane group q
+  constexpr int AT = FP8 ? 16 : 64;        // A bytes between MFMA t and t + 1
   const int K = p.K, ks = K / p.splits;
   const int kbeg = sp * ks, nsteps = ks / KC;
-  // weight rows of the two tiles, and the output / partial columns they feed
+  // weight rows: SwiGLU up takes rows [n0, n0 + 16) of W1 (tile 0) and of W3
+  // (tile 1), otherwise rows [n0, n0 + 32) of one matrix; the bases point at
+  // (row n0, column kbeg), the lane offsets add row and k-group
   const int n0 = swi ? nb * 16 : nb * 32;
-  int64_t woff[FN];
-  const char* wbase[FN];
+  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb + kbeg) * WB;
+  const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
+  const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
+  const char* wbase[FN] = {Bw, swi ? B3w : Bw};
+  uint32_t woff[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = swi ? n0 + c16 : n0 + j * 16 + c16;
-    wbase[j] = (swi && j == 1) ? B3w : Bw;
-    woff[j] = static_cast<int64_t>(n) * p.ldb + kbeg + q * 32;
+    const int r = swi ? c16 : j * 16 + c16;
+    woff[j] = static_cast<uint32_t>((r * static_cast<int>(p.ldb) + q * QK) * WB);
   }
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
+  const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda + kbeg);
   float s_a = 1.f, s_b = 1.f;
   if (FP8) {
     const float* sc = shared ? p.scale_s : p.scale_r;
@@ -138,11 +153,16 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   }
 
   for (int r0 = 0; r0 < gd.rows; r0 += 16 * RB) {
-    const uint16_t* ap[RB];
+    // opaque to the optimiser, so that the first loads' addresses are formed
+    // here from base + offset, not hoisted out of the pass loop as 64-bit pointers
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(woff[j]));
+    const char* Ap = A + static_cast<int64_t>(r0) * lda * 2;
+    uint32_t aoff[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int arow = min(r0 + rb * 16 + c16, gd.rows - 1);  // rows past the group compute garbage
-      ap[rb] = A + static_cast<int64_t>(arow) * lda + kbeg + q * 32;
+      const int arow = min(rb * 16 + c16, gd.rows - 1 - r0);  // rows past the group compute garbage
+      aoff[rb] = static_cast<uint32_t>((arow * static_cast<int>(lda) + q * QK) * 2);
     }
     floatx4_t acc[RB][FN];
 #pragma unroll
@@ -154,13 +174,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
       uint4 bw[KU][FN][4], a[KU][RB][4];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const int kk = min(st + u, nsteps - 1) * KC;  // a step past the end re-reads the last one
+        const uint32_t kk = static_cast<uint32_t>(min(st + u, nsteps - 1) * KC);  // a step past the end re-reads the last one
 #pragma unroll
-        for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk, bw[u][j]);
+        for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk * WB, bw[u][j]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) a[u][rb][t] = *reinterpret_cast<const uint4*>(ap[rb] + kk + t * 8);
+          for (int t = 0; t < 4; ++t)
+            a[u][rb][t] = *reinterpret_cast<const uint4*>(Ap + (aoff[rb] + kk * 2 + t * AT));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -267,6 +288,138 @@ __global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p,
   *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
 }
 
+// ---- at most two token rows per expert: a weight-row GEMV on the vector ALUs
+//
+// With one or two rows an MFMA tile would be 15/16 padding, and the k split it
+// needs for enough waves costs a partials pass. Here a wave owns NR weight rows
+// of one expert (SwiGLU up: NR/2 rows of W1 and the same NR/2 rows of W3) and
+// reads each over the whole k range in 1 KB segments, lane l taking 16 bytes
+// at 16 l. A burst loads U segments of all NR rows, so each row is read in runs
+// of U KB. Products are bf16 pair dots accumulated in fp32; each lane's sums
+// are reduced across the wave once, at the end (a fixed butterfly order).
+constexpr int kSeg = 1024;  // bytes of one weight row per segment
+constexpr int kGemvU = 4;   // segments per row and burst
+
+template <int R, bool FP8, int NR, int U>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const int lane = threadIdx.x & 63;
+  const bool swi = (p.epi == 1);
+  const int cols = swi ? NR / 2 : NR;  // output columns per wave
+  const int nblk = p.Nout / cols;
+  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = w / nblk;  // waves run over the groups that have rows only
+  if (slot >= p.active[0]) return;
+  const int g = p.active[1 + slot];
+  if (g >= p.n_groups) return;
+  const GroupDesc gd = p.groups[g];
+  if (gd.rows <= 0) return;
+  const int n0 = (w % nblk) * cols;
+  const bool shared = g >= p.n_routed;
+  const int ew = shared ? g - p.n_routed : g;
+  constexpr int WB = FP8 ? 1 : 2;
+  constexpr int KSEG = kSeg / WB;   // k per segment
+  constexpr int XW = FP8 ? 2 : 1;   // activation uint4 per lane and segment
+  const int nseg = p.K / KSEG;
+  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb) * WB;
+  const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
+  const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
+  const char* wrow[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const bool third = swi && j >= NR / 2;
+    wrow[j] = (third ? B3w : Bw) + static_cast<int64_t>(third ? j - NR / 2 : j) * p.ldb * WB;
+  }
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
+  const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda);
+  const char* arow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) arow[r] = A + static_cast<int64_t>(min(r, gd.rows - 1)) * lda * 2;
+  // lane l: weight bytes [16 l, 16 l + 16) of a segment, i.e. k from
+  // seg * KSEG + l * 16 / WB, and the bf16 activations of those k
+  const uint32_t wl = static_cast<uint32_t>(lane) * 16;
+  const uint32_t al = static_cast<uint32_t>(lane) * 16 * XW;
+  float s_a = 1.f, s_b = 1.f;
+  if (FP8) {
+    const float* sc = shared ? p.scale_s : p.scale_r;
+    s_a = sc[ew * 3 + p.scale_col];
+    s_b = swi ? sc[ew * 3 + p.scale_col + 1] : s_a;
+  }
+
+  float acc[NR][R];
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = 0.f;
+
+  for (int s0 = 0; s0 < nseg; s0 += U) {
+    uint4 wv[U][NR], xv[U][R][XW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t sg = static_cast<uint32_t>(min(s0 + u, nseg - 1));  // a segment past the end re-reads the last one
+#pragma unroll
+      for (int j = 0; j < NR; ++j) wv[u][j] = *reinterpret_cast<const uint4*>(wrow[j] + (wl + sg * kSeg));
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int x = 0; x < XW; ++x)
+          xv[u][r][x] = *reinterpret_cast<const uint4*>(arow[r] + (al + sg * (KSEG * 2) + 16 * x));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= nseg) break;
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        uint32_t wd[4 * XW];
+        if constexpr (FP8) {
+          const uint2 b0 = e4m3x4_to_bf16x4(wv[u][j].x), b1 = e4m3x4_to_bf16x4(wv[u][j].y);
+          const uint2 b2 = e4m3x4_to_bf16x4(wv[u][j].z), b3 = e4m3x4_to_bf16x4(wv[u][j].w);
+          wd[0] = b0.x; wd[1] = b0.y; wd[2] = b1.x; wd[3] = b1.y;
+          wd[4] = b2.x; wd[5] = b2.y; wd[6] = b3.x; wd[7] = b3.y;
+        } else {
+          wd[0] = wv[u][j].x; wd[1] = wv[u][j].y; wd[2] = wv[u][j].z; wd[3] = wv[u][j].w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float c = acc[j][r];
+#pragma unroll
+          for (int x = 0; x < XW; ++x) {
+            const uint32_t xd[4] = {xv[u][r][x].x, xv[u][r][x].y, xv[u][r][x].z, xv[u][r][x].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[4 * x + i]),
+                                                  __builtin_bit_cast(bf16x2, xd[i]), c, false);
+          }
+          acc[j][r] = c;
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc[j][r] += __shfl_xor(acc[j][r], o);
+
+  // lane c < cols writes output column n0 + c of each row
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= gd.rows) break;
+    uint16_t* C = (shared ? p.C_s : p.C_r) + (static_cast<int64_t>(gd.c_row0) + r) * p.ldc + n0;
+    const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      if (c >= cols || lane != c) continue;
+      const float v = swi ? epilogue(1, acc[c][r] * s_a, acc[(c + NR / 2) % NR][r] * s_b, 0.f)
+                          : epilogue(p.epi, acc[c][r] * s_a, 0.f, bias ? bias[c] : 0.f);
+      C[c] = f32_to_bf16(v);
+    }
+  }
+}
+
 // k splits for one GEMM: double while the touched experts' blocks give fewer
 // than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
 // which is more than HBM latency times bandwidth needs) and every split keeps
@@ -284,18 +437,43 @@ hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, h
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
   // at most 8 waves per CU: four k-steps per burst (their registers still fit 2 waves per SIMD)
   const bool deep = rb == 1 && waves <= 2048;
-#define MOE_STREAM_CASE(R)                                                                          \
-  if (rb == R) {                                                                                    \
-    if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, 2>), grid, dim3(kThreads), 0, s, p);        \
-    else hipLaunchKernelGGL((stream_kernel<R, false, 2>), grid, dim3(kThreads), 0, s, p);           \
-  }
+#define MOE_STREAM_LAUNCH(R, U)                                                                     \
+  if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, U>), grid, dim3(kThreads), 0, s, p);          \
+  else hipLaunchKernelGGL((stream_kernel<R, false, U>), grid, dim3(kThreads), 0, s, p);
   if (deep) {
-    if (fp8) hipLaunchKernelGGL((stream_kernel<1, true, 4>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((stream_kernel<1, false, 4>), grid, dim3(kThreads), 0, s, p);
+    MOE_STREAM_LAUNCH(1, 4)
+  } else if (rb == 1) {
+    MOE_STREAM_LAUNCH(1, 2)
+  } else if (rb == 2) {
+    MOE_STREAM_LAUNCH(2, 2)
   } else {
-    MOE_STREAM_CASE(1) MOE_STREAM_CASE(2) MOE_STREAM_CASE(4)
+    MOE_STREAM_LAUNCH(4, 2)
   }
-#undef MOE_STREAM_CASE
+#undef MOE_STREAM_LAUNCH
+  return hipGetLastError();
+}
+
+// The GEMV path: at most two rows per group and whole 1 KB segments per row.
+bool use_gemv(const FfnArgs& a) {
+  const int64_t kseg = a.w_dtype == 2 ? kSeg : kSeg / 2;
+  return a.T <= 2 && a.d % kseg == 0 && a.d_ff % kseg == 0;
+}
+
+// NR = 8 weight rows per wave while that still gives 2048 waves, else 4.
+hipError_t run_gemv(const StreamParams& p, int rows, bool fp8, int64_t slots, hipStream_t s) {
+  const bool swi = (p.epi == 1);
+  const int nr = slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4;
+  const int64_t waves = slots * p.Nout / (swi ? nr / 2 : nr);
+  const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
+#define MOE_GEMV_LAUNCH(R, NR)                                                                      \
+  if (fp8) hipLaunchKernelGGL((gemv_kernel<R, true, NR, kGemvU>), grid, dim3(kThreads), 0, s, p);   \
+  else hipLaunchKernelGGL((gemv_kernel<R, false, NR, kGemvU>), grid, dim3(kThreads), 0, s, p);
+  if (rows == 1) {
+    if (nr == 8) { MOE_GEMV_LAUNCH(1, 8) } else { MOE_GEMV_LAUNCH(1, 4) }
+  } else {
+    if (nr == 8) { MOE_GEMV_LAUNCH(2, 8) } else { MOE_GEMV_LAUNCH(2, 4) }
+  }
+#undef MOE_GEMV_LAUNCH
   return hipGetLastError();
 }
 
@@ -368,8 +546,13 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   // groups that can have rows: at most one routed expert per routed row, plus the shared ones
   const int64_t slots = std::min<int64_t>(a.routed_row_cap, a.n_routed) + a.n_shared;
   const int64_t up_blocks = slots * (swi ? a.d_ff / 16 : a.d_ff / 32);
+  const bool gemv = use_gemv(a);
+  if (gemv) {
+    p.splits = 1;
+    p.part = nullptr;
+  }
   stage_mark(kStageFfnUp, false, s);
-  hipError_t e = run_stream(p, sp.rb, fp8, up_blocks, s);
+  hipError_t e = gemv ? run_gemv(p, static_cast<int>(a.T), fp8, slots, s) : run_stream(p, sp.rb, fp8, up_blocks, s);
   if (e == hipSuccess && p.part) {
     const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
     hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);
@@ -403,8 +586,12 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.part = sp.down_splits > 1 ? part : nullptr;
   p.groups = down;
   const int64_t down_blocks = slots * (a.d / 32);
+  if (gemv) {
+    p.splits = 1;
+    p.part = nullptr;
+  }
   stage_mark(kStageFfnDown, false, s);
-  e = run_stream(p, sp.rb, fp8, down_blocks, s);
+  e = gemv ? run_gemv(p, static_cast<int>(a.T), fp8, slots, s) : run_stream(p, sp.rb, fp8, down_blocks, s);
   if (e == hipSuccess && p.part) {
     const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
     hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);

@@ -161,6 +161,12 @@ FFN_CASES = [
     dict(T=40, N=32, k=4, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=1536, wdt=gen.E4M3),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=512, n_shared=1, pad=64),       # decode path, padded
+    # one or two tokens with whole 1 KB weight segments: the vector-ALU GEMV
+    dict(T=2, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=2048, n_shared=1, pad=64),      # two rows, shared, padded; up 8 rows a wave
+    dict(T=1, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=4096, wdt=gen.E4M3),            # e4m3; up 8 rows a wave, down 4
+    dict(T=2, N=4, k=1, act=gen.GELU, d=1024, d_ff=1024, wdt=gen.E4M3, biases=True, n_shared=1),
+    dict(T=2, N=16, k=2, act=gen.GELU, d=512, d_ff=4096, biases=True),              # up 8 rows a wave, down 4
+    dict(T=1, N=8, k=2, act=gen.SWIGLU, d=640, d_ff=1024),                           # d not whole segments: MFMA streaming
     dict(T=400, N=16, k=1, act=gen.GELU, d=256, d_ff=512, wdt=gen.E4M3, biases=True, pad=32),  # fp8, padded
     dict(T=130, N=8, k=2, act=gen.SWIGLU, d=128, d_ff=256, dt=gen.F32, n_shared=1, pad=16),    # fp32, padded
     # prefill-sized calls (>= 2048 expert rows): the LDS-DMA tiles, 128 x 256
