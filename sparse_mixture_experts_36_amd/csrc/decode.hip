@@ -33,6 +33,8 @@ namespace {
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int KC = 128;        // k per step
 constexpr int kTStride = 64;   // bf16 weight bytes between MFMA t and t + 1 of a step
+// s_waitcnt immediate for vmcnt(n), the other counters left at their maximum
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 // KU: k-steps in flight per wave (a template argument: 1, 2 or 4; 4 when few
 // waves run and each must keep more bytes in flight)
 
@@ -99,8 +101,23 @@ __device__ __forceinline__ float epilogue(int epi, float a, float b, float bias)
 }
 
 // Wave -> (group g, block nb of 32 weight rows, k split sp).
-template <int RB, bool FP8, int KU>
+//
+// SHARED_A (RB >= 2, KU = 2): the four waves of a workgroup take four
+// consecutive blocks of one expert at one k range, and the token rows of each
+// burst (16 RB rows x 256 k) are brought into LDS once per workgroup by LDS DMA
+// (the weight loads fly at the same time) instead of once per wave into
+// registers. Row R's 16-byte chunk c sits at position c ^ (R & 15), so the 16
+// lanes that read one chunk of 16 rows hit 16 different bank groups. The two
+// LDS buffers alternate by burst, one barrier per burst; the host guarantees
+// an even number of bursts per pass.
+template <int RB, bool FP8, int KU, bool SHARED_A>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
+  static_assert(!SHARED_A || (RB >= 2 && KU == 2), "shared token rows: 32 or 64 rows, two k-steps a burst");
+  constexpr int AROWB = KU * KC * 2;                        // bytes of one token row per burst
+  constexpr int ATILE = SHARED_A ? 16 * RB * AROWB : 16;    // bytes of the burst's token rows
+  constexpr int ADMA = ATILE / (kThreads * 16);             // DMA instructions per lane and burst
+  __shared__ __attribute__((aligned(16))) char abuf0[ATILE];
+  __shared__ __attribute__((aligned(16))) char abuf1[ATILE];
   constexpr int FN = 2;  // 16-row weight tiles per wave
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, c16 = lane & 15;
@@ -116,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   if (g >= p.n_groups) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
-  const int nb = (w % per_g) / p.splits, sp = w % p.splits;
+  const int nb = SHARED_A ? (w % per_g) % nblk : (w % per_g) / p.splits;
+  const int sp = SHARED_A ? (w % per_g) / nblk : w % p.splits;
   const bool shared = g >= p.n_routed;
   const int ew = shared ? g - p.n_routed : g;
   constexpr int WB = FP8 ? 1 : 2;
@@ -170,6 +188,66 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[rb][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (SHARED_A) {
+      // DMA instruction i of wave v fills bytes [1024 (v ADMA + i), +1024) of
+      // the tile: lane L writes row R = (1024 (v ADMA + i) + 16 L) / AROWB at
+      // position L' = L % (AROWB / 16), which holds logical chunk L' ^ (R & 15)
+      // (k-step L' / 16 of the burst, k 8 (L' % 16) of that step)
+      const int wv = (threadIdx.x >> 6);
+      uint32_t doff[ADMA];
+#pragma unroll
+      for (int i = 0; i < ADMA; ++i) {
+        const int byte = (wv * ADMA + i) * 1024 + lane * 16;
+        const int R = byte / AROWB, pos = (byte % AROWB) / 16;
+        const int c = pos ^ (R & 15);
+        const int arow = min(R, gd.rows - 1 - r0);
+        doff[i] = static_cast<uint32_t>(arow * static_cast<int>(lda) * 2 + (c >> 4) * (KC * 2) + (c & 15) * 16);
+      }
+      // lane (c16, q) of MFMA t, k-step u, row block rb: logical chunk u*16 + ch(t, q)
+      auto burst = [&](char* abuf, int st) __attribute__((always_inline)) {
+        const uint32_t kb = static_cast<uint32_t>(st * KC * 2);
+#pragma unroll
+        for (int i = 0; i < ADMA; ++i)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(Ap + (doff[i] + kb)),
+                                           (__attribute__((address_space(3))) void*)(abuf + (wv * ADMA + i) * 1024),
+                                           16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 bw[KU][FN][4];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const uint32_t kk = static_cast<uint32_t>((st + u) * KC);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk * WB, bw[u][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's token-row DMA has landed (loads complete in issue order)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(KU * FN * (FP8 ? 2 : 4)));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int ch = u * 16 + (FP8 ? q * 4 + t : t * 4 + q);
+            uint4 av[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const int R = rb * 16 + c16;
+              av[rb] = *reinterpret_cast<const uint4*>(abuf + R * AROWB + ((ch ^ (R & 15)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const uint4 b = as_bf16<FP8>(bw[u][j][t]);
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(av[rb], b, acc[rb][j]);
+            }
+          }
+      };
+      for (int st = 0; st < nsteps; st += 2 * KU) {
+        burst(abuf0, st);
+        burst(abuf1, st + KU);
+      }
+    } else {
     for (int st = 0; st < nsteps; st += KU) {
       uint4 bw[KU][FN][4], a[KU][RB][4];
 #pragma unroll
@@ -196,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
             for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(a[u][rb][t], b, acc[rb][j]);
           }
       }
+    }
     }
 
     // tile j, lane (q, c16): rows r0 + rb*16 + 4q + i, weight row n of tile j
@@ -298,7 +377,6 @@ __global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p,
 // of U KB. Products are bf16 pair dots accumulated in fp32; each lane's sums
 // are reduced across the wave once, at the end (a fixed butterfly order).
 constexpr int kSeg = 1024;  // bytes of one weight row per segment
-constexpr int kGemvU = 4;   // segments per row and burst
 
 template <int R, bool FP8, int NR, int U>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
@@ -437,17 +515,19 @@ hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, h
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
   // at most 8 waves per CU: four k-steps per burst (their registers still fit 2 waves per SIMD)
   const bool deep = rb == 1 && waves <= 2048;
-#define MOE_STREAM_LAUNCH(R, U)                                                                     \
-  if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, U>), grid, dim3(kThreads), 0, s, p);          \
-  else hipLaunchKernelGGL((stream_kernel<R, false, U>), grid, dim3(kThreads), 0, s, p);
+  // 32 or 64 token rows: shared through LDS when the passes hold whole burst pairs
+  const bool shared_a = rb >= 2 && (p.K / p.splits / KC) % 4 == 0;
+#define MOE_STREAM_LAUNCH(R, U, SA)                                                                 \
+  if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, U, SA>), grid, dim3(kThreads), 0, s, p);      \
+  else hipLaunchKernelGGL((stream_kernel<R, false, U, SA>), grid, dim3(kThreads), 0, s, p);
   if (deep) {
-    MOE_STREAM_LAUNCH(1, 4)
+    MOE_STREAM_LAUNCH(1, 4, false)
   } else if (rb == 1) {
-    MOE_STREAM_LAUNCH(1, 2)
+    MOE_STREAM_LAUNCH(1, 2, false)
   } else if (rb == 2) {
-    MOE_STREAM_LAUNCH(2, 2)
+    if (shared_a) { MOE_STREAM_LAUNCH(2, 2, true) } else { MOE_STREAM_LAUNCH(2, 2, false) }
   } else {
-    MOE_STREAM_LAUNCH(4, 2)
+    if (shared_a) { MOE_STREAM_LAUNCH(4, 2, true) } else { MOE_STREAM_LAUNCH(4, 2, false) }
   }
 #undef MOE_STREAM_LAUNCH
   return hipGetLastError();
@@ -459,19 +539,20 @@ bool use_gemv(const FfnArgs& a) {
   return a.T <= 2 && a.d % kseg == 0 && a.d_ff % kseg == 0;
 }
 
-// NR = 8 weight rows per wave while that still gives 2048 waves, else 4.
+// NR = 8 weight rows per wave while that still gives 2048 waves, else 4;
+// each burst is 32 KB of one wave's rows.
 hipError_t run_gemv(const StreamParams& p, int rows, bool fp8, int64_t slots, hipStream_t s) {
   const bool swi = (p.epi == 1);
   const int nr = slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4;
   const int64_t waves = slots * p.Nout / (swi ? nr / 2 : nr);
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
-#define MOE_GEMV_LAUNCH(R, NR)                                                                      \
-  if (fp8) hipLaunchKernelGGL((gemv_kernel<R, true, NR, kGemvU>), grid, dim3(kThreads), 0, s, p);   \
-  else hipLaunchKernelGGL((gemv_kernel<R, false, NR, kGemvU>), grid, dim3(kThreads), 0, s, p);
+#define MOE_GEMV_LAUNCH(R, NR, U)                                                                   \
+  if (fp8) hipLaunchKernelGGL((gemv_kernel<R, true, NR, U>), grid, dim3(kThreads), 0, s, p);        \
+  else hipLaunchKernelGGL((gemv_kernel<R, false, NR, U>), grid, dim3(kThreads), 0, s, p);
   if (rows == 1) {
-    if (nr == 8) { MOE_GEMV_LAUNCH(1, 8) } else { MOE_GEMV_LAUNCH(1, 4) }
+    if (nr == 8) { MOE_GEMV_LAUNCH(1, 8, 4) } else { MOE_GEMV_LAUNCH(1, 4, 8) }
   } else {
-    if (nr == 8) { MOE_GEMV_LAUNCH(2, 8) } else { MOE_GEMV_LAUNCH(2, 4) }
+    if (nr == 8) { MOE_GEMV_LAUNCH(2, 8, 4) } else { MOE_GEMV_LAUNCH(2, 4, 8) }
   }
 #undef MOE_GEMV_LAUNCH
   return hipGetLastError();

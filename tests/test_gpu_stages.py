@@ -161,6 +161,12 @@ FFN_CASES = [
     dict(T=40, N=32, k=4, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=1536, wdt=gen.E4M3),
     dict(T=16, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=512, n_shared=1, pad=64),       # decode path, padded
+    # 32- or 64-row passes whose k range holds whole pairs of two-step bursts:
+    # token rows shared through LDS by the four waves of a workgroup
+    dict(T=64, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=2048, zipf=1.5),             # 32 rows; skewed: two-pass groups
+    dict(T=100, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=2048, pad=64),              # 64 rows, padded, split down
+    dict(T=64, N=16, k=1, act=gen.GELU, d=1024, d_ff=1024, wdt=gen.E4M3, biases=True),  # e4m3, split in two
+    dict(T=40, N=32, k=4, act=gen.SWIGLU, d=512, d_ff=512, n_shared=2, zipf=1.0),  # shared experts
     # one or two tokens with whole 1 KB weight segments: the vector-ALU GEMV
     dict(T=2, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=2048, n_shared=1, pad=64),      # two rows, shared, padded; up 8 rows a wave
     dict(T=1, N=8, k=2, act=gen.SWIGLU, d=1024, d_ff=4096, wdt=gen.E4M3),            # e4m3; up 8 rows a wave, down 4
