@@ -493,14 +493,20 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   if (!expert_offsets) expert_offsets = w.offsets;
   if (!perm_token) perm_token = w.perm_token;
 
+  // decode-sized layers: the expert kernels read routed rows from x through
+  // perm_token, so the permutation copies no rows
+  const bool gather = moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T);
   hipError_t e = moe::launch_route(
       route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
   if (e == hipSuccess)
-    e = moe::launch_permute(
-        perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, w.x_perm, ld_xp, stats, pw), stream);
-  if (e == hipSuccess)
-    e = moe::launch_grouped_ffn(
-        ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw), stream);
+    e = moe::launch_permute(perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map,
+                                      gather ? nullptr : w.x_perm, ld_xp, stats, pw),
+                            stream);
+  if (e == hipSuccess) {
+    moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
+    if (gather) fa.gather = perm_token;
+    e = moe::launch_grouped_ffn(fa, stream);
+  }
   if (e == hipSuccess) {
     moe::CombineArgs a{};
     a.T = s.T;

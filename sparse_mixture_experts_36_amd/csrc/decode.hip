@@ -39,7 +39,8 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 1
 // waves run and each must keep more bytes in flight)
 
 struct StreamParams {
-  const uint16_t* A_r;       // routed A rows (x_perm or h)
+  const uint16_t* A_r;       // routed A rows (x_perm or h; x when gathered)
+  const int32_t* gather;     // routed A row r of a group is row gather[a_row0 + r] of A_r, or null
   const uint16_t* A_s;       // shared A rows (x or h)
   int64_t lda_r, lda_s;      // A row pitches (elements)
   int64_t ldb;               // weight row pitch (elements)
@@ -162,7 +163,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
     woff[j] = static_cast<uint32_t>((r * static_cast<int>(p.ldb) + q * QK) * WB);
   }
   const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda + kbeg);
+  // A rows are addressed from the buffer's start (column kbeg): row r of the
+  // group is buffer row a_row0 + r, or gather[a_row0 + r]
+  const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + kbeg);
+  const int32_t* gth = shared ? nullptr : p.gather;
   float s_a = 1.f, s_b = 1.f;
   if (FP8) {
     const float* sc = shared ? p.scale_s : p.scale_r;
@@ -175,12 +179,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
     // here from base + offset, not hoisted out of the pass loop as 64-bit pointers
 #pragma unroll
     for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(woff[j]));
-    const char* Ap = A + static_cast<int64_t>(r0) * lda * 2;
+    const char* Ap = A;
     uint32_t aoff[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int arow = min(rb * 16 + c16, gd.rows - 1 - r0);  // rows past the group compute garbage
-      aoff[rb] = static_cast<uint32_t>((arow * static_cast<int>(lda) + q * QK) * 2);
+      const int arow = gd.a_row0 + min(r0 + rb * 16 + c16, gd.rows - 1);  // rows past the group compute garbage
+      const int src = gth ? gth[arow] : arow;
+      aoff[rb] = static_cast<uint32_t>((src * static_cast<int>(lda) + q * QK) * 2);
     }
     floatx4_t acc[RB][FN];
 #pragma unroll
@@ -200,8 +205,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
         const int byte = (wv * ADMA + i) * 1024 + lane * 16;
         const int R = byte / AROWB, pos = (byte % AROWB) / 16;
         const int c = pos ^ (R & 15);
-        const int arow = min(R, gd.rows - 1 - r0);
-        doff[i] = static_cast<uint32_t>(arow * static_cast<int>(lda) * 2 + (c >> 4) * (KC * 2) + (c & 15) * 16);
+        const int arow = gd.a_row0 + min(r0 + R, gd.rows - 1);
+        const int src = gth ? gth[arow] : arow;
+        doff[i] = static_cast<uint32_t>(src * static_cast<int>(lda) * 2 + (c >> 4) * (KC * 2) + (c & 15) * 16);
       }
       // lane (c16, q) of MFMA t, k-step u, row block rb: logical chunk u*16 + ch(t, q)
       auto burst = [&](char* abuf, int st) __attribute__((always_inline)) {
@@ -409,10 +415,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
     wrow[j] = (third ? B3w : Bw) + static_cast<int64_t>(third ? j - NR / 2 : j) * p.ldb * WB;
   }
   const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + static_cast<int64_t>(gd.a_row0) * lda);
+  const char* A = reinterpret_cast<const char*>(shared ? p.A_s : p.A_r);
+  const int32_t* gth = shared ? nullptr : p.gather;
   const char* arow[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) arow[r] = A + static_cast<int64_t>(min(r, gd.rows - 1)) * lda * 2;
+  for (int r = 0; r < R; ++r) {
+    const int ar = gd.a_row0 + min(r, gd.rows - 1);
+    arow[r] = A + static_cast<int64_t>(gth ? gth[ar] : ar) * lda * 2;
+  }
   // lane l: weight bytes [16 l, 16 l + 16) of a segment, i.e. k from
   // seg * KSEG + l * 16 / WB, and the bf16 activations of those k
   const uint32_t wl = static_cast<uint32_t>(lane) * 16;
@@ -598,9 +608,11 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.rows_total = a.routed_row_cap + a.n_shared * static_cast<int32_t>(a.T);
 
   // ---- up: [rows][d] x W1 (W3)^T -> h [rows][d_ff]
-  p.A_r = static_cast<const uint16_t*>(a.x_perm);
+  // routed rows: x_perm, or x through the permutation's token list
+  p.A_r = static_cast<const uint16_t*>(a.gather ? a.x : a.x_perm);
+  p.gather = a.gather;
   p.A_s = static_cast<const uint16_t*>(a.x);
-  p.lda_r = a.ld_xp;
+  p.lda_r = a.gather ? a.d : a.ld_xp;
   p.lda_s = a.d;
   p.B_r = static_cast<const char*>(a.w1);
   p.B3_r = static_cast<const char*>(a.w3);
@@ -644,6 +656,7 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
 
   // ---- down: h [rows][d_ff] x W2^T -> y [rows][d]
   p.A_r = static_cast<const uint16_t*>(a.h);
+  p.gather = nullptr;
   p.A_s = static_cast<const uint16_t*>(a.h);
   p.lda_r = a.ld_h;
   p.lda_s = a.ld_h;

@@ -964,6 +964,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T)) return launch_ffn_skinny(a, up, down, a.part, s);
+  if (a.gather) return hipErrorInvalidValue;  // the tiled GEMMs read routed rows from x_perm only
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
   const bool fp8 = (a.w_dtype == 2);

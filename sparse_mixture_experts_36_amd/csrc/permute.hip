@@ -14,6 +14,9 @@
 //     counts in block order, the capacity cut, and the expert offsets;
 //  3. scatter kernel: one wave per token writes inv_map / perm_token and copies
 //     the token's row once into each of its kept slots (x read once).
+// With at most 256 tokens the rank kernel's one block also does the scan, and
+// when no rows are copied (the caller's FFN reads x through perm_token) it
+// writes inv_map / perm_token itself: one launch instead of three.
 #include "common.h"
 #include "kernels.h"
 
@@ -91,8 +94,73 @@ __global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
     }
   }
   const int64_t b = blockIdx.x;
-  for (int e = tid; e < N; e += kThreads)
-    a.block_cnt[b * N + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+  if (gridDim.x > 1) {
+    for (int e = tid; e < N; e += kThreads)
+      a.block_cnt[b * N + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+    return;
+  }
+
+  // One block holds every token (T <= kPermTokens): the scan is this block's
+  // counts, block base 0. Wave 0 scans the kept counts: lane L owns experts
+  // [4L, 4L + 4), then an inclusive wave scan over the lanes (integer, exact).
+  __shared__ int32_t s_off[kMaxN + 1];
+  if (wave == 0) {
+    int32_t kept4[4], sum = 0, drop = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      int32_t cnt = 0, kept = 0;
+      if (e < N) {
+        cnt = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+        kept = (a.capacity >= 0 && cnt > a.capacity) ? static_cast<int32_t>(a.capacity) : cnt;
+        a.block_base[e] = 0;
+        a.kept[e] = kept;
+      }
+      kept4[i] = kept;
+      sum += kept;
+      drop += cnt - kept;
+    }
+    int32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int32_t off = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < N) {
+        s_off[e] = off;
+        a.offsets[e] = off;
+      }
+      off += kept4[i];
+    }
+    const int32_t total = __shfl(incl, 63);
+    if (lane == 0) {
+      s_off[N] = total;
+      a.offsets[N] = total;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
+    if (lane == 0) *a.n_dropped = drop;
+  }
+  // with no rows to copy, the slots are written here and no scatter pass runs
+  if (a.x_perm) return;
+  __syncthreads();
+  if (!live) return;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) break;
+    int32_t row = -1;
+    if (ex[j] >= 0) {
+      int r = rank[j];
+      for (int w = 0; w < wave; ++w) r += s_wcnt[w][ex[j]];
+      if (a.capacity < 0 || r < a.capacity) row = s_off[ex[j]] + r;
+    }
+    a.inv_map[t * k + j] = row;
+    if (row >= 0) a.perm_token[row] = static_cast<int32_t>(t);
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void perm_scan_kernel(PermuteArgs a, int nb) {
@@ -194,9 +262,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int nb = static_cast<int>(ceil_div(a.T, kPermTokens));
   stage_mark(kStagePermute, false, s);
   hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(a.T, 4))), dim3(kThreads), 0, s,
-                     a);
+  // one rank block also scans, and without rows to copy also writes the slots
+  if (nb > 1) hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  if (nb > 1 || a.x_perm)
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(a.T, 4))), dim3(kThreads), 0, s,
+                       a);
   stage_mark(kStagePermute, true, s);
   return hipGetLastError();
 }

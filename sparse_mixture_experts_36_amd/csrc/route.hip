@@ -1,5 +1,6 @@
-// Router: logits GEMM fused with softmax / top-k / gates and per-block
-// statistics partials, then a one-workgroup finalize of f, P, L_aux and z.
+// Router: logits GEMM (k-split partial logits), then softmax / top-k / gates
+// with per-block statistics, and a one-workgroup finalize of f, P, L_aux and z
+// (done by the routing workgroup itself when one covers all tokens).
 //
 // Pages: aigrafen.se "Mixture of Experts" (g = softmax(W_r x); L_aux =
 // alpha N sum f_i P_i; the `MoE` module's softmax -> top-k -> renormalise),
@@ -7,12 +8,12 @@
 // over the k), learn.starphix.com "Mixture of Experts (MoE)" / "Load Balancing
 // (Critical)" (load_balancing_loss, z_loss).
 //
-// Layout on the GPU: a workgroup owns 64 consecutive tokens; each of its four
-// waves owns 16 of them. The router GEMM leaves a wave's 16 x N logits in MFMA
-// accumulator layout: quarter-wave q (lanes 16q..16q+15) holds tokens 4q+i
-// (i < 4) with lane l%16 holding experts 16*nt + l%16. Every per-token step
-// (max, sum, top-k) is then a 16-lane reduction inside one quarter, with no LDS
-// round trip. Reductions run in a fixed order, so the result is bit-for-bit
+// Layout on the GPU: a workgroup owns 64 consecutive tokens. In the router
+// GEMM each of its four waves computes 16 tokens x N logits on MFMA; the
+// routing workgroup has 16 waves, and quarter-wave q of wave w (lanes
+// 16q..16q+15) owns token 4w + q, lane l%16 holding experts 16*nt + l%16. Every
+// per-token step (max, sum, top-k) is then a 16-lane reduction inside one
+// quarter. Reductions run in a fixed order, so the result is bit-for-bit
 // reproducible.
 #include <float.h>
 
@@ -143,139 +144,156 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(RouteArgs a, floa
   }
 }
 
-// Softmax / top-k / gates / block statistics over 64 tokens. Logits are the
-// given ones, or the sum of the k-split partial logits (in split order) plus
-// the router bias, which is then also stored as the router output.
+// Statistics from totals (fp64): counts, f = counts/(T k), P = sum/T, and
+// the f P products for L_aux.
+__device__ __forceinline__ void finalize_expert(const RouteArgs& a, int e, double p_sum, int64_t c, double* s_fp) {
+  const double T = static_cast<double>(a.T);
+  const double P = p_sum / T;
+  const double f = static_cast<double>(c) / (T * a.k);
+  if (a.counts) a.counts[e] = static_cast<int32_t>(c);
+  if (a.f) a.f[e] = static_cast<float>(f);
+  if (a.P) a.P[e] = static_cast<float>(P);
+  s_fp[e] = f * P;
+}
+
+// L_aux = alpha N sum_e f P (summed in expert order), z = mean(lse)^2.
+__device__ __forceinline__ void finalize_scalars(const RouteArgs& a, const double* s_fp, double lse_sum,
+                                                 double lse_sq_sum) {
+  const double T = static_cast<double>(a.T);
+  double dot = 0.0;
+  for (int e = 0; e < a.N; ++e) dot += s_fp[e];
+  const double lm = lse_sum / T;
+  if (a.l_aux) *a.l_aux = static_cast<float>(static_cast<double>(a.aux_alpha) * a.N * dot);
+  if (a.z_loss) *a.z_loss = static_cast<float>(lm * lm);
+  if (a.lse_mean) *a.lse_mean = static_cast<float>(lm);
+  if (a.lse_sq_mean) *a.lse_sq_mean = static_cast<float>(lse_sq_sum / T);
+}
+
+// Softmax / top-k / gates / block statistics over 64 tokens, one per
+// quarter-wave (16 waves): lane (q, c16) of wave w holds the logits of token
+// 4w + q for experts 16 nt + c16, so every per-token step is a 16-lane
+// reduction and no wave walks tokens one after another. Logits are the given
+// ones, or the sum of the k-split partial logits (in split order) plus the
+// router bias, which is then also stored as the router output. A launch of one
+// workgroup (T <= 64) also finishes the statistics itself.
+constexpr int kRouteWaves = kRouteTokens / 4;
+constexpr int kRouteThreads = 64 * kRouteWaves;
+
 template <int NT>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, const float* part, int splits) {
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a, const float* part, int splits) {
   __shared__ int32_t s_cnt[kMaxN];
-  __shared__ float s_P[4][kMaxN];
-  __shared__ float s_lse[4][2];
+  __shared__ float s_P[kRouteWaves][kMaxN];
+  __shared__ float s_lse[kRouteWaves][2];
+  __shared__ double s_fp[kMaxN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   const int N = a.N, k = a.k;
   const int64_t T = a.T;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 16;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 4 + q;
+  const bool live = t < T;  // uniform within the quarter
 
-  for (int e = tid; e < kMaxN; e += kThreads) s_cnt[e] = 0;
+  for (int e = tid; e < kMaxN; e += kRouteThreads) s_cnt[e] = 0;
 
-  // logits in accumulator layout: acc[nt][i] = l[t0 + 4q + i][16 nt + c16]
-  floatx4_t acc[NT];
+  float lg[NT];  // logit of expert 16 nt + c16
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = 16 * nt + c16;
+    float v = 0.f;
+    if (live && e < N) {
+      if (a.logits_given) {
+        v = a.logits[t * N + e];
+      } else {
+        // all split partials are loaded before the first add (one round
+        // trip, not one per split), then summed in split order
+        float pv[kMaxRouteSplits];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 4 * q + i;
-      const int e = 16 * nt + c16;
-      float v = 0.f;
-      if (t < T && e < N) {
-        if (a.logits_given) {
-          v = a.logits[t * N + e];
-        } else {
-          // all split partials are loaded before the first add (one round
-          // trip, not one per split), then summed in split order
-          float pv[kMaxRouteSplits];
+        for (int sp = 0; sp < kMaxRouteSplits; ++sp)
+          if (sp < splits) pv[sp] = part[(static_cast<int64_t>(sp) * T + t) * N + e];
+        v = pv[0];
 #pragma unroll
-          for (int sp = 0; sp < kMaxRouteSplits; ++sp)
-            if (sp < splits) pv[sp] = part[(static_cast<int64_t>(sp) * T + t) * N + e];
-          v = pv[0];
-#pragma unroll
-          for (int sp = 1; sp < kMaxRouteSplits; ++sp)
-            if (sp < splits) v += pv[sp];
-          if (a.b_router) v += a.b_router[e];
-          a.logits[t * N + e] = v;
-        }
+        for (int sp = 1; sp < kMaxRouteSplits; ++sp)
+          if (sp < splits) v += pv[sp];
+        if (a.b_router) v += a.b_router[e];
+        a.logits[t * N + e] = v;
       }
-      acc[nt][i] = v;
     }
+    lg[nt] = v;
+  }
   __syncthreads();  // s_cnt cleared before any count below
 
-  // ---- per token: softmax, top-k, gates, statistics
+  // selection: k rounds of a 16-lane arg-max under `better`
+  uint32_t taken = 0;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    if (16 * nt + c16 >= N) taken |= 1u << nt;
+  float selv[8];
+  int sele[8];
+  for (int j = 0; j < k; ++j) {
+    Sel b{-FLT_MAX, 0x7fffffff};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = 16 * nt + c16;
+      if (!(taken >> nt & 1u) && (b.e == 0x7fffffff || better(lg[nt], e, b.v, b.e))) {
+        b.v = lg[nt];
+        b.e = e;
+      }
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(b.v, o, 16);
+      const int e2 = __shfl_xor(b.e, o, 16);
+      if (e2 != 0x7fffffff && (b.e == 0x7fffffff || better(v2, e2, b.v, b.e))) {
+        b.v = v2;
+        b.e = e2;
+      }
+    }
+    selv[j] = b.v;
+    sele[j] = b.e;
+    if ((b.e & 15) == c16) taken |= 1u << (b.e >> 4);
+  }
+  // softmax over all N: the largest logit is the first selected one
+  const float m = selv[0];
+  float s = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    if (16 * nt + c16 < N) s += expf(lg[nt] - m);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  const float inv_s = 1.0f / s;
+  const float lse = m + logf(s);
   float pacc[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) pacc[nt] = 0.f;
-  float lse_s = 0.f, lse_sq = 0.f;
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + 4 * q + i;
-    const bool live = t < T;  // uniform within the quarter
-    // selection: k rounds of a 16-lane arg-max under `better`
-    uint32_t taken = 0;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (16 * nt + c16 >= N) taken |= 1u << nt;
-    float selv[8];
-    int sele[8];
-    for (int j = 0; j < k; ++j) {
-      Sel b{-FLT_MAX, 0x7fffffff};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int e = 16 * nt + c16;
-        if (!(taken >> nt & 1u) && (b.e == 0x7fffffff || better(acc[nt][i], e, b.v, b.e))) {
-          b.v = acc[nt][i];
-          b.e = e;
-        }
+  for (int nt = 0; nt < NT; ++nt) pacc[nt] = (live && 16 * nt + c16 < N) ? expf(lg[nt] - m) * inv_s : 0.f;
+  const float lse_s = live ? lse : 0.f, lse_sq = live ? lse * lse : 0.f;
+  if (live) {
+    float g[8];
+    if (a.gating == 0) {
+      for (int j = 0; j < k; ++j) g[j] = expf(selv[j] - m) * inv_s;
+    } else if (a.gating == 1) {
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) {
+        g[j] = expf(selv[j] - m) * inv_s;
+        den += g[j];
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(b.v, o, 16);
-        const int e2 = __shfl_xor(b.e, o, 16);
-        if (e2 != 0x7fffffff && (b.e == 0x7fffffff || better(v2, e2, b.v, b.e))) {
-          b.v = v2;
-          b.e = e2;
-        }
+      for (int j = 0; j < k; ++j) g[j] = g[j] / den;
+    } else {
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) {
+        g[j] = expf(selv[j] - m);
+        den += g[j];
       }
-      selv[j] = b.v;
-      sele[j] = b.e;
-      if ((b.e & 15) == c16) taken |= 1u << (b.e >> 4);
+      for (int j = 0; j < k; ++j) g[j] = g[j] / den;
     }
-    // softmax over all N: the largest logit is the first selected one
-    const float m = selv[0];
-    float s = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (16 * nt + c16 < N) s += expf(acc[nt][i] - m);
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
-    const float inv_s = 1.0f / s;
-    const float lse = m + logf(s);
-    if (live) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (16 * nt + c16 < N) pacc[nt] += expf(acc[nt][i] - m) * inv_s;
-      lse_s += lse;
-      lse_sq += lse * lse;
-      // gates
-      float g[8];
-      if (a.gating == 0) {
-        for (int j = 0; j < k; ++j) g[j] = expf(selv[j] - m) * inv_s;
-      } else if (a.gating == 1) {
-        float den = 0.f;
-        for (int j = 0; j < k; ++j) {
-          g[j] = expf(selv[j] - m) * inv_s;
-          den += g[j];
-        }
-        for (int j = 0; j < k; ++j) g[j] = g[j] / den;
-      } else {
-        float den = 0.f;
-        for (int j = 0; j < k; ++j) {
-          g[j] = expf(selv[j] - m);
-          den += g[j];
-        }
-        for (int j = 0; j < k; ++j) g[j] = g[j] / den;
+    for (int j = 0; j < k; ++j)
+      if (c16 == j) {
+        a.topk_idx[t * k + j] = sele[j];
+        a.topk_w[t * k + j] = g[j];
+        atomicAdd(&s_cnt[sele[j]], 1);
       }
-      for (int j = 0; j < k; ++j)
-        if (c16 == j) {
-          a.topk_idx[t * k + j] = sele[j];
-          a.topk_w[t * k + j] = g[j];
-          atomicAdd(&s_cnt[sele[j]], 1);
-        }
-    }
   }
 
-  // ---- block partials, fixed reduction order: quarters (xor 16, 32), then waves
+  // ---- block totals, fixed order: the wave's four tokens (xor 16, 32), then waves in order
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float v = pacc[nt];
@@ -283,10 +301,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, const floa
     v += __shfl_xor(v, 32);
     if (q == 0) s_P[wave][16 * nt + c16] = v;
   }
-  // lse sums live in every lane of a quarter; take lane 16q's
   {
-    float a1 = __shfl(lse_s, 0) + __shfl(lse_s, 16) + __shfl(lse_s, 32) + __shfl(lse_s, 48);
-    float a2 = __shfl(lse_sq, 0) + __shfl(lse_sq, 16) + __shfl(lse_sq, 32) + __shfl(lse_sq, 48);
+    const float a1 = __shfl(lse_s, 0) + __shfl(lse_s, 16) + __shfl(lse_s, 32) + __shfl(lse_s, 48);
+    const float a2 = __shfl(lse_sq, 0) + __shfl(lse_sq, 16) + __shfl(lse_sq, 32) + __shfl(lse_sq, 48);
     if (lane == 0) {
       s_lse[wave][0] = a1;
       s_lse[wave][1] = a2;
@@ -294,13 +311,30 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, const floa
   }
   __syncthreads();
   const int b = blockIdx.x;
-  for (int e = tid; e < N; e += kThreads) {
-    a.part_P[static_cast<int64_t>(b) * N + e] = ((s_P[0][e] + s_P[1][e]) + s_P[2][e]) + s_P[3][e];
-    a.part_cnt[static_cast<int64_t>(b) * N + e] = s_cnt[e];
+  const bool last = gridDim.x == 1;  // the only block: its totals are the layer's
+  for (int e = tid; e < N; e += kRouteThreads) {
+    float P = s_P[0][e];
+#pragma unroll
+    for (int w = 1; w < kRouteWaves; ++w) P += s_P[w][e];
+    if (last) {
+      finalize_expert(a, e, static_cast<double>(P), s_cnt[e], s_fp);
+    } else {
+      a.part_P[static_cast<int64_t>(b) * N + e] = P;
+      a.part_cnt[static_cast<int64_t>(b) * N + e] = s_cnt[e];
+    }
   }
-  if (tid == 0) {
-    a.part_lse[2 * b] = ((s_lse[0][0] + s_lse[1][0]) + s_lse[2][0]) + s_lse[3][0];
-    a.part_lse[2 * b + 1] = ((s_lse[0][1] + s_lse[1][1]) + s_lse[2][1]) + s_lse[3][1];
+  float l1 = s_lse[0][0], l2 = s_lse[0][1];
+#pragma unroll
+  for (int w = 1; w < kRouteWaves; ++w) {
+    l1 += s_lse[w][0];
+    l2 += s_lse[w][1];
+  }
+  if (last) {
+    __syncthreads();  // every f P product is in s_fp
+    if (tid == 0) finalize_scalars(a, s_fp, static_cast<double>(l1), static_cast<double>(l2));
+  } else if (tid == 0) {
+    a.part_lse[2 * b] = l1;
+    a.part_lse[2 * b + 1] = l2;
   }
 }
 
@@ -310,7 +344,6 @@ __global__ __launch_bounds__(kThreads) void route_finalize_kernel(RouteArgs a, i
   __shared__ double s_fp[kMaxN];
   const int tid = threadIdx.x;
   const int N = a.N;
-  const double T = static_cast<double>(a.T);
   for (int e = tid; e < kMaxN; e += kThreads) s_fp[e] = 0.0;
   __syncthreads();
   for (int e = tid; e < N; e += kThreads) {
@@ -320,26 +353,16 @@ __global__ __launch_bounds__(kThreads) void route_finalize_kernel(RouteArgs a, i
       p += static_cast<double>(a.part_P[static_cast<int64_t>(b) * N + e]);
       c += a.part_cnt[static_cast<int64_t>(b) * N + e];
     }
-    const double P = p / T;
-    const double f = static_cast<double>(c) / (T * a.k);
-    if (a.counts) a.counts[e] = static_cast<int32_t>(c);
-    if (a.f) a.f[e] = static_cast<float>(f);
-    if (a.P) a.P[e] = static_cast<float>(P);
-    s_fp[e] = f * P;
+    finalize_expert(a, e, p, c, s_fp);
   }
   __syncthreads();
   if (tid == 0) {
-    double dot = 0.0, ls = 0.0, lq = 0.0;
-    for (int e = 0; e < N; ++e) dot += s_fp[e];
+    double ls = 0.0, lq = 0.0;
     for (int b = 0; b < nb; ++b) {
       ls += static_cast<double>(a.part_lse[2 * b]);
       lq += static_cast<double>(a.part_lse[2 * b + 1]);
     }
-    const double lm = ls / T;
-    if (a.l_aux) *a.l_aux = static_cast<float>(static_cast<double>(a.aux_alpha) * N * dot);
-    if (a.z_loss) *a.z_loss = static_cast<float>(lm * lm);
-    if (a.lse_mean) *a.lse_mean = static_cast<float>(lm);
-    if (a.lse_sq_mean) *a.lse_sq_mean = static_cast<float>(lq / T);
+    finalize_scalars(a, s_fp, ls, lq);
   }
 }
 
@@ -351,7 +374,7 @@ hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kThreads), 0, s, a, a.part_logits, splits);
+  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kRouteThreads), 0, s, a, a.part_logits, splits);
   return hipGetLastError();
 }
 
@@ -382,7 +405,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  if (nb > 1) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
   stage_mark(kStageRoute, true, s);
   return hipGetLastError();
 }

@@ -114,6 +114,7 @@ REDUCED = {
     "mixtral-like-decode-T1": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
     "mixtral-like-decode-T64": gen.MIXTRAL_PREFILL.with_(T=64, d=1024, d_ff=1536),
     "fine-grained-like-decode": gen.FINE_GRAINED.with_(T=24, d=512, d_ff=256),
+    "fine-grained-like-decode-T2": gen.FINE_GRAINED.with_(T=2, d=512, d_ff=1024),  # GEMV: two rows, shared experts
     "switch-like-decode-fp8": gen.SWITCH_TOP1_FP8.with_(T=128, d=512, d_ff=1024),
 }
 
