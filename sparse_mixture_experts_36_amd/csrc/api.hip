@@ -498,15 +498,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   const bool gather = moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T);
   hipError_t e = moe::launch_route(
       route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
-  if (e == hipSuccess)
-    e = moe::launch_permute(perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map,
-                                      gather ? nullptr : w.x_perm, ld_xp, stats, pw),
-                            stream);
-  if (e == hipSuccess) {
-    moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
-    if (gather) fa.gather = perm_token;
-    e = moe::launch_grouped_ffn(fa, stream);
+  moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
+  moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
+                                  ld_xp, stats, pw);
+  if (gather) {
+    fa.gather = perm_token;
+    if (s.T <= moe::kPermTokens) {  // the one-block permutation also writes the FFN's group plan
+      pa.plan = moe::ffn_plan(fa);
+      fa.planned = true;
+    }
   }
+  if (e == hipSuccess) e = moe::launch_permute(pa, stream);
+  if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);
   if (e == hipSuccess) {
     moe::CombineArgs a{};
     a.T = s.T;

@@ -22,6 +22,7 @@
 // run together and share that weight tile in the XCD's L2.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 namespace {
@@ -816,49 +817,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------ plan
-// Group descriptors of both GEMMs and the row-tile prefix for tile height bm.
-// Routed expert e: rows [offsets[e], offsets[e+1]) of x_perm / h / y_perm,
-// clamped to the reserved routed rows. Shared expert s: the T token rows; its
-// hidden rows sit after the routed ones in h, its outputs in y_shared[s].
-// active[0] = the number of groups with rows, active[1..] those groups in order.
-__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, int32_t n_routed, int32_t n_shared,
-                                                        int32_t T, int32_t cap, int32_t bm, GroupDesc* up,
-                                                        GroupDesc* down, int32_t* tile_start, int32_t* active) {
-  __shared__ int32_t s_mt[kThreads + 8];
-  const int tid = threadIdx.x;
-  const int G = n_routed + n_shared;
-  for (int g = tid; g < G; g += kThreads) {
-    GroupDesc u, dn;
-    if (g < n_routed) {
-      int r0 = offsets[g], r1 = offsets[g + 1];
-      r0 = max(0, min(r0, cap));
-      r1 = max(r0, min(r1, cap));
-      u.a_row0 = u.c_row0 = dn.a_row0 = dn.c_row0 = r0;
-      u.rows = dn.rows = r1 - r0;
-    } else {
-      const int s = g - n_routed;
-      u.a_row0 = 0;
-      u.c_row0 = cap + s * T;
-      dn.a_row0 = cap + s * T;
-      dn.c_row0 = s * T;
-      u.rows = dn.rows = T;
-    }
-    u.widx = dn.widx = g;
-    up[g] = u;
-    down[g] = dn;
-    s_mt[g] = (u.rows + bm - 1) / bm;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0, n_active = 0;
-    for (int g = 0; g < G; ++g) {
-      tile_start[g] = acc;
-      acc += s_mt[g];
-      if (s_mt[g] > 0) active[1 + n_active++] = g;
-    }
-    tile_start[G] = acc;
-    active[0] = n_active;
-  }
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, FfnPlan pl) {
+  __shared__ int32_t s_mt[kMaxGroups];
+  plan_groups(offsets, pl, s_mt, threadIdx.x, kThreads);
 }
 
 template <int BM, int BNB, int WGM, int WGN, int EPI, bool FP8, int PF = MOE_GEMM_PF>
@@ -950,19 +911,38 @@ int device_cus() {
 
 }  // namespace
 
+FfnPlan ffn_plan(const FfnArgs& a) {
+  const int G = a.n_routed + a.n_shared;
+  FfnPlan pl;
+  pl.up = a.groups;
+  pl.down = a.groups + G;
+  pl.tile_start = a.tile_start;
+  pl.active = a.active;
+  pl.n_routed = a.n_routed;
+  pl.n_shared = a.n_shared;
+  pl.T = static_cast<int32_t>(a.T);
+  pl.cap = a.routed_row_cap;
+  pl.bm = a.act_dtype == 0 ? 64 : tile_rows(pick_cfg(a));
+  return pl;
+}
+
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
+  if (G > kMaxGroups) return hipErrorInvalidValue;
   const bool f32 = (a.act_dtype == 0);
   const int cfg = pick_cfg(a);
-  const int bm = f32 ? 64 : tile_rows(cfg);
-  GroupDesc* up = a.groups;
-  GroupDesc* down = a.groups + G;
-  stage_mark(kStageFfnPlan, false, s);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a.offsets, a.n_routed, a.n_shared,
-                     static_cast<int32_t>(a.T), a.routed_row_cap, bm, up, down, a.tile_start, a.active);
-  stage_mark(kStageFfnPlan, true, s);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  const FfnPlan pl = ffn_plan(a);
+  const int bm = pl.bm;
+  GroupDesc* up = pl.up;
+  GroupDesc* down = pl.down;
+  hipError_t err = hipSuccess;
+  if (!a.planned) {
+    stage_mark(kStageFfnPlan, false, s);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a.offsets, pl);
+    stage_mark(kStageFfnPlan, true, s);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T)) return launch_ffn_skinny(a, up, down, a.part, s);
   if (a.gather) return hipErrorInvalidValue;  // the tiled GEMMs read routed rows from x_perm only
   // upper bound on row tiles: every group may end in a partial tile

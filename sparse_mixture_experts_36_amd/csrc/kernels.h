@@ -37,6 +37,24 @@ constexpr int kMaxRouteSplits = 16;  // k splits of the router GEMM (partial log
 int route_splits(int64_t T, int64_t d);  // k splits of the router GEMM
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- FFN groups
+// One group = one weight set applied to a contiguous block of rows.
+struct GroupDesc {
+  int32_t a_row0;   // first row in the A source (routed: x_perm / h, shared: x / h)
+  int32_t c_row0;   // first row in the output
+  int32_t rows;
+  int32_t widx;     // expert index; shared experts are n_routed + s
+};
+constexpr int kMaxGroups = 260;  // routed experts (<= 256) plus shared experts (<= 4)
+// Where and how the grouped FFN's group plan is written (row tiles of bm rows).
+struct FfnPlan {
+  GroupDesc* up;             // [G] up-GEMM groups
+  GroupDesc* down;           // [G] down-GEMM groups
+  int32_t* tile_start;       // [G + 1] row-tile prefix
+  int32_t* active;           // [1 + G] count, then the groups with rows
+  int32_t n_routed, n_shared, T, cap, bm;
+};
+
 // ---------------------------------------------------------------- permute
 struct PermuteArgs {
   int64_t T, d;
@@ -55,18 +73,14 @@ struct PermuteArgs {
   int32_t* block_cnt;        // [nb][N]
   int32_t* block_base;       // [nb][N]
   int32_t* local_rank;       // [T*k]
+  // with x_perm null and one workgroup (T <= kPermTokens): also write the FFN
+  // group plan from the offsets (null plan.up: no plan)
+  FfnPlan plan;
 };
 constexpr int kPermTokens = 256;  // tokens per permute workgroup
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- grouped FFN
-// One group = one weight set applied to a contiguous block of rows.
-struct GroupDesc {
-  int32_t a_row0;   // first row in the A source (routed: x_perm / h, shared: x / h)
-  int32_t c_row0;   // first row in the output
-  int32_t rows;
-  int32_t widx;     // expert index; shared experts are n_routed + s
-};
 
 struct FfnArgs {
   int64_t T, d, d_ff;
@@ -91,7 +105,10 @@ struct FfnArgs {
   int32_t* active;            // [1 + n_routed + n_shared]: count, then the groups with rows (workspace)
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
   float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null
+  bool planned;               // groups, tile_start and active are already written (by the permutation)
 };
+// The group plan the FFN launch would write for these arguments.
+FfnPlan ffn_plan(const FfnArgs& a);
 // fp32 floats of the prefill path's k-split partial tiles: 256 tiles of 256 x 256
 constexpr int64_t kSplitPartFloats = 256LL * 256 * 256;
 

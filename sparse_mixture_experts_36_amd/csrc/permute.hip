@@ -19,6 +19,7 @@
 // writes inv_map / perm_token itself: one launch instead of three.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 namespace {
@@ -145,9 +146,14 @@ __global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
     for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
     if (lane == 0) *a.n_dropped = drop;
   }
-  // with no rows to copy, the slots are written here and no scatter pass runs
+  // with no rows to copy, the slots (and, when asked, the FFN's group plan)
+  // are written here and no scatter pass runs
   if (a.x_perm) return;
   __syncthreads();
+  if (a.plan.up) {
+    __shared__ int32_t s_mt[kMaxGroups];
+    plan_groups(s_off, a.plan, s_mt, tid, kThreads);
+  }
   if (!live) return;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
