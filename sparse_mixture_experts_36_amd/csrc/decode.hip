@@ -523,14 +523,19 @@ int pick_splits(int64_t K, int64_t blocks_touched) {
 hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, hipStream_t s) {
   const int64_t waves = blocks * p.splits;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
-  // at most 8 waves per CU: four k-steps per burst (their registers still fit 2 waves per SIMD)
-  const bool deep = rb == 1 && waves <= 2048;
   // 32 or 64 token rows: shared through LDS when the passes hold whole burst pairs
-  const bool shared_a = rb >= 2 && (p.K / p.splits / KC) % 4 == 0;
+  const bool pairs = (p.K / p.splits / KC) % 4 == 0;
+  const bool shared_a = rb >= 2 && pairs;
+  // at most 8 waves per CU: 16-row passes take the 32-row shared kernel when
+  // they can (measured faster there), else four k-steps per burst (whose
+  // registers still fit 2 waves per SIMD)
+  const bool deep = rb == 1 && waves <= 2048;
 #define MOE_STREAM_LAUNCH(R, U, SA)                                                                 \
   if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, U, SA>), grid, dim3(kThreads), 0, s, p);      \
   else hipLaunchKernelGGL((stream_kernel<R, false, U, SA>), grid, dim3(kThreads), 0, s, p);
-  if (deep) {
+  if (deep && pairs) {
+    MOE_STREAM_LAUNCH(2, 2, true)
+  } else if (deep) {
     MOE_STREAM_LAUNCH(1, 4, false)
   } else if (rb == 1) {
     MOE_STREAM_LAUNCH(1, 2, false)
