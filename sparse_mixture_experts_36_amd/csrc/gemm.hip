@@ -394,19 +394,22 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 1
 
 // Epilogue of a DMA tile held as per-wave MFMA fragments: bias and activation
 // (or the SwiGLU product of the W1 and W3 halves), bf16, and 16-byte stores
-// through an LDS staging buffer, one wave row (BM/2 rows) at a time (16-byte
-// chunk c of staged row r at position c ^ (r & 7)).
-template <int EPI, int BM, int W>
+// through an LDS staging buffer of STG bytes, RR rows (at most one wave row)
+// at a time (16-byte chunk c of staged row r at position c ^ (r & 7)).
+template <int EPI, int BM, int W, int STG = dma::Cfg<BM, W>::SBYTES>
 __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
                                                floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN],
                                                char* stage) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
-  constexpr int WTB = C_::WTB, FN = C_::FN, WGN = C_::WGN, NTH = C_::NTH;
+  constexpr int WTB = C_::WTB, FN = C_::FN, WGN = C_::WGN, NTH = C_::NTH, WTM = C_::WTM;
   constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
   constexpr int FNO = WTO / 16;
-  static_assert(C_::WTM * BNO * 2 <= C_::SBYTES, "output staging exceeds a stage buffer");
+  constexpr int RR0 = STG / (BNO * 2);
+  constexpr int RR = RR0 < WTM ? RR0 : WTM;  // rows per staging round
+  constexpr int FR = RR / 16;                 // fragment rows per round
+  static_assert(WTM % RR == 0 && RR % 16 == 0, "staging rounds");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
@@ -419,18 +422,21 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
   constexpr int OCH = BNO / 8;
 #pragma unroll
-  for (int h = 0; h < WGM; ++h) {
-    if (h * C_::WTM >= ti.rows) break;  // the same for the whole workgroup
-    if (wm == h) {
+  for (int h = 0; h < BM / RR; ++h) {
+    if (h * RR >= ti.rows) break;  // the same for the whole workgroup
+    if (wm == (h * RR) / WTM) {
+      constexpr int NI = C_::FM;
+      const int i0 = ((h * RR) % WTM) / 16;  // the wave's first fragment row of the round
 #pragma unroll
-      for (int i = 0; i < C_::FM; ++i) {
+      for (int i = 0; i < NI; ++i) {
+        if (i < i0 || i >= i0 + FR) continue;
 #pragma unroll
         for (int j = 0; j < FNO; ++j) {
           const int col = wn * WTO + j * 16 + c16;
           const float bv = bias ? bias[col] : 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int srow = i * 16 + q * 4 + r;  // row inside the staged part
+            const int srow = (i - i0) * 16 + q * 4 + r;  // row inside the staged part
             float v;
             if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
             else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
@@ -441,9 +447,9 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
       }
     }
     __syncthreads();
-    for (int c = tid; c < C_::WTM * OCH; c += NTH) {
+    for (int c = tid; c < RR * OCH; c += NTH) {
       const int srow = c / OCH, cc = c % OCH;
-      const int row = h * C_::WTM + srow;
+      const int row = h * RR + srow;
       if (row < ti.rows)
         *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
             *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
@@ -697,6 +703,232 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
 }
 
+// The 256 x 256 DMA tile with operands in separate buffers: two 32 KB buffers
+// of activation rows, filled one stage ahead, and a ring of three 32 KB
+// buffers of weight rows, filled two stages ahead (all 160 KB of LDS). The
+// weight rows come from HBM, so they get the longer lead; the activation rows
+// of a tile's group are mostly L2 hits. Waves, fragments, reads and the
+// epilogue are those of gemm_dma_kernel<EPI, 256, 8>.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
+  using namespace dma;
+  using C_ = Cfg<256, 8>;
+  constexpr int BM = 256, W = 8;
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int BNO = bno(EPI);
+  constexpr int FM = C_::FM, FN = C_::FN, WTM = C_::WTM, WTB = C_::WTB, WGN = C_::WGN;
+  constexpr int ADMA = C_::ADMA, BDMA = C_::BDMA, NDMA = C_::NDMA;
+  constexpr int HB = BM * RB;  // one operand of one stage (32 KB)
+  __shared__ __attribute__((aligned(16))) char SA0[HB];
+  __shared__ __attribute__((aligned(16))) char SA1[HB];
+  __shared__ __attribute__((aligned(16))) char SB0[HB];
+  __shared__ __attribute__((aligned(16))) char SB1[HB];
+  __shared__ __attribute__((aligned(16))) char SB2[HB];
+
+  const int K = p.K;
+  const int KS = K / BK;  // even: K is a multiple of 128
+  TileInfo ti;
+  int ks_begin = 0, ks_end = KS, unit = -1;
+  {
+    const SplitPlan sp = split_plan<BNO>(p, KS / 2);
+    const int bid = blockIdx.x;
+    if (sp.s == 1) {
+      if (!decode_tile<BM, BNO>(p, ti)) return;
+    } else if (bid < sp.full) {  // full rounds; sp.full is a multiple of the XCD count
+      const int per_xcd = sp.full / kXcds;
+      tile_from_linear<BM, BNO>(p, (bid % kXcds) * per_xcd + bid / kXcds, ti);
+    } else {
+      unit = bid - sp.full;
+      if (unit >= sp.r * sp.s) return;
+      const int c = unit % sp.s;
+      tile_from_linear<BM, BNO>(p, sp.full + unit / sp.s, ti);
+      ks_begin = 2 * ((c * (KS / 2)) / sp.s);  // chunks of whole stage pairs
+      ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
+    }
+  }
+  const int n_st = ks_end - ks_begin;  // even
+#define MOE_COL(j) (ks_begin + (j))
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level pointers stay in SGPRs
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int q = lane >> 4, c16 = lane & 15;
+  const bool shared = ti.g >= p.n_routed;
+  const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
+  const int n0 = ti.n_tile * BNO;
+  const int64_t lda = shared ? p.lda_s : p.lda_r;
+  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
+                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda * 2;
+  const int ar0 = wave * C_::AROWS, wr0 = wave * C_::BROWS;
+  const bool w3 = SWI && wr0 >= BNO;
+  const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
+                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) * 2;
+  uint32_t offa[ADMA], offb[BDMA];
+#pragma unroll
+  for (int i = 0; i < ADMA; ++i) {
+    const int r = ar0 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
+    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(lda) * 2 + chunk * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BDMA; ++i) {
+    const int r = wr0 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * static_cast<int>(p.ldb) * 2 + chunk * 16);
+  }
+  const int dst_a = ar0 * RB, dst_b = wr0 * RB;  // byte offsets inside a buffer
+#define MOE_LDS(x) ((__attribute__((address_space(3))) void*)(x))
+#define MOE_DMA_A(S, ks)                                                                             \
+  do {                                                                                               \
+    const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < ADMA; ++i_)                                              \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(A + (offa[i_] + ko_)), MOE_LDS((S) + dst_a + i_ * 1024), 16, 0, 0); \
+  } while (0)
+#define MOE_DMA_B(S, ks)                                                                             \
+  do {                                                                                               \
+    const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < BDMA; ++i_)                                              \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bw + (offb[i_] + ko_)), MOE_LDS((S) + dst_b + i_ * 1024), 16, 0, 0); \
+  } while (0)
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int rd0 = c16 * RB + ((q ^ (c16 & 7)) * 16);
+  const int rd1 = c16 * RB + (((4 + q) ^ (c16 & 7)) * 16);
+#define MOE_READ(SA, SB, RD, AF, BF)                                                                 \
+  do {                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
+        *reinterpret_cast<const uint4*>((SA) + (wm * WTM + i * 16) * RB + RD);                       \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                 \
+      const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
+                                           : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
+                           : wn * WTB + j * 16;                                                      \
+      BF[j] = *reinterpret_cast<const uint4*>((SB) + brow * RB + RD);                                \
+    }                                                                                                \
+  } while (0)
+#define MOE_MFMA(AC, BC)                                                                             \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                     \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(AC[i], BC[j], acc[i][j])
+  constexpr int REST = FM * FN - 2 * (FM + FN);
+  static_assert(REST >= 0 && BDMA <= FM + FN, "schedule shape");
+  // as in gemm_dma_kernel; after the barrier the B DMA instructions are spread
+  // among the MFMAs (the A ones go first, see MOE_STAGE5)
+#define MOE_SCHEDULE(WITH_DMA)                                                                       \
+  do {                                                                                               \
+    _Pragma("unroll") for (int g_ = 0; g_ < FM + FN; ++g_) {                                         \
+      if constexpr (WITH_DMA) {                                                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                           \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                           \
+        if (g_ < BDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                            \
+      } else {                                                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                           \
+      }                                                                                              \
+    }                                                                                                \
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                    \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+  } while (0)
+  // Stage ks: activation rows in SAC, weight rows in SBC, first k-step's
+  // fragments in af0/bf0. First half: read the second k-step's fragments, run
+  // the first's MFMAs. Then wait until only the newest weight DMA (stage
+  // ks + 2) may still fly, so stage ks + 1 has landed; barrier (everyone's
+  // stage ks + 1 is in, and all reads of SAC / SBC are done); refill SAC with
+  // stage ks + 2's activation rows and SBC with stage ks + 3's weight rows
+  // (the activation DMA first, so that it is older than the weight DMA that
+  // the next wait leaves in flight); read stage ks + 1's first fragments, run
+  // the second k-step's MFMAs.
+#define MOE_STAGE5(SAC, SBC, SAN, SBN, ks)                                                           \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): af0/bf0 have arrived */                       \
+    MOE_READ(SAC, SBC, rd1, af1, bf1);                                                               \
+    MOE_MFMA(af0, bf0);                                                                              \
+    MOE_SCHEDULE(false);                                                                             \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(BDMA));                                                     \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of SAC / SBC are done */             \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA_A(SAC, MOE_COL(min((ks) + 2, n_st - 1)));                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_DMA_B(SBC, MOE_COL(min((ks) + 3, n_st - 1)));                                                \
+    MOE_READ(SAN, SBN, rd0, af0, bf0);                                                               \
+    MOE_MFMA(af1, bf1);                                                                              \
+    MOE_SCHEDULE(true);                                                                              \
+  } while (0)
+  // a stage of a wave whose rows all lie past the group's end: the same DMA
+  // and barriers, no reads or MFMAs
+#define MOE_STAGE5_IDLE(SAC, SBC, SAN, SBN, ks)                                                      \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(BDMA));                                                     \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA_A(SAC, MOE_COL(min((ks) + 2, n_st - 1)));                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_DMA_B(SBC, MOE_COL(min((ks) + 3, n_st - 1)));                                                \
+  } while (0)
+  // whole rounds of six stages (activation buffers cycle by 2, weight buffers
+  // by 3) with no exit inside the loop, then the 0, 2 or 4 stages left
+#define MOE_STAGES5(STAGE)                                                                           \
+  do {                                                                                               \
+    const int n_round = n_st / 6 * 6;                                                                \
+    for (int ks = 0; ks < n_round; ks += 6) {                                                        \
+      STAGE(SA0, SB0, SA1, SB1, ks);                                                                 \
+      STAGE(SA1, SB1, SA0, SB2, ks + 1);                                                             \
+      STAGE(SA0, SB2, SA1, SB0, ks + 2);                                                             \
+      STAGE(SA1, SB0, SA0, SB1, ks + 3);                                                             \
+      STAGE(SA0, SB1, SA1, SB2, ks + 4);                                                             \
+      STAGE(SA1, SB2, SA0, SB0, ks + 5);                                                             \
+    }                                                                                                \
+    if (n_round < n_st) {                                                                            \
+      STAGE(SA0, SB0, SA1, SB1, n_round);                                                            \
+      STAGE(SA1, SB1, SA0, SB2, n_round + 1);                                                        \
+      if (n_round + 2 < n_st) {                                                                      \
+        STAGE(SA0, SB2, SA1, SB0, n_round + 2);                                                      \
+        STAGE(SA1, SB0, SA0, SB1, n_round + 3);                                                      \
+      }                                                                                              \
+    }                                                                                                \
+  } while (0)
+
+  uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
+  MOE_DMA_A(SA0, MOE_COL(0));
+  MOE_DMA_B(SB0, MOE_COL(0));
+  MOE_DMA_A(SA1, MOE_COL(1));
+  MOE_DMA_B(SB1, MOE_COL(1));
+  MOE_DMA_B(SB2, MOE_COL(min(2, n_st - 1)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(ADMA + 2 * BDMA));  // stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  if (wm * WTM < ti.rows) {
+    MOE_READ(SA0, SB0, rd0, af0, bf0);
+    MOE_STAGES5(MOE_STAGE5);
+  } else {
+    MOE_STAGES5(MOE_STAGE5_IDLE);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing DMAs have landed
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+#undef MOE_STAGES5
+#undef MOE_STAGE5_IDLE
+#undef MOE_STAGE5
+#undef MOE_SCHEDULE
+#undef MOE_MFMA
+#undef MOE_READ
+#undef MOE_DMA_B
+#undef MOE_DMA_A
+#undef MOE_LDS
+#undef MOE_COL
+
+  if (unit >= 0) {  // a k-chunk: raw fp32 partial sums, summed by the fix-up pass
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
+    return;
+  }
+  dma_store_tile<EPI, BM, W, HB>(p, ti, acc, SA0);
+}
+
 // Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
 // partial tiles in chunk order and runs the tile epilogue.
 template <int EPI, int BM, int W>
@@ -864,6 +1096,26 @@ hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 }
 
 template <int EPI>
+hipError_t run_dma5(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  constexpr int BNO = dma::bno(EPI);
+  if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
+  int64_t grid = max_mtiles * (p.Nout / BNO);
+  grid = ceil_div(grid, kXcds) * kXcds;
+  if (grid <= 0) return hipSuccess;
+  // a k-split tail runs at most total - r + kSplitUnits workgroups
+  if (p.split_part) grid += kSplitUnits;
+  hipLaunchKernelGGL((gemm_dma5_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, s, p);
+  if (p.split_part) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // split tiles: r <= kSplitUnits / 2 (each is cut at least in two); the
+    // partial tiles have gemm_dma_kernel<EPI, 256, 8>'s fragment layout
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, 256, 8>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int EPI>
 hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   int64_t grid = max_mtiles * (p.Nout / 64);
   grid = ceil_div(grid, kXcds) * kXcds;
@@ -879,7 +1131,7 @@ hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t
     return run_bf16<128, 128, 2, 2, EPI, true>(p, max_mtiles, s);
   } else {
     switch (cfg) {
-      case kDma256: return run_dma<EPI, 256, 8>(p, max_mtiles, s);
+      case kDma256: return run_dma5<EPI>(p, max_mtiles, s);
       case kDma128: return run_dma<EPI, 128, 8>(p, max_mtiles, s);
       default: return run_bf16<128, 128, 2, 2, EPI, false>(p, max_mtiles, s);
     }
