@@ -129,6 +129,17 @@ struct FwdWs {
   float* topk_w;
   void *x_perm, *y_perm, *y_shared;
 };
+// Whether moe_forward's expert kernels read routed rows from x through
+// perm_token (no permuted copy): bf16 layers, except prefill-sized ones whose x
+// rows are a multiple of 4 KB apart. Those rows, fetched at one k-column, fall
+// into few L2 channels, so they are copied into x_perm with padded rows; the
+// decode path reads its few rows either way.
+bool fwd_gathers(const moe_shape& s) {
+  if (s.act_dtype != MOE_BF16) return false;
+  if (moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T)) return true;
+  return (s.d * 2) % 4096 != 0;
+}
+
 FwdWs carve_fwd(Carver& c, const moe_shape& s) {
   const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(s.top_k);
   const size_t cap = static_cast<size_t>(routed_row_cap(s));
@@ -140,7 +151,8 @@ FwdWs carve_fwd(Carver& c, const moe_shape& s) {
   w.inv_map = c.take<int32_t>(T * k);
   w.offsets = c.take<int32_t>(s.n_experts + 1);
   w.perm_token = c.take<int32_t>(T * k);
-  w.x_perm = c.take<char>(cap * static_cast<size_t>(s.d + moe::kActPad) * act_bytes(s.act_dtype));
+  w.x_perm = nullptr;
+  if (!fwd_gathers(s)) w.x_perm = c.take<char>(cap * static_cast<size_t>(s.d + moe::kActPad) * act_bytes(s.act_dtype));
   w.y_perm = c.take<char>(cap * rowb);
   w.y_shared = c.take<char>(static_cast<size_t>(s.n_shared) * T * rowb);
   return w;
@@ -493,9 +505,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   if (!expert_offsets) expert_offsets = w.offsets;
   if (!perm_token) perm_token = w.perm_token;
 
-  // decode-sized layers: the expert kernels read routed rows from x through
-  // perm_token, so the permutation copies no rows
-  const bool gather = moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T);
+  const bool gather = fwd_gathers(s);  // then the permutation copies no rows
   hipError_t e = moe::launch_route(
       route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
   moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);

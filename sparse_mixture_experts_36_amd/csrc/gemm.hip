@@ -37,6 +37,7 @@ constexpr int kXcds = 8;
 
 struct GemmParams {
   const void* A_r;        // routed A rows
+  const int32_t* gather;  // routed A row r of a group is row gather[a_row0 + r] of A_r, or null (row a_row0 + r)
   const void* A_s;        // shared A rows
   int64_t lda_r, lda_s;   // A row pitches (elements, >= K)
   const void* B_r;        // routed weights [n_routed][Nout][K] (W1 or W2)
@@ -178,8 +179,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   const int K = p.K;
 
   const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) +
-                      (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda;
+  const int32_t* gth = shared ? nullptr : p.gather;
+  const int arow0 = ti.gd.a_row0 + ti.m_tile * BM;  // the tile's first row in the group's A rows
+  const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) + (gth ? 0 : static_cast<int64_t>(arow0) * lda);
   constexpr int WB = FP8 ? 1 : 2;  // weight bytes
   const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride * WB;
   const char* B3w = SWI ? static_cast<const char*>(shared ? p.B3_s : p.B3_r) +
@@ -196,7 +198,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
     const int kc = c & 7;
     a_dst[i] = r * S + ((kc ^ (r & 7)) * 8);
     if (r > ti.rows - 1) r = ti.rows - 1;  // rows past the group compute garbage, never stored
-    a_off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(lda) + kc * 8;
+    const int src = gth ? gth[arow0 + r] : r;
+    a_off[i] = static_cast<uint32_t>(src) * static_cast<uint32_t>(lda) + kc * 8;
   }
   // For SwiGLU the W3 rows are [BNO, 2 BNO). When that split falls on a chunk
   // boundary of every thread (chunks i >= B_CH / 2), the base choice is static.
@@ -513,8 +516,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
   const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
-                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda * 2;
+  const int32_t* gth = shared ? nullptr : p.gather;
+  const int arow0 = ti.gd.a_row0 + ti.m_tile * BM;  // the tile's first row in the group's A rows
+  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) + (gth ? 0 : static_cast<int64_t>(arow0) * lda * 2);
   // This wave loads A rows [AROWS w, AROWS (w + 1)) and weight rows
   // [BROWS w, BROWS (w + 1)), in instructions of 8 rows each. For SwiGLU the
   // weight rows [0, 128) of the tile are W1 rows and [128, 256) the matching
@@ -532,7 +536,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
     const int r = ar0 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (r & 7);
     const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
-    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(lda) * 2 + chunk * 16);
+    const int src = gth ? gth[arow0 + rr] : rr;
+    offa[i] = static_cast<uint32_t>(src * static_cast<int>(lda) * 2 + chunk * 16);
   }
 #pragma unroll
   for (int i = 0; i < BDMA; ++i) {
@@ -756,8 +761,9 @@ __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
   const int64_t lda = shared ? p.lda_s : p.lda_r;
-  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) +
-                  (static_cast<int64_t>(ti.gd.a_row0) + static_cast<int64_t>(ti.m_tile) * BM) * lda * 2;
+  const int32_t* gth = shared ? nullptr : p.gather;
+  const int arow0 = ti.gd.a_row0 + ti.m_tile * BM;  // the tile's first row in the group's A rows
+  const char* A = static_cast<const char*>(shared ? p.A_s : p.A_r) + (gth ? 0 : static_cast<int64_t>(arow0) * lda * 2);
   const int ar0 = wave * C_::AROWS, wr0 = wave * C_::BROWS;
   const bool w3 = SWI && wr0 >= BNO;
   const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
@@ -768,7 +774,8 @@ __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
     const int r = ar0 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (r & 7);
     const int rr = r > ti.rows - 1 ? ti.rows - 1 : r;  // rows past the group compute garbage, never stored
-    offa[i] = static_cast<uint32_t>(rr * static_cast<int>(lda) * 2 + chunk * 16);
+    const int src = gth ? gth[arow0 + rr] : rr;
+    offa[i] = static_cast<uint32_t>(src * static_cast<int>(lda) * 2 + chunk * 16);
   }
 #pragma unroll
   for (int i = 0; i < BDMA; ++i) {
@@ -1196,7 +1203,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T)) return launch_ffn_skinny(a, up, down, a.part, s);
-  if (a.gather) return hipErrorInvalidValue;  // the tiled GEMMs read routed rows from x_perm only
+  if (a.gather && f32) return hipErrorInvalidValue;  // the fp32 tiles read routed rows from x_perm only
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
   const bool fp8 = (a.w_dtype == 2);
@@ -1208,10 +1215,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   p.n_routed = a.n_routed;
   p.n_groups = G;
   p.tile_start = a.tile_start;
-  // up GEMM: [rows][d] x [d_ff][d]^T -> h [rows][d_ff]
-  p.A_r = a.x_perm;
+  // up GEMM: [rows][d] x [d_ff][d]^T -> h [rows][d_ff]; routed rows from
+  // x_perm, or from x through the permutation's token list
+  p.A_r = a.gather ? a.x : a.x_perm;
+  p.gather = a.gather;
   p.A_s = a.x;
-  p.lda_r = a.ld_xp;
+  p.lda_r = a.gather ? a.d : a.ld_xp;
   p.lda_s = a.d;
   p.B_r = a.w1;
   p.B3_r = a.w3;
@@ -1242,6 +1251,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
 
   // down GEMM: h [rows][d_ff] x [d][d_ff]^T -> y [rows][d]
   p.A_r = a.h;
+  p.gather = nullptr;
   p.A_s = a.h;
   p.lda_r = a.ld_h;
   p.lda_s = a.ld_h;

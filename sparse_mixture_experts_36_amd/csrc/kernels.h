@@ -89,7 +89,7 @@ struct FfnArgs {
   const int32_t* offsets;     // [n_routed+1] device
   const void* x_perm;         // routed A of the up GEMM, rows of pitch ld_xp
   int64_t ld_xp;              // x_perm row pitch (elements)
-  const int32_t* gather;      // decode path only: routed A row r is x row gather[r] (x_perm unused), or null
+  const int32_t* gather;      // bf16 activations only: routed A row r is x row gather[r] (x_perm unused), or null
   int64_t ld_h;               // h row pitch (elements)
   int64_t ld_up, ld_down;     // weight row pitches (elements): W1/W3, W2
   const void* x;              // shared A of the up GEMM
