@@ -169,30 +169,78 @@ __global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void perm_scan_kernel(PermuteArgs a, int nb) {
+// One workgroup of 1024 threads: per expert, the exclusive scan of the block
+// counts in block order (block_base), the capacity cut, and the expert
+// offsets. Expert e's nb counts are cut into S contiguous segments, one
+// thread each (S <= 1024 / NP, NP the power of two >= N, and at least 16
+// blocks a segment): segment sums (16 loads in flight), an in-order scan of
+// the segments, then each segment writes its blocks' bases. Integer
+// arithmetic: the result is exact.
+constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 16;
+
+__global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(PermuteArgs a, int nb) {
+  __shared__ int32_t s_seg[kScanThreads];
   __shared__ int32_t s_kept[kMaxN];
   __shared__ int32_t s_drop[kMaxN];
   const int tid = threadIdx.x, N = a.N;
-  for (int e = tid; e < N; e += kThreads) {
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  // at least one full batch of loads per segment
+  const int S = min(kScanThreads / NP, max(1, (nb + kScanBatch - 1) / kScanBatch));
+  const int e = tid % NP, seg = tid / NP;
+  const bool mine = e < N && seg < S;
+  const int b0 = static_cast<int>((static_cast<int64_t>(seg) * nb) / S);
+  const int b1 = static_cast<int>((static_cast<int64_t>(seg + 1) * nb) / S);
+  if (mine) {
+    int32_t sum = 0;
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (b + i < b1) v[i] = a.block_cnt[static_cast<int64_t>(b + i) * N + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (b + i < b1) sum += v[i];
+    }
+    s_seg[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < N) {  // segments of expert tid in order: exclusive offsets, then the totals
     int32_t run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * N + e;
-      a.block_base[i] = run;
-      run += a.block_cnt[i];
+    for (int sg = 0; sg < S; ++sg) {
+      const int32_t v = s_seg[sg * NP + tid];
+      s_seg[sg * NP + tid] = run;
+      run += v;
     }
     int32_t kept = run;
     if (a.capacity >= 0 && kept > a.capacity) kept = static_cast<int32_t>(a.capacity);
-    s_kept[e] = kept;
-    s_drop[e] = run - kept;
-    a.kept[e] = kept;
+    s_kept[tid] = kept;
+    s_drop[tid] = run - kept;
+    a.kept[tid] = kept;
   }
   __syncthreads();
+  if (mine) {
+    int32_t run = s_seg[tid];
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (b + i < b1) v[i] = a.block_cnt[static_cast<int64_t>(b + i) * N + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (b + i < b1) {
+          a.block_base[static_cast<int64_t>(b + i) * N + e] = run;
+          run += v[i];
+        }
+    }
+  }
   if (tid == 0) {
     int32_t off = 0, drop = 0;
-    for (int e = 0; e < N; ++e) {
-      a.offsets[e] = off;
-      off += s_kept[e];
-      drop += s_drop[e];
+    for (int x = 0; x < N; ++x) {
+      a.offsets[x] = off;
+      off += s_kept[x];
+      drop += s_drop[x];
     }
     a.offsets[N] = off;
     *a.n_dropped = drop;
@@ -262,14 +310,14 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   if (a.T <= 0) {
     // no tokens: the scan over zero blocks writes the empty layout
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, 0);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a, 0);
     return hipGetLastError();
   }
   const int nb = static_cast<int>(ceil_div(a.T, kPermTokens));
   stage_mark(kStagePermute, false, s);
   hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(kThreads), 0, s, a);
   // one rank block also scans, and without rows to copy also writes the slots
-  if (nb > 1) hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  if (nb > 1) hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a, nb);
   if (nb > 1 || a.x_perm)
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(a.T, 4))), dim3(kThreads), 0, s,
                        a);

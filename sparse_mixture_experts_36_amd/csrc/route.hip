@@ -338,29 +338,90 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a, const
   }
 }
 
-// One workgroup: sums the block partials in block order (fp64) and writes
+// One workgroup of 1024 threads: sums the block partials (fp64) and writes
 // counts, f = counts/(T k), P = sum/T, L_aux = alpha N sum f P, z = mean(lse)^2.
-__global__ __launch_bounds__(kThreads) void route_finalize_kernel(RouteArgs a, int nb) {
+// Expert e's nb partials are cut into S contiguous segments, one thread each
+// (S <= 1024 / NP, NP the power of two >= N, and at least 16 blocks a segment);
+// a segment is summed in block order with 16 loads in flight, then the
+// segments in order. The lse sums run the same way over up to 64 lanes of
+// wave 0. Every order is fixed.
+constexpr int kFinThreads = 1024;
+constexpr int kFinBatch = 16;
+
+__global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a, int nb) {
   __shared__ double s_fp[kMaxN];
+  __shared__ double s_segp[kFinThreads];
+  __shared__ int64_t s_segc[kFinThreads];
+  __shared__ double s_lse[2][64];
   const int tid = threadIdx.x;
   const int N = a.N;
-  for (int e = tid; e < kMaxN; e += kThreads) s_fp[e] = 0.0;
-  __syncthreads();
-  for (int e = tid; e < N; e += kThreads) {
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  // at least one full batch of loads per segment
+  const int S = min(kFinThreads / NP, max(1, (nb + kFinBatch - 1) / kFinBatch));
+  const int e = tid % NP, seg = tid / NP;
+  if (e < N && seg < S) {
+    const int b0 = static_cast<int>((static_cast<int64_t>(seg) * nb) / S);
+    const int b1 = static_cast<int>((static_cast<int64_t>(seg + 1) * nb) / S);
     double p = 0.0;
     int64_t c = 0;
-    for (int b = 0; b < nb; ++b) {
-      p += static_cast<double>(a.part_P[static_cast<int64_t>(b) * N + e]);
-      c += a.part_cnt[static_cast<int64_t>(b) * N + e];
+    for (int b = b0; b < b1; b += kFinBatch) {
+      float vp[kFinBatch];
+      int32_t vc[kFinBatch];
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+        if (b + i < b1) {
+          vp[i] = a.part_P[static_cast<int64_t>(b + i) * N + e];
+          vc[i] = a.part_cnt[static_cast<int64_t>(b + i) * N + e];
+        }
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+        if (b + i < b1) {
+          p += static_cast<double>(vp[i]);
+          c += vc[i];
+        }
     }
-    finalize_expert(a, e, p, c, s_fp);
+    s_segp[tid] = p;
+    s_segc[tid] = c;
+  }
+  const int SL = min(64, max(1, (nb + kFinBatch - 1) / kFinBatch));  // lse segments
+  if (tid < SL) {  // lse: lane L takes blocks [L nb / SL, (L + 1) nb / SL)
+    const int b0 = (tid * nb) / SL, b1 = ((tid + 1) * nb) / SL;
+    double ls = 0.0, lq = 0.0;
+    for (int b = b0; b < b1; b += kFinBatch) {
+      float v1[kFinBatch], v2[kFinBatch];
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+        if (b + i < b1) {
+          v1[i] = a.part_lse[2 * (b + i)];
+          v2[i] = a.part_lse[2 * (b + i) + 1];
+        }
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+        if (b + i < b1) {
+          ls += static_cast<double>(v1[i]);
+          lq += static_cast<double>(v2[i]);
+        }
+    }
+    s_lse[0][tid] = ls;
+    s_lse[1][tid] = lq;
+  }
+  __syncthreads();
+  if (tid < N) {
+    double p = 0.0;
+    int64_t c = 0;
+    for (int sg = 0; sg < S; ++sg) {
+      p += s_segp[sg * NP + tid];
+      c += s_segc[sg * NP + tid];
+    }
+    finalize_expert(a, tid, p, c, s_fp);
   }
   __syncthreads();
   if (tid == 0) {
     double ls = 0.0, lq = 0.0;
-    for (int b = 0; b < nb; ++b) {
-      ls += static_cast<double>(a.part_lse[2 * b]);
-      lq += static_cast<double>(a.part_lse[2 * b + 1]);
+    for (int l = 0; l < SL; ++l) {
+      ls += s_lse[0][l];
+      lq += s_lse[1][l];
     }
     finalize_scalars(a, s_fp, ls, lq);
   }
@@ -405,7 +466,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  if (nb > 1) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, s, a, nb);
+  if (nb > 1) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, a, nb);
   stage_mark(kStageRoute, true, s);
   return hipGetLastError();
 }
