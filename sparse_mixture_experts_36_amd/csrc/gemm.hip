@@ -1146,13 +1146,15 @@ hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t
 }
 
 // Tile configuration of a bf16 call: register-staged tiles for few rows; for
-// many rows the LDS-DMA tiles, 256 rows when the groups average at least 768
-// rows (little padding in a group's last tile), else 128.
+// many rows the LDS-DMA tiles, 256 rows when the groups average at least 384
+// rows, else 128 (less padding in each group's last tile). Measured: the
+// fine-grained layer (about 400 rows a group, two shared experts of 8192)
+// runs 4 % faster on 256-row tiles, the Switch layer (at most 320) 11 % slower.
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
   if (rows < 2048) return kReg128;
   if (a.w_dtype == 2) return kReg256;
-  return rows >= 768LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
+  return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
 // Compute units of the current device, cached per device.

@@ -182,7 +182,7 @@ FFN_CASES = [
     dict(T=400, N=16, k=1, act=gen.GELU, d=256, d_ff=512, wdt=gen.E4M3, biases=True, pad=32),  # fp8, padded
     dict(T=130, N=8, k=2, act=gen.SWIGLU, d=128, d_ff=256, dt=gen.F32, n_shared=1, pad=16),    # fp32, padded
     # prefill-sized calls (>= 2048 expert rows): the LDS-DMA tiles, 128 x 256
-    # when the groups average fewer than 768 rows, else 256 x 256. With 256
+    # when the groups average fewer than 384 rows, else 256 x 256. With 256
     # CUs, a launch whose last round holds r <= 128 tiles cuts those tiles
     # along k and sums the chunks in a fix-up pass; the comments give (tiles,
     # split) of the up and down GEMM.
@@ -192,7 +192,7 @@ FFN_CASES = [
     dict(T=3000, N=4, k=2, act=gen.SWIGLU, d=1024, d_ff=512),                 # 256 rows: (~100, 2), (~100, 2)
     dict(T=3072, N=4, k=1, act=gen.GELU, d=512, d_ff=1024, biases=True),      # 256 rows: (~52, 4), (~26, 8)
     dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512),                  # 128 rows: (~80, 4), (~40, 4)
-    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, pad=16),  # padded weights + shared
+    dict(T=1200, N=8, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, pad=16),  # padded weights + shared; 256 rows
     dict(T=1100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=4096),                 # 128 rows: (~768, none), (~24, 8)
     dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True),  # 128 rows: (~128, 2), (~32, 8)
     dict(T=1024, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),    # 128 rows: (~150, none), (~75, 2)
