@@ -356,9 +356,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 }
 
 // ------------------------------------------------------------------ bf16 MFMA, LDS DMA pipeline
-// BM x 256 tile (BM = 256 or 128), 8 waves (2 x 4, each BM/2 rows x 64 weight
-// rows), k-stages of 64 through LDS stage buffers: two of 64 KB for BM = 256,
-// three of 48 KB for BM = 128 (two stages in flight). Operands move from
+// BM x 256 tile, 8 waves (2 x 4, each BM/2 rows x 64 weight rows), k-stages of
+// 64 through LDS stage buffers. gemm_dma_kernel runs the 128-row tile with
+// three shared 48 KB buffers (two stages in flight); gemm_dma5_kernel runs the
+// 256-row tile with separate activation and weight buffers. Operands move from
 // memory to LDS with global_load_lds (no VGPR staging, no ds_write): each wave
 // instruction writes 1 KB = 8 rows x 128 B, so every fetched 128-byte line is
 // used whole, and the source address each lane fetches puts 16-byte chunk c of
@@ -713,7 +714,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
 // buffers of weight rows, filled two stages ahead (all 160 KB of LDS). The
 // weight rows come from HBM, so they get the longer lead; the activation rows
 // of a tile's group are mostly L2 hits. Waves, fragments, reads and the
-// epilogue are those of gemm_dma_kernel<EPI, 256, 8>.
+// epilogue follow dma::Cfg<256, 8>, as gemm_dma_kernel's do for its tile.
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
   using namespace dma;
@@ -1116,7 +1117,7 @@ hipError_t run_dma5(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // split tiles: r <= kSplitUnits / 2 (each is cut at least in two); the
-    // partial tiles have gemm_dma_kernel<EPI, 256, 8>'s fragment layout
+    // partial tiles have the fragment layout of dma::Cfg<256, 8>
     hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, 256, 8>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
   }
   return hipGetLastError();
