@@ -35,7 +35,8 @@
  *    moe_workspace_size() bytes for that entry point, 256-byte aligned. Its
  *    contents on entry do not matter; they are clobbered.
  *  - Limits: 1 <= N <= 256, 1 <= k <= min(8, N), n_shared <= 4, d and d_ff
- *    multiples of 128, T <= 2^24, T*k*max(d, d_ff) < 2^31. Otherwise
+ *    multiples of 128 and at most 2^20, T <= 2^24, T*k*max(d, d_ff) < 2^31,
+ *    weight row pitches (ld_up, ld_down) at most 2^21 elements. Otherwise
  *    MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_

@@ -19,6 +19,8 @@ thread_local int g_last_hip_error = 0;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxShared = 4;
+constexpr int64_t kMaxWidth = int64_t{1} << 20;  // d, d_ff
+constexpr int64_t kMaxPitch = int64_t{1} << 21;  // weight row pitches (elements)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -46,6 +48,8 @@ moe_status check_shape(const moe_shape* s) {
   if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (s->n_experts > kMaxExperts || s->top_k > kMaxTopK || s->n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // kernels form row offsets inside a tile or a pass in 32 bits
+  if (s->d > kMaxWidth || s->d_ff > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   if (s->w_dtype != s->act_dtype && !(s->w_dtype == MOE_FP8_E4M3 && s->act_dtype == MOE_BF16))
     return MOE_ERR_UNSUPPORTED;
   if (s->T > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
@@ -260,6 +264,7 @@ moe_status check_weights(const moe_shape& s, const moe_weights* w, bool need_rou
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (w->ld_up != 0 && (w->ld_up < s.d || w->ld_up % 16 != 0)) return MOE_ERR_INVALID_ARG;
   if (w->ld_down != 0 && (w->ld_down < s.d_ff || w->ld_down % 16 != 0)) return MOE_ERR_INVALID_ARG;
+  if (w->ld_up > kMaxPitch || w->ld_down > kMaxPitch) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -61,6 +61,8 @@ def _shape(**kw):
     (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(capacity=-2), moe.MOE_ERR_INVALID_ARG),
     (dict(n_shared=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1, d=(1 << 20) + 128), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1, d_ff=(1 << 20) + 128), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, status):
     n = ctypes.c_size_t()
@@ -123,6 +125,11 @@ def test_null_and_workspace_errors_return_before_launch():
         w = moe.Weights(w_router=1 << 20, w1=1 << 20, w3=1 << 20, w2=1 << 20, ld_up=ld_up, ld_down=ld_down)
         assert L.moe_forward(ctypes.byref(s), fake, ctypes.byref(w), fake, None, None, None, None, None, None,
                              None, fake, 1 << 34, None) == moe.MOE_ERR_INVALID_ARG, (ld_up, ld_down)
+    # pitches past 2^21 elements: valid, but beyond the 32-bit row offsets of the kernels
+    for ld_up, ld_down in (((1 << 21) + 16, 0), (0, (1 << 21) + 16)):
+        w = moe.Weights(w_router=1 << 20, w1=1 << 20, w3=1 << 20, w2=1 << 20, ld_up=ld_up, ld_down=ld_down)
+        assert L.moe_forward(ctypes.byref(s), fake, ctypes.byref(w), fake, None, None, None, None, None, None,
+                             None, fake, 1 << 34, None) == moe.MOE_ERR_UNSUPPORTED, (ld_up, ld_down)
 
 
 def test_weight_row_pitches_come_from_tensor_strides():
