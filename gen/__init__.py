@@ -34,6 +34,7 @@ F32, BF16, E4M3 = 0, 1, 2
 # activation / gating codes
 GELU, SWIGLU = 0, 1
 SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
+EXPERT_CHOICE = 3  # each expert takes its C tokens (top_k is 1, C = floor(cf*T/N))
 
 
 def build(verbose: bool = False) -> str:
@@ -170,8 +171,17 @@ SWITCH_TOP1 = Workload("switch-top1-bf16", 16384, 1024, 4096, 64, 1, GELU, SOFTM
                        zipf_s=1.2)
 SWITCH_TOP1_FP8 = SWITCH_TOP1.with_(name="switch-top1-fp8w", w_dtype=E4M3)
 
+# Expert-choice routing on the same layers: cf = 2 gives the Mixtral layer the
+# rows of its top-2 token-choice form (C = 1024 tokens per expert at T = 4096).
+TINY_GELU_EC = TINY_GELU.with_(name="tiny-gelu-fp32-ec", top_k=1, gating=EXPERT_CHOICE, capacity_factor=2.0)
+MIXTRAL_PREFILL_EC = MIXTRAL_PREFILL.with_(name="mixtral-prefill-ec-bf16", top_k=1, gating=EXPERT_CHOICE,
+                                           capacity_factor=2.0)
+FINE_GRAINED_EC = FINE_GRAINED.with_(name="fine-grained-160-ec-shared2-bf16", top_k=1, gating=EXPERT_CHOICE,
+                                     capacity_factor=6.0)
+
 WORKLOADS = {w.name: w for w in [TINY_GELU, MIXTRAL_PREFILL, *MIXTRAL_DECODE.values(), FINE_GRAINED,
-                                  SWITCH_TOP1, SWITCH_TOP1_FP8]}
+                                  SWITCH_TOP1, SWITCH_TOP1_FP8, TINY_GELU_EC, MIXTRAL_PREFILL_EC,
+                                  FINE_GRAINED_EC]}
 
 
 @dataclass

@@ -63,8 +63,13 @@ def lib():
         L.orc_expert_rows.argtypes = [sp, wp, i32, i32, vp, i64, vp]
         L.orc_moe_output.argtypes = [sp, vp, wp, vp, vp, vp, vp, i64, vp]
         L.orc_combine.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.orc_route_ec.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_dispatch_ec.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.orc_moe_output_ec.argtypes = [sp, vp, wp, vp, vp, vp, i64, vp]
+        L.orc_combine_ec.argtypes = [sp, vp, vp, vp, vp, vp]
         for name in ("orc_router_logits", "orc_route", "orc_dispatch", "orc_expert_rows",
-                     "orc_moe_output", "orc_combine", "orc_abi_version", "orc_threads"):
+                     "orc_moe_output", "orc_combine", "orc_route_ec", "orc_dispatch_ec", "orc_moe_output_ec",
+                     "orc_combine_ec", "orc_abi_version", "orc_threads"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("orc_bf16_value", "orc_gelu", "orc_silu"):
             getattr(L, name).restype = ctypes.c_double
@@ -198,11 +203,71 @@ def combine(shape: OrcShape, y_perm, inv_map, topk_w32, y_shared=None) -> np.nda
     return y
 
 
+EXPERT_CHOICE = 3  # OrcShape.gating of expert-choice routing
+
+
+@dataclass
+class RoutingEC:
+    ec_token: np.ndarray   # [N,C] int32, ascending per expert
+    ec_gate: np.ndarray    # [N,C] fp64 column-softmax probabilities
+    probs: np.ndarray      # [T,N] fp64 softmax over tokens, per expert
+    lse: np.ndarray        # [T] per-token logsumexp over experts
+    z: float
+    lse_sq_mean: float
+
+
+def route_ec(shape: OrcShape, logits32: np.ndarray) -> RoutingEC:
+    """Expert-choice selection and gates from fp32 logits [T,N] (shape.gating 3)."""
+    T, N, C = shape.T, shape.n_experts, shape.capacity
+    logits32 = np.ascontiguousarray(logits32, np.float32)
+    assert logits32.shape == (T, N)
+    tok = np.empty((N, C), np.int32)
+    gate = np.empty((N, C), np.float64)
+    probs = np.empty((T, N), np.float64)
+    lse = np.empty(T, np.float64)
+    z, lsq = ctypes.c_double(), ctypes.c_double()
+    _check(lib().orc_route_ec(ctypes.byref(shape), _p(logits32), _p(tok), _p(gate), _p(probs), _p(lse),
+                              ctypes.addressof(z), ctypes.addressof(lsq)), "route_ec")
+    return RoutingEC(tok, gate, probs, lse, z.value, lsq.value)
+
+
+def dispatch_ec(shape: OrcShape, ec_token: np.ndarray) -> Dispatch:
+    """Row layout of expert-choice assignments: rows e*C + j; inv_map [T,N];
+    n_dropped = tokens that no expert took."""
+    T, N, C = shape.T, shape.n_experts, shape.capacity
+    ec_token = np.ascontiguousarray(ec_token, np.int32)
+    off = np.empty(N + 1, np.int32)
+    perm = np.empty(N * C, np.int32)
+    inv = np.empty((T, N), np.int32)
+    nd = ctypes.c_int64()
+    _check(lib().orc_dispatch_ec(ctypes.byref(shape), _p(ec_token), _p(off), _p(perm), _p(inv),
+                                 ctypes.addressof(nd)), "dispatch_ec")
+    return Dispatch(np.full(N, C, np.int32), off, perm, inv, nd.value)
+
+
+def moe_output_ec(shape: OrcShape, x, inp, r: RoutingEC, tokens: np.ndarray) -> np.ndarray:
+    w, _keep = weights_of(inp)
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    y = np.empty((len(tokens), shape.d), np.float64)
+    _check(lib().orc_moe_output_ec(ctypes.byref(shape), _p(x), ctypes.byref(w), _p(r.ec_token),
+                                   _p(np.ascontiguousarray(r.ec_gate)), _p(tokens), len(tokens), _p(y)),
+           "moe_output_ec")
+    return y
+
+
+def combine_ec(shape: OrcShape, y_perm, inv_map, gate_row32, y_shared=None) -> np.ndarray:
+    y = np.empty((shape.T, shape.d), np.float64)
+    _check(lib().orc_combine_ec(ctypes.byref(shape), _p(y_perm), _p(np.ascontiguousarray(inv_map, np.int32)),
+                                _p(np.ascontiguousarray(gate_row32, np.float32)), _p(y_shared), _p(y)),
+           "combine_ec")
+    return y
+
+
 @dataclass
 class Forward:
     logits64: np.ndarray
     logits32: np.ndarray
-    routing: Routing
+    routing: Routing | RoutingEC
     disp: Dispatch
     tokens: np.ndarray
     y: np.ndarray            # [len(tokens), d] fp64
@@ -217,11 +282,16 @@ def forward(inp, tokens: np.ndarray | None = None, logits32: np.ndarray | None =
         l64, l32 = router_logits(shape, inp.x, inp)
     else:
         l64, l32 = logits32.astype(np.float64), np.ascontiguousarray(logits32, np.float32)
-    r = route(shape, l32)
-    dsp = dispatch(shape, r.topk_idx)
     if tokens is None:
         tokens = np.arange(wl.T, dtype=np.int64)
-    y = moe_output(shape, inp.x, inp, r, dsp, tokens)
+    if shape.gating == EXPERT_CHOICE:
+        r = route_ec(shape, l32)
+        dsp = dispatch_ec(shape, r.ec_token)
+        y = moe_output_ec(shape, inp.x, inp, r, tokens)
+    else:
+        r = route(shape, l32)
+        dsp = dispatch(shape, r.topk_idx)
+        y = moe_output(shape, inp.x, inp, r, dsp, tokens)
     return Forward(l64, l32, r, dsp, np.asarray(tokens, np.int64), y)
 
 

@@ -14,10 +14,14 @@
 //  [MOEA] vanos001 placement notes, "MoE Architecture": section "Expert Network
 //         Design" (SwiGLUExpert w2(silu(w1 x) * w3 x); StandardExpert
 //         Linear-GELU-Linear), "Router Design / Token-Choice Router" (top-k on
-//         logits, then softmax over the k), "Capacity and Token Dropping".
+//         logits, then softmax over the k), "Router Design / Expert-Choice
+//         Router" (softmax over tokens, each expert's top-capacity tokens) and
+//         the router comparison table, "Capacity and Token Dropping".
 //  [SPX]  learn.starphix.com, "Mixture of Experts (MoE)": sections "Key
 //         Equations", "Top-k Gating", "Load Balancing (Critical)"
 //         (load_balancing_loss, z_loss), "Shared + Specialized".
+//  [CFS]  chipfoundryservices.com glossary, "Mixture of Experts (MoE)": the
+//         "Expert Choice Routing" item (experts pick their tokens; balanced).
 //  [WIKI] wiki.ai-engineering.at, "Mixture of Experts (MoE)": the router /
 //         softmax / top-k / weighted-combination figure and the `MoELayer`
 //         snippet (top-k of the gate scores, softmax over the k).
@@ -37,6 +41,13 @@
 //  - GELU is the exact erf form; SiLU(u) = u / (1 + e^-u).
 //  - e4m3 weights: W = s * q, q an OCP e4m3fn code, one fp32 scale per
 //    (expert, matrix).
+//  - Expert choice [MOEA Expert-Choice Router]: the softmax runs over the
+//    tokens of each expert's column; an expert takes the C = int(T*cf/N)
+//    tokens of largest probability, exact ties to the lower token index, and
+//    lists them in ascending token order (the order inside an expert never
+//    reaches the output). The router there returns only the assignments; the
+//    gate of a taken (token, expert) pair is that column probability, and a
+//    token no expert took gets only the shared experts.
 //
 // Every function returns 0 on success and -1 when the arguments fall outside
 // the contract (k > N, N < 1, ...). Parallelism (OpenMP) only splits
@@ -57,7 +68,8 @@ struct OrcShape {
   int64_t T, d, d_ff;
   int32_t n_experts, top_k, n_shared;
   int32_t act;        // 0 GELU expert (Linear+bias, GELU, Linear+bias), 1 SwiGLU
-  int32_t gating;     // 0 softmax->top-k, 1 softmax->top-k->renormalise, 2 top-k->softmax
+  int32_t gating;     // 0 softmax->top-k, 1 softmax->top-k->renormalise, 2 top-k->softmax,
+                      // 3 expert choice (softmax over tokens, each expert takes C tokens)
   int32_t act_dtype;  // 0 fp32, 1 bf16 (x, router weight, layer output)
   int32_t w_dtype;    // 0 fp32, 1 bf16, 2 e4m3fn + per-(expert, matrix) fp32 scale
   int64_t capacity;   // < 0: no capacity limit
@@ -111,8 +123,19 @@ double elem(const void* p, int dtype, int64_t i, double scale) {
 bool shape_ok(const OrcShape* s) {
   return s && s->T >= 0 && s->d > 0 && s->d_ff > 0 && s->n_experts >= 1 && s->top_k >= 1 &&
          s->top_k <= s->n_experts && s->n_shared >= 0 && (s->act == 0 || s->act == 1) &&
-         s->gating >= 0 && s->gating <= 2 && (s->act_dtype == 0 || s->act_dtype == 1) &&
+         s->gating >= 0 && s->gating <= 3 && (s->act_dtype == 0 || s->act_dtype == 1) &&
          s->w_dtype >= 0 && s->w_dtype <= 2;
+}
+
+// token choice: gating 0..2
+bool shape_ok_tc(const OrcShape* s) { return shape_ok(s) && s->gating != 3; }
+
+// expert choice: gating 3, top_k 1, 0 <= C <= T
+bool shape_ok_ec(const OrcShape* s) {
+  return s && s->T >= 0 && s->d > 0 && s->d_ff > 0 && s->n_experts >= 1 && s->top_k == 1 &&
+         s->n_shared >= 0 && (s->act == 0 || s->act == 1) && s->gating == 3 &&
+         (s->act_dtype == 0 || s->act_dtype == 1) && s->w_dtype >= 0 && s->w_dtype <= 2 &&
+         s->capacity >= 0 && s->capacity <= s->T;
 }
 
 double gelu(double u) { return 0.5 * u * (1.0 + std::erf(u / std::sqrt(2.0))); }
@@ -238,7 +261,7 @@ int orc_route(const OrcShape* s, const float* logits, int32_t* topk_idx, double*
               double* probs, double* lse_out, double* margin_set, double* margin_order,
               int64_t* counts, double* f, double* P, double* l_aux, double* z,
               double* lse_sq_mean) {
-  if (!shape_ok(s) || !logits || !topk_idx) return -1;
+  if (!shape_ok_tc(s) || !logits || !topk_idx) return -1;
   const int64_t T = s->T, N = s->n_experts, k = s->top_k;
   std::vector<double> p_all(static_cast<size_t>(T * N));
   std::vector<double> lse(static_cast<size_t>(T));
@@ -332,7 +355,7 @@ int orc_route(const OrcShape* s, const float* logits, int32_t* topk_idx, double*
 //   inv_map[t*k + j] = row of pair (t, S_t[j]), or -1 if dropped.
 int orc_dispatch(const OrcShape* s, const int32_t* topk_idx, int32_t* kept, int32_t* offsets,
                  int32_t* perm_token, int32_t* inv_map, int64_t* n_dropped) {
-  if (!shape_ok(s) || !topk_idx) return -1;
+  if (!shape_ok_tc(s) || !topk_idx) return -1;
   const int64_t T = s->T, N = s->n_experts, k = s->top_k;
   const int64_t C = s->capacity;
   std::vector<std::vector<std::pair<int64_t, int64_t>>> lists(static_cast<size_t>(N));
@@ -388,7 +411,7 @@ int orc_expert_rows(const OrcShape* s, const OrcWeights* w, int shared, int e, c
 int orc_moe_output(const OrcShape* s, const void* x, const OrcWeights* w, const int32_t* topk_idx,
                    const double* topk_w, const int32_t* inv_map, const int64_t* tokens,
                    int64_t n_tok, double* y) {
-  if (!shape_ok(s) || !x || !w || !topk_idx || !topk_w || !tokens || !y) return -1;
+  if (!shape_ok_tc(s) || !x || !w || !topk_idx || !topk_w || !tokens || !y) return -1;
   const int64_t d = s->d, k = s->top_k, N = s->n_experts;
   for (int64_t i = 0; i < n_tok * d; ++i) y[i] = 0.0;
   for (int64_t e = 0; e < N; ++e) {
@@ -430,7 +453,7 @@ int orc_moe_output(const OrcShape* s, const void* x, const OrcWeights* w, const 
 // (+ sum_s y_shared[s][t] when y_shared is given, [S][T][d] activation dtype).
 int orc_combine(const OrcShape* s, const void* y_perm, const int32_t* inv_map, const float* topk_w,
                 const void* y_shared, double* y) {
-  if (!shape_ok(s) || !y_perm || !inv_map || !topk_w || !y) return -1;
+  if (!shape_ok_tc(s) || !y_perm || !inv_map || !topk_w || !y) return -1;
   const int64_t T = s->T, d = s->d, k = s->top_k;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
@@ -439,6 +462,159 @@ int orc_combine(const OrcShape* s, const void* y_perm, const int32_t* inv_map, c
       for (int64_t j = 0; j < k; ++j) {
         const int64_t row = inv_map[t * k + j];
         if (row >= 0) acc += static_cast<double>(topk_w[t * k + j]) * elem(y_perm, s->act_dtype, row * d + c, 1.0);
+      }
+      if (y_shared)
+        for (int64_t sh = 0; sh < s->n_shared; ++sh)
+          acc += elem(y_shared, s->act_dtype, (sh * T + t) * d + c, 1.0);
+      y[t * d + c] = acc;
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------- expert choice
+// [MOEA "Router Design", Expert-Choice Router and the router comparison table;
+// AIG, the variants paragraph; chipfoundryservices glossary, "Expert Choice
+// Routing"; SPX routing-variants table]. Every expert picks its own tokens:
+//   probs[t][e] = exp(l[t][e] - m_e) / sum_t' exp(l[t'][e] - m_e), m_e = max_t l[t][e]
+//                 (softmax over the TOKENS of column e)
+//   expert e takes the C tokens with the largest probs[:, e] (exact ties to the
+//   lower token index), C = capacity (0 <= C <= T), and lists them in
+//   ascending token order; the gate of (t, e) is probs[t][e].
+// A token may be taken by any number of experts, none included.
+// Shape contract: gating 3, top_k 1, 0 <= capacity <= T.
+
+// Selection and gates from fp32 logits [T][N]:
+//   ec_token [N][C] the tokens of expert e, ascending; ec_gate [N][C] their
+//   probs[t][e]; probs [T][N] (optional) the whole column softmax; lse [T]
+//   (optional) and z / lse_sq_mean: the router's per-token logsumexp over the
+//   experts, the same z statistics as token choice [SPX z_loss].
+int orc_route_ec(const OrcShape* s, const float* logits, int32_t* ec_token, double* ec_gate, double* probs,
+                 double* lse_out, double* z, double* lse_sq_mean) {
+  if (!shape_ok_ec(s) || !logits || (s->capacity > 0 && (!ec_token || !ec_gate))) return -1;
+  const int64_t T = s->T, N = s->n_experts, C = s->capacity;
+  std::vector<double> p(static_cast<size_t>(T * N));
+  for (int64_t e = 0; e < N; ++e) {
+    double m = -std::numeric_limits<double>::infinity();
+    for (int64_t t = 0; t < T; ++t) m = std::max(m, static_cast<double>(logits[t * N + e]));
+    double sum = 0.0;
+    for (int64_t t = 0; t < T; ++t) sum += std::exp(static_cast<double>(logits[t * N + e]) - m);
+    for (int64_t t = 0; t < T; ++t) p[t * N + e] = std::exp(static_cast<double>(logits[t * N + e]) - m) / sum;
+
+    // top-C of the column: tokens ordered by probability, descending; the
+    // stable sort keeps ascending token order among equal probabilities
+    std::vector<int64_t> order(static_cast<size_t>(T));
+    for (int64_t t = 0; t < T; ++t) order[t] = t;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return p[a * N + e] > p[b * N + e]; });
+    std::vector<int64_t> pick(order.begin(), order.begin() + C);
+    std::sort(pick.begin(), pick.end());
+    for (int64_t j = 0; j < C; ++j) {
+      ec_token[e * C + j] = static_cast<int32_t>(pick[j]);
+      ec_gate[e * C + j] = p[pick[j] * N + e];
+    }
+  }
+  if (probs) std::memcpy(probs, p.data(), sizeof(double) * static_cast<size_t>(T * N));
+  double lse_sum = 0.0, lse_sq = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    double m = -std::numeric_limits<double>::infinity();
+    for (int64_t e = 0; e < N; ++e) m = std::max(m, static_cast<double>(logits[t * N + e]));
+    double sum = 0.0;
+    for (int64_t e = 0; e < N; ++e) sum += std::exp(static_cast<double>(logits[t * N + e]) - m);
+    const double l = m + std::log(sum);
+    if (lse_out) lse_out[t] = l;
+    lse_sum += l;
+    lse_sq += l * l;
+  }
+  const double lm = (T > 0) ? lse_sum / static_cast<double>(T) : 0.0;
+  if (z) *z = lm * lm;
+  if (lse_sq_mean) *lse_sq_mean = (T > 0) ? lse_sq / static_cast<double>(T) : 0.0;
+  return 0;
+}
+
+// Row layout of the expert-choice assignments: expert e's j-th token sits in
+// row e*C + j, so offsets[e] = e*C, perm_token[e*C + j] = ec_token[e][j],
+// inv_map[t][e] = the row of (t, e) or -1, and n_untouched = the number of
+// tokens no expert took. ec_token rows must be ascending and within [0, T).
+int orc_dispatch_ec(const OrcShape* s, const int32_t* ec_token, int32_t* offsets, int32_t* perm_token,
+                    int32_t* inv_map, int64_t* n_untouched) {
+  if (!shape_ok_ec(s) || (s->capacity > 0 && !ec_token)) return -1;
+  const int64_t T = s->T, N = s->n_experts, C = s->capacity;
+  if (inv_map)
+    for (int64_t i = 0; i < T * N; ++i) inv_map[i] = -1;
+  std::vector<int32_t> taken(static_cast<size_t>(T), 0);
+  for (int64_t e = 0; e < N; ++e) {
+    if (offsets) offsets[e] = static_cast<int32_t>(e * C);
+    for (int64_t j = 0; j < C; ++j) {
+      const int64_t t = ec_token[e * C + j];
+      if (t < 0 || t >= T || (j > 0 && t <= ec_token[e * C + j - 1])) return -1;
+      if (perm_token) perm_token[e * C + j] = static_cast<int32_t>(t);
+      if (inv_map) inv_map[t * N + e] = static_cast<int32_t>(e * C + j);
+      taken[t] = 1;
+    }
+  }
+  if (offsets) offsets[N] = static_cast<int32_t>(N * C);
+  if (n_untouched) {
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; ++t) n += taken[t] ? 0 : 1;
+    *n_untouched = n;
+  }
+  return 0;
+}
+
+// Layer output of the listed tokens under expert choice: each expert runs on
+// the tokens it took and adds gate * output into them, then the shared experts
+// [SPX "Shared + Specialized"]:
+//   y_t = sum_{e : t in ec_token[e]} probs[t][e] E_e(x_t) + sum_s E^sh_s(x_t)
+int orc_moe_output_ec(const OrcShape* s, const void* x, const OrcWeights* w, const int32_t* ec_token,
+                      const double* ec_gate, const int64_t* tokens, int64_t n_tok, double* y) {
+  if (!shape_ok_ec(s) || !x || !w || !tokens || !y || (s->capacity > 0 && (!ec_token || !ec_gate))) return -1;
+  const int64_t d = s->d, N = s->n_experts, C = s->capacity;
+  for (int64_t i = 0; i < n_tok * d; ++i) y[i] = 0.0;
+  for (int64_t e = 0; e < N; ++e) {
+    std::vector<int64_t> which;  // position in `tokens`
+    std::vector<double> gate;
+    for (int64_t i = 0; i < n_tok; ++i)
+      for (int64_t j = 0; j < C; ++j)
+        if (ec_token[e * C + j] == tokens[i]) {
+          which.push_back(i);
+          gate.push_back(ec_gate[e * C + j]);
+        }
+    if (which.empty()) continue;
+    const int64_t n = static_cast<int64_t>(which.size());
+    std::vector<double> X(static_cast<size_t>(n * d)), Y(static_cast<size_t>(n * d));
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) X[r * d + c] = elem(x, s->act_dtype, tokens[which[r]] * d + c, 1.0);
+    expert_rows(s, w, false, static_cast<int>(e), X.data(), n, Y.data());
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) y[which[r] * d + c] += gate[r] * Y[r * d + c];
+  }
+  if (s->n_shared > 0) {
+    std::vector<double> X(static_cast<size_t>(n_tok * d)), Y(static_cast<size_t>(n_tok * d));
+    for (int64_t r = 0; r < n_tok; ++r)
+      for (int64_t c = 0; c < d; ++c) X[r * d + c] = elem(x, s->act_dtype, tokens[r] * d + c, 1.0);
+    for (int sh = 0; sh < s->n_shared; ++sh) {
+      expert_rows(s, w, true, sh, X.data(), n_tok, Y.data());
+      for (int64_t i = 0; i < n_tok * d; ++i) y[i] += Y[i];
+    }
+  }
+  return 0;
+}
+
+// Combine alone under expert choice: y_t = sum over experts e ascending with
+// inv_map[t][e] >= 0 of gate_row[r] * y_perm[r], r = inv_map[t][e] (gates
+// indexed by row, [N*C] fp32), plus the shared outputs when given.
+int orc_combine_ec(const OrcShape* s, const void* y_perm, const int32_t* inv_map, const float* gate_row,
+                   const void* y_shared, double* y) {
+  if (!shape_ok_ec(s) || !y_perm || !inv_map || !gate_row || !y) return -1;
+  const int64_t T = s->T, d = s->d, N = s->n_experts;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t e = 0; e < N; ++e) {
+        const int64_t row = inv_map[t * N + e];
+        if (row >= 0) acc += static_cast<double>(gate_row[row]) * elem(y_perm, s->act_dtype, row * d + c, 1.0);
       }
       if (y_shared)
         for (int64_t sh = 0; sh < s->n_shared; ++sh)
