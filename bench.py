@@ -274,6 +274,14 @@ def cpu_baseline(wl, inp, target_s=15.0):
                       f"weights), fp64, {dt:.1f} s"}
 
 
+def dropped_of(wl, latest) -> int:
+    """Dropped (token, expert) pairs under token choice; under expert choice
+    the tokens that no expert took."""
+    import gen
+    per = wl.T if wl.gating == gen.EXPERT_CHOICE else wl.T * wl.top_k
+    return int(latest["dropped_share"] * per + 0.5)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,7 +350,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "d_ff": wl.d_ff, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "act": "swiglu" if wl.act == gen.SWIGLU else "gelu",
-                   "gating": ["softmax_topk", "softmax_topk_renorm", "topk_softmax"][wl.gating],
+                   "gating": ["softmax_topk", "softmax_topk_renorm", "topk_softmax", "expert_choice"][wl.gating],
                    "capacity": wl.capacity(), "n_shared": wl.n_shared,
                    "w_dtype": {0: "f32", 1: "bf16", 2: "e4m3"}[wl.w_dtype], "parallelism": "single-gpu"},
         "roofline": {"kernel": "grouped up GEMM + fused activation", "bound": "mfma",
@@ -353,8 +361,9 @@ def main():
         "layer": {"mfma_frac": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "ffn_mfma_frac": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in st.items()},
-                  "rows": r["rows"], "dropped": int(r["latest"]["dropped_share"] * wl.T * wl.top_k + 0.5),
-                  "l_aux": round(r["latest"]["aux_loss"], 6), "z_loss": round(r["latest"]["z_loss"], 5)},
+                  "rows": r["rows"], "dropped": dropped_of(wl, r["latest"]),
+                  "l_aux": None if r["latest"]["aux_loss"] is None else round(r["latest"]["aux_loss"], 6),
+                  "z_loss": round(r["latest"]["z_loss"], 5)},
     }
     if not args.no_decode and wl.name == "mixtral-prefill-bf16":
         del r

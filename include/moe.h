@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) top-k token-choice Mixture-of-Experts
- * layer forward.
+ * layer forward, with expert-choice routing as a second routing mode.
  *
  * The layer (pages, cited by title and section or equation):
  *   aigrafen.se "Mixture of Experts": y = sum_{i in top-k} g_i E_i(x) with
@@ -13,6 +13,10 @@
  *   learn.starphix.com "Mixture of Experts (MoE)": "Key Equations", "Top-k
  *     Gating", "Load Balancing (Critical)" (load_balancing_loss, z_loss),
  *     "Shared + Specialized", "Quantization".
+ *   Expert choice: vanos001 "MoE Architecture" / "Router Design",
+ *     Expert-Choice Router (softmax over the tokens, each expert takes its
+ *     top-capacity tokens) and the router comparison table; chipfoundryservices
+ *     glossary "Mixture of Experts (MoE)", Expert Choice Routing.
  *
  * Conventions for every entry point:
  *  - Memory: every pointer argument is DEVICE memory except the moe_shape /
@@ -36,8 +40,13 @@
  *    contents on entry do not matter; they are clobbered.
  *  - Limits: 1 <= N <= 256, 1 <= k <= min(8, N), n_shared <= 4, d and d_ff
  *    multiples of 128 and at most 2^20, T <= 2^24, T*k*max(d, d_ff) < 2^31,
- *    weight row pitches (ld_up, ld_down) at most 2^21 elements. Otherwise
- *    MOE_ERR_UNSUPPORTED.
+ *    weight row pitches (ld_up, ld_down) at most 2^21 elements. Expert choice:
+ *    T <= 32768 and N*C*max(d, d_ff) < 2^31. Otherwise MOE_ERR_UNSUPPORTED.
+ *  - Expert choice (gating MOE_GATE_EXPERT_CHOICE): top_k must be 1 and
+ *    capacity is C, the tokens each expert takes, 0 <= C <= T (see
+ *    moe_capacity); otherwise MOE_ERR_INVALID_ARG. The per-token arrays then
+ *    change shape as each entry point states: topk_idx / topk_w become [N][C]
+ *    (expert-major), inv_map [T][N], perm_token [N*C].
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -76,11 +85,18 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
  *  SOFTMAX_TOPK_RENORM: the same, divided by their sum (aigrafen `MoE` module)
  *  TOPK_SOFTMAX:        softmax over the k selected logits (vanos001
  *                       Token-Choice Router; starphix "Top-k Gating") --
- *                       equal to SOFTMAX_TOPK_RENORM in exact arithmetic. */
+ *                       equal to SOFTMAX_TOPK_RENORM in exact arithmetic.
+ * EXPERT_CHOICE: no per-token selection. p[t][e] = softmax over the TOKENS t
+ *                of column e of the logits; expert e takes the C tokens with
+ *                the largest p[:, e] (exact ties to the lower token index),
+ *                listed in ascending token order, with gates p[t][e] (vanos001
+ *                Expert-Choice Router). A token may be taken by several
+ *                experts or by none. */
 typedef enum {
   MOE_GATE_SOFTMAX_TOPK = 0,
   MOE_GATE_SOFTMAX_TOPK_RENORM = 1,
-  MOE_GATE_TOPK_SOFTMAX = 2
+  MOE_GATE_TOPK_SOFTMAX = 2,
+  MOE_GATE_EXPERT_CHOICE = 3
 } moe_gating;
 
 typedef struct {
@@ -88,14 +104,15 @@ typedef struct {
   int64_t d;          /* model width */
   int64_t d_ff;       /* expert hidden width */
   int32_t n_experts;  /* N routed experts */
-  int32_t top_k;      /* k */
+  int32_t top_k;      /* k (1 under expert choice) */
   int32_t n_shared;   /* always-on shared experts, same shape and act (0..4) */
   int32_t act;        /* moe_act */
   int32_t gating;     /* moe_gating */
   int32_t act_dtype;  /* moe_dtype of x, W_r, the layer output: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;    /* moe_dtype of expert weights: same as act_dtype, or
                          MOE_FP8_E4M3 with act_dtype MOE_BF16 */
-  int64_t capacity;   /* C pairs per expert; -1 = no limit (dropless) */
+  int64_t capacity;   /* C pairs per expert; -1 = no limit (dropless).
+                         Expert choice: C tokens per expert, 0 <= C <= T */
   float aux_alpha;    /* alpha of L_aux (the pages use about 0.01) */
 } moe_shape;
 
@@ -127,7 +144,11 @@ typedef struct {
 /* Router statistics (aigrafen L_aux equation and `latest` dict; starphix
  * load_balancing_loss and z_loss). Every member is a device pointer; any
  * member may be NULL (not written). Written by moe_route (counts, f, P, l_aux,
- * z_loss, lse_mean, lse_sq_mean) and moe_permute (kept, n_dropped). */
+ * z_loss, lse_mean, lse_sq_mean) and moe_permute (kept, n_dropped).
+ * Expert choice balances by construction (vanos001 router comparison table):
+ * counts and kept are C for every expert, n_dropped is the number of tokens
+ * no expert took, z_loss / lse_mean / lse_sq_mean are as for token choice
+ * (per-token logsumexp over the experts), and f, P and l_aux are not written. */
 typedef struct {
   int32_t* counts;      /* [N] pairs that selected expert e, before capacity drops */
   int32_t* kept;        /* [N] pairs kept after the capacity cut */
@@ -163,7 +184,8 @@ int moe_last_hip_error(void);
 
 /* Expert capacity C = floor(cf * T * k / N), evaluated in fp64 (aigrafen
  * capacity equation with the module's int(cf*T*k/N)). Returns -1 for cf < 0
- * (no limit) and for N < 1. Host function. */
+ * (no limit) and for N < 1. With k = 1 it is the expert-choice capacity
+ * int(T*cf/N) of the vanos001 Expert-Choice Router. Host function. */
 int64_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf);
 
 /* Device workspace bytes that `entry` needs for `shape`. */
@@ -177,6 +199,8 @@ moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* byt
  *   lower index), gates per shape->gating; statistics into `stats`.
  * x [T][d] act_dtype; logits [T][N] fp32 (written, or read with
  * MOE_ROUTE_LOGITS_GIVEN); topk_idx [T][k] int32; topk_w [T][k] fp32.
+ * Expert choice: topk_idx [N][C] gets the tokens expert e takes (ascending)
+ * and topk_w [N][C] their gates; the logits must not be NaN.
  * Deterministic: identical inputs give identical bits.
  */
 moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router,
@@ -196,6 +220,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
  *   x_perm [T*k][d] (act_dtype): x_perm[r] = x[perm_token[r]] for r < M
  * topk_idx [T][k] int32 with values in [0, N), distinct within a row.
  * Writes stats->kept and stats->n_dropped when given. Bit-deterministic.
+ * Expert choice: topk_idx is moe_route's [N][C] (each row strictly ascending,
+ * tokens in [0, T)); expert e's j-th token gets row e*C + j, so
+ * offsets[e] = e*C, perm_token [N*C] is topk_idx itself, inv_map [T][N] holds
+ * the row of (t, e) or -1, and x_perm has N*C rows.
  */
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                        int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
@@ -226,6 +254,9 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
  * A dropped pair adds 0 (the residual connection is outside this layer); the
  * gates are not renormalised after drops. y_shared may be NULL.
  * fp32 accumulation in a fixed order (slots ascending, then shared experts).
+ * Expert choice: inv_map [T][N] and topk_w [N*C] indexed by row:
+ *   y[t] = sum_{e : inv_map[t][e] >= 0} topk_w[inv_map[t][e]] * y_perm[inv_map[t][e]]
+ *          + sum_s y_shared[s][t], experts ascending.
  */
 moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_map,
                        const float* topk_w, const void* y_shared, void* y, hipStream_t stream);
@@ -235,7 +266,8 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
  * -> moe_combine, enqueued on one stream with no host synchronisation.
  * x [T][d], y [T][d] act_dtype. logits [T][N], topk_idx/topk_w/inv_map [T][k],
  * expert_offsets [N+1], perm_token [T*k] are optional outputs (NULL: kept in
- * the workspace). stats may be NULL.
+ * the workspace); under expert choice they have the shapes moe_route,
+ * moe_permute and moe_combine give them. stats may be NULL.
  */
 moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights* weights,
                        void* y, float* logits, int32_t* topk_idx, float* topk_w,

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) top-k token-choice Mixture-of-Experts layer forward.
+"""MI355X (gfx950) top-k token-choice Mixture-of-Experts layer forward, with
+expert-choice routing as a second routing mode.
 
 Thin Python binding over the C ABI in ``include/moe.h`` (``libmoe.so``, built
 in-tree by ``sparse_mixture_experts_36_amd.build``). The functions here only
@@ -20,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2
 GELU, SWIGLU = 0, 1
-SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
+SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX, EXPERT_CHOICE = 0, 1, 2, 3
 ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_FFN, ENTRY_FORWARD = 0, 1, 2, 3
 ROUTE_LOGITS_GIVEN = 1
 
@@ -113,8 +114,20 @@ def make_shape(T, d, d_ff, n_experts, top_k, act, gating, act_dtype, w_dtype, ca
 
 
 def capacity(T: int, k: int, N: int, cf: float | None) -> int:
-    """floor(cf*T*k/N) (moe_capacity); -1 when cf is None (dropless)."""
+    """floor(cf*T*k/N) (moe_capacity); -1 when cf is None (dropless). With k = 1
+    it is the expert-choice capacity int(T*cf/N)."""
     return -1 if cf is None else lib().moe_capacity(T, k, N, cf)
+
+
+def routing_shapes(shape: Shape) -> dict:
+    """Shapes of the routing arrays for this layer: topk_idx / topk_w are
+    [T, k] under token choice and [N, C] (expert-major) under expert choice;
+    inv_map is [T, k] or [T, N]; perm_token has T*k or N*C entries."""
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    if shape.gating == EXPERT_CHOICE:
+        C = shape.capacity
+        return {"topk": (N, C), "inv_map": (T, N), "perm_token": (N * C,)}
+    return {"topk": (T, k), "inv_map": (T, k), "perm_token": (T * k,)}
 
 
 def workspace_size(shape: Shape, entry: int = ENTRY_FORWARD) -> int:
@@ -266,15 +279,16 @@ class MoELayer:
         self.tensors = tensors
         self.weights = weights_struct(tensors)
         self.ws = workspace(shape, ENTRY_FORWARD, device)
-        T, N, k = shape.T, shape.n_experts, shape.top_k
+        T, N = shape.T, shape.n_experts
+        rs = routing_shapes(shape)
         i32 = dict(dtype=torch.int32, device=device)
         self.out = LayerOutputs(
             y=torch.empty((T, shape.d), dtype=torch.float32 if shape.act_dtype == F32 else torch.bfloat16,
                           device=device),
             logits=torch.empty((T, N), dtype=torch.float32, device=device),
-            topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
-            expert_offsets=torch.empty(N + 1, **i32), perm_token=torch.empty(T * k, **i32),
-            inv_map=torch.empty((T, k), **i32), stats=alloc_stats(N, device))
+            topk_idx=torch.empty(rs["topk"], **i32), topk_w=torch.empty(rs["topk"], dtype=torch.float32, device=device),
+            expert_offsets=torch.empty(N + 1, **i32), perm_token=torch.empty(rs["perm_token"], **i32),
+            inv_map=torch.empty(rs["inv_map"], **i32), stats=alloc_stats(N, device))
 
     def __call__(self, x, stream=None) -> LayerOutputs:
         o = self.out
@@ -303,6 +317,16 @@ class MoELayer:
         """Host copy of the router statistics (synchronises): aux loss, z-loss,
         dropped share and the per-expert token shares."""
         st = {k: v.cpu() for k, v in self.out.stats.items()}
+        if self.shape.gating == EXPERT_CHOICE:
+            # balanced by construction: every expert takes C tokens; the share
+            # dropped is that of the tokens no expert took
+            counts = [int(v) for v in st["counts"]]
+            tot = max(sum(counts), 1)
+            dist = [c / tot for c in counts]
+            return {"aux_loss": None, "z_loss": float(st["z_loss"][0]),
+                    "dropped_share": int(st["n_dropped"][0]) / max(self.shape.T, 1),
+                    "distribution": dist, "counts": counts, "kept": [int(v) for v in st["kept"]],
+                    "entropy": routing_entropy(dist)}
         tk = self.shape.T * self.shape.top_k
         return {"aux_loss": float(st["l_aux"][0]), "z_loss": float(st["z_loss"][0]),
                 "dropped_share": int(st["n_dropped"][0]) / max(tk, 1),

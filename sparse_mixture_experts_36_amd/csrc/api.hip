@@ -29,8 +29,18 @@ int act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Rows reserved for routed experts: every kept pair has one row.
+bool is_ec(const moe_shape& s) { return s.gating == MOE_GATE_EXPERT_CHOICE; }
+
+// Entries per token of inv_map (and of topk_idx / topk_w under token choice).
+int64_t slots(const moe_shape& s) { return is_ec(s) ? s.n_experts : s.top_k; }
+
+// Row pitch of the column-major logit copy of expert choice (16-byte rows).
+int64_t ec_ld(const moe_shape& s) { return (s.T + 3) / 4 * 4; }
+
+// Rows reserved for routed experts: every kept pair has one row (expert
+// choice: exactly C per expert).
 int64_t routed_row_cap(const moe_shape& s) {
+  if (is_ec(s)) return static_cast<int64_t>(s.n_experts) * s.capacity;
   const int64_t tk = s.T * s.top_k;
   if (s.capacity < 0) return tk;
   const int64_t nc = static_cast<int64_t>(s.n_experts) * s.capacity;
@@ -43,7 +53,9 @@ moe_status check_shape(const moe_shape* s) {
       s->n_shared < 0 || s->capacity < -1)
     return MOE_ERR_INVALID_ARG;
   if (s->act != MOE_ACT_GELU && s->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  if (s->gating < MOE_GATE_SOFTMAX_TOPK || s->gating > MOE_GATE_TOPK_SOFTMAX) return MOE_ERR_INVALID_ARG;
+  if (s->gating < MOE_GATE_SOFTMAX_TOPK || s->gating > MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
+  if (s->gating == MOE_GATE_EXPERT_CHOICE && (s->top_k != 1 || s->capacity < 0 || s->capacity > s->T))
+    return MOE_ERR_INVALID_ARG;
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (s->n_experts > kMaxExperts || s->top_k > kMaxTopK || s->n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
@@ -53,7 +65,9 @@ moe_status check_shape(const moe_shape* s) {
   if (s->w_dtype != s->act_dtype && !(s->w_dtype == MOE_FP8_E4M3 && s->act_dtype == MOE_BF16))
     return MOE_ERR_UNSUPPORTED;
   if (s->T > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
-  const int64_t rows = s->T * s->top_k + static_cast<int64_t>(s->n_shared) * s->T;
+  if (s->gating == MOE_GATE_EXPERT_CHOICE && s->T > moe::kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = (s->gating == MOE_GATE_EXPERT_CHOICE ? s->n_experts * s->capacity : s->T * s->top_k) +
+                       static_cast<int64_t>(s->n_shared) * s->T;
   const int64_t wmax = s->d > s->d_ff ? s->d : s->d_ff;
   if (rows * wmax >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -76,6 +90,7 @@ struct RouteWs {
   int32_t* part_cnt;
   float* part_lse;
   float* part_logits;
+  float* logits_t;  // expert choice: [N][ec_ld]
 };
 RouteWs carve_route(Carver& c, const moe_shape& s) {
   const size_t nb = static_cast<size_t>(moe::ceil_div(s.T, moe::kRouteTokens));
@@ -84,11 +99,12 @@ RouteWs carve_route(Carver& c, const moe_shape& s) {
   w.part_cnt = c.take<int32_t>(nb * s.n_experts);
   w.part_lse = c.take<float>(2 * nb);
   w.part_logits = c.take<float>(static_cast<size_t>(moe::route_splits(s.T, s.d)) * s.T * s.n_experts);
+  w.logits_t = is_ec(s) ? c.take<float>(static_cast<size_t>(s.n_experts) * ec_ld(s)) : nullptr;
   return w;
 }
 
 struct PermWs {
-  int32_t *block_cnt, *block_base, *local_rank, *kept, *n_dropped;
+  int32_t *block_cnt, *block_base, *local_rank, *kept, *n_dropped, *ec_part;
 };
 PermWs carve_perm(Carver& c, const moe_shape& s) {
   const size_t nb = static_cast<size_t>(moe::ceil_div(s.T, moe::kPermTokens));
@@ -98,6 +114,7 @@ PermWs carve_perm(Carver& c, const moe_shape& s) {
   w.local_rank = c.take<int32_t>(static_cast<size_t>(s.T) * s.top_k);
   w.kept = c.take<int32_t>(s.n_experts);
   w.n_dropped = c.take<int32_t>(1);
+  w.ec_part = is_ec(s) ? c.take<int32_t>(static_cast<size_t>(moe::ceil_div(s.T, 4))) : nullptr;
   return w;
 }
 
@@ -145,16 +162,17 @@ bool fwd_gathers(const moe_shape& s) {
 }
 
 FwdWs carve_fwd(Carver& c, const moe_shape& s) {
-  const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(s.top_k);
+  const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(slots(s));
   const size_t cap = static_cast<size_t>(routed_row_cap(s));
   const size_t rowb = static_cast<size_t>(s.d) * act_bytes(s.act_dtype);
+  const size_t sel = is_ec(s) ? cap : T * k;  // topk_idx / topk_w entries
   FwdWs w;
   w.logits = c.take<float>(T * s.n_experts);
-  w.topk_idx = c.take<int32_t>(T * k);
-  w.topk_w = c.take<float>(T * k);
+  w.topk_idx = c.take<int32_t>(sel);
+  w.topk_w = c.take<float>(sel);
   w.inv_map = c.take<int32_t>(T * k);
   w.offsets = c.take<int32_t>(s.n_experts + 1);
-  w.perm_token = c.take<int32_t>(T * k);
+  w.perm_token = c.take<int32_t>(is_ec(s) ? cap : T * k);
   w.x_perm = nullptr;
   if (!fwd_gathers(s)) w.x_perm = c.take<char>(cap * static_cast<size_t>(s.d + moe::kActPad) * act_bytes(s.act_dtype));
   w.y_perm = c.take<char>(cap * rowb);
@@ -211,6 +229,10 @@ moe::RouteArgs route_args(const moe_shape& s, const void* x, const void* w_route
   a.part_cnt = w.part_cnt;
   a.part_lse = w.part_lse;
   a.part_logits = w.part_logits;
+  a.ec = is_ec(s);
+  a.cap = s.capacity;
+  a.logits_t = w.logits_t;
+  a.ld_lt = ec_ld(s);
   if (st) {
     a.counts = st->counts;
     a.f = st->f;
@@ -246,6 +268,9 @@ moe::PermuteArgs perm_args(const moe_shape& s, const int32_t* topk_idx, const vo
   a.block_cnt = w.block_cnt;
   a.block_base = w.block_base;
   a.local_rank = w.local_rank;
+  a.ec = is_ec(s);
+  a.ec_part = w.ec_part;
+  if (a.ec) a.n_dropped = (st && st->n_dropped) ? st->n_dropped : nullptr;
   return a;
 }
 
@@ -426,7 +451,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
   if (st != MOE_OK) return st;
   const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
   if ((flags & ~MOE_ROUTE_LOGITS_GIVEN) != 0) return MOE_ERR_INVALID_ARG;
-  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  const bool no_sel = is_ec(*shape) && shape->capacity == 0;  // expert choice with C = 0: empty lists
+  if (!logits || (!no_sel && (!topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
   if (!given && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(*shape, MOE_ENTRY_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -440,7 +466,8 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, const vo
                        size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!topk_idx || !expert_offsets || !perm_token || !inv_map) return MOE_ERR_INVALID_ARG;
+  const bool no_sel = is_ec(*shape) && shape->capacity == 0;  // expert choice with C = 0: no rows
+  if (!expert_offsets || !inv_map || (!no_sel && (!topk_idx || !perm_token))) return MOE_ERR_INVALID_ARG;
   if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(*shape, MOE_ENTRY_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -471,12 +498,15 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
                        const void* y_shared, void* y, hipStream_t stream) {
   const moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!y_perm || !inv_map || !topk_w || !y || !aligned16(y_perm) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const bool no_rows = is_ec(*shape) && shape->capacity == 0;  // expert choice with C = 0
+  if (!inv_map || !y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!no_rows && (!y_perm || !topk_w || !aligned16(y_perm))) return MOE_ERR_INVALID_ARG;
   if (y_shared && !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
   moe::CombineArgs a{};
   a.T = shape->T;
   a.d = shape->d;
-  a.k = shape->top_k;
+  a.k = static_cast<int32_t>(slots(*shape));
+  a.ec = is_ec(*shape);
   a.n_shared = shape->n_shared;
   a.act_dtype = shape->act_dtype;
   a.y_perm = y_perm;
@@ -516,12 +546,12 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
   moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
                                   ld_xp, stats, pw);
-  if (gather) {
-    fa.gather = perm_token;
-    if (s.T <= moe::kPermTokens) {  // the one-block permutation also writes the FFN's group plan
-      pa.plan = moe::ffn_plan(fa);
-      fa.planned = true;
-    }
+  if (gather) fa.gather = perm_token;
+  // the one-block permutation, and expert choice's (whose offsets are fixed),
+  // also write the FFN's group plan
+  if (is_ec(s) || (gather && s.T <= moe::kPermTokens)) {
+    pa.plan = moe::ffn_plan(fa);
+    fa.planned = true;
   }
   if (e == hipSuccess) e = moe::launch_permute(pa, stream);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);
@@ -529,7 +559,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
     moe::CombineArgs a{};
     a.T = s.T;
     a.d = s.d;
-    a.k = s.top_k;
+    a.k = static_cast<int32_t>(slots(s));
+    a.ec = is_ec(s);
     a.n_shared = s.n_shared;
     a.act_dtype = s.act_dtype;
     a.y_perm = w.y_perm;

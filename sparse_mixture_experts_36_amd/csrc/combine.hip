@@ -93,12 +93,119 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Expert choice: a token has a row for every expert that took it (any number,
+// none included). inv_map is [T][N]; the gates are indexed by row. The
+// workgroup first lists the token's rows in expert order in LDS, then sums
+// them eight at a time (loads of a group in flight together), then the shared
+// experts: the same fixed order on every run.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void combine_ec_kernel(CombineArgs a) {
+  __shared__ int32_t s_row[kThreads];
+  __shared__ float s_g[kThreads];
+  __shared__ int32_t s_wc[kThreads / 64];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.k;
+  int32_t row = -1;
+  if (tid < N) row = a.inv_map[t * N + tid];
+  const uint64_t bal = __ballot(row >= 0);
+  if (lane == 0) s_wc[wave] = __popcll(bal);
+  __syncthreads();
+  int base = 0, n = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    if (w < wave) base += s_wc[w];
+    n += s_wc[w];
+  }
+  if (row >= 0) {
+    const int i = base + __popcll(bal & ((uint64_t{1} << lane) - 1));
+    s_row[i] = row;
+    s_g[i] = a.topk_w[row];
+  }
+  __syncthreads();
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr int U = 2;
+  constexpr int G = 8;
+  const int64_t nch = a.d / E;
+  const int nsh = a.y_shared ? a.n_shared : 0;
+  for (int64_t c0 = tid; c0 < nch; c0 += U * kThreads) {
+    float acc[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[u][e] = 0.f;
+    auto add = [&](float (&ac)[E], const uint4& x, float w) {
+      if constexpr (BF16) {
+        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ac[2 * e] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xFFFFu)), ac[2 * e]);
+          ac[2 * e + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)), ac[2 * e + 1]);
+        }
+      } else {
+        ac[0] = fmaf(w, __uint_as_float(x.x), ac[0]);
+        ac[1] = fmaf(w, __uint_as_float(x.y), ac[1]);
+        ac[2] = fmaf(w, __uint_as_float(x.z), ac[2]);
+        ac[3] = fmaf(w, __uint_as_float(x.w), ac[3]);
+      }
+    };
+    for (int j0 = 0; j0 < n; j0 += G) {
+      uint4 v[U][G];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kThreads;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (c < nch && j0 + j < n) v[u][j] = reinterpret_cast<const uint4*>(a.y_perm)[s_row[j0 + j] * nch + c];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kThreads;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (c < nch && j0 + j < n) add(acc[u], v[u][j], s_g[j0 + j]);
+      }
+    }
+    uint4 vs[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (c < nch && s < nsh) vs[u][s] = reinterpret_cast<const uint4*>(a.y_shared)[(s * a.T + t) * nch + c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nch) break;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < nsh) add(acc[u], vs[u][s], 1.0f);
+      uint4 o;
+      if constexpr (BF16) {
+        o = make_uint4(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                       pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7]));
+      } else {
+        o = make_uint4(__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]), __float_as_uint(acc[u][2]),
+                       __float_as_uint(acc[u][3]));
+      }
+      reinterpret_cast<uint4*>(a.y)[t * nch + c] = o;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   stage_mark(kStageCombine, false, s);
-  if (a.act_dtype == 1)
+  if (a.ec) {
+    if (a.k > kThreads) return hipErrorInvalidValue;
+    if (a.act_dtype == 1)
+      hipLaunchKernelGGL(combine_ec_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(combine_ec_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+  } else if (a.act_dtype == 1)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);

@@ -8,6 +8,9 @@ namespace moe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
+// 16-byte chunk as a vector type: arrays of it stay in registers where arrays
+// of the uint4 struct can be left in scratch memory.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 

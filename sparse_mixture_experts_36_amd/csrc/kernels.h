@@ -27,12 +27,20 @@ struct RouteArgs {
   int32_t* part_cnt;        // [nb][N]
   float* part_lse;          // [nb][2]
   float* part_logits;       // [splits][T][N] k-split partial logits (workspace)
+  // expert choice (gating 3): topk_idx / topk_w are then [N][cap], the tokens
+  // each expert takes (ascending) and their gates; logits_t [N][ld_lt] is the
+  // column-major copy of the logits the per-expert selection reads (workspace)
+  bool ec;
+  int64_t cap;
+  float* logits_t;
+  int64_t ld_lt;
   // statistics outputs (any may be null)
   int32_t* counts;
   float *f, *P, *l_aux, *z_loss, *lse_mean, *lse_sq_mean;
   float aux_alpha;
 };
 constexpr int kRouteTokens = 64;  // tokens per route workgroup
+constexpr int64_t kEcMaxTokens = 32768;  // expert choice: a column is held by one workgroup's registers
 constexpr int kMaxRouteSplits = 16;  // k splits of the router GEMM (partial logit planes)
 int route_splits(int64_t T, int64_t d);  // k splits of the router GEMM
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
@@ -76,6 +84,11 @@ struct PermuteArgs {
   // with x_perm null and one workgroup (T <= kPermTokens): also write the FFN
   // group plan from the offsets (null plan.up: no plan)
   FfnPlan plan;
+  // expert choice: topk_idx is [N][capacity], the tokens each expert takes in
+  // ascending order; inv_map is [T][N]; n_dropped counts the tokens no expert
+  // took (from per-block counts in ec_part, [ceil(T / 4)] ints of workspace)
+  bool ec;
+  int32_t* ec_part;
 };
 constexpr int kPermTokens = 256;  // tokens per permute workgroup
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
@@ -140,6 +153,7 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
 struct CombineArgs {
   int64_t T, d;
   int32_t k, n_shared, act_dtype;
+  bool ec;                    // expert choice: k = N slots per token, topk_w indexed by row
   const void* y_perm;
   const int32_t* inv_map;
   const float* topk_w;

@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
   // below, so the two latencies overlap
   constexpr int U = 8;
   const int64_t nchunk = a.x_perm ? a.d * a.act_bytes / 16 : 0;
-  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
-  uint4 v[U];
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.x) + t * a.d * a.act_bytes);
+  u32x4_t v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = u * 64 + lane;
@@ -283,8 +283,14 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
     }
   }
   if (!a.x_perm) return;
+  // lane j keeps slot j's row, read back one slot at a time: a loop over the
+  // slots then needs no per-slot registers for addresses
+  int32_t rowv = -1;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (lane == j) rowv = static_cast<int32_t>(row[j]);
   const int64_t ochunk = a.ld_out * a.act_bytes / 16;  // 16-byte chunks per x_perm row
-  uint4* dst = reinterpret_cast<uint4*>(a.x_perm);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x_perm);
   for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
     if (c0 > 0) {
 #pragma unroll
@@ -293,21 +299,134 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
         if (c < nchunk) v[u] = src[c];
       }
     }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k || row[j] < 0) continue;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = __builtin_amdgcn_readlane(rowv, j);
+      if (r < 0) continue;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t c = c0 + u * 64 + lane;
-        if (c < nchunk) dst[row[j] * ochunk + c] = v[u];
+        if (c < nchunk) dst[static_cast<int64_t>(r) * ochunk + c] = v[u];
       }
     }
+  }
+}
+
+// Expert choice: expert e's j-th token sits in row e*C + j, so the offsets are
+// e*C. One wave per token finds, for every expert (a lane each), the token in
+// that expert's ascending list by binary search; it writes inv_map[t][e] and
+// perm_token, lists its rows in expert order, and copies the token's row (read
+// once) into each of them. Block 0 writes the offsets (and the FFN group plan
+// when asked). Tokens taken by no expert are counted per block.
+__global__ __launch_bounds__(kThreads) void ec_permute_kernel(PermuteArgs a) {
+  __shared__ int32_t s_off[kMaxN + 1];
+  __shared__ int32_t s_mt[kMaxGroups];
+  __shared__ int32_t s_none[4];
+  __shared__ int32_t s_rows[4][kMaxN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N;
+  const int32_t C = static_cast<int32_t>(a.capacity);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= N; e += kThreads) {
+      a.offsets[e] = e * C;
+      s_off[e] = e * C;
+      if (e < N && a.kept) a.kept[e] = C;
+    }
+    if (a.plan.up) {
+      __syncthreads();
+      plan_groups(s_off, a.plan, s_mt, tid, kThreads);
+    }
+  }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool live = t < a.T;
+  constexpr int U = 8;
+  const int64_t nchunk = (a.x_perm && live) ? a.d * a.act_bytes / 16 : 0;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.x) + (live ? t : 0) * a.d * a.act_bytes);
+  // the token's first 64*U chunks are loaded before the searches, so the two
+  // latencies overlap
+  u32x4_t v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = u * 64 + lane;
+    if (c < nchunk) v[u] = src[c];
+  }
+  int nrows = 0;  // rows of this token, listed in s_rows[wave] in expert order
+  for (int e0 = 0; e0 < N; e0 += 64) {
+    const int e = e0 + lane;
+    int32_t row = -1;
+    if (live && e < N) {
+      if (C > 0) {
+        const int32_t* list = a.topk_idx + static_cast<int64_t>(e) * C;
+        int lo = 0, hi = C;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (list[mid] < t) lo = mid + 1;
+          else hi = mid;
+        }
+        if (lo < C && list[lo] == t) row = e * C + lo;
+      }
+      a.inv_map[t * N + e] = row;
+      if (row >= 0) a.perm_token[row] = static_cast<int32_t>(t);
+    }
+    const uint64_t found = __ballot(row >= 0);
+    if (row >= 0) s_rows[wave][nrows + __popcll(found & ((uint64_t{1} << lane) - 1))] = row;
+    nrows += __popcll(found);
+  }
+  __syncthreads();
+  const int64_t ochunk = a.ld_out * a.act_bytes / 16;
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x_perm);
+  for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nchunk) v[u] = src[c];
+      }
+    }
+    for (int j = 0; j < nrows; ++j) {
+      const int64_t r = s_rows[wave][j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nchunk) dst[r * ochunk + c] = v[u];
+      }
+    }
+  }
+  const bool taken = nrows > 0;
+  if (a.n_dropped) {
+    if (lane == 0) s_none[wave] = (live && !taken) ? 1 : 0;
+    __syncthreads();
+    if (tid == 0) a.ec_part[blockIdx.x] = s_none[0] + s_none[1] + s_none[2] + s_none[3];
+  }
+}
+
+// Sum of the per-block counts of tokens no expert took.
+__global__ __launch_bounds__(1024) void ec_untouched_kernel(PermuteArgs a, int nb) {
+  __shared__ int32_t s_w[16];
+  int32_t c = 0;
+  for (int b = threadIdx.x; b < nb; b += 1024) c += a.ec_part[b];
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t tot = 0;
+    for (int w = 0; w < 16; ++w) tot += s_w[w];
+    *a.n_dropped = tot;
   }
 }
 
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.ec) {
+    if (a.T <= 0) return hipSuccess;
+    const int nb = static_cast<int>(ceil_div(a.T, 4));
+    stage_mark(kStagePermute, false, s);
+    hipLaunchKernelGGL(ec_permute_kernel, dim3(nb), dim3(kThreads), 0, s, a);
+    if (a.n_dropped) hipLaunchKernelGGL(ec_untouched_kernel, dim3(1), dim3(1024), 0, s, a, nb);
+    stage_mark(kStagePermute, true, s);
+    return hipGetLastError();
+  }
   if (a.T <= 0) {
     // no tokens: the scan over zero blocks writes the empty layout
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a, 0);

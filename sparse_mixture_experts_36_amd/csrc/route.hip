@@ -161,12 +161,49 @@ __device__ __forceinline__ void finalize_scalars(const RouteArgs& a, const doubl
                                                  double lse_sq_sum) {
   const double T = static_cast<double>(a.T);
   double dot = 0.0;
-  for (int e = 0; e < a.N; ++e) dot += s_fp[e];
+  if (!a.ec)
+    for (int e = 0; e < a.N; ++e) dot += s_fp[e];
   const double lm = lse_sum / T;
-  if (a.l_aux) *a.l_aux = static_cast<float>(static_cast<double>(a.aux_alpha) * a.N * dot);
+  if (a.l_aux && !a.ec) *a.l_aux = static_cast<float>(static_cast<double>(a.aux_alpha) * a.N * dot);
   if (a.z_loss) *a.z_loss = static_cast<float>(lm * lm);
   if (a.lse_mean) *a.lse_mean = static_cast<float>(lm);
   if (a.lse_sq_mean) *a.lse_sq_mean = static_cast<float>(lse_sq_sum / T);
+}
+
+// Logits of token t for experts 16 nt + c16: the given ones, or the sum of
+// the k-split partial logits (in split order) plus the router bias, which is
+// then also stored as the router output (and, for expert choice, into the
+// column-major copy).
+template <int NT>
+__device__ __forceinline__ void token_logits(const RouteArgs& a, const float* part, int splits, int64_t t,
+                                             bool live, int c16, float (&lg)[NT]) {
+  const int N = a.N;
+  const int64_t T = a.T;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = 16 * nt + c16;
+    float v = 0.f;
+    if (live && e < N) {
+      if (a.logits_given) {
+        v = a.logits[t * N + e];
+      } else {
+        // all split partials are loaded before the first add (one round
+        // trip, not one per split), then summed in split order
+        float pv[kMaxRouteSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxRouteSplits; ++sp)
+          if (sp < splits) pv[sp] = part[(static_cast<int64_t>(sp) * T + t) * N + e];
+        v = pv[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxRouteSplits; ++sp)
+          if (sp < splits) v += pv[sp];
+        if (a.b_router) v += a.b_router[e];
+        a.logits[t * N + e] = v;
+      }
+      if (a.ec) a.logits_t[e * a.ld_lt + t] = v;
+    }
+    lg[nt] = v;
+  }
 }
 
 // Softmax / top-k / gates / block statistics over 64 tokens, one per
@@ -196,30 +233,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a, const
   for (int e = tid; e < kMaxN; e += kRouteThreads) s_cnt[e] = 0;
 
   float lg[NT];  // logit of expert 16 nt + c16
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = 16 * nt + c16;
-    float v = 0.f;
-    if (live && e < N) {
-      if (a.logits_given) {
-        v = a.logits[t * N + e];
-      } else {
-        // all split partials are loaded before the first add (one round
-        // trip, not one per split), then summed in split order
-        float pv[kMaxRouteSplits];
-#pragma unroll
-        for (int sp = 0; sp < kMaxRouteSplits; ++sp)
-          if (sp < splits) pv[sp] = part[(static_cast<int64_t>(sp) * T + t) * N + e];
-        v = pv[0];
-#pragma unroll
-        for (int sp = 1; sp < kMaxRouteSplits; ++sp)
-          if (sp < splits) v += pv[sp];
-        if (a.b_router) v += a.b_router[e];
-        a.logits[t * N + e] = v;
-      }
-    }
-    lg[nt] = v;
-  }
+  token_logits<NT>(a, part, splits, t, live, c16, lg);
   __syncthreads();  // s_cnt cleared before any count below
 
   // selection: k rounds of a 16-lane arg-max under `better`
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a
   // at least one full batch of loads per segment
   const int S = min(kFinThreads / NP, max(1, (nb + kFinBatch - 1) / kFinBatch));
   const int e = tid % NP, seg = tid / NP;
-  if (e < N && seg < S) {
+  if (!a.ec && e < N && seg < S) {
     const int b0 = static_cast<int>((static_cast<int64_t>(seg) * nb) / S);
     const int b1 = static_cast<int>((static_cast<int64_t>(seg + 1) * nb) / S);
     double p = 0.0;
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a
     s_lse[1][tid] = lq;
   }
   __syncthreads();
-  if (tid < N) {
+  if (!a.ec && tid < N) {
     double p = 0.0;
     int64_t c = 0;
     for (int sg = 0; sg < S; ++sg) {
@@ -427,6 +441,258 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a
   }
 }
 
+// ---------------------------------------------------------------- expert choice
+// vanos001 "MoE Architecture" / "Router Design", Expert-Choice Router: the
+// softmax runs over the tokens of each expert's column and every expert takes
+// the C tokens of largest probability. Ranking by that probability is ranking
+// by the logit (the column softmax is strictly increasing), so the selection
+// compares fp32 logits; exact ties go to the lower token index.
+
+// Per-token pass: logits (and their column-major copy), the logsumexp over the
+// experts for the z statistics; no per-token selection.
+template <int NT>
+__global__ __launch_bounds__(kRouteThreads) void route_ec_kernel(RouteArgs a, const float* part, int splits) {
+  __shared__ float s_lse[kRouteWaves][2];
+  __shared__ double s_fp[1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int N = a.N;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 4 + q;
+  const bool live = t < a.T;
+  float lg[NT];
+  token_logits<NT>(a, part, splits, t, live, c16, lg);
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    if (16 * nt + c16 < N) m = fmaxf(m, lg[nt]);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+  float s = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    if (16 * nt + c16 < N) s += expf(lg[nt] - m);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  const float lse = m + logf(s);
+  const float lse_s = live ? lse : 0.f, lse_sq = live ? lse * lse : 0.f;
+  {
+    const float a1 = __shfl(lse_s, 0) + __shfl(lse_s, 16) + __shfl(lse_s, 32) + __shfl(lse_s, 48);
+    const float a2 = __shfl(lse_sq, 0) + __shfl(lse_sq, 16) + __shfl(lse_sq, 32) + __shfl(lse_sq, 48);
+    if (lane == 0) {
+      s_lse[wave][0] = a1;
+      s_lse[wave][1] = a2;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float l1 = s_lse[0][0], l2 = s_lse[0][1];
+    for (int w = 1; w < kRouteWaves; ++w) {
+      l1 += s_lse[w][0];
+      l2 += s_lse[w][1];
+    }
+    if (gridDim.x == 1) {
+      finalize_scalars(a, s_fp, static_cast<double>(l1), static_cast<double>(l2));
+    } else {
+      a.part_lse[2 * blockIdx.x] = l1;
+      a.part_lse[2 * blockIdx.x + 1] = l2;
+    }
+  }
+}
+
+constexpr int kEcThreads = 1024;
+constexpr int kEcWaves = kEcThreads / 64;
+
+// Order-preserving key of an fp32 value (larger value, larger key); -0 and +0
+// share one key, as they compare equal.
+__device__ __forceinline__ uint32_t ec_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The fp32 value of a key (-0 comes back as +0).
+__device__ __forceinline__ float ec_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Exclusive prefix sum over the workgroup in thread order; `total` gets the
+// sum of all. s_w holds one value per wave.
+__device__ __forceinline__ uint32_t ec_scan(uint32_t v, uint32_t* s_w, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kEcWaves; ++w) {
+    const uint32_t c = s_w[w];
+    if (w < wave) base += c;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// One workgroup per expert e; thread i holds tokens [CH i, CH i + CH) of the
+// column (T <= 1024 CH). Column softmax: max, then the sum of exp (fp64,
+// fixed order). Selection: a most-significant-digit radix select (4 passes of
+// 8 bits over the order-preserving keys, per-wave histograms) finds the C-th
+// largest key K and how many keys equal to K are taken; the tokens above K and
+// the first of those equal to K in token order are kept. Two prefix sums in
+// token order give each kept token its row e*C + j, so the list comes out in
+// ascending token order. Every order is fixed: the output is reproducible.
+template <int CH>
+__global__ __launch_bounds__(kEcThreads) void ec_select_kernel(RouteArgs a) {
+  __shared__ uint32_t s_hist[kEcWaves][256];
+  __shared__ uint32_t s_w[kEcWaves];
+  __shared__ float s_m[kEcWaves];
+  __shared__ double s_s[kEcWaves];
+  __shared__ uint32_t s_pick[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  const int64_t T = a.T;
+  const int C = static_cast<int>(a.cap);
+  if (tid == 0 && a.counts) a.counts[e] = C;
+  if (C == 0) return;
+  const float* col = a.logits_t + static_cast<int64_t>(e) * a.ld_lt;
+  const int t0 = tid * CH;
+  uint32_t key[CH];  // the values are kept only as their keys (a bijection)
+#pragma unroll
+  for (int j = 0; j < CH; j += 4) {
+    float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t0 + j < T) q = *reinterpret_cast<const float4*>(col + t0 + j);  // ld_lt: a multiple of 4 >= T
+    key[j] = ec_key(q.x);
+    key[j + 1] = ec_key(q.y);
+    key[j + 2] = ec_key(q.z);
+    key[j + 3] = ec_key(q.w);
+  }
+  int nv = static_cast<int>(T) - t0;  // valid tokens of this thread
+  nv = nv < 0 ? 0 : (nv > CH ? CH : nv);
+
+  // column softmax denominators
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    if (i < nv) m = fmaxf(m, ec_value(key[i]));
+  m = wave_max(m);
+  if (lane == 0) s_m[wave] = m;
+  __syncthreads();
+  m = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kEcWaves; ++w) m = fmaxf(m, s_m[w]);
+  double S = 0.0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    if (i < nv) S += static_cast<double>(expf(ec_value(key[i]) - m));
+  S = wave_sum(S);
+  if (lane == 0) s_s[wave] = S;
+
+  // radix select of the C-th largest key
+  uint32_t prefix = 0, pmask = 0, rem = static_cast<uint32_t>(C);
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < kEcWaves * 256; i += kEcThreads) (&s_hist[0][0])[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (i < nv && (key[i] & pmask) == prefix) atomicAdd(&s_hist[wave][(key[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 255 - 4l - j, j < 4: lanes in ascending order walk the bins downward
+      uint32_t c[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = 255 - 4 * lane - j;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kEcWaves; ++w) sum += s_hist[w][b];
+        c[j] = sum;
+        loc += sum;
+      }
+      uint32_t inc = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const uint32_t exc = inc - loc;
+      if (exc < rem && rem <= inc) {
+        uint32_t acc = exc;
+        int pick = 0;
+        uint32_t left = 0;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!found && acc + c[j] >= rem) {
+            pick = 255 - 4 * lane - j;
+            left = rem - acc;
+            found = true;
+          }
+          acc += c[j];
+        }
+        s_pick[0] = static_cast<uint32_t>(pick);
+        s_pick[1] = left;
+      }
+    }
+    __syncthreads();
+    prefix |= s_pick[0] << shift;
+    pmask |= 0xFFu << shift;
+    rem = s_pick[1];
+  }
+  // prefix = K, rem = how many keys equal to K are taken (lowest tokens first)
+  S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kEcWaves; ++w) S += s_s[w];
+
+  uint32_t neq = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    if (i < nv && key[i] == prefix) ++neq;
+  uint32_t total;
+  uint32_t eqr = ec_scan(neq, s_w, total);
+  uint32_t sel = 0, nsel = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    bool take = false;
+    if (i < nv) {
+      if (key[i] > prefix) {
+        take = true;
+      } else if (key[i] == prefix) {
+        take = eqr < rem;
+        ++eqr;
+      }
+    }
+    if (take) {
+      sel |= 1u << i;
+      ++nsel;
+    }
+  }
+  uint32_t pos = ec_scan(nsel, s_w, total);
+  int32_t* tok = a.topk_idx + static_cast<int64_t>(e) * C;
+  float* gate = a.topk_w + static_cast<int64_t>(e) * C;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if ((sel >> i & 1u) && pos < static_cast<uint32_t>(C)) {
+      tok[pos] = t0 + i;
+      gate[pos] = static_cast<float>(static_cast<double>(expf(ec_value(key[i]) - m)) / S);
+      ++pos;
+    }
+  }
+}
+
+template <int CH>
+hipError_t launch_ec_select(const RouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(ec_select_kernel<CH>, dim3(a.N), dim3(kEcThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
   if (!a.logits_given) {
@@ -435,7 +701,10 @@ hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kRouteThreads), 0, s, a, a.part_logits, splits);
+  if (a.ec)
+    hipLaunchKernelGGL(route_ec_kernel<NT>, dim3(nb), dim3(kRouteThreads), 0, s, a, a.part_logits, splits);
+  else
+    hipLaunchKernelGGL(route_kernel<NT>, dim3(nb), dim3(kRouteThreads), 0, s, a, a.part_logits, splits);
   return hipGetLastError();
 }
 
@@ -467,6 +736,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   if (err != hipSuccess) return err;
   if (nb > 1) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, a, nb);
+  if (a.ec) {
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (a.T > kEcMaxTokens) return hipErrorInvalidValue;
+    if (a.T <= 4 * kEcThreads) err = launch_ec_select<4>(a, s);
+    else if (a.T <= 8 * kEcThreads) err = launch_ec_select<8>(a, s);
+    else if (a.T <= 16 * kEcThreads) err = launch_ec_select<16>(a, s);
+    else err = launch_ec_select<32>(a, s);
+    if (err != hipSuccess) return err;
+  }
   stage_mark(kStageRoute, true, s);
   return hipGetLastError();
 }

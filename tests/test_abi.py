@@ -54,7 +54,14 @@ def _shape(**kw):
     (dict(d=200), moe.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=192), moe.MOE_ERR_UNSUPPORTED),
     (dict(act=5), moe.MOE_ERR_INVALID_ARG),
-    (dict(gating=3), moe.MOE_ERR_INVALID_ARG),
+    (dict(gating=4), moe.MOE_ERR_INVALID_ARG),
+    # expert choice: top_k 1 and 0 <= C <= T; at most 32768 tokens
+    (dict(gating=moe.EXPERT_CHOICE, top_k=2, capacity=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(gating=moe.EXPERT_CHOICE, top_k=1, capacity=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(gating=moe.EXPERT_CHOICE, top_k=1, capacity=65), moe.MOE_ERR_INVALID_ARG),
+    (dict(gating=moe.EXPERT_CHOICE, top_k=1, T=32769, capacity=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(gating=moe.EXPERT_CHOICE, top_k=1, T=32768, d=65536, n_experts=256, capacity=32768),
+     moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=moe.FP8_E4M3), moe.MOE_ERR_INVALID_ARG),
     (dict(act_dtype=moe.F32, w_dtype=moe.BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=moe.F32, w_dtype=moe.FP8_E4M3), moe.MOE_ERR_UNSUPPORTED),
@@ -67,6 +74,22 @@ def _shape(**kw):
 def test_invalid_shapes_rejected(kw, status):
     n = ctypes.c_size_t()
     assert moe.lib().moe_workspace_size(ctypes.byref(_shape(**kw)), moe.ENTRY_FORWARD, ctypes.byref(n)) == status
+
+
+@pytest.mark.parametrize("T,C", [(64, 0), (64, 16), (64, 64), (32768, 8192)])
+def test_expert_choice_shapes_accepted(T, C):
+    s = _shape(T=T, top_k=1, gating=moe.EXPERT_CHOICE, capacity=C)
+    sizes = [moe.workspace_size(s, e) for e in range(4)]
+    # forward holds h and y_perm for the N*C routed rows
+    assert sizes[3] >= 8 * C * (512 + 256) * 2
+    rs = moe.routing_shapes(s)
+    assert rs == {"topk": (8, C), "inv_map": (T, 8), "perm_token": (8 * C,)}
+
+
+def test_expert_choice_capacity_is_the_pages_int():
+    # int(num_tokens * capacity_factor / num_experts)
+    for T, N, cf in [(4096, 8, 2.0), (8192, 160, 6.0), (256, 8, 2.0), (10, 3, 1.0), (100, 7, 1.25)]:
+        assert moe.capacity(T, 1, N, cf) == int(T * cf / N)
 
 
 def test_workspace_sizes_grow_with_entry():
