@@ -31,6 +31,7 @@ T_X, T_WR, T_W1, T_W3, T_W2, T_B1, T_B2, T_SW1, T_SW3, T_SW2, T_LOGITS = range(1
 
 # dtype codes shared by convention with every consumer (plain integers)
 F32, BF16, E4M3 = 0, 1, 2
+INT_W = 3  # weight-only integers: 8 or 4 bits per expert, one fp32 scale per weight row
 # activation / gating codes
 GELU, SWIGLU = 0, 1
 SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
@@ -65,6 +66,7 @@ def lib():
         L.gen_grid_f32.argtypes = [u64, u32, u64, u64, dbl, i32, i32, vp]
         L.gen_grid_bf16.argtypes = [u64, u32, u64, u64, dbl, i32, i32, vp]
         L.gen_e4m3_groups.argtypes = [u64, u32, u64, u64, u64, dbl, vp, vp, u64]
+        L.gen_int_rows.argtypes = [u64, u32, u64, u64, u64, dbl, i32, vp, vp, u64]
         L.gen_bf16_of.argtypes = [ctypes.c_float]
         L.gen_bf16_of.restype = ctypes.c_uint16
         L.gen_e4m3_of.argtypes = [dbl]
@@ -72,7 +74,7 @@ def lib():
         L.gen_normal_at.argtypes = [u64, u32, u64]
         L.gen_normal_at.restype = dbl
         for f in (L.gen_normal_f32, L.gen_normal_bf16, L.gen_grid_f32, L.gen_grid_bf16,
-                  L.gen_e4m3_groups):
+                  L.gen_e4m3_groups, L.gen_int_rows):
             f.restype = None
         _lib = L
     return _lib
@@ -128,6 +130,19 @@ def e4m3_groups(tensor: int, n_groups: int, group_shape, scale: float, seed: int
     return q, scales_out[:, scale_col]
 
 
+def int_rows(tensor: int, shape, scale: float, bits: int, seed: int = SEED, offset: int = 0,
+             scales_out: np.ndarray | None = None):
+    """Integer weight rows [rows, cols] (int8 codes within +-(2^(bits-1) - 1),
+    one per byte) and their fp32 row scales: round-half-even(w / s_r) with
+    s_r = amax_r / qmax, w the fp32-rounded draws scale*N(0,1)."""
+    rows, cols = shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32) if scales_out is None else scales_out
+    assert s.dtype == np.float32 and s.flags["C_CONTIGUOUS"] and s.shape == (rows,)
+    lib().gen_int_rows(seed, tensor, offset, rows, cols, scale, (1 << (bits - 1)) - 1, _ptr(q), _ptr(s), 1)
+    return q, s
+
+
 def zipf_bias(n_experts: int, s: float) -> np.ndarray:
     """b_e = -s*ln(e+1): softmax(b) is the Zipf(s) law over experts."""
     return np.array([-s * math.log(e + 1) for e in range(n_experts)], np.float32)
@@ -149,6 +164,11 @@ class Workload:
     n_shared: int = 0
     zipf_s: float | None = None
     aux_alpha: float = 0.01
+    n_int8: int = 0  # INT_W weights: experts 0 .. n_int8-1 take 8 bits, the others 4; shared experts 8
+
+    def expert_bits(self) -> np.ndarray:
+        """Bits per routed expert under INT_W weights (8 for the high-traffic ones)."""
+        return np.array([8 if e < self.n_int8 else 4 for e in range(self.n_experts)], np.uint8)
 
     def capacity(self) -> int:
         """floor(cf*T*k/N) in fp64, or -1 for dropless."""
@@ -179,9 +199,15 @@ MIXTRAL_PREFILL_EC = MIXTRAL_PREFILL.with_(name="mixtral-prefill-ec-bf16", top_k
 FINE_GRAINED_EC = FINE_GRAINED.with_(name="fine-grained-160-ec-shared2-bf16", top_k=1, gating=EXPERT_CHOICE,
                                      capacity_factor=6.0)
 
+# Per-expert integer weights on the Mixtral layer: the two high-traffic experts
+# (0 and 1) in INT8, the other six in INT4, one fp32 scale per weight row.
+MIXTRAL_PREFILL_INT = MIXTRAL_PREFILL.with_(name="mixtral-prefill-int8x2-int4x6", w_dtype=INT_W, n_int8=2)
+MIXTRAL_DECODE_INT = {T: MIXTRAL_PREFILL_INT.with_(name=f"mixtral-decode-int8x2-int4x6-T{T}", T=T)
+                      for T in (1, 16, 64)}
+
 WORKLOADS = {w.name: w for w in [TINY_GELU, MIXTRAL_PREFILL, *MIXTRAL_DECODE.values(), FINE_GRAINED,
                                   SWITCH_TOP1, SWITCH_TOP1_FP8, TINY_GELU_EC, MIXTRAL_PREFILL_EC,
-                                  FINE_GRAINED_EC]}
+                                  FINE_GRAINED_EC, MIXTRAL_PREFILL_INT, *MIXTRAL_DECODE_INT.values()]}
 
 
 @dataclass
@@ -196,19 +222,36 @@ class Inputs:
     w2: np.ndarray
     b1: np.ndarray | None
     b2: np.ndarray | None
-    w_scale: np.ndarray | None       # [N][3] fp32 (W1, W3, W2) for e4m3 weights
+    w_scale: np.ndarray | None       # [N][3] fp32 (W1, W3, W2) for e4m3 weights; [N][2 d_ff + d] row scales for INT_W
     sw1: np.ndarray | None = None
     sw3: np.ndarray | None = None
     sw2: np.ndarray | None = None
     sw_scale: np.ndarray | None = None
+    w_bits: np.ndarray | None = None   # INT_W: [N] uint8, 8 or 4
+    sw_bits: np.ndarray | None = None  # INT_W: [n_shared] uint8 (8)
 
 
-def _weights(wl: Workload, ids, n: int, seed: int):
+def _weights(wl: Workload, ids, n: int, seed: int, bits=None):
     """Stacked expert weights for n experts: (w1, w3, w2, scales)."""
     t1, t3, t2 = ids
     s_in, s_hid = 1.0 / math.sqrt(wl.d), 1.0 / math.sqrt(wl.d_ff)
     shp1, shp2 = (wl.d_ff, wl.d), (wl.d, wl.d_ff)
     swiglu = wl.act == SWIGLU
+    if wl.w_dtype == INT_W:
+        # codes [n][rows][cols] (int8, one per weight) and row scales
+        # [n][2 d_ff + d]: W1 rows, W3 rows (ones for GELU), W2 rows
+        f, d = wl.d_ff, wl.d
+        sc = np.ones((n, 2 * f + d), np.float32)
+        w1 = np.empty((n,) + shp1, np.int8)
+        w3 = np.empty((n,) + shp1, np.int8) if swiglu else None
+        w2 = np.empty((n,) + shp2, np.int8)
+        for e in range(n):
+            b = int(bits[e])
+            w1[e] = int_rows(t1, shp1, s_in, b, seed, e * f * d, sc[e, :f])[0]
+            if swiglu:
+                w3[e] = int_rows(t3, shp1, s_in, b, seed, e * f * d, sc[e, f:2 * f])[0]
+            w2[e] = int_rows(t2, shp2, s_hid, b, seed, e * d * f, sc[e, 2 * f:])[0]
+        return w1, w3, w2, sc
     if wl.w_dtype == E4M3:
         sc = np.ones((n, 3), np.float32)
         w1, _ = e4m3_groups(t1, n, shp1, s_in, seed, sc, 0)
@@ -244,14 +287,17 @@ def make_inputs(wl: Workload, seed: int = SEED, router_grid: bool = False) -> In
         if router_grid:
             q = float(2 ** (4 + p))
             b_router = (np.round(b_router.astype(np.float64) * q) / q).astype(np.float32)
-    w1, w3, w2, sc = _weights(wl, (T_W1, T_W3, T_W2), N, seed)
+    bits = wl.expert_bits() if wl.w_dtype == INT_W else None
+    w1, w3, w2, sc = _weights(wl, (T_W1, T_W3, T_W2), N, seed, bits)
     b1 = b2 = None
     if wl.act == GELU:
         b1 = np.zeros((N, wl.d_ff), np.float32)
         b2 = np.zeros((N, d), np.float32)
-    inp = Inputs(wl, x, wr, b_router, w1, w3, w2, b1, b2, sc)
+    inp = Inputs(wl, x, wr, b_router, w1, w3, w2, b1, b2, sc, w_bits=bits)
     if wl.n_shared:
-        inp.sw1, inp.sw3, inp.sw2, inp.sw_scale = _weights(wl, (T_SW1, T_SW3, T_SW2), wl.n_shared, seed)
+        sbits = np.full(wl.n_shared, 8, np.uint8) if wl.w_dtype == INT_W else None
+        inp.sw1, inp.sw3, inp.sw2, inp.sw_scale = _weights(wl, (T_SW1, T_SW3, T_SW2), wl.n_shared, seed, sbits)
+        inp.sw_bits = sbits
     return inp
 
 

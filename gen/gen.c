@@ -141,6 +141,35 @@ void gen_e4m3_groups(uint64_t seed, uint32_t tensor, uint64_t offset, uint64_t n
   }
 }
 
+/* Weight-only integer rows: row r of `n_rows` rows of `cols` weights (draws
+ * offset + r*cols + j, times `scale`, rounded to fp32 first) gets the fp32
+ * scale s_r = amax_r / qmax (1 for an all-zero row) and the codes
+ * q = round-half-even(w / s_r) clamped to [-qmax, qmax], one int8 per weight.
+ * Scale r is written to s[r * s_stride]. */
+void gen_int_rows(uint64_t seed, uint32_t tensor, uint64_t offset, uint64_t n_rows, uint64_t cols,
+                  double scale, int32_t qmax, int8_t* q, float* s, uint64_t s_stride) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)n_rows; ++r) {
+    const uint64_t base = offset + (uint64_t)r * cols;
+    double amax = 0.0;
+    for (uint64_t j = 0; j < cols; ++j) {
+      double a = fabs((double)(float)(scale * normal_at(seed, tensor, base + j)));
+      if (a > amax) amax = a;
+    }
+    float sr = (float)(amax / (double)qmax);
+    if (sr == 0.0f) sr = 1.0f;
+    s[(uint64_t)r * s_stride] = sr;
+    int8_t* qr = q + (uint64_t)r * cols;
+    for (uint64_t j = 0; j < cols; ++j) {
+      double w = (double)(float)(scale * normal_at(seed, tensor, base + j));
+      double v = nearbyint(w / (double)sr); /* default rounding mode: half to even */
+      if (v > qmax) v = qmax;
+      if (v < -qmax) v = -qmax;
+      qr[j] = (int8_t)v;
+    }
+  }
+}
+
 /* Exposed for the generator's own tests. */
 uint16_t gen_bf16_of(float f) { return f32_to_bf16_rne(f); }
 uint8_t gen_e4m3_of(double v) { return f64_to_e4m3_rne_sat(v); }

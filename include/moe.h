@@ -21,7 +21,8 @@
  * Conventions for every entry point:
  *  - Memory: every pointer argument is DEVICE memory except the moe_shape /
  *    moe_weights / moe_stats structs themselves, which are read on the host
- *    during the call (the pointers inside them are device pointers). The
+ *    during the call (the pointers inside them are device pointers, except
+ *    moe_weights.w_bits / sw_bits, which are host arrays). The
  *    caller allocates and owns every buffer; the library never allocates,
  *    frees or keeps a pointer after returning. Buffers must stay valid until
  *    the work enqueued on `stream` has finished.
@@ -70,7 +71,15 @@ typedef enum {
   MOE_ERR_WORKSPACE = -4    /* ws is null, misaligned or smaller than required */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+/* MOE_INT_W: weight-only integers (starphix "Quantization": INT8 for
+ * high-traffic experts, INT4 for the rest, the router kept in 16 bits). Each
+ * expert has 8 or 4 bits (moe_weights.w_bits) and one fp32 scale per weight
+ * row: W[r][c] = s_r * q[r][c], q symmetric two's complement. Expert matrices
+ * keep byte rows (pitch ld_up / ld_down bytes, at least d / d_ff): an 8-bit
+ * expert's row holds one int8 code per column, a 4-bit expert's row holds two
+ * codes per byte in its first d/2 (d_ff/2) bytes, column 2i in the low nibble
+ * of byte i and column 2i + 1 in the high nibble. Activations stay bf16. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT_W = 3 } moe_dtype;
 
 /* Expert FFN. GELU: y = W2 gelu(W1 x + b1) + b2 with the exact erf GELU
  * (aigrafen "Mixture of Experts", `MoE` module; vanos001 "Expert Network
@@ -110,7 +119,7 @@ typedef struct {
   int32_t gating;     /* moe_gating */
   int32_t act_dtype;  /* moe_dtype of x, W_r, the layer output: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;    /* moe_dtype of expert weights: same as act_dtype, or
-                         MOE_FP8_E4M3 with act_dtype MOE_BF16 */
+                         MOE_FP8_E4M3 or MOE_INT_W with act_dtype MOE_BF16 */
   int64_t capacity;   /* C pairs per expert; -1 = no limit (dropless).
                          Expert choice: C tokens per expert, 0 <= C <= T */
   float aux_alpha;    /* alpha of L_aux (the pages use about 0.01) */
@@ -125,12 +134,15 @@ typedef struct {
   const float* b1;        /* [N][d_ff] fp32 or NULL (GELU only) */
   const float* b2;        /* [N][d] fp32 or NULL (GELU only) */
   const float* w_scale;   /* [N][3] fp32 per-tensor scales of (W1, W3, W2) for
-                             MOE_FP8_E4M3 (W = scale * code), else NULL */
+                             MOE_FP8_E4M3 (W = scale * code); for MOE_INT_W
+                             [N][2 d_ff + d] row scales: W1's d_ff rows, W3's
+                             d_ff rows (unused by GELU), W2's d rows; else NULL */
   const void* sw1;        /* shared experts: [n_shared][d_ff][d] */
   const void* sw3;        /* [n_shared][d_ff][d] (SwiGLU) */
   const void* sw2;        /* [n_shared][d][d_ff] */
-  const float* sw_scale;  /* [n_shared][3] for MOE_FP8_E4M3 */
-  /* Row pitches of the expert matrices, in elements (0 = contiguous rows).
+  const float* sw_scale;  /* [n_shared][3] for MOE_FP8_E4M3, [n_shared][2 d_ff + d] for MOE_INT_W */
+  /* Row pitches of the expert matrices, in elements (MOE_INT_W: bytes; 0 =
+   * contiguous rows: d or d_ff elements, also for 4-bit experts).
    * ld_up applies to w1, w3, sw1, sw3: row j of expert e starts at element
    * (e * d_ff + j) * ld_up, ld_up >= d. ld_down applies to w2 and sw2:
    * (e * d + j) * ld_down, ld_down >= d_ff. Nonzero pitches must be multiples
@@ -139,6 +151,11 @@ typedef struct {
    * of 4096 and is the layout the prefill GEMM runs fastest on. */
   int64_t ld_up;
   int64_t ld_down;
+  /* MOE_INT_W only: bits of each routed / shared expert, 8 or 4. These two are
+   * HOST arrays (the one exception to the device-pointer rule): the width of
+   * each expert decides the launches, and is read during the call. */
+  const uint8_t* w_bits;  /* [N] */
+  const uint8_t* sw_bits; /* [n_shared] */
 } moe_weights;
 
 /* Router statistics (aigrafen L_aux equation and `latest` dict; starphix

@@ -41,6 +41,10 @@
 //  - GELU is the exact erf form; SiLU(u) = u / (1 + e^-u).
 //  - e4m3 weights: W = s * q, q an OCP e4m3fn code, one fp32 scale per
 //    (expert, matrix).
+//  - Integer weights [SPX "Quantization": INT8 for high-traffic experts, INT4
+//    for the rest, the router kept in 16 bits]: W[r][c] = s_r * q[r][c] with
+//    one fp32 scale per weight row and symmetric codes (|q| <= 127 or <= 7);
+//    the oracle reads one code per byte whatever the expert's bit width.
 //  - Expert choice [MOEA Expert-Choice Router]: the softmax runs over the
 //    tokens of each expert's column; an expert takes the C = int(T*cf/N)
 //    tokens of largest probability, exact ties to the lower token index, and
@@ -71,7 +75,8 @@ struct OrcShape {
   int32_t gating;     // 0 softmax->top-k, 1 softmax->top-k->renormalise, 2 top-k->softmax,
                       // 3 expert choice (softmax over tokens, each expert takes C tokens)
   int32_t act_dtype;  // 0 fp32, 1 bf16 (x, router weight, layer output)
-  int32_t w_dtype;    // 0 fp32, 1 bf16, 2 e4m3fn + per-(expert, matrix) fp32 scale
+  int32_t w_dtype;    // 0 fp32, 1 bf16, 2 e4m3fn + per-(expert, matrix) fp32 scale,
+                      // 3 integer codes (int8 storage, |q| <= 127 or <= 7) + per-row fp32 scale
   int64_t capacity;   // < 0: no capacity limit
   double aux_alpha;
 };
@@ -84,7 +89,8 @@ struct OrcWeights {
   const void* w2;              // [N][d][d_ff]
   const float* b1;             // [N][d_ff] or null (GELU only)
   const float* b2;             // [N][d] or null (GELU only)
-  const float* w_scale;        // [N][3] scales of (W1, W3, W2) for e4m3
+  const float* w_scale;        // [N][3] scales of (W1, W3, W2) for e4m3; for integer
+                               // codes [N][2 d_ff + d] row scales: W1 rows, W3 rows, W2 rows
   const void* sw1;             // shared experts [S][d_ff][d]
   const void* sw3;             // [S][d_ff][d]
   const void* sw2;             // [S][d][d_ff]
@@ -111,12 +117,14 @@ double e4m3_value(uint8_t q) {
   return (q & 0x80) ? -v : v;
 }
 
-// Element i of a tensor stored in `dtype`, times `scale` (e4m3 only).
+// Element i of a tensor stored in `dtype`, times `scale` (e4m3 and integer
+// codes only).
 double elem(const void* p, int dtype, int64_t i, double scale) {
   switch (dtype) {
     case 0: return static_cast<double>(static_cast<const float*>(p)[i]);
     case 1: return bf16_value(static_cast<const uint16_t*>(p)[i]);
-    default: return scale * e4m3_value(static_cast<const uint8_t*>(p)[i]);
+    case 2: return scale * e4m3_value(static_cast<const uint8_t*>(p)[i]);
+    default: return scale * static_cast<double>(static_cast<const int8_t*>(p)[i]);
   }
 }
 
@@ -124,7 +132,7 @@ bool shape_ok(const OrcShape* s) {
   return s && s->T >= 0 && s->d > 0 && s->d_ff > 0 && s->n_experts >= 1 && s->top_k >= 1 &&
          s->top_k <= s->n_experts && s->n_shared >= 0 && (s->act == 0 || s->act == 1) &&
          s->gating >= 0 && s->gating <= 3 && (s->act_dtype == 0 || s->act_dtype == 1) &&
-         s->w_dtype >= 0 && s->w_dtype <= 2;
+         s->w_dtype >= 0 && s->w_dtype <= 3;
 }
 
 // token choice: gating 0..2
@@ -134,7 +142,7 @@ bool shape_ok_tc(const OrcShape* s) { return shape_ok(s) && s->gating != 3; }
 bool shape_ok_ec(const OrcShape* s) {
   return s && s->T >= 0 && s->d > 0 && s->d_ff > 0 && s->n_experts >= 1 && s->top_k == 1 &&
          s->n_shared >= 0 && (s->act == 0 || s->act == 1) && s->gating == 3 &&
-         (s->act_dtype == 0 || s->act_dtype == 1) && s->w_dtype >= 0 && s->w_dtype <= 2 &&
+         (s->act_dtype == 0 || s->act_dtype == 1) && s->w_dtype >= 0 && s->w_dtype <= 3 &&
          s->capacity >= 0 && s->capacity <= s->T;
 }
 
@@ -155,9 +163,12 @@ void expert_rows(const OrcShape* s, const OrcWeights* w, bool shared, int e, con
   const float* sc = shared ? w->sw_scale : w->w_scale;
   const float* b1 = shared ? nullptr : w->b1;
   const float* b2 = shared ? nullptr : w->b2;
-  const double s1 = (s->w_dtype == 2) ? sc[3 * e + 0] : 1.0;
-  const double s3 = (s->w_dtype == 2) ? sc[3 * e + 1] : 1.0;
-  const double s2 = (s->w_dtype == 2) ? sc[3 * e + 2] : 1.0;
+  // e4m3: one scale per matrix; integer codes: one per weight row
+  const bool rowsc = (s->w_dtype == 3);
+  const int64_t rs0 = static_cast<int64_t>(e) * (2 * f + d);  // the expert's row scales
+  auto s1 = [&](int64_t i) { return rowsc ? sc[rs0 + i] : (s->w_dtype == 2) ? sc[3 * e + 0] : 1.0; };
+  auto s3 = [&](int64_t i) { return rowsc ? sc[rs0 + f + i] : (s->w_dtype == 2) ? sc[3 * e + 1] : 1.0; };
+  auto s2 = [&](int64_t o) { return rowsc ? sc[rs0 + 2 * f + o] : (s->w_dtype == 2) ? sc[3 * e + 2] : 1.0; };
   const int64_t base1 = static_cast<int64_t>(e) * f * d;  // expert e in [N][d_ff][d]
   const int64_t base2 = static_cast<int64_t>(e) * d * f;  // expert e in [N][d][d_ff]
   std::vector<double> H(static_cast<size_t>(n * f));
@@ -167,9 +178,9 @@ void expert_rows(const OrcShape* s, const OrcWeights* w, bool shared, int e, con
     std::vector<double> a(d), g(d);
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < f; ++i) {
-      for (int64_t j = 0; j < d; ++j) a[j] = elem(W1, s->w_dtype, base1 + i * d + j, s1);
+      for (int64_t j = 0; j < d; ++j) a[j] = elem(W1, s->w_dtype, base1 + i * d + j, s1(i));
       if (s->act == 1)
-        for (int64_t j = 0; j < d; ++j) g[j] = elem(W3, s->w_dtype, base1 + i * d + j, s3);
+        for (int64_t j = 0; j < d; ++j) g[j] = elem(W3, s->w_dtype, base1 + i * d + j, s3(i));
       for (int64_t r = 0; r < n; ++r) {
         const double* x = X + r * d;
         double u = 0.0;
@@ -191,7 +202,7 @@ void expert_rows(const OrcShape* s, const OrcWeights* w, bool shared, int e, con
     std::vector<double> a(f);
 #pragma omp for schedule(static)
     for (int64_t o = 0; o < d; ++o) {
-      for (int64_t i = 0; i < f; ++i) a[i] = elem(W2, s->w_dtype, base2 + o * f + i, s2);
+      for (int64_t i = 0; i < f; ++i) a[i] = elem(W2, s->w_dtype, base2 + o * f + i, s2(o));
       for (int64_t r = 0; r < n; ++r) {
         const double* h = H.data() + r * f;
         double u = 0.0;

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = 0, -1, -2, -3, -4
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, INT_W = 0, 1, 2, 3
 GELU, SWIGLU = 0, 1
 SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX, EXPERT_CHOICE = 0, 1, 2, 3
 ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_FFN, ENTRY_FORWARD = 0, 1, 2, 3
@@ -35,10 +35,12 @@ class Shape(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    """moe_weights (device pointers, then the row pitches of the expert matrices)"""
+    """moe_weights (device pointers, the row pitches of the expert matrices,
+    then the host arrays of integer bit widths)"""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_router", "b_router", "w1", "w3", "w2", "b1", "b2", "w_scale", "sw1", "sw3", "sw2",
-                 "sw_scale")] + [("ld_up", ctypes.c_int64), ("ld_down", ctypes.c_int64)]
+                 "sw_scale")] + [("ld_up", ctypes.c_int64), ("ld_down", ctypes.c_int64),
+                                 ("w_bits", ctypes.c_void_p), ("sw_bits", ctypes.c_void_p)]
 
 
 class Stats(ctypes.Structure):
@@ -234,11 +236,41 @@ def _row_pitch(ts, what):
 
 def weights_struct(t: dict) -> Weights:
     """moe_weights from a dict of device tensors (missing keys are NULL). The
-    row pitches come from the strides of w1/w3/sw1/sw3 and of w2/sw2."""
-    w = Weights(**{k: _ptr(v) for k, v in t.items() if v is not None})
+    row pitches come from the strides of w1/w3/sw1/sw3 and of w2/sw2. Integer
+    weights: "w_bits" / "sw_bits" are host numpy uint8 arrays, kept alive by
+    the returned struct."""
+    import numpy as np
+    dev_keys = {k: v for k, v in t.items() if v is not None and k not in ("w_bits", "sw_bits")}
+    w = Weights(**{k: _ptr(v) for k, v in dev_keys.items()})
     w.ld_up = _row_pitch([t.get(k) for k in ("w1", "w3", "sw1", "sw3")], "w1/w3/sw1/sw3")
     w.ld_down = _row_pitch([t.get(k) for k in ("w2", "sw2")], "w2/sw2")
+    keep = []
+    for k in ("w_bits", "sw_bits"):
+        if t.get(k) is not None:
+            a = np.ascontiguousarray(t[k], np.uint8)
+            keep.append(a)
+            setattr(w, k, a.ctypes.data)
+    w._host_arrays = keep
     return w
+
+
+def pack_int_weights(codes, bits, pad: int = 0):
+    """Integer expert matrices in the library's layout: codes [E][rows][cols]
+    (int8, one code per element) and bits [E] (8 or 4) -> uint8 [E][rows][cols
+    + pad] byte rows; an 8-bit expert's row holds its codes, a 4-bit expert's
+    row holds column 2i in the low nibble and 2i + 1 in the high nibble of byte
+    i (the rest of the row is zero). Host numpy in, host numpy out."""
+    import numpy as np
+    codes = np.asarray(codes, np.int8)
+    E, R, C = codes.shape
+    out = np.zeros((E, R, C + pad), np.uint8)
+    for e in range(E):
+        if int(bits[e]) == 8:
+            out[e, :, :C] = codes[e].view(np.uint8)
+        else:
+            u = codes[e].view(np.uint8) & 0x0F
+            out[e, :, :C // 2] = u[:, 0::2] | (u[:, 1::2] << 4)
+    return out
 
 
 def padded(t, pad: int = 64):

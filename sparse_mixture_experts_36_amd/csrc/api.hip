@@ -57,12 +57,13 @@ moe_status check_shape(const moe_shape* s) {
   if (s->gating == MOE_GATE_EXPERT_CHOICE && (s->top_k != 1 || s->capacity < 0 || s->capacity > s->T))
     return MOE_ERR_INVALID_ARG;
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_INT_W) return MOE_ERR_INVALID_ARG;
   if (s->n_experts > kMaxExperts || s->top_k > kMaxTopK || s->n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
   // kernels form row offsets inside a tile or a pass in 32 bits
   if (s->d > kMaxWidth || s->d_ff > kMaxWidth) return MOE_ERR_UNSUPPORTED;
-  if (s->w_dtype != s->act_dtype && !(s->w_dtype == MOE_FP8_E4M3 && s->act_dtype == MOE_BF16))
+  if (s->w_dtype != s->act_dtype &&
+      !((s->w_dtype == MOE_FP8_E4M3 || s->w_dtype == MOE_INT_W) && s->act_dtype == MOE_BF16))
     return MOE_ERR_UNSUPPORTED;
   if (s->T > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
   if (s->gating == MOE_GATE_EXPERT_CHOICE && s->T > moe::kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
@@ -279,10 +280,17 @@ moe_status check_weights(const moe_shape& s, const moe_weights* w, bool need_rou
   if (need_router && !w->w_router) return MOE_ERR_INVALID_ARG;
   if (!w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARG;
-  if (s.w_dtype == MOE_FP8_E4M3 && !w->w_scale) return MOE_ERR_INVALID_ARG;
+  if ((s.w_dtype == MOE_FP8_E4M3 || s.w_dtype == MOE_INT_W) && !w->w_scale) return MOE_ERR_INVALID_ARG;
   if (s.n_shared > 0) {
     if (!w->sw1 || !w->sw2 || (s.act == MOE_ACT_SWIGLU && !w->sw3)) return MOE_ERR_INVALID_ARG;
-    if (s.w_dtype == MOE_FP8_E4M3 && !w->sw_scale) return MOE_ERR_INVALID_ARG;
+    if ((s.w_dtype == MOE_FP8_E4M3 || s.w_dtype == MOE_INT_W) && !w->sw_scale) return MOE_ERR_INVALID_ARG;
+  }
+  if (s.w_dtype == MOE_INT_W) {  // bit widths: host arrays, 8 or 4 per expert
+    if (!w->w_bits || (s.n_shared > 0 && !w->sw_bits)) return MOE_ERR_INVALID_ARG;
+    for (int e = 0; e < s.n_experts; ++e)
+      if (w->w_bits[e] != 8 && w->w_bits[e] != 4) return MOE_ERR_INVALID_ARG;
+    for (int e = 0; e < s.n_shared; ++e)
+      if (w->sw_bits[e] != 8 && w->sw_bits[e] != 4) return MOE_ERR_INVALID_ARG;
   }
   const void* ptrs[] = {w->w_router, w->w1, w->w3, w->w2, w->sw1, w->sw3, w->sw2};
   for (const void* p : ptrs)
@@ -330,6 +338,8 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.active = fw.active;
   a.part = fw.part;
   a.split_part = fw.split_part;
+  a.w_bits = w->w_bits;
+  a.sw_bits = w->sw_bits;
   return a;
 }
 

@@ -40,6 +40,34 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Weight storage formats of the expert kernels (template argument WF).
+enum WeightFormat { kWBf16 = 0, kWE4m3 = 1, kWInt8 = 2, kWInt4 = 3 };
+
+// The bf16 pair (lo, hi) from the upper halves of two fp32 values: exact when
+// both are small integers, as decoded integer codes are.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Four int8 codes (byte i of w is code i) -> four bf16 values, exactly
+// (|q| <= 128 fits bf16's 8-bit significand).
+__device__ __forceinline__ uint2 int8x4_to_bf16x4(uint32_t w) {
+  const float f0 = static_cast<float>(static_cast<int32_t>(w << 24) >> 24);
+  const float f1 = static_cast<float>(static_cast<int32_t>(w << 16) >> 24);
+  const float f2 = static_cast<float>(static_cast<int32_t>(w << 8) >> 24);
+  const float f3 = static_cast<float>(static_cast<int32_t>(w) >> 24);
+  return make_uint2(pack_hi16(f0, f1), pack_hi16(f2, f3));
+}
+
+// Eight int4 codes (nibble i of w, from the least significant, is code i, two's
+// complement) -> eight bf16 values, exactly.
+__device__ __forceinline__ uint4 int4x8_to_bf16x8(uint32_t w) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+  return make_uint4(pack_hi16(f[0], f[1]), pack_hi16(f[2], f[3]), pack_hi16(f[4], f[5]), pack_hi16(f[6], f[7]));
+}
+
 // D += A(16x32) * B(32x16), bf16 inputs, fp32 accumulation. Lane l supplies
 // row (l % 16) of A and column (l % 16) of B, each as 8 consecutive k values of
 // the k-group (l / 16); it receives D rows 4*(l/16) + i, i < 4, column l % 16.

@@ -50,9 +50,13 @@ struct StreamParams {
   const char* B3_s;
   int64_t b_stride;          // elements per expert matrix
   const float* bias;         // [n_routed][Nout] (routed GELU experts) or null
-  const float* scale_r;      // e4m3 scales [n_routed][3]
+  const float* scale_r;      // e4m3 scales [n_routed][3]; integer weights: row scales [n_routed][scale_pitch]
   const float* scale_s;
   int scale_col;
+  int32_t scale_pitch;       // integer weights: floats per expert in the row-scale arrays (2 d_ff + d)
+  int32_t scale_row0;        // integer weights: offset of this GEMM's matrix rows (W1 0, W2 2 d_ff)
+  int32_t scale_row3;        // integer weights: offset of W3's rows (d_ff)
+  uint32_t skip[9];          // bit g set: group g is left to another launch (its experts' other bit width)
   uint16_t* C_r;             // outputs (h / y_perm) for routed groups
   uint16_t* C_s;             //              (h / y_shared) for shared groups
   int64_t ldc;
@@ -66,33 +70,70 @@ struct StreamParams {
   const int32_t* active;     // [0]: groups with rows, [1..]: those groups
 };
 
-// 8 bf16 weights per uint4; e4m3 codes are decoded to bf16 in registers.
+// Bytes of k consecutive weights of a row: bf16 2k, e4m3 and int8 k, int4 k/2
+// (integer rows live at a pitch of ldb bytes whatever the expert's bit width).
+template <int WF>
+__device__ __forceinline__ constexpr uint32_t kbytes(uint32_t k) {
+  return WF == kWBf16 ? 2 * k : (WF == kWInt4 ? k / 2 : k);
+}
+// Bytes of one row-pitch element.
+template <int WF>
+constexpr int pitch_bytes() { return WF == kWBf16 ? 2 : 1; }
+// Weight load instructions per k-step of one row (16 bytes each).
+template <int WF>
+constexpr int loads_per_step() { return WF == kWBf16 ? 4 : (WF == kWInt4 ? 1 : 2); }
+
 // One k-step of a weight row for lane (row, q): 32 weights from byte offset
-// `off` of a wave-uniform base (8 bf16 weights per uint4; e4m3 codes are
-// decoded to bf16 in registers).
-template <bool FP8>
+// `off` of a wave-uniform base, w[t] holding MFMA t's eight (8 bf16 weights
+// per uint4; e4m3 and int8 codes in .x/.y, int4 codes in .x, decoded to bf16
+// in registers).
+template <int WF>
 __device__ __forceinline__ void load_w(const char* base, uint32_t off, uint4 (&w)[4]) {
-  if constexpr (FP8) {
+  if constexpr (WF == kWE4m3 || WF == kWInt8) {
     const uint4 q0 = *reinterpret_cast<const uint4*>(base + off);
     const uint4 q1 = *reinterpret_cast<const uint4*>(base + (off + 16));
     w[0] = make_uint4(q0.x, q0.y, 0, 0);
     w[1] = make_uint4(q0.z, q0.w, 0, 0);
     w[2] = make_uint4(q1.x, q1.y, 0, 0);
     w[3] = make_uint4(q1.z, q1.w, 0, 0);
+  } else if constexpr (WF == kWInt4) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(base + off);
+    w[0] = make_uint4(q0.x, 0, 0, 0);
+    w[1] = make_uint4(q0.y, 0, 0, 0);
+    w[2] = make_uint4(q0.z, 0, 0, 0);
+    w[3] = make_uint4(q0.w, 0, 0, 0);
   } else {
 #pragma unroll
     for (int t = 0; t < 4; ++t) w[t] = *reinterpret_cast<const uint4*>(base + (off + kTStride * t));
   }
 }
 
-template <bool FP8>
+template <int WF>
 __device__ __forceinline__ uint4 as_bf16(const uint4& w) {
-  if constexpr (FP8) {
+  if constexpr (WF == kWE4m3) {
     const uint2 a = e4m3x4_to_bf16x4(w.x), b = e4m3x4_to_bf16x4(w.y);
     return make_uint4(a.x, a.y, b.x, b.y);
+  } else if constexpr (WF == kWInt8) {
+    const uint2 a = int8x4_to_bf16x4(w.x), b = int8x4_to_bf16x4(w.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  } else if constexpr (WF == kWInt4) {
+    return int4x8_to_bf16x8(w.x);
   } else {
     return w;
   }
+}
+
+// Whether group g is left to another launch (integer weights of the other bit width).
+__device__ __forceinline__ bool skipped(const StreamParams& p, int g) { return (p.skip[g >> 5] >> (g & 31)) & 1u; }
+
+// The scale of weight row `row` of matrix offset `moff` (integer weights: one
+// per row), or the e4m3 scale of the matrix, or 1.
+template <int WF>
+__device__ __forceinline__ float wscale(const StreamParams& p, bool shared, int ew, int moff, int row, int col) {
+  const float* sc = shared ? p.scale_s : p.scale_r;
+  if constexpr (WF == kWE4m3) return sc[ew * 3 + col];
+  if constexpr (WF == kWInt8 || WF == kWInt4) return sc[static_cast<int64_t>(ew) * p.scale_pitch + moff + row];
+  return 1.f;
 }
 
 __device__ __forceinline__ float epilogue(int epi, float a, float b, float bias) {
@@ -111,7 +152,7 @@ __device__ __forceinline__ float epilogue(int epi, float a, float b, float bias)
 // lanes that read one chunk of 16 rows hit 16 different bank groups. The two
 // LDS buffers alternate by burst, one barrier per burst; the host guarantees
 // an even number of bursts per pass.
-template <int RB, bool FP8, int KU, bool SHARED_A>
+template <int RB, int WF, int KU, bool SHARED_A>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   static_assert(!SHARED_A || (RB >= 2 && KU == 2), "shared token rows: 32 or 64 rows, two k-steps a burst");
   constexpr int AROWB = KU * KC * 2;                        // bytes of one token row per burst
@@ -131,48 +172,47 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   const int slot = w / per_g;  // waves run over the groups that have rows only
   if (slot >= p.active[0]) return;
   const int g = p.active[1 + slot];
-  if (g >= p.n_groups) return;
+  if (g >= p.n_groups || skipped(p, g)) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
   const int nb = SHARED_A ? (w % per_g) % nblk : (w % per_g) / p.splits;
   const int sp = SHARED_A ? (w % per_g) / nblk : w % p.splits;
   const bool shared = g >= p.n_routed;
   const int ew = shared ? g - p.n_routed : g;
-  constexpr int WB = FP8 ? 1 : 2;
+  constexpr int EB = pitch_bytes<WF>();
+  constexpr bool BYTE = WF != kWBf16;  // a byte or half a byte per weight
   // k order inside a 128-wide step (the same for both operands, so any order
   // gives the same sums): bf16 MFMA t takes k [32t, 32t + 32), lane group q
   // its 8 k at 8q, so the four lanes of a row read 64 contiguous bytes per
-  // load; e4m3 lane group q takes k [32q, 32q + 32) in two 16-byte loads, MFMA
-  // t its 8 k at 8t
-  constexpr int QK = FP8 ? 32 : 8;         // k offset of lane group q
-  constexpr int AT = FP8 ? 16 : 64;        // A bytes between MFMA t and t + 1
+  // load; with e4m3 / int8 codes lane group q takes k [32q, 32q + 32) in two
+  // 16-byte loads (int4: one), MFMA t its 8 k at 8t
+  constexpr int QK = BYTE ? 32 : 8;        // k offset of lane group q
+  constexpr int AT = BYTE ? 16 : 64;       // A bytes between MFMA t and t + 1
   const int K = p.K, ks = K / p.splits;
   const int kbeg = sp * ks, nsteps = ks / KC;
   // weight rows: SwiGLU up takes rows [n0, n0 + 16) of W1 (tile 0) and of W3
   // (tile 1), otherwise rows [n0, n0 + 32) of one matrix; the bases point at
   // (row n0, column kbeg), the lane offsets add row and k-group
   const int n0 = swi ? nb * 16 : nb * 32;
-  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb + kbeg) * WB;
+  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb) * EB +
+                       kbytes<WF>(static_cast<uint32_t>(kbeg));
   const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
   const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
   const char* wbase[FN] = {Bw, swi ? B3w : Bw};
   uint32_t woff[FN];
+  float sw[FN];  // the scale of the lane's weight row in tile j
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int r = swi ? c16 : j * 16 + c16;
-    woff[j] = static_cast<uint32_t>((r * static_cast<int>(p.ldb) + q * QK) * WB);
+    woff[j] = static_cast<uint32_t>(r * static_cast<int>(p.ldb) * EB) + kbytes<WF>(static_cast<uint32_t>(q * QK));
+    const bool third = swi && j == 1;
+    sw[j] = wscale<WF>(p, shared, ew, third ? p.scale_row3 : p.scale_row0, n0 + r, p.scale_col + (third ? 1 : 0));
   }
   const int64_t lda = shared ? p.lda_s : p.lda_r;
   // A rows are addressed from the buffer's start (column kbeg): row r of the
   // group is buffer row a_row0 + r, or gather[a_row0 + r]
   const char* A = reinterpret_cast<const char*>((shared ? p.A_s : p.A_r) + kbeg);
   const int32_t* gth = shared ? nullptr : p.gather;
-  float s_a = 1.f, s_b = 1.f;
-  if (FP8) {
-    const float* sc = shared ? p.scale_s : p.scale_r;
-    s_a = sc[ew * 3 + p.scale_col];
-    s_b = swi ? sc[ew * 3 + p.scale_col + 1] : s_a;
-  }
 
   for (int r0 = 0; r0 < gd.rows; r0 += 16 * RB) {
     // opaque to the optimiser, so that the first loads' addresses are formed
@@ -223,18 +263,18 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
         for (int u = 0; u < KU; ++u) {
           const uint32_t kk = static_cast<uint32_t>((st + u) * KC);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk * WB, bw[u][j]);
+          for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), bw[u][j]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // this wave's token-row DMA has landed (loads complete in issue order)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(KU * FN * (FP8 ? 2 : 4)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(KU * FN * loads_per_step<WF>()));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const int ch = u * 16 + (FP8 ? q * 4 + t : t * 4 + q);
+            const int ch = u * 16 + (BYTE ? q * 4 + t : t * 4 + q);
             uint4 av[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -243,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-              const uint4 b = as_bf16<FP8>(bw[u][j][t]);
+              const uint4 b = as_bf16<WF>(bw[u][j][t]);
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(av[rb], b, acc[rb][j]);
             }
@@ -260,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
       for (int u = 0; u < KU; ++u) {
         const uint32_t kk = static_cast<uint32_t>(min(st + u, nsteps - 1) * KC);  // a step past the end re-reads the last one
 #pragma unroll
-        for (int j = 0; j < FN; ++j) load_w<FP8>(wbase[j], woff[j] + kk * WB, bw[u][j]);
+        for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), bw[u][j]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const uint4 b = as_bf16<FP8>(bw[u][j][t]);
+            const uint4 b = as_bf16<WF>(bw[u][j][t]);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(a[u][rb][t], b, acc[rb][j]);
           }
@@ -297,18 +337,18 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
           for (int j = 0; j < FN; ++j) {
             // partial columns: SwiGLU [W1 results | W3 results], otherwise the output columns
             const int col = swi ? (j == 0 ? n0 + c16 : p.Nout + n0 + c16) : n0 + j * 16 + c16;
-            dst[col] = acc[rb][j][i] * (j == 1 ? s_b : s_a);
+            dst[col] = acc[rb][j][i] * sw[j];
           }
         } else {
           uint16_t* C = (shared ? p.C_s : p.C_r) + (static_cast<int64_t>(gd.c_row0) + row) * p.ldc;
           const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout : nullptr;
           if (swi) {
-            C[n0 + c16] = f32_to_bf16(epilogue(1, acc[rb][0][i] * s_a, acc[rb][1][i] * s_b, 0.f));
+            C[n0 + c16] = f32_to_bf16(epilogue(1, acc[rb][0][i] * sw[0], acc[rb][1][i] * sw[1], 0.f));
           } else {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
               const int col = n0 + j * 16 + c16;
-              C[col] = f32_to_bf16(epilogue(p.epi, acc[rb][j][i] * s_a, 0.f, bias ? bias[col] : 0.f));
+              C[col] = f32_to_bf16(epilogue(p.epi, acc[rb][j][i] * sw[j], 0.f, bias ? bias[col] : 0.f));
             }
           }
         }
@@ -384,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p,
 // are reduced across the wave once, at the end (a fixed butterfly order).
 constexpr int kSeg = 1024;  // bytes of one weight row per segment
 
-template <int R, bool FP8, int NR, int U>
+template <int R, int WF, int NR, int U>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int lane = threadIdx.x & 63;
@@ -395,24 +435,24 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
   const int slot = w / nblk;  // waves run over the groups that have rows only
   if (slot >= p.active[0]) return;
   const int g = p.active[1 + slot];
-  if (g >= p.n_groups) return;
+  if (g >= p.n_groups || skipped(p, g)) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
   const int n0 = (w % nblk) * cols;
   const bool shared = g >= p.n_routed;
   const int ew = shared ? g - p.n_routed : g;
-  constexpr int WB = FP8 ? 1 : 2;
-  constexpr int KSEG = kSeg / WB;   // k per segment
-  constexpr int XW = FP8 ? 2 : 1;   // activation uint4 per lane and segment
+  constexpr int EB = pitch_bytes<WF>();
+  constexpr int KSEG = WF == kWBf16 ? kSeg / 2 : (WF == kWInt4 ? 2 * kSeg : kSeg);  // k per segment
+  constexpr int XW = KSEG / 512;    // activation uint4 per lane and segment
   const int nseg = p.K / KSEG;
-  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb) * WB;
+  const int64_t eoff = (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb) * EB;
   const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
   const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
   const char* wrow[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     const bool third = swi && j >= NR / 2;
-    wrow[j] = (third ? B3w : Bw) + static_cast<int64_t>(third ? j - NR / 2 : j) * p.ldb * WB;
+    wrow[j] = (third ? B3w : Bw) + static_cast<int64_t>(third ? j - NR / 2 : j) * p.ldb * EB;
   }
   const int64_t lda = shared ? p.lda_s : p.lda_r;
   const char* A = reinterpret_cast<const char*>(shared ? p.A_s : p.A_r);
@@ -424,15 +464,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
     arow[r] = A + static_cast<int64_t>(gth ? gth[ar] : ar) * lda * 2;
   }
   // lane l: weight bytes [16 l, 16 l + 16) of a segment, i.e. k from
-  // seg * KSEG + l * 16 / WB, and the bf16 activations of those k
+  // seg * KSEG + l * KSEG / 64, and the bf16 activations of those k
   const uint32_t wl = static_cast<uint32_t>(lane) * 16;
   const uint32_t al = static_cast<uint32_t>(lane) * 16 * XW;
-  float s_a = 1.f, s_b = 1.f;
-  if (FP8) {
-    const float* sc = shared ? p.scale_s : p.scale_r;
-    s_a = sc[ew * 3 + p.scale_col];
-    s_b = swi ? sc[ew * 3 + p.scale_col + 1] : s_a;
-  }
 
   float acc[NR][R];
 #pragma unroll
@@ -460,11 +494,24 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         uint32_t wd[4 * XW];
-        if constexpr (FP8) {
-          const uint2 b0 = e4m3x4_to_bf16x4(wv[u][j].x), b1 = e4m3x4_to_bf16x4(wv[u][j].y);
-          const uint2 b2 = e4m3x4_to_bf16x4(wv[u][j].z), b3 = e4m3x4_to_bf16x4(wv[u][j].w);
-          wd[0] = b0.x; wd[1] = b0.y; wd[2] = b1.x; wd[3] = b1.y;
-          wd[4] = b2.x; wd[5] = b2.y; wd[6] = b3.x; wd[7] = b3.y;
+        if constexpr (WF == kWE4m3 || WF == kWInt8) {
+          const uint32_t q4[4] = {wv[u][j].x, wv[u][j].y, wv[u][j].z, wv[u][j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint2 b = WF == kWE4m3 ? e4m3x4_to_bf16x4(q4[i]) : int8x4_to_bf16x4(q4[i]);
+            wd[2 * i] = b.x;
+            wd[2 * i + 1] = b.y;
+          }
+        } else if constexpr (WF == kWInt4) {
+          const uint32_t q4[4] = {wv[u][j].x, wv[u][j].y, wv[u][j].z, wv[u][j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 b = int4x8_to_bf16x8(q4[i]);
+            wd[4 * i] = b.x;
+            wd[4 * i + 1] = b.y;
+            wd[4 * i + 2] = b.z;
+            wd[4 * i + 3] = b.w;
+          }
         } else {
           wd[0] = wv[u][j].x; wd[1] = wv[u][j].y; wd[2] = wv[u][j].z; wd[3] = wv[u][j].w;
         }
@@ -501,6 +548,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
 #pragma unroll
     for (int c = 0; c < NR; ++c) {
       if (c >= cols || lane != c) continue;
+      const float s_a = wscale<WF>(p, shared, ew, p.scale_row0, n0 + c, p.scale_col);
+      const float s_b = swi ? wscale<WF>(p, shared, ew, p.scale_row3, n0 + c, p.scale_col + 1) : s_a;
       const float v = swi ? epilogue(1, acc[c][r] * s_a, acc[(c + NR / 2) % NR][r] * s_b, 0.f)
                           : epilogue(p.epi, acc[c][r] * s_a, 0.f, bias ? bias[c] : 0.f);
       C[c] = f32_to_bf16(v);
@@ -520,7 +569,7 @@ int pick_splits(int64_t K, int64_t blocks_touched) {
   return s;
 }
 
-hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, hipStream_t s) {
+hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hipStream_t s) {
   const int64_t waves = blocks * p.splits;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
   // 32 or 64 token rows: shared through LDS when the passes hold whole burst pairs
@@ -530,9 +579,13 @@ hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, h
   // they can (measured faster there), else four k-steps per burst (whose
   // registers still fit 2 waves per SIMD)
   const bool deep = rb == 1 && waves <= 2048;
-#define MOE_STREAM_LAUNCH(R, U, SA)                                                                 \
-  if (fp8) hipLaunchKernelGGL((stream_kernel<R, true, U, SA>), grid, dim3(kThreads), 0, s, p);      \
-  else hipLaunchKernelGGL((stream_kernel<R, false, U, SA>), grid, dim3(kThreads), 0, s, p);
+#define MOE_STREAM_LAUNCH(R, U, SA)                                                                        \
+  switch (wf) {                                                                                            \
+    case kWE4m3: hipLaunchKernelGGL((stream_kernel<R, kWE4m3, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
+    case kWInt8: hipLaunchKernelGGL((stream_kernel<R, kWInt8, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
+    case kWInt4: hipLaunchKernelGGL((stream_kernel<R, kWInt4, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
+    default: hipLaunchKernelGGL((stream_kernel<R, kWBf16, U, SA>), grid, dim3(kThreads), 0, s, p); break;     \
+  }
   if (deep && pairs) {
     MOE_STREAM_LAUNCH(2, 2, true)
   } else if (deep) {
@@ -548,22 +601,29 @@ hipError_t run_stream(const StreamParams& p, int rb, bool fp8, int64_t blocks, h
   return hipGetLastError();
 }
 
-// The GEMV path: at most two rows per group and whole 1 KB segments per row.
+// The GEMV path: at most two rows per group and whole 1 KB segments per row
+// (k per segment: bf16 512, e4m3 1024, integer weights 2048, which also
+// covers the int8 experts' 1024).
 bool use_gemv(const FfnArgs& a) {
-  const int64_t kseg = a.w_dtype == 2 ? kSeg : kSeg / 2;
+  const int64_t kseg = a.w_dtype == 2 ? kSeg : (a.w_dtype == 3 ? 2 * kSeg : kSeg / 2);
   return a.T <= 2 && a.d % kseg == 0 && a.d_ff % kseg == 0;
 }
 
 // NR = 8 weight rows per wave while that still gives 2048 waves, else 4;
-// each burst is 32 KB of one wave's rows.
-hipError_t run_gemv(const StreamParams& p, int rows, bool fp8, int64_t slots, hipStream_t s) {
+// each burst is 32 KB of one wave's rows (int4: 16 KB, as a segment's
+// activations are four times those of bf16 and would not fit the registers).
+hipError_t run_gemv(const StreamParams& p, int rows, int wf, int64_t slots, hipStream_t s) {
   const bool swi = (p.epi == 1);
   const int nr = slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4;
   const int64_t waves = slots * p.Nout / (swi ? nr / 2 : nr);
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
-#define MOE_GEMV_LAUNCH(R, NR, U)                                                                   \
-  if (fp8) hipLaunchKernelGGL((gemv_kernel<R, true, NR, U>), grid, dim3(kThreads), 0, s, p);        \
-  else hipLaunchKernelGGL((gemv_kernel<R, false, NR, U>), grid, dim3(kThreads), 0, s, p);
+#define MOE_GEMV_LAUNCH(R, NR, U)                                                                          \
+  switch (wf) {                                                                                            \
+    case kWE4m3: hipLaunchKernelGGL((gemv_kernel<R, kWE4m3, NR, U>), grid, dim3(kThreads), 0, s, p); break;   \
+    case kWInt8: hipLaunchKernelGGL((gemv_kernel<R, kWInt8, NR, U>), grid, dim3(kThreads), 0, s, p); break;   \
+    case kWInt4: hipLaunchKernelGGL((gemv_kernel<R, kWInt4, NR, U / 2>), grid, dim3(kThreads), 0, s, p); break; \
+    default: hipLaunchKernelGGL((gemv_kernel<R, kWBf16, NR, U>), grid, dim3(kThreads), 0, s, p); break;       \
+  }
   if (rows == 1) {
     if (nr == 8) { MOE_GEMV_LAUNCH(1, 8, 4) } else { MOE_GEMV_LAUNCH(1, 4, 8) }
   } else {
@@ -604,12 +664,23 @@ size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, 
 hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
                              hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
-  const bool fp8 = (a.w_dtype == 2);
   const bool swi = (a.act == 1);
   const SplitPlan sp = plan_splits(a.T, a.d, a.d_ff, a.n_routed, a.n_shared, a.act, a.routed_row_cap);
   StreamParams p{};
   p.n_routed = a.n_routed;
   p.n_groups = G;
+  // integer weights: one launch per bit width present, each skipping the
+  // groups of the other width
+  const WeightClasses wc = weight_classes(a);
+  p.scale_pitch = static_cast<int32_t>(2 * a.d_ff + a.d);
+  auto run_classes = [&](auto&& run) -> hipError_t {
+    hipError_t e = hipSuccess;
+    for (int c = 0; c < wc.n && e == hipSuccess; ++c) {
+      for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
+      e = run(wc.wf[c]);
+    }
+    return e;
+  };
   p.rows_total = a.routed_row_cap + a.n_shared * static_cast<int32_t>(a.T);
 
   // ---- up: [rows][d] x W1 (W3)^T -> h [rows][d_ff]
@@ -629,6 +700,8 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.scale_r = a.w_scale;
   p.scale_s = a.sw_scale;
   p.scale_col = 0;
+  p.scale_row0 = 0;
+  p.scale_row3 = static_cast<int32_t>(a.d_ff);
   p.C_r = static_cast<uint16_t*>(a.h);
   p.C_s = static_cast<uint16_t*>(a.h);
   p.ldc = a.ld_h;
@@ -650,7 +723,9 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
     p.part = nullptr;
   }
   stage_mark(kStageFfnUp, false, s);
-  hipError_t e = gemv ? run_gemv(p, static_cast<int>(a.T), fp8, slots, s) : run_stream(p, sp.rb, fp8, up_blocks, s);
+  hipError_t e = run_classes([&](int wf) {
+    return gemv ? run_gemv(p, static_cast<int>(a.T), wf, slots, s) : run_stream(p, sp.rb, wf, up_blocks, s);
+  });
   if (e == hipSuccess && p.part) {
     const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
     hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);
@@ -673,6 +748,8 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   p.b_stride = a.d * a.ld_down;
   p.bias = swi ? nullptr : a.b2;
   p.scale_col = 2;
+  p.scale_row0 = static_cast<int32_t>(2 * a.d_ff);
+  p.scale_row3 = 0;
   p.C_r = static_cast<uint16_t*>(a.y_perm);
   p.C_s = static_cast<uint16_t*>(a.y_shared);
   p.ldc = a.d;
@@ -690,7 +767,9 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
     p.part = nullptr;
   }
   stage_mark(kStageFfnDown, false, s);
-  e = gemv ? run_gemv(p, static_cast<int>(a.T), fp8, slots, s) : run_stream(p, sp.rb, fp8, down_blocks, s);
+  e = run_classes([&](int wf) {
+    return gemv ? run_gemv(p, static_cast<int>(a.T), wf, slots, s) : run_stream(p, sp.rb, wf, down_blocks, s);
+  });
   if (e == hipSuccess && p.part) {
     const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
     hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);

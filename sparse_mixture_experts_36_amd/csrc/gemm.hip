@@ -47,9 +47,13 @@ struct GemmParams {
   int64_t ldb;            // weight row pitch (elements, >= K)
   int64_t b_stride;       // elements per expert matrix = Nout * ldb
   const float* bias;      // [n_routed][Nout] or null (routed GELU experts only)
-  const float* scale_r;   // [n_routed][3] (e4m3) or null
-  const float* scale_s;   // [n_shared][3]
+  const float* scale_r;   // [n_routed][3] (e4m3), [n_routed][scale_pitch] row scales (integer weights), or null
+  const float* scale_s;   // [n_shared][3] or [n_shared][scale_pitch]
   int scale_col;          // 0 for the up GEMM (W1, W3 at +1), 2 for the down GEMM
+  int32_t scale_pitch;    // integer weights: floats per expert in the row-scale arrays (2 d_ff + d)
+  int32_t scale_row0;     // integer weights: offset of this GEMM's matrix rows (W1 0, W2 2 d_ff)
+  int32_t scale_row3;     // integer weights: offset of W3's rows (d_ff)
+  uint32_t skip[9];       // bit g set: group g is left to another launch (its experts' other bit width)
   void* C_r;
   void* C_s;
   int64_t ldc;            // = Nout
@@ -143,7 +147,7 @@ __device__ __forceinline__ SplitPlan split_plan(const GemmParams& p, int ks_pair
 // rows of an MFMA operand read then hit distinct banks, so ds_read_b128 runs at
 // the full 256 B/clk of a gfx950 CU (a 16-byte row pad only reaches half of
 // it). The epilogue stages the bf16 output tile through LDS for 16-byte stores.
-template <int BM, int BNB, int WGM, int WGN, int EPI, bool FP8, int PF>
+template <int BM, int BNB, int WGM, int WGN, int EPI, int WF, int PF>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NTH = 64 * WGM * WGN;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
@@ -157,7 +161,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   constexpr int FN = WTB / 16;
   constexpr int FNO = WTO / 16;
   constexpr int A_CH = BM * (BK / 8) / NTH;  // 16-byte chunks per thread
-  constexpr int CPR = FP8 ? BK / 16 : BK / 8;  // weight chunks per row
+  constexpr bool BYTE = WF != kWBf16;         // e4m3 / int8 / int4 codes, decoded in registers
+  // 16-byte weight chunks per row and k-step: 8 bf16, 16 e4m3 or int8, 32 int4 weights each
+  constexpr int CPR = WF == kWBf16 ? BK / 8 : (WF == kWInt4 ? BK / 32 : BK / 16);
+  constexpr int DCH = (BK / 8) / CPR;          // bf16 chunks one weight chunk decodes to
   constexpr int B_CH = BNB * CPR / NTH;
   constexpr int STAGE = (BM + BNB) * S;      // elements per LDS buffer
   constexpr int SO = BNO + 8;                // output staging row (elements)
@@ -168,6 +175,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
 
   TileInfo ti;
   if (!decode_tile<BM, BNO>(p, ti)) return;
+  if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -182,10 +190,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   const int32_t* gth = shared ? nullptr : p.gather;
   const int arow0 = ti.gd.a_row0 + ti.m_tile * BM;  // the tile's first row in the group's A rows
   const uint16_t* A = static_cast<const uint16_t*>(shared ? p.A_s : p.A_r) + (gth ? 0 : static_cast<int64_t>(arow0) * lda);
-  constexpr int WB = FP8 ? 1 : 2;  // weight bytes
-  const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride * WB;
+  constexpr int EB = BYTE ? 1 : 2;  // bytes per row-pitch element
+  const char* Bw = static_cast<const char*>(shared ? p.B_s : p.B_r) + static_cast<int64_t>(ew) * p.b_stride * EB;
   const char* B3w = SWI ? static_cast<const char*>(shared ? p.B3_s : p.B3_r) +
-                              static_cast<int64_t>(ew) * p.b_stride * WB
+                              static_cast<int64_t>(ew) * p.b_stride * EB
                         : Bw;
 
   // per-thread chunk offsets (elements from A / bytes from the weight bases)
@@ -211,11 +219,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   for (int i = 0; i < B_CH; ++i) {
     const int c = tid + i * NTH;
     const int r = c / CPR, kc = c % CPR;
-    // bf16: one chunk; e4m3: 16 codes become the two bf16 chunks 2 kc, 2 kc + 1
-    b_dst[i] = BM * S + r * S + (FP8 ? 0 : ((kc ^ (r & 7)) * 8));
+    // bf16: one chunk; codes: chunk kc decodes to the bf16 chunks DCH kc .. DCH kc + DCH - 1
+    b_dst[i] = BM * S + r * S + (BYTE ? 0 : ((kc ^ (r & 7)) * 8));
     b_w3[i] = SWI && (SPLIT ? (i >= B_CH / 2) : (r >= BNO));
     const int wr = n0 + (b_w3[i] ? r - BNO : r);
-    b_off[i] = (static_cast<uint32_t>(wr) * static_cast<uint32_t>(p.ldb) + kc * (FP8 ? 16 : 8)) * WB;
+    b_off[i] = static_cast<uint32_t>(wr) * static_cast<uint32_t>(p.ldb) * EB + kc * 16;
   }
 
   floatx4_t acc[FM][FN];
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
         *reinterpret_cast<const uint4*>(A + a_off[i] + (kb));                                       \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) RB[i] = *reinterpret_cast<const uint4*>(       \
         ((SPLIT ? (SWI && i >= B_CH / 2) : b_w3[i]) ? B3w : Bw) + b_off[i] +                        \
-        static_cast<uint32_t>(kb) * WB);                                                            \
+        (WF == kWBf16 ? 2u : 1u) * static_cast<uint32_t>(kb) / (WF == kWInt4 ? 2u : 1u));          \
   } while (0)
 #define MOE_LSTORE(RA, RB, buf)                                                                     \
   do {                                                                                              \
@@ -238,14 +246,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                \
         *reinterpret_cast<uint4*>(st_ + a_dst[i]) = RA[i];                                          \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                              \
-      if constexpr (FP8) {                                                                          \
+      if constexpr (WF == kWE4m3 || WF == kWInt8) {                                                 \
         const int r_ = (tid + i * NTH) / CPR, k2_ = 2 * ((tid + i * NTH) % CPR);                    \
-        const uint2 x0 = e4m3x4_to_bf16x4(RB[i].x), x1 = e4m3x4_to_bf16x4(RB[i].y);                 \
-        const uint2 x2 = e4m3x4_to_bf16x4(RB[i].z), x3 = e4m3x4_to_bf16x4(RB[i].w);                 \
+        const uint2 x0 = WF == kWE4m3 ? e4m3x4_to_bf16x4(RB[i].x) : int8x4_to_bf16x4(RB[i].x);      \
+        const uint2 x1 = WF == kWE4m3 ? e4m3x4_to_bf16x4(RB[i].y) : int8x4_to_bf16x4(RB[i].y);      \
+        const uint2 x2 = WF == kWE4m3 ? e4m3x4_to_bf16x4(RB[i].z) : int8x4_to_bf16x4(RB[i].z);      \
+        const uint2 x3 = WF == kWE4m3 ? e4m3x4_to_bf16x4(RB[i].w) : int8x4_to_bf16x4(RB[i].w);      \
         *reinterpret_cast<uint4*>(st_ + b_dst[i] + ((k2_ ^ (r_ & 7)) * 8)) =                        \
             make_uint4(x0.x, x0.y, x1.x, x1.y);                                                     \
         *reinterpret_cast<uint4*>(st_ + b_dst[i] + (((k2_ + 1) ^ (r_ & 7)) * 8)) =                  \
             make_uint4(x2.x, x2.y, x3.x, x3.y);                                                     \
+      } else if constexpr (WF == kWInt4) {                                                          \
+        const int r_ = (tid + i * NTH) / CPR, k4_ = DCH * ((tid + i * NTH) % CPR);                  \
+        const uint32_t q_[4] = {RB[i].x, RB[i].y, RB[i].z, RB[i].w};                                \
+        _Pragma("unroll") for (int m_ = 0; m_ < 4; ++m_)                                            \
+            *reinterpret_cast<uint4*>(st_ + b_dst[i] + (((k4_ + m_) ^ (r_ & 7)) * 8)) =             \
+                int4x8_to_bf16x8(q_[m_]);                                                           \
       } else {                                                                                      \
         *reinterpret_cast<uint4*>(st_ + b_dst[i]) = RB[i];                                          \
       }                                                                                             \
@@ -316,16 +332,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bf16_kernel(GemmParams
   // ---- epilogue: activation in registers, bf16 tile staged in LDS, 16-byte stores
   const float* sc = shared ? p.scale_s : p.scale_r;
   float s_a = 1.f, s_b = 1.f;
-  if (FP8 && sc) {
+  if (WF == kWE4m3 && sc) {
     s_a = sc[ew * 3 + p.scale_col];
     if (SWI) s_b = sc[ew * 3 + p.scale_col + 1];
   }
+  // integer weights: one scale per weight row (output column)
+  const float* rs = (WF == kWInt8 || WF == kWInt4) ? sc + static_cast<int64_t>(ew) * p.scale_pitch + n0 : nullptr;
   const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
   uint16_t* so = smem;
 #pragma unroll
   for (int j = 0; j < FNO; ++j) {
     const int col = wn * WTO + j * 16 + c16;
     const float bv = bias ? bias[col] : 0.f;
+    if (rs) {
+      s_a = rs[p.scale_row0 + col];
+      if (SWI) s_b = rs[p.scale_row3 + col];
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -1062,14 +1084,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, 
   plan_groups(offsets, pl, s_mt, threadIdx.x, kThreads);
 }
 
-template <int BM, int BNB, int WGM, int WGN, int EPI, bool FP8, int PF = MOE_GEMM_PF>
+template <int BM, int BNB, int WGM, int WGN, int EPI, int WF, int PF = MOE_GEMM_PF>
 hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;
   if (p.Nout % BNO != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
   grid = ceil_div(grid, kXcds) * kXcds;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB, WGM, WGN, EPI, FP8, PF>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB, WGM, WGN, EPI, WF, PF>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
 }
@@ -1077,7 +1099,7 @@ hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 // Tile configurations of the bf16 path.
 enum TileCfg {
   kReg128 = 0,  // register-staged 128 x 128, 4 waves: fewer than 2048 rows
-  kReg256 = 1,  // register-staged 256 x 256, 8 waves: e4m3 weights (decoded in registers)
+  kReg256 = 1,  // register-staged 256 x 256, 8 waves: e4m3 or integer weights (decoded in registers)
   kDma256 = 2,  // LDS-DMA 256 x 256: bf16, many rows per group
   kDma128 = 3,  // LDS-DMA 128 x 256: bf16, few rows per group
 };
@@ -1132,17 +1154,27 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, bool FP8>
+template <int EPI, int WF>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  if constexpr (FP8) {
-    if (cfg == kReg256) return run_bf16<256, 256, 2, 4, EPI, true>(p, max_mtiles, s);
-    return run_bf16<128, 128, 2, 2, EPI, true>(p, max_mtiles, s);
+  if constexpr (WF != kWBf16) {
+    if (cfg == kReg256) return run_bf16<256, 256, 2, 4, EPI, WF>(p, max_mtiles, s);
+    return run_bf16<128, 128, 2, 2, EPI, WF>(p, max_mtiles, s);
   } else {
     switch (cfg) {
       case kDma256: return run_dma5<EPI>(p, max_mtiles, s);
       case kDma128: return run_dma<EPI, 128, 8>(p, max_mtiles, s);
-      default: return run_bf16<128, 128, 2, 2, EPI, false>(p, max_mtiles, s);
+      default: return run_bf16<128, 128, 2, 2, EPI, kWBf16>(p, max_mtiles, s);
     }
+  }
+}
+
+template <int EPI>
+hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+  switch (wf) {
+    case kWE4m3: return run_cfg<EPI, kWE4m3>(cfg, p, max_mtiles, s);
+    case kWInt8: return run_cfg<EPI, kWInt8>(cfg, p, max_mtiles, s);
+    case kWInt4: return run_cfg<EPI, kWInt4>(cfg, p, max_mtiles, s);
+    default: return run_cfg<EPI, kWBf16>(cfg, p, max_mtiles, s);
   }
 }
 
@@ -1154,7 +1186,7 @@ hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
   if (rows < 2048) return kReg128;
-  if (a.w_dtype == 2) return kReg256;
+  if (a.w_dtype == 2 || a.w_dtype == 3) return kReg256;
   return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
@@ -1172,6 +1204,38 @@ int device_cus() {
 }
 
 }  // namespace
+
+WeightClasses weight_classes(const FfnArgs& a) {
+  WeightClasses wc{};
+  if (a.w_dtype != 3) {
+    wc.n = 1;
+    wc.wf[0] = a.w_dtype == 2 ? kWE4m3 : kWBf16;
+    return wc;
+  }
+  const int G = a.n_routed + a.n_shared;
+  uint32_t m4[9] = {};
+  bool any8 = false, any4 = false;
+  for (int g = 0; g < G; ++g) {
+    const int b = g < a.n_routed ? a.w_bits[g] : a.sw_bits[g - a.n_routed];
+    if (b == 4) {
+      m4[g >> 5] |= 1u << (g & 31);
+      any4 = true;
+    } else {
+      any8 = true;
+    }
+  }
+  if (any8) {
+    wc.wf[wc.n] = kWInt8;
+    for (int i = 0; i < 9; ++i) wc.skip[wc.n][i] = m4[i];
+    ++wc.n;
+  }
+  if (any4) {
+    wc.wf[wc.n] = kWInt4;
+    for (int i = 0; i < 9; ++i) wc.skip[wc.n][i] = ~m4[i];
+    ++wc.n;
+  }
+  return wc;
+}
 
 FfnPlan ffn_plan(const FfnArgs& a) {
   const int G = a.n_routed + a.n_shared;
@@ -1209,8 +1273,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.gather && f32) return hipErrorInvalidValue;  // the fp32 tiles read routed rows from x_perm only
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
-  const bool fp8 = (a.w_dtype == 2);
   const bool swi = (a.act == 1);
+  // integer weights: one launch per bit width present, each skipping the other width's groups
+  const WeightClasses wc = weight_classes(a);
 
   GemmParams p{};
   p.split_part = a.split_part;
@@ -1235,6 +1300,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   p.scale_r = a.w_scale;
   p.scale_s = a.sw_scale;
   p.scale_col = 0;
+  p.scale_pitch = static_cast<int32_t>(2 * a.d_ff + a.d);
+  p.scale_row0 = 0;
+  p.scale_row3 = static_cast<int32_t>(a.d_ff);
   p.C_r = a.h;
   p.C_s = a.h;
   p.ldc = a.ld_h;
@@ -1244,10 +1312,11 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   stage_mark(kStageFfnUp, false, s);
   if (f32) {
     err = swi ? run_f32<EPI_SWIGLU>(p, max_mtiles, s) : run_f32<EPI_GELU>(p, max_mtiles, s);
-  } else if (swi) {
-    err = fp8 ? run_cfg<EPI_SWIGLU, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_SWIGLU, false>(cfg, p, max_mtiles, s);
   } else {
-    err = fp8 ? run_cfg<EPI_GELU, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_GELU, false>(cfg, p, max_mtiles, s);
+    for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
+      for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
+      err = swi ? run_wf<EPI_SWIGLU>(wc.wf[c], cfg, p, max_mtiles, s) : run_wf<EPI_GELU>(wc.wf[c], cfg, p, max_mtiles, s);
+    }
   }
   stage_mark(kStageFfnUp, true, s);
   if (err != hipSuccess) return err;
@@ -1266,6 +1335,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   p.b_stride = a.d * a.ld_down;
   p.bias = swi ? nullptr : a.b2;
   p.scale_col = 2;
+  p.scale_row0 = static_cast<int32_t>(2 * a.d_ff);
+  p.scale_row3 = 0;
   p.C_r = a.y_perm;
   p.C_s = a.y_shared;
   p.ldc = a.d;
@@ -1276,7 +1347,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   if (f32) {
     err = run_f32<EPI_PLAIN>(p, max_mtiles, s);
   } else {
-    err = fp8 ? run_cfg<EPI_PLAIN, true>(cfg, p, max_mtiles, s) : run_cfg<EPI_PLAIN, false>(cfg, p, max_mtiles, s);
+    for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
+      for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
+      err = run_wf<EPI_PLAIN>(wc.wf[c], cfg, p, max_mtiles, s);
+    }
   }
   stage_mark(kStageFfnDown, true, s);
   return err;

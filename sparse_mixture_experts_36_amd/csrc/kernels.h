@@ -119,7 +119,19 @@ struct FfnArgs {
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
   float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null
   bool planned;               // groups, tile_start and active are already written (by the permutation)
+  const uint8_t* w_bits;      // integer weights (w_dtype 3): HOST [n_routed], 8 or 4
+  const uint8_t* sw_bits;     // HOST [n_shared]
 };
+
+// Launch classes of a layer's weights: one for bf16 / e4m3 / uniform integer
+// widths, two for mixed 8- and 4-bit experts (each launch skips, by group bit,
+// the groups of the other width).
+struct WeightClasses {
+  int n;
+  int wf[2];
+  uint32_t skip[2][9];
+};
+WeightClasses weight_classes(const FfnArgs& a);
 // The group plan the FFN launch would write for these arguments.
 FfnPlan ffn_plan(const FfnArgs& a);
 // fp32 floats of the prefill path's k-split partial tiles: 256 tiles of 256 x 256

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_mixture_experts_36_amd as moe
@@ -90,6 +91,27 @@ def test_expert_choice_capacity_is_the_pages_int():
     # int(num_tokens * capacity_factor / num_experts)
     for T, N, cf in [(4096, 8, 2.0), (8192, 160, 6.0), (256, 8, 2.0), (10, 3, 1.0), (100, 7, 1.25)]:
         assert moe.capacity(T, 1, N, cf) == int(T * cf / N)
+
+
+def test_int_weights_shapes_and_packing():
+    n = ctypes.c_size_t()
+    ok = _shape(w_dtype=moe.INT_W)
+    assert moe.lib().moe_workspace_size(ctypes.byref(ok), moe.ENTRY_FORWARD, ctypes.byref(n)) == moe.MOE_OK
+    bad = _shape(w_dtype=moe.INT_W, act_dtype=moe.F32)
+    assert moe.lib().moe_workspace_size(ctypes.byref(bad), moe.ENTRY_FORWARD, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    # byte rows: 8-bit experts verbatim, 4-bit experts two codes a byte (low nibble first)
+    rng = np.random.default_rng(0)
+    codes = np.concatenate([rng.integers(-127, 128, (1, 3, 8)), rng.integers(-7, 8, (2, 3, 8))]).astype(np.int8)
+    packed = moe.pack_int_weights(codes, [8, 4, 4], pad=4)
+    assert packed.shape == (3, 3, 12) and packed.dtype == np.uint8
+    assert np.array_equal(packed[0, :, :8].view(np.int8), codes[0])
+    for e in (1, 2):
+        lo = (packed[e, :, :4] & 0x0F).astype(np.int8)
+        hi = (packed[e, :, :4] >> 4).astype(np.int8)
+        lo[lo > 7] -= 16
+        hi[hi > 7] -= 16
+        assert np.array_equal(lo, codes[e, :, 0::2]) and np.array_equal(hi, codes[e, :, 1::2])
+        assert (packed[e, :, 4:] == 0).all()
 
 
 def test_workspace_sizes_grow_with_entry():

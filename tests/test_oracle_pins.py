@@ -30,6 +30,14 @@ def _weights64(inp, shared=False):
         w1, w3, w2, sc = inp.sw1, inp.sw3, inp.sw2, inp.sw_scale
     else:
         w1, w3, w2, sc = inp.w1, inp.w3, inp.w2, inp.w_scale
+    if wl.w_dtype == gen.INT_W:
+        # codes times one fp32 scale per weight row: W1 rows, W3 rows, W2 rows
+        f = wl.d_ff
+        s = torch.from_numpy(sc.astype(np.float64))
+        W1 = torch.from_numpy(w1.astype(np.float64)) * s[:, :f, None]
+        W3 = torch.from_numpy(w3.astype(np.float64)) * s[:, f:2 * f, None] if w3 is not None else None
+        W2 = torch.from_numpy(w2.astype(np.float64)) * s[:, 2 * f:, None]
+        return W1, W3, W2
     W1, W2 = _t64(w1, wl.w_dtype), _t64(w2, wl.w_dtype)
     W3 = _t64(w3, wl.w_dtype) if w3 is not None else None
     if wl.w_dtype == gen.E4M3:
@@ -50,9 +58,9 @@ def _dense_expert(wl, W1, W3, W2, b1, b2, e, X):
 
 
 def _tiny(act, gating, w_dtype=gen.F32, act_dtype=gen.F32, T=48, d=32, d_ff=64, N=8, k=2, cf=None,
-          n_shared=0, zipf=None):
+          n_shared=0, zipf=None, n_int8=None):
     return gen.Workload("tiny", T, d, d_ff, N, k, act, gating, act_dtype, w_dtype, cf, n_shared=n_shared,
-                        zipf_s=zipf)
+                        zipf_s=zipf, n_int8=N // 3 if n_int8 is None else n_int8)
 
 
 def _with_random_biases(inp, seed=5):
@@ -255,7 +263,8 @@ def test_capacity_formula_matches_pages_examples():
 
 @pytest.mark.parametrize("act,w_dtype,act_dtype", [(gen.GELU, gen.F32, gen.F32), (gen.SWIGLU, gen.BF16, gen.BF16),
                                                    (gen.GELU, gen.E4M3, gen.BF16), (gen.SWIGLU, gen.E4M3, gen.BF16),
-                                                   (gen.SWIGLU, gen.F32, gen.F32)])
+                                                   (gen.SWIGLU, gen.F32, gen.F32), (gen.SWIGLU, gen.INT_W, gen.BF16),
+                                                   (gen.GELU, gen.INT_W, gen.BF16)])
 def test_expert_rows_against_torch_fp64(act, w_dtype, act_dtype):
     wl = _tiny(act, gen.SOFTMAX_TOPK, w_dtype=w_dtype, act_dtype=act_dtype, T=24, d=48, d_ff=80, N=3, k=1)
     inp = _with_random_biases(gen.make_inputs(wl, seed=9))
@@ -313,6 +322,8 @@ def _brute_force_layer(inp, C, gating):
          act_dtype=gen.BF16, w_dtype=gen.BF16),
     dict(act=gen.GELU, gating=gen.SOFTMAX_TOPK, cf=1.25, N=8, k=1, zipf=1.2, act_dtype=gen.BF16,
          w_dtype=gen.E4M3),
+    dict(act=gen.SWIGLU, gating=gen.TOPK_SOFTMAX, cf=None, N=8, k=2, n_shared=1, act_dtype=gen.BF16,
+         w_dtype=gen.INT_W),
 ])
 def test_layer_output_brute_force_dense_then_mask(case):
     case = dict(case)
@@ -398,6 +409,38 @@ def test_combine_against_numpy_gather():
 
 
 # ---------------------------------------------------------------- the generator
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_int_rows_quantiser(bits):
+    """Integer rows against the fp32 draws of the same tensor: symmetric codes
+    within +-qmax, each row's largest weight on +-qmax, every weight within half
+    a step of its code times the row scale, ties rounded to even."""
+    rows, cols, qmax = 40, 96, (1 << (bits - 1)) - 1
+    q, s = gen.int_rows(gen.T_W1, (rows, cols), 0.3, bits, seed=4, offset=1000)
+    w = gen.normal(gen.T_W1, (rows, cols), 0.3, gen.F32, seed=4, offset=1000).astype(np.float64)
+    assert q.dtype == np.int8 and np.abs(q).max() <= qmax
+    amax = np.abs(w).max(1)
+    assert np.allclose(s, (amax / qmax).astype(np.float32), rtol=0, atol=0)
+    assert (np.abs(q).max(1) == qmax).all()
+    err = np.abs(w - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 1e-9)).all()
+    assert np.array_equal(q, np.clip(np.round(w / s[:, None].astype(np.float64)), -qmax, qmax).astype(np.int8))
+
+
+def test_int_workload_bits_and_scales_layout():
+    wl = _tiny(gen.SWIGLU, gen.SOFTMAX_TOPK, w_dtype=gen.INT_W, act_dtype=gen.BF16, d=64, d_ff=96, N=6,
+               n_shared=1, n_int8=2)
+    inp = gen.make_inputs(wl, seed=3)
+    assert inp.w_bits.tolist() == [8, 8, 4, 4, 4, 4] and inp.sw_bits.tolist() == [8]
+    assert inp.w_scale.shape == (6, 2 * 96 + 64) and inp.w1.dtype == np.int8
+    for e in range(6):
+        qmax = 127 if e < 2 else 7
+        for m in (inp.w1[e], inp.w3[e], inp.w2[e]):
+            assert np.abs(m).max() == qmax
+    # W3's scales are those of W3's own rows (tensor id 4), not W1's
+    q3, s3 = gen.int_rows(gen.T_W3, (96, 64), 1.0 / 8.0, 8, seed=3, offset=0)
+    assert np.array_equal(inp.w3[0], q3) and np.array_equal(inp.w_scale[0, 96:192], s3)
+
 
 def test_generator_is_counter_based_and_prefix_stable():
     a = gen.normal(gen.T_X, (64, 32), 1.0, gen.BF16)
