@@ -76,9 +76,12 @@ typedef enum {
  * expert has 8 or 4 bits (moe_weights.w_bits) and one fp32 scale per weight
  * row: W[r][c] = s_r * q[r][c], q symmetric two's complement. Expert matrices
  * keep byte rows (pitch ld_up / ld_down bytes, at least d / d_ff): an 8-bit
- * expert's row holds one int8 code per column, a 4-bit expert's row holds two
- * codes per byte in its first d/2 (d_ff/2) bytes, column 2i in the low nibble
- * of byte i and column 2i + 1 in the high nibble. Activations stay bf16. */
+ * expert's row holds one int8 code per column; a 4-bit expert's row holds its
+ * codes in its first d/2 (d_ff/2) bytes, each 8 consecutive columns 8m..8m+7
+ * as one little-endian 32-bit word with column 8m + 2j in bits [4j, 4j + 4)
+ * and column 8m + 2j + 1 in bits [16 + 4j, 20 + 4j), two's complement. (That
+ * order lets the kernels turn two codes into a bf16 pair with one shift and
+ * one and-or.) Activations stay bf16. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT_W = 3 } moe_dtype;
 
 /* Expert FFN. GELU: y = W2 gelu(W1 x + b1) + b2 with the exact erf GELU

@@ -257,9 +257,11 @@ def weights_struct(t: dict) -> Weights:
 def pack_int_weights(codes, bits, pad: int = 0):
     """Integer expert matrices in the library's layout: codes [E][rows][cols]
     (int8, one code per element) and bits [E] (8 or 4) -> uint8 [E][rows][cols
-    + pad] byte rows; an 8-bit expert's row holds its codes, a 4-bit expert's
-    row holds column 2i in the low nibble and 2i + 1 in the high nibble of byte
-    i (the rest of the row is zero). Host numpy in, host numpy out."""
+    + pad] byte rows. An 8-bit expert's row holds its codes. A 4-bit expert's
+    row holds cols/2 bytes: each 8 consecutive codes form one little-endian
+    32-bit word with code 8m + 2j in bits [4j, 4j + 4) and code 8m + 2j + 1 in
+    bits [16 + 4j, 20 + 4j) (two's complement nibbles); the rest of the row is
+    zero. Host numpy in, host numpy out."""
     import numpy as np
     codes = np.asarray(codes, np.int8)
     E, R, C = codes.shape
@@ -268,8 +270,12 @@ def pack_int_weights(codes, bits, pad: int = 0):
         if int(bits[e]) == 8:
             out[e, :, :C] = codes[e].view(np.uint8)
         else:
-            u = codes[e].view(np.uint8) & 0x0F
-            out[e, :, :C // 2] = u[:, 0::2] | (u[:, 1::2] << 4)
+            u = (codes[e].view(np.uint8) & 0x0F).astype(np.uint32).reshape(R, C // 8, 8)
+            word = np.zeros((R, C // 8), np.uint32)
+            for j in range(4):
+                word |= u[:, :, 2 * j] << (4 * j)
+                word |= u[:, :, 2 * j + 1] << (16 + 4 * j)
+            out[e, :, :C // 2] = word.astype("<u4").view(np.uint8).reshape(R, C // 2)
     return out
 
 

@@ -126,6 +126,7 @@ struct FfnWs {
   int32_t* active;
   float* part;
   float* split_part;
+  void* wdq;
 };
 FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
@@ -138,10 +139,13 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   w.part = nullptr;
   if (moe::use_skinny(s.act_dtype, routed_row_cap(s), s.n_shared, s.T))
     w.part = c.take<float>(
-        moe::skinny_part_floats(s.T, s.d, s.d_ff, s.n_experts, s.n_shared, s.act, routed_row_cap(s)));
+        moe::skinny_part_floats(s.T, s.d, s.d_ff, s.n_experts, s.n_shared, s.act, routed_row_cap(s), s.w_dtype));
   w.split_part = nullptr;
   if (moe::uses_prefill_gemm(s.act_dtype, s.w_dtype, routed_row_cap(s), s.n_shared, s.T))
     w.split_part = c.take<float>(static_cast<size_t>(moe::kSplitPartFloats));
+  w.wdq = nullptr;
+  if (moe::uses_int_dequant(s.act_dtype, s.w_dtype, routed_row_cap(s), s.n_shared, s.T))
+    w.wdq = c.take<char>(moe::dq_bytes(s.d, s.d_ff, s.n_experts, s.n_shared, s.act));
   return w;
 }
 
@@ -340,6 +344,7 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.split_part = fw.split_part;
   a.w_bits = w->w_bits;
   a.sw_bits = w->sw_bits;
+  a.wdq = fw.wdq;
   return a;
 }
 

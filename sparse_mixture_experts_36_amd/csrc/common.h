@@ -59,13 +59,32 @@ __device__ __forceinline__ uint2 int8x4_to_bf16x4(uint32_t w) {
   return make_uint2(pack_hi16(f0, f1), pack_hi16(f2, f3));
 }
 
-// Eight int4 codes (nibble i of w, from the least significant, is code i, two's
-// complement) -> eight bf16 values, exactly.
+// Eight int4 codes in one 32-bit word, two's complement: code 2j in bits
+// [4j, 4j + 4), code 2j + 1 in bits [16 + 4j, 16 + 4j + 4), j < 4. This order
+// puts codes 2j and 2j + 1 sixteen bits apart, where one shift and one
+// and-or turn them into a bf16 pair (int4x8_to_bf16x8_biased).
+
+// -> eight bf16 values, exactly, in code order.
 __device__ __forceinline__ uint4 int4x8_to_bf16x8(uint32_t w) {
   float f[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = static_cast<float>(static_cast<int32_t>(w << (28 - 4 * j)) >> 28);
+    f[2 * j + 1] = static_cast<float>(static_cast<int32_t>(w << (12 - 4 * j)) >> 28);
+  }
   return make_uint4(pack_hi16(f[0], f[1]), pack_hi16(f[2], f[3]), pack_hi16(f[4], f[5]), pack_hi16(f[6], f[7]));
+}
+
+// -> the eight bf16 values q + 136, in code order: flipping each nibble's sign
+// bit gives u = q + 8 in [0, 15], and 0x4300 | u is the bf16 of 128 + u
+// (exact: bf16 steps by 1 between 128 and 256). About one instruction per
+// weight; the caller subtracts 136 times the sum of the activations.
+constexpr float kInt4Bias = 136.f;
+constexpr uint32_t kInt4BiasPair = 0x43084308u;  // two bf16 136
+__device__ __forceinline__ uint4 int4x8_to_bf16x8_biased(uint32_t w) {
+  const uint32_t v = w ^ 0x88888888u;
+  return make_uint4((v & 0x000F000Fu) | 0x43004300u, ((v >> 4) & 0x000F000Fu) | 0x43004300u,
+                    ((v >> 8) & 0x000F000Fu) | 0x43004300u, ((v >> 12) & 0x000F000Fu) | 0x43004300u);
 }
 
 // D += A(16x32) * B(32x16), bf16 inputs, fp32 accumulation. Lane l supplies

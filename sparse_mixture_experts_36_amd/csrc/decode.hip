@@ -117,10 +117,16 @@ __device__ __forceinline__ uint4 as_bf16(const uint4& w) {
     const uint2 a = int8x4_to_bf16x4(w.x), b = int8x4_to_bf16x4(w.y);
     return make_uint4(a.x, a.y, b.x, b.y);
   } else if constexpr (WF == kWInt4) {
-    return int4x8_to_bf16x8(w.x);
+    return int4x8_to_bf16x8_biased(w.x);  // q + 136: the kernels subtract 136 * sum(x)
   } else {
     return w;
   }
+}
+
+// MFMA B operand of bf16 136 in every element: A times it is 136 * sum(x) per
+// token row, the correction of the biased int4 products.
+__device__ __forceinline__ uint4 int4_bias_b() {
+  return make_uint4(kInt4BiasPair, kInt4BiasPair, kInt4BiasPair, kInt4BiasPair);
 }
 
 // Whether group g is left to another launch (integer weights of the other bit width).
@@ -228,10 +234,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
       aoff[rb] = static_cast<uint32_t>((src * static_cast<int>(lda) + q * QK) * 2);
     }
     floatx4_t acc[RB][FN];
+    floatx4_t accc[RB];  // int4: 136 * sum(x) of each token row (the bias of the decoded codes)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+      accc[rb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[rb][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     if constexpr (SHARED_A) {
       // DMA instruction i of wave v fills bytes [1024 (v ADMA + i), +1024) of
@@ -287,6 +296,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(av[rb], b, acc[rb][j]);
             }
+            if constexpr (WF == kWInt4) {
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) accc[rb] = mfma16x16x32(av[rb], int4_bias_b(), accc[rb]);
+            }
           }
       };
       for (int st = 0; st < nsteps; st += 2 * KU) {
@@ -312,15 +325,26 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
       for (int u = 0; u < KU; ++u) {
         if (st + u >= nsteps) break;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const uint4 b = as_bf16<WF>(bw[u][j][t]);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(a[u][rb][t], b, acc[rb][j]);
           }
+          if constexpr (WF == kWInt4) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) accc[rb] = mfma16x16x32(a[u][rb][t], int4_bias_b(), accc[rb]);
+          }
+        }
       }
     }
+    }
+    if constexpr (WF == kWInt4) {  // remove the bias: sum((q + 136) x) - 136 sum(x)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[rb][j] -= accc[rb];
     }
 
     // tile j, lane (q, c16): rows r0 + rb*16 + 4q + i, weight row n of tile j
@@ -469,10 +493,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
   const uint32_t al = static_cast<uint32_t>(lane) * 16 * XW;
 
   float acc[NR][R];
+  float accc[R];  // int4: 136 * sum(x) over the lane's k (the bias of the decoded codes)
 #pragma unroll
-  for (int j = 0; j < NR; ++j)
+  for (int r = 0; r < R; ++r) {
+    accc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[j][r] = 0.f;
+    for (int j = 0; j < NR; ++j) acc[j][r] = 0.f;
+  }
 
   for (int s0 = 0; s0 < nseg; s0 += U) {
     uint4 wv[U][NR], xv[U][R][XW];
@@ -491,6 +518,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u >= nseg) break;
+      if constexpr (WF == kWInt4) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float c = accc[r];
+#pragma unroll
+          for (int x = 0; x < XW; ++x) {
+            const uint32_t xd[4] = {xv[u][r][x].x, xv[u][r][x].y, xv[u][r][x].z, xv[u][r][x].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kInt4BiasPair),
+                                                  __builtin_bit_cast(bf16x2, xd[i]), c, false);
+          }
+          accc[r] = c;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         uint32_t wd[4 * XW];
@@ -506,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
           const uint32_t q4[4] = {wv[u][j].x, wv[u][j].y, wv[u][j].z, wv[u][j].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint4 b = int4x8_to_bf16x8(q4[i]);
+            const uint4 b = int4x8_to_bf16x8_biased(q4[i]);  // q + 136
             wd[4 * i] = b.x;
             wd[4 * i + 1] = b.y;
             wd[4 * i + 2] = b.z;
@@ -538,6 +580,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc[j][r] += __shfl_xor(acc[j][r], o);
+  if constexpr (WF == kWInt4) {  // remove the bias: sum((q + 136) x) - 136 sum(x)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) accc[r] += __shfl_xor(accc[r], o);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j][r] -= accc[r];
+    }
+  }
 
   // lane c < cols writes output column n0 + c of each row
 #pragma unroll
@@ -561,11 +612,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
 // than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
 // which is more than HBM latency times bandwidth needs) and every split keeps
 // at least two 128-wide k-steps. Fewer splits means less partial traffic and,
-// at one split, no reduction pass.
-int pick_splits(int64_t K, int64_t blocks_touched) {
+// at one split, no reduction pass. Integer weights aim at 4096 waves: a wave
+// then has fewer bytes in flight per k-step and decodes the codes on the
+// vector ALUs, which other waves on the SIMD must cover.
+int pick_splits(int64_t K, int64_t blocks_touched, bool intw) {
   const int64_t steps = K / KC;
+  const int64_t target = intw ? 4096 : 1024;
   int s = 1;
-  while (blocks_touched * s < 1024 && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
+  while (blocks_touched * s < target && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
   return s;
 }
 
@@ -591,7 +645,8 @@ hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hip
   } else if (deep) {
     MOE_STREAM_LAUNCH(1, 4, false)
   } else if (rb == 1) {
-    MOE_STREAM_LAUNCH(1, 2, false)
+    // integer codes: four k-steps a burst, so a wave keeps as many bytes in flight
+    if (wf == kWInt8 || wf == kWInt4) { MOE_STREAM_LAUNCH(1, 4, false) } else { MOE_STREAM_LAUNCH(1, 2, false) }
   } else if (rb == 2) {
     if (shared_a) { MOE_STREAM_LAUNCH(2, 2, true) } else { MOE_STREAM_LAUNCH(2, 2, false) }
   } else {
@@ -638,23 +693,24 @@ struct SplitPlan {
 };
 
 SplitPlan plan_splits(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
-                      int64_t cap) {
+                      int64_t cap, int32_t w_dtype) {
+  const bool intw = (w_dtype == 3);
   SplitPlan sp;
   const int64_t rows = cap + n_shared * T;
   sp.rb = rows <= 32 ? 1 : (rows <= 128 ? 2 : 4);
   // experts that can have rows: at most one per routed row, plus the shared ones
   const int64_t touched = (cap < n_routed ? cap : n_routed) + n_shared;
   const int64_t up_blocks = (act == 1 ? d_ff / 16 : d_ff / 32);
-  sp.up_splits = pick_splits(d, touched * up_blocks);
-  sp.down_splits = pick_splits(d_ff, touched * (d / 32));
+  sp.up_splits = pick_splits(d, touched * up_blocks, intw);
+  sp.down_splits = pick_splits(d_ff, touched * (d / 32), intw);
   return sp;
 }
 
 }  // namespace
 
 size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
-                          int64_t cap) {
-  const SplitPlan sp = plan_splits(T, d, d_ff, n_routed, n_shared, act, cap);
+                          int64_t cap, int32_t w_dtype) {
+  const SplitPlan sp = plan_splits(T, d, d_ff, n_routed, n_shared, act, cap, w_dtype);
   const int64_t rows = cap + n_shared * T;
   const int64_t up = sp.up_splits > 1 ? sp.up_splits * rows * (act == 1 ? 2 * d_ff : d_ff) : 0;
   const int64_t down = sp.down_splits > 1 ? sp.down_splits * rows * d : 0;
@@ -665,7 +721,7 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
                              hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
   const bool swi = (a.act == 1);
-  const SplitPlan sp = plan_splits(a.T, a.d, a.d_ff, a.n_routed, a.n_shared, a.act, a.routed_row_cap);
+  const SplitPlan sp = plan_splits(a.T, a.d, a.d_ff, a.n_routed, a.n_shared, a.act, a.routed_row_cap, a.w_dtype);
   StreamParams p{};
   p.n_routed = a.n_routed;
   p.n_groups = G;

@@ -54,6 +54,7 @@ struct GemmParams {
   int32_t scale_row0;     // integer weights: offset of this GEMM's matrix rows (W1 0, W2 2 d_ff)
   int32_t scale_row3;     // integer weights: offset of W3's rows (d_ff)
   uint32_t skip[9];       // bit g set: group g is left to another launch (its experts' other bit width)
+  int32_t col_scaled;     // 1: the bf16 weights are integer codes; output column n takes row scale n
   void* C_r;
   void* C_s;
   int64_t ldc;            // = Nout
@@ -443,6 +444,9 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
   const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+  // integer codes as bf16 weights: one scale per output column (weight row)
+  const float* rs = p.col_scaled ? (shared ? p.scale_s : p.scale_r) + static_cast<int64_t>(ew) * p.scale_pitch + n0
+                                 : nullptr;
   uint16_t* so = reinterpret_cast<uint16_t*>(stage);
   uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
@@ -460,13 +464,15 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
         for (int j = 0; j < FNO; ++j) {
           const int col = wn * WTO + j * 16 + c16;
           const float bv = bias ? bias[col] : 0.f;
+          const float sa = rs ? rs[p.scale_row0 + col] : 1.f;
+          const float sb = (rs && EPI == EPI_SWIGLU) ? rs[p.scale_row3 + col] : 1.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int srow = (i - i0) * 16 + q * 4 + r;  // row inside the staged part
             float v;
-            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + FN / 2][r];
-            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] + bv);
-            else v = acc[i][j][r] + bv;
+            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r] * sa) * (acc[i][j + FN / 2][r] * sb);
+            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] * sa + bv);
+            else v = acc[i][j][r] * sa + bv;
             so[srow * BNO + (((col >> 3) ^ (srow & 7)) << 3) + (col & 7)] = f32_to_bf16(v);
           }
         }
@@ -1079,6 +1085,60 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------ plan
+// Integer codes -> bf16 codes (exact), one wave per weight row: row r of
+// expert e's matrix (rows_e rows of `cols` codes at pitch ld_src bytes) goes
+// to bf16 row r at pitch ld_dst elements. 8-bit rows: 16 codes per lane and
+// step, 4-bit rows: 32.
+struct DequantArgs {
+  const char* src;
+  uint16_t* dst;
+  int64_t rows_e, cols, ld_src, ld_dst;
+  int32_t n_experts;
+  uint8_t bits[kMaxGroups];
+};
+
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t R = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (R >= a.rows_e * a.n_experts) return;
+  const int e = static_cast<int>(R / a.rows_e);
+  const char* src = a.src + R * a.ld_src;
+  uint16_t* dst = a.dst + R * a.ld_dst;
+  if (a.bits[e] == 8) {
+    for (int64_t c = lane * 16; c < a.cols; c += 64 * 16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(src + c);
+      const uint2 b0 = int8x4_to_bf16x4(q.x), b1 = int8x4_to_bf16x4(q.y);
+      const uint2 b2 = int8x4_to_bf16x4(q.z), b3 = int8x4_to_bf16x4(q.w);
+      *reinterpret_cast<uint4*>(dst + c) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+      *reinterpret_cast<uint4*>(dst + c + 8) = make_uint4(b2.x, b2.y, b3.x, b3.y);
+    }
+  } else {
+    for (int64_t c = lane * 32; c < a.cols; c += 64 * 32) {
+      const uint4 q = *reinterpret_cast<const uint4*>(src + c / 2);
+      *reinterpret_cast<uint4*>(dst + c) = int4x8_to_bf16x8(q.x);
+      *reinterpret_cast<uint4*>(dst + c + 8) = int4x8_to_bf16x8(q.y);
+      *reinterpret_cast<uint4*>(dst + c + 16) = int4x8_to_bf16x8(q.z);
+      *reinterpret_cast<uint4*>(dst + c + 24) = int4x8_to_bf16x8(q.w);
+    }
+  }
+}
+
+hipError_t launch_dequant(const void* src, void* dst, int64_t rows_e, int64_t cols, int64_t ld_src, int64_t ld_dst,
+                          int32_t n, const uint8_t* bits, hipStream_t s) {
+  if (!src || n <= 0) return hipSuccess;
+  DequantArgs a{};
+  a.src = static_cast<const char*>(src);
+  a.dst = static_cast<uint16_t*>(dst);
+  a.rows_e = rows_e;
+  a.cols = cols;
+  a.ld_src = ld_src;
+  a.ld_dst = ld_dst;
+  a.n_experts = n;
+  for (int e = 0; e < n; ++e) a.bits[e] = bits[e];
+  hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(ceil_div(rows_e * n, 4))), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, FfnPlan pl) {
   __shared__ int32_t s_mt[kMaxGroups];
   plan_groups(offsets, pl, s_mt, threadIdx.x, kThreads);
@@ -1186,7 +1246,7 @@ hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipS
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
   if (rows < 2048) return kReg128;
-  if (a.w_dtype == 2 || a.w_dtype == 3) return kReg256;
+  if (a.w_dtype == 2 || (a.w_dtype == 3 && !a.wdq)) return kReg256;
   return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
@@ -1205,9 +1265,16 @@ int device_cus() {
 
 }  // namespace
 
+bool swi_layer(const FfnArgs& a) { return a.act == 1; }
+
+size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act) {
+  const int64_t up = (act == 1 ? 2 : 1) * d_ff * (d + kActPad), down = d * (d_ff + kActPad);
+  return static_cast<size_t>((up + down) * (n_routed + n_shared) * 2);
+}
+
 WeightClasses weight_classes(const FfnArgs& a) {
   WeightClasses wc{};
-  if (a.w_dtype != 3) {
+  if (a.w_dtype != 3 || a.wdq) {
     wc.n = 1;
     wc.wf[0] = a.w_dtype == 2 ? kWE4m3 : kWBf16;
     return wc;
@@ -1252,7 +1319,8 @@ FfnPlan ffn_plan(const FfnArgs& a) {
   return pl;
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
+  FfnArgs a = a_in;
   const int G = a.n_routed + a.n_shared;
   if (G > kMaxGroups) return hipErrorInvalidValue;
   const bool f32 = (a.act_dtype == 0);
@@ -1274,10 +1342,42 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
   const bool swi = (a.act == 1);
+  // integer weights on the prefill tiles: every expert's codes to bf16 first
+  // (exact), then the bf16 tiles with the row scales per output column
+  const bool dq = (a.w_dtype == 3 && a.wdq);
+  if (dq) {
+    const int64_t ldu = a.d + kActPad, ldd = a.d_ff + kActPad;
+    const int64_t up_e = a.d_ff * ldu, down_e = a.d * ldd;  // bf16 elements per expert matrix
+    uint16_t* q = static_cast<uint16_t*>(a.wdq);
+    uint16_t* w1 = q;
+    uint16_t* w3 = w1 + a.n_routed * up_e;
+    uint16_t* w2 = w3 + (swi_layer(a) ? a.n_routed * up_e : 0);
+    uint16_t* sw1 = w2 + a.n_routed * down_e;
+    uint16_t* sw3 = sw1 + a.n_shared * up_e;
+    uint16_t* sw2 = sw3 + (swi_layer(a) ? a.n_shared * up_e : 0);
+    const int64_t lu = a.ld_up, ld = a.ld_down;  // code row pitches (bytes)
+    err = launch_dequant(a.w1, w1, a.d_ff, a.d, lu, ldu, a.n_routed, a.w_bits, s);
+    if (err == hipSuccess && swi_layer(a)) err = launch_dequant(a.w3, w3, a.d_ff, a.d, lu, ldu, a.n_routed, a.w_bits, s);
+    if (err == hipSuccess) err = launch_dequant(a.w2, w2, a.d, a.d_ff, ld, ldd, a.n_routed, a.w_bits, s);
+    if (err == hipSuccess) err = launch_dequant(a.sw1, sw1, a.d_ff, a.d, lu, ldu, a.n_shared, a.sw_bits, s);
+    if (err == hipSuccess && swi_layer(a))
+      err = launch_dequant(a.sw3, sw3, a.d_ff, a.d, lu, ldu, a.n_shared, a.sw_bits, s);
+    if (err == hipSuccess) err = launch_dequant(a.sw2, sw2, a.d, a.d_ff, ld, ldd, a.n_shared, a.sw_bits, s);
+    if (err != hipSuccess) return err;
+    a.w1 = w1;
+    a.w3 = swi_layer(a) ? w3 : nullptr;
+    a.w2 = w2;
+    a.sw1 = sw1;
+    a.sw3 = swi_layer(a) ? sw3 : nullptr;
+    a.sw2 = sw2;
+    a.ld_up = ldu;
+    a.ld_down = ldd;
+  }
   // integer weights: one launch per bit width present, each skipping the other width's groups
   const WeightClasses wc = weight_classes(a);
 
   GemmParams p{};
+  p.col_scaled = dq ? 1 : 0;
   p.split_part = a.split_part;
   p.ncu = device_cus();
   p.n_routed = a.n_routed;

@@ -121,7 +121,13 @@ struct FfnArgs {
   bool planned;               // groups, tile_start and active are already written (by the permutation)
   const uint8_t* w_bits;      // integer weights (w_dtype 3): HOST [n_routed], 8 or 4
   const uint8_t* sw_bits;     // HOST [n_shared]
+  void* wdq;                  // integer weights, prefill: workspace for every expert's codes as bf16 (dq_bytes), or null
 };
+// Integer weights on the prefill tiles: the codes of every expert are first
+// written out as bf16 (exact) into this many workspace bytes, with rows
+// kActPad elements longer than d / d_ff, and the bf16 tiles apply the row
+// scales per output column.
+size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act);
 
 // Launch classes of a layer's weights: one for bf16 / e4m3 / uniform integer
 // widths, two for mixed 8- and 4-bit experts (each launch skips, by group bit,
@@ -151,13 +157,21 @@ inline bool use_skinny(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shar
 }
 // whether a layer's FFN may take the bf16 prefill GEMM, which uses the k-split
 // partial tiles
+// whether an integer-weight layer's FFN dequantizes its codes for the bf16
+// prefill tiles (2048 rows or more; fewer run on tiles that decode in registers)
+inline bool uses_int_dequant(int32_t act_dtype, int32_t w_dtype, int64_t routed_row_cap, int32_t n_shared,
+                             int64_t T) {
+  return act_dtype == 1 && w_dtype == 3 && !use_skinny(act_dtype, routed_row_cap, n_shared, T) &&
+         routed_row_cap + n_shared * T >= 2048;
+}
 inline bool uses_prefill_gemm(int32_t act_dtype, int32_t w_dtype, int64_t routed_row_cap, int32_t n_shared,
                               int64_t T) {
-  return act_dtype == 1 && w_dtype == 1 && !use_skinny(act_dtype, routed_row_cap, n_shared, T);
+  return act_dtype == 1 && !use_skinny(act_dtype, routed_row_cap, n_shared, T) &&
+         (w_dtype == 1 || uses_int_dequant(act_dtype, w_dtype, routed_row_cap, n_shared, T));
 }
 // fp32 partial-sum floats the decode path needs (0 when no GEMM is split)
 size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
-                          int64_t cap);
+                          int64_t cap, int32_t w_dtype);
 hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
                              hipStream_t s);
 

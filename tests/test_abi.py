@@ -106,11 +106,13 @@ def test_int_weights_shapes_and_packing():
     assert packed.shape == (3, 3, 12) and packed.dtype == np.uint8
     assert np.array_equal(packed[0, :, :8].view(np.int8), codes[0])
     for e in (1, 2):
-        lo = (packed[e, :, :4] & 0x0F).astype(np.int8)
-        hi = (packed[e, :, :4] >> 4).astype(np.int8)
-        lo[lo > 7] -= 16
-        hi[hi > 7] -= 16
-        assert np.array_equal(lo, codes[e, :, 0::2]) and np.array_equal(hi, codes[e, :, 1::2])
+        # one little-endian word per 8 codes: code 2j in bits 4j.., code 2j + 1 in bits 16 + 4j..
+        word = packed[e, :, :4].copy().view("<u4")[:, 0]
+        for j in range(4):
+            for c, shift in ((2 * j, 4 * j), (2 * j + 1, 16 + 4 * j)):
+                v = ((word >> shift) & 0xF).astype(np.int8)
+                v[v > 7] -= 16
+                assert np.array_equal(v, codes[e, :, c])
         assert (packed[e, :, 4:] == 0).all()
 
 
