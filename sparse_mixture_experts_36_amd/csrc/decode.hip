@@ -625,6 +625,7 @@ int pick_splits(int64_t K, int64_t blocks_touched, bool intw) {
 
 hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hipStream_t s) {
   const int64_t waves = blocks * p.splits;
+  if (waves <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
   // 32 or 64 token rows: shared through LDS when the passes hold whole burst pairs
   const bool pairs = (p.K / p.splits / KC) % 4 == 0;
@@ -671,6 +672,7 @@ hipError_t run_gemv(const StreamParams& p, int rows, int wf, int64_t slots, hipS
   const bool swi = (p.epi == 1);
   const int nr = slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4;
   const int64_t waves = slots * p.Nout / (swi ? nr / 2 : nr);
+  if (waves <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
 #define MOE_GEMV_LAUNCH(R, NR, U)                                                                          \
   switch (wf) {                                                                                            \

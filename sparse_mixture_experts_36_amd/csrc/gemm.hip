@@ -1323,6 +1323,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   FfnArgs a = a_in;
   const int G = a.n_routed + a.n_shared;
   if (G > kMaxGroups) return hipErrorInvalidValue;
+  if (a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T == 0) return hipSuccess;  // no rows at all
   const bool f32 = (a.act_dtype == 0);
   const int cfg = pick_cfg(a);
   const FfnPlan pl = ffn_plan(a);

@@ -146,6 +146,34 @@ def test_forward_is_deterministic():
         assert torch.equal(sa[k], b.stats[k]), k
 
 
+def test_forward_shared_experts_from_two_streams():
+    """Shared experts run on the library's side stream, forked from and joined
+    to the caller's stream. Two layers called back to back on two different
+    streams, with no synchronisation between the calls, must each give the
+    result of a call made alone."""
+    import torch
+    wa = gen.FINE_GRAINED.with_(T=512, d=512, d_ff=256)
+    wb = gen.FINE_GRAINED.with_(T=96, d=512, d_ff=256, n_shared=1)
+    ia, ib = gen.make_inputs(wa, seed=3), gen.make_inputs(wb, seed=4)
+    la = moe.MoELayer(shape_of(wa), device_weights(ia))
+    lb = moe.MoELayer(shape_of(wb), device_weights(ib))
+    xa, xb = dev(ia.x), dev(ib.x)
+    ya, yb = la(xa).y.clone(), lb(xb).y.clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        la.out.y.zero_()
+        lb.out.y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            la(xa, stream=s1)
+        with torch.cuda.stream(s2):
+            lb(xb, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(la.out.y.view(torch.int16), ya.view(torch.int16))
+        assert torch.equal(lb.out.y.view(torch.int16), yb.view(torch.int16))
+
+
 # ---------------------------------------------------------------- full sizes, sampled tokens
 
 def test_full_tiny_gelu_fp32():
