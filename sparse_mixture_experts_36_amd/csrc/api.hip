@@ -154,26 +154,6 @@ FfnWs carve_ffn(Carver& c, const moe_shape& s) {
   return carve_ffn_for(c, s, s.n_experts, s.n_shared, routed_row_cap(s));
 }
 
-// moe_forward runs the shared experts on a second stream, concurrently with
-// routing, dispatch and the routed experts (starphix "Parallelism", the
-// shared experts computed while the dispatch is in flight): each launch set
-// then has workspace of its own.
-bool fwd_overlaps(const moe_shape& s) { return s.n_shared > 0; }
-
-struct FwdFfnWs {
-  FfnWs routed, shared;  // shared unused without overlap
-};
-FwdFfnWs carve_fwd_ffn(Carver& c, const moe_shape& s) {
-  FwdFfnWs w{};
-  if (!fwd_overlaps(s)) {
-    w.routed = carve_ffn(c, s);
-    return w;
-  }
-  w.routed = carve_ffn_for(c, s, s.n_experts, 0, routed_row_cap(s));
-  w.shared = carve_ffn_for(c, s, 0, s.n_shared, 0);
-  return w;
-}
-
 struct FwdWs {
   float* logits;
   int32_t *topk_idx, *inv_map, *offsets, *perm_token;
@@ -219,7 +199,7 @@ size_t ws_bytes_for(const moe_shape& s, int32_t entry) {
     default:
       carve_route(c, s);
       carve_perm(c, s);
-      carve_fwd_ffn(c, s);
+      carve_ffn(c, s);
       carve_fwd(c, s);
       break;
   }
@@ -371,38 +351,6 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.sw_bits = w->sw_bits;
   a.wdq = fw.wdq;
   return a;
-}
-
-// ---------------------------------------------------------------- side stream
-// One per device, created on first use (default priority), with the two
-// events of the fork and the join. Enqueueing a forward that uses them holds
-// side_mutex(), so that the events' records and waits of concurrent callers do
-// not interleave.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-std::mutex& side_mutex() {
-  static std::mutex m;
-  return m;
-}
-// The current device's side stream, or null when it cannot be created (the
-// shared experts then run on the caller's stream). Call with side_mutex() held.
-SideStream* side_stream() {
-  static SideStream ss[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& x = ss[dev];
-  if (!x.s && !x.failed) {
-    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
-      x.failed = true;
-      (void)hipGetLastError();
-    }
-  }
-  return x.failed ? nullptr : &x;
 }
 
 // ---------------------------------------------------------------- stage timing
@@ -602,8 +550,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   Carver c{static_cast<char*>(ws)};
   const RouteWs rw = carve_route(c, s);
   const PermWs pw = carve_perm(c, s);
-  const FwdFfnWs fws = carve_fwd_ffn(c, s);
-  const FfnWs& fw = fws.routed;
+  const FfnWs fw = carve_ffn(c, s);
   const FwdWs w = carve_fwd(c, s);
   const int64_t ld_xp = s.d + moe::kActPad;  // the internal x_perm has a padded row pitch
   if (!logits) logits = w.logits;
@@ -614,33 +561,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   if (!perm_token) perm_token = w.perm_token;
 
   const bool gather = fwd_gathers(s);  // then the permutation copies no rows
-  std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
-  SideStream* side = nullptr;
-  hipError_t e = hipSuccess;
-  if (fwd_overlaps(s)) {
-    side_lock.lock();
-    side = side_stream();
-  }
-  // with shared experts the FFN runs as two launch sets: routed, and shared
-  // (which needs only x, so it starts at once on the side stream)
-  const bool split = fwd_overlaps(s);
-  moe::FfnArgs fs{};
-  if (split) {
-    fs = ffn_args(s, nullptr, ld_xp, expert_offsets, x, weights, nullptr, w.y_shared, fws.shared);
-    fs.n_routed = 0;
-    fs.routed_row_cap = 0;
-  }
-  if (side) {
-    e = hipEventRecord(side->fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-    if (e == hipSuccess) e = moe::launch_grouped_ffn(fs, side->s);
-    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
-  }
-  if (e == hipSuccess)
-    e = moe::launch_route(
-        route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
+  hipError_t e = moe::launch_route(
+      route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
   moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
-  if (split) fa.n_shared = 0;
   moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
                                   ld_xp, stats, pw);
   if (gather) fa.gather = perm_token;
@@ -652,8 +575,6 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   }
   if (e == hipSuccess) e = moe::launch_permute(pa, stream);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);
-  if (e == hipSuccess && split && !side) e = moe::launch_grouped_ffn(fs, stream);  // no side stream: in order
-  if (e == hipSuccess && side) e = hipStreamWaitEvent(stream, side->join, 0);  // join before the combine
   if (e == hipSuccess) {
     moe::CombineArgs a{};
     a.T = s.T;

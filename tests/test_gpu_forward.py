@@ -147,10 +147,9 @@ def test_forward_is_deterministic():
 
 
 def test_forward_shared_experts_from_two_streams():
-    """Shared experts run on the library's side stream, forked from and joined
-    to the caller's stream. Two layers called back to back on two different
+    """Two layers with shared experts called back to back on two different
     streams, with no synchronisation between the calls, must each give the
-    result of a call made alone."""
+    result of a call made alone (the library keeps no state between calls)."""
     import torch
     wa = gen.FINE_GRAINED.with_(T=512, d=512, d_ff=256)
     wb = gen.FINE_GRAINED.with_(T=96, d=512, d_ff=256, n_shared=1)
