@@ -123,6 +123,8 @@ struct FfnWs {
   void* h;
   moe::GroupDesc* groups;
   int32_t* tile_start;
+  moe::GroupDesc* groups_t;
+  int32_t* tile_start_t;
   int32_t* active;
   float* part;
   float* split_part;
@@ -137,6 +139,8 @@ FfnWs carve_ffn_for(Carver& c, const moe_shape& s, int32_t n_routed, int32_t n_s
   w.h = c.take<char>(hrows * static_cast<size_t>(s.d_ff + moe::kActPad) * act_bytes(s.act_dtype));
   w.groups = c.take<moe::GroupDesc>(2 * G);
   w.tile_start = c.take<int32_t>(G + 1);
+  w.groups_t = c.take<moe::GroupDesc>(2 * G);
+  w.tile_start_t = c.take<int32_t>(G + 1);
   w.active = c.take<int32_t>(G + 1);
   w.part = nullptr;
   if (moe::use_skinny(s.act_dtype, cap, n_shared, s.T))
@@ -344,6 +348,8 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.y_shared = y_shared;
   a.groups = fw.groups;
   a.tile_start = fw.tile_start;
+  a.groups_t = fw.groups_t;
+  a.tile_start_t = fw.tile_start_t;
   a.active = fw.active;
   a.part = fw.part;
   a.split_part = fw.split_part;

@@ -1140,7 +1140,7 @@ hipError_t launch_dequant(const void* src, void* dst, int64_t rows_e, int64_t co
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, FfnPlan pl) {
-  __shared__ int32_t s_mt[kMaxGroups];
+  __shared__ int32_t s_mt[2 * kMaxGroups];
   plan_groups(offsets, pl, s_mt, threadIdx.x, kThreads);
 }
 
@@ -1315,7 +1315,13 @@ FfnPlan ffn_plan(const FfnArgs& a) {
   pl.n_shared = a.n_shared;
   pl.T = static_cast<int32_t>(a.T);
   pl.cap = a.routed_row_cap;
-  pl.bm = a.act_dtype == 0 ? 64 : tile_rows(pick_cfg(a));
+  const int cfg = a.act_dtype == 0 ? -1 : pick_cfg(a);
+  pl.bm = a.act_dtype == 0 ? 64 : tile_rows(cfg);
+  // 256-row tiles leave tails of at most 128 rows to 128-row tiles
+  pl.bm_t = (cfg == kDma256 && a.groups_t && a.tile_start_t) ? 128 : 0;
+  pl.up_t = a.groups_t;
+  pl.down_t = a.groups_t ? a.groups_t + G : nullptr;
+  pl.tile_start_t = a.tile_start_t;
   return pl;
 }
 
@@ -1418,6 +1424,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
       err = swi ? run_wf<EPI_SWIGLU>(wc.wf[c], cfg, p, max_mtiles, s) : run_wf<EPI_GELU>(wc.wf[c], cfg, p, max_mtiles, s);
     }
+    if (err == hipSuccess && pl.bm_t > 0) {  // the groups' short tails on 128-row tiles
+      GemmParams pt = p;
+      pt.groups = pl.up_t;
+      pt.tile_start = pl.tile_start_t;
+      err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, G, s) : run_dma<EPI_GELU, 128, 8>(pt, G, s);
+    }
   }
   stage_mark(kStageFfnUp, true, s);
   if (err != hipSuccess) return err;
@@ -1451,6 +1463,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
     for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
       err = run_wf<EPI_PLAIN>(wc.wf[c], cfg, p, max_mtiles, s);
+    }
+    if (err == hipSuccess && pl.bm_t > 0) {
+      GemmParams pt = p;
+      pt.groups = pl.down_t;
+      pt.tile_start = pl.tile_start_t;
+      err = run_dma<EPI_PLAIN, 128, 8>(pt, G, s);
     }
   }
   stage_mark(kStageFfnDown, true, s);

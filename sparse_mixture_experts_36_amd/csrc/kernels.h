@@ -61,6 +61,12 @@ struct FfnPlan {
   int32_t* tile_start;       // [G + 1] row-tile prefix
   int32_t* active;           // [1 + G] count, then the groups with rows
   int32_t n_routed, n_shared, T, cap, bm;
+  // tail tiles (bm_t > 0): a group whose last bm-row tile would hold at most
+  // bm_t rows leaves those rows to a second launch of bm_t-row tiles
+  GroupDesc* up_t;           // [G] the tails' up-GEMM groups
+  GroupDesc* down_t;         // [G]
+  int32_t* tile_start_t;     // [G + 1]
+  int32_t bm_t;
 };
 
 // ---------------------------------------------------------------- permute
@@ -115,6 +121,8 @@ struct FfnArgs {
   void* y_shared;             // [n_shared][T][d]
   GroupDesc* groups;          // [2][n_routed + n_shared] (workspace)
   int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
+  GroupDesc* groups_t;        // [2][n_routed + n_shared]: tail tiles' groups (workspace)
+  int32_t* tile_start_t;      // [n_routed + n_shared + 1] (workspace)
   int32_t* active;            // [1 + n_routed + n_shared]: count, then the groups with rows (workspace)
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
   float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null

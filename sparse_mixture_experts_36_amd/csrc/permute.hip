@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
   if (a.x_perm) return;
   __syncthreads();
   if (a.plan.up) {
-    __shared__ int32_t s_mt[kMaxGroups];
+    __shared__ int32_t s_mt[2 * kMaxGroups];
     plan_groups(s_off, a.plan, s_mt, tid, kThreads);
   }
   if (!live) return;
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(PermuteArgs a) {
 // when asked). Tokens taken by no expert are counted per block.
 __global__ __launch_bounds__(kThreads) void ec_permute_kernel(PermuteArgs a) {
   __shared__ int32_t s_off[kMaxN + 1];
-  __shared__ int32_t s_mt[kMaxGroups];
+  __shared__ int32_t s_mt[2 * kMaxGroups];
   __shared__ int32_t s_none[4];
   __shared__ int32_t s_rows[4][kMaxN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -11,9 +11,12 @@ namespace moe {
 // Routed expert e: rows [offsets[e], offsets[e+1]) of x_perm / h / y_perm,
 // clamped to the reserved routed rows. Shared expert s: the T token rows; its
 // hidden rows sit after the routed ones in h, its outputs in y_shared[s].
-// active[0] = the number of groups with rows, active[1..] those groups in
-// order. Run by all threads of one workgroup; s_mt holds n_routed + n_shared
-// ints of LDS. Ends with a workgroup barrier.
+// With bm_t > 0, a group whose last tile would hold r <= bm_t rows gives those
+// r rows to the tail plan (one bm_t-row tile, a second launch) and keeps the
+// rest: less padding in the last tile. active[0] = the number of groups with
+// rows, active[1..] those groups in order. Run by all threads of one
+// workgroup; s_mt holds 2 (n_routed + n_shared) ints of LDS. Ends with a
+// workgroup barrier.
 __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPlan& pl, int32_t* s_mt, int tid,
                                             int nthreads) {
   const int G = pl.n_routed + pl.n_shared;
@@ -34,6 +37,22 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
       u.rows = dn.rows = pl.T;
     }
     u.widx = dn.widx = g;
+    int tail = 0;
+    if (pl.bm_t > 0) {
+      const int rem = u.rows % pl.bm;
+      if (rem > 0 && rem <= pl.bm_t) tail = rem;
+      const int keep = u.rows - tail;
+      GroupDesc ut = u, dt = dn;
+      ut.a_row0 += keep;
+      ut.c_row0 += keep;
+      dt.a_row0 += keep;
+      dt.c_row0 += keep;
+      ut.rows = dt.rows = tail;
+      pl.up_t[g] = ut;
+      pl.down_t[g] = dt;
+      u.rows = dn.rows = keep;
+      s_mt[G + g] = tail > 0 ? 1 : 0;
+    }
     pl.up[g] = u;
     pl.down[g] = dn;
     s_mt[g] = (u.rows + pl.bm - 1) / pl.bm;
@@ -48,6 +67,13 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
     }
     pl.tile_start[G] = acc;
     pl.active[0] = n_active;
+  } else if (tid == 1 && pl.bm_t > 0) {
+    int32_t acc = 0;
+    for (int g = 0; g < G; ++g) {
+      pl.tile_start_t[g] = acc;
+      acc += s_mt[G + g];
+    }
+    pl.tile_start_t[G] = acc;
   }
   __syncthreads();
 }
