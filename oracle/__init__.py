@@ -67,9 +67,10 @@ def lib():
         L.orc_dispatch_ec.argtypes = [sp, vp, vp, vp, vp, vp]
         L.orc_moe_output_ec.argtypes = [sp, vp, wp, vp, vp, vp, i64, vp]
         L.orc_combine_ec.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.orc_backward.argtypes = [sp, vp, wp, vp, ctypes.c_double, ctypes.c_double] + [vp] * 11
         for name in ("orc_router_logits", "orc_route", "orc_dispatch", "orc_expert_rows",
                      "orc_moe_output", "orc_combine", "orc_route_ec", "orc_dispatch_ec", "orc_moe_output_ec",
-                     "orc_combine_ec", "orc_abi_version", "orc_threads"):
+                     "orc_combine_ec", "orc_backward", "orc_abi_version", "orc_threads"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("orc_bf16_value", "orc_gelu", "orc_silu"):
             getattr(L, name).restype = ctypes.c_double
@@ -293,6 +294,41 @@ def forward(inp, tokens: np.ndarray | None = None, logits32: np.ndarray | None =
         dsp = dispatch(shape, r.topk_idx)
         y = moe_output(shape, inp.x, inp, r, dsp, tokens)
     return Forward(l64, l32, r, dsp, np.asarray(tokens, np.int64), y)
+
+
+@dataclass
+class Grads:
+    dx: np.ndarray            # [T, d]
+    dWr: np.ndarray           # [N, d]
+    dbr: np.ndarray           # [N]
+    dW1: np.ndarray           # [N, d_ff, d]
+    dW3: np.ndarray | None
+    dW2: np.ndarray           # [N, d, d_ff]
+    db1: np.ndarray | None    # GELU
+    db2: np.ndarray | None
+    dsW1: np.ndarray | None   # shared experts
+    dsW3: np.ndarray | None
+    dsW2: np.ndarray | None
+
+
+def backward(inp, dy: np.ndarray, c_aux: float = 0.0, c_z: float = 0.0) -> Grads:
+    """Gradients of sum <dy, y> + c_aux L_aux + c_z z with respect to x and
+    every parameter (fp64), routing decisions held fixed."""
+    wl = inp.wl
+    shape = shape_of(wl)
+    w, _keep = weights_of(inp)
+    T, d, f, N, S = wl.T, wl.d, wl.d_ff, wl.n_experts, wl.n_shared
+    swi = wl.act == 1
+    g = Grads(np.empty((T, d)), np.empty((N, d)), np.empty(N), np.empty((N, f, d)),
+              np.empty((N, f, d)) if swi else None, np.empty((N, d, f)),
+              None if swi else np.empty((N, f)), None if swi else np.empty((N, d)),
+              np.empty((S, f, d)) if S else None, np.empty((S, f, d)) if (S and swi) else None,
+              np.empty((S, d, f)) if S else None)
+    dy = np.ascontiguousarray(dy)
+    _check(lib().orc_backward(ctypes.byref(shape), _p(inp.x), ctypes.byref(w), _p(dy), c_aux, c_z, _p(g.dx),
+                              _p(g.dWr), _p(g.dbr), _p(g.dW1), _p(g.dW3), _p(g.dW2), _p(g.db1), _p(g.db2),
+                              _p(g.dsW1), _p(g.dsW3), _p(g.dsW2)), "backward")
+    return g
 
 
 def threads() -> int:

@@ -636,6 +636,243 @@ int orc_combine_ec(const OrcShape* s, const void* y_perm, const int32_t* inv_map
   return 0;
 }
 
+// ---------------------------------------------------------------- backward
+// Gradients of the token-choice layer [AIG y/g equation, `MoE` module and L_aux
+// equation; SPX "Key Equations", "Load Balancing (Critical)" z_loss; MOEA
+// "Expert Network Design"], for the scalar
+//   loss = sum_t <dy_t, y_t> + c_aux * L_aux + c_z * z
+// (dy is the gradient arriving at the layer output). The routing decision
+// (which experts, which pairs the capacity keeps) is held fixed and the fp32
+// rounding of the logits passes gradients through unchanged; everything else
+// is differentiated exactly in fp64:
+//  combine   dY_e[r] = g * dy_t for kept pair (t, j -> e, row r); dg_tj = <dy_t, E_e(x_t)>;
+//            shared experts: dY = dy
+//  expert    dH = dY W2;  dW2 += dY^T H;  db2 += sum dY
+//            SwiGLU: dU = dH * V * silu'(U), dV = dH * silu(U); GELU: dU = dH * gelu'(U)
+//            dW1 += dU^T X;  dW3 += dV^T X;  db1 += sum dU;  dx += dU W1 (+ dV W3)
+//  gates     mode 0: dp_S += dg;  mode 1: g = p_S / s -> dp_S += (dg - <dg, g>) / s;
+//            mode 2: dl_S += g * (dg - <dg, g>)
+//  L_aux     f is a count (no gradient); P_e = mean_t p_te -> dp_te += c_aux alpha N f_e / T
+//  z         z = (mean_t lse_t)^2 -> dl_te += c_z 2 mean(lse) / T * p_te
+//  softmax   dl += p * (dp - <dp, p>)
+//  router    dW_r += dl^T x;  db_r += sum_t dl;  dx += dl W_r
+// Outputs (fp64, any may be null except dx): dx [T][d], dWr [N][d], dbr [N],
+// dW1 / dW3 [N][d_ff][d], dW2 [N][d][d_ff], db1 [N][d_ff], db2 [N][d], and the
+// shared experts' dsW1 / dsW3 [S][d_ff][d], dsW2 [S][d][d_ff].
+int orc_backward(const OrcShape* s, const void* x, const OrcWeights* w, const void* dy, double c_aux, double c_z,
+                 double* dx, double* dWr, double* dbr, double* dW1, double* dW3, double* dW2, double* db1,
+                 double* db2, double* dsW1, double* dsW3, double* dsW2) {
+  if (!shape_ok_tc(s) || !x || !w || !w->w_router || !dy || !dx) return -1;
+  if (s->w_dtype >= 2) return -1;  // gradients of fp32 / bf16 weights only
+  const int64_t T = s->T, d = s->d, f = s->d_ff, N = s->n_experts, k = s->top_k, S = s->n_shared;
+  const bool swi = (s->act == 1);
+
+  // forward decisions and values
+  std::vector<double> l64(static_cast<size_t>(T * N));
+  std::vector<float> l32(static_cast<size_t>(T * N));
+  orc_router_logits(s, x, w, l64.data(), l32.data());
+  std::vector<int32_t> idx(static_cast<size_t>(T * k));
+  std::vector<double> gate(static_cast<size_t>(T * k)), p(static_cast<size_t>(T * N)), lse(static_cast<size_t>(T));
+  std::vector<int64_t> counts(static_cast<size_t>(N));
+  orc_route(s, l32.data(), idx.data(), gate.data(), p.data(), lse.data(), nullptr, nullptr, counts.data(), nullptr,
+            nullptr, nullptr, nullptr, nullptr);
+  std::vector<int32_t> inv(static_cast<size_t>(T * k));
+  orc_dispatch(s, idx.data(), nullptr, nullptr, nullptr, inv.data(), nullptr);
+
+  for (int64_t i = 0; i < T * d; ++i) dx[i] = 0.0;
+  std::vector<double> dg(static_cast<size_t>(T * k), 0.0);
+  auto zero = [](double* a, int64_t n) { if (a) for (int64_t i = 0; i < n; ++i) a[i] = 0.0; };
+  zero(dWr, N * d); zero(dbr, N); zero(dW1, N * f * d); zero(dW3, N * f * d); zero(dW2, N * d * f);
+  zero(db1, N * f); zero(db2, N * d); zero(dsW1, S * f * d); zero(dsW3, S * f * d); zero(dsW2, S * d * f);
+
+  // one expert over rows X [n][d] with output gradients dY [n][d]: parameter
+  // gradients into gW1/gW3/gW2/gb1/gb2 (may be null), input gradients into dX,
+  // and the expert's outputs into Yout (may be null)
+  auto expert_bwd = [&](bool shared, int e, const std::vector<double>& X, const std::vector<double>& dY, int64_t n,
+                        double* gW1, double* gW3, double* gW2, double* gb1, double* gb2, std::vector<double>& dX) {
+    const void* W1 = shared ? w->sw1 : w->w1;
+    const void* W3 = shared ? w->sw3 : w->w3;
+    const void* W2 = shared ? w->sw2 : w->w2;
+    const float* b1 = shared ? nullptr : w->b1;
+    const int64_t base1 = static_cast<int64_t>(e) * f * d, base2 = static_cast<int64_t>(e) * d * f;
+    auto w1 = [&](int64_t i, int64_t j) { return elem(W1, s->w_dtype, base1 + i * d + j, 1.0); };
+    auto w3 = [&](int64_t i, int64_t j) { return elem(W3, s->w_dtype, base1 + i * d + j, 1.0); };
+    auto w2 = [&](int64_t o, int64_t i) { return elem(W2, s->w_dtype, base2 + o * f + i, 1.0); };
+    std::vector<double> U(static_cast<size_t>(n * f)), V(static_cast<size_t>(n * f)), H(static_cast<size_t>(n * f));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < f; ++i)
+      for (int64_t r = 0; r < n; ++r) {
+        double u = 0.0, v = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+          u += w1(i, j) * X[r * d + j];
+          if (swi) v += w3(i, j) * X[r * d + j];
+        }
+        if (!swi && b1) u += static_cast<double>(b1[static_cast<int64_t>(e) * f + i]);
+        U[r * f + i] = u;
+        V[r * f + i] = v;
+        H[r * f + i] = swi ? silu(u) * v : gelu(u);
+      }
+    // dH = dY W2, dW2 += dY^T H, db2 += sum dY
+    std::vector<double> dH(static_cast<size_t>(n * f), 0.0);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < f; ++i)
+      for (int64_t r = 0; r < n; ++r) {
+        double a = 0.0;
+        for (int64_t o = 0; o < d; ++o) a += dY[r * d + o] * w2(o, i);
+        dH[r * f + i] = a;
+      }
+    if (gW2)
+#pragma omp parallel for schedule(static)
+      for (int64_t o = 0; o < d; ++o)
+        for (int64_t i = 0; i < f; ++i) {
+          double a = 0.0;
+          for (int64_t r = 0; r < n; ++r) a += dY[r * d + o] * H[r * f + i];
+          gW2[base2 + o * f + i] += a;
+        }
+    if (gb2)
+      for (int64_t o = 0; o < d; ++o)
+        for (int64_t r = 0; r < n; ++r) gb2[static_cast<int64_t>(e) * d + o] += dY[r * d + o];
+    // activation backward
+    std::vector<double> dU(static_cast<size_t>(n * f)), dV(static_cast<size_t>(n * f), 0.0);
+    for (int64_t q = 0; q < n * f; ++q) {
+      const double u = U[q];
+      if (swi) {
+        const double sg = 1.0 / (1.0 + std::exp(-u));
+        dU[q] = dH[q] * V[q] * (sg + u * sg * (1.0 - sg));
+        dV[q] = dH[q] * u * sg;
+      } else {
+        const double cdf = 0.5 * (1.0 + std::erf(u / std::sqrt(2.0)));
+        const double pdf = std::exp(-0.5 * u * u) / std::sqrt(2.0 * 3.14159265358979323846);
+        dU[q] = dH[q] * (cdf + u * pdf);
+      }
+    }
+    // dW1 += dU^T X, dW3 += dV^T X, db1 += sum dU, dX = dU W1 (+ dV W3)
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < f; ++i)
+      for (int64_t j = 0; j < d; ++j) {
+        double a = 0.0, c = 0.0;
+        for (int64_t r = 0; r < n; ++r) {
+          a += dU[r * f + i] * X[r * d + j];
+          if (swi) c += dV[r * f + i] * X[r * d + j];
+        }
+        if (gW1) gW1[base1 + i * d + j] += a;
+        if (swi && gW3) gW3[base1 + i * d + j] += c;
+      }
+    if (gb1 && !swi)
+      for (int64_t i = 0; i < f; ++i)
+        for (int64_t r = 0; r < n; ++r) gb1[static_cast<int64_t>(e) * f + i] += dU[r * f + i];
+    dX.assign(static_cast<size_t>(n * d), 0.0);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t j = 0; j < d; ++j) {
+        double a = 0.0;
+        for (int64_t i = 0; i < f; ++i) {
+          a += dU[r * f + i] * w1(i, j);
+          if (swi) a += dV[r * f + i] * w3(i, j);
+        }
+        dX[r * d + j] = a;
+      }
+  };
+
+  // routed experts: rows are the kept pairs of expert e in ascending token order
+  for (int64_t e = 0; e < N; ++e) {
+    std::vector<int64_t> tok, slot;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t j = 0; j < k; ++j)
+        if (idx[t * k + j] == e && inv[t * k + j] >= 0) {
+          tok.push_back(t);
+          slot.push_back(t * k + j);
+        }
+    const int64_t n = static_cast<int64_t>(tok.size());
+    if (n == 0) continue;
+    std::vector<double> X(static_cast<size_t>(n * d)), dY(static_cast<size_t>(n * d)), Y(static_cast<size_t>(n * d));
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) {
+        X[r * d + c] = elem(x, s->act_dtype, tok[r] * d + c, 1.0);
+        dY[r * d + c] = gate[slot[r]] * elem(dy, s->act_dtype, tok[r] * d + c, 1.0);
+      }
+    expert_rows(s, w, false, static_cast<int>(e), X.data(), n, Y.data());
+    for (int64_t r = 0; r < n; ++r) {
+      double a = 0.0;
+      for (int64_t c = 0; c < d; ++c) a += elem(dy, s->act_dtype, tok[r] * d + c, 1.0) * Y[r * d + c];
+      dg[slot[r]] = a;
+    }
+    std::vector<double> dX;
+    expert_bwd(false, static_cast<int>(e), X, dY, n, dW1, dW3, dW2, db1, db2, dX);
+    for (int64_t r = 0; r < n; ++r)
+      for (int64_t c = 0; c < d; ++c) dx[tok[r] * d + c] += dX[r * d + c];
+  }
+  // shared experts: every token, output gradient dy
+  if (S > 0) {
+    std::vector<double> X(static_cast<size_t>(T * d)), dY(static_cast<size_t>(T * d));
+    for (int64_t i = 0; i < T * d; ++i) {
+      X[i] = elem(x, s->act_dtype, i, 1.0);
+      dY[i] = elem(dy, s->act_dtype, i, 1.0);
+    }
+    for (int sh = 0; sh < S; ++sh) {
+      std::vector<double> dX;
+      expert_bwd(true, sh, X, dY, T, dsW1, dsW3, dsW2, nullptr, nullptr, dX);
+      for (int64_t i = 0; i < T * d; ++i) dx[i] += dX[i];
+    }
+  }
+
+  // router: gates, L_aux and z to the logits, then to W_r, b_r and x
+  std::vector<double> dl(static_cast<size_t>(T * N), 0.0);
+  double lm = 0.0;
+  for (int64_t t = 0; t < T; ++t) lm += lse[t];
+  lm = (T > 0) ? lm / static_cast<double>(T) : 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    std::vector<double> dp(static_cast<size_t>(N), 0.0);
+    const int32_t* St = idx.data() + t * k;
+    const double* g = gate.data() + t * k;
+    const double* dgt = dg.data() + t * k;
+    double* dlt = dl.data() + t * N;
+    const double* pt = p.data() + t * N;
+    if (s->gating == 0) {
+      for (int64_t j = 0; j < k; ++j) dp[St[j]] += dgt[j];
+    } else if (s->gating == 1) {
+      double ssum = 0.0, dot = 0.0;
+      for (int64_t j = 0; j < k; ++j) { ssum += pt[St[j]]; dot += dgt[j] * g[j]; }
+      for (int64_t j = 0; j < k; ++j) dp[St[j]] += (dgt[j] - dot) / ssum;
+    } else {
+      double dot = 0.0;
+      for (int64_t j = 0; j < k; ++j) dot += dgt[j] * g[j];
+      for (int64_t j = 0; j < k; ++j) dlt[St[j]] += g[j] * (dgt[j] - dot);
+    }
+    for (int64_t e = 0; e < N; ++e)
+      dp[e] += c_aux * s->aux_alpha * static_cast<double>(N) * (static_cast<double>(counts[e]) /
+                                                               static_cast<double>(T * k)) / static_cast<double>(T);
+    double dpp = 0.0;
+    for (int64_t e = 0; e < N; ++e) dpp += dp[e] * pt[e];
+    for (int64_t e = 0; e < N; ++e) {
+      dlt[e] += pt[e] * (dp[e] - dpp);
+      dlt[e] += c_z * 2.0 * lm / static_cast<double>(T) * pt[e];
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < d; ++c) {
+      double a = 0.0;
+      for (int64_t e = 0; e < N; ++e) a += dl[t * N + e] * elem(w->w_router, s->act_dtype, e * d + c, 1.0);
+      dx[t * d + c] += a;
+    }
+  if (dWr)
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < N; ++e)
+      for (int64_t c = 0; c < d; ++c) {
+        double a = 0.0;
+        for (int64_t t = 0; t < T; ++t) a += dl[t * N + e] * elem(x, s->act_dtype, t * d + c, 1.0);
+        dWr[e * d + c] = a;
+      }
+  if (dbr)
+    for (int64_t e = 0; e < N; ++e) {
+      double a = 0.0;
+      for (int64_t t = 0; t < T; ++t) a += dl[t * N + e];
+      dbr[e] = a;
+    }
+  return 0;
+}
+
 // Exact decoders, exported so that tests can pin them to library conversions.
 double orc_bf16_value(uint16_t b) { return bf16_value(b); }
 double orc_e4m3_value(uint8_t q) { return e4m3_value(q); }
