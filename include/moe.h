@@ -186,7 +186,8 @@ typedef enum {
   MOE_ENTRY_ROUTE = 0,
   MOE_ENTRY_PERMUTE = 1,
   MOE_ENTRY_GROUPED_FFN = 2,
-  MOE_ENTRY_FORWARD = 3
+  MOE_ENTRY_FORWARD = 3,
+  MOE_ENTRY_BACKWARD = 4
 } moe_entry;
 
 /* moe_route flag: take the fp32 logits from `logits` instead of computing the
@@ -293,6 +294,48 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
                        void* y, float* logits, int32_t* topk_idx, float* topk_w,
                        int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
                        const moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients written by moe_backward. dx is required; every other member may be
+ * NULL (that gradient is not computed). Weight gradients are fp32 in the
+ * contiguous nn.Linear layout of the weights they belong to (no row pitch),
+ * one matrix per expert, and are overwritten (not accumulated into).
+ */
+typedef struct {
+  void* dx;          /* [T][d] act_dtype */
+  float* dw_router;  /* [N][d] */
+  float* db_router;  /* [N] */
+  float* dw1;        /* [N][d_ff][d] */
+  float* dw3;        /* [N][d_ff][d] (SwiGLU) */
+  float* dw2;        /* [N][d][d_ff] */
+  float* db1;        /* [N][d_ff] (GELU) */
+  float* db2;        /* [N][d] (GELU) */
+  float* dsw1;       /* [n_shared][d_ff][d] */
+  float* dsw3;       /* [n_shared][d_ff][d] (SwiGLU) */
+  float* dsw2;       /* [n_shared][d][d_ff] */
+} moe_grads;
+
+/*
+ * Layer backward (the training step of the aigrafen `MoE` module, whose loss
+ * adds alpha-weighted L_aux; starphix "Load Balancing (Critical)" adds the
+ * z_loss): the gradients of
+ *   L = sum_t <dy[t], y[t]> + c_aux * L_aux + c_z * z
+ * with respect to x, W_r, b_r and every expert's (and shared expert's)
+ * weights and GELU biases, where y is moe_forward's output for the same x and
+ * weights. The routing decision (the selected experts, the capacity cut, the
+ * counts behind f) is held fixed, as it is piecewise constant; the gates, P
+ * and the logsumexp carry gradient. The fp32 rounding of the logits passes
+ * the gradient unchanged. The forward is recomputed inside the call (nothing
+ * is kept from an earlier moe_forward).
+ * Token choice only (gating 0..2; expert choice gives MOE_ERR_UNSUPPORTED),
+ * act_dtype = w_dtype = MOE_BF16 (else MOE_ERR_UNSUPPORTED). x, dy [T][d]
+ * bf16. Intermediate products are rounded to bf16 where they feed a matrix
+ * product (H, dY = g dy, dU, dV, the logit gradient as a bf16 pair);
+ * accumulation is fp32. Deterministic: identical inputs give identical bits.
+ */
+moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights* weights, const void* dy,
+                        float c_aux, float c_z, const moe_grads* grads, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /*
  * Stage timing, for profiling. Between moe_timing_start and moe_timing_stop

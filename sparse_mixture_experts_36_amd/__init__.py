@@ -22,7 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE
 F32, BF16, FP8_E4M3, INT_W = 0, 1, 2, 3
 GELU, SWIGLU = 0, 1
 SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX, EXPERT_CHOICE = 0, 1, 2, 3
-ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_FFN, ENTRY_FORWARD = 0, 1, 2, 3
+ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_FFN, ENTRY_FORWARD, ENTRY_BACKWARD = 0, 1, 2, 3, 4
 ROUTE_LOGITS_GIVEN = 1
 
 
@@ -47,6 +47,12 @@ class Stats(ctypes.Structure):
     """moe_stats (device pointers)"""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("counts", "kept", "f", "P", "l_aux", "z_loss", "lse_mean", "lse_sq_mean", "n_dropped")]
+
+
+class Grads(ctypes.Structure):
+    """moe_grads (device pointers)"""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "db_router", "dw1", "dw3", "dw2", "db1", "db2", "dsw1", "dsw3", "dsw2")]
 
 
 class MoEError(RuntimeError):
@@ -83,10 +89,12 @@ def lib():
         L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [sp, vp, wp, vp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
+        L.moe_backward.argtypes = [sp, vp, wp, vp, ctypes.c_float, ctypes.c_float, ctypes.POINTER(Grads), vp, sz,
+                                   vp]
         L.moe_timing_start.argtypes = [ctypes.c_int32]
         L.moe_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         for f in ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                  "moe_forward", "moe_timing_start", "moe_timing_stop"):
+                  "moe_forward", "moe_backward", "moe_timing_start", "moe_timing_stop"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,6 +208,34 @@ def forward(shape, x, weights: Weights, y, logits=None, topk_idx=None, topk_w=No
                            _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_token), _ptr(inv_map),
                            ctypes.byref(st) if st else None, _ptr(ws_), ws_.numel(), _stream(stream))
     _check(rc, "moe_forward")
+
+
+def alloc_grads(shape: Shape, device="cuda") -> dict:
+    """Output tensors for moe_backward: dx bf16 [T][d], fp32 weight gradients
+    for every weight the layer has (the router bias and GELU biases included)."""
+    import torch
+    T, d, f, N, S = shape.T, shape.d, shape.d_ff, shape.n_experts, shape.n_shared
+    f32 = dict(dtype=torch.float32, device=device)
+    swi = shape.act == SWIGLU
+    g = {"dx": torch.empty(T, d, dtype=torch.bfloat16, device=device), "dw_router": torch.empty(N, d, **f32),
+         "db_router": torch.empty(N, **f32), "dw1": torch.empty(N, f, d, **f32),
+         "dw3": torch.empty(N, f, d, **f32) if swi else None, "dw2": torch.empty(N, d, f, **f32),
+         "db1": None if swi else torch.empty(N, f, **f32), "db2": None if swi else torch.empty(N, d, **f32)}
+    if S:
+        g.update(dsw1=torch.empty(S, f, d, **f32), dsw3=torch.empty(S, f, d, **f32) if swi else None,
+                 dsw2=torch.empty(S, d, f, **f32))
+    return g
+
+
+def backward(shape, x, weights: Weights, dy, grads: dict, c_aux: float = 0.0, c_z: float = 0.0, ws=None,
+             stream=None):
+    """moe_backward: gradients of sum <dy, y> + c_aux L_aux + c_z z into the
+    tensors of `grads` (keys of moe_grads; missing or None: not computed)."""
+    gs = Grads(**{k: _ptr(v) for k, v in grads.items() if v is not None})
+    ws_ = ws if ws is not None else workspace(shape, ENTRY_BACKWARD)
+    rc = lib().moe_backward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(dy), c_aux, c_z,
+                            ctypes.byref(gs), _ptr(ws_), ws_.numel(), _stream(stream))
+    _check(rc, "moe_backward")
 
 
 STAGES = ("route", "permute", "ffn_plan", "ffn_up", "ffn_down", "combine")

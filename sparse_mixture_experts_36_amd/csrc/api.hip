@@ -194,12 +194,62 @@ FwdWs carve_fwd(Carver& c, const moe_shape& s) {
   return w;
 }
 
+// Backward: the recomputed routing, then every row-space product of the
+// routed rows [0, cap) and the shared experts' T rows each.
+struct BwdWs {
+  float* logits;
+  int32_t *topk_idx, *inv_map, *offsets, *perm_token, *counts, *tile_start;
+  float *topk_w, *lse_mean;
+  uint16_t* x_perm;
+  float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
+  uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
+};
+int32_t bwd_ldl(const moe_shape& s) { return (s.n_experts + 7) / 8 * 8; }
+BwdWs carve_bwd(Carver& c, const moe_shape& s) {
+  const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(s.top_k), N = s.n_experts;
+  const size_t cap = static_cast<size_t>(routed_row_cap(s));
+  const size_t rows = cap + static_cast<size_t>(s.n_shared) * T;
+  const size_t d = static_cast<size_t>(s.d), f = static_cast<size_t>(s.d_ff);
+  const bool swi = s.act == MOE_ACT_SWIGLU;
+  BwdWs w;
+  w.logits = c.take<float>(T * N);
+  w.topk_idx = c.take<int32_t>(T * k);
+  w.topk_w = c.take<float>(T * k);
+  w.inv_map = c.take<int32_t>(T * k);
+  w.offsets = c.take<int32_t>(N + 1);
+  w.perm_token = c.take<int32_t>(T * k);
+  w.counts = c.take<int32_t>(N);
+  w.lse_mean = c.take<float>(1);
+  w.tile_start = c.take<int32_t>(N + 1);
+  w.x_perm = c.take<uint16_t>(cap * d);
+  w.U = c.take<float>(rows * f);
+  w.V = swi ? c.take<float>(rows * f) : nullptr;
+  w.H = c.take<uint16_t>(rows * f);
+  w.Y = c.take<float>(cap * d);
+  w.dY = c.take<uint16_t>(cap * d);
+  w.dH = c.take<float>(rows * f);
+  w.dU = c.take<uint16_t>(rows * f);
+  w.dV = swi ? c.take<uint16_t>(rows * f) : nullptr;
+  w.dX = c.take<float>(rows * d);
+  w.dg = c.take<float>(T * k);
+  w.dl32 = c.take<float>(T * N);
+  w.dl_hi = c.take<uint16_t>(T * static_cast<size_t>(bwd_ldl(s)));
+  w.dl_lo = c.take<uint16_t>(T * static_cast<size_t>(bwd_ldl(s)));
+  w.dxr = c.take<float>(T * d);
+  return w;
+}
+
 size_t ws_bytes_for(const moe_shape& s, int32_t entry) {
   Carver c{nullptr};
   switch (entry) {
     case MOE_ENTRY_ROUTE: carve_route(c, s); break;
     case MOE_ENTRY_PERMUTE: carve_perm(c, s); break;
     case MOE_ENTRY_GROUPED_FFN: carve_ffn(c, s); break;
+    case MOE_ENTRY_BACKWARD:
+      carve_route(c, s);
+      carve_perm(c, s);
+      carve_bwd(c, s);
+      break;
     default:
       carve_route(c, s);
       carve_perm(c, s);
@@ -465,7 +515,7 @@ int64_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf) {
 moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* bytes) {
   const moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!bytes || entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_FORWARD) return MOE_ERR_INVALID_ARG;
+  if (!bytes || entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_BACKWARD) return MOE_ERR_INVALID_ARG;
   *bytes = ws_bytes_for(*shape, entry);
   return MOE_OK;
 }
@@ -597,6 +647,94 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
     e = moe::launch_combine(a, stream);
   }
   return hip_status(e);
+}
+
+moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights* weights, const void* dy,
+                        float c_aux, float c_z, const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (is_ec(s) || s.act_dtype != MOE_BF16 || s.w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!x || !dy || !g || !g->dx || !aligned16(x) || !aligned16(dy) || !aligned16(g->dx)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weights(s, weights, true)) != MOE_OK) return st;
+  if ((st = check_ws(s, MOE_ENTRY_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  Carver c{static_cast<char*>(ws)};
+  const RouteWs rw = carve_route(c, s);
+  const PermWs pw = carve_perm(c, s);
+  const BwdWs w = carve_bwd(c, s);
+  moe_stats rst{};
+  rst.counts = w.counts;
+  rst.lse_mean = w.lse_mean;
+  hipError_t e = moe::launch_route(route_args(s, x, weights->w_router, weights->b_router, w.logits, false,
+                                              w.topk_idx, w.topk_w, &rst, rw),
+                                   stream);
+  if (e == hipSuccess)
+    e = moe::launch_permute(
+        perm_args(s, w.topk_idx, x, w.offsets, w.perm_token, w.inv_map, w.x_perm, s.d, nullptr, pw), stream);
+  if (e != hipSuccess) return hip_status(e);
+  moe::BwdArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.d_ff = s.d_ff;
+  a.cap = routed_row_cap(s);
+  a.N = s.n_experts;
+  a.k = s.top_k;
+  a.S = s.n_shared;
+  a.act = s.act;
+  a.gating = s.gating;
+  a.ldl = bwd_ldl(s);
+  a.aux_alpha = s.aux_alpha;
+  a.c_aux = c_aux;
+  a.c_z = c_z;
+  a.x = static_cast<const uint16_t*>(x);
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.w_router = static_cast<const uint16_t*>(weights->w_router);
+  a.x_perm = w.x_perm;
+  a.w1 = static_cast<const uint16_t*>(weights->w1);
+  a.w3 = static_cast<const uint16_t*>(weights->w3);
+  a.w2 = static_cast<const uint16_t*>(weights->w2);
+  a.sw1 = static_cast<const uint16_t*>(weights->sw1);
+  a.sw3 = static_cast<const uint16_t*>(weights->sw3);
+  a.sw2 = static_cast<const uint16_t*>(weights->sw2);
+  a.ld_up = weights->ld_up ? weights->ld_up : s.d;
+  a.ld_down = weights->ld_down ? weights->ld_down : s.d_ff;
+  a.b1 = weights->b1;
+  a.b2 = weights->b2;
+  a.logits = w.logits;
+  a.topk_idx = w.topk_idx;
+  a.inv_map = w.inv_map;
+  a.offsets = w.offsets;
+  a.counts = w.counts;
+  a.topk_w = w.topk_w;
+  a.lse_mean = w.lse_mean;
+  a.U = w.U;
+  a.V = w.V;
+  a.Y = w.Y;
+  a.dH = w.dH;
+  a.dX = w.dX;
+  a.dl32 = w.dl32;
+  a.dxr = w.dxr;
+  a.dg = w.dg;
+  a.H = w.H;
+  a.dY = w.dY;
+  a.dU = w.dU;
+  a.dV = w.dV;
+  a.dl_hi = w.dl_hi;
+  a.dl_lo = w.dl_lo;
+  a.tile_start = w.tile_start;
+  a.dx = static_cast<uint16_t*>(g->dx);
+  a.dWr = g->dw_router;
+  a.dbr = g->db_router;
+  a.dW1 = g->dw1;
+  a.dW3 = s.act == MOE_ACT_SWIGLU ? g->dw3 : nullptr;
+  a.dW2 = g->dw2;
+  a.db1 = s.act == MOE_ACT_GELU ? g->db1 : nullptr;
+  a.db2 = s.act == MOE_ACT_GELU ? g->db2 : nullptr;
+  a.dsW1 = s.n_shared > 0 ? g->dsw1 : nullptr;
+  a.dsW3 = (s.n_shared > 0 && s.act == MOE_ACT_SWIGLU) ? g->dsw3 : nullptr;
+  a.dsW2 = s.n_shared > 0 ? g->dsw2 : nullptr;
+  return hip_status(moe::launch_backward(a, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,368 @@
+// Layer backward: gradients of sum_t <dy_t, y_t> + c_aux L_aux + c_z z with
+// respect to x, the router weight and bias, and every expert's weights (and
+// GELU biases), with the routing decision held fixed.
+//
+// Pages: aigrafen.se "Mixture of Experts" (y = sum g_i E_i(x); L_aux =
+// alpha N sum f_i P_i; the `MoE` module), learn.starphix.com "Mixture of
+// Experts (MoE)" / "Load Balancing (Critical)" (z_loss), vanos001 "MoE
+// Architecture" / "Expert Network Design" (SwiGLU, GELU experts).
+//
+// Steps (all on the caller's stream):
+//  1. forward again: router, permutation with the rows copied, U = X W1^T
+//     (+ b1) and V = X W3^T in fp32, H = act(U, V) in bf16, the routed
+//     outputs Y = H W2^T; shared experts on all T rows;
+//  2. combine backward: dY_row = g dy_t (bf16), dg = <dy_t, Y_row + b2>;
+//  3. dH = dY W2 (fp32); dU, dV from dH, U, V (bf16); dX = dU W1 + dV W3 (fp32);
+//  4. dW2 = dY^T H, dW1 = dU^T X, dW3 = dV^T X (fp32, one matrix per expert),
+//     b1 / b2 gradients as column sums;
+//  5. router: dl from dg through the gates' mode, the L_aux and z terms and
+//     the token softmax; dW_r = dl^T x and dx += dl W_r (dl split into two
+//     bf16 halves whose sum is dl to about 2^-16), db_r = column sums of dl;
+//  6. dx_t = sum of its kept rows of dX (slots ascending) + the shared rows +
+//     the router term, bf16.
+// Every sum runs in a fixed order: identical inputs give identical bits.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSlots = 8;  // top-k limit
+
+// H = act(U (+ b1), V) for every row; U takes the bias in place (GELU,
+// routed rows: the row's expert from the offsets).
+__global__ __launch_bounds__(kThreads) void act_fwd_kernel(BwdArgs a, float* U, const float* V, uint16_t* H,
+                                                            int64_t rows) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * a.d_ff) return;
+  const int64_t r = i / a.d_ff, c = i % a.d_ff;
+  float u = U[i];
+  if (a.act == 0 && a.b1 && r < a.cap) {
+    int lo = 0, hi = a.N - 1;  // expert of routed row r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.offsets[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    u += a.b1[static_cast<int64_t>(lo) * a.d_ff + c];
+    U[i] = u;
+  }
+  H[i] = f32_to_bf16(a.act == 1 ? silu(u) * V[i] : gelu_erf(u));
+}
+
+// Per token: dY rows of its kept slots = g dy (bf16) and dg = <dy, Y + b2>.
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
+  __shared__ float s_red[kThreads / 64][kMaxSlots];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* dy = a.dy + t * a.d;
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    if (j >= a.k) break;
+    const int row = a.inv_map[t * a.k + j];
+    float s = 0.f;
+    if (row >= 0) {  // uniform: dropped pairs carry nothing
+      const int e = a.topk_idx[t * a.k + j];
+      const float g = a.topk_w[t * a.k + j];
+      const float* y = a.Y + static_cast<int64_t>(row) * a.d;
+      uint16_t* dY = a.dY + static_cast<int64_t>(row) * a.d;
+      const float* b2 = (a.act == 0 && a.b2) ? a.b2 + static_cast<int64_t>(e) * a.d : nullptr;
+      for (int64_t c = tid; c < a.d; c += kThreads) {
+        const float v = bf16_to_f32(dy[c]);
+        dY[c] = f32_to_bf16(g * v);
+        s = fmaf(v, y[c] + (b2 ? b2[c] : 0.f), s);
+      }
+    }
+    s = wave_sum(s);
+    if (lane == 0) s_red[wave][j] = s;
+  }
+  __syncthreads();
+  if (tid < a.k) {
+    float s = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) s += s_red[w][tid];
+    a.dg[t * a.k + tid] = a.inv_map[t * a.k + tid] >= 0 ? s : 0.f;
+  }
+}
+
+// dU, dV (bf16) from dH and the pre-activations: SwiGLU dU = dH V silu'(U),
+// dV = dH silu(U); GELU dU = dH gelu'(U).
+__global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a, const float* dH, const float* U, const float* V,
+                                                            uint16_t* dU, uint16_t* dV, int64_t rows) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * a.d_ff) return;
+  const float u = U[i], h = dH[i];
+  if (a.act == 1) {
+    const float sg = 1.f / (1.f + expf(-u));
+    dU[i] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
+    dV[i] = f32_to_bf16(h * u * sg);
+  } else {
+    const float cdf = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+    const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
+    dU[i] = f32_to_bf16(h * (cdf + u * pdf));
+  }
+}
+
+// Router backward, one token per quarter-wave (16 lanes): p from the logits,
+// the gate gradient by mode, the L_aux and z terms, then through the softmax.
+// dl is written in fp32 (for the bias gradient) and as two bf16 halves
+// (hi = bf16(dl), lo = bf16(dl - hi)) of row pitch ldl, the pad columns zero.
+__global__ __launch_bounds__(kThreads) void router_bwd_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + wave * 4 + q;
+  if (t >= a.T) return;  // uniform within the quarter
+  const int N = a.N, k = a.k;
+  const float* l = a.logits + t * N;
+  float m = -3.0e38f;
+  for (int e = c16; e < N; e += 16) m = fmaxf(m, l[e]);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+  float s = 0.f;
+  for (int e = c16; e < N; e += 16) s += expf(l[e] - m);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  const float inv_s = 1.f / s;
+  // <dg, g> and the sum of the selected p (renormalised gates)
+  float dot = 0.f, psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    if (j >= k) break;
+    dot += a.dg[t * k + j] * a.topk_w[t * k + j];
+    psum += expf(l[a.topk_idx[t * k + j]] - m) * inv_s;
+  }
+  const float zc = a.c_z * 2.f * (*a.lse_mean) / static_cast<float>(a.T);
+  // d L_aux / d p_e = alpha N f_e / T with f_e = counts_e / (T k)
+  const float ac = a.c_aux * a.aux_alpha * static_cast<float>(N) /
+                   (static_cast<float>(a.T) * static_cast<float>(a.T) * static_cast<float>(k));
+  // dp_e (gradient onto the full softmax) and dq_e (onto the logit directly:
+  // the softmax over the k selected logits)
+  auto grad_of = [&](int e, float& dq) {
+    float dp = ac * static_cast<float>(a.counts[e]);
+    dq = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+      if (j >= k) break;
+      if (a.topk_idx[t * k + j] != e) continue;
+      const float dgj = a.dg[t * k + j];
+      if (a.gating == 0) dp += dgj;
+      else if (a.gating == 1) dp += (dgj - dot) / psum;
+      else dq += a.topk_w[t * k + j] * (dgj - dot);
+    }
+    return dp;
+  };
+  float dpp = 0.f;
+  for (int e = c16; e < N; e += 16) {
+    float dq;
+    dpp += grad_of(e, dq) * expf(l[e] - m) * inv_s;
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) dpp += __shfl_xor(dpp, o, 16);
+  for (int e = c16; e < a.ldl; e += 16) {
+    float dl = 0.f;
+    if (e < N) {
+      const float p = expf(l[e] - m) * inv_s;
+      float dq;
+      const float dp = grad_of(e, dq);
+      dl = dq + p * (dp - dpp) + zc * p;
+      a.dl32[t * N + e] = dl;
+    }
+    const uint16_t hi = f32_to_bf16(dl);
+    a.dl_hi[t * a.ldl + e] = hi;
+    a.dl_lo[t * a.ldl + e] = f32_to_bf16(dl - bf16_to_f32(hi));
+  }
+}
+
+// Column sums over the rows of each group (fixed order): out[g][c] = sum_r
+// in[r][c], rows [off[g], off[g+1]) (off null: rows [0, rows) as one group).
+template <typename TI>
+__global__ __launch_bounds__(kThreads) void colsum_kernel(const TI* in, int64_t ld, const int32_t* off, int32_t cap,
+                                                          int64_t rows, int64_t cols, float* out) {
+  const int g = blockIdx.y;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  int64_t r0 = 0, r1 = rows;
+  if (off) {
+    r0 = max(0, min(off[g], cap));
+    r1 = max(static_cast<int>(r0), min(off[g + 1], cap));
+  }
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) {
+    if constexpr (sizeof(TI) == 2) s += bf16_to_f32(in[r * ld + c]);
+    else s += in[r * ld + c];
+  }
+  out[static_cast<int64_t>(g) * cols + c] = s;
+}
+
+// dx_t = sum over its kept slots of dX[row] (ascending) + the shared experts'
+// rows + the router term, to bf16.
+__global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a, const float* dX, const float* dxr, uint16_t* dx) {
+  const int64_t t = blockIdx.x;
+  for (int64_t c = threadIdx.x; c < a.d; c += kThreads) {
+    float s = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      const int row = a.inv_map[t * a.k + j];
+      if (row >= 0) s += dX[static_cast<int64_t>(row) * a.d + c];
+    }
+    for (int sh = 0; sh < a.S; ++sh) s += dX[(a.cap + static_cast<int64_t>(sh) * a.T + t) * a.d + c];
+    s += dxr[t * a.d + c];
+    dx[t * a.d + c] = f32_to_bf16(s);
+  }
+}
+
+unsigned blocks_for(int64_t n) { return static_cast<unsigned>(ceil_div(n, kThreads)); }
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  const int64_t T = a.T, d = a.d, f = a.d_ff, cap = a.cap, S = a.S;
+  const int64_t rows = cap + S * T;  // routed rows, then T per shared expert
+  const bool swi = (a.act == 1);
+  auto ok = [&]() { return e == hipSuccess; };
+  auto check = [&]() { if (e == hipSuccess) e = hipGetLastError(); };
+
+  // ---- 1. forward again (router and permutation are done by the caller)
+  BGemm up{};  // U / V = X W^T: routed rows from x_perm, shared rows from x
+  up.off = a.offsets; up.n_groups = a.N; up.cap = static_cast<int32_t>(cap); up.K = static_cast<int32_t>(d);
+  up.N = static_cast<int32_t>(f); up.A = a.x_perm; up.lda = d; up.ldb = a.ld_up; up.b_gs = f * a.ld_up;
+  up.ldc = f;
+  for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
+    up.B = w == 0 ? a.w1 : a.w3;
+    up.C = w == 0 ? a.U : a.V;
+    e = launch_bgemm(up, false, true, true, false, a.tile_start, s);
+  }
+  if (S > 0) {
+    BGemm sh = up;
+    sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.x;
+    sh.c_gs = T * f;
+    for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
+      sh.B = w == 0 ? a.sw1 : a.sw3;
+      sh.C = (w == 0 ? a.U : a.V) + cap * f;
+      e = launch_bgemm(sh, false, true, true, false, a.tile_start, s);
+    }
+  }
+  if (ok()) {
+    hipLaunchKernelGGL(act_fwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.U, a.V, a.H, rows);
+    check();
+  }
+  if (ok() && cap > 0) {  // Y = H W2^T for the routed rows (the gates' gradient)
+    BGemm y{};
+    y.off = a.offsets; y.n_groups = a.N; y.cap = static_cast<int32_t>(cap); y.K = static_cast<int32_t>(f);
+    y.N = static_cast<int32_t>(d); y.A = a.H; y.lda = f; y.B = a.w2; y.ldb = a.ld_down; y.b_gs = d * a.ld_down;
+    y.C = a.Y; y.ldc = d;
+    e = launch_bgemm(y, false, true, true, false, a.tile_start, s);
+  }
+  // ---- 2. combine backward
+  if (ok()) {
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, a);
+    check();
+  }
+  // ---- 3. dH, dU / dV, dX
+  BGemm dh{};  // dH = dY W2 (routed), dy W2s (shared)
+  dh.off = a.offsets; dh.n_groups = a.N; dh.cap = static_cast<int32_t>(cap); dh.K = static_cast<int32_t>(d);
+  dh.N = static_cast<int32_t>(f); dh.A = a.dY; dh.lda = d; dh.B = a.w2; dh.ldb = a.ld_down; dh.b_gs = d * a.ld_down;
+  dh.C = a.dH; dh.ldc = f;
+  if (ok() && cap > 0) e = launch_bgemm(dh, false, false, true, false, a.tile_start, s);
+  if (ok() && S > 0) {
+    BGemm sh = dh;
+    sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.dy;
+    sh.B = a.sw2; sh.C = a.dH + cap * f; sh.c_gs = T * f;
+    e = launch_bgemm(sh, false, false, true, false, a.tile_start, s);
+  }
+  if (ok()) {
+    hipLaunchKernelGGL(act_bwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.dH, a.U, a.V, a.dU,
+                       a.dV, rows);
+    check();
+  }
+  BGemm dxg{};  // dX = dU W1 (+ dV W3)
+  dxg.off = a.offsets; dxg.n_groups = a.N; dxg.cap = static_cast<int32_t>(cap); dxg.K = static_cast<int32_t>(f);
+  dxg.N = static_cast<int32_t>(d); dxg.lda = f; dxg.ldb = a.ld_up; dxg.b_gs = f * a.ld_up; dxg.C = a.dX;
+  dxg.ldc = d;
+  for (int w = 0; w < (swi ? 2 : 1) && ok() && cap > 0; ++w) {
+    dxg.A = w == 0 ? a.dU : a.dV;
+    dxg.B = w == 0 ? a.w1 : a.w3;
+    e = launch_bgemm(dxg, false, false, true, w == 1, a.tile_start, s);
+  }
+  if (S > 0) {
+    BGemm sh = dxg;
+    sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T);
+    sh.a_gs = T * f; sh.b_gs = f * a.ld_up; sh.C = a.dX + cap * d; sh.c_gs = T * d;
+    for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
+      sh.A = (w == 0 ? a.dU : a.dV) + cap * f;
+      sh.B = w == 0 ? a.sw1 : a.sw3;
+      e = launch_bgemm(sh, false, false, true, w == 1, a.tile_start, s);
+    }
+  }
+  // ---- 4. weight gradients: rows-K, one matrix per expert
+  BGemm dw{};
+  dw.off = a.offsets; dw.n_groups = a.N; dw.cap = static_cast<int32_t>(cap);
+  if (ok() && a.dW2) {  // dW2 = dY^T H: [d][d_ff]
+    dw.M = static_cast<int32_t>(d); dw.N = static_cast<int32_t>(f); dw.A = a.dY; dw.lda = d; dw.B = a.H; dw.ldb = f;
+    dw.C = a.dW2; dw.ldc = f; dw.c_gs = d * f;
+    e = launch_bgemm(dw, true, false, true, false, a.tile_start, s);
+  }
+  for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {  // dW1 = dU^T X, dW3 = dV^T X: [d_ff][d]
+    float* out = w == 0 ? a.dW1 : a.dW3;
+    if (!out) continue;
+    dw.M = static_cast<int32_t>(f); dw.N = static_cast<int32_t>(d); dw.A = w == 0 ? a.dU : a.dV; dw.lda = f;
+    dw.B = a.x_perm; dw.ldb = d; dw.C = out; dw.ldc = d; dw.c_gs = f * d;
+    e = launch_bgemm(dw, true, false, true, false, a.tile_start, s);
+  }
+  if (S > 0) {
+    BGemm sw{};
+    sw.n_groups = static_cast<int32_t>(S); sw.rows_all = static_cast<int32_t>(T);
+    if (ok() && a.dsW2) {
+      sw.M = static_cast<int32_t>(d); sw.N = static_cast<int32_t>(f); sw.A = a.dy; sw.lda = d;
+      sw.B = a.H + cap * f; sw.ldb = f; sw.b_gs = T * f; sw.C = a.dsW2; sw.ldc = f; sw.c_gs = d * f;
+      e = launch_bgemm(sw, true, false, true, false, a.tile_start, s);
+    }
+    for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
+      float* out = w == 0 ? a.dsW1 : a.dsW3;
+      if (!out) continue;
+      sw.M = static_cast<int32_t>(f); sw.N = static_cast<int32_t>(d); sw.A = (w == 0 ? a.dU : a.dV) + cap * f;
+      sw.lda = f; sw.a_gs = T * f; sw.B = a.x; sw.ldb = d; sw.b_gs = 0; sw.C = out; sw.ldc = d; sw.c_gs = f * d;
+      e = launch_bgemm(sw, true, false, true, false, a.tile_start, s);
+    }
+  }
+  if (ok() && !swi && a.db1) {
+    hipLaunchKernelGGL(colsum_kernel<uint16_t>, dim3(blocks_for(f), a.N), dim3(kThreads), 0, s, a.dU, f, a.offsets,
+                       static_cast<int32_t>(cap), cap, f, a.db1);
+    check();
+  }
+  if (ok() && !swi && a.db2) {
+    hipLaunchKernelGGL(colsum_kernel<uint16_t>, dim3(blocks_for(d), a.N), dim3(kThreads), 0, s, a.dY, d, a.offsets,
+                       static_cast<int32_t>(cap), cap, d, a.db2);
+    check();
+  }
+  // ---- 5. router
+  if (ok()) {
+    hipLaunchKernelGGL(router_bwd_kernel, dim3(static_cast<unsigned>(ceil_div(T, 16))), dim3(kThreads), 0, s, a);
+    check();
+  }
+  for (int h = 0; h < 2 && ok(); ++h) {  // dW_r = dl^T x and dx_r = dl W_r, each as hi + lo
+    if (a.dWr) {
+      BGemm r{};
+      r.n_groups = 1; r.rows_all = static_cast<int32_t>(T); r.M = a.N; r.N = static_cast<int32_t>(d);
+      r.A = h == 0 ? a.dl_hi : a.dl_lo; r.lda = a.ldl; r.B = a.x; r.ldb = d; r.C = a.dWr; r.ldc = d;
+      e = launch_bgemm(r, true, false, true, h == 1, a.tile_start, s);
+      if (!ok()) break;
+    }
+    BGemm x{};
+    x.n_groups = 1; x.rows_all = static_cast<int32_t>(T); x.K = a.N; x.N = static_cast<int32_t>(d);
+    x.A = h == 0 ? a.dl_hi : a.dl_lo; x.lda = a.ldl; x.B = a.w_router; x.ldb = d; x.C = a.dxr; x.ldc = d;
+    e = launch_bgemm(x, false, false, true, h == 1, a.tile_start, s);
+  }
+  if (ok() && a.dbr) {
+    hipLaunchKernelGGL(colsum_kernel<float>, dim3(blocks_for(a.N), 1), dim3(kThreads), 0, s, a.dl32,
+                       static_cast<int64_t>(a.N), nullptr, 0, T, static_cast<int64_t>(a.N), a.dbr);
+    check();
+  }
+  // ---- 6. dx
+  if (ok()) {
+    hipLaunchKernelGGL(dx_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, a, a.dX, a.dxr, a.dx);
+    check();
+  }
+  return e;
+}
+
+}  // namespace moe

@@ -183,6 +183,56 @@ size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, 
 hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
                              hipStream_t s);
 
+// ---------------------------------------------------------------- backward GEMM
+// C_g(m, n) (+)= sum_k A_g(m, k) B_g(k, n), bf16 operands, fp32 accumulation.
+// Group g's rows are [off[g], off[g+1]) clamped to cap (off null: rows_all rows
+// from 0 for every group). rows-M form: those rows are A's rows (A k-contiguous,
+// lda) and C's rows, K fixed. rows-K form: they are the contraction, A m-
+// contiguous (A(m, k) = A[(r0 + k) lda + m]), B(k, n) = B[(r0 + k) ldb + n], M
+// fixed, one C matrix per group. B k-contiguous (b_kc): B(k, n) = B[n ldb + k],
+// else n-contiguous. Per-group base offsets (elements): a_gs, b_gs, c_gs.
+struct BGemm {
+  const int32_t* off;
+  int32_t n_groups, cap, rows_all;
+  int32_t M, N, K;
+  const uint16_t* A;
+  int64_t lda, a_gs;
+  const uint16_t* B;
+  int64_t ldb, b_gs;
+  void* C;
+  int64_t ldc, c_gs;
+};
+// tile_start: [n_groups + 1] ints of workspace (rows-M form with offsets)
+hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool c_f32, bool acc, int32_t* tile_start,
+                        hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+// Token-choice layer backward, bf16 activations and weights. The caller has
+// run the router (logits, topk_idx, topk_w, counts, lse_mean) and the
+// permutation (offsets, inv_map, x_perm of pitch d). Routed rows are
+// [0, cap), shared expert s owns rows [cap + s T, cap + (s+1) T) of every
+// row-space buffer (U, V, H, dH, dU, dV, dX).
+struct BwdArgs {
+  int64_t T, d, d_ff, cap;
+  int32_t N, k, S, act, gating, ldl;  // ldl: row pitch of dl_hi / dl_lo, N rounded up to 8
+  float aux_alpha, c_aux, c_z;
+  const uint16_t *x, *dy, *w_router, *x_perm;
+  const uint16_t *w1, *w3, *w2, *sw1, *sw3, *sw2;
+  int64_t ld_up, ld_down;
+  const float *b1, *b2;
+  const float* logits;
+  const int32_t *topk_idx, *inv_map, *offsets, *counts;
+  const float *topk_w, *lse_mean;
+  // workspace
+  float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
+  uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
+  int32_t* tile_start;
+  // outputs (weight gradients may be null: not computed)
+  uint16_t* dx;
+  float *dWr, *dbr, *dW1, *dW3, *dW2, *db1, *db2, *dsW1, *dsW3, *dsW2;
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 struct CombineArgs {
   int64_t T, d;

@@ -210,3 +210,34 @@ def test_host_helpers_reproduce_pages_worked_examples():
     for name in ("collapsed", "balanced"):
         assert round(moe.routing_entropy(ent[name]["f"]), ent["digits"]) == ent[name]["printed"]
     assert round(__import__("math").log(8), 3) == ent["max_printed"]
+
+
+def test_backward_host_checks_return_before_launch():
+    """moe_backward's validation, all on the host (a launch would report
+    MOE_ERR_HIP here, where no GPU exists)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    s = _shape(act_dtype=moe.BF16, w_dtype=moe.BF16)
+    w = moe.Weights(w_router=1 << 20, w1=1 << 20, w3=1 << 20, w2=1 << 20)
+    g = moe.Grads(dx=1 << 20)
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(s), moe.ENTRY_BACKWARD, ctypes.byref(n)) == moe.MOE_OK
+    # the backward keeps U, V, H, dH, dU, dV and dX over every row
+    rows = s.T * s.top_k
+    assert n.value >= rows * s.d_ff * (4 + 4 + 2 + 4 + 2 + 2) + rows * s.d * 4
+    assert L.moe_backward(ctypes.byref(s), fake, ctypes.byref(w), fake, 0.0, 0.0, ctypes.byref(g), fake, 16,
+                          None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_backward(ctypes.byref(s), fake, ctypes.byref(w), None, 0.0, 0.0, ctypes.byref(g), fake, 1 << 40,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_backward(ctypes.byref(s), fake, ctypes.byref(w), fake, 0.0, 0.0, ctypes.byref(moe.Grads()), fake,
+                          1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    # router weight required
+    w0 = moe.Weights(w1=1 << 20, w3=1 << 20, w2=1 << 20)
+    assert L.moe_backward(ctypes.byref(s), fake, ctypes.byref(w0), fake, 0.0, 0.0, ctypes.byref(g), fake, 1 << 40,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    # bf16 token choice only
+    for kw in (dict(), dict(act_dtype=moe.BF16, w_dtype=moe.FP8_E4M3), dict(act_dtype=moe.F32, w_dtype=moe.F32),
+               dict(act_dtype=moe.BF16, w_dtype=moe.BF16, gating=moe.EXPERT_CHOICE, top_k=1, capacity=8)):
+        su = _shape(**kw) if kw else _shape(act_dtype=moe.BF16, w_dtype=moe.INT_W)
+        assert L.moe_backward(ctypes.byref(su), fake, ctypes.byref(w), fake, 0.0, 0.0, ctypes.byref(g), fake,
+                              1 << 40, None) == moe.MOE_ERR_UNSUPPORTED, kw
