@@ -18,7 +18,10 @@ in HBM GB/s of algorithmic bytes (every touched expert's three matrices once,
 the router weight, x and y): whole steps replayed from captured HIP graphs
 (`us_per_step`; eager launches in `us_per_step_eager`) and the expert FFN
 alone (`ffn_us`, from hipEvents on a separate pass). `cpu_baseline` times the
-fp64 CPU oracle on a bounded sample of the same workload.
+fp64 CPU oracle on a bounded sample of the same workload. `backward` times
+moe_backward (forward recompute plus every gradient) on the prefill layer.
+Other workloads (--workload): the expert-choice and INT8/INT4 variants of the
+Mixtral-shape layer, the fine-grained and top-1 layers.
 """
 from __future__ import annotations
 
@@ -265,6 +268,47 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
     return out
 
 
+def run_backward(wl, inp, steps, warmup):
+    """moe_backward on the same layer and input with a seeded bf16 dy: dx and
+    every weight gradient, L_aux and z terms on. One step recomputes the
+    forward (3 of the 9 expert GEMMs) and runs the 6 gradient GEMMs, so it
+    does 3 x the forward FFN's flops per kept pair; flops and MFMA fraction
+    count all of them. Time from hipEvents around the whole step."""
+    import torch
+
+    import gen
+    import sparse_mixture_experts_36_amd as moe
+
+    shape = shape_for(wl)
+    tensors = layer_weights(inp)
+    w = moe.weights_struct(tensors)
+    x = to_dev(inp.x)
+    dy = to_dev(gen.normal(97, (wl.T, wl.d), 1.0, gen.BF16))
+    g = moe.alloc_grads(shape)
+    ws = moe.workspace(shape, moe.ENTRY_BACKWARD)
+    for _ in range(warmup):
+        moe.backward(shape, x, w, dy, g, 1.0, 1e-3, ws=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        moe.backward(shape, x, w, dy, g, 1.0, 1e-3, ws=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # rows: every kept pair (dropless here) plus T per shared expert
+    rows = wl.T * wl.top_k + wl.n_shared * wl.T if wl.capacity() < 0 else None
+    out = {"ms_per_step": round(ms, 4), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
+           "workspace_GB": round(moe.workspace_size(shape, moe.ENTRY_BACKWARD) / 1e9, 3)}
+    if rows is not None:
+        flops = 3 * rows * ffn_flops_per_pair(wl) + 2.0 * wl.T * wl.d * wl.n_experts * 5
+        out.update(flops_per_step=flops, TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 1),
+                   mfma_frac=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    log(f"backward: {out}")
+    return out
+
+
 def cpu_baseline(wl, inp, target_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample: the first S tokens as
     their own batch (S grown from 8 until one run takes a few seconds, then the
@@ -312,6 +356,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode shapes (T = 1, 16, 64) on the prefill weights; prints their JSON")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the layer backward (moe_backward) on the workload; prints its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel that scales the PMC byte counters")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -342,6 +389,9 @@ def main():
     log(f"inputs generated in {time.perf_counter() - t:.1f} s")
     if args.decode_only:
         print(json.dumps({"decode": run_decode(wl, inp, max(args.steps, 16), args.warmup)}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": run_backward(wl, inp, args.steps, args.warmup)}), flush=True)
         return
 
     r = run_gpu(wl, inp, args.steps, args.warmup)
@@ -389,6 +439,8 @@ def main():
     if not args.no_decode and wl.name == "mixtral-prefill-bf16":
         del r
         result["decode"] = run_decode(wl, inp, max(args.steps, 16), args.warmup)
+    if not args.no_backward and wl.name == "mixtral-prefill-bf16":
+        result["backward"] = run_backward(wl, inp, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(result), flush=True)
