@@ -193,6 +193,24 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(const TI* in, int64_t 
   out[static_cast<int64_t>(g) * cols + c] = s;
 }
 
+// db_r[e] = sum_t dl[t][e]: one workgroup per expert, each thread a strided
+// share of the tokens, then the waves in order.
+__global__ __launch_bounds__(kThreads) void router_bias_grad_kernel(const float* dl, int64_t T, int32_t N,
+                                                                    float* dbr) {
+  __shared__ float s_w[kThreads / 64];
+  const int e = blockIdx.x;
+  float s = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += kThreads) s += dl[t * N + e];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) v += s_w[w];
+    dbr[e] = v;
+  }
+}
+
 // dx_t = sum over its kept slots of dX[row] (ascending) + the shared experts'
 // rows + the router term, to bf16.
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a, const float* dX, const float* dxr, uint16_t* dx) {
@@ -229,7 +247,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
     up.B = w == 0 ? a.w1 : a.w3;
     up.C = w == 0 ? a.U : a.V;
-    e = launch_bgemm(up, false, true, true, false, a.tile_start, s);
+    e = launch_bgemm(up, false, true, false, a.tile_start, s);
   }
   if (S > 0) {
     BGemm sh = up;
@@ -238,7 +256,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
       sh.B = w == 0 ? a.sw1 : a.sw3;
       sh.C = (w == 0 ? a.U : a.V) + cap * f;
-      e = launch_bgemm(sh, false, true, true, false, a.tile_start, s);
+      e = launch_bgemm(sh, false, true, false, a.tile_start, s);
     }
   }
   if (ok()) {
@@ -250,7 +268,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     y.off = a.offsets; y.n_groups = a.N; y.cap = static_cast<int32_t>(cap); y.K = static_cast<int32_t>(f);
     y.N = static_cast<int32_t>(d); y.A = a.H; y.lda = f; y.B = a.w2; y.ldb = a.ld_down; y.b_gs = d * a.ld_down;
     y.C = a.Y; y.ldc = d;
-    e = launch_bgemm(y, false, true, true, false, a.tile_start, s);
+    e = launch_bgemm(y, false, true, false, a.tile_start, s);
   }
   // ---- 2. combine backward
   if (ok()) {
@@ -262,12 +280,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   dh.off = a.offsets; dh.n_groups = a.N; dh.cap = static_cast<int32_t>(cap); dh.K = static_cast<int32_t>(d);
   dh.N = static_cast<int32_t>(f); dh.A = a.dY; dh.lda = d; dh.B = a.w2; dh.ldb = a.ld_down; dh.b_gs = d * a.ld_down;
   dh.C = a.dH; dh.ldc = f;
-  if (ok() && cap > 0) e = launch_bgemm(dh, false, false, true, false, a.tile_start, s);
+  if (ok() && cap > 0) e = launch_bgemm(dh, false, false, false, a.tile_start, s);
   if (ok() && S > 0) {
     BGemm sh = dh;
     sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.dy;
     sh.B = a.sw2; sh.C = a.dH + cap * f; sh.c_gs = T * f;
-    e = launch_bgemm(sh, false, false, true, false, a.tile_start, s);
+    e = launch_bgemm(sh, false, false, false, a.tile_start, s);
   }
   if (ok()) {
     hipLaunchKernelGGL(act_bwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.dH, a.U, a.V, a.dU,
@@ -281,7 +299,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   for (int w = 0; w < (swi ? 2 : 1) && ok() && cap > 0; ++w) {
     dxg.A = w == 0 ? a.dU : a.dV;
     dxg.B = w == 0 ? a.w1 : a.w3;
-    e = launch_bgemm(dxg, false, false, true, w == 1, a.tile_start, s);
+    e = launch_bgemm(dxg, false, false, w == 1, a.tile_start, s);
   }
   if (S > 0) {
     BGemm sh = dxg;
@@ -290,7 +308,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
       sh.A = (w == 0 ? a.dU : a.dV) + cap * f;
       sh.B = w == 0 ? a.sw1 : a.sw3;
-      e = launch_bgemm(sh, false, false, true, w == 1, a.tile_start, s);
+      e = launch_bgemm(sh, false, false, w == 1, a.tile_start, s);
     }
   }
   // ---- 4. weight gradients: rows-K, one matrix per expert
@@ -299,14 +317,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   if (ok() && a.dW2) {  // dW2 = dY^T H: [d][d_ff]
     dw.M = static_cast<int32_t>(d); dw.N = static_cast<int32_t>(f); dw.A = a.dY; dw.lda = d; dw.B = a.H; dw.ldb = f;
     dw.C = a.dW2; dw.ldc = f; dw.c_gs = d * f;
-    e = launch_bgemm(dw, true, false, true, false, a.tile_start, s);
+    e = launch_bgemm(dw, true, false, false, a.tile_start, s);
   }
   for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {  // dW1 = dU^T X, dW3 = dV^T X: [d_ff][d]
     float* out = w == 0 ? a.dW1 : a.dW3;
     if (!out) continue;
     dw.M = static_cast<int32_t>(f); dw.N = static_cast<int32_t>(d); dw.A = w == 0 ? a.dU : a.dV; dw.lda = f;
     dw.B = a.x_perm; dw.ldb = d; dw.C = out; dw.ldc = d; dw.c_gs = f * d;
-    e = launch_bgemm(dw, true, false, true, false, a.tile_start, s);
+    e = launch_bgemm(dw, true, false, false, a.tile_start, s);
   }
   if (S > 0) {
     BGemm sw{};
@@ -314,14 +332,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     if (ok() && a.dsW2) {
       sw.M = static_cast<int32_t>(d); sw.N = static_cast<int32_t>(f); sw.A = a.dy; sw.lda = d;
       sw.B = a.H + cap * f; sw.ldb = f; sw.b_gs = T * f; sw.C = a.dsW2; sw.ldc = f; sw.c_gs = d * f;
-      e = launch_bgemm(sw, true, false, true, false, a.tile_start, s);
+      e = launch_bgemm(sw, true, false, false, a.tile_start, s);
     }
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
       float* out = w == 0 ? a.dsW1 : a.dsW3;
       if (!out) continue;
       sw.M = static_cast<int32_t>(f); sw.N = static_cast<int32_t>(d); sw.A = (w == 0 ? a.dU : a.dV) + cap * f;
       sw.lda = f; sw.a_gs = T * f; sw.B = a.x; sw.ldb = d; sw.b_gs = 0; sw.C = out; sw.ldc = d; sw.c_gs = f * d;
-      e = launch_bgemm(sw, true, false, true, false, a.tile_start, s);
+      e = launch_bgemm(sw, true, false, false, a.tile_start, s);
     }
   }
   if (ok() && !swi && a.db1) {
@@ -344,17 +362,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
       BGemm r{};
       r.n_groups = 1; r.rows_all = static_cast<int32_t>(T); r.M = a.N; r.N = static_cast<int32_t>(d);
       r.A = h == 0 ? a.dl_hi : a.dl_lo; r.lda = a.ldl; r.B = a.x; r.ldb = d; r.C = a.dWr; r.ldc = d;
-      e = launch_bgemm(r, true, false, true, h == 1, a.tile_start, s);
+      e = launch_bgemm(r, true, false, h == 1, a.tile_start, s);
       if (!ok()) break;
     }
     BGemm x{};
     x.n_groups = 1; x.rows_all = static_cast<int32_t>(T); x.K = a.N; x.N = static_cast<int32_t>(d);
     x.A = h == 0 ? a.dl_hi : a.dl_lo; x.lda = a.ldl; x.B = a.w_router; x.ldb = d; x.C = a.dxr; x.ldc = d;
-    e = launch_bgemm(x, false, false, true, h == 1, a.tile_start, s);
+    e = launch_bgemm(x, false, false, h == 1, a.tile_start, s);
   }
   if (ok() && a.dbr) {
-    hipLaunchKernelGGL(colsum_kernel<float>, dim3(blocks_for(a.N), 1), dim3(kThreads), 0, s, a.dl32,
-                       static_cast<int64_t>(a.N), nullptr, 0, T, static_cast<int64_t>(a.N), a.dbr);
+    hipLaunchKernelGGL(router_bias_grad_kernel, dim3(static_cast<unsigned>(a.N)), dim3(kThreads), 0, s, a.dl32, T,
+                       a.N, a.dbr);
     check();
   }
   // ---- 6. dx

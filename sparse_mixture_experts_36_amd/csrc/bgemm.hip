@@ -7,12 +7,14 @@
 // form they are the contraction (dW2 = dY^T H, dW1 = dU^T X), so every group
 // has its own k range and writes its own output matrix.
 //
-// Tiles of 128 x 128 outputs, 4 waves (2 x 2), each 64 x 64 as 4 x 4 MFMA
-// 16x16x32 fragments; k-steps of 32 through LDS rows of 32 k (+8 pad). An
-// operand stored k-contiguous is copied to LDS in 16-byte chunks; one stored
-// with m (or n) contiguous is loaded in 16-byte chunks along m and written to
-// LDS transposed, one bf16 at a time. The next k-step's global loads are in
-// flight while the current one computes. Rows, columns and k past the ends
+// Tiles of 128 x 256 outputs (m x n), 4 waves (2 x 2), each 64 x 128 as
+// 4 x 8 MFMA 16x16x32 fragments; k-steps of 64 through LDS rows of 64 k (+8 pad), the
+// next step's global loads in flight while the current one computes.
+// An operand stored k-contiguous is copied in 16-byte chunks. One stored m-
+// (or n-) contiguous is loaded as 4 k-rows x 8 columns per thread (four
+// 16-byte loads), transposed in registers and written as eight 8-byte runs
+// of 4 k. The 16-byte k-chunks of LDS row R sit at chunk ^ ((R / 8) % 8), so
+// that those writes spread over the banks. Rows, columns and k past the ends
 // load zeros; outputs past the ends are not written.
 #include "common.h"
 #include "kernels.h"
@@ -21,9 +23,11 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kT = 128;   // tile edge
-constexpr int kBK = 32;   // k per step
-constexpr int kLS = kBK + 8;  // LDS row (bf16): 80 bytes
+constexpr int kT = 128;   // tile rows (m)
+constexpr int kBN = 256;  // tile columns (n)
+constexpr int kFN = kBN / 32;  // n fragments per wave
+constexpr int kBK = 64;   // k per step
+constexpr int kLS = kBK + 8;  // LDS row (bf16): 144 bytes
 
 __device__ __forceinline__ int group_rows(const BGemm& p, int g, int& r0) {
   if (!p.off) {
@@ -53,11 +57,76 @@ __global__ __launch_bounds__(kThreads) void bgemm_plan_kernel(BGemm p, int32_t* 
   }
 }
 
-template <bool ROWS_K, bool B_KC, bool C_F32, bool ACC>
-__global__ __launch_bounds__(kThreads) void bgemm_kernel(BGemm p, const int32_t* tile_start) {
+// LDS element offset of (row, 16-byte k-chunk c) with the chunk swizzle.
+__device__ __forceinline__ int lds_at(int row, int c) { return row * kLS + ((c ^ ((row >> 3) & 7)) << 3); }
+
+// One operand tile (ROWS rows x 64 k) per k-step. KC: element (row, k) at
+// src[row * ld + k], ROWS / 32 16-byte chunks a thread; otherwise at
+// src[k * ld + row], ROWS / 128 units of 4 k-rows x 8 rows a thread. Rows >=
+// nrows and k >= nk read as zero.
+template <bool KC, int ROWS>
+struct Stage {
+  static constexpr int NV = KC ? ROWS / 32 : 4 * (ROWS / 128);
+  static constexpr int RC = ROWS / 8;  // 8-row chunks (transposed form)
+  uint4 v[NV];
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t ld, int nrows, int nk, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    if (KC) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = tid + i * kThreads, row = c >> 3, k = k0 + (c & 7) * 8;
+        if (row < nrows && k < nk) v[i] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(row) * ld + k);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NV / 4; ++u) {
+        const int t = tid + u * kThreads, row = (t % RC) * 8, kq = t / RC;
+        if (row < nrows) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = k0 + kq * 4 + i;
+            if (k < nk) v[4 * u + i] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(k) * ld + row);
+          }
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* S, int tid) const {
+    if (KC) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = tid + i * kThreads;
+        *reinterpret_cast<uint4*>(S + lds_at(c >> 3, c & 7)) = v[i];
+      }
+    } else {
+      // v[4u + i] holds rows 8mc..8mc+7 at k = 4kq + i; each row's four k go
+      // to one 8-byte run
+#pragma unroll
+      for (int u = 0; u < NV / 4; ++u) {
+        const int t = tid + u * kThreads, mc = t % RC, kq = t / RC;
+        const uint4* x = v + 4 * u;
+        const uint32_t w[4][4] = {{x[0].x, x[0].y, x[0].z, x[0].w}, {x[1].x, x[1].y, x[1].z, x[1].w},
+                                  {x[2].x, x[2].y, x[2].z, x[2].w}, {x[3].x, x[3].y, x[3].z, x[3].w}};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 lo = make_uint2((w[0][j] & 0xFFFFu) | (w[1][j] << 16), (w[2][j] & 0xFFFFu) | (w[3][j] << 16));
+          const uint2 hi = make_uint2((w[0][j] >> 16) | (w[1][j] & 0xFFFF0000u),
+                                      (w[2][j] >> 16) | (w[3][j] & 0xFFFF0000u));
+          const int r = mc * 8 + 2 * j;
+          *reinterpret_cast<uint2*>(S + lds_at(r, kq >> 1) + (kq & 1) * 4) = lo;
+          *reinterpret_cast<uint2*>(S + lds_at(r + 1, kq >> 1) + (kq & 1) * 4) = hi;
+        }
+      }
+    }
+  }
+};
+
+template <bool ROWS_K, bool B_KC, bool ACC>
+__global__ __launch_bounds__(kThreads, 2) void bgemm_kernel(BGemm p, const int32_t* tile_start) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kT * kLS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kT * kLS];
-  const int ntn = (p.N + kT - 1) / kT;
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLS];
+  const int ntn = (p.N + kBN - 1) / kBN;
   int g, mt, nt;
   if (ROWS_K || !p.off) {
     const int mtn = ((ROWS_K ? p.M : p.rows_all) + kT - 1) / kT;
@@ -84,97 +153,59 @@ __global__ __launch_bounds__(kThreads) void bgemm_kernel(BGemm p, const int32_t*
   const int rows = group_rows(p, g, r0);
   const int M = ROWS_K ? p.M : rows;
   const int K = ROWS_K ? rows : p.K;
-  const int m0 = mt * kT, n0 = nt * kT;
+  const int m0 = mt * kT, n0 = nt * kBN;
   if (!ROWS_K && m0 >= M) return;
 
-  const uint16_t* A = p.A + p.a_gs * g + (ROWS_K ? 0 : static_cast<int64_t>(r0 + m0) * p.lda);
-  const uint16_t* B = p.B + p.b_gs * g;
+  // A tile source: rows-M k-contiguous rows r0 + m0.., rows-K [k][m] from row r0
+  const uint16_t* A = p.A + p.a_gs * g +
+                      (ROWS_K ? static_cast<int64_t>(r0) * p.lda + m0 : static_cast<int64_t>(r0 + m0) * p.lda);
+  const uint16_t* B = p.B + p.b_gs * g +
+                      (B_KC ? static_cast<int64_t>(n0) * p.ldb
+                            : static_cast<int64_t>(ROWS_K ? r0 : 0) * p.ldb + n0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, c16 = lane & 15;
 
-  // two 16-byte chunks per operand and thread and k-step
-  auto load = [&](int k0, uint4 (&ra)[2], uint4 (&rb)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      ra[i] = make_uint4(0, 0, 0, 0);
-      rb[i] = make_uint4(0, 0, 0, 0);
-      if (!ROWS_K) {  // A k-contiguous: row c / 4, k chunk c % 4
-        const int r = c >> 2, k = k0 + (c & 3) * 8;
-        if (m0 + r < M && k < K) ra[i] = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(r) * p.lda + k);
-      } else {  // A m-contiguous: k row c / 16, m chunk c % 16
-        const int kk = c >> 4, m = m0 + (c & 15) * 8;
-        if (k0 + kk < K && m < M)
-          ra[i] = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(r0 + k0 + kk) * p.lda + m);
-      }
-      if (B_KC) {  // B(k, n) at B[n ldb + k]: row n = c / 4, k chunk c % 4
-        const int n = n0 + (c >> 2), k = k0 + (c & 3) * 8;
-        if (n < p.N && k < K) rb[i] = *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(n) * p.ldb + k);
-      } else {  // B(k, n) at B[(k (+ r0)) ldb + n]: k row c / 16, n chunk c % 16
-        const int kk = c >> 4, n = n0 + (c & 15) * 8;
-        const int64_t brow = (ROWS_K ? r0 : 0) + k0 + kk;
-        if (k0 + kk < K && n < p.N) rb[i] = *reinterpret_cast<const uint4*>(B + brow * p.ldb + n);
-      }
-    }
-  };
-  auto store = [&](const uint4 (&ra)[2], const uint4 (&rb)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      if (!ROWS_K) {
-        *reinterpret_cast<uint4*>(As + (c >> 2) * kLS + (c & 3) * 8) = ra[i];
-      } else {
-        const int kk = c >> 4, m = (c & 15) * 8;
-        const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          As[(m + 2 * e) * kLS + kk] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-          As[(m + 2 * e + 1) * kLS + kk] = static_cast<uint16_t>(w[e] >> 16);
-        }
-      }
-      if (B_KC) {
-        *reinterpret_cast<uint4*>(Bs + (c >> 2) * kLS + (c & 3) * 8) = rb[i];
-      } else {
-        const int kk = c >> 4, n = (c & 15) * 8;
-        const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Bs[(n + 2 * e) * kLS + kk] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-          Bs[(n + 2 * e + 1) * kLS + kk] = static_cast<uint16_t>(w[e] >> 16);
-        }
-      }
-    }
-  };
-
-  floatx4_t acc[4][4];
+  floatx4_t acc[4][kFN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kFN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[2], rb[2];
-  if (K > 0) load(0, ra, rb);
+  Stage<!ROWS_K, kT> sa;
+  Stage<B_KC, kBN> sb;
+  if (K > 0) {
+    sa.load(A, p.lda, M - m0, K, 0, tid);
+    sb.load(B, p.ldb, p.N - n0, K, 0, tid);
+  }
   for (int k0 = 0; k0 < K; k0 += kBK) {
-    store(ra, rb);
+    sa.store(As, tid);
+    sb.store(Bs, tid);
     __syncthreads();
-    if (k0 + kBK < K) load(k0 + kBK, ra, rb);  // in flight during this step's MFMAs
-    uint4 af[4], bf[4];
+    if (k0 + kBK < K) {  // in flight during this step's MFMAs
+      sa.load(A, p.lda, M - m0, K, k0 + kBK, tid);
+      sb.load(B, p.ldb, p.N - n0, K, k0 + kBK, tid);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 16 + c16) * kLS + q * 8);
+    for (int s2 = 0; s2 < kBK / 32; ++s2) {
+      // the A fragments stay in registers; the B fragments are read one at a
+      // time, so that the accumulators and both stages fit two waves a SIMD
+      uint4 af[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + j * 16 + c16) * kLS + q * 8);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(As + lds_at(wm * 64 + i * 16 + c16, s2 * 4 + q));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < kFN; ++j) {
+        const uint4 bf = *reinterpret_cast<const uint4*>(Bs + lds_at(wn * (kBN / 2) + j * 16 + c16, s2 * 4 + q));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16x16x32(af[i], bf, acc[i][j]);
+      }
+    }
     __syncthreads();
   }
 
   // lane (q, c16) of fragment (i, j): rows 4q + r, column c16
   const int64_t crow0 = ROWS_K ? 0 : r0;
+  float* Cg = static_cast<float*>(p.C) + p.c_gs * g;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -182,27 +213,20 @@ __global__ __launch_bounds__(kThreads) void bgemm_kernel(BGemm p, const int32_t*
       const int m = m0 + wm * 64 + i * 16 + q * 4 + r;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + c16;
+      for (int j = 0; j < kFN; ++j) {
+        const int n = n0 + wn * (kBN / 2) + j * 16 + c16;
         if (n >= p.N) continue;
-        const int64_t ci = p.c_gs * g + (crow0 + m) * p.ldc + n;
-        if (C_F32) {
-          float* C = static_cast<float*>(p.C) + ci;
-          *C = ACC ? *C + acc[i][j][r] : acc[i][j][r];
-        } else {
-          uint16_t* C = static_cast<uint16_t*>(p.C) + ci;
-          *C = f32_to_bf16(ACC ? bf16_to_f32(*C) + acc[i][j][r] : acc[i][j][r]);
-        }
+        float* C = Cg + (crow0 + m) * p.ldc + n;
+        *C = ACC ? *C + acc[i][j][r] : acc[i][j][r];
       }
     }
 }
 
 }  // namespace
 
-hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool c_f32, bool acc, int32_t* tile_start,
-                        hipStream_t s) {
+hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool acc, int32_t* tile_start, hipStream_t s) {
   if (p.n_groups <= 0 || p.N <= 0) return hipSuccess;
-  const int ntn = (p.N + kT - 1) / kT;
+  const int ntn = (p.N + kBN - 1) / kBN;
   int64_t grid;
   if (rows_k || !p.off) {
     grid = static_cast<int64_t>(p.n_groups) * (((rows_k ? p.M : p.rows_all) + kT - 1) / kT) * ntn;
@@ -212,16 +236,16 @@ hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool c_f32, bool
   }
   if (grid <= 0) return hipSuccess;
   const dim3 gd(static_cast<unsigned>(grid));
-#define MOE_BG(RK, BK, CF, AC)                                                                      \
-  if (rows_k == RK && b_kc == BK && c_f32 == CF && acc == AC) {                                     \
-    hipLaunchKernelGGL((bgemm_kernel<RK, BK, CF, AC>), gd, dim3(kThreads), 0, s, p, tile_start);    \
+#define MOE_BG(RK, BK, AC)                                                                          \
+  if (rows_k == RK && b_kc == BK && acc == AC) {                                                    \
+    hipLaunchKernelGGL((bgemm_kernel<RK, BK, AC>), gd, dim3(kThreads), 0, s, p, tile_start);        \
     return hipGetLastError();                                                                       \
   }
-  MOE_BG(false, true, true, false)   // forward recompute: U = X W^T, Y = H W2^T (fp32)
-  MOE_BG(false, false, true, false)  // dH = dY W2, dX = dU W1 (fp32)
-  MOE_BG(false, false, true, true)   // dX += dV W3
-  MOE_BG(true, false, true, false)   // dW = dY^T H, dU^T X (fp32)
-  MOE_BG(true, false, true, true)    // dW_r += dl_lo^T x
+  MOE_BG(false, true, false)   // forward recompute: U = X W^T, Y = H W2^T
+  MOE_BG(false, false, false)  // dH = dY W2, dX = dU W1, dl W_r
+  MOE_BG(false, false, true)   // dX += dV W3, += dl_lo W_r
+  MOE_BG(true, false, false)   // dW = dY^T H, dU^T X, dl^T x
+  MOE_BG(true, false, true)    // dW_r += dl_lo^T x
 #undef MOE_BG
   return hipErrorInvalidValue;
 }

@@ -184,7 +184,7 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
                              hipStream_t s);
 
 // ---------------------------------------------------------------- backward GEMM
-// C_g(m, n) (+)= sum_k A_g(m, k) B_g(k, n), bf16 operands, fp32 accumulation.
+// C_g(m, n) (+)= sum_k A_g(m, k) B_g(k, n), bf16 operands, fp32 accumulation and output.
 // Group g's rows are [off[g], off[g+1]) clamped to cap (off null: rows_all rows
 // from 0 for every group). rows-M form: those rows are A's rows (A k-contiguous,
 // lda) and C's rows, K fixed. rows-K form: they are the contraction, A m-
@@ -203,8 +203,7 @@ struct BGemm {
   int64_t ldc, c_gs;
 };
 // tile_start: [n_groups + 1] ints of workspace (rows-M form with offsets)
-hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool c_f32, bool acc, int32_t* tile_start,
-                        hipStream_t s);
+hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool acc, int32_t* tile_start, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // Token-choice layer backward, bf16 activations and weights. The caller has
