@@ -68,9 +68,11 @@ def lib():
         L.orc_moe_output_ec.argtypes = [sp, vp, wp, vp, vp, vp, i64, vp]
         L.orc_combine_ec.argtypes = [sp, vp, vp, vp, vp, vp]
         L.orc_backward.argtypes = [sp, vp, wp, vp, ctypes.c_double, ctypes.c_double] + [vp] * 11
+        L.orc_backward_sampled.argtypes = [sp, vp, wp, vp, ctypes.c_double, ctypes.c_double, vp, ctypes.c_int64, vp,
+                                           vp, ctypes.c_int64, vp, vp, vp]
         for name in ("orc_router_logits", "orc_route", "orc_dispatch", "orc_expert_rows",
                      "orc_moe_output", "orc_combine", "orc_route_ec", "orc_dispatch_ec", "orc_moe_output_ec",
-                     "orc_combine_ec", "orc_backward", "orc_abi_version", "orc_threads"):
+                     "orc_combine_ec", "orc_backward", "orc_backward_sampled", "orc_abi_version", "orc_threads"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("orc_bf16_value", "orc_gelu", "orc_silu"):
             getattr(L, name).restype = ctypes.c_double
@@ -329,6 +331,27 @@ def backward(inp, dy: np.ndarray, c_aux: float = 0.0, c_z: float = 0.0) -> Grads
                               _p(g.dWr), _p(g.dbr), _p(g.dW1), _p(g.dW3), _p(g.dW2), _p(g.db1), _p(g.db2),
                               _p(g.dsW1), _p(g.dsW3), _p(g.dsW2)), "backward")
     return g
+
+
+def backward_sampled(inp, dy: np.ndarray, tokens, units, c_aux: float = 0.0, c_z: float = 0.0):
+    """Parts of backward() at sizes where the whole pass is too slow: dx rows
+    of `tokens`, and for each (expert e, hidden unit i) in `units`, row i of
+    dW1[e] / dW3[e] and column i of dW2[e]. Returns (dx_rows [n][d],
+    dW1_rows [m][d], dW3_rows [m][d] or None, dW2_cols [m][d]), fp64."""
+    wl = inp.wl
+    shape = shape_of(wl)
+    w, _keep = weights_of(inp)
+    tok = np.ascontiguousarray(tokens, np.int32)
+    un = np.ascontiguousarray(units, np.int32).reshape(-1, 2)
+    d = wl.d
+    dx = np.empty((len(tok), d))
+    d1, d2 = np.empty((len(un), d)), np.empty((len(un), d))
+    d3 = np.empty((len(un), d)) if wl.act == 1 else None
+    dy = np.ascontiguousarray(dy)
+    _check(lib().orc_backward_sampled(ctypes.byref(shape), _p(inp.x), ctypes.byref(w), _p(dy), c_aux, c_z, _p(tok),
+                                      len(tok), _p(dx), _p(un), len(un), _p(d1), _p(d3), _p(d2)),
+           "backward_sampled")
+    return dx, d1, d3, d2
 
 
 def threads() -> int:

@@ -873,6 +873,200 @@ int orc_backward(const OrcShape* s, const void* x, const OrcWeights* w, const vo
   return 0;
 }
 
+// Parts of the same gradients, for layers whose whole backward is too slow
+// here: dx for the listed tokens, and for each listed (expert e, hidden unit i)
+// pair, row i of dW1[e] and of dW3[e] (SwiGLU) and column i of dW2[e]. Each
+// value follows orc_backward's definitions term by term; only the rows and
+// units that these outputs need are formed. The router, the statistics and
+// the capacity cut still run over all T tokens.
+// tokens [n_tok] in [0, T); units [n_units][2] = (e, i), e in [0, N), i in
+// [0, d_ff). Outputs: dx_rows [n_tok][d], dW1_rows / dW3_rows [n_units][d]
+// (dW3_rows may be null), dW2_cols [n_units][d].
+int orc_backward_sampled(const OrcShape* s, const void* x, const OrcWeights* w, const void* dy, double c_aux,
+                         double c_z, const int32_t* tokens, int64_t n_tok, double* dx_rows, const int32_t* units,
+                         int64_t n_units, double* dW1_rows, double* dW3_rows, double* dW2_cols) {
+  if (!shape_ok_tc(s) || !x || !w || !w->w_router || !dy) return -1;
+  if (s->w_dtype >= 2) return -1;
+  const int64_t T = s->T, d = s->d, f = s->d_ff, N = s->n_experts, k = s->top_k, S = s->n_shared;
+  const bool swi = (s->act == 1);
+  if (n_tok > 0 && (!tokens || !dx_rows)) return -1;
+  if (n_units > 0 && (!units || !dW1_rows || !dW2_cols)) return -1;
+  for (int64_t a = 0; a < n_tok; ++a)
+    if (tokens[a] < 0 || tokens[a] >= T) return -1;
+  for (int64_t b = 0; b < n_units; ++b)
+    if (units[2 * b] < 0 || units[2 * b] >= N || units[2 * b + 1] < 0 || units[2 * b + 1] >= f) return -1;
+
+  std::vector<double> l64(static_cast<size_t>(T * N));
+  std::vector<float> l32(static_cast<size_t>(T * N));
+  orc_router_logits(s, x, w, l64.data(), l32.data());
+  std::vector<int32_t> idx(static_cast<size_t>(T * k));
+  std::vector<double> gate(static_cast<size_t>(T * k)), p(static_cast<size_t>(T * N)), lse(static_cast<size_t>(T));
+  std::vector<int64_t> counts(static_cast<size_t>(N));
+  orc_route(s, l32.data(), idx.data(), gate.data(), p.data(), lse.data(), nullptr, nullptr, counts.data(), nullptr,
+            nullptr, nullptr, nullptr, nullptr);
+  std::vector<int32_t> inv(static_cast<size_t>(T * k));
+  orc_dispatch(s, idx.data(), nullptr, nullptr, nullptr, inv.data(), nullptr);
+  double lm = 0.0;
+  for (int64_t t = 0; t < T; ++t) lm += lse[t];
+  lm = (T > 0) ? lm / static_cast<double>(T) : 0.0;
+
+  auto xv = [&](int64_t t, int64_t c) { return elem(x, s->act_dtype, t * d + c, 1.0); };
+  auto dyv = [&](int64_t t, int64_t c) { return elem(dy, s->act_dtype, t * d + c, 1.0); };
+  auto W1 = [&](bool sh, int64_t e, int64_t i, int64_t j) {
+    return elem(sh ? w->sw1 : w->w1, s->w_dtype, (e * f + i) * d + j, 1.0);
+  };
+  auto W3 = [&](bool sh, int64_t e, int64_t i, int64_t j) {
+    return elem(sh ? w->sw3 : w->w3, s->w_dtype, (e * f + i) * d + j, 1.0);
+  };
+  auto W2 = [&](bool sh, int64_t e, int64_t o, int64_t i) {
+    return elem(sh ? w->sw2 : w->w2, s->w_dtype, (e * d + o) * f + i, 1.0);
+  };
+
+  // dx of one token: its kept pairs, the shared experts, the router
+  for (int64_t a = 0; a < n_tok; ++a) {
+    const int64_t t = tokens[a];
+    double* out = dx_rows + a * d;
+    for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+    std::vector<double> dg(static_cast<size_t>(k), 0.0);
+    std::vector<double> U(f), V(f), H(f), Y(d), dY(d), dH(f), dU(f), dV(f), dX(d);
+    auto expert = [&](bool sh, int64_t e, double g, double* dg_out) {
+      const float* b1 = (!sh && !swi) ? w->b1 : nullptr;
+      const float* b2 = (!sh && !swi) ? w->b2 : nullptr;
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < f; ++i) {
+        double u = 0.0, v = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+          u += W1(sh, e, i, j) * xv(t, j);
+          if (swi) v += W3(sh, e, i, j) * xv(t, j);
+        }
+        if (b1) u += static_cast<double>(b1[e * f + i]);
+        U[i] = u;
+        V[i] = v;
+        H[i] = swi ? silu(u) * v : gelu(u);
+      }
+      if (dg_out) {  // the expert's output, for the gate's gradient
+#pragma omp parallel for schedule(static)
+        for (int64_t o = 0; o < d; ++o) {
+          double yo = 0.0;
+          for (int64_t i = 0; i < f; ++i) yo += W2(sh, e, o, i) * H[i];
+          if (b2) yo += static_cast<double>(b2[e * d + o]);
+          Y[o] = yo;
+        }
+        double acc = 0.0;
+        for (int64_t o = 0; o < d; ++o) acc += dyv(t, o) * Y[o];
+        *dg_out = acc;
+      }
+      for (int64_t o = 0; o < d; ++o) dY[o] = g * dyv(t, o);
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < f; ++i) {
+        double h = 0.0;
+        for (int64_t o = 0; o < d; ++o) h += dY[o] * W2(sh, e, o, i);
+        const double u = U[i];
+        if (swi) {
+          const double sg = 1.0 / (1.0 + std::exp(-u));
+          dU[i] = h * V[i] * (sg + u * sg * (1.0 - sg));
+          dV[i] = h * u * sg;
+        } else {
+          const double cdf = 0.5 * (1.0 + std::erf(u / std::sqrt(2.0)));
+          const double pdf = std::exp(-0.5 * u * u) / std::sqrt(2.0 * 3.14159265358979323846);
+          dU[i] = h * (cdf + u * pdf);
+          dV[i] = 0.0;
+        }
+      }
+#pragma omp parallel for schedule(static)
+      for (int64_t j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < f; ++i) {
+          acc += dU[i] * W1(sh, e, i, j);
+          if (swi) acc += dV[i] * W3(sh, e, i, j);
+        }
+        dX[j] = acc;
+      }
+      for (int64_t j = 0; j < d; ++j) out[j] += dX[j];
+    };
+    for (int64_t j = 0; j < k; ++j)
+      if (inv[t * k + j] >= 0) expert(false, idx[t * k + j], gate[t * k + j], &dg[j]);
+    for (int64_t sh = 0; sh < S; ++sh) expert(true, sh, 1.0, nullptr);
+    // router: the same chain as orc_backward for this token's row of dl
+    std::vector<double> dp(static_cast<size_t>(N), 0.0), dl(static_cast<size_t>(N), 0.0);
+    const int32_t* St = idx.data() + t * k;
+    const double* g = gate.data() + t * k;
+    const double* pt = p.data() + t * N;
+    if (s->gating == 0) {
+      for (int64_t j = 0; j < k; ++j) dp[St[j]] += dg[j];
+    } else if (s->gating == 1) {
+      double ssum = 0.0, dot = 0.0;
+      for (int64_t j = 0; j < k; ++j) { ssum += pt[St[j]]; dot += dg[j] * g[j]; }
+      for (int64_t j = 0; j < k; ++j) dp[St[j]] += (dg[j] - dot) / ssum;
+    } else {
+      double dot = 0.0;
+      for (int64_t j = 0; j < k; ++j) dot += dg[j] * g[j];
+      for (int64_t j = 0; j < k; ++j) dl[St[j]] += g[j] * (dg[j] - dot);
+    }
+    for (int64_t e = 0; e < N; ++e)
+      dp[e] += c_aux * s->aux_alpha * static_cast<double>(N) * (static_cast<double>(counts[e]) /
+                                                               static_cast<double>(T * k)) / static_cast<double>(T);
+    double dpp = 0.0;
+    for (int64_t e = 0; e < N; ++e) dpp += dp[e] * pt[e];
+    for (int64_t e = 0; e < N; ++e) dl[e] += pt[e] * (dp[e] - dpp) + c_z * 2.0 * lm / static_cast<double>(T) * pt[e];
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t e = 0; e < N; ++e) acc += dl[e] * elem(w->w_router, s->act_dtype, e * d + c, 1.0);
+      out[c] += acc;
+    }
+  }
+
+  // one hidden unit i of expert e over the expert's kept rows (ascending tokens)
+  for (int64_t b = 0; b < n_units; ++b) {
+    const int64_t e = units[2 * b], i = units[2 * b + 1];
+    std::vector<int64_t> tok;
+    std::vector<double> gr;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t j = 0; j < k; ++j)
+        if (idx[t * k + j] == e && inv[t * k + j] >= 0) {
+          tok.push_back(t);
+          gr.push_back(gate[t * k + j]);
+        }
+    const int64_t n = static_cast<int64_t>(tok.size());
+    std::vector<double> H(n), dU(n), dV(n);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      const int64_t t = tok[r];
+      double u = 0.0, v = 0.0, h = 0.0;
+      for (int64_t j = 0; j < d; ++j) {
+        u += W1(false, e, i, j) * xv(t, j);
+        if (swi) v += W3(false, e, i, j) * xv(t, j);
+      }
+      if (!swi && w->b1) u += static_cast<double>(w->b1[e * f + i]);
+      for (int64_t o = 0; o < d; ++o) h += gr[r] * dyv(t, o) * W2(false, e, o, i);
+      H[r] = swi ? silu(u) * v : gelu(u);
+      if (swi) {
+        const double sg = 1.0 / (1.0 + std::exp(-u));
+        dU[r] = h * v * (sg + u * sg * (1.0 - sg));
+        dV[r] = h * u * sg;
+      } else {
+        const double cdf = 0.5 * (1.0 + std::erf(u / std::sqrt(2.0)));
+        const double pdf = std::exp(-0.5 * u * u) / std::sqrt(2.0 * 3.14159265358979323846);
+        dU[r] = h * (cdf + u * pdf);
+        dV[r] = 0.0;
+      }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < d; ++c) {
+      double a1 = 0.0, a3 = 0.0, a2 = 0.0;
+      for (int64_t r = 0; r < n; ++r) {
+        a1 += dU[r] * xv(tok[r], c);
+        a3 += dV[r] * xv(tok[r], c);
+        a2 += gr[r] * dyv(tok[r], c) * H[r];
+      }
+      dW1_rows[b * d + c] = a1;
+      if (dW3_rows) dW3_rows[b * d + c] = swi ? a3 : 0.0;
+      dW2_cols[b * d + c] = a2;
+    }
+  }
+  return 0;
+}
+
 // Exact decoders, exported so that tests can pin them to library conversions.
 double orc_bf16_value(uint16_t b) { return bf16_value(b); }
 double orc_e4m3_value(uint8_t q) { return e4m3_value(q); }

@@ -147,3 +147,48 @@ def test_backward_router_only_when_all_dropped():
     for k in ("dw1", "dw3", "dw2", "dsw1", "dsw3", "dsw2"):
         assert not torch.any(g[k]).item(), k
     assert torch.any(g["dw_router"]).item()
+
+
+def test_backward_mixtral_prefill_full_size_sampled():
+    """The Mixtral-shape prefill layer at full size (T=4096, d=4096,
+    d_ff=14336, 8 experts, top-2), weights with the padded rows the benchmark
+    uses, same dy and loss coefficients: dx rows of sampled tokens and, for
+    sampled (expert, hidden unit) pairs, the dW1 / dW3 rows and dW2 columns,
+    against the oracle's sampled backward. Tokens routed differently from the
+    oracle (near ties), and experts they touch, are left out of the sample."""
+    import torch
+    wl = gen.MIXTRAL_PREFILL
+    say(f"backward full size {wl.name}: generating inputs")
+    inp = gen.make_inputs(wl)
+    dy = gen.normal(97, (wl.T, wl.d), 1.0, gen.BF16)
+    t = device_weights(inp, pad=64)
+    s = shape_of(wl)
+    x = dev(inp.x)
+    logits = torch.empty(wl.T, wl.n_experts, dtype=torch.float32, device="cuda")
+    idx = torch.empty(wl.T, wl.top_k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(wl.T, wl.top_k, dtype=torch.float32, device="cuda")
+    moe.route(s, x, t["w_router"], t["b_router"], logits, idx, gw)
+    g = moe.alloc_grads(s)
+    moe.backward(s, x, moe.weights_struct(t), dev(dy), g, 1.0, 1e-3)
+    torch.cuda.synchronize()
+    so = oracle.shape_of(wl)
+    _, l32 = oracle.router_logits(so, inp.x, inp)
+    r = oracle.route(so, l32)
+    gi = host(idx)
+    diff = (gi != r.topk_idx).any(1)
+    moved = set(gi[diff].ravel().tolist()) | set(r.topk_idx[diff].ravel().tolist())
+    tokens = [tk for tk in (0, 1, 2047, 3001, 4095) if not diff[tk]]
+    units = [(e, i) for e, i in ((0, 0), (1, 4097), (3, 7777), (5, 12000), (7, 14335)) if e not in moved]
+    say(f"  routed differently: {int(diff.sum())} tokens; sampled {len(tokens)} tokens, {len(units)} units")
+    assert tokens and units
+    dx, d1, d3, d2 = oracle.backward_sampled(inp, dy, tokens, units, 1.0, 1e-3)
+    got = as_f64(host(g["dx"][torch.tensor(tokens, device="cuda")]))
+    e = rel_err(got, dx)
+    say(f"  dx rows: max|d|/max|ref| = {e:.3e}")
+    assert e <= TOL
+    for name, ref, pick in (("dw1", d1, lambda m, e_, i: m[e_, i]), ("dw3", d3, lambda m, e_, i: m[e_, i]),
+                            ("dw2", d2, lambda m, e_, i: m[e_, :, i])):
+        got = np.stack([host(pick(g[name], e_, i)).astype(np.float64) for e_, i in units])
+        e = rel_err(got, ref)
+        say(f"  {name} sampled: max|d|/max|ref| = {e:.3e}")
+        assert e <= TOL, name

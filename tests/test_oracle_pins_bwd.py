@@ -114,3 +114,28 @@ def test_backward_linear_in_dy():
         lhs = getattr(gab, name)
         rhs = getattr(ga, name) + 2 * getattr(gb, name)
         assert np.allclose(lhs, rhs, rtol=0, atol=1e-9 * np.abs(rhs).max()), name
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_sampled_backward_equals_the_full_one(case):
+    """backward_sampled's dx rows and dW1 / dW3 rows and dW2 columns are the
+    matching entries of the full backward (itself pinned to autograd above)."""
+    case = dict(case)
+    cf = case.pop("cf")
+    wl = _tiny(T=40, d=32, d_ff=48, cf=cf, **case)
+    inp = _with_random_biases(gen.make_inputs(wl, seed=21))
+    if wl.act_dtype == gen.BF16:
+        dy = gen.normal(97, (wl.T, wl.d), 1.0, gen.BF16, seed=3)
+    else:
+        dy = gen.normal(97, (wl.T, wl.d), 1.0, gen.F32, seed=3)
+    full = oracle.backward(inp, dy, 1.0, 0.1)
+    tokens = [0, 7, 19, wl.T - 1]
+    units = [(0, 0), (1, 5), (wl.n_experts - 1, wl.d_ff - 1), (wl.n_experts // 2, 17)]
+    dx, d1, d3, d2 = oracle.backward_sampled(inp, dy, tokens, units, 1.0, 0.1)
+    scale = np.abs(full.dx).max()
+    assert np.allclose(dx, full.dx[tokens], rtol=0, atol=1e-12 * scale)
+    for b, (e, i) in enumerate(units):
+        assert np.allclose(d1[b], full.dW1[e, i], rtol=0, atol=1e-12 * np.abs(full.dW1).max()), (e, i)
+        assert np.allclose(d2[b], full.dW2[e, :, i], rtol=0, atol=1e-12 * np.abs(full.dW2).max()), (e, i)
+        if full.dW3 is not None:
+            assert np.allclose(d3[b], full.dW3[e, i], rtol=0, atol=1e-12 * np.abs(full.dW3).max()), (e, i)
