@@ -203,6 +203,8 @@ struct BwdWs {
   uint16_t* x_perm;
   float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
   uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
+  int32_t* wr_off;
+  float* wr_part;
 };
 int32_t bwd_ldl(const moe_shape& s) { return (s.n_experts + 7) / 8 * 8; }
 BwdWs carve_bwd(Carver& c, const moe_shape& s) {
@@ -236,6 +238,9 @@ BwdWs carve_bwd(Carver& c, const moe_shape& s) {
   w.dl_hi = c.take<uint16_t>(T * static_cast<size_t>(bwd_ldl(s)));
   w.dl_lo = c.take<uint16_t>(T * static_cast<size_t>(bwd_ldl(s)));
   w.dxr = c.take<float>(T * d);
+  const int32_t sp = moe::bwd_router_splits(s.T, s.n_experts, s.d);
+  w.wr_off = c.take<int32_t>(static_cast<size_t>(sp) + 1);
+  w.wr_part = sp > 1 ? c.take<float>(static_cast<size_t>(sp) * N * d) : nullptr;
   return w;
 }
 
@@ -723,6 +728,9 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights
   a.dl_hi = w.dl_hi;
   a.dl_lo = w.dl_lo;
   a.tile_start = w.tile_start;
+  a.wr_splits = moe::bwd_router_splits(s.T, s.n_experts, s.d);
+  a.wr_off = w.wr_off;
+  a.wr_part = w.wr_part;
   a.dx = static_cast<uint16_t*>(g->dx);
   a.dWr = g->dw_router;
   a.dbr = g->db_router;

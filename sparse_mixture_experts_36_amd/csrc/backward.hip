@@ -211,6 +211,22 @@ __global__ __launch_bounds__(kThreads) void router_bias_grad_kernel(const float*
   }
 }
 
+// Bounds of `splits` equal token chunks: off[i] = i T / splits.
+__global__ void split_bounds_kernel(int32_t* off, int32_t splits, int64_t T) {
+  const int i = threadIdx.x;
+  if (i <= splits) off[i] = static_cast<int32_t>(i * T / splits);
+}
+
+// out[i] = sum over chunks c (in order) of part[c][i].
+__global__ __launch_bounds__(kThreads) void sum_parts_kernel(const float* part, int32_t splits, int64_t n,
+                                                             float* out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.f;
+  for (int c = 0; c < splits; ++c) v += part[c * n + i];
+  out[i] = v;
+}
+
 // dx_t = sum over its kept slots of dX[row] (ascending) + the shared experts'
 // rows + the router term, to bf16.
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a, const float* dX, const float* dxr, uint16_t* dx) {
@@ -357,11 +373,18 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(router_bwd_kernel, dim3(static_cast<unsigned>(ceil_div(T, 16))), dim3(kThreads), 0, s, a);
     check();
   }
+  const bool wr_split = a.dWr && a.wr_splits > 1;
+  if (ok() && wr_split) {
+    hipLaunchKernelGGL(split_bounds_kernel, dim3(1), dim3(128), 0, s, a.wr_off, a.wr_splits, T);
+    check();
+  }
   for (int h = 0; h < 2 && ok(); ++h) {  // dW_r = dl^T x and dx_r = dl W_r, each as hi + lo
-    if (a.dWr) {
+    if (a.dWr) {  // token chunks as groups of a rows-K product, one partial matrix each
       BGemm r{};
-      r.n_groups = 1; r.rows_all = static_cast<int32_t>(T); r.M = a.N; r.N = static_cast<int32_t>(d);
-      r.A = h == 0 ? a.dl_hi : a.dl_lo; r.lda = a.ldl; r.B = a.x; r.ldb = d; r.C = a.dWr; r.ldc = d;
+      r.off = wr_split ? a.wr_off : nullptr; r.n_groups = wr_split ? a.wr_splits : 1;
+      r.cap = static_cast<int32_t>(T); r.rows_all = static_cast<int32_t>(T);
+      r.M = a.N; r.N = static_cast<int32_t>(d); r.A = h == 0 ? a.dl_hi : a.dl_lo; r.lda = a.ldl; r.B = a.x;
+      r.ldb = d; r.C = wr_split ? a.wr_part : a.dWr; r.ldc = d; r.c_gs = wr_split ? a.N * d : 0;
       e = launch_bgemm(r, true, false, h == 1, a.tile_start, s);
       if (!ok()) break;
     }
@@ -369,6 +392,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     x.n_groups = 1; x.rows_all = static_cast<int32_t>(T); x.K = a.N; x.N = static_cast<int32_t>(d);
     x.A = h == 0 ? a.dl_hi : a.dl_lo; x.lda = a.ldl; x.B = a.w_router; x.ldb = d; x.C = a.dxr; x.ldc = d;
     e = launch_bgemm(x, false, false, h == 1, a.tile_start, s);
+  }
+  if (ok() && wr_split) {
+    hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks_for(a.N * d)), dim3(kThreads), 0, s, a.wr_part, a.wr_splits,
+                       a.N * d, a.dWr);
+    check();
   }
   if (ok() && a.dbr) {
     hipLaunchKernelGGL(router_bias_grad_kernel, dim3(static_cast<unsigned>(a.N)), dim3(kThreads), 0, s, a.dl32, T,

@@ -226,11 +226,27 @@ struct BwdArgs {
   float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
   uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
   int32_t* tile_start;
+  // dW_r = dl^T x over wr_splits token chunks (bounds wr_off [splits + 1]),
+  // each into its own fp32 partial [N][d] of wr_part, summed in chunk order
+  int32_t wr_splits;
+  int32_t* wr_off;
+  float* wr_part;
   // outputs (weight gradients may be null: not computed)
   uint16_t* dx;
   float *dWr, *dbr, *dW1, *dW3, *dW2, *db1, *db2, *dsW1, *dsW3, *dsW2;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+// Token chunks of dW_r: enough workgroups for a few experts' rows (about 512
+// tiles), at least 64 tokens a chunk, at most 64 chunks and 2^25 partial floats.
+inline int32_t bwd_router_splits(int64_t T, int32_t N, int64_t d) {
+  const int64_t tiles = ((N + 127) / 128) * ((d + 255) / 256);
+  int64_t sp = (512 + tiles - 1) / tiles;
+  const int64_t by_tokens = (T + 63) / 64, by_mem = (int64_t{1} << 25) / (static_cast<int64_t>(N) * d);
+  if (sp > by_tokens) sp = by_tokens;
+  if (sp > 64) sp = 64;
+  if (sp > by_mem) sp = by_mem;
+  return static_cast<int32_t>(sp < 1 ? 1 : sp);
+}
 
 // ---------------------------------------------------------------- combine
 struct CombineArgs {
