@@ -205,7 +205,15 @@ struct BwdWs {
   uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
   int32_t* wr_off;
   float* wr_part;
+  // the forward's grouped FFN for the recompute (bwd_uses_ffn)
+  moe::GroupDesc *groups, *groups_t;
+  int32_t *ffn_tiles, *ffn_tiles_t, *active;
+  float* split_part;
 };
+int64_t bwd_rows(const moe_shape& s) { return routed_row_cap(s) + static_cast<int64_t>(s.n_shared) * s.T; }
+bool bwd_uses_ffn(const moe_shape& s) {
+  return moe::ffn_uses_dma(s.act_dtype, s.w_dtype, bwd_rows(s), s.act, s.d, s.d_ff);
+}
 int32_t bwd_ldl(const moe_shape& s) { return (s.n_experts + 7) / 8 * 8; }
 BwdWs carve_bwd(Carver& c, const moe_shape& s) {
   const size_t T = static_cast<size_t>(s.T), k = static_cast<size_t>(s.top_k), N = s.n_experts;
@@ -241,6 +249,18 @@ BwdWs carve_bwd(Carver& c, const moe_shape& s) {
   const int32_t sp = moe::bwd_router_splits(s.T, s.n_experts, s.d);
   w.wr_off = c.take<int32_t>(static_cast<size_t>(sp) + 1);
   w.wr_part = sp > 1 ? c.take<float>(static_cast<size_t>(sp) * N * d) : nullptr;
+  w.groups = w.groups_t = nullptr;
+  w.ffn_tiles = w.ffn_tiles_t = w.active = nullptr;
+  w.split_part = nullptr;
+  if (bwd_uses_ffn(s)) {
+    const size_t G = static_cast<size_t>(s.n_experts + s.n_shared);
+    w.groups = c.take<moe::GroupDesc>(2 * G);
+    w.groups_t = c.take<moe::GroupDesc>(2 * G);
+    w.ffn_tiles = c.take<int32_t>(G + 1);
+    w.ffn_tiles_t = c.take<int32_t>(G + 1);
+    w.active = c.take<int32_t>(G + 1);
+    w.split_part = c.take<float>(static_cast<size_t>(moe::kSplitPartFloats));
+  }
   return w;
 }
 
@@ -731,6 +751,26 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights
   a.wr_splits = moe::bwd_router_splits(s.T, s.n_experts, s.d);
   a.wr_off = w.wr_off;
   a.wr_part = w.wr_part;
+  a.use_ffn = bwd_uses_ffn(s);
+  if (a.use_ffn) {  // U, V, H and Y from the forward's grouped FFN
+    FfnWs fw{};
+    fw.h = w.H;
+    fw.groups = w.groups;
+    fw.tile_start = w.ffn_tiles;
+    fw.groups_t = w.groups_t;
+    fw.tile_start_t = w.ffn_tiles_t;
+    fw.active = w.active;
+    fw.split_part = w.split_part;
+    // its bf16 outputs are not used: the routed ones land in dY and the
+    // shared ones in dX, both written again later in the pass
+    a.ffn = ffn_args(s, w.x_perm, s.d, w.offsets, x, weights, w.dY, w.dX, fw);
+    a.ffn.ld_h = s.d_ff;
+    a.ffn.pre_up_u = w.U;
+    a.ffn.pre_up_v = w.V;
+    a.ffn.ld_pre_up = s.d_ff;
+    a.ffn.pre_down = w.Y;
+    a.ffn.ld_pre_down = s.d;
+  }
   a.dx = static_cast<uint16_t*>(g->dx);
   a.dWr = g->dw_router;
   a.dbr = g->db_router;

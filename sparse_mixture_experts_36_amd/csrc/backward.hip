@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
       const float g = a.topk_w[t * a.k + j];
       const float* y = a.Y + static_cast<int64_t>(row) * a.d;
       uint16_t* dY = a.dY + static_cast<int64_t>(row) * a.d;
-      const float* b2 = (a.act == 0 && a.b2) ? a.b2 + static_cast<int64_t>(e) * a.d : nullptr;
+      // Y holds b2 already when the forward's FFN recomputed it
+      const float* b2 = (a.act == 0 && a.b2 && !a.use_ffn) ? a.b2 + static_cast<int64_t>(e) * a.d : nullptr;
       for (int64_t c = tid; c < a.d; c += kThreads) {
         const float v = bf16_to_f32(dy[c]);
         dY[c] = f32_to_bf16(g * v);
@@ -255,36 +256,42 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   auto ok = [&]() { return e == hipSuccess; };
   auto check = [&]() { if (e == hipSuccess) e = hipGetLastError(); };
 
-  // ---- 1. forward again (router and permutation are done by the caller)
-  BGemm up{};  // U / V = X W^T: routed rows from x_perm, shared rows from x
-  up.off = a.offsets; up.n_groups = a.N; up.cap = static_cast<int32_t>(cap); up.K = static_cast<int32_t>(d);
-  up.N = static_cast<int32_t>(f); up.A = a.x_perm; up.lda = d; up.ldb = a.ld_up; up.b_gs = f * a.ld_up;
-  up.ldc = f;
-  for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
-    up.B = w == 0 ? a.w1 : a.w3;
-    up.C = w == 0 ? a.U : a.V;
-    e = launch_bgemm(up, false, true, false, a.tile_start, s);
-  }
-  if (S > 0) {
-    BGemm sh = up;
-    sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.x;
-    sh.c_gs = T * f;
+  // ---- 1. forward again (router and permutation are done by the caller):
+  // on the forward's grouped FFN when its DMA tiles take these rows (U, V,
+  // H and Y in one up and one down launch), else on the backward GEMM
+  if (a.use_ffn) {
+    e = launch_grouped_ffn(a.ffn, s);
+  } else {
+    BGemm up{};  // U / V = X W^T: routed rows from x_perm, shared rows from x
+    up.off = a.offsets; up.n_groups = a.N; up.cap = static_cast<int32_t>(cap); up.K = static_cast<int32_t>(d);
+    up.N = static_cast<int32_t>(f); up.A = a.x_perm; up.lda = d; up.ldb = a.ld_up; up.b_gs = f * a.ld_up;
+    up.ldc = f;
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
-      sh.B = w == 0 ? a.sw1 : a.sw3;
-      sh.C = (w == 0 ? a.U : a.V) + cap * f;
-      e = launch_bgemm(sh, false, true, false, a.tile_start, s);
+      up.B = w == 0 ? a.w1 : a.w3;
+      up.C = w == 0 ? a.U : a.V;
+      e = launch_bgemm(up, false, true, false, a.tile_start, s);
     }
-  }
-  if (ok()) {
-    hipLaunchKernelGGL(act_fwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.U, a.V, a.H, rows);
-    check();
-  }
-  if (ok() && cap > 0) {  // Y = H W2^T for the routed rows (the gates' gradient)
-    BGemm y{};
-    y.off = a.offsets; y.n_groups = a.N; y.cap = static_cast<int32_t>(cap); y.K = static_cast<int32_t>(f);
-    y.N = static_cast<int32_t>(d); y.A = a.H; y.lda = f; y.B = a.w2; y.ldb = a.ld_down; y.b_gs = d * a.ld_down;
-    y.C = a.Y; y.ldc = d;
-    e = launch_bgemm(y, false, true, false, a.tile_start, s);
+    if (S > 0) {
+      BGemm sh = up;
+      sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.x;
+      sh.c_gs = T * f;
+      for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
+        sh.B = w == 0 ? a.sw1 : a.sw3;
+        sh.C = (w == 0 ? a.U : a.V) + cap * f;
+        e = launch_bgemm(sh, false, true, false, a.tile_start, s);
+      }
+    }
+    if (ok()) {
+      hipLaunchKernelGGL(act_fwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.U, a.V, a.H, rows);
+      check();
+    }
+    if (ok() && cap > 0) {  // Y = H W2^T for the routed rows (the gates' gradient)
+      BGemm y{};
+      y.off = a.offsets; y.n_groups = a.N; y.cap = static_cast<int32_t>(cap); y.K = static_cast<int32_t>(f);
+      y.N = static_cast<int32_t>(d); y.A = a.H; y.lda = f; y.B = a.w2; y.ldb = a.ld_down; y.b_gs = d * a.ld_down;
+      y.C = a.Y; y.ldc = d;
+      e = launch_bgemm(y, false, true, false, a.tile_start, s);
+    }
   }
   // ---- 2. combine backward
   if (ok()) {

@@ -64,6 +64,12 @@ struct GemmParams {
   const int32_t* tile_start;  // [n_groups+1] row-tile prefix
   float* split_part;          // fp32 partial tiles of the k-split tail, or null (no split)
   int32_t ncu;                // compute units of the device
+  // fp32 copies of the values before the activation, for the layer backward
+  // (DMA tiles only; null: not written): pre_u gets W1 x (+ b1) or the down
+  // GEMM's output with its bias, pre_v gets W3 x; _r for routed groups, _s for
+  // shared ones; row c_row0 + r of the group, pitch ld_pre
+  float *pre_u_r, *pre_u_s, *pre_v_r, *pre_v_s;
+  int64_t ld_pre;
 };
 
 enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_PLAIN = 2 };
@@ -490,6 +496,46 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
   }
 }
 
+// fp32 copies of a DMA tile's values before the activation, for the layer
+// backward (bf16 weights): W1 x (+ b1) into pre_u and W3 x into pre_v, or the
+// down GEMM's output with its bias into pre_u; straight from the fragments
+// (16 lanes write 64 contiguous bytes of a row). Called only when requested.
+template <int EPI, int BM, int W>
+__device__ __forceinline__ void dma_store_pre(const GemmParams& p, const TileInfo& ti,
+                                              floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN]) {
+  using namespace dma;
+  using C_ = Cfg<BM, W>;
+  constexpr int BNO = bno(EPI);
+  constexpr int WTB = C_::WTB, FN = C_::FN, WGN = C_::WGN, WTM = C_::WTM;
+  constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
+  constexpr int FNO = WTO / 16;
+  const bool shared = ti.g >= p.n_routed;
+  float* pu = shared ? p.pre_u_s : p.pre_u_r;
+  if (!pu) return;
+  float* pv = EPI == EPI_SWIGLU ? (shared ? p.pre_v_s : p.pre_v_r) : nullptr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
+  const int n0 = ti.n_tile * BNO;
+  const float* bias = (!shared && p.bias) ? p.bias + static_cast<int64_t>(ew) * p.Nout + n0 : nullptr;
+  const int64_t off = (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ld_pre + n0;
+#pragma unroll
+  for (int i = 0; i < C_::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wm * WTM + i * 16 + q * 4 + r;
+      if (row >= ti.rows) continue;
+#pragma unroll
+      for (int j = 0; j < FNO; ++j) {
+        const int col = wn * WTO + j * 16 + c16;
+        const int64_t o = off + static_cast<int64_t>(row) * p.ld_pre + col;
+        pu[o] = acc[i][j][r] + (bias ? bias[col] : 0.f);
+        if (pv) pv[o] = acc[i][j + FN / 2][r];
+      }
+    }
+}
+
 // fp32 partial tile of a k-chunk, in fragment order: fragment (wave, i, j) is
 // 64 lanes x 4 floats, 1 KB contiguous.
 template <int BM, int W>
@@ -734,6 +780,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
         *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
+  dma_store_pre<EPI, BM, W>(p, ti, acc);
   dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
 }
 
@@ -962,6 +1009,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
         *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
+  dma_store_pre<EPI, BM, W>(p, ti, acc);
   dma_store_tile<EPI, BM, W, HB>(p, ti, acc, SA0);
 }
 
@@ -995,6 +1043,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams 
         acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM, W>(p.split_part, b * sp.s + c, wave, i, j) +
                                                          lane * 4);
   }
+  dma_store_pre<EPI, BM, W>(p, ti, acc);
   dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
 }
 
@@ -1243,9 +1292,10 @@ hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipS
 // rows, else 128 (less padding in each group's last tile). Measured: the
 // fine-grained layer (about 400 rows a group, two shared experts of 8192)
 // runs 4 % faster on 256-row tiles, the Switch layer (at most 320) 11 % slower.
+// Widths that the 256-column tiles do not fit take the 128 x 128 tiles.
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
-  if (rows < 2048) return kReg128;
+  if (rows < 2048 || !wide_tiles_fit(a.act, a.d, a.d_ff)) return kReg128;
   if (a.w_dtype == 2 || (a.w_dtype == 3 && !a.wdq)) return kReg256;
   return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
@@ -1272,9 +1322,17 @@ size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int
   return static_cast<size_t>((up + down) * (n_routed + n_shared) * 2);
 }
 
+// Integer weights written out as bf16 for the DMA tiles (only when those
+// tiles take the call; otherwise the codes are decoded in registers).
+static bool dequantizes(const FfnArgs& a) {
+  if (a.w_dtype != 3 || !a.wdq) return false;
+  const int cfg = pick_cfg(a);
+  return cfg == kDma256 || cfg == kDma128;
+}
+
 WeightClasses weight_classes(const FfnArgs& a) {
   WeightClasses wc{};
-  if (a.w_dtype != 3 || a.wdq) {
+  if (a.w_dtype != 3 || dequantizes(a)) {
     wc.n = 1;
     wc.wf[0] = a.w_dtype == 2 ? kWE4m3 : kWBf16;
     return wc;
@@ -1332,6 +1390,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   if (a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T == 0) return hipSuccess;  // no rows at all
   const bool f32 = (a.act_dtype == 0);
   const int cfg = pick_cfg(a);
+  if ((a.pre_up_u || a.pre_down) && ((cfg != kDma256 && cfg != kDma128) || a.w_dtype != 1))
+    return hipErrorInvalidValue;  // DMA tiles on bf16 weights only
   const FfnPlan pl = ffn_plan(a);
   const int bm = pl.bm;
   GroupDesc* up = pl.up;
@@ -1351,7 +1411,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   const bool swi = (a.act == 1);
   // integer weights on the prefill tiles: every expert's codes to bf16 first
   // (exact), then the bf16 tiles with the row scales per output column
-  const bool dq = (a.w_dtype == 3 && a.wdq);
+  const bool dq = dequantizes(a);
   if (dq) {
     const int64_t ldu = a.d + kActPad, ldd = a.d_ff + kActPad;
     const int64_t up_e = a.d_ff * ldu, down_e = a.d * ldd;  // bf16 elements per expert matrix
@@ -1385,6 +1445,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
 
   GemmParams p{};
   p.col_scaled = dq ? 1 : 0;
+  p.pre_u_r = p.pre_u_s = a.pre_up_u;
+  p.pre_v_r = p.pre_v_s = a.pre_up_v;
+  p.ld_pre = a.ld_pre_up;
   p.split_part = a.split_part;
   p.ncu = device_cus();
   p.n_routed = a.n_routed;
@@ -1453,6 +1516,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   p.C_r = a.y_perm;
   p.C_s = a.y_shared;
   p.ldc = a.d;
+  p.pre_u_r = a.pre_down;  // routed rows only
+  p.pre_u_s = p.pre_v_r = p.pre_v_s = nullptr;
+  p.ld_pre = a.ld_pre_down;
   p.K = static_cast<int32_t>(a.d_ff);
   p.Nout = static_cast<int32_t>(a.d);
   p.groups = down;

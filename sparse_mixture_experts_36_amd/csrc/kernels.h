@@ -130,7 +130,23 @@ struct FfnArgs {
   const uint8_t* w_bits;      // integer weights (w_dtype 3): HOST [n_routed], 8 or 4
   const uint8_t* sw_bits;     // HOST [n_shared]
   void* wdq;                  // integer weights, prefill: workspace for every expert's codes as bf16 (dq_bytes), or null
+  // the layer backward's forward recompute (DMA tiles only, else the launch
+  // fails): fp32 W1 x (+ b1) and W3 x of every row (pitch ld_pre_up), and the
+  // down GEMM's routed outputs with their bias (pitch ld_pre_down); null: none
+  float *pre_up_u, *pre_up_v, *pre_down;
+  int64_t ld_pre_up, ld_pre_down;
 };
+// Whether the 256-column tiles (LDS-DMA, and the 256 x 256 register-staged
+// ones) fit a layer: each GEMM's output width a multiple of the columns a
+// tile yields (256; the SwiGLU up tile yields 128 of its 256 weight rows).
+inline bool wide_tiles_fit(int32_t act, int64_t d, int64_t d_ff) {
+  return d % 256 == 0 && (act == 1 ? d_ff % 128 == 0 : d_ff % 256 == 0);
+}
+// Whether the grouped FFN of these rows runs on the LDS-DMA tiles (bf16
+// activations and weights, 2048 rows or more, widths that fit them).
+inline bool ffn_uses_dma(int32_t act_dtype, int32_t w_dtype, int64_t rows, int32_t act, int64_t d, int64_t d_ff) {
+  return act_dtype == 1 && w_dtype == 1 && rows >= 2048 && wide_tiles_fit(act, d, d_ff);
+}
 // Integer weights on the prefill tiles: the codes of every expert are first
 // written out as bf16 (exact) into this many workspace bytes, with rows
 // kActPad elements longer than d / d_ff, and the bf16 tiles apply the row
@@ -231,6 +247,10 @@ struct BwdArgs {
   int32_t wr_splits;
   int32_t* wr_off;
   float* wr_part;
+  // with use_ffn the forward recompute runs on the forward's grouped FFN
+  // (ffn: its arguments, writing U, V, H and Y with the bias b2 included)
+  bool use_ffn;
+  FfnArgs ffn;
   // outputs (weight gradients may be null: not computed)
   uint16_t* dx;
   float *dWr, *dbr, *dW1, *dW3, *dW2, *db1, *db2, *dsW1, *dsW3, *dsW2;

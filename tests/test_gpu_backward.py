@@ -2,8 +2,9 @@
 backward on the same seeded inputs: dx, the router weight and bias, every
 expert's and shared expert's weights, the GELU biases, with and without the
 L_aux and z terms, in all three token-choice gate modes, with capacity drops,
-skewed routing, empty experts and an all-dropped layer. Every size spans
-several 128-row tiles with ragged tails.
+skewed routing, empty experts and an all-dropped layer, on both forward-
+recompute paths (the backward GEMM below 2048 rows, the forward's grouped FFN
+from 2048 rows). Every size spans several tiles with ragged tails.
 
 The gradients are only comparable when both sides route identically, so each
 case first checks that the library's selection equals the oracle's (the seeds
@@ -48,6 +49,11 @@ CASES = {
     "mixtral-like-T512": _wl("b6", 512, 1024, 1536, 8, 2, gen.SWIGLU, gen.TOPK_SOFTMAX),
     "fine-grained-like-64x6-shared2": _wl("b7", 256, 256, 256, 64, 6, gen.SWIGLU, gen.SOFTMAX_TOPK, n_shared=2,
                                           zipf=1.0),
+    # 2048 rows or more: the forward recompute runs on the forward's grouped
+    # FFN (256-row DMA tiles here; 128-row ones with GELU, biases and drops)
+    "swiglu-ffn-dma256-T2048-shared1": _wl("b8", 2048, 256, 512, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
+    "gelu-ffn-dma128-renorm-cf1-biases": _wl("b9", 1024, 256, 384, 8, 2, gen.GELU, gen.SOFTMAX_TOPK_RENORM, cf=1.0,
+                                             zipf=1.0),
 }
 
 

@@ -110,6 +110,10 @@ REDUCED = {
     "switch-like": gen.SWITCH_TOP1.with_(T=2048, d=512, d_ff=1024),
     "switch-like-fp8": gen.SWITCH_TOP1_FP8.with_(T=2048, d=512, d_ff=1024),
     "switch-like-renorm": gen.SWITCH_TOP1.with_(T=1024, d=256, d_ff=512, gating=gen.SOFTMAX_TOPK_RENORM),
+    # 2048 rows or more with widths the 256-column tiles do not fit (GELU
+    # d_ff = 384; d = 384): the 128 x 128 tiles take them
+    "switch-like-d_ff-384": gen.SWITCH_TOP1.with_(T=4096, d=512, d_ff=384),
+    "mixtral-like-d-384": gen.MIXTRAL_PREFILL.with_(T=1024, d=384, d_ff=512),
     # decode-sized: the weight-streaming path
     "mixtral-like-decode-T1": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
     "mixtral-like-decode-T64": gen.MIXTRAL_PREFILL.with_(T=64, d=1024, d_ff=1536),

@@ -47,6 +47,9 @@ REDUCED = {
     "fine-grained-like-int": FG.with_(T=512, d=512, d_ff=256),
     "switch-like-int-gelu": SW.with_(T=2048, d=512, d_ff=1024),
     "switch-like-int-gelu-decode": SW.with_(T=128, d=512, d_ff=1024),
+    # 2048 rows or more, but a GELU d_ff the 256-column tiles do not fit: the
+    # codes are decoded in registers on 128 x 128 tiles, not written out as bf16
+    "switch-like-int-gelu-d_ff-384": SW.with_(T=4096, d=512, d_ff=384),
 }
 
 
