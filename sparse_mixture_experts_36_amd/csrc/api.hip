@@ -238,8 +238,8 @@ BwdWs carve_bwd(Carver& c, const moe_shape& s) {
   w.Y = c.take<float>(cap * d);
   w.dY = c.take<uint16_t>(cap * d);
   w.dH = c.take<float>(rows * f);
-  w.dU = c.take<uint16_t>(rows * f);
-  w.dV = swi ? c.take<uint16_t>(rows * f) : nullptr;
+  w.dU = c.take<uint16_t>(rows * f * (swi ? 2 : 1));  // [dU | dV] rows for SwiGLU
+  w.dV = (swi && w.dU) ? w.dU + f : nullptr;
   w.dX = c.take<float>(rows * d);
   w.dg = c.take<float>(T * k);
   w.dl32 = c.take<float>(T * N);
@@ -709,6 +709,7 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights
   a.act = s.act;
   a.gating = s.gating;
   a.ldl = bwd_ldl(s);
+  a.ld_du = s.act == MOE_ACT_SWIGLU ? 2 * s.d_ff : s.d_ff;
   a.aux_alpha = s.aux_alpha;
   a.c_aux = c_aux;
   a.c_z = c_z;

@@ -12,7 +12,8 @@
 //     (+ b1) and V = X W3^T in fp32, H = act(U, V) in bf16, the routed
 //     outputs Y = H W2^T; shared experts on all T rows;
 //  2. combine backward: dY_row = g dy_t (bf16), dg = <dy_t, Y_row + b2>;
-//  3. dH = dY W2 (fp32); dU, dV from dH, U, V (bf16); dX = dU W1 + dV W3 (fp32);
+//  3. dH = dY W2 (fp32); dU, dV from dH, U, V (bf16, one [dU | dV] row each);
+//     dX = [dU dV] [W1; W3] (fp32);
 //  4. dW2 = dY^T H, dW1 = dU^T X, dW3 = dV^T X (fp32, one matrix per expert),
 //     b1 / b2 gradients as column sums;
 //  5. router: dl from dg through the gates' mode, the L_aux and z terms and
@@ -92,14 +93,15 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a, const floa
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= rows * a.d_ff) return;
   const float u = U[i], h = dH[i];
+  const int64_t o = (i / a.d_ff) * a.ld_du + i % a.d_ff;  // dU / dV rows of pitch ld_du
   if (a.act == 1) {
     const float sg = 1.f / (1.f + expf(-u));
-    dU[i] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
-    dV[i] = f32_to_bf16(h * u * sg);
+    dU[o] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
+    dV[o] = f32_to_bf16(h * u * sg);
   } else {
     const float cdf = 0.5f * (1.f + erff(u * 0.70710678118654752f));
     const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-    dU[i] = f32_to_bf16(h * (cdf + u * pdf));
+    dU[o] = f32_to_bf16(h * (cdf + u * pdf));
   }
 }
 
@@ -298,41 +300,37 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(combine_bwd_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, a);
     check();
   }
-  // ---- 3. dH, dU / dV, dX
+  // ---- 3. dH, dU / dV, dX on the DMA tiles (B read along the weights' rows)
+  const int64_t ldu = a.ld_du;  // dU and dV share rows: [dU | dV] (SwiGLU) or dU
   BGemm dh{};  // dH = dY W2 (routed), dy W2s (shared)
   dh.off = a.offsets; dh.n_groups = a.N; dh.cap = static_cast<int32_t>(cap); dh.K = static_cast<int32_t>(d);
   dh.N = static_cast<int32_t>(f); dh.A = a.dY; dh.lda = d; dh.B = a.w2; dh.ldb = a.ld_down; dh.b_gs = d * a.ld_down;
   dh.C = a.dH; dh.ldc = f;
-  if (ok() && cap > 0) e = launch_bgemm(dh, false, false, false, a.tile_start, s);
+  if (ok() && cap > 0) e = launch_bgemm_dma(dh, a.tile_start, s);
   if (ok() && S > 0) {
     BGemm sh = dh;
     sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T); sh.A = a.dy;
     sh.B = a.sw2; sh.C = a.dH + cap * f; sh.c_gs = T * f;
-    e = launch_bgemm(sh, false, false, false, a.tile_start, s);
+    e = launch_bgemm_dma(sh, a.tile_start, s);
   }
   if (ok()) {
     hipLaunchKernelGGL(act_bwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.dH, a.U, a.V, a.dU,
                        a.dV, rows);
     check();
   }
-  BGemm dxg{};  // dX = dU W1 (+ dV W3)
-  dxg.off = a.offsets; dxg.n_groups = a.N; dxg.cap = static_cast<int32_t>(cap); dxg.K = static_cast<int32_t>(f);
-  dxg.N = static_cast<int32_t>(d); dxg.lda = f; dxg.ldb = a.ld_up; dxg.b_gs = f * a.ld_up; dxg.C = a.dX;
-  dxg.ldc = d;
-  for (int w = 0; w < (swi ? 2 : 1) && ok() && cap > 0; ++w) {
-    dxg.A = w == 0 ? a.dU : a.dV;
-    dxg.B = w == 0 ? a.w1 : a.w3;
-    e = launch_bgemm(dxg, false, false, w == 1, a.tile_start, s);
-  }
-  if (S > 0) {
+  // dX = [dU dV] [W1; W3]: one product over k = 2 d_ff, W3 past k = d_ff
+  BGemm dxg{};
+  dxg.off = a.offsets; dxg.n_groups = a.N; dxg.cap = static_cast<int32_t>(cap);
+  dxg.K = static_cast<int32_t>(swi ? 2 * f : f); dxg.N = static_cast<int32_t>(d); dxg.A = a.dU; dxg.lda = ldu;
+  dxg.B = a.w1; dxg.B2 = swi ? a.w3 : nullptr; dxg.k_split = static_cast<int32_t>(f); dxg.ldb = a.ld_up;
+  dxg.b_gs = f * a.ld_up; dxg.C = a.dX; dxg.ldc = d;
+  if (ok() && cap > 0) e = launch_bgemm_dma(dxg, a.tile_start, s);
+  if (ok() && S > 0) {
     BGemm sh = dxg;
     sh.off = nullptr; sh.n_groups = static_cast<int32_t>(S); sh.rows_all = static_cast<int32_t>(T);
-    sh.a_gs = T * f; sh.b_gs = f * a.ld_up; sh.C = a.dX + cap * d; sh.c_gs = T * d;
-    for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
-      sh.A = (w == 0 ? a.dU : a.dV) + cap * f;
-      sh.B = w == 0 ? a.sw1 : a.sw3;
-      e = launch_bgemm(sh, false, false, w == 1, a.tile_start, s);
-    }
+    sh.A = a.dU + cap * ldu; sh.a_gs = T * ldu; sh.B = a.sw1; sh.B2 = swi ? a.sw3 : nullptr;
+    sh.C = a.dX + cap * d; sh.c_gs = T * d;
+    e = launch_bgemm_dma(sh, a.tile_start, s);
   }
   // ---- 4. weight gradients: rows-K, one matrix per expert
   BGemm dw{};
@@ -345,7 +343,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {  // dW1 = dU^T X, dW3 = dV^T X: [d_ff][d]
     float* out = w == 0 ? a.dW1 : a.dW3;
     if (!out) continue;
-    dw.M = static_cast<int32_t>(f); dw.N = static_cast<int32_t>(d); dw.A = w == 0 ? a.dU : a.dV; dw.lda = f;
+    dw.M = static_cast<int32_t>(f); dw.N = static_cast<int32_t>(d); dw.A = w == 0 ? a.dU : a.dV; dw.lda = ldu;
     dw.B = a.x_perm; dw.ldb = d; dw.C = out; dw.ldc = d; dw.c_gs = f * d;
     e = launch_bgemm(dw, true, false, false, a.tile_start, s);
   }
@@ -360,13 +358,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
       float* out = w == 0 ? a.dsW1 : a.dsW3;
       if (!out) continue;
-      sw.M = static_cast<int32_t>(f); sw.N = static_cast<int32_t>(d); sw.A = (w == 0 ? a.dU : a.dV) + cap * f;
-      sw.lda = f; sw.a_gs = T * f; sw.B = a.x; sw.ldb = d; sw.b_gs = 0; sw.C = out; sw.ldc = d; sw.c_gs = f * d;
+      sw.M = static_cast<int32_t>(f); sw.N = static_cast<int32_t>(d); sw.A = (w == 0 ? a.dU : a.dV) + cap * ldu;
+      sw.lda = ldu; sw.a_gs = T * ldu; sw.B = a.x; sw.ldb = d; sw.b_gs = 0; sw.C = out; sw.ldc = d; sw.c_gs = f * d;
       e = launch_bgemm(sw, true, false, false, a.tile_start, s);
     }
   }
   if (ok() && !swi && a.db1) {
-    hipLaunchKernelGGL(colsum_kernel<uint16_t>, dim3(blocks_for(f), a.N), dim3(kThreads), 0, s, a.dU, f, a.offsets,
+    hipLaunchKernelGGL(colsum_kernel<uint16_t>, dim3(blocks_for(f), a.N), dim3(kThreads), 0, s, a.dU, ldu, a.offsets,
                        static_cast<int32_t>(cap), cap, f, a.db1);
     check();
   }

@@ -1,0 +1,259 @@
+// Grouped rows-M GEMM of the layer backward with B stored n-contiguous, on
+// LDS DMA: C_g = A_g B_g in fp32, A_g the group's rows (k-contiguous), B_g
+// element (k, n) at B[k ldb + n] (the weights in their [out][in] layout read
+// along their rows: dH = dY W2; dX = [dU dV] [W1; W3] with B2 = W3 past
+// k_split = d_ff).
+//
+// Tile 256 x 256, 8 waves (4 x 2), each 64 x 128 as 4 x 8 MFMA 16x16x32
+// fragments. k-stages of 32 in a ring of four LDS buffers per operand (16 KB
+// each), filled by global_load_lds three stages ahead: no VGPR staging, so
+// the loads in flight are bounded by LDS, not by registers.
+//  - A stage: 256 rows x 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 1) & 3).
+//  - B stage: 32 k-rows x 256 columns (512 bytes), as stored; chunk c of k-row
+//    k at c ^ key(k). The MFMA operand (8 consecutive k of one column per lane)
+//    comes from two ds_read_b64_tr_b16: in each 16-lane group, lane i receives
+//    element i mod 4 of the 8-byte runs that lanes 4j + i/4 (j = 0..3) point
+//    at, so lane s points at k-row k0 + s/4, columns n0 + 4 (s mod 4), and
+//    lane i gets k0..k0+3 of column n0 + i. key(k) spreads the eight k-rows one
+//    half-wave reads over all banks.
+// Rows past a group's end and columns past N load clamped (valid) data that
+// is computed and never stored.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kNT = 512;          // 8 waves
+constexpr int kTM = 256, kTN = 256, kTK = 32;
+constexpr int kSA = kTM * kTK * 2;  // A stage bytes (16 KB)
+constexpr int kSB = kTK * kTN * 2;  // B stage bytes (16 KB)
+constexpr int kXcd = 8;
+
+// s_waitcnt immediates: vmcnt(n) alone; lgkmcnt(0) alone
+constexpr int vm_wait(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
+constexpr int kLgkm0 = 0xc07f;
+
+__device__ __forceinline__ int group_rows(const BGemm& p, int g, int& r0) {
+  if (!p.off) {
+    r0 = 0;
+    return p.rows_all;
+  }
+  const int a = max(0, min(p.off[g], p.cap)), b = max(a, min(p.off[g + 1], p.cap));
+  r0 = a;
+  return b - a;
+}
+
+__device__ __forceinline__ int bkey(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+
+__global__ __launch_bounds__(256) void dma_plan_kernel(BGemm p, int32_t* tile_start) {
+  __shared__ int32_t s_mt[kMaxGroups];
+  for (int g = threadIdx.x; g < p.n_groups; g += 256) {
+    int r0;
+    s_mt[g] = (group_rows(p, g, r0) + kTM - 1) / kTM;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int g = 0; g < p.n_groups; ++g) {
+      tile_start[g] = acc;
+      acc += s_mt[g];
+    }
+    tile_start[p.n_groups] = acc;
+  }
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define MOE_L(x) ((__attribute__((address_space(3))) void*)(x))
+
+__global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* tile_start) {
+  __shared__ __attribute__((aligned(16))) char A0[kSA];
+  __shared__ __attribute__((aligned(16))) char A1[kSA];
+  __shared__ __attribute__((aligned(16))) char A2[kSA];
+  __shared__ __attribute__((aligned(16))) char A3[kSA];
+  __shared__ __attribute__((aligned(16))) char B0[kSB];
+  __shared__ __attribute__((aligned(16))) char B1[kSB];
+  __shared__ __attribute__((aligned(16))) char B2s[kSB];
+  __shared__ __attribute__((aligned(16))) char B3[kSB];
+
+  // tile: consecutive tiles (the row tiles of one column tile) on one XCD
+  const int per_xcd = gridDim.x / kXcd;
+  const int L = (blockIdx.x % kXcd) * per_xcd + blockIdx.x / kXcd;
+  const int ntn = (p.N + kTN - 1) / kTN;
+  int g, mt, nt;
+  if (!p.off) {
+    const int mtn = (p.rows_all + kTM - 1) / kTM;
+    if (L >= p.n_groups * mtn * ntn) return;
+    g = L / (mtn * ntn);
+    nt = (L % (mtn * ntn)) / mtn;
+    mt = L % mtn;
+  } else {
+    if (L >= tile_start[p.n_groups] * ntn) return;
+    int lo = 0, hi = p.n_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_start[mid] * ntn <= L) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int mtg = tile_start[g + 1] - tile_start[g];
+    const int local = L - tile_start[g] * ntn;
+    nt = local / mtg;
+    mt = local % mtg;
+  }
+  int r0;
+  const int M = group_rows(p, g, r0);
+  const int m0 = mt * kTM, n0 = nt * kTN;
+  if (m0 >= M) return;
+  const int K = p.K, KS = K / kTK;  // a multiple of 4
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, c16 = lane & 15;
+
+  // DMA sources: wave-uniform bases, 32-bit lane offsets (elements)
+  const uint16_t* Ab = p.A + p.a_gs * g + static_cast<int64_t>(r0 + m0) * p.lda;
+  const uint16_t* Bb = p.B + p.b_gs * g + n0;
+  const uint16_t* B2b = p.B2 ? p.B2 + p.b_gs * g + n0 : nullptr;
+  uint32_t offa[2], offb[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = wave * 32 + t * 16 + (lane >> 2);                 // tile row this lane fills
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);                  // its global k-chunk
+    const int srow = min(row, M - m0 - 1);                           // rows past the group: clamped
+    offa[t] = static_cast<uint32_t>(srow * static_cast<int>(p.lda) + chunk * 8);
+    const int krow = wave * 4 + t * 2 + (lane >> 5);
+    const int lastc = (min(kTN, p.N - n0) >> 3) - 1;                 // columns past N: clamped
+    const int bc = min((lane & 31) ^ bkey(krow), lastc);
+    offb[t] = static_cast<uint32_t>(krow * static_cast<int>(p.ldb) + bc * 8);
+  }
+  const int dsta = wave * 32 * 64, dstb = wave * 4 * 512;  // byte offsets in a stage buffer
+
+  floatx4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // LDS read addresses (bytes) inside a stage
+  int rda[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 64 + i * 16 + c16;
+    rda[i] = row * 64 + ((q ^ ((row >> 1) & 3)) << 4);
+  }
+  // B fragment j, half h: k-row kr_h = 8q + 4h + c16/4, column wn 128 + 16j +
+  // 4 (c16 mod 4), i.e. chunk 16 wn + 2j + x (x = (c16 mod 4) / 2) at half
+  // c16 mod 2; bkey is even, so the swizzled chunk is 16 wn + ((2j) ^ key_h) + x
+  int rbase[2], rkey[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int krow = 8 * q + 4 * h + (c16 >> 2);
+    rbase[h] = krow * 512 + ((wn * 16 + ((c16 & 3) >> 1)) << 4) + (c16 & 1) * 8;
+    rkey[h] = bkey(krow);
+  }
+
+#define MOE_DMA(SA, SB, ks)                                                                          \
+  do {                                                                                               \
+    const int k0_ = (ks) * kTK;                                                                      \
+    const uint16_t* ba_ = Ab + k0_;                                                                  \
+    const uint16_t* bb_ = (B2b && k0_ >= p.k_split) ? B2b + static_cast<int64_t>(k0_ - p.k_split) * p.ldb \
+                                                    : Bb + static_cast<int64_t>(k0_) * p.ldb;        \
+    _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                               \
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ba_ + offa[t_]), MOE_L((SA) + dsta + t_ * 1024), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bb_ + offb[t_]), MOE_L((SB) + dstb + t_ * 1024), 16, 0, 0); \
+    }                                                                                                \
+  } while (0)
+  // the B fragment of column block j + 1 is read while block j's MFMAs run
+#define MOE_BFRAG(SB, j, OUT)                                                                        \
+  do {                                                                                               \
+    const v4s lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                         \
+        (__attribute__((address_space(3))) v4s*)((SB) + rbase[0] + (((2 * (j)) ^ rkey[0]) << 4)));    \
+    const v4s hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                         \
+        (__attribute__((address_space(3))) v4s*)((SB) + rbase[1] + (((2 * (j)) ^ rkey[1]) << 4)));    \
+    const uint2 l2_ = __builtin_bit_cast(uint2, lo_), h2_ = __builtin_bit_cast(uint2, hi_);          \
+    OUT = make_uint4(l2_.x, l2_.y, h2_.x, h2_.y);                                                    \
+  } while (0)
+#define MOE_COMPUTE(SA, SB)                                                                          \
+  do {                                                                                               \
+    uint4 af_[4], bc_, bn_;                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) af_[i_] = *reinterpret_cast<const uint4*>((SA) + rda[i_]); \
+    MOE_BFRAG(SB, 0, bc_);                                                                           \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) {                                               \
+      if (j_ + 1 < 8) MOE_BFRAG(SB, j_ + 1, bn_);                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) acc[i_][j_] = mfma16x16x32(af_[i_], bc_, acc[i_][j_]); \
+      bc_ = bn_;                                                                                     \
+    }                                                                                                \
+  } while (0)
+  // stage ks from buffers (SA, SB): wait until at most VM DMA instructions
+  // (the next stages') are in flight, barrier, refill (SAN, SBN) with stage
+  // ks + 3 when DMA, then compute. The main loop runs unconditionally (every
+  // stage refills; a conditional refill made the compiler drain all DMA at the
+  // loop head); the last four stages are written out with their own waits.
+#define MOE_STAGE(SA, SB, SAN, SBN, ks, VM, DMA)                                                     \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(vm_wait(VM));                                                         \
+    __builtin_amdgcn_s_waitcnt(kLgkm0);                                                              \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    if (DMA) MOE_DMA(SAN, SBN, (ks) + 3);                                                            \
+    MOE_COMPUTE(SA, SB);                                                                             \
+  } while (0)
+
+  MOE_DMA(A0, B0, 0);
+  MOE_DMA(A1, B1, 1);
+  MOE_DMA(A2, B2s, 2);
+  int ks = 0;
+  for (; ks + 4 < KS; ks += 4) {  // every stage refills: ks + 6 < KS
+    MOE_STAGE(A0, B0, A3, B3, ks, 8, true);
+    MOE_STAGE(A1, B1, A0, B0, ks + 1, 8, true);
+    MOE_STAGE(A2, B2s, A1, B1, ks + 2, 8, true);
+    MOE_STAGE(A3, B3, A2, B2s, ks + 3, 8, true);
+  }
+  // the last four stages: ks = KS - 4
+  MOE_STAGE(A0, B0, A3, B3, ks, 8, true);
+  MOE_STAGE(A1, B1, A0, B0, ks + 1, 8, false);
+  MOE_STAGE(A2, B2s, A1, B1, ks + 2, 4, false);
+  MOE_STAGE(A3, B3, A2, B2s, ks + 3, 0, false);
+#undef MOE_STAGE
+#undef MOE_COMPUTE
+#undef MOE_BFRAG
+#undef MOE_DMA
+
+  // lane (q, c16) of fragment (i, j): rows 4q + r, column c16
+  float* C = static_cast<float*>(p.C) + p.c_gs * g + static_cast<int64_t>(r0 + m0) * p.ldc + n0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = wm * 64 + i * 16 + q * 4 + r;
+      if (m >= M - m0) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = wn * 128 + j * 16 + c16;
+        if (n0 + n < p.N) C[static_cast<int64_t>(m) * p.ldc + n] = acc[i][j][r];
+      }
+    }
+}
+#undef MOE_L
+
+}  // namespace
+
+hipError_t launch_bgemm_dma(const BGemm& p, int32_t* tile_start, hipStream_t s) {
+  if (p.n_groups <= 0 || p.N <= 0) return hipSuccess;
+  if (p.K % 128 != 0 || p.lda % 8 != 0 || p.ldb % 8 != 0 || p.N % 8 != 0) return hipErrorInvalidValue;
+  if (p.B2 && (p.k_split % kTK != 0 || p.k_split <= 0)) return hipErrorInvalidValue;
+  const int ntn = (p.N + kTN - 1) / kTN;
+  int64_t grid;
+  if (!p.off) {
+    grid = static_cast<int64_t>(p.n_groups) * ((p.rows_all + kTM - 1) / kTM) * ntn;
+  } else {
+    hipLaunchKernelGGL(dma_plan_kernel, dim3(1), dim3(256), 0, s, p, tile_start);
+    grid = (static_cast<int64_t>(p.cap) / kTM + p.n_groups) * ntn;
+  }
+  if (grid <= 0) return hipSuccess;
+  grid = (grid + kXcd - 1) / kXcd * kXcd;
+  hipLaunchKernelGGL(bgemm_dma_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -217,9 +217,17 @@ struct BGemm {
   int64_t ldb, b_gs;
   void* C;
   int64_t ldc, c_gs;
+  // bgemm_dma only: k >= k_split reads B2 (same layout, its row k - k_split)
+  const uint16_t* B2;
+  int32_t k_split;
 };
 // tile_start: [n_groups + 1] ints of workspace (rows-M form with offsets)
 hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool acc, int32_t* tile_start, hipStream_t s);
+// Rows-M products with B n-contiguous (dH = dY W2, dX = [dU dV] [W1; W3]) on
+// LDS-DMA tiles: C = A B in fp32 (overwritten). Needs K a multiple of 128,
+// k_split (if B2) a multiple of 32, lda and ldb multiples of 8, N a multiple
+// of 8; otherwise hipErrorInvalidValue.
+hipError_t launch_bgemm_dma(const BGemm& p, int32_t* tile_start, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // Token-choice layer backward, bf16 activations and weights. The caller has
@@ -230,6 +238,7 @@ hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool acc, int32_
 struct BwdArgs {
   int64_t T, d, d_ff, cap;
   int32_t N, k, S, act, gating, ldl;  // ldl: row pitch of dl_hi / dl_lo, N rounded up to 8
+  int64_t ld_du;                      // row pitch of dU (2 d_ff for SwiGLU: dV = dU + d_ff, else d_ff)
   float aux_alpha, c_aux, c_z;
   const uint16_t *x, *dy, *w_router, *x_perm;
   const uint16_t *w1, *w3, *w2, *sw1, *sw3, *sw2;
