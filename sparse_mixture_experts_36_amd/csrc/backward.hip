@@ -332,20 +332,20 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     sh.C = a.dX + cap * d; sh.c_gs = T * d;
     e = launch_bgemm_dma(sh, a.tile_start, s);
   }
-  // ---- 4. weight gradients: rows-K, one matrix per expert
+  // ---- 4. weight gradients: rows-K on the DMA tiles, one matrix per expert
   BGemm dw{};
   dw.off = a.offsets; dw.n_groups = a.N; dw.cap = static_cast<int32_t>(cap);
   if (ok() && a.dW2) {  // dW2 = dY^T H: [d][d_ff]
     dw.M = static_cast<int32_t>(d); dw.N = static_cast<int32_t>(f); dw.A = a.dY; dw.lda = d; dw.B = a.H; dw.ldb = f;
     dw.C = a.dW2; dw.ldc = f; dw.c_gs = d * f;
-    e = launch_bgemm(dw, true, false, false, a.tile_start, s);
+    e = launch_bgemm_dma_rk(dw, s);
   }
   for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {  // dW1 = dU^T X, dW3 = dV^T X: [d_ff][d]
     float* out = w == 0 ? a.dW1 : a.dW3;
     if (!out) continue;
     dw.M = static_cast<int32_t>(f); dw.N = static_cast<int32_t>(d); dw.A = w == 0 ? a.dU : a.dV; dw.lda = ldu;
     dw.B = a.x_perm; dw.ldb = d; dw.C = out; dw.ldc = d; dw.c_gs = f * d;
-    e = launch_bgemm(dw, true, false, false, a.tile_start, s);
+    e = launch_bgemm_dma_rk(dw, s);
   }
   if (S > 0) {
     BGemm sw{};
@@ -353,14 +353,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     if (ok() && a.dsW2) {
       sw.M = static_cast<int32_t>(d); sw.N = static_cast<int32_t>(f); sw.A = a.dy; sw.lda = d;
       sw.B = a.H + cap * f; sw.ldb = f; sw.b_gs = T * f; sw.C = a.dsW2; sw.ldc = f; sw.c_gs = d * f;
-      e = launch_bgemm(sw, true, false, false, a.tile_start, s);
+      e = launch_bgemm_dma_rk(sw, s);
     }
     for (int w = 0; w < (swi ? 2 : 1) && ok(); ++w) {
       float* out = w == 0 ? a.dsW1 : a.dsW3;
       if (!out) continue;
       sw.M = static_cast<int32_t>(f); sw.N = static_cast<int32_t>(d); sw.A = (w == 0 ? a.dU : a.dV) + cap * ldu;
       sw.lda = ldu; sw.a_gs = T * ldu; sw.B = a.x; sw.ldb = d; sw.b_gs = 0; sw.C = out; sw.ldc = d; sw.c_gs = f * d;
-      e = launch_bgemm(sw, true, false, false, a.tile_start, s);
+      e = launch_bgemm_dma_rk(sw, s);
     }
   }
   if (ok() && !swi && a.db1) {

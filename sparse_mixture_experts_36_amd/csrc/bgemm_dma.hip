@@ -18,6 +18,13 @@
 //    half-wave reads over all banks.
 // Rows past a group's end and columns past N load clamped (valid) data that
 // is computed and never stored.
+//
+// Rows-K form (RK): C_g = A_g^T B_g over the group's rows r (dW2 = dY^T H,
+// dW1 = dU^T X, dW3 = dV^T X): both operands are stored [r][m] / [r][n], so
+// both take the B path above (k-rows of 512 bytes, transpose reads). The k
+// range is the group's row count; k-rows past it load the group's last row
+// (the stage count is padded to a multiple of four), and on those stages the
+// A fragment values of k past the range are set to zero before the MFMAs.
 #include "common.h"
 #include "kernels.h"
 
@@ -66,6 +73,7 @@ __global__ __launch_bounds__(256) void dma_plan_kernel(BGemm p, int32_t* tile_st
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define MOE_L(x) ((__attribute__((address_space(3))) void*)(x))
 
+template <bool RK>
 __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* tile_start) {
   __shared__ __attribute__((aligned(16))) char A0[kSA];
   __shared__ __attribute__((aligned(16))) char A1[kSA];
@@ -81,8 +89,8 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
   const int L = (blockIdx.x % kXcd) * per_xcd + blockIdx.x / kXcd;
   const int ntn = (p.N + kTN - 1) / kTN;
   int g, mt, nt;
-  if (!p.off) {
-    const int mtn = (p.rows_all + kTM - 1) / kTM;
+  if (RK || !p.off) {
+    const int mtn = ((RK ? p.M : p.rows_all) + kTM - 1) / kTM;
     if (L >= p.n_groups * mtn * ntn) return;
     g = L / (mtn * ntn);
     nt = (L % (mtn * ntn)) / mtn;
@@ -101,33 +109,43 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
     mt = local % mtg;
   }
   int r0;
-  const int M = group_rows(p, g, r0);
+  const int rows = group_rows(p, g, r0);
+  const int M = RK ? p.M : rows;
   const int m0 = mt * kTM, n0 = nt * kTN;
   if (m0 >= M) return;
-  const int K = p.K, KS = K / kTK;  // a multiple of 4
+  const int K = RK ? rows : p.K;
+  const int KS = ((K + kTK - 1) / kTK + 3) / 4 * 4;  // rows-M: K / 32, a multiple of 4
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, c16 = lane & 15;
 
-  // DMA sources: wave-uniform bases, 32-bit lane offsets (elements)
-  const uint16_t* Ab = p.A + p.a_gs * g + static_cast<int64_t>(r0 + m0) * p.lda;
-  const uint16_t* Bb = p.B + p.b_gs * g + n0;
+  // DMA sources: wave-uniform bases, 32-bit lane offsets (elements). Rows-M:
+  // A rows r0 + m0.. (k-contiguous); rows-K: A k-rows r0.. of 256 columns m0..
+  const uint16_t* Ab = p.A + p.a_gs * g +
+                       (RK ? static_cast<int64_t>(r0) * p.lda + m0 : static_cast<int64_t>(r0 + m0) * p.lda);
+  const uint16_t* Bb = p.B + p.b_gs * g + (RK ? static_cast<int64_t>(r0) * p.ldb : 0) + n0;
   const uint16_t* B2b = p.B2 ? p.B2 + p.b_gs * g + n0 : nullptr;
   uint32_t offa[2], offb[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = wave * 32 + t * 16 + (lane >> 2);                 // tile row this lane fills
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);                  // its global k-chunk
-    const int srow = min(row, M - m0 - 1);                           // rows past the group: clamped
-    offa[t] = static_cast<uint32_t>(srow * static_cast<int>(p.lda) + chunk * 8);
     const int krow = wave * 4 + t * 2 + (lane >> 5);
-    const int lastc = (min(kTN, p.N - n0) >> 3) - 1;                 // columns past N: clamped
+    if (RK) {
+      const int lastm = (min(kTM, M - m0) >> 3) - 1;                   // columns past M: clamped
+      const int ac = min((lane & 31) ^ bkey(krow), lastm);
+      offa[t] = static_cast<uint32_t>(ac * 8);  // + the k-row's offset, per stage
+    } else {
+      const int row = wave * 32 + t * 16 + (lane >> 2);               // tile row this lane fills
+      const int chunk = (lane & 3) ^ ((row >> 1) & 3);                // its global k-chunk
+      const int srow = min(row, M - m0 - 1);                         // rows past the group: clamped
+      offa[t] = static_cast<uint32_t>(srow * static_cast<int>(p.lda) + chunk * 8);
+    }
+    const int lastc = (min(kTN, p.N - n0) >> 3) - 1;                   // columns past N: clamped
     const int bc = min((lane & 31) ^ bkey(krow), lastc);
-    offb[t] = static_cast<uint32_t>(krow * static_cast<int>(p.ldb) + bc * 8);
+    offb[t] = static_cast<uint32_t>((RK ? 0 : krow * static_cast<int>(p.ldb)) + bc * 8);
   }
-  const int dsta = wave * 32 * 64, dstb = wave * 4 * 512;  // byte offsets in a stage buffer
+  const int dsta = RK ? wave * 4 * 512 : wave * 32 * 64, dstb = wave * 4 * 512;  // byte offsets in a stage
 
   floatx4_t acc[4][8];
 #pragma unroll
@@ -136,11 +154,19 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
     for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // LDS read addresses (bytes) inside a stage
-  int rda[4];
+  int rda[4];  // rows-M: the swizzled 64-byte A rows
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 64 + i * 16 + c16;
     rda[i] = row * 64 + ((q ^ ((row >> 1) & 3)) << 4);
+  }
+  // rows-K: A fragment i, half h through the transpose read, chunk
+  // ((8 wm + 2i) ^ key_h) + x of k-row kr_h (as for B, with m for n)
+  int abase[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int krow = 8 * q + 4 * h + (c16 >> 2);
+    abase[h] = krow * 512 + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
   }
   // B fragment j, half h: k-row kr_h = 8q + 4h + c16/4, column wn 128 + 16j +
   // 4 (c16 mod 4), i.e. chunk 16 wn + 2j + x (x = (c16 mod 4) / 2) at half
@@ -156,12 +182,23 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
 #define MOE_DMA(SA, SB, ks)                                                                          \
   do {                                                                                               \
     const int k0_ = (ks) * kTK;                                                                      \
-    const uint16_t* ba_ = Ab + k0_;                                                                  \
-    const uint16_t* bb_ = (B2b && k0_ >= p.k_split) ? B2b + static_cast<int64_t>(k0_ - p.k_split) * p.ldb \
-                                                    : Bb + static_cast<int64_t>(k0_) * p.ldb;        \
-    _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                               \
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ba_ + offa[t_]), MOE_L((SA) + dsta + t_ * 1024), 16, 0, 0); \
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bb_ + offb[t_]), MOE_L((SB) + dstb + t_ * 1024), 16, 0, 0); \
+    if (RK) {                                                                                        \
+      _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                             \
+        /* this lane's k-row k0 + 4 wave + 2 t + lane / 32, past the group: its last row */          \
+        const int kr_ = min(k0_ + wave * 4 + 2 * t_ + (lane >> 5), K - 1);                           \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Ab + (static_cast<int64_t>(kr_) * p.lda + offa[t_])), \
+                                         MOE_L((SA) + dsta + t_ * 1024), 16, 0, 0);                  \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bb + (static_cast<int64_t>(kr_) * p.ldb + offb[t_])), \
+                                         MOE_L((SB) + dstb + t_ * 1024), 16, 0, 0);                  \
+      }                                                                                              \
+    } else {                                                                                         \
+      const uint16_t* ba_ = Ab + k0_;                                                                \
+      const uint16_t* bb_ = (B2b && k0_ >= p.k_split) ? B2b + static_cast<int64_t>(k0_ - p.k_split) * p.ldb \
+                                                      : Bb + static_cast<int64_t>(k0_) * p.ldb;      \
+      _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                             \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(ba_ + offa[t_]), MOE_L((SA) + dsta + t_ * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bb_ + offb[t_]), MOE_L((SB) + dstb + t_ * 1024), 16, 0, 0); \
+      }                                                                                              \
     }                                                                                                \
   } while (0)
   // the B fragment of column block j + 1 is read while block j's MFMAs run
@@ -174,10 +211,32 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
     const uint2 l2_ = __builtin_bit_cast(uint2, lo_), h2_ = __builtin_bit_cast(uint2, hi_);          \
     OUT = make_uint4(l2_.x, l2_.y, h2_.x, h2_.y);                                                    \
   } while (0)
-#define MOE_COMPUTE(SA, SB)                                                                          \
+#define MOE_COMPUTE(SA, SB, ks)                                                                      \
   do {                                                                                               \
     uint4 af_[4], bc_, bn_;                                                                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) af_[i_] = *reinterpret_cast<const uint4*>((SA) + rda[i_]); \
+    if (RK) {                                                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                             \
+        const v4s lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)( \
+            (SA) + abase[0] + (((8 * wm + 2 * i_) ^ rkey[0]) << 4)));                                \
+        const v4s hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)( \
+            (SA) + abase[1] + (((8 * wm + 2 * i_) ^ rkey[1]) << 4)));                                \
+        const uint2 l2_ = __builtin_bit_cast(uint2, lo_), h2_ = __builtin_bit_cast(uint2, hi_);      \
+        af_[i_] = make_uint4(l2_.x, l2_.y, h2_.x, h2_.y);                                            \
+      }                                                                                              \
+      const int kv_ = K - (ks) * kTK;  /* valid k of this stage; lane holds k 8q .. 8q + 7 */        \
+      if (kv_ < kTK) {                                                                               \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                           \
+          uint32_t w_[4] = {af_[i_].x, af_[i_].y, af_[i_].z, af_[i_].w};                             \
+          _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                                         \
+            if (8 * q + 2 * e_ >= kv_) w_[e_] &= 0xFFFF0000u;                                        \
+            if (8 * q + 2 * e_ + 1 >= kv_) w_[e_] &= 0x0000FFFFu;                                    \
+          }                                                                                          \
+          af_[i_] = make_uint4(w_[0], w_[1], w_[2], w_[3]);                                          \
+        }                                                                                            \
+      }                                                                                              \
+    } else {                                                                                         \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) af_[i_] = *reinterpret_cast<const uint4*>((SA) + rda[i_]); \
+    }                                                                                                \
     MOE_BFRAG(SB, 0, bc_);                                                                           \
     _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) {                                               \
       if (j_ + 1 < 8) MOE_BFRAG(SB, j_ + 1, bn_);                                                    \
@@ -196,9 +255,10 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
     __builtin_amdgcn_s_waitcnt(kLgkm0);                                                              \
     __builtin_amdgcn_s_barrier();                                                                    \
     if (DMA) MOE_DMA(SAN, SBN, (ks) + 3);                                                            \
-    MOE_COMPUTE(SA, SB);                                                                             \
+    MOE_COMPUTE(SA, SB, ks);                                                                         \
   } while (0)
 
+  if (KS > 0) {
   MOE_DMA(A0, B0, 0);
   MOE_DMA(A1, B1, 1);
   MOE_DMA(A2, B2s, 2);
@@ -214,13 +274,14 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
   MOE_STAGE(A1, B1, A0, B0, ks + 1, 8, false);
   MOE_STAGE(A2, B2s, A1, B1, ks + 2, 4, false);
   MOE_STAGE(A3, B3, A2, B2s, ks + 3, 0, false);
+  }
 #undef MOE_STAGE
 #undef MOE_COMPUTE
 #undef MOE_BFRAG
 #undef MOE_DMA
 
   // lane (q, c16) of fragment (i, j): rows 4q + r, column c16
-  float* C = static_cast<float*>(p.C) + p.c_gs * g + static_cast<int64_t>(r0 + m0) * p.ldc + n0;
+  float* C = static_cast<float*>(p.C) + p.c_gs * g + static_cast<int64_t>((RK ? 0 : r0) + m0) * p.ldc + n0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -252,7 +313,16 @@ hipError_t launch_bgemm_dma(const BGemm& p, int32_t* tile_start, hipStream_t s) 
   }
   if (grid <= 0) return hipSuccess;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL(bgemm_dma_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
+  hipLaunchKernelGGL(bgemm_dma_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_bgemm_dma_rk(const BGemm& p, hipStream_t s) {
+  if (p.n_groups <= 0 || p.N <= 0 || p.M <= 0) return hipSuccess;
+  if (p.M % 8 != 0 || p.N % 8 != 0 || p.lda % 8 != 0 || p.ldb % 8 != 0) return hipErrorInvalidValue;
+  int64_t grid = static_cast<int64_t>(p.n_groups) * ((p.M + kTM - 1) / kTM) * ((p.N + kTN - 1) / kTN);
+  grid = (grid + kXcd - 1) / kXcd * kXcd;
+  hipLaunchKernelGGL(bgemm_dma_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, nullptr);
   return hipGetLastError();
 }
 

@@ -228,6 +228,10 @@ hipError_t launch_bgemm(const BGemm& p, bool rows_k, bool b_kc, bool acc, int32_
 // k_split (if B2) a multiple of 32, lda and ldb multiples of 8, N a multiple
 // of 8; otherwise hipErrorInvalidValue.
 hipError_t launch_bgemm_dma(const BGemm& p, int32_t* tile_start, hipStream_t s);
+// Rows-K products (dW = dY^T H, dU^T X, dV^T X) on the same tiles: C = A^T B
+// in fp32 over each group's rows. Needs M, N, lda, ldb multiples of 8;
+// otherwise hipErrorInvalidValue.
+hipError_t launch_bgemm_dma_rk(const BGemm& p, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // Token-choice layer backward, bf16 activations and weights. The caller has
