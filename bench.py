@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_36_amd", "csrc", "gemm.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm-dma-up-swiglu_mixtral-prefill_hbm-traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm-dma-up-swiglu_mixtral-prefill_hbm-traffic.txt")
 COPY_BYTES = 1 << 30        # the calibration kernel reads and writes this many bytes
 
 
