@@ -54,6 +54,9 @@ CASES = {
     "swiglu-ffn-dma256-T2048-shared1": _wl("b8", 2048, 256, 512, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
     "gelu-ffn-dma128-renorm-cf1-biases": _wl("b9", 1024, 256, 384, 8, 2, gen.GELU, gen.SOFTMAX_TOPK_RENORM, cf=1.0,
                                              zipf=1.0),
+    # widths the 256-wide tiles do not divide: clamped columns in every
+    # product, and the recompute on the backward GEMM although rows >= 2048
+    "swiglu-d384-dff384-T1024-shared1": _wl("b10", 1024, 384, 384, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
 }
 
 
@@ -83,12 +86,12 @@ def _same_routing(inp, t):
     return np.array_equal(host(idx), r.topk_idx)
 
 
-def _check(inp, dy, c_aux, c_z, label):
+def _check(inp, dy, c_aux, c_z, label, pad=0):
     import torch
     wl = inp.wl
     say(f"backward {label}: T={wl.T} d={wl.d} d_ff={wl.d_ff} N={wl.n_experts} k={wl.top_k} C={wl.capacity()} "
-        f"shared={wl.n_shared} c_aux={c_aux} c_z={c_z}")
-    t = device_weights(inp)
+        f"shared={wl.n_shared} c_aux={c_aux} c_z={c_z} weight row pad={pad}")
+    t = device_weights(inp, pad)
     assert _same_routing(inp, t), "routing differs from the oracle's: pick a seed without near ties"
     s = shape_of(wl)
     g = moe.alloc_grads(s)
@@ -123,6 +126,15 @@ def _check(inp, dy, c_aux, c_z, label):
 def test_backward_matches_oracle(name, c_aux, c_z):
     inp, dy = _inputs(CASES[name], seed=11)
     _check(inp, dy, c_aux, c_z, name)
+
+
+@pytest.mark.parametrize("name", ["gelu-renorm-cf0.75-biases", "swiglu-ffn-dma256-T2048-shared1",
+                                  "swiglu-d384-dff384-T1024-shared1"])
+def test_backward_padded_weight_rows(name):
+    """Expert matrices with rows 64 elements longer than their width (the
+    layout the benchmark uses), on both recompute paths."""
+    inp, dy = _inputs(CASES[name], seed=11)
+    _check(inp, dy, 1.0, 0.1, name, pad=64)
 
 
 def test_backward_is_deterministic():
