@@ -10,12 +10,13 @@
 // Steps (all on the caller's stream):
 //  1. forward again: router, permutation with the rows copied, U = X W1^T
 //     (+ b1) and V = X W3^T in fp32, H = act(U, V) in bf16, the routed
-//     outputs Y = H W2^T; shared experts on all T rows;
+//     outputs Y = H W2^T; shared experts on all T rows (on the forward's
+//     grouped FFN when its DMA tiles take the call);
 //  2. combine backward: dY_row = g dy_t (bf16), dg = <dy_t, Y_row + b2>;
 //  3. dH = dY W2 (fp32); dU, dV from dH, U, V (bf16, one [dU | dV] row each);
-//     dX = [dU dV] [W1; W3] (fp32);
-//  4. dW2 = dY^T H, dW1 = dU^T X, dW3 = dV^T X (fp32, one matrix per expert),
-//     b1 / b2 gradients as column sums;
+//     dX = [dU dV] [W1; W3] (fp32), both on the LDS-DMA GEMM;
+//  4. dW2 = dY^T H, dW1 = dU^T X, dW3 = dV^T X (fp32, one matrix per expert,
+//     LDS-DMA GEMM), b1 / b2 gradients as column sums;
 //  5. router: dl from dg through the gates' mode, the L_aux and z terms and
 //     the token softmax; dW_r = dl^T x and dx += dl W_r (dl split into two
 //     bf16 halves whose sum is dl to about 2^-16), db_r = column sums of dl;

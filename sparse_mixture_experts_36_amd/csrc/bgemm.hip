@@ -3,9 +3,12 @@
 //   C_g(m, n) (+)= sum_k A_g(m, k) B_g(k, n),   bf16 operands, fp32 accumulation.
 // Group g owns rows [r0, r1) of a row space (the permuted rows of expert g, or
 // the T token rows of a shared expert). In rows-M form those rows are A's and
-// C's rows (dH = dY W2, dX = dU W1, and the forward's U = X W1^T); in rows-K
-// form they are the contraction (dW2 = dY^T H, dW1 = dU^T X), so every group
-// has its own k range and writes its own output matrix.
+// C's rows; in rows-K form they are the contraction, so every group has its
+// own k range and writes its own output matrix. The expert products of large
+// layers run on the LDS-DMA kernels (the forward's grouped FFN for the
+// recompute, bgemm_dma for the gradients); this register-staged kernel takes
+// the router's products (dl^T x, dl W_r) and the recompute of layers below
+// those kernels' row threshold (U = X W1^T, Y = H W2^T).
 //
 // Tiles of 128 x 256 outputs (m x n), 4 waves (2 x 2), each 64 x 128 as
 // 4 x 8 MFMA 16x16x32 fragments; k-steps of 64 through LDS rows of 64 k (+8 pad), the
