@@ -270,10 +270,12 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
 
 def run_backward(wl, inp, steps, warmup):
     """moe_backward on the same layer and input with a seeded bf16 dy: dx and
-    every weight gradient, L_aux and z terms on. One step recomputes the
-    forward (3 of the 9 expert GEMMs) and runs the 6 gradient GEMMs, so it
-    does 3 x the forward FFN's flops per kept pair; flops and MFMA fraction
-    count all of them. Time from hipEvents around the whole step."""
+    every weight gradient, L_aux and z terms on. One step recomputes the up
+    GEMM (U = W1 x, V = W3 x) and runs the gradient GEMMs (dH = dy W2, dX =
+    dU W1 + dV W3, dW2, dW1, dW3): per kept pair 3 x the up GEMM's flops plus
+    2 x the down GEMM's (16 d d_ff for SwiGLU), plus the router's 5 x 2 d N per
+    token. flops and MFMA fraction count all of them. Time from hipEvents
+    around the whole step."""
     import torch
 
     import gen
@@ -302,7 +304,7 @@ def run_backward(wl, inp, steps, warmup):
     out = {"ms_per_step": round(ms, 4), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
            "workspace_GB": round(moe.workspace_size(shape, moe.ENTRY_BACKWARD) / 1e9, 3)}
     if rows is not None:
-        flops = 3 * rows * ffn_flops_per_pair(wl) + 2.0 * wl.T * wl.d * wl.n_experts * 5
+        flops = rows * (3 * up_flops_per_pair(wl) + 2 * 2.0 * wl.d * wl.d_ff) + 2.0 * wl.T * wl.d * wl.n_experts * 5
         out.update(flops_per_step=flops, TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 1),
                    mfma_frac=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
     log(f"backward: {out}")

@@ -201,8 +201,10 @@ struct BwdWs {
   int32_t *topk_idx, *inv_map, *offsets, *perm_token, *counts, *tile_start;
   float *topk_w, *lse_mean;
   uint16_t* x_perm;
-  float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
-  uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
+  float *U, *V, *dH, *dX, *dl32, *dxr, *dg;
+  uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo, *dYu;
+  int32_t* row_pair;
+  float* row_gate;
   int32_t* wr_off;
   float* wr_part;
   // the forward's grouped FFN for the recompute (bwd_uses_ffn)
@@ -235,8 +237,10 @@ BwdWs carve_bwd(Carver& c, const moe_shape& s) {
   w.U = c.take<float>(rows * f);
   w.V = swi ? c.take<float>(rows * f) : nullptr;
   w.H = c.take<uint16_t>(rows * f);
-  w.Y = c.take<float>(cap * d);
   w.dY = c.take<uint16_t>(cap * d);
+  w.dYu = c.take<uint16_t>(cap * d);
+  w.row_pair = c.take<int32_t>(cap);
+  w.row_gate = c.take<float>(cap);
   w.dH = c.take<float>(rows * f);
   w.dU = c.take<uint16_t>(rows * f * (swi ? 2 : 1));  // [dU | dV] rows for SwiGLU
   w.dV = (swi && w.dU) ? w.dU + f : nullptr;
@@ -736,7 +740,9 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights
   a.lse_mean = w.lse_mean;
   a.U = w.U;
   a.V = w.V;
-  a.Y = w.Y;
+  a.dYu = w.dYu;
+  a.row_pair = w.row_pair;
+  a.row_gate = w.row_gate;
   a.dH = w.dH;
   a.dX = w.dX;
   a.dl32 = w.dl32;
@@ -762,15 +768,13 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights
     fw.tile_start_t = w.ffn_tiles_t;
     fw.active = w.active;
     fw.split_part = w.split_part;
-    // its bf16 outputs are not used: the routed ones land in dY and the
-    // shared ones in dX, both written again later in the pass
+    // only its up GEMM runs (the down GEMM's outputs would land in dY and dX)
     a.ffn = ffn_args(s, w.x_perm, s.d, w.offsets, x, weights, w.dY, w.dX, fw);
     a.ffn.ld_h = s.d_ff;
     a.ffn.pre_up_u = w.U;
     a.ffn.pre_up_v = w.V;
     a.ffn.ld_pre_up = s.d_ff;
-    a.ffn.pre_down = w.Y;
-    a.ffn.ld_pre_down = s.d;
+    a.ffn.up_only = true;
   }
   a.dx = static_cast<uint16_t*>(g->dx);
   a.dWr = g->dw_router;

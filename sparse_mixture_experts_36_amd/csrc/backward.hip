@@ -9,12 +9,14 @@
 //
 // Steps (all on the caller's stream):
 //  1. forward again: router, permutation with the rows copied, U = X W1^T
-//     (+ b1) and V = X W3^T in fp32, H = act(U, V) in bf16, the routed
-//     outputs Y = H W2^T; shared experts on all T rows (on the forward's
-//     grouped FFN when its DMA tiles take the call);
-//  2. combine backward: dY_row = g dy_t (bf16), dg = <dy_t, Y_row + b2>;
-//  3. dH = dY W2 (fp32); dU, dV from dH, U, V (bf16, one [dU | dV] row each);
-//     dX = [dU dV] [W1; W3] (fp32), both on the LDS-DMA GEMM;
+//     (+ b1) and V = X W3^T in fp32, H = act(U, V) in bf16, shared experts on
+//     all T rows (on the forward's grouped FFN, up GEMM only, when its DMA
+//     tiles take the call). The layer output itself is not needed: the gate
+//     gradient dg = <dy, E(x)> = <dy W2, H> (+ <dy, b2>) comes from dH;
+//  2. combine backward: the kept rows' dy unscaled (dYu) and scaled by the
+//     gate (dY = g dy, bf16);
+//  3. dH = dYu W2 (fp32, LDS-DMA GEMM); per row dg, then dU, dV from g dH, U,
+//     V (bf16, one [dU | dV] row each); dX = [dU dV] [W1; W3] (fp32, LDS-DMA);
 //  4. dW2 = dY^T H, dW1 = dU^T X, dW3 = dV^T X (fp32, one matrix per expert,
 //     LDS-DMA GEMM), b1 / b2 gradients as column sums;
 //  5. router: dl from dg through the gates' mode, the L_aux and z terms and
@@ -52,57 +54,94 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(BwdArgs a, float* U, 
   H[i] = f32_to_bf16(a.act == 1 ? silu(u) * V[i] : gelu_erf(u));
 }
 
-// Per token: dY rows of its kept slots = g dy (bf16) and dg = <dy, Y + b2>.
+// Per token: for each kept slot j (routed row r), dy into row r as it is
+// (dYu: the dH product's input) and scaled by the gate (dY = g dy, bf16: the
+// dW2 product's input), the row's pair index and gate; dg = 0 for a dropped
+// pair (kept pairs get theirs in act_bwd_kernel).
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
-  __shared__ float s_red[kThreads / 64][kMaxSlots];
   const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* dy = a.dy + t * a.d;
-#pragma unroll
-  for (int j = 0; j < kMaxSlots; ++j) {
-    if (j >= a.k) break;
-    const int row = a.inv_map[t * a.k + j];
-    float s = 0.f;
-    if (row >= 0) {  // uniform: dropped pairs carry nothing
-      const int e = a.topk_idx[t * a.k + j];
-      const float g = a.topk_w[t * a.k + j];
-      const float* y = a.Y + static_cast<int64_t>(row) * a.d;
-      uint16_t* dY = a.dY + static_cast<int64_t>(row) * a.d;
-      // Y holds b2 already when the forward's FFN recomputed it
-      const float* b2 = (a.act == 0 && a.b2 && !a.use_ffn) ? a.b2 + static_cast<int64_t>(e) * a.d : nullptr;
-      for (int64_t c = tid; c < a.d; c += kThreads) {
-        const float v = bf16_to_f32(dy[c]);
-        dY[c] = f32_to_bf16(g * v);
-        s = fmaf(v, y[c] + (b2 ? b2[c] : 0.f), s);
-      }
+  const uint4* dy = reinterpret_cast<const uint4*>(a.dy + t * a.d);
+  const int64_t n8 = a.d / 8;
+  for (int j = 0; j < a.k; ++j) {
+    const int row = a.inv_map[t * a.k + j];  // uniform
+    if (row < 0) {
+      if (threadIdx.x == 0) a.dg[t * a.k + j] = 0.f;
+      continue;
     }
-    s = wave_sum(s);
-    if (lane == 0) s_red[wave][j] = s;
-  }
-  __syncthreads();
-  if (tid < a.k) {
-    float s = 0.f;
-    for (int w = 0; w < kThreads / 64; ++w) s += s_red[w][tid];
-    a.dg[t * a.k + tid] = a.inv_map[t * a.k + tid] >= 0 ? s : 0.f;
+    const float g = a.topk_w[t * a.k + j];
+    uint4* du = reinterpret_cast<uint4*>(a.dYu + static_cast<int64_t>(row) * a.d);
+    uint4* ds = reinterpret_cast<uint4*>(a.dY + static_cast<int64_t>(row) * a.d);
+    for (int64_t c = threadIdx.x; c < n8; c += kThreads) {
+      const uint4 v = dy[c];
+      du[c] = v;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = static_cast<uint32_t>(f32_to_bf16(g * bf16_to_f32(static_cast<uint16_t>(w[e] & 0xFFFFu)))) |
+               (static_cast<uint32_t>(f32_to_bf16(g * bf16_to_f32(static_cast<uint16_t>(w[e] >> 16)))) << 16);
+      ds[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (threadIdx.x == 0) {
+      a.row_pair[row] = static_cast<int32_t>(t * a.k + j);
+      a.row_gate[row] = g;
+    }
   }
 }
 
-// dU, dV (bf16) from dH and the pre-activations: SwiGLU dU = dH V silu'(U),
-// dV = dH silu(U); GELU dU = dH gelu'(U).
-__global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a, const float* dH, const float* U, const float* V,
-                                                            uint16_t* dU, uint16_t* dV, int64_t rows) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= rows * a.d_ff) return;
-  const float u = U[i], h = dH[i];
-  const int64_t o = (i / a.d_ff) * a.ld_du + i % a.d_ff;  // dU / dV rows of pitch ld_du
-  if (a.act == 1) {
-    const float sg = 1.f / (1.f + expf(-u));
-    dU[o] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
-    dV[o] = f32_to_bf16(h * u * sg);
-  } else {
-    const float cdf = 0.5f * (1.f + erff(u * 0.70710678118654752f));
-    const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-    dU[o] = f32_to_bf16(h * (cdf + u * pdf));
+// One workgroup per row of the row space. dH holds dy W2 for the row (routed:
+// its token's dy, unscaled; shared: dy); with the row's gate g (1 for shared
+// rows) dH = g (dy W2), and dU, dV (bf16, row pitch ld_du) follow from dH, U, V:
+// SwiGLU dU = dH V silu'(U), dV = dH silu(U); GELU dU = dH gelu'(U). A routed
+// row also gives its pair's gate gradient dg = <dy, E(x)> = <dy W2, H> (+ <dy,
+// b2> for GELU), summed in a fixed order.
+__global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a) {
+  __shared__ float s_red[kThreads / 64];
+  const int64_t r = blockIdx.x;
+  const bool routed = r < a.cap;
+  if (routed && r >= a.offsets[a.N]) return;  // rows past the kept pairs (uniform)
+  const int tid = threadIdx.x;
+  const int64_t f = a.d_ff;
+  const float g = routed ? a.row_gate[r] : 1.f;
+  const float* dh = a.dH + r * f;
+  const float* U = a.U + r * f;
+  const float* V = a.act == 1 ? a.V + r * f : nullptr;
+  const uint16_t* H = a.H + r * f;
+  uint16_t* dU = a.dU + r * a.ld_du;
+  uint16_t* dV = a.act == 1 ? a.dV + r * a.ld_du : nullptr;
+  float dot = 0.f;
+  for (int64_t i = tid; i < f; i += kThreads) {
+    const float hp = dh[i], u = U[i], h = g * hp;
+    dot = fmaf(hp, bf16_to_f32(H[i]), dot);
+    if (a.act == 1) {
+      const float sg = 1.f / (1.f + expf(-u));
+      dU[i] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
+      dV[i] = f32_to_bf16(h * u * sg);
+    } else {
+      const float cdf = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+      const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
+      dU[i] = f32_to_bf16(h * (cdf + u * pdf));
+    }
+  }
+  if (!routed) return;  // uniform
+  const int32_t pair = a.row_pair[r];
+  if (a.act == 0 && a.b2) {  // the output bias: <dy, b2_e>
+    int lo = 0, hi = a.N - 1;  // expert of row r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.offsets[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const uint16_t* dy = a.dy + static_cast<int64_t>(pair / a.k) * a.d;
+    const float* b2 = a.b2 + static_cast<int64_t>(lo) * a.d;
+    for (int64_t o = tid; o < a.d; o += kThreads) dot = fmaf(bf16_to_f32(dy[o]), b2[o], dot);
+  }
+  dot = wave_sum(dot);
+  if ((tid & 63) == 0) s_red[tid >> 6] = dot;
+  __syncthreads();
+  if (tid == 0) {
+    float v = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) v += s_red[w];
+    a.dg[pair] = v;
   }
 }
 
@@ -288,13 +327,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(act_fwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.U, a.V, a.H, rows);
       check();
     }
-    if (ok() && cap > 0) {  // Y = H W2^T for the routed rows (the gates' gradient)
-      BGemm y{};
-      y.off = a.offsets; y.n_groups = a.N; y.cap = static_cast<int32_t>(cap); y.K = static_cast<int32_t>(f);
-      y.N = static_cast<int32_t>(d); y.A = a.H; y.lda = f; y.B = a.w2; y.ldb = a.ld_down; y.b_gs = d * a.ld_down;
-      y.C = a.Y; y.ldc = d;
-      e = launch_bgemm(y, false, true, false, a.tile_start, s);
-    }
   }
   // ---- 2. combine backward
   if (ok()) {
@@ -303,9 +335,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   }
   // ---- 3. dH, dU / dV, dX on the DMA tiles (B read along the weights' rows)
   const int64_t ldu = a.ld_du;  // dU and dV share rows: [dU | dV] (SwiGLU) or dU
-  BGemm dh{};  // dH = dY W2 (routed), dy W2s (shared)
+  BGemm dh{};  // dH = dy W2 (routed rows: the token's dy, unscaled), dy W2s (shared)
   dh.off = a.offsets; dh.n_groups = a.N; dh.cap = static_cast<int32_t>(cap); dh.K = static_cast<int32_t>(d);
-  dh.N = static_cast<int32_t>(f); dh.A = a.dY; dh.lda = d; dh.B = a.w2; dh.ldb = a.ld_down; dh.b_gs = d * a.ld_down;
+  dh.N = static_cast<int32_t>(f); dh.A = a.dYu; dh.lda = d; dh.B = a.w2; dh.ldb = a.ld_down; dh.b_gs = d * a.ld_down;
   dh.C = a.dH; dh.ldc = f;
   if (ok() && cap > 0) e = launch_bgemm_dma(dh, a.tile_start, s);
   if (ok() && S > 0) {
@@ -315,8 +347,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     e = launch_bgemm_dma(sh, a.tile_start, s);
   }
   if (ok()) {
-    hipLaunchKernelGGL(act_bwd_kernel, dim3(blocks_for(rows * f)), dim3(kThreads), 0, s, a, a.dH, a.U, a.V, a.dU,
-                       a.dV, rows);
+    hipLaunchKernelGGL(act_bwd_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, s, a);
     check();
   }
   // dX = [dU dV] [W1; W3]: one product over k = 2 d_ff, W3 past k = d_ff

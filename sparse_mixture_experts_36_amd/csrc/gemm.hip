@@ -1495,7 +1495,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
     }
   }
   stage_mark(kStageFfnUp, true, s);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || a.up_only) return err;
 
   // down GEMM: h [rows][d_ff] x [d][d_ff]^T -> y [rows][d]
   p.A_r = a.h;

@@ -135,6 +135,7 @@ struct FfnArgs {
   // down GEMM's routed outputs with their bias (pitch ld_pre_down); null: none
   float *pre_up_u, *pre_up_v, *pre_down;
   int64_t ld_pre_up, ld_pre_down;
+  bool up_only;  // the up GEMM alone (h and the copies above; no y)
 };
 // Whether the 256-column tiles (LDS-DMA, and the 256 x 256 register-staged
 // ones) fit a layer: each GEMM's output width a multiple of the columns a
@@ -252,8 +253,13 @@ struct BwdArgs {
   const int32_t *topk_idx, *inv_map, *offsets, *counts;
   const float *topk_w, *lse_mean;
   // workspace
-  float *U, *V, *Y, *dH, *dX, *dl32, *dxr, *dg;
+  float *U, *V, *dH, *dX, *dl32, *dxr, *dg;
   uint16_t *H, *dY, *dU, *dV, *dl_hi, *dl_lo;
+  // per routed row: dy of its token (unscaled), its (token, slot) pair index
+  // and gate; dH holds dy W2 for those rows until the activation pass scales it
+  uint16_t* dYu;
+  int32_t* row_pair;
+  float* row_gate;
   int32_t* tile_start;
   // dW_r = dl^T x over wr_splits token chunks (bounds wr_off [splits + 1]),
   // each into its own fp32 partial [N][d] of wr_part, summed in chunk order
@@ -261,7 +267,7 @@ struct BwdArgs {
   int32_t* wr_off;
   float* wr_part;
   // with use_ffn the forward recompute runs on the forward's grouped FFN
-  // (ffn: its arguments, writing U, V, H and Y with the bias b2 included)
+  // (ffn: its arguments; its up GEMM writes U, V and H)
   bool use_ffn;
   FfnArgs ffn;
   // outputs (weight gradients may be null: not computed)
