@@ -64,10 +64,10 @@ struct GemmParams {
   const int32_t* tile_start;  // [n_groups+1] row-tile prefix
   float* split_part;          // fp32 partial tiles of the k-split tail, or null (no split)
   int32_t ncu;                // compute units of the device
-  // fp32 copies of the values before the activation, for the layer backward
-  // (DMA tiles only; null: not written): pre_u gets W1 x (+ b1) or the down
-  // GEMM's output with its bias, pre_v gets W3 x; _r for routed groups, _s for
-  // shared ones; row c_row0 + r of the group, pitch ld_pre
+  // fp32 copies of the up GEMM's values before the activation, for the layer
+  // backward (DMA tiles only; null: not written): pre_u gets W1 x (+ b1),
+  // pre_v gets W3 x; _r for routed groups, _s for shared ones; row c_row0 + r
+  // of the group, pitch ld_pre
   float *pre_u_r, *pre_u_s, *pre_v_r, *pre_v_s;
   int64_t ld_pre;
 };
@@ -496,10 +496,9 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
   }
 }
 
-// fp32 copies of a DMA tile's values before the activation, for the layer
-// backward (bf16 weights): W1 x (+ b1) into pre_u and W3 x into pre_v, or the
-// down GEMM's output with its bias into pre_u; straight from the fragments
-// (16 lanes write 64 contiguous bytes of a row). Called only when requested.
+// fp32 copies of an up-GEMM DMA tile's values before the activation, for the
+// layer backward (bf16 weights): W1 x (+ b1) into pre_u and W3 x into pre_v,
+// straight from the fragments (16 lanes write 64 contiguous bytes of a row).
 template <int EPI, int BM, int W>
 __device__ __forceinline__ void dma_store_pre(const GemmParams& p, const TileInfo& ti,
                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN]) {
@@ -1390,7 +1389,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   if (a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T == 0) return hipSuccess;  // no rows at all
   const bool f32 = (a.act_dtype == 0);
   const int cfg = pick_cfg(a);
-  if ((a.pre_up_u || a.pre_down) && ((cfg != kDma256 && cfg != kDma128) || a.w_dtype != 1))
+  if (a.pre_up_u && ((cfg != kDma256 && cfg != kDma128) || a.w_dtype != 1))
     return hipErrorInvalidValue;  // DMA tiles on bf16 weights only
   const FfnPlan pl = ffn_plan(a);
   const int bm = pl.bm;
@@ -1516,9 +1515,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   p.C_r = a.y_perm;
   p.C_s = a.y_shared;
   p.ldc = a.d;
-  p.pre_u_r = a.pre_down;  // routed rows only
-  p.pre_u_s = p.pre_v_r = p.pre_v_s = nullptr;
-  p.ld_pre = a.ld_pre_down;
+  p.pre_u_r = p.pre_u_s = p.pre_v_r = p.pre_v_s = nullptr;
   p.K = static_cast<int32_t>(a.d_ff);
   p.Nout = static_cast<int32_t>(a.d);
   p.groups = down;

@@ -131,10 +131,9 @@ struct FfnArgs {
   const uint8_t* sw_bits;     // HOST [n_shared]
   void* wdq;                  // integer weights, prefill: workspace for every expert's codes as bf16 (dq_bytes), or null
   // the layer backward's forward recompute (DMA tiles only, else the launch
-  // fails): fp32 W1 x (+ b1) and W3 x of every row (pitch ld_pre_up), and the
-  // down GEMM's routed outputs with their bias (pitch ld_pre_down); null: none
-  float *pre_up_u, *pre_up_v, *pre_down;
-  int64_t ld_pre_up, ld_pre_down;
+  // fails): fp32 W1 x (+ b1) and W3 x of every row (pitch ld_pre_up); null: none
+  float *pre_up_u, *pre_up_v;
+  int64_t ld_pre_up;
   bool up_only;  // the up GEMM alone (h and the copies above; no y)
 };
 // Whether the 256-column tiles (LDS-DMA, and the 256 x 256 register-staged
