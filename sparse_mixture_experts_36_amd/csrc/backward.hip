@@ -110,18 +110,40 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a) {
   uint16_t* dU = a.dU + r * a.ld_du;
   uint16_t* dV = a.act == 1 ? a.dV + r * a.ld_du : nullptr;
   float dot = 0.f;
-  for (int64_t i = tid; i < f; i += kThreads) {
-    const float hp = dh[i], u = U[i], h = g * hp;
-    dot = fmaf(hp, bf16_to_f32(H[i]), dot);
+  // four elements a thread and step (d_ff is a multiple of 128: rows stay 16-byte aligned)
+  for (int64_t i = 4 * tid; i < f; i += 4 * kThreads) {
+    const float4 hp4 = *reinterpret_cast<const float4*>(dh + i);
+    const float4 u4 = *reinterpret_cast<const float4*>(U + i);
+    const uint2 h2 = *reinterpret_cast<const uint2*>(H + i);
+    const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
+    const uint16_t hb[4] = {static_cast<uint16_t>(h2.x & 0xFFFFu), static_cast<uint16_t>(h2.x >> 16),
+                            static_cast<uint16_t>(h2.y & 0xFFFFu), static_cast<uint16_t>(h2.y >> 16)};
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (a.act == 1) {
-      const float sg = 1.f / (1.f + expf(-u));
-      dU[i] = f32_to_bf16(h * V[i] * (sg + u * sg * (1.f - sg)));
-      dV[i] = f32_to_bf16(h * u * sg);
-    } else {
-      const float cdf = 0.5f * (1.f + erff(u * 0.70710678118654752f));
-      const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-      dU[i] = f32_to_bf16(h * (cdf + u * pdf));
+      const float4 v4 = *reinterpret_cast<const float4*>(V + i);
+      v[0] = v4.x; v[1] = v4.y; v[2] = v4.z; v[3] = v4.w;
     }
+    uint16_t ou[4], ov[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float h = g * hp[e];
+      dot = fmaf(hp[e], bf16_to_f32(hb[e]), dot);
+      if (a.act == 1) {
+        const float sg = 1.f / (1.f + expf(-u[e]));
+        ou[e] = f32_to_bf16(h * v[e] * (sg + u[e] * sg * (1.f - sg)));
+        ov[e] = f32_to_bf16(h * u[e] * sg);
+      } else {
+        const float cdf = 0.5f * (1.f + erff(u[e] * 0.70710678118654752f));
+        const float pdf = expf(-0.5f * u[e] * u[e]) * 0.39894228040143268f;
+        ou[e] = f32_to_bf16(h * (cdf + u[e] * pdf));
+        ov[e] = 0;
+      }
+    }
+    *reinterpret_cast<uint2*>(dU + i) = make_uint2(ou[0] | (static_cast<uint32_t>(ou[1]) << 16),
+                                                   ou[2] | (static_cast<uint32_t>(ou[3]) << 16));
+    if (a.act == 1)
+      *reinterpret_cast<uint2*>(dV + i) = make_uint2(ov[0] | (static_cast<uint32_t>(ov[1]) << 16),
+                                                     ov[2] | (static_cast<uint32_t>(ov[3]) << 16));
   }
   if (!routed) return;  // uniform
   const int32_t pair = a.row_pair[r];
