@@ -23,8 +23,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two values, round-to-nearest-even, lo in the low half (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Four OCP e4m3fn codes (one per byte of `w`) -> four bf16 values, exactly:
@@ -99,7 +102,31 @@ __device__ __forceinline__ float gelu_erf(float u) {
   return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
 }
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// silu(u) = u sigmoid(u) with the hardware exponential and reciprocal (about
+// 1 ulp each in fp32; the results feed bf16 values).
+__device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+
+// 4 x 4 transpose of bf16 values across the four lanes of a quad (DPP moves,
+// no LDS). On entry lane t (t = lane % 4) holds column t of the block as
+// c01 = (M[0][t], M[1][t]) and c23 = (M[2][t], M[3][t]), low half first; on
+// exit it holds row t as r01 = (M[t][0], M[t][1]) and r23 = (M[t][2], M[t][3]).
+// The off-diagonal 2 x 2 blocks move between lanes t and t ^ 2, then each
+// 2 x 2 block is transposed between lanes t and t ^ 1.
+__device__ __forceinline__ void quad_transpose_bf16(uint32_t c01, uint32_t c23, int t, uint32_t& r01,
+                                                    uint32_t& r23) {
+  const bool hi2 = (t & 2) != 0, odd = (t & 1) != 0;
+  const uint32_t send = hi2 ? c01 : c23;
+  const uint32_t recv = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(send), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  const uint32_t q0 = hi2 ? recv : c01;
+  const uint32_t q1 = hi2 ? c23 : recv;
+  // even lanes pass on the high halves of q0, q1; odd lanes the low halves
+  const uint32_t s = __builtin_amdgcn_perm(q1, q0, odd ? 0x05040100u : 0x07060302u);
+  const uint32_t x = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(s), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  r01 = __builtin_amdgcn_perm(x, q0, odd ? 0x03020504u : 0x05040100u);
+  r23 = __builtin_amdgcn_perm(x, q1, odd ? 0x03020706u : 0x07060100u);
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {

@@ -426,26 +426,23 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 1
 }  // namespace dma
 
 // Epilogue of a DMA tile held as per-wave MFMA fragments: bias and activation
-// (or the SwiGLU product of the W1 and W3 halves), bf16, and 16-byte stores
-// through an LDS staging buffer of STG bytes, RR rows (at most one wave row)
-// at a time (16-byte chunk c of staged row r at position c ^ (r & 7)).
-template <int EPI, int BM, int W, int STG = dma::Cfg<BM, W>::SBYTES>
+// (or the SwiGLU product of the W1 and W3 halves), bf16, straight from the
+// registers to memory. Every wave converts its own fragments at once (no LDS,
+// no barrier). A fragment gives lane l rows 4 (l / 16) + r, r < 4, of column
+// l % 16; the quad transpose turns that into four consecutive columns of row
+// 4 (l / 16) + l % 4, stored as 8 bytes.
+template <int EPI, int BM, int W>
 __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
-                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN],
-                                               char* stage) {
+                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN]) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
-  constexpr int WTB = C_::WTB, FN = C_::FN, WGN = C_::WGN, NTH = C_::NTH, WTM = C_::WTM;
+  constexpr int WTB = C_::WTB, FN = C_::FN, FM = C_::FM, WGN = C_::WGN, WTM = C_::WTM;
   constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
   constexpr int FNO = WTO / 16;
-  constexpr int RR0 = STG / (BNO * 2);
-  constexpr int RR = RR0 < WTM ? RR0 : WTM;  // rows per staging round
-  constexpr int FR = RR / 16;                 // fragment rows per round
-  static_assert(WTM % RR == 0 && RR % 16 == 0, "staging rounds");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int q = lane >> 4, c16 = lane & 15;
+  const int q = lane >> 4, c16 = lane & 15, t = lane & 3;
   const bool shared = ti.g >= p.n_routed;
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
   const int n0 = ti.n_tile * BNO;
@@ -453,46 +450,30 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
   // integer codes as bf16 weights: one scale per output column (weight row)
   const float* rs = p.col_scaled ? (shared ? p.scale_s : p.scale_r) + static_cast<int64_t>(ew) * p.scale_pitch + n0
                                  : nullptr;
-  uint16_t* so = reinterpret_cast<uint16_t*>(stage);
   uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
-  constexpr int OCH = BNO / 8;
 #pragma unroll
-  for (int h = 0; h < BM / RR; ++h) {
-    if (h * RR >= ti.rows) break;  // the same for the whole workgroup
-    if (wm == (h * RR) / WTM) {
-      constexpr int NI = C_::FM;
-      const int i0 = ((h * RR) % WTM) / 16;  // the wave's first fragment row of the round
+  for (int j = 0; j < FNO; ++j) {
+    const int col = wn * WTO + j * 16 + c16;         // this lane's column in the fragments
+    const int ocol = wn * WTO + j * 16 + 4 * (c16 >> 2);  // the four columns it stores
+    const float bv = bias ? bias[col] : 0.f;
+    const float sa = rs ? rs[p.scale_row0 + col] : 1.f;
+    const float sb = (rs && EPI == EPI_SWIGLU) ? rs[p.scale_row3 + col] : 1.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if (i < i0 || i >= i0 + FR) continue;
+    for (int i = 0; i < FM; ++i) {
+      float v[4];
 #pragma unroll
-        for (int j = 0; j < FNO; ++j) {
-          const int col = wn * WTO + j * 16 + c16;
-          const float bv = bias ? bias[col] : 0.f;
-          const float sa = rs ? rs[p.scale_row0 + col] : 1.f;
-          const float sb = (rs && EPI == EPI_SWIGLU) ? rs[p.scale_row3 + col] : 1.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int srow = (i - i0) * 16 + q * 4 + r;  // row inside the staged part
-            float v;
-            if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][r] * sa) * (acc[i][j + FN / 2][r] * sb);
-            else if constexpr (EPI == EPI_GELU) v = gelu_erf(acc[i][j][r] * sa + bv);
-            else v = acc[i][j][r] * sa + bv;
-            so[srow * BNO + (((col >> 3) ^ (srow & 7)) << 3) + (col & 7)] = f32_to_bf16(v);
-          }
-        }
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (EPI == EPI_SWIGLU) v[r] = silu(acc[i][j][r] * sa) * (acc[i][j + FN / 2][r] * sb);
+        else if constexpr (EPI == EPI_GELU) v[r] = gelu_erf(acc[i][j][r] * sa + bv);
+        else v[r] = acc[i][j][r] * sa + bv;
       }
-    }
-    __syncthreads();
-    for (int c = tid; c < RR * OCH; c += NTH) {
-      const int srow = c / OCH, cc = c % OCH;
-      const int row = h * RR + srow;
+      uint32_t r01, r23;
+      quad_transpose_bf16(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), t, r01, r23);
+      const int row = wm * WTM + i * 16 + q * 4 + t;
       if (row < ti.rows)
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * p.ldc + cc * 8) =
-            *reinterpret_cast<const uint4*>(so + srow * BNO + ((cc ^ (srow & 7)) << 3));
+        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + ocol) = make_uint2(r01, r23);
     }
-    __syncthreads();
   }
 }
 
@@ -780,7 +761,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
     return;
   }
   dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM, W>(p, ti, acc);
 }
 
 // The 256 x 256 DMA tile with operands in separate buffers: two 32 KB buffers
@@ -1009,7 +990,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
     return;
   }
   dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W, HB>(p, ti, acc, SA0);
+  dma_store_tile<EPI, BM, W>(p, ti, acc);
 }
 
 // Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
@@ -1020,7 +1001,6 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams 
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
   constexpr int FM = C_::FM, FN = C_::FN;
-  __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
   const SplitPlan sp = split_plan<BNO>(p, p.K / BK / 2);
   const int b = blockIdx.x;
   if (sp.s == 1 || b >= sp.r) return;
@@ -1043,7 +1023,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams 
                                                          lane * 4);
   }
   dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W>(p, ti, acc, S0);
+  dma_store_tile<EPI, BM, W>(p, ti, acc);
 }
 
 // ------------------------------------------------------------------ fp32
