@@ -180,6 +180,7 @@ def run_gpu(wl, inp, steps, warmup):
     import numpy as np
     import torch
 
+    import gen
     import sparse_mixture_experts_36_amd as moe
 
     tensors = layer_weights(inp)
@@ -196,9 +197,10 @@ def run_gpu(wl, inp, steps, warmup):
     t1 = time.perf_counter()
     stages = moe.timing_stop()
     latest = layer.latest()
+    near = near_ties(layer.out.logits.cpu().numpy(), wl.top_k) if wl.gating != gen.EXPERT_CHOICE else None
     kept = int(sum(latest["kept"]))
     shared_rows = wl.n_shared * wl.T
-    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "stages": stages, "latest": latest, "kept": kept,
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "stages": stages, "latest": latest, "kept": kept, "near": near,
             "rows": kept + shared_rows, "layer": layer, "tensors": tensors}
 
 
@@ -340,6 +342,25 @@ def cpu_baseline(wl, inp, target_s=15.0):
                       f"weights), fp64, {dt:.1f} s"}
 
 
+NEAR_TIE = 1e-3  # the checking protocol's top-k margin threshold on the fp32 logits
+
+
+def near_ties(logits, k: int) -> dict:
+    """Tokens of the timed step whose top-k set margin l_(k) - l_(k+1) or
+    slot-order margin min_j l_(j) - l_(j+1), j < k, is below 1e-3 on the
+    layer's own fp32 logits: the tokens whose routing a last-bit change of a
+    logit could move. (The tests compare these tokens' routing with the
+    oracle's.)"""
+    import numpy as np
+    s = -np.sort(-logits.astype(np.float64), axis=1)
+    n = s.shape[1]
+    set_m = s[:, k - 1] - s[:, k] if k < n else np.full(s.shape[0], np.inf)
+    order_m = (s[:, :k - 1] - s[:, 1:k]).min(1) if k > 1 else np.full(s.shape[0], np.inf)
+    return {"threshold": NEAR_TIE, "set_margin_below": int((set_m < NEAR_TIE).sum()),
+            "order_margin_below": int((order_m < NEAR_TIE).sum()),
+            "either_below": int(((set_m < NEAR_TIE) | (order_m < NEAR_TIE)).sum()), "tokens": int(s.shape[0])}
+
+
 def dropped_of(wl, latest) -> int:
     """Dropped (token, expert) pairs under token choice; under expert choice
     the tokens that no expert took."""
@@ -434,7 +455,7 @@ def main():
         "layer": {"mfma_frac": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "ffn_mfma_frac": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in st.items()},
-                  "rows": r["rows"], "dropped": dropped_of(wl, r["latest"]),
+                  "rows": r["rows"], "dropped": dropped_of(wl, r["latest"]), "near_tie_tokens": r["near"],
                   "l_aux": None if r["latest"]["aux_loss"] is None else round(r["latest"]["aux_loss"], 6),
                   "z_loss": round(r["latest"]["z_loss"], 5)},
     }

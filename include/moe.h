@@ -190,6 +190,17 @@ typedef enum {
   MOE_ENTRY_BACKWARD = 4
 } moe_entry;
 
+/* Kernel family of the expert FFN (diagnostic; returned by moe_ffn_path). */
+typedef enum {
+  MOE_PATH_F32 = 0,     /* fp32 layers: FMA tiles */
+  MOE_PATH_STREAM = 1,  /* few rows (decode): weights streamed once, GEMV for T <= 2 */
+  MOE_PATH_REG128 = 2,  /* register-staged 128 x 128 MFMA tiles */
+  MOE_PATH_REG256 = 3,  /* register-staged 256 x 256 MFMA tiles (weights decoded in registers) */
+  MOE_PATH_DMA256 = 4,  /* LDS-DMA 256-row tiles, short group tails on 128-row tiles */
+  MOE_PATH_DMA128 = 5,  /* LDS-DMA 128-row tiles */
+  MOE_PATH_BGEMM = 6    /* moe_backward only: forward recompute on the backward GEMM */
+} moe_path;
+
 /* moe_route flag: take the fp32 logits from `logits` instead of computing the
  * router GEMM (x and w_router are then ignored and may be NULL). */
 #define MOE_ROUTE_LOGITS_GIVEN 1u
@@ -211,6 +222,14 @@ int64_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf);
 
 /* Device workspace bytes that `entry` needs for `shape`. */
 moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* bytes);
+
+/* Diagnostic, host only: the moe_path that the expert FFN of `entry`
+ * (MOE_ENTRY_GROUPED_FFN or MOE_ENTRY_FORWARD) takes for `shape`, or, for
+ * MOE_ENTRY_BACKWARD, the path of moe_backward's forward recompute (an FFN
+ * path, or MOE_PATH_BGEMM). The choice depends on the shape only (dtypes,
+ * widths and the capacity-bound row count), never on the routing. Returns a
+ * negative moe_status for an invalid shape or entry. */
+int32_t moe_ffn_path(const moe_shape* shape, int32_t entry);
 
 /*
  * Router (aigrafen y/g equation; starphix "Key Equations" router_logits = x W_r^T;

@@ -84,6 +84,8 @@ def lib():
         L.moe_capacity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
         L.moe_capacity.restype = ctypes.c_int64
         L.moe_workspace_size.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(sz)]
+        L.moe_ffn_path.argtypes = [sp, ctypes.c_int32]
+        L.moe_ffn_path.restype = ctypes.c_int32
         L.moe_route.argtypes = [sp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, stp, vp, sz, vp]
         L.moe_permute.argtypes = [sp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
         L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
@@ -144,6 +146,17 @@ def workspace_size(shape: Shape, entry: int = ENTRY_FORWARD) -> int:
     n = ctypes.c_size_t()
     _check(lib().moe_workspace_size(ctypes.byref(shape), entry, ctypes.byref(n)), "moe_workspace_size")
     return n.value
+
+
+PATH_F32, PATH_STREAM, PATH_REG128, PATH_REG256, PATH_DMA256, PATH_DMA128, PATH_BGEMM = range(7)
+
+
+def ffn_path(shape: Shape, entry: int = ENTRY_FORWARD) -> int:
+    """moe_ffn_path: the kernel family of the expert FFN (or of moe_backward's
+    forward recompute) for this shape."""
+    rc = lib().moe_ffn_path(ctypes.byref(shape), entry)
+    _check(rc if rc < 0 else MOE_OK, "moe_ffn_path")
+    return rc
 
 
 def workspace(shape: Shape, entry: int = ENTRY_FORWARD, device="cuda"):

@@ -549,6 +549,29 @@ moe_status moe_workspace_size(const moe_shape* shape, int32_t entry, size_t* byt
   return MOE_OK;
 }
 
+int32_t moe_ffn_path(const moe_shape* shape, int32_t entry) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (entry != MOE_ENTRY_GROUPED_FFN && entry != MOE_ENTRY_FORWARD && entry != MOE_ENTRY_BACKWARD)
+    return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *shape;
+  if (entry == MOE_ENTRY_BACKWARD && !bwd_uses_ffn(s)) return moe::kPathBgemm;
+  moe::FfnArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.d_ff = s.d_ff;
+  a.n_routed = s.n_experts;
+  a.n_shared = s.n_shared;
+  a.act = s.act;
+  a.act_dtype = s.act_dtype;
+  a.w_dtype = s.w_dtype;
+  a.routed_row_cap = routed_row_cap(s);
+  // the integer-weight prefill tiles need the bf16 copy the workspace then holds
+  static char dq_marker;
+  a.wdq = moe::uses_int_dequant(s.act_dtype, s.w_dtype, a.routed_row_cap, s.n_shared, s.T) ? &dq_marker : nullptr;
+  return moe::ffn_path_of(a);
+}
+
 moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
                      float* logits, uint32_t flags, int32_t* topk_idx, float* topk_w, const moe_stats* stats,
                      void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -137,7 +137,9 @@ __device__ __forceinline__ SplitPlan split_plan(const GemmParams& p, int ks_pair
   sp.total = p.tile_start[p.n_groups] * (p.Nout / BNO);
   sp.r = sp.total % p.ncu;
   sp.s = 1;
-  if (p.split_part && sp.r > 0 && 2 * sp.r <= p.ncu)
+  // the full rounds are then a multiple of the CU count; their XCD-ordered
+  // mapping needs that to be a multiple of the XCD count as well
+  if (p.split_part && sp.r > 0 && 2 * sp.r <= p.ncu && p.ncu % kXcds == 0)
     sp.s = min(min(p.ncu / sp.r, kMaxSplit), min(kSplitUnits / sp.r, ks_pairs));
   if (sp.s < 2) sp.s = 1;
   sp.full = sp.s > 1 ? sp.total - sp.r : sp.total;
@@ -1295,6 +1297,17 @@ int device_cus() {
 }  // namespace
 
 bool swi_layer(const FfnArgs& a) { return a.act == 1; }
+
+int ffn_path_of(const FfnArgs& a) {
+  if (use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T)) return kPathStream;
+  if (a.act_dtype == 0) return kPathF32;
+  switch (pick_cfg(a)) {
+    case kReg256: return kPathReg256;
+    case kDma256: return kPathDma256;
+    case kDma128: return kPathDma128;
+    default: return kPathReg128;
+  }
+}
 
 size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act) {
   const int64_t up = (act == 1 ? 2 : 1) * d_ff * (d + kActPad), down = d * (d_ff + kActPad);

@@ -168,6 +168,11 @@ FfnPlan ffn_plan(const FfnArgs& a);
 constexpr int64_t kSplitPartFloats = 256LL * 256 * 256;
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+// Kernel family launch_grouped_ffn takes for these arguments (the values of
+// moe_ffn_path in moe.h).
+enum FfnPath { kPathF32 = 0, kPathStream = 1, kPathReg128 = 2, kPathReg256 = 3, kPathDma256 = 4, kPathDma128 = 5,
+               kPathBgemm = 6 };
+int ffn_path_of(const FfnArgs& a);
 
 // Decode-sized layers (few rows per expert) stream expert weights instead of
 // tiling rows: taken when all expert rows of the call fit in kSkinnyMaxRows.

@@ -8,7 +8,9 @@ import re
 import numpy as np
 import pytest
 
+import gen
 import sparse_mixture_experts_36_amd as moe
+from helpers import shape_of
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -241,3 +243,25 @@ def test_backward_host_checks_return_before_launch():
         su = _shape(**kw) if kw else _shape(act_dtype=moe.BF16, w_dtype=moe.INT_W)
         assert L.moe_backward(ctypes.byref(su), fake, ctypes.byref(w), fake, 0.0, 0.0, ctypes.byref(g), fake,
                               1 << 40, None) == moe.MOE_ERR_UNSUPPORTED, kw
+
+
+def test_ffn_path_of_each_workload():
+    """moe_ffn_path (host only): the kernel family each workload's expert FFN
+    takes, and the backward recompute's."""
+    expect = {
+        "tiny-gelu-fp32": moe.PATH_F32,
+        "mixtral-prefill-bf16": moe.PATH_DMA256,
+        "fine-grained-160x6-shared2-bf16": moe.PATH_DMA256,
+        "switch-top1-bf16": moe.PATH_DMA128,
+        "switch-top1-fp8w": moe.PATH_REG256,
+        "mixtral-prefill-int8x2-int4x6": moe.PATH_DMA256,
+    }
+    for name, path in expect.items():
+        wl = gen.WORKLOADS[name]
+        assert moe.ffn_path(shape_of(wl)) == path, name
+    for T in (1, 16, 64):
+        assert moe.ffn_path(shape_of(gen.MIXTRAL_DECODE[T])) == moe.PATH_STREAM
+    assert moe.ffn_path(shape_of(gen.MIXTRAL_PREFILL), moe.ENTRY_BACKWARD) == moe.PATH_DMA256
+    assert moe.ffn_path(shape_of(gen.MIXTRAL_PREFILL.with_(T=512)), moe.ENTRY_BACKWARD) == moe.PATH_BGEMM
+    with pytest.raises(moe.MoEError):
+        moe.ffn_path(shape_of(gen.MIXTRAL_PREFILL), moe.ENTRY_ROUTE)

@@ -50,14 +50,31 @@ CASES = {
     "fine-grained-like-64x6-shared2": _wl("b7", 256, 256, 256, 64, 6, gen.SWIGLU, gen.SOFTMAX_TOPK, n_shared=2,
                                           zipf=1.0),
     # 2048 rows or more: the forward recompute runs on the forward's grouped
-    # FFN (256-row DMA tiles here; 128-row ones with GELU, biases and drops)
+    # FFN: 256-row DMA tiles (SwiGLU with a shared expert; GELU with biases,
+    # where three of the four experts end in a short tail on 128-row tiles)
+    # and 128-row DMA tiles (GELU, biases and capacity drops)
     "swiglu-ffn-dma256-T2048-shared1": _wl("b8", 2048, 256, 512, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
-    "gelu-ffn-dma128-renorm-cf1-biases": _wl("b9", 1024, 256, 384, 8, 2, gen.GELU, gen.SOFTMAX_TOPK_RENORM, cf=1.0,
+    "gelu-ffn-dma128-renorm-cf1-biases": _wl("b9", 1024, 256, 512, 8, 2, gen.GELU, gen.SOFTMAX_TOPK_RENORM, cf=1.0,
                                              zipf=1.0),
+    "gelu-ffn-dma256-tails-biases": _wl("b11", 2048, 256, 512, 4, 2, gen.GELU, gen.SOFTMAX_TOPK, zipf=0.5),
     # widths the 256-wide tiles do not divide: clamped columns in every
     # product, and the recompute on the backward GEMM although rows >= 2048
     "swiglu-d384-dff384-T1024-shared1": _wl("b10", 1024, 384, 384, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
 }
+
+
+# the kernel family of each case's forward recompute (moe_ffn_path)
+RECOMPUTE_PATH = {
+    "swiglu-ffn-dma256-T2048-shared1": moe.PATH_DMA256,
+    "gelu-ffn-dma128-renorm-cf1-biases": moe.PATH_DMA128,
+    "gelu-ffn-dma256-tails-biases": moe.PATH_DMA256,
+}
+
+
+def test_backward_cases_reach_their_recompute_paths():
+    for name, wl in CASES.items():
+        got = moe.ffn_path(shape_of(wl), moe.ENTRY_BACKWARD)
+        assert got == RECOMPUTE_PATH.get(name, moe.PATH_BGEMM), (name, got)
 
 
 def _inputs(wl, seed):

@@ -282,15 +282,15 @@ def test_ec_full_mixtral_prefill(pad):
     """T = 4096, d = 4096, d_ff = 14336, N = 8, C = 1024 (cf 2); pad=64 is the
     weight layout the benchmark times."""
     inp = gen.make_inputs(gen.MIXTRAL_PREFILL_EC, router_grid=True)
-    run_ec(inp, sample=_sample(4096, 10), label="mixtral-prefill-ec (full)", pad=pad)
+    run_ec(inp, sample=_sample(4096, 64), label="mixtral-prefill-ec (full)", pad=pad)
 
 
 def test_ec_full_mixtral_prefill_real_logits():
     inp = gen.make_inputs(gen.MIXTRAL_PREFILL_EC)
-    run_ec(inp, sample=_sample(4096, 8, seed=1), label="mixtral-prefill-ec real logits (full)", pad=64,
+    run_ec(inp, sample=_sample(4096, 64, seed=1), label="mixtral-prefill-ec real logits (full)", pad=64,
            exact=False)
 
 
 def test_ec_full_fine_grained():
     inp = gen.make_inputs(gen.FINE_GRAINED_EC, router_grid=True)
-    run_ec(inp, sample=_sample(8192, 6), label="fine-grained-ec (full)", pad=64)
+    run_ec(inp, sample=_sample(8192, 64), label="fine-grained-ec (full)", pad=64)

@@ -29,6 +29,24 @@ def _cuda():
     torch.cuda.synchronize()
 
 
+MARGIN = 1e-3  # the checking protocol's near-tie threshold on the fp32 logits
+
+
+def margin_report(r, diff, inv_gpu, inv_ref, capped):
+    """Tokens whose top-k set margin l_(k) - l_(k+1) or slot-order margin
+    min_j l_(j) - l_(j+1) (j < k) is below 1e-3, counted apart from the rest,
+    with the routing differences among them and the tokens whose kept / dropped
+    pattern differs. Returns the near-tie mask."""
+    near_set = r.margin_set < MARGIN
+    near_order = r.margin_order < MARGIN
+    near = near_set | near_order
+    drop_diff = ((inv_gpu < 0) != (inv_ref < 0)).any(1) if capped else np.zeros(len(diff), bool)
+    say(f"  margin < {MARGIN:g}: set {int(near_set.sum())}, slot order {int(near_order.sum())}; "
+        f"routed differently among them {int((diff & near).sum())}, elsewhere {int((diff & ~near).sum())}; "
+        f"tokens with a different drop pattern {int(drop_diff.sum())}")
+    return near
+
+
 def run_and_check(inp, sample=None, exact_routing=False, label="", pad=0):
     import torch
     wl = inp.wl
@@ -58,6 +76,9 @@ def run_and_check(inp, sample=None, exact_routing=False, label="", pad=0):
             assert (l64[t, gi[t]] >= kth - thr).all()
         diff = (gi != r.topk_idx).any(1)
         say(f"  logit err {err:.2e}; near-tie tokens {int(amb.sum())}; routed differently {int(diff.sum())}")
+    near = margin_report(r, diff, host(out.inv_map), dsp.inv_map, wl.capacity() >= 0)
+    # every token clear of a tie by the protocol's 1e-3 routes bit-identically
+    assert not (diff & ~near).any()
     assert np.allclose(host(out.topk_w)[~diff], r.topk_w[~diff], rtol=1e-4, atol=1e-6)
 
     # tokens whose result the comparison can trust
@@ -187,24 +208,24 @@ def test_full_tiny_gelu_fp32():
 def test_full_mixtral_prefill(pad):
     """pad=64 is the weight layout the benchmark times."""
     inp = gen.make_inputs(gen.MIXTRAL_PREFILL)
-    run_and_check(inp, sample=_sample(4096, 12), label="mixtral-prefill (full)", pad=pad)
+    run_and_check(inp, sample=_sample(4096, 64), label="mixtral-prefill (full)", pad=pad)
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])
 def test_full_mixtral_decode(T):
     inp = gen.make_inputs(gen.MIXTRAL_DECODE[T])
-    run_and_check(inp, sample=None if T <= 16 else _sample(T, 12), label=f"mixtral-decode T={T}", pad=64)
+    run_and_check(inp, sample=None, label=f"mixtral-decode T={T}", pad=64)
 
 
 def test_full_fine_grained():
     inp = gen.make_inputs(gen.FINE_GRAINED)
-    run_and_check(inp, sample=_sample(8192, 6), label="fine-grained (full)", pad=64)
+    run_and_check(inp, sample=_sample(8192, 64), label="fine-grained (full)", pad=64)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_full_switch(fp8):
     wl = gen.SWITCH_TOP1_FP8 if fp8 else gen.SWITCH_TOP1
-    run_and_check(gen.make_inputs(wl), sample=_sample(16384, 48), label=wl.name + " (full)")
+    run_and_check(gen.make_inputs(wl), sample=_sample(16384, 64), label=wl.name + " (full)")
 
 
 def test_full_switch_exact_routing_grid():

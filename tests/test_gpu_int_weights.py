@@ -72,7 +72,7 @@ def test_int_full_mixtral_decode(T):
 
 def test_int_full_mixtral_prefill():
     inp = gen.make_inputs(gen.MIXTRAL_PREFILL_INT)
-    run_and_check(inp, sample=_sample(4096, 8), label="mixtral-prefill-int (full)", pad=64)
+    run_and_check(inp, sample=_sample(4096, 64), label="mixtral-prefill-int (full)", pad=64)
 
 
 def test_int_bits_validated_on_host():
