@@ -47,6 +47,7 @@ CASES = {
     "gelu-top1-T1": _wl("b4", 1, 128, 128, 4, 1, gen.GELU, gen.SOFTMAX_TOPK),
     "swiglu-capacity0-shared1": _wl("b5", 64, 128, 128, 8, 1, gen.SWIGLU, gen.TOPK_SOFTMAX, cf=0.01, n_shared=1),
     "mixtral-like-T512": _wl("b6", 512, 1024, 1536, 8, 2, gen.SWIGLU, gen.TOPK_SOFTMAX),
+    # 64 experts and two shared ones: 1536 routed + 512 shared rows, 128-row DMA tiles for the recompute
     "fine-grained-like-64x6-shared2": _wl("b7", 256, 256, 256, 64, 6, gen.SWIGLU, gen.SOFTMAX_TOPK, n_shared=2,
                                           zipf=1.0),
     # 2048 rows or more: the forward recompute runs on the forward's grouped
@@ -65,6 +66,7 @@ CASES = {
 
 # the kernel family of each case's forward recompute (moe_ffn_path)
 RECOMPUTE_PATH = {
+    "fine-grained-like-64x6-shared2": moe.PATH_DMA128,  # 2048 rows with the shared experts' T each
     "swiglu-ffn-dma256-T2048-shared1": moe.PATH_DMA256,
     "gelu-ffn-dma128-renorm-cf1-biases": moe.PATH_DMA128,
     "gelu-ffn-dma256-tails-biases": moe.PATH_DMA256,
