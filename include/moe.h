@@ -315,6 +315,27 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
                        const moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and outputs as moe_forward, with the workspace
+ * taken from a device array inside the library instead of `ws`. That array
+ * holds MOE_NOALLOC_SCRATCH_BYTES on each GPU the call runs on; it is created
+ * with the library's code on that GPU and kept until the process ends. The
+ * call allocates nothing. Shapes whose MOE_ENTRY_FORWARD workspace
+ * (moe_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES return
+ * MOE_ERR_WORKSPACE and launch nothing: this covers decode-sized layers (the
+ * Mixtral-shape layer up to 128 tokens) but not prefill. Every call on one GPU
+ * uses that GPU's single array: calls that overlap on one GPU (concurrent
+ * streams, or host threads) race and give undefined results; calls ordered on
+ * one stream are safe. The array's contents between calls do not matter.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const moe_weights* weights,
+                               void* y, float* logits, int32_t* topk_idx, float* topk_w,
+                               int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_map,
+                               const moe_stats* stats, hipStream_t stream);
+
+/*
  * Gradients written by moe_backward. dx is required; every other member may be
  * NULL (that gradient is not computed). Weight gradients are fp32 in the
  * contiguous nn.Linear layout of the weights they belong to (no row pitch),

@@ -91,12 +91,13 @@ def lib():
         L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [sp, vp, wp, vp, vp, vp, vp, vp, vp, vp, stp, vp, sz, vp]
+        L.moe_forward_noalloc.argtypes = [sp, vp, wp, vp, vp, vp, vp, vp, vp, vp, stp, vp]
         L.moe_backward.argtypes = [sp, vp, wp, vp, ctypes.c_float, ctypes.c_float, ctypes.POINTER(Grads), vp, sz,
                                    vp]
         L.moe_timing_start.argtypes = [ctypes.c_int32]
         L.moe_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         for f in ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                  "moe_forward", "moe_backward", "moe_timing_start", "moe_timing_stop"):
+                  "moe_forward", "moe_forward_noalloc", "moe_backward", "moe_timing_start", "moe_timing_stop"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,6 +222,21 @@ def forward(shape, x, weights: Weights, y, logits=None, topk_idx=None, topk_w=No
                            _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_token), _ptr(inv_map),
                            ctypes.byref(st) if st else None, _ptr(ws_), ws_.numel(), _stream(stream))
     _check(rc, "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(shape, x, weights: Weights, y, logits=None, topk_idx=None, topk_w=None, expert_offsets=None,
+                    perm_token=None, inv_map=None, stats=None, stream=None):
+    """moe_forward_noalloc: moe_forward with the library's own device scratch
+    (no workspace argument, nothing allocated; shapes whose forward workspace
+    exceeds NOALLOC_SCRATCH_BYTES raise MoEError with MOE_ERR_WORKSPACE)."""
+    st = stats_struct(stats)
+    rc = lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y), _ptr(logits),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_token),
+                                   _ptr(inv_map), ctypes.byref(st) if st else None, _stream(stream))
+    _check(rc, "moe_forward_noalloc")
 
 
 def alloc_grads(shape: Shape, device="cuda") -> dict:

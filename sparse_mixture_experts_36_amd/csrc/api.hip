@@ -478,6 +478,36 @@ void stage_mark(int stage, bool end, hipStream_t s) {
 }
 }  // namespace moe
 
+// moe_forward_noalloc's workspace: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends. Its name is a host-side
+// stand-in in host code (never passed to a kernel); the device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+
 extern "C" {
 
 moe_status moe_timing_start(int32_t max_launches) {
@@ -699,6 +729,19 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
     e = moe::launch_combine(a, stream);
   }
   return hip_status(e);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const moe_weights* weights, void* y,
+                               float* logits, int32_t* topk_idx, float* topk_w, int32_t* expert_offsets,
+                               int32_t* perm_token, int32_t* inv_map, const moe_stats* stats, hipStream_t stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (ws_bytes_for(*shape, MOE_ENTRY_FORWARD) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const moe_status sp = scratch_ptr(&ws);
+  if (sp != MOE_OK) return sp;
+  return moe_forward(shape, x, weights, y, logits, topk_idx, topk_w, expert_offsets, perm_token, inv_map, stats, ws,
+                     MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_backward(const moe_shape* shape, const void* x, const moe_weights* weights, const void* dy,

@@ -1,0 +1,72 @@
+"""moe_forward_noalloc (the forward that takes its workspace from the
+library's own device array) against moe_forward with a caller workspace, through
+the C ABI: two calls in a row, the second on a smaller input, must give the
+same bits as moe_forward on the same inputs; a shape whose workspace exceeds the
+array is refused before anything is launched."""
+import numpy as np
+import pytest
+
+import gen
+import sparse_mixture_experts_36_amd as moe
+from helpers import dev, device_weights, host, say, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(shape, device="cuda"):
+    import torch
+    T, N = shape.T, shape.n_experts
+    rs = moe.routing_shapes(shape)
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(y=torch.full((T, shape.d), float("nan"), dtype=torch.bfloat16, device=device),
+                logits=torch.empty((T, N), dtype=torch.float32, device=device),
+                topk_idx=torch.empty(rs["topk"], **i32),
+                topk_w=torch.empty(rs["topk"], dtype=torch.float32, device=device),
+                expert_offsets=torch.empty(N + 1, **i32), perm_token=torch.empty(rs["perm_token"], **i32),
+                inv_map=torch.empty(rs["inv_map"], **i32), stats=moe.alloc_stats(N, device))
+
+
+def _same(a: dict, b: dict, M: int):
+    for k in ("y", "logits", "topk_idx", "topk_w", "expert_offsets", "inv_map"):
+        assert np.array_equal(host(a[k]).view(np.uint8), host(b[k]).view(np.uint8)), k
+    assert np.array_equal(host(a["perm_token"])[:M], host(b["perm_token"])[:M])
+    for k in a["stats"]:
+        assert np.array_equal(host(a["stats"][k]).view(np.uint8), host(b["stats"][k]).view(np.uint8)), k
+
+
+def test_noalloc_forward_matches_forward_twice():
+    import torch
+    base = gen.MIXTRAL_PREFILL.with_(d=1024, d_ff=1536)
+    inp = gen.make_inputs(base.with_(T=64))
+    w = moe.weights_struct(device_weights(inp, 64))
+    x_all = dev(inp.x)
+    for T in (64, 16):  # the second call on a smaller input
+        shape = shape_of(base.with_(T=T))
+        assert moe.workspace_size(shape, moe.ENTRY_FORWARD) <= moe.NOALLOC_SCRATCH_BYTES
+        x = x_all[:T].contiguous()
+        ref, got = _outputs(shape), _outputs(shape)
+        moe.forward(shape, x, w, ref["y"], ref["logits"], ref["topk_idx"], ref["topk_w"], ref["expert_offsets"],
+                    ref["perm_token"], ref["inv_map"], ref["stats"])
+        moe.forward_noalloc(shape, x, w, got["y"], got["logits"], got["topk_idx"], got["topk_w"],
+                            got["expert_offsets"], got["perm_token"], got["inv_map"], got["stats"])
+        torch.cuda.synchronize()
+        M = int(host(ref["expert_offsets"])[-1])
+        assert torch.isfinite(got["y"].float()).all()
+        _same(got, ref, M)
+        say(f"noalloc forward T={T}: identical to moe_forward ({M} routed rows)")
+
+
+def test_noalloc_forward_refuses_large_workspace():
+    import torch
+    wl = gen.MIXTRAL_PREFILL.with_(T=256, d=1024, d_ff=1536)
+    shape = shape_of(wl)
+    assert moe.workspace_size(shape, moe.ENTRY_FORWARD) > moe.NOALLOC_SCRATCH_BYTES
+    inp = gen.make_inputs(wl)
+    w = moe.weights_struct(device_weights(inp))
+    out = _outputs(shape)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.forward_noalloc(shape, dev(inp.x), w, out["y"], out["logits"], out["topk_idx"], out["topk_w"],
+                            out["expert_offsets"], out["perm_token"], out["inv_map"], out["stats"])
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.isnan(out["y"].float()).all()  # nothing was launched
