@@ -233,3 +233,44 @@ def test_full_switch_exact_routing_grid():
     set and the counts must match the oracle bit for bit."""
     inp = gen.make_inputs(gen.SWITCH_TOP1, router_grid=True)
     run_and_check(inp, sample=_sample(16384, 32), exact_routing=True, label="switch exact-grid (full)")
+
+
+WS_CASES = {
+    "decode-T1-gemv": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
+    "decode-T2-gemv-shared": gen.FINE_GRAINED.with_(T=2, d=512, d_ff=1024),
+    "decode-T16-stream": gen.MIXTRAL_PREFILL.with_(T=16, d=1024, d_ff=1536),
+    "decode-T24-shared": gen.FINE_GRAINED.with_(T=24, d=512, d_ff=256),
+    "prefill-dma128-drops": gen.SWITCH_TOP1.with_(T=2048, d=512, d_ff=1024),
+    "prefill-dma256-split-tails": gen.MIXTRAL_PREFILL.with_(T=4096, d=1024, d_ff=1536),
+    "prefill-reg128": gen.MIXTRAL_PREFILL.with_(T=512, d=1024, d_ff=1536),
+    "prefill-fp8-reg256": gen.SWITCH_TOP1_FP8.with_(T=4096, d=512, d_ff=1024),
+    "tiny-fp32": gen.TINY_GELU,
+    "expert-choice": gen.WORKLOADS["tiny-gelu-fp32-ec"],
+}
+
+
+@pytest.mark.parametrize("name", list(WS_CASES))
+def test_forward_ignores_workspace_contents(name):
+    """The workspace's contents on entry do not matter: one filled with 0xFF
+    bytes (NaN as floats) and one filled with zeros give the same bits."""
+    import torch
+    wl = WS_CASES[name]
+    inp = gen.make_inputs(wl)
+    s = shape_of(wl)
+    t = device_weights(inp, 64 if wl.act_dtype == gen.BF16 else 0)  # kept alive: the struct holds raw pointers
+    w = moe.weights_struct(t)
+    x = dev(inp.x)
+    res = []
+    for fill in (0x00, 0xFF):
+        ws = moe.workspace(s, moe.ENTRY_FORWARD)
+        ws.view(torch.uint8).fill_(fill)
+        o = moe.MoELayer(s, t).out  # its output tensors; the call below takes the workspace filled above
+        moe.forward(s, x, w, o.y, o.logits, o.topk_idx, o.topk_w, o.expert_offsets, o.perm_token, o.inv_map,
+                    o.stats, ws=ws)
+        torch.cuda.synchronize()
+        res.append({k: host(getattr(o, k)).copy() for k in ("y", "logits", "topk_idx", "topk_w", "inv_map")})
+        res[-1].update({"stats." + k: host(v).copy() for k, v in o.stats.items()})
+    for k in res[0]:
+        assert np.array_equal(res[0][k].view(np.uint8), res[1][k].view(np.uint8)), k
+    assert np.isfinite(as_f64(res[0]["y"])).all()
+    say(f"workspace contents {name}: identical outputs")

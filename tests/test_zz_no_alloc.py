@@ -38,7 +38,8 @@ def test_noalloc_forward_matches_forward_twice():
     import torch
     base = gen.MIXTRAL_PREFILL.with_(d=1024, d_ff=1536)
     inp = gen.make_inputs(base.with_(T=64))
-    w = moe.weights_struct(device_weights(inp, 64))
+    t = device_weights(inp, 64)  # kept alive: the struct holds raw device pointers
+    w = moe.weights_struct(t)
     x_all = dev(inp.x)
     for T in (64, 16):  # the second call on a smaller input
         shape = shape_of(base.with_(T=T))
@@ -62,7 +63,8 @@ def test_noalloc_forward_refuses_large_workspace():
     shape = shape_of(wl)
     assert moe.workspace_size(shape, moe.ENTRY_FORWARD) > moe.NOALLOC_SCRATCH_BYTES
     inp = gen.make_inputs(wl)
-    w = moe.weights_struct(device_weights(inp))
+    t = device_weights(inp)  # kept alive: the struct holds raw device pointers
+    w = moe.weights_struct(t)
     out = _outputs(shape)
     with pytest.raises(moe.MoEError) as ei:
         moe.forward_noalloc(shape, dev(inp.x), w, out["y"], out["logits"], out["topk_idx"], out["topk_w"],
