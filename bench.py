@@ -103,6 +103,27 @@ def weight_bytes_per_expert(wl, e: int = 0) -> int:
     return params * wb
 
 
+def layer_bytes(wl, kept) -> tuple[int, int, int]:
+    """Algorithmic HBM bytes of one layer call: every touched expert's weights
+    once (plus the shared experts'), the router weight, x read once and y
+    written once. Returns (layer bytes, expert-weight bytes, touched experts)."""
+    import gen
+    import sparse_mixture_experts_36_amd as moe
+    touched = [e for e in range(wl.n_experts) if kept[e] > 0]
+    wbytes = sum(weight_bytes_per_expert(wl, e) for e in touched)
+    if wl.n_shared:
+        params = moe.expert_params(wl.d, wl.d_ff, wl.act)
+        if wl.w_dtype == gen.INT_W:
+            rows = (2 if wl.act == gen.SWIGLU else 1) * wl.d_ff + wl.d
+            per = params * 8 // 8 + 4 * rows  # shared experts keep 8-bit codes
+        else:
+            per = params * {gen.F32: 4, gen.BF16: 2, gen.E4M3: 1}[wl.w_dtype]
+        wbytes += wl.n_shared * per
+    act_b = 4 if wl.act_dtype == gen.F32 else 2
+    io = 2 * wl.T * wl.d * act_b + wl.n_experts * wl.d * act_b
+    return wbytes + io, wbytes, len(touched)
+
+
 def up_flops_per_pair(wl) -> float:
     """Up GEMM: d x d_ff per matrix, two matrices (W1, W3) for SwiGLU."""
     return 2.0 * wl.d * wl.d_ff * (2 if wl.act == 1 else 1)
@@ -428,6 +449,7 @@ def main():
     router_flops = 2.0 * wl.T * wl.d * wl.n_experts
     bf16 = wl.act_dtype == gen.BF16
     achieved = up_flops / (up_ms * 1e-3) / 1e12
+    lbytes, wbytes, touched = layer_bytes(wl, r["latest"]["kept"])
     result = {
         "metric": "MoE-layer tokens/s (Mixtral-shape prefill) + % bf16 MFMA peak; decode HBM GB/s",
         "value": round(wl.T / (ms * 1e-3), 1),
@@ -454,6 +476,9 @@ def main():
                      "algorithmic_flops_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4)},
         "layer": {"mfma_frac": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "ffn_mfma_frac": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "hbm_frac": round(lbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "ffn_hbm_frac": round(wbytes / ((up_ms + down_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "alg_bytes": lbytes, "expert_weight_bytes": wbytes, "touched_experts": touched,
                   "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in st.items()},
                   "rows": r["rows"], "dropped": dropped_of(wl, r["latest"]), "near_tie_tokens": r["near"],
                   "l_aux": None if r["latest"]["aux_loss"] is None else round(r["latest"]["aux_loss"], 6),

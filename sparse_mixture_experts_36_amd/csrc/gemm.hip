@@ -1479,11 +1479,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
       err = swi ? run_wf<EPI_SWIGLU>(wc.wf[c], cfg, p, max_mtiles, s) : run_wf<EPI_GELU>(wc.wf[c], cfg, p, max_mtiles, s);
     }
-    if (err == hipSuccess && pl.bm_t > 0) {  // the groups' short tails on 128-row tiles
+    if (err == hipSuccess && pl.bm_t > 0) {  // small groups and the groups' short tails on 128-row tiles
       GemmParams pt = p;
       pt.groups = pl.up_t;
       pt.tile_start = pl.tile_start_t;
-      err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, G, s) : run_dma<EPI_GELU, 128, 8>(pt, G, s);
+      const int64_t mt = static_cast<int64_t>(kSmallGroupTiles) * G;  // row tiles of the second plan, at most
+      err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, mt, s) : run_dma<EPI_GELU, 128, 8>(pt, mt, s);
     }
   }
   stage_mark(kStageFfnUp, true, s);
@@ -1524,7 +1525,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
       GemmParams pt = p;
       pt.groups = pl.down_t;
       pt.tile_start = pl.tile_start_t;
-      err = run_dma<EPI_PLAIN, 128, 8>(pt, G, s);
+      err = run_dma<EPI_PLAIN, 128, 8>(pt, static_cast<int64_t>(kSmallGroupTiles) * G, s);
     }
   }
   stage_mark(kStageFfnDown, true, s);

@@ -168,6 +168,9 @@ FfnPlan ffn_plan(const FfnArgs& a);
 constexpr int64_t kSplitPartFloats = 256LL * 256 * 256;
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+// Groups of at most this many 128-row tiles run whole on the 128-row tiles
+// next to the 256-row launch (see plan_groups).
+constexpr int kSmallGroupTiles = 3;
 // Kernel family launch_grouped_ffn takes for these arguments (the values of
 // moe_ffn_path in moe.h).
 enum FfnPath { kPathF32 = 0, kPathStream = 1, kPathReg128 = 2, kPathReg256 = 3, kPathDma256 = 4, kPathDma128 = 5,

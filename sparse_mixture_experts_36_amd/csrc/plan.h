@@ -11,9 +11,13 @@ namespace moe {
 // Routed expert e: rows [offsets[e], offsets[e+1]) of x_perm / h / y_perm,
 // clamped to the reserved routed rows. Shared expert s: the T token rows; its
 // hidden rows sit after the routed ones in h, its outputs in y_shared[s].
-// With bm_t > 0, a group whose last tile would hold r <= bm_t rows gives those
-// r rows to the tail plan (one bm_t-row tile, a second launch) and keeps the
-// rest: less padding in the last tile. active[0] = the number of groups with
+// With bm_t > 0, a group of at most kSmallGroupTiles * bm_t rows goes to the
+// second plan (bm_t-row tiles, a second launch) whole: its few row tiles then
+// run side by side there and share each weight tile in L2, where a separate
+// tail tile would stream the expert's weights from HBM a second time. A larger
+// group whose last tile would hold r <= bm_t rows gives those r rows to the
+// second plan (one tile) and keeps the rest: less padding in its last tile.
+// active[0] = the number of groups with
 // rows, active[1..] those groups in order. Run by all threads of one
 // workgroup; s_mt holds 2 (n_routed + n_shared) ints of LDS. Ends with a
 // workgroup barrier.
@@ -40,7 +44,8 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
     int tail = 0;
     if (pl.bm_t > 0) {
       const int rem = u.rows % pl.bm;
-      if (rem > 0 && rem <= pl.bm_t) tail = rem;
+      if (u.rows <= kSmallGroupTiles * pl.bm_t) tail = u.rows;
+      else if (rem > 0 && rem <= pl.bm_t) tail = rem;
       const int keep = u.rows - tail;
       GroupDesc ut = u, dt = dn;
       ut.a_row0 += keep;
@@ -51,7 +56,7 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
       pl.up_t[g] = ut;
       pl.down_t[g] = dt;
       u.rows = dn.rows = keep;
-      s_mt[G + g] = tail > 0 ? 1 : 0;
+      s_mt[G + g] = (tail + pl.bm_t - 1) / pl.bm_t;
     }
     pl.up[g] = u;
     pl.down[g] = dn;

@@ -58,6 +58,9 @@ CASES = {
     "gelu-ffn-dma128-renorm-cf1-biases": _wl("b9", 1024, 256, 512, 8, 2, gen.GELU, gen.SOFTMAX_TOPK_RENORM, cf=1.0,
                                              zipf=1.0),
     "gelu-ffn-dma256-tails-biases": _wl("b11", 2048, 256, 512, 4, 2, gen.GELU, gen.SOFTMAX_TOPK, zipf=0.5),
+    # skewed groups on 256-row tiles: nine small groups whole on 128-row tiles
+    "swiglu-ffn-dma256-small-groups-shared1": _wl("b12", 2048, 512, 512, 12, 2, gen.SWIGLU, gen.SOFTMAX_TOPK,
+                                                  n_shared=1, zipf=1.0),
     # widths the 256-wide tiles do not divide: clamped columns in every
     # product, and the recompute on the backward GEMM although rows >= 2048
     "swiglu-d384-dff384-T1024-shared1": _wl("b10", 1024, 384, 384, 4, 2, gen.SWIGLU, gen.TOPK_SOFTMAX, n_shared=1),
@@ -70,6 +73,7 @@ RECOMPUTE_PATH = {
     "swiglu-ffn-dma256-T2048-shared1": moe.PATH_DMA256,
     "gelu-ffn-dma128-renorm-cf1-biases": moe.PATH_DMA128,
     "gelu-ffn-dma256-tails-biases": moe.PATH_DMA256,
+    "swiglu-ffn-dma256-small-groups-shared1": moe.PATH_DMA256,
 }
 
 

@@ -135,6 +135,10 @@ REDUCED = {
     # d_ff = 384; d = 384): the 128 x 128 tiles take them
     "switch-like-d_ff-384": gen.SWITCH_TOP1.with_(T=4096, d=512, d_ff=384),
     "mixtral-like-d-384": gen.MIXTRAL_PREFILL.with_(T=1024, d=384, d_ff=512),
+    # 256-row tiles with skewed groups: nine of at most 384 rows run whole on
+    # the 128-row tiles, two larger ones end in short tails, one shared expert
+    "fine-grained-like-dma256-small-groups": gen.FINE_GRAINED.with_(T=2048, d=512, d_ff=512, n_experts=12, top_k=2,
+                                                                    n_shared=1, zipf_s=1.0),
     # decode-sized: the weight-streaming path
     "mixtral-like-decode-T1": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
     "mixtral-like-decode-T64": gen.MIXTRAL_PREFILL.with_(T=64, d=1024, d_ff=1536),
