@@ -55,6 +55,7 @@ struct GemmParams {
   int32_t scale_row3;     // integer weights: offset of W3's rows (d_ff)
   uint32_t skip[9];       // bit g set: group g is left to another launch (its experts' other bit width)
   int32_t col_scaled;     // 1: the bf16 weights are integer codes; output column n takes row scale n
+  int32_t mat_scaled;     // 1: e4m3 weights on the DMA tiles; the epilogue applies the per-matrix scales
   void* C_r;
   void* C_s;
   int64_t ldc;            // = Nout
@@ -452,6 +453,13 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
   // integer codes as bf16 weights: one scale per output column (weight row)
   const float* rs = p.col_scaled ? (shared ? p.scale_s : p.scale_r) + static_cast<int64_t>(ew) * p.scale_pitch + n0
                                  : nullptr;
+  // e4m3 weights: one scale per expert matrix (W1 or W2, and W3)
+  float ma = 1.f, mb = 1.f;
+  if (p.mat_scaled) {
+    const float* ms = (shared ? p.scale_s : p.scale_r) + ew * 3 + p.scale_col;
+    ma = ms[0];
+    if (EPI == EPI_SWIGLU) mb = ms[1];
+  }
   uint16_t* C = static_cast<uint16_t*>(shared ? p.C_s : p.C_r) +
                 (static_cast<int64_t>(ti.gd.c_row0) + static_cast<int64_t>(ti.m_tile) * BM) * p.ldc + n0;
 #pragma unroll
@@ -459,8 +467,8 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
     const int col = wn * WTO + j * 16 + c16;         // this lane's column in the fragments
     const int ocol = wn * WTO + j * 16 + 4 * (c16 >> 2);  // the four columns it stores
     const float bv = bias ? bias[col] : 0.f;
-    const float sa = rs ? rs[p.scale_row0 + col] : 1.f;
-    const float sb = (rs && EPI == EPI_SWIGLU) ? rs[p.scale_row3 + col] : 1.f;
+    const float sa = rs ? rs[p.scale_row0 + col] : ma;
+    const float sb = (rs && EPI == EPI_SWIGLU) ? rs[p.scale_row3 + col] : mb;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       float v[4];
@@ -527,17 +535,28 @@ __device__ __forceinline__ float* dma_part_frag(float* part, int unit, int wave,
   return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * C_::FM + i) * C_::FN + j) * 256;
 }
 
-template <int EPI, int BM, int W>
+// WF = kWE4m3: the weight rows arrive as e4m3 bytes (64-byte stage rows, half
+// the bytes); a wave reads each weight fragment as 8 bytes and converts it
+// exactly to bf16 (hardware fp8 conversion) before its MFMAs, and the epilogue
+// applies the per-matrix scale. Those rows keep chunk c of row r at position
+// c ^ ((r >> 2) & 3), at which the 8-byte fragment reads of 16 rows are
+// conflict-free; one DMA instruction fills 16 of them.
+template <int EPI, int BM, int W, int WF>
 __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int BNO = bno(EPI);
   constexpr int FM = C_::FM, FN = C_::FN, WTM = C_::WTM, WTB = C_::WTB, WGN = C_::WGN;
-  constexpr int ADMA = C_::ADMA, BDMA = C_::BDMA, NDMA = C_::NDMA, NSTAGE = C_::NSTAGE;
-  __shared__ __attribute__((aligned(16))) char S0[C_::SBYTES];
-  __shared__ __attribute__((aligned(16))) char S1[C_::SBYTES];
-  __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? C_::SBYTES : 16];
+  constexpr bool F8 = (WF == kWE4m3);
+  static_assert(WF == kWBf16 || F8, "bf16 or e4m3 weights");
+  constexpr int RBB = F8 ? RB / 2 : RB;     // weight row bytes in a stage
+  constexpr int SBY = BM * RB + BNB * RBB;  // one stage buffer
+  constexpr int ADMA = C_::ADMA, BDMA = F8 ? C_::BROWS / 16 : C_::BDMA, NDMA = ADMA + BDMA;
+  constexpr int NSTAGE = F8 ? 3 : C_::NSTAGE;
+  __shared__ __attribute__((aligned(16))) char S0[SBY];
+  __shared__ __attribute__((aligned(16))) char S1[SBY];
+  __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? SBY : 16];
 
   const int K = p.K;
   const int KS = K / BK;  // even: K is a multiple of 128
@@ -583,7 +602,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   const int ar0 = wave * C_::AROWS, wr0 = wave * C_::BROWS;
   const bool w3 = SWI && wr0 >= BNO;
   const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
-                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) * 2;
+                   (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) *
+                       (F8 ? 1 : 2);
   // Lane L of an instruction over rows [r0, r0 + 8) fills row r0 + L/8,
   // position L%8 with logical chunk (L%8) ^ (row & 7); byte offsets are
   // relative to the tile's first A row and the wave's first weight row.
@@ -598,21 +618,27 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   }
 #pragma unroll
   for (int i = 0; i < BDMA; ++i) {
-    const int r = wr0 + i * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (r & 7);
-    offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * static_cast<int>(p.ldb) * 2 + chunk * 16);
+    if constexpr (F8) {  // 16 rows of 64 bytes an instruction: lane L fills row r0 + L/4, position L%4
+      const int r = wr0 + i * 16 + (lane >> 2);
+      const int chunk = (lane & 3) ^ ((r >> 2) & 3);
+      offb[i] = static_cast<uint32_t>((i * 16 + (lane >> 2)) * static_cast<int>(p.ldb) + chunk * 16);
+    } else {
+      const int r = wr0 + i * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (r & 7);
+      offb[i] = static_cast<uint32_t>((i * 8 + (lane >> 3)) * static_cast<int>(p.ldb) * 2 + chunk * 16);
+    }
   }
-  const int dst_a = ar0 * RB, dst_b = BM * RB + wr0 * RB;  // byte offsets inside a stage
+  const int dst_a = ar0 * RB, dst_b = BM * RB + wr0 * RBB;  // byte offsets inside a stage
 // (the source pointer is passed as const void*: with a char* argument the host
 // compilation pass silently drops the kernel's launch stub)
 #define MOE_LDS(x) ((__attribute__((address_space(3))) void*)(x))
 #define MOE_DMA(S, ks)                                                                               \
   do {                                                                                               \
-    const uint32_t ko_ = static_cast<uint32_t>(ks) * RB;                                             \
+    const uint32_t ko_ = static_cast<uint32_t>(ks) * RB, kb_ = static_cast<uint32_t>(ks) * RBB;      \
     _Pragma("unroll") for (int i_ = 0; i_ < ADMA; ++i_)                                              \
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(A + (offa[i_] + ko_)), MOE_LDS((S) + dst_a + i_ * 1024), 16, 0, 0); \
     _Pragma("unroll") for (int i_ = 0; i_ < BDMA; ++i_)                                              \
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bw + (offb[i_] + ko_)), MOE_LDS((S) + dst_b + i_ * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Bw + (offb[i_] + kb_)), MOE_LDS((S) + dst_b + i_ * 1024), 16, 0, 0); \
   } while (0)
 
   floatx4_t acc[FM][FN];
@@ -625,7 +651,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   // u * 4 + q of row c16 (mod 8) sits at position (u * 4 + q) ^ (c16 & 7)
   const int rd0 = c16 * RB + ((q ^ (c16 & 7)) * 16);
   const int rd1 = c16 * RB + (((4 + q) ^ (c16 & 7)) * 16);
-#define MOE_READ(S, RD, AF, BF)                                                                      \
+  // e4m3 weight fragments: k-step u, lane group q takes bytes [32 u + 8 q, +8)
+  // of row c16: chunk 2 u + q / 2, half q % 2
+  const int rdb0 = c16 * RBB + (((q >> 1) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
+  const int rdb1 = c16 * RBB + (((2 + (q >> 1)) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
+  // reads a k-step's fragments: A into AF; weights into BF (bf16) or, raw, into BQ (e4m3)
+#define MOE_READ(S, RD, RDB, AF, BF, BQ)                                                             \
   do {                                                                                               \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
         *reinterpret_cast<const uint4*>((S) + (wm * WTM + i * 16) * RB + RD);                        \
@@ -633,7 +664,18 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
       const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
                                            : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
                            : wn * WTB + j * 16;                                                      \
-      BF[j] = *reinterpret_cast<const uint4*>((S) + BM * RB + brow * RB + RD);                       \
+      if constexpr (F8) BQ[j] = *reinterpret_cast<const uint2*>((S) + BM * RB + brow * RBB + RDB);   \
+      else BF[j] = *reinterpret_cast<const uint4*>((S) + BM * RB + brow * RB + RD);                  \
+    }                                                                                                \
+  } while (0)
+  // e4m3 -> bf16, exact (after the reads have arrived)
+#define MOE_CVT(BQ, BF)                                                                              \
+  do {                                                                                               \
+    if constexpr (F8) {                                                                              \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                               \
+        const uint2 lo_ = e4m3x4_to_bf16x4(BQ[j].x), hi_ = e4m3x4_to_bf16x4(BQ[j].y);                \
+        BF[j] = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                              \
+      }                                                                                              \
     }                                                                                                \
   } while (0)
 #define MOE_MFMA(AC, BC)                                                                             \
@@ -670,7 +712,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
 #define MOE_STAGE(SC, SN, ks)                                                                        \
   do {                                                                                               \
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): af0/bf0 have arrived */                       \
-    MOE_READ(SC, rd1, af1, bf1);                                                                     \
+    MOE_CVT(bq0, bf0);                                                                               \
+    MOE_READ(SC, rd1, rdb1, af1, bf1, bq1);                                                          \
     MOE_MFMA(af0, bf0);                                                                              \
     MOE_SCHEDULE(false);                                                                             \
     /* stage ks+1 landed; the DMA of the NSTAGE-2 later stages may still fly */                      \
@@ -678,7 +721,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): my reads of SC are done */                    \
     __builtin_amdgcn_s_barrier();                                                                    \
     MOE_DMA(SC, MOE_COL(min((ks) + NSTAGE, n_st - 1)));                                              \
-    MOE_READ(SN, rd0, af0, bf0);                                                                     \
+    MOE_CVT(bq1, bf1);                                                                               \
+    MOE_READ(SN, rd0, rdb0, af0, bf0, bq0);                                                          \
     MOE_MFMA(af1, bf1);                                                                              \
     MOE_SCHEDULE(true);                                                                              \
   } while (0)
@@ -724,13 +768,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
 #define MOE_IDLE2(ks) MOE_STAGE_IDLE(S2, ks)
 
   uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
+  uint2 bq0[FN], bq1[FN];  // raw e4m3 fragments (unused for bf16 weights)
   MOE_DMA(S0, MOE_COL(0));
   MOE_DMA(S1, MOE_COL(1));
   if constexpr (NSTAGE == 3) MOE_DMA(S2, MOE_COL(min(2, n_st - 1)));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 1) * NDMA));  // the first stage landed
   __builtin_amdgcn_s_barrier();
   if (wm * WTM < ti.rows) {
-    MOE_READ(S0, rd0, af0, bf0);
+    MOE_READ(S0, rd0, rdb0, af0, bf0, bq0);
     MOE_STAGES(MOE_LIVE0, MOE_LIVE1, MOE_LIVE2);
   } else {
     MOE_STAGES(MOE_IDLE0, MOE_IDLE1, MOE_IDLE2);
@@ -750,6 +795,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
 #undef MOE_SCHEDULE
 #undef MOE_MFMA
 #undef MOE_READ
+#undef MOE_CVT
 #undef MOE_DMA
 #undef MOE_COL
 #undef MOE_LDS
@@ -1189,14 +1235,16 @@ hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 // Tile configurations of the bf16 path.
 enum TileCfg {
   kReg128 = 0,  // register-staged 128 x 128, 4 waves: fewer than 2048 rows
-  kReg256 = 1,  // register-staged 256 x 256, 8 waves: e4m3 or integer weights (decoded in registers)
-  kDma256 = 2,  // LDS-DMA 256 x 256: bf16, many rows per group
-  kDma128 = 3,  // LDS-DMA 128 x 256: bf16, few rows per group
+  kReg256 = 1,  // register-staged 256 x 256, 8 waves: integer weights (decoded in registers)
+  kDma256 = 2,  // LDS-DMA 256 x 256: bf16 or e4m3, many rows per group
+  kDma128 = 3,  // LDS-DMA 128 x 256: bf16 or e4m3, few rows per group
 };
 constexpr int tile_rows(int cfg) { return (cfg == kReg256 || cfg == kDma256) ? 256 : 128; }
 
-template <int EPI, int BM, int W>
-hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
+template <int EPI, int BM, int W, int WF = kWBf16>
+hipError_t run_dma(const GemmParams& p_in, int64_t max_mtiles, hipStream_t s) {
+  GemmParams p = p_in;
+  p.mat_scaled = WF == kWE4m3 ? 1 : 0;
   constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
@@ -1205,7 +1253,7 @@ hipError_t run_dma(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   // a k-split tail runs at most total - r + kSplitUnits workgroups
   if (p.split_part) grid += kSplitUnits;
   constexpr int NTH = dma::Cfg<BM, W>::NTH;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI, BM, W>), dim3(static_cast<unsigned>(grid)), dim3(NTH), 0, s, p);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, BM, W, WF>), dim3(static_cast<unsigned>(grid)), dim3(NTH), 0, s, p);
   if (p.split_part) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1246,7 +1294,13 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 template <int EPI, int WF>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  if constexpr (WF != kWBf16) {
+  if constexpr (WF == kWE4m3) {
+    switch (cfg) {
+      case kDma256: return run_dma<EPI, 256, 8, WF>(p, max_mtiles, s);
+      case kDma128: return run_dma<EPI, 128, 8, WF>(p, max_mtiles, s);
+      default: return run_bf16<128, 128, 2, 2, EPI, WF>(p, max_mtiles, s);
+    }
+  } else if constexpr (WF != kWBf16) {
     if (cfg == kReg256) return run_bf16<256, 256, 2, 4, EPI, WF>(p, max_mtiles, s);
     return run_bf16<128, 128, 2, 2, EPI, WF>(p, max_mtiles, s);
   } else {
@@ -1268,16 +1322,17 @@ hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipS
   }
 }
 
-// Tile configuration of a bf16 call: register-staged tiles for few rows; for
-// many rows the LDS-DMA tiles, 256 rows when the groups average at least 384
+// Tile configuration of a bf16 or e4m3 call: register-staged tiles for few
+// rows; for many rows the LDS-DMA tiles, 256 rows when the groups average at least 384
 // rows, else 128 (less padding in each group's last tile). Measured: the
 // fine-grained layer (about 400 rows a group, two shared experts of 8192)
 // runs 4 % faster on 256-row tiles, the Switch layer (at most 320) 11 % slower.
 // Widths that the 256-column tiles do not fit take the 128 x 128 tiles.
+// Integer codes decoded in registers take the 256 x 256 register-staged tiles.
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
   if (rows < 2048 || !wide_tiles_fit(a.act, a.d, a.d_ff)) return kReg128;
-  if (a.w_dtype == 2 || (a.w_dtype == 3 && !a.wdq)) return kReg256;
+  if (a.w_dtype == 3 && !a.wdq) return kReg256;
   return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
@@ -1484,7 +1539,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
       pt.groups = pl.up_t;
       pt.tile_start = pl.tile_start_t;
       const int64_t mt = static_cast<int64_t>(kSmallGroupTiles) * G;  // row tiles of the second plan, at most
-      err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, mt, s) : run_dma<EPI_GELU, 128, 8>(pt, mt, s);
+      if (a.w_dtype == 2)
+        err = swi ? run_dma<EPI_SWIGLU, 128, 8, kWE4m3>(pt, mt, s) : run_dma<EPI_GELU, 128, 8, kWE4m3>(pt, mt, s);
+      else
+        err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, mt, s) : run_dma<EPI_GELU, 128, 8>(pt, mt, s);
     }
   }
   stage_mark(kStageFfnUp, true, s);
@@ -1525,7 +1583,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
       GemmParams pt = p;
       pt.groups = pl.down_t;
       pt.tile_start = pl.tile_start_t;
-      err = run_dma<EPI_PLAIN, 128, 8>(pt, static_cast<int64_t>(kSmallGroupTiles) * G, s);
+      const int64_t mt = static_cast<int64_t>(kSmallGroupTiles) * G;
+      err = a.w_dtype == 2 ? run_dma<EPI_PLAIN, 128, 8, kWE4m3>(pt, mt, s) : run_dma<EPI_PLAIN, 128, 8>(pt, mt, s);
     }
   }
   stage_mark(kStageFfnDown, true, s);

@@ -253,7 +253,7 @@ def test_ffn_path_of_each_workload():
         "mixtral-prefill-bf16": moe.PATH_DMA256,
         "fine-grained-160x6-shared2-bf16": moe.PATH_DMA256,
         "switch-top1-bf16": moe.PATH_DMA128,
-        "switch-top1-fp8w": moe.PATH_REG256,
+        "switch-top1-fp8w": moe.PATH_DMA128,
         "mixtral-prefill-int8x2-int4x6": moe.PATH_DMA256,
     }
     for name, path in expect.items():

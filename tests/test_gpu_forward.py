@@ -247,7 +247,7 @@ WS_CASES = {
     "prefill-dma128-drops": gen.SWITCH_TOP1.with_(T=2048, d=512, d_ff=1024),
     "prefill-dma256-split-tails": gen.MIXTRAL_PREFILL.with_(T=4096, d=1024, d_ff=1536),
     "prefill-reg128": gen.MIXTRAL_PREFILL.with_(T=512, d=1024, d_ff=1536),
-    "prefill-fp8-reg256": gen.SWITCH_TOP1_FP8.with_(T=4096, d=512, d_ff=1024),
+    "prefill-fp8-dma128": gen.SWITCH_TOP1_FP8.with_(T=4096, d=512, d_ff=1024),
     "tiny-fp32": gen.TINY_GELU,
     "expert-choice": gen.WORKLOADS["tiny-gelu-fp32-ec"],
 }

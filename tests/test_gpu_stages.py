@@ -196,6 +196,11 @@ FFN_CASES = [
     dict(T=1100, N=8, k=2, act=gen.SWIGLU, d=256, d_ff=4096),                 # 128 rows: (~768, none), (~24, 8)
     dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True),  # 128 rows: (~128, 2), (~32, 8)
     dict(T=1024, N=32, k=6, act=gen.SWIGLU, d=256, d_ff=256, n_shared=2, zipf=1.0),    # 128 rows: (~150, none), (~75, 2)
+    # e4m3 weights on the LDS-DMA tiles (bytes DMA'd, fragments converted on read)
+    dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True, wdt=gen.E4M3),  # 128 rows
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, wdt=gen.E4M3),             # 256 rows, split, tails
+    dict(T=3000, N=4, k=2, act=gen.SWIGLU, d=1024, d_ff=512, n_shared=1, pad=64, wdt=gen.E4M3),  # 256 rows, shared
+    dict(T=2048, N=12, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, zipf=1.0, wdt=gen.E4M3),  # small groups
 ]
 
 
