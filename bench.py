@@ -225,11 +225,16 @@ def run_gpu(wl, inp, steps, warmup):
             "rows": kept + shared_rows, "layer": layer, "tensors": tensors}
 
 
+DECODE_WEIGHT_COPIES = 4  # consecutive decode steps read different copies of the weights
+
+
 def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
     """Decode shapes on the prefill weights. Each timed step takes a different
-    slice of the prefill tokens, so consecutive steps touch different experts'
-    weights where routing allows; the bytes of each step are counted from its
-    own routing (read once before the timed loop)."""
+    slice of the prefill tokens and one of DECODE_WEIGHT_COPIES device copies of
+    the layer's weights, in turn, so no step can find the weights it streams in
+    the 256 MB last-level cache from the step before (each step reads at least
+    two experts, 704 MB); the bytes of each step are counted from its own
+    routing (read once before the timed loop)."""
     import numpy as np
     import torch
 
@@ -238,15 +243,17 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
     out = {}
     per_expert = [weight_bytes_per_expert(wl_prefill, e) for e in range(wl_prefill.n_experts)]
     x_all = to_dev(inp.x)
-    tensors = layer_weights(inp)
+    copies = [layer_weights(inp) for _ in range(DECODE_WEIGHT_COPIES)]
     for T in Ts:
         wl = wl_prefill.with_(T=T)
-        layer = moe.MoELayer(shape_for(wl), tensors)
+        layers = [moe.MoELayer(shape_for(wl), tensors) for tensors in copies]
         nslices = min(steps, wl_prefill.T // T)
         xs = [x_all[i * T:(i + 1) * T].contiguous() for i in range(nslices)]
+        lay = [layers[i % len(layers)] for i in range(nslices)]  # the copy step i reads
+        layer = layers[0]
         touched, wbytes = [], []
-        for xi in xs:
-            o = layer(xi)
+        for li, xi in zip(lay, xs):
+            o = li(xi)
             ex = set(o.topk_idx.cpu().numpy().ravel().tolist())
             touched.append(len(ex))
             wbytes.append(sum(per_expert[e] for e in ex))
@@ -264,17 +271,17 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
             return (time.perf_counter() - t0) * 1e6 / nslices
 
         # eager launches, stage timing off
-        us_eager = timed(lambda: [layer(xi) for xi in xs])
+        us_eager = timed(lambda: [li(xi) for li, xi in zip(lay, xs)])
         # each step replayed from a captured HIP graph: no host launch gaps
-        graphs = [layer.capture(xi) for xi in xs]
+        graphs = [li.capture(xi) for li, xi in zip(lay, xs)]
         for g in graphs[:warmup]:
             g.replay()
         us = timed(lambda: [g.replay() for g in graphs])
         del graphs
         # stage timing (hipEvents around the FFN launches) on a separate eager pass
         moe.timing_start(8 * nslices + 8)
-        for xi in xs:
-            layer(xi)
+        for li, xi in zip(lay, xs):
+            li(xi)
         torch.cuda.synchronize()
         st = moe.timing_stop()
         nbytes = sum(b + fixed for b in wbytes) / nslices
@@ -286,7 +293,7 @@ def run_decode(wl_prefill, inp, steps, warmup, Ts=(1, 16, 64)):
                         "ffn_us": round(ffn_us, 2),
                         "ffn_GB_per_s": round((nbytes - fixed) / ffn_us / 1e3, 1),
                         "ffn_hbm_frac": round((nbytes - fixed) / ffn_us / 1e3 / PEAK_HBM_GBS, 4),
-                        "steps": nslices}
+                        "steps": nslices, "weight_copies": len(layers)}
         log(f"decode T={T}: {out[f'T{T}']}")
     return out
 

@@ -99,7 +99,7 @@ RouteWs carve_route(Carver& c, const moe_shape& s) {
   w.part_P = c.take<float>(nb * s.n_experts);
   w.part_cnt = c.take<int32_t>(nb * s.n_experts);
   w.part_lse = c.take<float>(2 * nb);
-  w.part_logits = c.take<float>(static_cast<size_t>(moe::route_splits(s.T, s.d)) * s.T * s.n_experts);
+  w.part_logits = c.take<float>(static_cast<size_t>(moe::route_splits(s.T, s.d, s.n_experts)) * s.T * s.n_experts);
   w.logits_t = is_ec(s) ? c.take<float>(static_cast<size_t>(s.n_experts) * ec_ld(s)) : nullptr;
   return w;
 }

@@ -18,77 +18,91 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxK = 8;
 
-template <bool BF16>
+// TW tokens a workgroup (consecutive): every thread takes 16-byte chunks of
+// all TW tokens' rows and issues the loads of U chunks x TW tokens x (k routed
+// + shared) rows before the first sum, so the dependent chain (inv_map, row,
+// store) of one token overlaps the others'. A token has KS = k + shared slots,
+// at most 8 / TW (12 with TW = 1): the loads stay in registers.
+template <bool BF16, int TW>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  const int64_t t = blockIdx.x;
+  constexpr int KM = TW == 1 ? kMaxK + 4 : 8 / TW;  // slots a token may have
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TW;
   const int k = a.k;
-  int64_t row[kMaxK];
-  float g[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    row[j] = -1;
-    g[j] = 0.f;
-    if (j < k) {
-      row[j] = a.inv_map[t * k + j];
-      g[j] = a.topk_w[t * k + j];
-    }
-  }
-  constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
-  constexpr int U = 2;             // chunks per thread whose loads are in flight together
-  const int64_t nch = a.d / E;
   const int nsh = a.y_shared ? a.n_shared : 0;
+  // slot j < k: routed row (or -1, dropped) with its gate; j in [k, k + nsh): shared expert j - k
+  int64_t row[TW][KM];
+  float g[TW][KM];
+#pragma unroll
+  for (int w = 0; w < TW; ++w)
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      row[w][j] = -1;
+      g[w][j] = 1.f;
+      if (t0 + w < a.T) {
+        if (j < k) {
+          row[w][j] = a.inv_map[(t0 + w) * k + j];
+          g[w][j] = a.topk_w[(t0 + w) * k + j];
+        } else if (j < k + nsh) {
+          row[w][j] = (j - k) * a.T + t0 + w;  // row of y_shared
+        }
+      }
+    }
+  constexpr int E = BF16 ? 8 : 4;     // elements per 16-byte chunk
+  constexpr int U = TW == 1 ? 2 : 1;  // chunks per thread whose loads are in flight together
+  const int64_t nch = a.d / E;
   for (int64_t c0 = threadIdx.x; c0 < nch; c0 += U * kThreads) {
-    // every load of the U chunks (k routed rows, then the shared rows) first
-    uint4 v[U][kMaxK + 4];
+    uint4 v[U][TW][KM];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * kThreads;
       if (c >= nch) break;
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j)
-        if (j < k && row[j] >= 0) v[u][j] = reinterpret_cast<const uint4*>(a.y_perm)[row[j] * nch + c];
+      for (int w = 0; w < TW; ++w)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < nsh) v[u][kMaxK + s] = reinterpret_cast<const uint4*>(a.y_shared)[(s * a.T + t) * nch + c];
+        for (int j = 0; j < KM; ++j)
+          if (row[w][j] >= 0)
+            v[u][w][j] = reinterpret_cast<const uint4*>(j < k ? a.y_perm : a.y_shared)[row[w][j] * nch + c];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * kThreads;
       if (c >= nch) break;
-      float acc[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.f;
-      auto add = [&](const uint4& x, float w) {
-        if constexpr (BF16) {
-          const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+      for (int w = 0; w < TW; ++w) {
+        if (t0 + w >= a.T) break;
+        float acc[E];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xFFFFu)), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)), acc[2 * e + 1]);
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
+        // fixed order: routed slots ascending, then the shared experts
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (row[w][j] < 0) continue;
+          const uint4 x = v[u][w][j];
+          const float wt = g[w][j];
+          if constexpr (BF16) {
+            const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] = fmaf(wt, bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xFFFFu)), acc[2 * e]);
+              acc[2 * e + 1] = fmaf(wt, bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)), acc[2 * e + 1]);
+            }
+          } else {
+            acc[0] = fmaf(wt, __uint_as_float(x.x), acc[0]);
+            acc[1] = fmaf(wt, __uint_as_float(x.y), acc[1]);
+            acc[2] = fmaf(wt, __uint_as_float(x.z), acc[2]);
+            acc[3] = fmaf(wt, __uint_as_float(x.w), acc[3]);
           }
-        } else {
-          acc[0] = fmaf(w, __uint_as_float(x.x), acc[0]);
-          acc[1] = fmaf(w, __uint_as_float(x.y), acc[1]);
-          acc[2] = fmaf(w, __uint_as_float(x.z), acc[2]);
-          acc[3] = fmaf(w, __uint_as_float(x.w), acc[3]);
         }
-      };
-      // fixed order: routed slots ascending, then the shared experts
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j)
-        if (j < k && row[j] >= 0) add(v[u][j], g[j]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < nsh) add(v[u][kMaxK + s], 1.0f);
-      uint4 o;
-      if constexpr (BF16) {
-        o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                       pack_bf16x2(acc[6], acc[7]));
-      } else {
-        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                       __float_as_uint(acc[3]));
+        uint4 o;
+        if constexpr (BF16) {
+          o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7]));
+        } else {
+          o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                         __float_as_uint(acc[3]));
+        }
+        reinterpret_cast<uint4*>(a.y)[(t0 + w) * nch + c] = o;
       }
-      reinterpret_cast<uint4*>(a.y)[t * nch + c] = o;
     }
   }
 }
@@ -205,10 +219,23 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(combine_ec_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL(combine_ec_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
-  } else if (a.act_dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(a.T)), dim3(kThreads), 0, s, a);
+  } else {
+    // tokens a workgroup: as many as keep TW (k + shared) <= 8 loads in flight
+    const int slots = a.k + (a.y_shared ? a.n_shared : 0);
+    const int tw = slots <= 1 ? 8 : (slots <= 2 ? 4 : (slots <= 4 ? 2 : 1));
+    const dim3 grid(static_cast<unsigned>(ceil_div(a.T, tw)));
+    if (a.act_dtype == 1) {
+      if (tw == 8) hipLaunchKernelGGL((combine_kernel<true, 8>), grid, dim3(kThreads), 0, s, a);
+      else if (tw == 4) hipLaunchKernelGGL((combine_kernel<true, 4>), grid, dim3(kThreads), 0, s, a);
+      else if (tw == 2) hipLaunchKernelGGL((combine_kernel<true, 2>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<true, 1>), grid, dim3(kThreads), 0, s, a);
+    } else {
+      if (tw == 8) hipLaunchKernelGGL((combine_kernel<false, 8>), grid, dim3(kThreads), 0, s, a);
+      else if (tw == 4) hipLaunchKernelGGL((combine_kernel<false, 4>), grid, dim3(kThreads), 0, s, a);
+      else if (tw == 2) hipLaunchKernelGGL((combine_kernel<false, 2>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<false, 1>), grid, dim3(kThreads), 0, s, a);
+    }
+  }
   stage_mark(kStageCombine, true, s);
   return hipGetLastError();
 }

@@ -42,7 +42,8 @@ struct RouteArgs {
 constexpr int kRouteTokens = 64;  // tokens per route workgroup
 constexpr int64_t kEcMaxTokens = 32768;  // expert choice: a column is held by one workgroup's registers
 constexpr int kMaxRouteSplits = 16;  // k splits of the router GEMM (partial logit planes)
-int route_splits(int64_t T, int64_t d);  // k splits of the router GEMM
+int route_splits(int64_t T, int64_t d, int32_t N);  // k splits of the router GEMM
+int router_kstep(int64_t T, int64_t d, int32_t N);  // its k-step (64, 128 or 256)
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- FFN groups

@@ -24,8 +24,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRK = 64;            // k-step of the router GEMM
-constexpr int kWStride = kRK + 8;  // padded LDS row (bf16 elements): 144 B spreads the banks
 constexpr int kMaxN = 256;
 
 struct Sel {
@@ -42,10 +40,16 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
 // all experts. Grid (token blocks, k splits). bf16 runs on MFMA with the
 // router-weight tile for all experts in LDS (double buffered); the next
 // k-step's tile and token fragments are loaded while the current one computes.
-template <int NT>
+// KR is the k-step: 64 for decode-sized calls (many k splits, little data a
+// step), 128 or 256 for prefill, where each workgroup walks a long k range and
+// wider steps keep more bytes in flight between its barriers.
+template <int NT, int KR>
 __global__ __launch_bounds__(kThreads) void router_gemm_kernel(RouteArgs a, float* part, int k_len) {
-  __shared__ __attribute__((aligned(16))) uint16_t wtile[2][NT * 16 * kWStride];
-  constexpr int WCH = (NT * 16 * (kRK / 8) + kThreads - 1) / kThreads;  // 16-byte weight chunks per thread
+  constexpr int WS = KR + 8;                     // padded LDS row (bf16 elements)
+  constexpr int KC = KR / 8;                     // 16-byte chunks of a weight row per step
+  constexpr int XL = KR / 32;                    // 16-byte token chunks per lane and step
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[2][NT * 16 * WS];
+  constexpr int WCH = (NT * 16 * KC + kThreads - 1) / kThreads;  // 16-byte weight chunks per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   const int N = a.N;
@@ -59,52 +63,53 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(RouteArgs a, floa
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   if (a.act_dtype == 1) {
-    // Lane (row c16, k-group q) takes 16 consecutive k of its token row per step.
+    // Lane (row c16, k-group q) takes KR/4 consecutive k of its token row per
+    // step, as XL chunks of 8 (the same k order for the weight fragments).
     const uint16_t* xr = static_cast<const uint16_t*>(a.x);
     const uint16_t* wr = static_cast<const uint16_t*>(a.w_router);
     int64_t trow = t0 + c16;
     if (trow > T - 1) trow = T - 1;  // rows past T compute garbage that is never stored
-    const uint16_t* xrow = xr + trow * d + k0 + q * 16;
-    const int nsteps = k_len / kRK;
+    const uint16_t* xrow = xr + trow * d + k0 + q * (KR / 4);
+    const int nsteps = k_len / KR;
     uint4 wv[WCH];
     auto wload = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < WCH; ++i) {
         const int c = tid + i * kThreads;
-        const int e = c >> 3, kc = c & 7;
+        const int e = c / KC, kc = c % KC;
         wv[i] = make_uint4(0, 0, 0, 0);
-        if (c < NT * 16 * 8 && e < N) wv[i] = *reinterpret_cast<const uint4*>(wr + e * d + k0 + step * kRK + kc * 8);
+        if (c < NT * 16 * KC && e < N) wv[i] = *reinterpret_cast<const uint4*>(wr + e * d + k0 + step * KR + kc * 8);
       }
     };
     auto wstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < WCH; ++i) {
         const int c = tid + i * kThreads;
-        const int e = c >> 3, kc = c & 7;
-        if (c < NT * 16 * 8) *reinterpret_cast<uint4*>(&wtile[buf][e * kWStride + kc * 8]) = wv[i];
+        const int e = c / KC, kc = c % KC;
+        if (c < NT * 16 * KC) *reinterpret_cast<uint4*>(&wtile[buf][e * WS + kc * 8]) = wv[i];
       }
     };
+    uint4 xc[XL], xn[XL];
     wload(0);
-    uint4 x0 = *reinterpret_cast<const uint4*>(xrow);
-    uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 8);
+#pragma unroll
+    for (int m = 0; m < XL; ++m) xc[m] = *reinterpret_cast<const uint4*>(xrow + m * 8);
     wstore(0);
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
       const int nx = (st + 1 < nsteps) ? st + 1 : st;  // the last step re-reads itself into the idle buffer
       wload(nx);
-      const uint4 y0 = *reinterpret_cast<const uint4*>(xrow + nx * kRK);
-      const uint4 y1 = *reinterpret_cast<const uint4*>(xrow + nx * kRK + 8);
+#pragma unroll
+      for (int m = 0; m < XL; ++m) xn[m] = *reinterpret_cast<const uint4*>(xrow + nx * KR + m * 8);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const uint16_t* wp = &wtile[st & 1][(16 * nt + c16) * kWStride + q * 16];
-        const uint4 b0 = *reinterpret_cast<const uint4*>(wp);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(wp + 8);
-        acc[nt] = mfma16x16x32(x0, b0, acc[nt]);
-        acc[nt] = mfma16x16x32(x1, b1, acc[nt]);
+        const uint16_t* wp = &wtile[st & 1][(16 * nt + c16) * WS + q * (KR / 4)];
+#pragma unroll
+        for (int m = 0; m < XL; ++m)
+          acc[nt] = mfma16x16x32(xc[m], *reinterpret_cast<const uint4*>(wp + m * 8), acc[nt]);
       }
       wstore((st + 1) & 1);
-      x0 = y0;
-      x1 = y1;
+#pragma unroll
+      for (int m = 0; m < XL; ++m) xc[m] = xn[m];
       __syncthreads();
     }
   } else {
@@ -696,8 +701,16 @@ hipError_t launch_ec_select(const RouteArgs& a, hipStream_t s) {
 template <int NT>
 hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
   if (!a.logits_given) {
-    hipLaunchKernelGGL(router_gemm_kernel<NT>, dim3(nb, splits), dim3(kThreads), 0, s, a, a.part_logits,
-                       static_cast<int>(a.d / splits));
+    const int kr = router_kstep(a.T, a.d, a.N);
+    const dim3 grid(nb, splits);
+    const int k_len = static_cast<int>(a.d / splits);
+    if constexpr (NT <= 4) {  // the 256-wide weight tile fits LDS for at most 64 experts
+      if (kr == 256) hipLaunchKernelGGL((router_gemm_kernel<NT, 256>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+    }
+    if (kr == 256) {
+      if constexpr (NT > 4) return hipErrorInvalidValue;
+    } else if (kr == 128) hipLaunchKernelGGL((router_gemm_kernel<NT, 128>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+    else hipLaunchKernelGGL((router_gemm_kernel<NT, 64>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -710,8 +723,14 @@ hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
 
 }  // namespace
 
-int route_splits(int64_t T, int64_t d) {
-  const int64_t nb = ceil_div(T, kRouteTokens), steps = d / kRK;
+int router_kstep(int64_t T, int64_t d, int32_t N) {
+  if (T < 1024) return 64;
+  if (N <= 64 && d % 256 == 0) return 256;
+  return 128;
+}
+
+int route_splits(int64_t T, int64_t d, int32_t N) {
+  const int64_t nb = ceil_div(T, kRouteTokens), steps = d / router_kstep(T, d, N);
   int s = 1;
   while (nb * s < 256 && s < kMaxRouteSplits && steps % (2 * s) == 0 && steps / (2 * s) >= 4) s *= 2;
   return s;
@@ -721,7 +740,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const int nb = static_cast<int>(ceil_div(a.T, kRouteTokens));
   const int nt = static_cast<int>(ceil_div(a.N, 16));
-  const int splits = a.logits_given ? 1 : route_splits(a.T, a.d);
+  const int splits = a.logits_given ? 1 : route_splits(a.T, a.d, a.N);
   hipError_t err;
   stage_mark(kStageRoute, false, s);
   switch (nt) {
