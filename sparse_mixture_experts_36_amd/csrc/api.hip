@@ -699,8 +699,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   if (!perm_token) perm_token = w.perm_token;
 
   const bool gather = fwd_gathers(s);  // then the permutation copies no rows
-  hipError_t e = moe::launch_route(
-      route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw), stream);
+  const moe::RouteArgs ra =
+      route_args(s, x, weights->w_router, weights->b_router, logits, false, topk_idx, topk_w, stats, rw);
   moe::FfnArgs fa = ffn_args(s, w.x_perm, ld_xp, expert_offsets, x, weights, w.y_perm, w.y_shared, fw);
   moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
                                   ld_xp, stats, pw);
@@ -711,7 +711,13 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
     pa.plan = moe::ffn_plan(fa);
     fa.planned = true;
   }
-  if (e == hipSuccess) e = moe::launch_permute(pa, stream);
+  hipError_t e = hipSuccess;
+  if (moe::front_fits(ra, pa)) {  // decode sizes: router GEMM, routing and permutation in one launch
+    e = moe::launch_front(ra, pa, stream);
+  } else {
+    e = moe::launch_route(ra, stream);
+    if (e == hipSuccess) e = moe::launch_permute(pa, stream);
+  }
   if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);
   if (e == hipSuccess) {
     moe::CombineArgs a{};

@@ -1,0 +1,121 @@
+// Decode front end in one workgroup: the router GEMM, the routing (softmax,
+// top-k, gates, statistics) and the permutation (rank, scan, slots and the
+// FFN group plan) of a call with at most 16 tokens and 64 experts, in one
+// launch where the general path takes three (router GEMM, routing,
+// permutation), each with its own launch latency and global round trip.
+//
+// Pages: aigrafen.se "Mixture of Experts" (g = softmax(W_r x), the capacity
+// equation and the `MoE` module's `nonzero`-order dispatch); vanos001 "MoE
+// Architecture" / "Router Design" and "Capacity and Token Dropping";
+// learn.starphix.com "Mixture of Experts (MoE)" / "Load Balancing (Critical)".
+#include "common.h"
+#include "kernels.h"
+#include "perm_block.h"
+#include "route_block.h"
+
+namespace moe {
+namespace {
+
+constexpr int kFrontTokens = 16;  // tokens the front end takes (one MFMA row block)
+constexpr int kFrontMaxNT = 4;    // 16-expert column blocks (64 experts)
+constexpr int kFrontWaves = kRouteThreads / 64;
+static_assert(kFrontWaves == 16, "the k range is cut in 16 wave slices");
+
+// Router GEMM: wave w takes k [w d/16, (w + 1) d/16) of every token and
+// expert as MFMA 16x16x32 products (tokens as rows, clamped to T - 1; experts
+// 16 nt + c16 as columns), with SB k-steps of loads in flight; the 16 wave
+// partials are then summed in wave order (fixed, so the logits are
+// reproducible bit for bit). Then the routing of the 16-token block and the
+// one-block permutation, as in the general kernels.
+template <int NT>
+__global__ __launch_bounds__(kRouteThreads) void front_kernel(RouteArgs ra, PermuteArgs pa) {
+  __shared__ floatx4_t s_part[kFrontWaves][NT][64];
+  __shared__ float s_logit[kFrontTokens][NT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int N = ra.N;
+  const int64_t T = ra.T, d = ra.d;
+
+  const int64_t kw = d / kFrontWaves;  // a multiple of 32
+  const int64_t kb = wave * kw;
+  const int64_t trow = c16 < T ? c16 : T - 1;
+  const uint16_t* xr = static_cast<const uint16_t*>(ra.x) + trow * d + kb + q * 8;
+  const uint16_t* wr = static_cast<const uint16_t*>(ra.w_router) + kb + q * 8;
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int steps = static_cast<int>(kw / 32);
+  constexpr int SB = NT == 1 ? 8 : NT == 2 ? 6 : 4;  // (NT + 1) SB 16-byte loads a lane in flight
+  for (int s0 = 0; s0 < steps; s0 += SB) {
+    uint4 xa[SB], wb[SB][NT];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      if (s0 + u >= steps) break;
+      xa[u] = *reinterpret_cast<const uint4*>(xr + (s0 + u) * 32);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = 16 * nt + c16;
+        wb[u][nt] = e < N ? *reinterpret_cast<const uint4*>(wr + static_cast<int64_t>(e) * d + (s0 + u) * 32)
+                          : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      if (s0 + u >= steps) break;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(xa[u], wb[u][nt], acc[nt]);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) s_part[wave][nt][lane] = acc[nt];
+  __syncthreads();
+  // lane l of a fragment holds tokens 4 (l / 16) + i, i < 4, of expert column l % 16
+  if (tid < kFrontTokens * NT * 16) {
+    const int t = tid / (NT * 16), e = tid % (NT * 16);
+    const int nt = e / 16, l = 16 * (t / 4) + (e % 16), i = t % 4;
+    float v = s_part[0][nt][l][i];
+#pragma unroll
+    for (int w = 1; w < kFrontWaves; ++w) v += s_part[w][nt][l][i];
+    if (e < N) {
+      if (ra.b_router) v += ra.b_router[e];
+      if (t < T) ra.logits[static_cast<int64_t>(t) * N + e] = v;
+    }
+    s_logit[t][e] = v;
+  }
+  __syncthreads();
+
+  // routing: token 4 w + q in the lanes of quarter q of wave w (waves 0..3)
+  const int64_t t = wave * 4 + q;
+  const bool live = t < T;
+  float lg[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) lg[nt] = live ? s_logit[t][16 * nt + c16] : 0.f;
+  __shared__ int32_t s_topk[kFrontTokens * kPermMaxK];
+  route_block<NT>(ra, t, live, lg, 0, true, s_topk);
+  __syncthreads();  // this block's top-k lists are in LDS
+
+  perm_rank_block<kRouteThreads>(pa, 0, 1, s_topk);
+}
+
+}  // namespace
+
+bool front_fits(const RouteArgs& ra, const PermuteArgs& pa) {
+  return ra.act_dtype == 1 && !ra.ec && !ra.logits_given && ra.T >= 1 && ra.T <= kFrontTokens && ra.N >= 1 &&
+         ra.N <= 16 * kFrontMaxNT && ra.k >= 1 && ra.k <= kPermMaxK && ra.d % (32 * kFrontWaves) == 0 &&
+         pa.x_perm == nullptr;
+}
+
+hipError_t launch_front(const RouteArgs& ra, const PermuteArgs& pa, hipStream_t s) {
+  stage_mark(kStageRoute, false, s);
+  switch ((ra.N + 15) / 16) {
+    case 1: hipLaunchKernelGGL(front_kernel<1>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;
+    case 2: hipLaunchKernelGGL(front_kernel<2>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;
+    case 3: hipLaunchKernelGGL(front_kernel<3>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;
+    case 4: hipLaunchKernelGGL(front_kernel<4>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;
+    default: return hipErrorInvalidValue;
+  }
+  stage_mark(kStageRoute, true, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -99,6 +99,11 @@ struct PermuteArgs {
 };
 constexpr int kPermTokens = 256;  // tokens per permute workgroup
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Decode front end: router GEMM, routing and the one-block permutation in one
+// workgroup, for bf16 token-choice calls of at most 16 tokens and 64 experts
+// whose FFN reads routed rows from x (front_fits).
+bool front_fits(const RouteArgs& ra, const PermuteArgs& pa);
+hipError_t launch_front(const RouteArgs& ra, const PermuteArgs& pa, hipStream_t s);
 
 // ---------------------------------------------------------------- grouped FFN
 

@@ -19,6 +19,7 @@
 // writes inv_map / perm_token itself: one launch instead of three.
 #include "common.h"
 #include "kernels.h"
+#include "perm_block.h"
 #include "plan.h"
 
 namespace moe {
@@ -29,144 +30,7 @@ constexpr int kMaxN = 256;
 constexpr int kMaxK = 8;
 
 __global__ __launch_bounds__(kThreads) void perm_rank_kernel(PermuteArgs a) {
-  __shared__ int32_t s_wcnt[4][kMaxN];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.N, k = a.k;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermTokens + wave * 64 + lane;
-  const bool live = t < a.T;
-
-  for (int i = tid; i < 4 * kMaxN; i += kThreads) (&s_wcnt[0][0])[i] = 0;
-
-  int ex[kMaxK], rank[kMaxK];
-  uint64_t rem[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    ex[j] = -1;
-    rank[j] = 0;
-    if (j < k && live) {
-      const int e = a.topk_idx[t * k + j];
-      ex[j] = (e >= 0 && e < N) ? e : -1;  // out-of-range ids are treated as dropped
-    }
-    rem[j] = (j < k) ? __ballot(ex[j] >= 0) : 0ull;
-  }
-  __syncthreads();
-
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (;;) {
-    int j0 = -1;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j0 < 0 && rem[j] != 0ull) j0 = j;
-    if (j0 < 0) break;
-    uint64_t r0 = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j == j0) r0 = rem[j];
-    const int src = __builtin_ctzll(r0);
-    int v = -1;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j == j0) v = __shfl(ex[j], src);
-    uint64_t m = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      const uint64_t bj = __ballot(ex[j] == v) & rem[j];
-      m |= bj;
-      rem[j] &= ~bj;
-    }
-    const int pos = __popcll(m & below);
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (ex[j] == v) rank[j] = pos;
-    if (lane == 0) s_wcnt[wave][v] = __popcll(m);
-  }
-  __syncthreads();
-
-  if (live) {
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k) break;
-      int r = -1;
-      if (ex[j] >= 0) {
-        r = rank[j];
-        for (int w = 0; w < wave; ++w) r += s_wcnt[w][ex[j]];
-      }
-      a.local_rank[t * k + j] = r;  // -1: out-of-range expert id
-    }
-  }
-  const int64_t b = blockIdx.x;
-  if (gridDim.x > 1) {
-    for (int e = tid; e < N; e += kThreads)
-      a.block_cnt[b * N + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
-    return;
-  }
-
-  // One block holds every token (T <= kPermTokens): the scan is this block's
-  // counts, block base 0. Wave 0 scans the kept counts: lane L owns experts
-  // [4L, 4L + 4), then an inclusive wave scan over the lanes (integer, exact).
-  __shared__ int32_t s_off[kMaxN + 1];
-  if (wave == 0) {
-    int32_t kept4[4], sum = 0, drop = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i;
-      int32_t cnt = 0, kept = 0;
-      if (e < N) {
-        cnt = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
-        kept = (a.capacity >= 0 && cnt > a.capacity) ? static_cast<int32_t>(a.capacity) : cnt;
-        a.block_base[e] = 0;
-        a.kept[e] = kept;
-      }
-      kept4[i] = kept;
-      sum += kept;
-      drop += cnt - kept;
-    }
-    int32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    int32_t off = incl - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i;
-      if (e < N) {
-        s_off[e] = off;
-        a.offsets[e] = off;
-      }
-      off += kept4[i];
-    }
-    const int32_t total = __shfl(incl, 63);
-    if (lane == 0) {
-      s_off[N] = total;
-      a.offsets[N] = total;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
-    if (lane == 0) *a.n_dropped = drop;
-  }
-  // with no rows to copy, the slots (and, when asked, the FFN's group plan)
-  // are written here and no scatter pass runs
-  if (a.x_perm) return;
-  __syncthreads();
-  if (a.plan.up) {
-    __shared__ int32_t s_mt[2 * kMaxGroups];
-    plan_groups(s_off, a.plan, s_mt, tid, kThreads);
-  }
-  if (!live) return;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j >= k) break;
-    int32_t row = -1;
-    if (ex[j] >= 0) {
-      int r = rank[j];
-      for (int w = 0; w < wave; ++w) r += s_wcnt[w][ex[j]];
-      if (a.capacity < 0 || r < a.capacity) row = s_off[ex[j]] + r;
-    }
-    a.inv_map[t * k + j] = row;
-    if (row >= 0) a.perm_token[row] = static_cast<int32_t>(t);
-  }
+  perm_rank_block<kThreads>(a, blockIdx.x, gridDim.x);
 }
 
 // One workgroup of 1024 threads: per expert, the exclusive scan of the block

@@ -145,6 +145,12 @@ REDUCED = {
     "fine-grained-like-decode": gen.FINE_GRAINED.with_(T=24, d=512, d_ff=256),
     "fine-grained-like-decode-T2": gen.FINE_GRAINED.with_(T=2, d=512, d_ff=1024),  # GEMV: two rows, shared experts
     "switch-like-decode-fp8": gen.SWITCH_TOP1_FP8.with_(T=128, d=512, d_ff=1024),
+    # at most 16 tokens and 64 experts: router GEMM, routing and permutation in
+    # one workgroup (capacity drops, router bias, a shared expert, 3 column blocks)
+    "front-end-T16-N48-k4-cf2-shared": gen.FINE_GRAINED.with_(T=16, d=512, d_ff=256, n_experts=48, top_k=4,
+                                                              capacity_factor=2.0, n_shared=1),
+    "front-end-T5-N64-renorm": gen.MIXTRAL_PREFILL.with_(T=5, d=1024, d_ff=512, n_experts=64, top_k=3,
+                                                         gating=gen.SOFTMAX_TOPK_RENORM),
 }
 
 
