@@ -195,10 +195,9 @@ typedef enum {
   MOE_PATH_F32 = 0,     /* fp32 layers: FMA tiles */
   MOE_PATH_STREAM = 1,  /* few rows (decode): weights streamed once, GEMV for T <= 2 */
   MOE_PATH_REG128 = 2,  /* register-staged 128 x 128 MFMA tiles */
-  MOE_PATH_REG256 = 3,  /* register-staged 256 x 256 MFMA tiles (weights decoded in registers) */
-  MOE_PATH_DMA256 = 4,  /* LDS-DMA 256-row tiles, short group tails on 128-row tiles */
-  MOE_PATH_DMA128 = 5,  /* LDS-DMA 128-row tiles */
-  MOE_PATH_BGEMM = 6    /* moe_backward only: forward recompute on the backward GEMM */
+  MOE_PATH_DMA256 = 3,  /* LDS-DMA 256-row tiles, small groups and short group tails on 128-row tiles */
+  MOE_PATH_DMA128 = 4,  /* LDS-DMA 128-row tiles */
+  MOE_PATH_BGEMM = 5    /* moe_backward only: forward recompute on the backward GEMM */
 } moe_path;
 
 /* moe_route flag: take the fp32 logits from `logits` instead of computing the

@@ -149,7 +149,7 @@ def workspace_size(shape: Shape, entry: int = ENTRY_FORWARD) -> int:
     return n.value
 
 
-PATH_F32, PATH_STREAM, PATH_REG128, PATH_REG256, PATH_DMA256, PATH_DMA128, PATH_BGEMM = range(7)
+PATH_F32, PATH_STREAM, PATH_REG128, PATH_DMA256, PATH_DMA128, PATH_BGEMM = range(6)
 
 
 def ffn_path(shape: Shape, entry: int = ENTRY_FORWARD) -> int:

@@ -125,10 +125,10 @@ struct FfnWs {
   int32_t* tile_start;
   moe::GroupDesc* groups_t;
   int32_t* tile_start_t;
+  int32_t* tile_start_c;
   int32_t* active;
   float* part;
   float* split_part;
-  void* wdq;
 };
 // Workspace of one grouped-FFN launch set over n_routed routed experts (cap
 // rows) and n_shared shared experts (T rows each).
@@ -141,16 +141,14 @@ FfnWs carve_ffn_for(Carver& c, const moe_shape& s, int32_t n_routed, int32_t n_s
   w.tile_start = c.take<int32_t>(G + 1);
   w.groups_t = c.take<moe::GroupDesc>(2 * G);
   w.tile_start_t = c.take<int32_t>(G + 1);
+  w.tile_start_c = s.w_dtype == MOE_INT_W ? c.take<int32_t>(4 * (G + 1)) : nullptr;
   w.active = c.take<int32_t>(G + 1);
   w.part = nullptr;
   if (moe::use_skinny(s.act_dtype, cap, n_shared, s.T))
     w.part = c.take<float>(moe::skinny_part_floats(s.T, s.d, s.d_ff, n_routed, n_shared, s.act, cap, s.w_dtype));
   w.split_part = nullptr;
-  if (moe::uses_prefill_gemm(s.act_dtype, s.w_dtype, cap, n_shared, s.T))
+  if (moe::uses_prefill_gemm(s.act_dtype, cap, n_shared, s.T))
     w.split_part = c.take<float>(static_cast<size_t>(moe::kSplitPartFloats));
-  w.wdq = nullptr;
-  if (moe::uses_int_dequant(s.act_dtype, s.w_dtype, cap, n_shared, s.T))
-    w.wdq = c.take<char>(moe::dq_bytes(s.d, s.d_ff, n_routed, n_shared, s.act));
   return w;
 }
 
@@ -429,12 +427,12 @@ moe::FfnArgs ffn_args(const moe_shape& s, const void* x_perm, int64_t ld_x_perm,
   a.tile_start = fw.tile_start;
   a.groups_t = fw.groups_t;
   a.tile_start_t = fw.tile_start_t;
+  a.tile_start_c = fw.tile_start_c;
   a.active = fw.active;
   a.part = fw.part;
   a.split_part = fw.split_part;
   a.w_bits = w->w_bits;
   a.sw_bits = w->sw_bits;
-  a.wdq = fw.wdq;
   return a;
 }
 
@@ -596,9 +594,6 @@ int32_t moe_ffn_path(const moe_shape* shape, int32_t entry) {
   a.act_dtype = s.act_dtype;
   a.w_dtype = s.w_dtype;
   a.routed_row_cap = routed_row_cap(s);
-  // the integer-weight prefill tiles need the bf16 copy the workspace then holds
-  static char dq_marker;
-  a.wdq = moe::uses_int_dequant(s.act_dtype, s.w_dtype, a.routed_row_cap, s.n_shared, s.T) ? &dq_marker : nullptr;
   return moe::ffn_path_of(a);
 }
 

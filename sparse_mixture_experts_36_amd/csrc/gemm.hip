@@ -535,12 +535,38 @@ __device__ __forceinline__ float* dma_part_frag(float* part, int unit, int wave,
   return part + static_cast<int64_t>(unit) * (BM * BNB) + ((wave * C_::FM + i) * C_::FN + j) * 256;
 }
 
-// WF = kWE4m3: the weight rows arrive as e4m3 bytes (64-byte stage rows, half
-// the bytes); a wave reads each weight fragment as 8 bytes and converts it
-// exactly to bf16 (hardware fp8 conversion) before its MFMAs, and the epilogue
-// applies the per-matrix scale. Those rows keep chunk c of row r at position
-// c ^ ((r >> 2) & 3), at which the 8-byte fragment reads of 16 rows are
-// conflict-free; one DMA instruction fills 16 of them.
+// A weight fragment's 8 codes as read from LDS: 8 bytes (e4m3, int8) or one
+// 32-bit word (int4), and their exact bf16 values.
+template <int WF>
+struct CodeFrag {
+  typedef uint2 type;
+};
+template <>
+struct CodeFrag<kWInt4> {
+  typedef uint32_t type;
+};
+template <int WF>
+__device__ __forceinline__ uint4 frag_to_bf16(uint2 c) {
+  const uint2 lo = WF == kWE4m3 ? e4m3x4_to_bf16x4(c.x) : int8x4_to_bf16x4(c.x);
+  const uint2 hi = WF == kWE4m3 ? e4m3x4_to_bf16x4(c.y) : int8x4_to_bf16x4(c.y);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+template <int WF>
+__device__ __forceinline__ uint4 frag_to_bf16(uint32_t c) {
+  return int4x8_to_bf16x8(c);
+}
+
+// Weight codes (WF other than kWBf16) arrive in LDS as stored and are turned
+// into bf16 fragments exactly, after a wave's reads land and before its MFMAs:
+// - kWE4m3 and kWInt8: one byte a weight, 64-byte stage rows. A fragment is 8
+//   bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3), where the
+//   8-byte reads of 16 rows are conflict-free, and one DMA instruction fills
+//   16 rows. e4m3 decodes in hardware; the epilogue applies the per-matrix
+//   scales.
+// - kWInt4: half a byte a weight, 32-byte stage rows. A fragment is one
+//   32-bit word of 8 codes; chunk c of row r sits at c ^ ((r >> 3) & 1), and
+//   one DMA instruction fills 32 rows.
+// Integer codes take the row scales in the epilogue, one per output column.
 template <int EPI, int BM, int W, int WF>
 __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   using namespace dma;
@@ -548,12 +574,15 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int BNO = bno(EPI);
   constexpr int FM = C_::FM, FN = C_::FN, WTM = C_::WTM, WTB = C_::WTB, WGN = C_::WGN;
-  constexpr bool F8 = (WF == kWE4m3);
-  static_assert(WF == kWBf16 || F8, "bf16 or e4m3 weights");
-  constexpr int RBB = F8 ? RB / 2 : RB;     // weight row bytes in a stage
-  constexpr int SBY = BM * RB + BNB * RBB;  // one stage buffer
-  constexpr int ADMA = C_::ADMA, BDMA = F8 ? C_::BROWS / 16 : C_::BDMA, NDMA = ADMA + BDMA;
-  constexpr int NSTAGE = F8 ? 3 : C_::NSTAGE;
+  constexpr bool F8 = (WF == kWE4m3 || WF == kWInt8);  // byte codes
+  constexpr bool I4 = (WF == kWInt4);
+  constexpr bool CODES = F8 || I4;
+  static_assert(!I4 || C_::BROWS % 32 == 0, "int4 rows go 32 to a DMA instruction");
+  constexpr int RBB = F8 ? RB / 2 : (I4 ? RB / 4 : RB);  // weight row bytes in a stage
+  constexpr int SBY = BM * RB + BNB * RBB;                // one stage buffer
+  constexpr int ADMA = C_::ADMA, BDMA = F8 ? C_::BROWS / 16 : (I4 ? C_::BROWS / 32 : C_::BDMA), NDMA = ADMA + BDMA;
+  constexpr int NSTAGE = CODES ? 3 : C_::NSTAGE;
+  typedef typename CodeFrag<WF>::type BQT;
   __shared__ __attribute__((aligned(16))) char S0[SBY];
   __shared__ __attribute__((aligned(16))) char S1[SBY];
   __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? SBY : 16];
@@ -579,6 +608,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
       ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
     }
   }
+  if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
   // stage j of the loops below loads k-column ks_begin + j; all tiles walk k
   // in the same order, so tiles that share a weight tile or A rows read the
   // same lines at about the same time and L2 keeps them
@@ -603,7 +633,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   const bool w3 = SWI && wr0 >= BNO;
   const char* Bw = static_cast<const char*>(w3 ? (shared ? p.B3_s : p.B3_r) : (shared ? p.B_s : p.B_r)) +
                    (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0 + (w3 ? wr0 - BNO : wr0)) * p.ldb) *
-                       (F8 ? 1 : 2);
+                       (CODES ? 1 : 2);  // code pitches are in bytes
   // Lane L of an instruction over rows [r0, r0 + 8) fills row r0 + L/8,
   // position L%8 with logical chunk (L%8) ^ (row & 7); byte offsets are
   // relative to the tile's first A row and the wave's first weight row.
@@ -622,6 +652,10 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
       const int r = wr0 + i * 16 + (lane >> 2);
       const int chunk = (lane & 3) ^ ((r >> 2) & 3);
       offb[i] = static_cast<uint32_t>((i * 16 + (lane >> 2)) * static_cast<int>(p.ldb) + chunk * 16);
+    } else if constexpr (I4) {  // 32 rows of 32 bytes an instruction: lane L fills row r0 + L/2, position L%2
+      const int r = wr0 + i * 32 + (lane >> 1);
+      const int chunk = (lane & 1) ^ ((r >> 3) & 1);
+      offb[i] = static_cast<uint32_t>((i * 32 + (lane >> 1)) * static_cast<int>(p.ldb) + chunk * 16);
     } else {
       const int r = wr0 + i * 8 + (lane >> 3);
       const int chunk = (lane & 7) ^ (r & 7);
@@ -651,11 +685,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   // u * 4 + q of row c16 (mod 8) sits at position (u * 4 + q) ^ (c16 & 7)
   const int rd0 = c16 * RB + ((q ^ (c16 & 7)) * 16);
   const int rd1 = c16 * RB + (((4 + q) ^ (c16 & 7)) * 16);
-  // e4m3 weight fragments: k-step u, lane group q takes bytes [32 u + 8 q, +8)
-  // of row c16: chunk 2 u + q / 2, half q % 2
-  const int rdb0 = c16 * RBB + (((q >> 1) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
-  const int rdb1 = c16 * RBB + (((2 + (q >> 1)) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
-  // reads a k-step's fragments: A into AF; weights into BF (bf16) or, raw, into BQ (e4m3)
+  // byte-code weight fragments: k-step u, lane group q takes bytes
+  // [32 u + 8 q, +8) of row c16: chunk 2 u + q / 2, half q % 2. int4: bytes
+  // [16 u + 4 q, +4): chunk u, word q.
+  const int rdb0 = I4 ? c16 * RBB + ((c16 >> 3) & 1) * 16 + q * 4
+                      : c16 * RBB + (((q >> 1) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
+  const int rdb1 = I4 ? c16 * RBB + ((1 ^ ((c16 >> 3) & 1)) * 16) + q * 4
+                      : c16 * RBB + (((2 + (q >> 1)) ^ ((c16 >> 2) & 3)) * 16) + (q & 1) * 8;
+  // reads a k-step's fragments: A into AF; weights into BF (bf16) or, raw, into BQ (codes)
 #define MOE_READ(S, RD, RDB, AF, BF, BQ)                                                             \
   do {                                                                                               \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                           \
@@ -664,17 +701,17 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
       const int brow = SWI ? ((j < FN / 2) ? wn * (WTB / 2) + j * 16                                 \
                                            : BNO + wn * (WTB / 2) + (j - FN / 2) * 16)               \
                            : wn * WTB + j * 16;                                                      \
-      if constexpr (F8) BQ[j] = *reinterpret_cast<const uint2*>((S) + BM * RB + brow * RBB + RDB);   \
+      if constexpr (CODES) BQ[j] = *reinterpret_cast<const BQT*>((S) + BM * RB + brow * RBB + RDB);  \
       else BF[j] = *reinterpret_cast<const uint4*>((S) + BM * RB + brow * RB + RD);                  \
     }                                                                                                \
   } while (0)
-  // e4m3 -> bf16, exact (after the reads have arrived)
+  // codes -> bf16, exact (after the reads have arrived)
 #define MOE_CVT(BQ, BF)                                                                              \
   do {                                                                                               \
-    if constexpr (F8) {                                                                              \
+    if constexpr (CODES) {                                                                           \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                               \
-        const uint2 lo_ = e4m3x4_to_bf16x4(BQ[j].x), hi_ = e4m3x4_to_bf16x4(BQ[j].y);                \
-        BF[j] = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                              \
+        BF[j] = frag_to_bf16<WF>(BQ[j]);                                                             \
+        if constexpr (I4) __builtin_amdgcn_sched_barrier(0); /* one fragment's temporaries at a time */ \
       }                                                                                              \
     }                                                                                                \
   } while (0)
@@ -768,7 +805,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
 #define MOE_IDLE2(ks) MOE_STAGE_IDLE(S2, ks)
 
   uint4 af0[FM], bf0[FN], af1[FM], bf1[FN];
-  uint2 bq0[FN], bq1[FN];  // raw e4m3 fragments (unused for bf16 weights)
+  BQT bq0[FN], bq1[FN];  // raw code fragments (unused for bf16 weights)
   MOE_DMA(S0, MOE_COL(0));
   MOE_DMA(S1, MOE_COL(1));
   if constexpr (NSTAGE == 3) MOE_DMA(S2, MOE_COL(min(2, n_st - 1)));
@@ -1054,6 +1091,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams 
   if (sp.s == 1 || b >= sp.r) return;
   TileInfo ti;
   tile_from_linear<BM, BNO>(p, sp.full + b, ti);
+  if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   floatx4_t acc[FM][FN];
 #pragma unroll
@@ -1161,60 +1199,6 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------ plan
-// Integer codes -> bf16 codes (exact), one wave per weight row: row r of
-// expert e's matrix (rows_e rows of `cols` codes at pitch ld_src bytes) goes
-// to bf16 row r at pitch ld_dst elements. 8-bit rows: 16 codes per lane and
-// step, 4-bit rows: 32.
-struct DequantArgs {
-  const char* src;
-  uint16_t* dst;
-  int64_t rows_e, cols, ld_src, ld_dst;
-  int32_t n_experts;
-  uint8_t bits[kMaxGroups];
-};
-
-__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t R = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (R >= a.rows_e * a.n_experts) return;
-  const int e = static_cast<int>(R / a.rows_e);
-  const char* src = a.src + R * a.ld_src;
-  uint16_t* dst = a.dst + R * a.ld_dst;
-  if (a.bits[e] == 8) {
-    for (int64_t c = lane * 16; c < a.cols; c += 64 * 16) {
-      const uint4 q = *reinterpret_cast<const uint4*>(src + c);
-      const uint2 b0 = int8x4_to_bf16x4(q.x), b1 = int8x4_to_bf16x4(q.y);
-      const uint2 b2 = int8x4_to_bf16x4(q.z), b3 = int8x4_to_bf16x4(q.w);
-      *reinterpret_cast<uint4*>(dst + c) = make_uint4(b0.x, b0.y, b1.x, b1.y);
-      *reinterpret_cast<uint4*>(dst + c + 8) = make_uint4(b2.x, b2.y, b3.x, b3.y);
-    }
-  } else {
-    for (int64_t c = lane * 32; c < a.cols; c += 64 * 32) {
-      const uint4 q = *reinterpret_cast<const uint4*>(src + c / 2);
-      *reinterpret_cast<uint4*>(dst + c) = int4x8_to_bf16x8(q.x);
-      *reinterpret_cast<uint4*>(dst + c + 8) = int4x8_to_bf16x8(q.y);
-      *reinterpret_cast<uint4*>(dst + c + 16) = int4x8_to_bf16x8(q.z);
-      *reinterpret_cast<uint4*>(dst + c + 24) = int4x8_to_bf16x8(q.w);
-    }
-  }
-}
-
-hipError_t launch_dequant(const void* src, void* dst, int64_t rows_e, int64_t cols, int64_t ld_src, int64_t ld_dst,
-                          int32_t n, const uint8_t* bits, hipStream_t s) {
-  if (!src || n <= 0) return hipSuccess;
-  DequantArgs a{};
-  a.src = static_cast<const char*>(src);
-  a.dst = static_cast<uint16_t*>(dst);
-  a.rows_e = rows_e;
-  a.cols = cols;
-  a.ld_src = ld_src;
-  a.ld_dst = ld_dst;
-  a.n_experts = n;
-  for (int e = 0; e < n; ++e) a.bits[e] = bits[e];
-  hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(ceil_div(rows_e * n, 4))), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* offsets, FfnPlan pl) {
   __shared__ int32_t s_mt[2 * kMaxGroups];
   plan_groups(offsets, pl, s_mt, threadIdx.x, kThreads);
@@ -1232,19 +1216,19 @@ hipError_t run_bf16(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile configurations of the bf16 path.
+// Tile configurations of the bf16-activation path (any weight format).
 enum TileCfg {
   kReg128 = 0,  // register-staged 128 x 128, 4 waves: fewer than 2048 rows
-  kReg256 = 1,  // register-staged 256 x 256, 8 waves: integer weights (decoded in registers)
-  kDma256 = 2,  // LDS-DMA 256 x 256: bf16 or e4m3, many rows per group
-  kDma128 = 3,  // LDS-DMA 128 x 256: bf16 or e4m3, few rows per group
+  kDma256 = 1,  // LDS-DMA 256 x 256: many rows per group
+  kDma128 = 2,  // LDS-DMA 128 x 256: few rows per group
 };
-constexpr int tile_rows(int cfg) { return (cfg == kReg256 || cfg == kDma256) ? 256 : 128; }
+constexpr int tile_rows(int cfg) { return cfg == kDma256 ? 256 : 128; }
 
 template <int EPI, int BM, int W, int WF = kWBf16>
 hipError_t run_dma(const GemmParams& p_in, int64_t max_mtiles, hipStream_t s) {
   GemmParams p = p_in;
   p.mat_scaled = WF == kWE4m3 ? 1 : 0;
+  p.col_scaled = (WF == kWInt8 || WF == kWInt4) ? 1 : 0;
   constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
@@ -1294,15 +1278,12 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 template <int EPI, int WF>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  if constexpr (WF == kWE4m3) {
+  if constexpr (WF != kWBf16) {
     switch (cfg) {
       case kDma256: return run_dma<EPI, 256, 8, WF>(p, max_mtiles, s);
       case kDma128: return run_dma<EPI, 128, 8, WF>(p, max_mtiles, s);
       default: return run_bf16<128, 128, 2, 2, EPI, WF>(p, max_mtiles, s);
     }
-  } else if constexpr (WF != kWBf16) {
-    if (cfg == kReg256) return run_bf16<256, 256, 2, 4, EPI, WF>(p, max_mtiles, s);
-    return run_bf16<128, 128, 2, 2, EPI, WF>(p, max_mtiles, s);
   } else {
     switch (cfg) {
       case kDma256: return run_dma5<EPI>(p, max_mtiles, s);
@@ -1322,17 +1303,16 @@ hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipS
   }
 }
 
-// Tile configuration of a bf16 or e4m3 call: register-staged tiles for few
-// rows; for many rows the LDS-DMA tiles, 256 rows when the groups average at least 384
-// rows, else 128 (less padding in each group's last tile). Measured: the
-// fine-grained layer (about 400 rows a group, two shared experts of 8192)
-// runs 4 % faster on 256-row tiles, the Switch layer (at most 320) 11 % slower.
-// Widths that the 256-column tiles do not fit take the 128 x 128 tiles.
-// Integer codes decoded in registers take the 256 x 256 register-staged tiles.
+// Tile configuration of a call (any weight format): register-staged tiles for
+// few rows; for many rows the LDS-DMA tiles, 256 rows when the groups average
+// at least 384 rows, else 128 (less padding in each group's last tile).
+// Measured: the fine-grained layer (about 400 rows a group, two shared
+// experts of 8192) runs 4 % faster on 256-row tiles, the Switch layer (at most
+// 320) 11 % slower. Widths that the 256-column tiles do not fit take the
+// 128 x 128 tiles.
 int pick_cfg(const FfnArgs& a) {
   const int64_t rows = a.routed_row_cap + static_cast<int64_t>(a.n_shared) * a.T;
   if (rows < 2048 || !wide_tiles_fit(a.act, a.d, a.d_ff)) return kReg128;
-  if (a.w_dtype == 3 && !a.wdq) return kReg256;
   return rows >= 384LL * (a.n_routed + a.n_shared) ? kDma256 : kDma128;
 }
 
@@ -1357,29 +1337,15 @@ int ffn_path_of(const FfnArgs& a) {
   if (use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T)) return kPathStream;
   if (a.act_dtype == 0) return kPathF32;
   switch (pick_cfg(a)) {
-    case kReg256: return kPathReg256;
     case kDma256: return kPathDma256;
     case kDma128: return kPathDma128;
     default: return kPathReg128;
   }
 }
 
-size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act) {
-  const int64_t up = (act == 1 ? 2 : 1) * d_ff * (d + kActPad), down = d * (d_ff + kActPad);
-  return static_cast<size_t>((up + down) * (n_routed + n_shared) * 2);
-}
-
-// Integer weights written out as bf16 for the DMA tiles (only when those
-// tiles take the call; otherwise the codes are decoded in registers).
-static bool dequantizes(const FfnArgs& a) {
-  if (a.w_dtype != 3 || !a.wdq) return false;
-  const int cfg = pick_cfg(a);
-  return cfg == kDma256 || cfg == kDma128;
-}
-
 WeightClasses weight_classes(const FfnArgs& a) {
   WeightClasses wc{};
-  if (a.w_dtype != 3 || dequantizes(a)) {
+  if (a.w_dtype != 3) {
     wc.n = 1;
     wc.wf[0] = a.w_dtype == 2 ? kWE4m3 : kWBf16;
     return wc;
@@ -1427,6 +1393,9 @@ FfnPlan ffn_plan(const FfnArgs& a) {
   pl.up_t = a.groups_t;
   pl.down_t = a.groups_t ? a.groups_t + G : nullptr;
   pl.tile_start_t = a.tile_start_t;
+  const WeightClasses wc = weight_classes(a);
+  pl.tile_start_c = wc.n == 2 ? a.tile_start_c : nullptr;
+  for (int i = 0; i < 9; ++i) pl.cls1[i] = wc.n == 2 ? wc.skip[0][i] : 0u;  // width 0 skips the 4-bit groups
   return pl;
 }
 
@@ -1456,42 +1425,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
   const bool swi = (a.act == 1);
-  // integer weights on the prefill tiles: every expert's codes to bf16 first
-  // (exact), then the bf16 tiles with the row scales per output column
-  const bool dq = dequantizes(a);
-  if (dq) {
-    const int64_t ldu = a.d + kActPad, ldd = a.d_ff + kActPad;
-    const int64_t up_e = a.d_ff * ldu, down_e = a.d * ldd;  // bf16 elements per expert matrix
-    uint16_t* q = static_cast<uint16_t*>(a.wdq);
-    uint16_t* w1 = q;
-    uint16_t* w3 = w1 + a.n_routed * up_e;
-    uint16_t* w2 = w3 + (swi_layer(a) ? a.n_routed * up_e : 0);
-    uint16_t* sw1 = w2 + a.n_routed * down_e;
-    uint16_t* sw3 = sw1 + a.n_shared * up_e;
-    uint16_t* sw2 = sw3 + (swi_layer(a) ? a.n_shared * up_e : 0);
-    const int64_t lu = a.ld_up, ld = a.ld_down;  // code row pitches (bytes)
-    err = launch_dequant(a.w1, w1, a.d_ff, a.d, lu, ldu, a.n_routed, a.w_bits, s);
-    if (err == hipSuccess && swi_layer(a)) err = launch_dequant(a.w3, w3, a.d_ff, a.d, lu, ldu, a.n_routed, a.w_bits, s);
-    if (err == hipSuccess) err = launch_dequant(a.w2, w2, a.d, a.d_ff, ld, ldd, a.n_routed, a.w_bits, s);
-    if (err == hipSuccess) err = launch_dequant(a.sw1, sw1, a.d_ff, a.d, lu, ldu, a.n_shared, a.sw_bits, s);
-    if (err == hipSuccess && swi_layer(a))
-      err = launch_dequant(a.sw3, sw3, a.d_ff, a.d, lu, ldu, a.n_shared, a.sw_bits, s);
-    if (err == hipSuccess) err = launch_dequant(a.sw2, sw2, a.d, a.d_ff, ld, ldd, a.n_shared, a.sw_bits, s);
-    if (err != hipSuccess) return err;
-    a.w1 = w1;
-    a.w3 = swi_layer(a) ? w3 : nullptr;
-    a.w2 = w2;
-    a.sw1 = sw1;
-    a.sw3 = swi_layer(a) ? sw3 : nullptr;
-    a.sw2 = sw2;
-    a.ld_up = ldu;
-    a.ld_down = ldd;
-  }
   // integer weights: one launch per bit width present, each skipping the other width's groups
   const WeightClasses wc = weight_classes(a);
 
   GemmParams p{};
-  p.col_scaled = dq ? 1 : 0;
   p.pre_u_r = p.pre_u_s = a.pre_up_u;
   p.pre_v_r = p.pre_v_s = a.pre_up_v;
   p.ld_pre = a.ld_pre_up;
@@ -1532,17 +1469,19 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   } else {
     for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
+      if (pl.tile_start_c) p.tile_start = pl.tile_start_c + 2 * c * (G + 1);
       err = swi ? run_wf<EPI_SWIGLU>(wc.wf[c], cfg, p, max_mtiles, s) : run_wf<EPI_GELU>(wc.wf[c], cfg, p, max_mtiles, s);
     }
-    if (err == hipSuccess && pl.bm_t > 0) {  // small groups and the groups' short tails on 128-row tiles
+    if (pl.bm_t > 0) {  // small groups and the groups' short tails on 128-row tiles
       GemmParams pt = p;
       pt.groups = pl.up_t;
       pt.tile_start = pl.tile_start_t;
       const int64_t mt = static_cast<int64_t>(kSmallGroupTiles) * G;  // row tiles of the second plan, at most
-      if (a.w_dtype == 2)
-        err = swi ? run_dma<EPI_SWIGLU, 128, 8, kWE4m3>(pt, mt, s) : run_dma<EPI_GELU, 128, 8, kWE4m3>(pt, mt, s);
-      else
-        err = swi ? run_dma<EPI_SWIGLU, 128, 8>(pt, mt, s) : run_dma<EPI_GELU, 128, 8>(pt, mt, s);
+      for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
+        for (int i = 0; i < 9; ++i) pt.skip[i] = wc.skip[c][i];
+        if (pl.tile_start_c) pt.tile_start = pl.tile_start_c + (2 * c + 1) * (G + 1);
+        err = swi ? run_wf<EPI_SWIGLU>(wc.wf[c], kDma128, pt, mt, s) : run_wf<EPI_GELU>(wc.wf[c], kDma128, pt, mt, s);
+      }
     }
   }
   stage_mark(kStageFfnUp, true, s);
@@ -1577,14 +1516,19 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   } else {
     for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
+      if (pl.tile_start_c) p.tile_start = pl.tile_start_c + 2 * c * (G + 1);
       err = run_wf<EPI_PLAIN>(wc.wf[c], cfg, p, max_mtiles, s);
     }
-    if (err == hipSuccess && pl.bm_t > 0) {
+    if (pl.bm_t > 0) {
       GemmParams pt = p;
       pt.groups = pl.down_t;
       pt.tile_start = pl.tile_start_t;
       const int64_t mt = static_cast<int64_t>(kSmallGroupTiles) * G;
-      err = a.w_dtype == 2 ? run_dma<EPI_PLAIN, 128, 8, kWE4m3>(pt, mt, s) : run_dma<EPI_PLAIN, 128, 8>(pt, mt, s);
+      for (int c = 0; c < wc.n && err == hipSuccess; ++c) {
+        for (int i = 0; i < 9; ++i) pt.skip[i] = wc.skip[c][i];
+        if (pl.tile_start_c) pt.tile_start = pl.tile_start_c + (2 * c + 1) * (G + 1);
+        err = run_wf<EPI_PLAIN>(wc.wf[c], kDma128, pt, mt, s);
+      }
     }
   }
   stage_mark(kStageFfnDown, true, s);

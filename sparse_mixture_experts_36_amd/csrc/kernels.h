@@ -68,6 +68,13 @@ struct FfnPlan {
   GroupDesc* down_t;         // [G]
   int32_t* tile_start_t;     // [G + 1]
   int32_t bm_t;
+  // integer layers with 8- and 4-bit experts (one launch per width): the
+  // row-tile prefix of each width's groups alone, [width][plan][G + 1] (plan
+  // 0: bm-row tiles, 1: bm_t-row tiles), so that each launch's tiles are dealt
+  // over all XCDs; null for one width. Bit g of cls1: group g has the second
+  // width (4 bits).
+  int32_t* tile_start_c;
+  uint32_t cls1[9];
 };
 
 // ---------------------------------------------------------------- permute
@@ -129,13 +136,13 @@ struct FfnArgs {
   int32_t* tile_start;        // [n_routed + n_shared + 1] (workspace)
   GroupDesc* groups_t;        // [2][n_routed + n_shared]: tail tiles' groups (workspace)
   int32_t* tile_start_t;      // [n_routed + n_shared + 1] (workspace)
+  int32_t* tile_start_c;      // [2][2][n_routed + n_shared + 1] per-width prefixes (workspace; integer weights)
   int32_t* active;            // [1 + n_routed + n_shared]: count, then the groups with rows (workspace)
   float* part;                // decode path: [splits][rows][d] fp32 partials (workspace)
   float* split_part;          // prefill path: k-split partial tiles, kSplitPartFloats (workspace) or null
   bool planned;               // groups, tile_start and active are already written (by the permutation)
   const uint8_t* w_bits;      // integer weights (w_dtype 3): HOST [n_routed], 8 or 4
   const uint8_t* sw_bits;     // HOST [n_shared]
-  void* wdq;                  // integer weights, prefill: workspace for every expert's codes as bf16 (dq_bytes), or null
   // the layer backward's forward recompute (DMA tiles only, else the launch
   // fails): fp32 W1 x (+ b1) and W3 x of every row (pitch ld_pre_up); null: none
   float *pre_up_u, *pre_up_v;
@@ -153,12 +160,6 @@ inline bool wide_tiles_fit(int32_t act, int64_t d, int64_t d_ff) {
 inline bool ffn_uses_dma(int32_t act_dtype, int32_t w_dtype, int64_t rows, int32_t act, int64_t d, int64_t d_ff) {
   return act_dtype == 1 && w_dtype == 1 && rows >= 2048 && wide_tiles_fit(act, d, d_ff);
 }
-// Integer weights on the prefill tiles: the codes of every expert are first
-// written out as bf16 (exact) into this many workspace bytes, with rows
-// kActPad elements longer than d / d_ff, and the bf16 tiles apply the row
-// scales per output column.
-size_t dq_bytes(int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act);
-
 // Launch classes of a layer's weights: one for bf16 / e4m3 / uniform integer
 // widths, two for mixed 8- and 4-bit experts (each launch skips, by group bit,
 // the groups of the other width).
@@ -179,8 +180,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 constexpr int kSmallGroupTiles = 3;
 // Kernel family launch_grouped_ffn takes for these arguments (the values of
 // moe_ffn_path in moe.h).
-enum FfnPath { kPathF32 = 0, kPathStream = 1, kPathReg128 = 2, kPathReg256 = 3, kPathDma256 = 4, kPathDma128 = 5,
-               kPathBgemm = 6 };
+enum FfnPath { kPathF32 = 0, kPathStream = 1, kPathReg128 = 2, kPathDma256 = 3, kPathDma128 = 4,
+               kPathBgemm = 5 };
 int ffn_path_of(const FfnArgs& a);
 
 // Decode-sized layers (few rows per expert) stream expert weights instead of
@@ -193,19 +194,10 @@ constexpr int64_t kActPad = 64;
 inline bool use_skinny(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shared, int64_t T) {
   return act_dtype == 1 && routed_row_cap + n_shared * T <= kSkinnyMaxRows;
 }
-// whether a layer's FFN may take the bf16 prefill GEMM, which uses the k-split
-// partial tiles
-// whether an integer-weight layer's FFN dequantizes its codes for the bf16
-// prefill tiles (2048 rows or more; fewer run on tiles that decode in registers)
-inline bool uses_int_dequant(int32_t act_dtype, int32_t w_dtype, int64_t routed_row_cap, int32_t n_shared,
-                             int64_t T) {
-  return act_dtype == 1 && w_dtype == 3 && !use_skinny(act_dtype, routed_row_cap, n_shared, T) &&
-         routed_row_cap + n_shared * T >= 2048;
-}
-inline bool uses_prefill_gemm(int32_t act_dtype, int32_t w_dtype, int64_t routed_row_cap, int32_t n_shared,
-                              int64_t T) {
-  return act_dtype == 1 && !use_skinny(act_dtype, routed_row_cap, n_shared, T) &&
-         (w_dtype == 1 || uses_int_dequant(act_dtype, w_dtype, routed_row_cap, n_shared, T));
+// whether a layer's FFN may take the prefill tiles (bf16 activations, any
+// weight format), which use the k-split partial tiles
+inline bool uses_prefill_gemm(int32_t act_dtype, int64_t routed_row_cap, int32_t n_shared, int64_t T) {
+  return act_dtype == 1 && !use_skinny(act_dtype, routed_row_cap, n_shared, T);
 }
 // fp32 partial-sum floats the decode path needs (0 when no GEMM is split)
 size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,

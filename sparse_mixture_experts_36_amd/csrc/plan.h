@@ -79,6 +79,18 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
       acc += s_mt[G + g];
     }
     pl.tile_start_t[G] = acc;
+  } else if (pl.tile_start_c && tid >= 2 && tid < 6) {  // per-width prefixes: width c, plan t
+    const uint32_t c = static_cast<uint32_t>(tid - 2) >> 1;
+    const int t = (tid - 2) & 1;
+    if (t == 0 || pl.bm_t > 0) {
+      int32_t* ts = pl.tile_start_c + (2 * c + t) * (G + 1);
+      int32_t acc = 0;
+      for (int g = 0; g < G; ++g) {
+        ts[g] = acc;
+        if (((pl.cls1[g >> 5] >> (g & 31)) & 1u) == c) acc += s_mt[t * G + g];
+      }
+      ts[G] = acc;
+    }
   }
   __syncthreads();
 }

@@ -1,7 +1,8 @@
 """Per-expert integer weights (INT8 for the high-traffic experts, INT4 for the
 rest, one fp32 scale per weight row) through every expert path: the GEMV and
 streaming decode kernels, which decode the codes in registers while the bytes
-stream, and the register-staged prefill tiles. The library reads packed byte
+stream, the register-staged tiles (fewer than 2048 rows) and the LDS-DMA
+tiles, which convert each fragment's codes after its LDS read. The library reads packed byte
 rows (two INT4 codes a byte); the oracle reads the unpacked codes. End-to-end
 against the CPU oracle, reduced sizes (every token) and full Mixtral sizes
 (sampled tokens)."""
@@ -40,15 +41,18 @@ REDUCED = {
     "mixtral-like-int-T100": MIX.with_(T=100, d=1024, d_ff=1536),
     "mixtral-like-int-T64-all-int8": MIX.with_(T=64, d=1024, d_ff=1536, n_int8=8),
     "fine-grained-like-int-decode": FG.with_(T=24, d=512, d_ff=256),
-    # register-staged prefill tiles (128 x 128 below 2048 rows, 256 x 256 above)
-    "mixtral-like-int-prefill-128": MIX.with_(T=300, d=1024, d_ff=1536),
-    "mixtral-like-int-prefill-256": MIX.with_(T=1024, d=1024, d_ff=1536),
+    # prefill tiles: register-staged 128 x 128 below 2048 rows, else LDS-DMA
+    # 128-row tiles (groups averaging under 384 rows) or 256-row tiles
+    "mixtral-like-int-prefill-reg128": MIX.with_(T=300, d=1024, d_ff=1536),
+    "mixtral-like-int-prefill-dma128": MIX.with_(T=1024, d=1024, d_ff=1536),
+    "mixtral-like-int-prefill-dma256": MIX.with_(T=2048, d=1024, d_ff=1536),
+    "mixtral-like-int-prefill-dma256-skewed": MIX.with_(T=2048, d=1024, d_ff=1536, zipf_s=1.2),
     "mixtral-like-int-prefill-all-int4": MIX.with_(T=1024, d=512, d_ff=768, n_int8=0),
     "fine-grained-like-int": FG.with_(T=512, d=512, d_ff=256),
     "switch-like-int-gelu": SW.with_(T=2048, d=512, d_ff=1024),
     "switch-like-int-gelu-decode": SW.with_(T=128, d=512, d_ff=1024),
     # 2048 rows or more, but a GELU d_ff the 256-column tiles do not fit: the
-    # codes are decoded in registers on 128 x 128 tiles, not written out as bf16
+    # codes are decoded in registers on 128 x 128 tiles
     "switch-like-int-gelu-d_ff-384": SW.with_(T=4096, d=512, d_ff=384),
 }
 
@@ -58,10 +62,12 @@ def test_int_forward_reduced(name):
     run_and_check(gen.make_inputs(REDUCED[name]), label=name)
 
 
+@pytest.mark.parametrize("T", [64, 2048])
 @pytest.mark.parametrize("pad", [0, 64])
-def test_int_forward_reduced_padded_rows(pad):
-    """Byte rows longer than the codes (ld_up / ld_down = d + pad, d_ff + pad)."""
-    run_and_check(gen.make_inputs(MIX.with_(T=64, d=1024, d_ff=1536)), label=f"int rows pad {pad}", pad=pad)
+def test_int_forward_reduced_padded_rows(pad, T):
+    """Byte rows longer than the codes (ld_up / ld_down = d + pad, d_ff + pad),
+    on the streaming kernels (T = 64) and the 256-row DMA tiles (T = 2048)."""
+    run_and_check(gen.make_inputs(MIX.with_(T=T, d=1024, d_ff=1536)), label=f"int rows pad {pad} T={T}", pad=pad)
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])

@@ -23,9 +23,9 @@ def _cuda():
 
 
 def _wl(T, N, k, gating=gen.SOFTMAX_TOPK, act=gen.SWIGLU, d=256, d_ff=384, dt=gen.BF16, wdt=None, cf=None,
-        n_shared=0, zipf=None):
+        n_shared=0, zipf=None, n_int8=0):
     return gen.Workload("t", T, d, d_ff, N, k, act, gating, dt, dt if wdt is None else wdt, cf, n_shared=n_shared,
-                        zipf_s=zipf)
+                        zipf_s=zipf, n_int8=n_int8)
 
 
 # ---------------------------------------------------------------- routing on given logits: bit-exact
@@ -201,6 +201,15 @@ FFN_CASES = [
     dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, wdt=gen.E4M3),             # 256 rows, split, tails
     dict(T=3000, N=4, k=2, act=gen.SWIGLU, d=1024, d_ff=512, n_shared=1, pad=64, wdt=gen.E4M3),  # 256 rows, shared
     dict(T=2048, N=12, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, zipf=1.0, wdt=gen.E4M3),  # small groups
+    # integer codes on the LDS-DMA tiles (INT8: byte rows as e4m3; INT4: 32-byte
+    # stage rows), one launch per width present, row scales in the epilogue;
+    # experts below n_int8 and the shared ones take 8 bits, the others 4
+    dict(T=2048, N=16, k=1, act=gen.GELU, d=256, d_ff=1024, n_shared=1, biases=True, wdt=gen.INT_W, n_int8=6),  # 128
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, wdt=gen.INT_W, n_int8=2),  # 256 rows, split, tails
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, wdt=gen.INT_W, n_int8=0),  # all INT4
+    dict(T=2048, N=4, k=2, act=gen.SWIGLU, d=256, d_ff=512, wdt=gen.INT_W, n_int8=4),  # all INT8
+    dict(T=3000, N=4, k=2, act=gen.SWIGLU, d=1024, d_ff=512, n_shared=1, pad=64, wdt=gen.INT_W, n_int8=1),  # padded
+    dict(T=2048, N=12, k=2, act=gen.SWIGLU, d=512, d_ff=512, n_shared=1, zipf=1.0, wdt=gen.INT_W, n_int8=4),  # small
 ]
 
 
