@@ -43,8 +43,10 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-// Weight storage formats of the expert kernels (template argument WF).
-enum WeightFormat { kWBf16 = 0, kWE4m3 = 1, kWInt8 = 2, kWInt4 = 3 };
+// Weight storage formats of the expert kernels (template argument WF);
+// kWIntMix: 8- and 4-bit integer experts in one launch, each group taking its
+// own width.
+enum WeightFormat { kWBf16 = 0, kWE4m3 = 1, kWInt8 = 2, kWInt4 = 3, kWIntMix = 4 };
 
 // The bf16 pair (lo, hi) from the upper halves of two fp32 values: exact when
 // both are small integers, as decoded integer codes are.

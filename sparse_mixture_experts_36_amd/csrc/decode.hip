@@ -57,6 +57,7 @@ struct StreamParams {
   int32_t scale_row0;        // integer weights: offset of this GEMM's matrix rows (W1 0, W2 2 d_ff)
   int32_t scale_row3;        // integer weights: offset of W3's rows (d_ff)
   uint32_t skip[9];          // bit g set: group g is left to another launch (its experts' other bit width)
+  uint32_t bits4[9];         // mixed-width launches (kWIntMix): bit g set: group g has 4-bit codes, else 8
   uint16_t* C_r;             // outputs (h / y_perm) for routed groups
   uint16_t* C_s;             //              (h / y_shared) for shared groups
   int64_t ldc;
@@ -158,27 +159,24 @@ __device__ __forceinline__ float epilogue(int epi, float a, float b, float bias)
 // lanes that read one chunk of 16 rows hit 16 different bank groups. The two
 // LDS buffers alternate by burst, one barrier per burst; the host guarantees
 // an even number of bursts per pass.
+template <int RB, int KU, bool SHARED_A>
+constexpr int stream_atile() { return SHARED_A ? 16 * RB * KU * KC * 2 : 16; }  // bytes of a burst's token rows
+
+// Wave w's share of the streaming GEMM: group g (which has rows), block and k
+// split from w; abuf0 / abuf1 hold the token rows of alternate bursts
+// (SHARED_A).
 template <int RB, int WF, int KU, bool SHARED_A>
-__global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
-  static_assert(!SHARED_A || (RB >= 2 && KU == 2), "shared token rows: 32 or 64 rows, two k-steps a burst");
-  constexpr int AROWB = KU * KC * 2;                        // bytes of one token row per burst
-  constexpr int ATILE = SHARED_A ? 16 * RB * AROWB : 16;    // bytes of the burst's token rows
-  constexpr int ADMA = ATILE / (kThreads * 16);             // DMA instructions per lane and burst
-  __shared__ __attribute__((aligned(16))) char abuf0[ATILE];
-  __shared__ __attribute__((aligned(16))) char abuf1[ATILE];
+__device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, char* abuf1, int w, int g) {
+  static_assert(!SHARED_A || KU == 2 || KU == 4, "shared token rows: two or four k-steps a burst");
+  constexpr int AROWB = KU * KC * 2;                         // bytes of one token row per burst
+  constexpr int ATILE = stream_atile<RB, KU, SHARED_A>();
+  constexpr int ADMA = ATILE / (kThreads * 16);              // DMA instructions per lane and burst
   constexpr int FN = 2;  // 16-row weight tiles per wave
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, c16 = lane & 15;
   const bool swi = (p.epi == 1);
   const int nblk = swi ? p.Nout / 16 : p.Nout / 32;  // blocks per expert
-  // the wave index is made wave-uniform, so that group, expert and base
-  // pointers live in scalar registers and loads take a 32-bit lane offset
-  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int per_g = nblk * p.splits;
-  const int slot = w / per_g;  // waves run over the groups that have rows only
-  if (slot >= p.active[0]) return;
-  const int g = p.active[1 + slot];
-  if (g >= p.n_groups || skipped(p, g)) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
   const int nb = SHARED_A ? (w % per_g) % nblk : (w % per_g) / p.splits;
@@ -302,9 +300,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
             }
           }
       };
+      // the buffers alternate by burst; the barrier inside each burst also
+      // tells that every wave is done with the buffer the next burst refills.
+      // nsteps is a multiple of KU (the host checks), not always of 2 KU.
       for (int st = 0; st < nsteps; st += 2 * KU) {
         burst(abuf0, st);
-        burst(abuf1, st + KU);
+        if (st + KU < nsteps) burst(abuf1, st + KU);
       }
     } else {
     for (int st = 0; st < nsteps; st += KU) {
@@ -381,6 +382,33 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
   }
 }
 
+// Whether group g of a mixed-width launch has 4-bit codes.
+__device__ __forceinline__ bool group_int4(const StreamParams& p, int g) { return (p.bits4[g >> 5] >> (g & 31)) & 1u; }
+
+// The streaming GEMM: wave w -> group, block and k split. WF = kWIntMix runs
+// the 8- and 4-bit experts of an integer layer in one launch, each wave taking
+// its group's width.
+template <int RB, int WF, int KU, bool SHARED_A>
+__global__ __launch_bounds__(kThreads) void stream_kernel(StreamParams p) {
+  constexpr int ATILE = stream_atile<RB, KU, SHARED_A>();
+  __shared__ __attribute__((aligned(16))) char abuf0[ATILE];
+  __shared__ __attribute__((aligned(16))) char abuf1[ATILE];
+  const int nblk = p.epi == 1 ? p.Nout / 16 : p.Nout / 32;  // blocks per expert
+  // the wave index is made wave-uniform, so that group, expert and base
+  // pointers live in scalar registers and loads take a 32-bit lane offset
+  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = w / (nblk * p.splits);  // waves run over the groups that have rows only
+  if (slot >= p.active[0]) return;
+  const int g = p.active[1 + slot];
+  if (g >= p.n_groups || skipped(p, g)) return;
+  if constexpr (WF == kWIntMix) {
+    if (group_int4(p, g)) stream_body<RB, kWInt4, KU, SHARED_A>(p, abuf0, abuf1, w, g);
+    else stream_body<RB, kWInt8, KU, SHARED_A>(p, abuf0, abuf1, w, g);
+  } else {
+    stream_body<RB, WF, KU, SHARED_A>(p, abuf0, abuf1, w, g);
+  }
+}
+
 // Sums the split partials in split order, applies the activation / bias and
 // writes bf16. Block (x, R): partial row R, columns [x*1024, x*1024 + 1024), four
 // per thread; all split loads are issued before the fixed-order sum. Rows never
@@ -448,18 +476,14 @@ __global__ __launch_bounds__(kThreads) void stream_reduce_kernel(StreamParams p,
 // are reduced across the wave once, at the end (a fixed butterfly order).
 constexpr int kSeg = 1024;  // bytes of one weight row per segment
 
+// Wave w's NR weight rows of group g (which has rows).
 template <int R, int WF, int NR, int U>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
+__device__ __forceinline__ void gemv_body(const StreamParams& p, int w, int g) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int lane = threadIdx.x & 63;
   const bool swi = (p.epi == 1);
   const int cols = swi ? NR / 2 : NR;  // output columns per wave
   const int nblk = p.Nout / cols;
-  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = w / nblk;  // waves run over the groups that have rows only
-  if (slot >= p.active[0]) return;
-  const int g = p.active[1 + slot];
-  if (g >= p.n_groups || skipped(p, g)) return;
   const GroupDesc gd = p.groups[g];
   if (gd.rows <= 0) return;
   const int n0 = (w % nblk) * cols;
@@ -608,6 +632,25 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
   }
 }
 
+// The GEMV: wave w -> group and row block. WF = kWIntMix runs the 8- and
+// 4-bit experts in one launch (4-bit rows with half the segments a burst, as
+// in their own launches).
+template <int R, int WF, int NR, int U>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
+  const int nblk = p.Nout / (p.epi == 1 ? NR / 2 : NR);
+  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = w / nblk;  // waves run over the groups that have rows only
+  if (slot >= p.active[0]) return;
+  const int g = p.active[1 + slot];
+  if (g >= p.n_groups || skipped(p, g)) return;
+  if constexpr (WF == kWIntMix) {
+    if (group_int4(p, g)) gemv_body<R, kWInt4, NR, U / 2>(p, w, g);
+    else gemv_body<R, kWInt8, NR, U>(p, w, g);
+  } else {
+    gemv_body<R, WF, NR, U>(p, w, g);
+  }
+}
+
 // k splits for one GEMM: double while the touched experts' blocks give fewer
 // than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
 // which is more than HBM latency times bandwidth needs) and every split keeps
@@ -630,6 +673,17 @@ hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hip
   // 32 or 64 token rows: shared through LDS when the passes hold whole burst pairs
   const bool pairs = (p.K / p.splits / KC) % 4 == 0;
   const bool shared_a = rb >= 2 && pairs;
+  // 16-row passes of integer codes: four k-steps a burst (runs of 256 or 512
+  // bytes per weight row) with the token rows in LDS, which frees the
+  // registers a wave would hold them in. Measured at 16 tokens (Mixtral
+  // shape, INT8 x 2 + INT4 x 6): FFN 228 -> 213 us.
+  const bool intw = wf == kWInt8 || wf == kWInt4 || wf == kWIntMix;
+  if (intw && rb == 1 && (p.K / p.splits / KC) % 4 == 0) {
+    if (wf == kWInt8) hipLaunchKernelGGL((stream_kernel<1, kWInt8, 4, true>), grid, dim3(kThreads), 0, s, p);
+    else if (wf == kWInt4) hipLaunchKernelGGL((stream_kernel<1, kWInt4, 4, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((stream_kernel<1, kWIntMix, 4, true>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+  }
   // at most 8 waves per CU: 16-row passes take the 32-row shared kernel when
   // they can (measured faster there), else four k-steps per burst (whose
   // registers still fit 2 waves per SIMD)
@@ -639,6 +693,7 @@ hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hip
     case kWE4m3: hipLaunchKernelGGL((stream_kernel<R, kWE4m3, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
     case kWInt8: hipLaunchKernelGGL((stream_kernel<R, kWInt8, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
     case kWInt4: hipLaunchKernelGGL((stream_kernel<R, kWInt4, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
+    case kWIntMix: hipLaunchKernelGGL((stream_kernel<R, kWIntMix, U, SA>), grid, dim3(kThreads), 0, s, p); break; \
     default: hipLaunchKernelGGL((stream_kernel<R, kWBf16, U, SA>), grid, dim3(kThreads), 0, s, p); break;     \
   }
   if (deep && pairs) {
@@ -647,7 +702,7 @@ hipError_t run_stream(const StreamParams& p, int rb, int wf, int64_t blocks, hip
     MOE_STREAM_LAUNCH(1, 4, false)
   } else if (rb == 1) {
     // integer codes: four k-steps a burst, so a wave keeps as many bytes in flight
-    if (wf == kWInt8 || wf == kWInt4) { MOE_STREAM_LAUNCH(1, 4, false) } else { MOE_STREAM_LAUNCH(1, 2, false) }
+    if (intw) { MOE_STREAM_LAUNCH(1, 4, false) } else { MOE_STREAM_LAUNCH(1, 2, false) }
   } else if (rb == 2) {
     if (shared_a) { MOE_STREAM_LAUNCH(2, 2, true) } else { MOE_STREAM_LAUNCH(2, 2, false) }
   } else {
@@ -679,6 +734,7 @@ hipError_t run_gemv(const StreamParams& p, int rows, int wf, int64_t slots, hipS
     case kWE4m3: hipLaunchKernelGGL((gemv_kernel<R, kWE4m3, NR, U>), grid, dim3(kThreads), 0, s, p); break;   \
     case kWInt8: hipLaunchKernelGGL((gemv_kernel<R, kWInt8, NR, U>), grid, dim3(kThreads), 0, s, p); break;   \
     case kWInt4: hipLaunchKernelGGL((gemv_kernel<R, kWInt4, NR, U / 2>), grid, dim3(kThreads), 0, s, p); break; \
+    case kWIntMix: hipLaunchKernelGGL((gemv_kernel<R, kWIntMix, NR, U>), grid, dim3(kThreads), 0, s, p); break; \
     default: hipLaunchKernelGGL((gemv_kernel<R, kWBf16, NR, U>), grid, dim3(kThreads), 0, s, p); break;       \
   }
   if (rows == 1) {
@@ -731,7 +787,17 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
   // groups of the other width
   const WeightClasses wc = weight_classes(a);
   p.scale_pitch = static_cast<int32_t>(2 * a.d_ff + a.d);
+  // mixed 8- and 4-bit experts run in one launch per GEMM, each wave taking
+  // its group's width: two launches would each leave the GPU part idle and
+  // pay their own ramp and drain
   auto run_classes = [&](auto&& run) -> hipError_t {
+    if (wc.n == 2) {
+      for (int i = 0; i < 9; ++i) {
+        p.skip[i] = 0;
+        p.bits4[i] = wc.skip[0][i];  // the 8-bit class skips the 4-bit groups
+      }
+      return run(static_cast<int>(kWIntMix));
+    }
     hipError_t e = hipSuccess;
     for (int c = 0; c < wc.n && e == hipSuccess; ++c) {
       for (int i = 0; i < 9; ++i) p.skip[i] = wc.skip[c][i];
