@@ -54,6 +54,7 @@ struct GemmParams {
   int32_t scale_row0;     // integer weights: offset of this GEMM's matrix rows (W1 0, W2 2 d_ff)
   int32_t scale_row3;     // integer weights: offset of W3's rows (d_ff)
   uint32_t skip[9];       // bit g set: group g is left to another launch (its experts' other bit width)
+  uint32_t bits4[9];      // mixed-width launches (kWIntMix): bit g set: group g has 4-bit codes, else 8
   int32_t col_scaled;     // 1: the bf16 weights are integer codes; output column n takes row scale n
   int32_t mat_scaled;     // 1: e4m3 weights on the DMA tiles; the epilogue applies the per-matrix scales
   void* C_r;
@@ -567,8 +568,21 @@ __device__ __forceinline__ uint4 frag_to_bf16(uint32_t c) {
 //   32-bit word of 8 codes; chunk c of row r sits at c ^ ((r >> 3) & 1), and
 //   one DMA instruction fills 32 rows.
 // Integer codes take the row scales in the epilogue, one per output column.
+// Bytes of one stage buffer (activation rows, then weight rows) and the
+// number of stage buffers of the DMA tile for weight format WF.
+template <int BM, int WF>
+constexpr int dma_stage_bytes() {
+  return BM * dma::RB + dma::BNB * ((WF == kWE4m3 || WF == kWInt8) ? dma::RB / 2 : (WF == kWInt4 ? dma::RB / 4 : dma::RB));
+}
+template <int BM, int W, int WF>
+constexpr int dma_nstage() { return WF != kWBf16 ? 3 : dma::Cfg<BM, W>::NSTAGE; }
+
+// One tile (or k-chunk ks_begin .. ks_end of a tile; unit >= 0: a k-split
+// chunk whose raw partial sums go to the split workspace) with the stage
+// buffers S0, S1, S2 in LDS.
 template <int EPI, int BM, int W, int WF>
-__global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
+__device__ __forceinline__ void dma_tile_body(const GemmParams& p, const TileInfo& ti, int ks_begin, int ks_end,
+                                              int unit, char* S0, char* S1, char* S2) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
@@ -579,36 +593,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr bool CODES = F8 || I4;
   static_assert(!I4 || C_::BROWS % 32 == 0, "int4 rows go 32 to a DMA instruction");
   constexpr int RBB = F8 ? RB / 2 : (I4 ? RB / 4 : RB);  // weight row bytes in a stage
-  constexpr int SBY = BM * RB + BNB * RBB;                // one stage buffer
   constexpr int ADMA = C_::ADMA, BDMA = F8 ? C_::BROWS / 16 : (I4 ? C_::BROWS / 32 : C_::BDMA), NDMA = ADMA + BDMA;
-  constexpr int NSTAGE = CODES ? 3 : C_::NSTAGE;
+  constexpr int NSTAGE = dma_nstage<BM, W, WF>();
   typedef typename CodeFrag<WF>::type BQT;
-  __shared__ __attribute__((aligned(16))) char S0[SBY];
-  __shared__ __attribute__((aligned(16))) char S1[SBY];
-  __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? SBY : 16];
-
-  const int K = p.K;
-  const int KS = K / BK;  // even: K is a multiple of 128
-  TileInfo ti;
-  int ks_begin = 0, ks_end = KS, unit = -1;
-  {
-    const SplitPlan sp = split_plan<BNO>(p, KS / 2);
-    const int bid = blockIdx.x;
-    if (sp.s == 1) {
-      if (!decode_tile<BM, BNO>(p, ti)) return;
-    } else if (bid < sp.full) {  // full rounds; sp.full is a multiple of the XCD count
-      const int per_xcd = sp.full / kXcds;
-      tile_from_linear<BM, BNO>(p, (bid % kXcds) * per_xcd + bid / kXcds, ti);
-    } else {
-      unit = bid - sp.full;
-      if (unit >= sp.r * sp.s) return;
-      const int c = unit % sp.s;
-      tile_from_linear<BM, BNO>(p, sp.full + unit / sp.s, ti);
-      ks_begin = 2 * ((c * (KS / 2)) / sp.s);  // chunks of whole stage pairs
-      ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
-    }
-  }
-  if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
   // stage j of the loops below loads k-column ks_begin + j; all tiles walk k
   // in the same order, so tiles that share a weight tile or A rows read the
   // same lines at about the same time and L2 keeps them
@@ -847,6 +834,49 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
   }
   dma_store_pre<EPI, BM, W>(p, ti, acc);
   dma_store_tile<EPI, BM, W>(p, ti, acc);
+}
+
+template <int EPI, int BM, int W, int WF>
+__global__ __launch_bounds__(64 * W, 1) void gemm_dma_kernel(GemmParams p) {
+  using namespace dma;
+  constexpr int BNO = bno(EPI);
+  // a mixed-width launch holds the larger of the two formats' buffers
+  constexpr int SBY = WF == kWIntMix ? dma_stage_bytes<BM, kWInt8>() : dma_stage_bytes<BM, WF>();
+  constexpr int NSTAGE = dma_nstage<BM, W, WF>();
+  __shared__ __attribute__((aligned(16))) char S0[SBY];
+  __shared__ __attribute__((aligned(16))) char S1[SBY];
+  __shared__ __attribute__((aligned(16))) char S2[NSTAGE == 3 ? SBY : 16];
+
+  const int K = p.K;
+  const int KS = K / BK;  // even: K is a multiple of 128
+  TileInfo ti;
+  int ks_begin = 0, ks_end = KS, unit = -1;
+  {
+    const SplitPlan sp = split_plan<BNO>(p, KS / 2);
+    const int bid = blockIdx.x;
+    if (sp.s == 1) {
+      if (!decode_tile<BM, BNO>(p, ti)) return;
+    } else if (bid < sp.full) {  // full rounds; sp.full is a multiple of the XCD count
+      const int per_xcd = sp.full / kXcds;
+      tile_from_linear<BM, BNO>(p, (bid % kXcds) * per_xcd + bid / kXcds, ti);
+    } else {
+      unit = bid - sp.full;
+      if (unit >= sp.r * sp.s) return;
+      const int c = unit % sp.s;
+      tile_from_linear<BM, BNO>(p, sp.full + unit / sp.s, ti);
+      ks_begin = 2 * ((c * (KS / 2)) / sp.s);  // chunks of whole stage pairs
+      ks_end = 2 * (((c + 1) * (KS / 2)) / sp.s);
+    }
+  }
+  if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
+  if constexpr (WF == kWIntMix) {  // each tile takes its group's width
+    if ((p.bits4[ti.g >> 5] >> (ti.g & 31)) & 1u)
+      dma_tile_body<EPI, BM, W, kWInt4>(p, ti, ks_begin, ks_end, unit, S0, S1, S2);
+    else
+      dma_tile_body<EPI, BM, W, kWInt8>(p, ti, ks_begin, ks_end, unit, S0, S1, S2);
+  } else {
+    dma_tile_body<EPI, BM, W, WF>(p, ti, ks_begin, ks_end, unit, S0, S1, S2);
+  }
 }
 
 // The 256 x 256 DMA tile with operands in separate buffers: two 32 KB buffers
@@ -1228,7 +1258,7 @@ template <int EPI, int BM, int W, int WF = kWBf16>
 hipError_t run_dma(const GemmParams& p_in, int64_t max_mtiles, hipStream_t s) {
   GemmParams p = p_in;
   p.mat_scaled = WF == kWE4m3 ? 1 : 0;
-  p.col_scaled = (WF == kWInt8 || WF == kWInt4) ? 1 : 0;
+  p.col_scaled = (WF == kWInt8 || WF == kWInt4 || WF == kWIntMix) ? 1 : 0;
   constexpr int BNO = dma::bno(EPI);
   if (p.Nout % BNO != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
   int64_t grid = max_mtiles * (p.Nout / BNO);
@@ -1278,7 +1308,13 @@ hipError_t run_f32(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
 
 template <int EPI, int WF>
 hipError_t run_cfg(int cfg, const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
-  if constexpr (WF != kWBf16) {
+  if constexpr (WF == kWIntMix) {  // the DMA tiles only
+    switch (cfg) {
+      case kDma256: return run_dma<EPI, 256, 8, WF>(p, max_mtiles, s);
+      case kDma128: return run_dma<EPI, 128, 8, WF>(p, max_mtiles, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else if constexpr (WF != kWBf16) {
     switch (cfg) {
       case kDma256: return run_dma<EPI, 256, 8, WF>(p, max_mtiles, s);
       case kDma128: return run_dma<EPI, 128, 8, WF>(p, max_mtiles, s);
@@ -1299,6 +1335,7 @@ hipError_t run_wf(int wf, int cfg, const GemmParams& p, int64_t max_mtiles, hipS
     case kWE4m3: return run_cfg<EPI, kWE4m3>(cfg, p, max_mtiles, s);
     case kWInt8: return run_cfg<EPI, kWInt8>(cfg, p, max_mtiles, s);
     case kWInt4: return run_cfg<EPI, kWInt4>(cfg, p, max_mtiles, s);
+    case kWIntMix: return run_cfg<EPI, kWIntMix>(cfg, p, max_mtiles, s);
     default: return run_cfg<EPI, kWBf16>(cfg, p, max_mtiles, s);
   }
 }
@@ -1393,9 +1430,12 @@ FfnPlan ffn_plan(const FfnArgs& a) {
   pl.up_t = a.groups_t;
   pl.down_t = a.groups_t ? a.groups_t + G : nullptr;
   pl.tile_start_t = a.tile_start_t;
+  // per-width prefixes: mixed widths on the register-staged tiles (one launch
+  // per width); the DMA tiles take both widths in one launch
   const WeightClasses wc = weight_classes(a);
-  pl.tile_start_c = wc.n == 2 ? a.tile_start_c : nullptr;
-  for (int i = 0; i < 9; ++i) pl.cls1[i] = wc.n == 2 ? wc.skip[0][i] : 0u;  // width 0 skips the 4-bit groups
+  const bool per_width = wc.n == 2 && cfg != kDma256 && cfg != kDma128;
+  pl.tile_start_c = per_width ? a.tile_start_c : nullptr;
+  for (int i = 0; i < 9; ++i) pl.cls1[i] = per_width ? wc.skip[0][i] : 0u;  // width 0 skips the 4-bit groups
   return pl;
 }
 
@@ -1425,10 +1465,21 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, hipStream_t s) {
   // upper bound on row tiles: every group may end in a partial tile
   const int64_t max_mtiles = ceil_div(a.routed_row_cap, bm) + a.n_routed + a.n_shared * ceil_div(a.T, bm);
   const bool swi = (a.act == 1);
-  // integer weights: one launch per bit width present, each skipping the other width's groups
-  const WeightClasses wc = weight_classes(a);
-
+  // integer weights with 8- and 4-bit experts: on the DMA tiles one launch
+  // (kWIntMix, each tile taking its group's width); on the register-staged
+  // tiles one launch per width, each skipping the other width's groups and
+  // walking its own row-tile prefix
+  WeightClasses wc = weight_classes(a);
   GemmParams p{};
+  if (wc.n == 2 && !pl.tile_start_c) {
+    for (int i = 0; i < 9; ++i) {
+      p.bits4[i] = wc.skip[0][i];  // the 8-bit class skips the 4-bit groups
+      wc.skip[0][i] = 0;
+    }
+    wc.n = 1;
+    wc.wf[0] = kWIntMix;
+  }
+
   p.pre_u_r = p.pre_u_s = a.pre_up_u;
   p.pre_v_r = p.pre_v_s = a.pre_up_v;
   p.ld_pre = a.ld_pre_up;
