@@ -149,9 +149,9 @@ struct FfnArgs {
   int64_t ld_pre_up;
   bool up_only;  // the up GEMM alone (h and the copies above; no y)
 };
-// Whether the 256-column tiles (LDS-DMA, and the 256 x 256 register-staged
-// ones) fit a layer: each GEMM's output width a multiple of the columns a
-// tile yields (256; the SwiGLU up tile yields 128 of its 256 weight rows).
+// Whether the 256-column LDS-DMA tiles fit a layer: each GEMM's output width a
+// multiple of the columns a tile yields (256; the SwiGLU up tile yields 128 of
+// its 256 weight rows).
 inline bool wide_tiles_fit(int32_t act, int64_t d, int64_t d_ff) {
   return d % 256 == 0 && (act == 1 ? d_ff % 128 == 0 : d_ff % 256 == 0);
 }
