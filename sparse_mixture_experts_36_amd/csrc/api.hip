@@ -700,12 +700,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
                                   ld_xp, stats, pw);
   if (gather) fa.gather = perm_token;
-  // the one-block permutation, and expert choice's (whose offsets are fixed),
-  // also write the FFN's group plan
-  if (is_ec(s) || (gather && s.T <= moe::kPermTokens)) {
-    pa.plan = moe::ffn_plan(fa);
-    fa.planned = true;
-  }
+  // the permutation writes the FFN's group plan where it forms the offsets
+  // (its scan pass, or its one block), and expert choice's where they are fixed:
+  // no plan launch
+  pa.plan = moe::ffn_plan(fa);
+  fa.planned = true;
   hipError_t e = hipSuccess;
   if (moe::front_fits(ra, pa)) {  // decode sizes: router GEMM, routing and permutation in one launch
     e = moe::launch_front(ra, pa, stream);

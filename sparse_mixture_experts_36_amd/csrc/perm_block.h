@@ -141,15 +141,14 @@ __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, i
     for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
     if (lane == 0) *a.n_dropped = drop;
   }
-  // with no rows to copy, the slots (and, when asked, the FFN's group plan)
-  // are written here and no scatter pass runs
-  if (a.x_perm) return;
+  // the FFN's group plan, when asked; with no rows to copy also the slots
+  // (no scatter pass runs)
   __syncthreads();
   if (a.plan.up) {
     __shared__ int32_t s_mt[2 * kMaxGroups];
     plan_groups(s_off, a.plan, s_mt, tid, NTH);
   }
-  if (!live) return;
+  if (a.x_perm || !live) return;
 #pragma unroll
   for (int j = 0; j < kPermMaxK; ++j) {
     if (j >= k) break;

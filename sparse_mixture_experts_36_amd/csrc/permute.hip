@@ -99,15 +99,23 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(PermuteArgs a, 
         }
     }
   }
+  __shared__ int32_t s_off[kMaxN + 1];
   if (tid == 0) {
     int32_t off = 0, drop = 0;
     for (int x = 0; x < N; ++x) {
       a.offsets[x] = off;
+      s_off[x] = off;
       off += s_kept[x];
       drop += s_drop[x];
     }
     a.offsets[N] = off;
+    s_off[N] = off;
     *a.n_dropped = drop;
+  }
+  if (a.plan.up) {  // the FFN's group plan from the offsets just formed
+    __shared__ int32_t s_mt[2 * kMaxGroups];
+    __syncthreads();
+    plan_groups(s_off, a.plan, s_mt, tid, kScanThreads);
   }
 }
 
