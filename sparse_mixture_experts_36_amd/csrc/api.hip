@@ -700,6 +700,13 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   moe::PermuteArgs pa = perm_args(s, topk_idx, x, expert_offsets, perm_token, inv_map, gather ? nullptr : w.x_perm,
                                   ld_xp, stats, pw);
   if (gather) fa.gather = perm_token;
+  if (!is_ec(s)) {  // a one-token call may fold the combine into the down GEMM
+    fa.fuse_inv_map = inv_map;
+    fa.fuse_topk_idx = topk_idx;
+    fa.fuse_topk_w = topk_w;
+    fa.fuse_k = static_cast<int32_t>(s.top_k);
+    fa.fuse_y = y;
+  }
   // the permutation writes the FFN's group plan where it forms the offsets
   // (its scan pass, or its one block), and expert choice's where they are fixed:
   // no plan launch
@@ -713,7 +720,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
     if (e == hipSuccess) e = moe::launch_permute(pa, stream);
   }
   if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !moe::ffn_fuses_combine(fa)) {
     moe::CombineArgs a{};
     a.T = s.T;
     a.d = s.d;

@@ -71,6 +71,16 @@ struct StreamParams {
   const int32_t* active;     // [0]: groups with rows, [1..]: those groups
 };
 
+// The combine folded into the decode down GEMM (one token): its slots' rows,
+// gates and expert ids, and the layer output row.
+struct FusedCombine {
+  const int32_t* inv_map;   // [k] row of each routed slot, -1 dropped
+  const int32_t* topk_idx;  // [k]
+  const float* topk_w;      // [k]
+  int32_t k, n_shared;
+  void* y;                  // [d] bf16
+};
+
 // Bytes of k consecutive weights of a row: bf16 2k, e4m3 and int8 k, int4 k/2
 // (integer rows live at a pitch of ldb bytes whatever the expert's bit width).
 template <int WF>
@@ -651,6 +661,143 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(StreamParams p) {
   }
 }
 
+// One token (T = 1): the down GEMM with the combine folded in. Wave w owns
+// output columns [NC w, NC w + NC) and streams those W2 rows of every slot of
+// the token -- its routed slots in order (a dropped one is skipped), then the
+// shared experts -- against the slot's row of h, in 1 KB segments of each row
+// as the GEMV does. Each lane's sums are reduced across the wave in a fixed
+// order, then the slots are added with their gates in slot order (the
+// combine's order) and the layer output is written in bf16. The expert
+// outputs are not rounded to bf16 before that sum, as y_perm rows are.
+template <int WF, int S, int NC, int U>
+__global__ __launch_bounds__(kThreads) void gemv_combine_kernel(StreamParams p, FusedCombine f) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  static_assert(WF == kWBf16 || WF == kWE4m3, "bf16 or e4m3 weights");
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = w * NC;
+  if (n0 >= p.Nout) return;
+  constexpr int EB = pitch_bytes<WF>();
+  constexpr int KSEG = WF == kWBf16 ? kSeg / 2 : kSeg;  // k per segment
+  constexpr int XW = KSEG / 512;                        // activation uint4 per lane and segment
+  const int nseg = p.K / KSEG;
+  // slot s: group (-1: none), row of h, gate; all wave-uniform
+  int grp[S], hrow[S];
+  float gate[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    grp[s] = -1;
+    hrow[s] = 0;
+    gate[s] = 1.f;
+    if (s < f.k) {
+      const int r = f.inv_map[s];
+      if (r >= 0) {
+        grp[s] = f.topk_idx[s];
+        hrow[s] = r;
+        gate[s] = f.topk_w[s];
+      }
+    } else if (s < f.k + f.n_shared) {
+      grp[s] = p.n_routed + (s - f.k);
+      hrow[s] = p.groups[grp[s]].a_row0;
+    }
+    grp[s] = __builtin_amdgcn_readfirstlane(grp[s]);
+    hrow[s] = __builtin_amdgcn_readfirstlane(hrow[s]);
+  }
+  const char* wrow[S][NC];
+  const char* arow[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool shared = grp[s] >= p.n_routed;
+    const int ew = grp[s] < 0 ? 0 : (shared ? grp[s] - p.n_routed : grp[s]);
+    const char* base = (shared ? p.B_s : p.B_r) + (static_cast<int64_t>(ew) * p.b_stride + static_cast<int64_t>(n0) * p.ldb) * EB;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) wrow[s][c] = base + static_cast<int64_t>(c) * p.ldb * EB;
+    arow[s] = reinterpret_cast<const char*>(shared ? p.A_s : p.A_r) +
+              static_cast<int64_t>(hrow[s]) * (shared ? p.lda_s : p.lda_r) * 2;
+  }
+  const uint32_t wl = static_cast<uint32_t>(lane) * 16;
+  const uint32_t al = static_cast<uint32_t>(lane) * 16 * XW;
+  float acc[S][NC];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[s][c] = 0.f;
+
+  for (int s0 = 0; s0 < nseg; s0 += U) {
+    uint4 wv[U][S][NC], xv[U][S][XW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t sg = static_cast<uint32_t>(min(s0 + u, nseg - 1));  // a segment past the end re-reads the last one
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if (grp[s] < 0) continue;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) wv[u][s][c] = *reinterpret_cast<const uint4*>(wrow[s][c] + (wl + sg * kSeg));
+#pragma unroll
+        for (int x = 0; x < XW; ++x)
+          xv[u][s][x] = *reinterpret_cast<const uint4*>(arow[s] + (al + sg * (KSEG * 2) + 16 * x));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= nseg) break;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if (grp[s] < 0) continue;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          uint32_t wd[4 * XW];
+          if constexpr (WF == kWE4m3) {
+            const uint32_t q4[4] = {wv[u][s][c].x, wv[u][s][c].y, wv[u][s][c].z, wv[u][s][c].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint2 b = e4m3x4_to_bf16x4(q4[i]);
+              wd[2 * i] = b.x;
+              wd[2 * i + 1] = b.y;
+            }
+          } else {
+            wd[0] = wv[u][s][c].x; wd[1] = wv[u][s][c].y; wd[2] = wv[u][s][c].z; wd[3] = wv[u][s][c].w;
+          }
+          float a = acc[s][c];
+#pragma unroll
+          for (int x = 0; x < XW; ++x) {
+            const uint32_t xd[4] = {xv[u][s][x].x, xv[u][s][x].y, xv[u][s][x].z, xv[u][s][x].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[4 * x + i]),
+                                                  __builtin_bit_cast(bf16x2, xd[i]), a, false);
+          }
+          acc[s][c] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc[s][c] += __shfl_xor(acc[s][c], o);
+  // lane c < NC writes output column n0 + c: slots in order, each scaled (and
+  // biased, routed GELU experts) as its own output row would be
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (lane != c) continue;
+    float y = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (grp[s] < 0) continue;
+      const bool shared = grp[s] >= p.n_routed;
+      const int ew = shared ? grp[s] - p.n_routed : grp[s];
+      const float sc = wscale<WF>(p, shared, ew, p.scale_row0, n0 + c, p.scale_col);
+      const float b = (!shared && p.bias) ? p.bias[static_cast<int64_t>(ew) * p.Nout + n0 + c] : 0.f;
+      y += gate[s] * (acc[s][c] * sc + b);
+    }
+    static_cast<uint16_t*>(f.y)[n0 + c] = f32_to_bf16(y);
+  }
+}
+
 // k splits for one GEMM: double while the touched experts' blocks give fewer
 // than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
 // which is more than HBM latency times bandwidth needs) and every split keeps
@@ -765,6 +912,11 @@ SplitPlan plan_splits(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int3
 }
 
 }  // namespace
+
+bool ffn_fuses_combine(const FfnArgs& a) {
+  return a.fuse_y && a.T == 1 && a.act_dtype == 1 && (a.w_dtype == 1 || a.w_dtype == 2) && a.fuse_k >= 1 &&
+         a.fuse_k + a.n_shared <= 4 && use_skinny(a.act_dtype, a.routed_row_cap, a.n_shared, a.T) && use_gemv(a);
+}
 
 size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, int32_t n_shared, int32_t act,
                           int64_t cap, int32_t w_dtype) {
@@ -891,9 +1043,28 @@ hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupD
     p.part = nullptr;
   }
   stage_mark(kStageFfnDown, false, s);
-  e = run_classes([&](int wf) {
-    return gemv ? run_gemv(p, static_cast<int>(a.T), wf, slots, s) : run_stream(p, sp.rb, wf, down_blocks, s);
-  });
+  if (ffn_fuses_combine(a)) {  // one token: the combine runs in this launch
+    FusedCombine f{a.fuse_inv_map, a.fuse_topk_idx, a.fuse_topk_w, a.fuse_k, a.n_shared, a.fuse_y};
+    // one output column a wave, four segments of each slot's row a burst.
+    // Measured at the Mixtral shape (T = 1 step): 2 columns a wave with 8 or 4
+    // segments 143.6 us, 1 column with 8 segments 140.4, with 4 140.3; the
+    // separate combine 142.3-143.1.
+    constexpr int NC = 1;
+    const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(a.d, NC), kThreads / 64)));
+    const bool e4 = a.w_dtype == 2;
+    if (a.fuse_k + a.n_shared <= 2) {
+      if (e4) hipLaunchKernelGGL((gemv_combine_kernel<kWE4m3, 2, NC, 4>), grid, dim3(kThreads), 0, s, p, f);
+      else hipLaunchKernelGGL((gemv_combine_kernel<kWBf16, 2, NC, 4>), grid, dim3(kThreads), 0, s, p, f);
+    } else {
+      if (e4) hipLaunchKernelGGL((gemv_combine_kernel<kWE4m3, 4, NC, 2>), grid, dim3(kThreads), 0, s, p, f);
+      else hipLaunchKernelGGL((gemv_combine_kernel<kWBf16, 4, NC, 4>), grid, dim3(kThreads), 0, s, p, f);
+    }
+    e = hipGetLastError();
+  } else {
+    e = run_classes([&](int wf) {
+      return gemv ? run_gemv(p, static_cast<int>(a.T), wf, slots, s) : run_stream(p, sp.rb, wf, down_blocks, s);
+    });
+  }
   if (e == hipSuccess && p.part) {
     const dim3 rgrid(static_cast<unsigned>(ceil_div(p.Nout, kRedCols)), static_cast<unsigned>(p.rows_total));
     hipLaunchKernelGGL(stream_reduce_kernel, rgrid, dim3(kThreads), 0, s, p, a.offsets, a.routed_row_cap);

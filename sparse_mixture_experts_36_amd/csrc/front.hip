@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(RouteArgs ra, Perm
   route_block<NT>(ra, t, live, lg, 0, true, s_topk);
   __syncthreads();  // this block's top-k lists are in LDS
 
-  perm_rank_block<kRouteThreads>(pa, 0, 1, s_topk);
+  perm_rank_block<kRouteThreads, true>(pa, 0, 1, s_topk);
 }
 
 }  // namespace

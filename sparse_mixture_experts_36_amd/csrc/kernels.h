@@ -148,6 +148,14 @@ struct FfnArgs {
   float *pre_up_u, *pre_up_v;
   int64_t ld_pre_up;
   bool up_only;  // the up GEMM alone (h and the copies above; no y)
+  // one token, decode path: the combine folded into the down GEMM (see
+  // ffn_fuses_combine), which then writes the layer output row fuse_y (bf16)
+  // from the slots' rows (fuse_inv_map), experts and gates instead of y_perm
+  const int32_t* fuse_inv_map;
+  const int32_t* fuse_topk_idx;
+  const float* fuse_topk_w;
+  int32_t fuse_k;
+  void* fuse_y;
 };
 // Whether the 256-column LDS-DMA tiles fit a layer: each GEMM's output width a
 // multiple of the columns a tile yields (256; the SwiGLU up tile yields 128 of
@@ -204,6 +212,10 @@ size_t skinny_part_floats(int64_t T, int64_t d, int64_t d_ff, int32_t n_routed, 
                           int64_t cap, int32_t w_dtype);
 hipError_t launch_ffn_skinny(const FfnArgs& a, const GroupDesc* up, const GroupDesc* down, float* part,
                              hipStream_t s);
+// Whether the decode down GEMM writes the layer output itself (fuse_y set,
+// one token, bf16 or e4m3 weights on the GEMV path, k + n_shared <= 4): the
+// caller then runs no combine.
+bool ffn_fuses_combine(const FfnArgs& a);
 
 // ---------------------------------------------------------------- backward GEMM
 // C_g(m, n) (+)= sum_k A_g(m, k) B_g(k, n), bf16 operands, fp32 accumulation and output.

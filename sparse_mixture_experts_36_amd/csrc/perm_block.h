@@ -19,9 +19,9 @@ constexpr int kPermMaxK = 8;
 // Rank of the pairs of permutation block `bid` (of nblocks) by NTH threads:
 // the first four waves hold its 256 tokens (one a lane), further waves only
 // join the barriers and the block-wide loops.
-// topk, when given, holds the block's top-k lists in LDS ([token][k], as
-// a.topk_idx) and is read instead of a.topk_idx.
-template <int NTH>
+// TOPK_LDS: topk_lds holds the block's top-k lists in LDS ([token][k], as
+// a.topk_idx, at most 16 tokens) and is read instead of a.topk_idx.
+template <int NTH, bool TOPK_LDS = false>
 __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, int nblocks,
                                                 const int32_t* topk_lds = nullptr) {
   __shared__ int32_t s_wcnt[4][kPermMaxN];
@@ -34,12 +34,19 @@ __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, i
 
   int ex[kPermMaxK], rank[kPermMaxK];
   uint64_t rem[kPermMaxK];
+  int lk[kPermMaxK];  // the LDS lists, read before any use (the addresses are LDS, so no flat loads)
+  if constexpr (TOPK_LDS) {
+    const auto* tl = (const __attribute__((address_space(3))) int32_t*)(topk_lds);
+    const int tt = live ? static_cast<int>(t - static_cast<int64_t>(bid) * kPermTokens) : 0;
+#pragma unroll
+    for (int j = 0; j < kPermMaxK; ++j) lk[j] = j < k ? tl[tt * k + j] : -1;
+  }
 #pragma unroll
   for (int j = 0; j < kPermMaxK; ++j) {
     ex[j] = -1;
     rank[j] = 0;
     if (j < k && live) {
-      const int e = topk_lds ? topk_lds[(t - static_cast<int64_t>(bid) * kPermTokens) * k + j] : a.topk_idx[t * k + j];
+      const int e = TOPK_LDS ? lk[j] : a.topk_idx[t * k + j];
       ex[j] = (e >= 0 && e < N) ? e : -1;  // out-of-range ids are treated as dropped
     }
     rem[j] = (j < k) ? __ballot(ex[j] >= 0) : 0ull;

@@ -141,6 +141,12 @@ REDUCED = {
                                                                     n_shared=1, zipf_s=1.0),
     # decode-sized: the weight-streaming path
     "mixtral-like-decode-T1": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=1536),
+    # one token: the combine folded into the down GEMV (k + shared <= 4 slots,
+    # bf16 or e4m3), dropped slots skipped; more slots take the separate combine
+    "decode-T1-fused-fp8-gelu-shared": gen.SWITCH_TOP1_FP8.with_(T=1, d=1024, d_ff=2048, n_shared=1),
+    "decode-T1-fused-k2-shared2": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=1024, top_k=2),
+    "decode-T1-fused-all-dropped-shared2": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=1024, top_k=2, capacity_factor=0.0),
+    "decode-T1-k6-shared2-separate-combine": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=1024),
     "mixtral-like-decode-T64": gen.MIXTRAL_PREFILL.with_(T=64, d=1024, d_ff=1536),
     "fine-grained-like-decode": gen.FINE_GRAINED.with_(T=24, d=512, d_ff=256),
     "fine-grained-like-decode-T2": gen.FINE_GRAINED.with_(T=2, d=512, d_ff=1024),  # GEMV: two rows, shared experts
