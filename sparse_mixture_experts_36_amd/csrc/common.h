@@ -130,6 +130,31 @@ __device__ __forceinline__ void quad_transpose_bf16(uint32_t c01, uint32_t c23, 
   r23 = __builtin_amdgcn_perm(x, q1, odd ? 0x03020706u : 0x07060100u);
 }
 
+// Lane exchanges inside each row of 16 lanes by DPP (no LDS round trip, as
+// a __shfl through ds_bpermute takes): step 0 rotates the row by 8, step 1 by
+// 4, step 2 swaps lanes at distance 2, step 3 neighbours. After the four
+// steps of an all-reduce with a commutative, associative merge every lane of
+// the row holds the result of all 16, and the lanes of a row combine their
+// operands in the same pairs, so they agree bit for bit.
+template <int STEP>
+__device__ __forceinline__ int dpp_row16(int v) {
+  static_assert(STEP >= 0 && STEP < 4, "four steps");
+  constexpr int kCtrl = STEP == 0 ? 0x128 : STEP == 1 ? 0x124 : STEP == 2 ? 0x4E : 0xB1;  // row_ror:8, row_ror:4, quad [2,3,0,1], quad [1,0,3,2]
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ float dpp_row16(float v) {
+  return __int_as_float(dpp_row16<STEP>(__float_as_int(v)));
+}
+// Sum over each row of 16 lanes (every lane gets the row's sum).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_row16<0>(v);
+  v += dpp_row16<1>(v);
+  v += dpp_row16<2>(v);
+  v += dpp_row16<3>(v);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -68,7 +68,7 @@ __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, i
     int v = -1;
 #pragma unroll
     for (int j = 0; j < kPermMaxK; ++j)
-      if (j == j0) v = __shfl(ex[j], src);
+      if (j == j0) v = __builtin_amdgcn_readlane(ex[j], src);  // src is wave-uniform
     uint64_t m = 0;
 #pragma unroll
     for (int j = 0; j < kPermMaxK; ++j) {

@@ -138,15 +138,18 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool 
         b.e = e;
       }
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(b.v, o, 16);
-      const int e2 = __shfl_xor(b.e, o, 16);
+    // 16-lane arg-max by DPP exchanges (the order of the pairs does not
+    // change the result: `better` is a total order)
+    auto merge = [&](float v2, int e2) __attribute__((always_inline)) {
       if (e2 != 0x7fffffff && (b.e == 0x7fffffff || better(v2, e2, b.v, b.e))) {
         b.v = v2;
         b.e = e2;
       }
-    }
+    };
+    merge(dpp_row16<0>(b.v), dpp_row16<0>(b.e));
+    merge(dpp_row16<1>(b.v), dpp_row16<1>(b.e));
+    merge(dpp_row16<2>(b.v), dpp_row16<2>(b.e));
+    merge(dpp_row16<3>(b.v), dpp_row16<3>(b.e));
     selv[j] = b.v;
     sele[j] = b.e;
     if ((b.e & 15) == c16) taken |= 1u << (b.e >> 4);
@@ -157,8 +160,7 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
     if (16 * nt + c16 < N) s += expf(lg[nt] - m);
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  s = row16_sum(s);
   const float inv_s = 1.0f / s;
   const float lse = m + logf(s);
   float pacc[NT];
@@ -202,8 +204,11 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool 
     if (q == 0) s_P[wave][16 * nt + c16] = v;
   }
   {
-    const float a1 = __shfl(lse_s, 0) + __shfl(lse_s, 16) + __shfl(lse_s, 32) + __shfl(lse_s, 48);
-    const float a2 = __shfl(lse_sq, 0) + __shfl(lse_sq, 16) + __shfl(lse_sq, 32) + __shfl(lse_sq, 48);
+    auto at = [](float v, int l) __attribute__((always_inline)) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+    };
+    const float a1 = at(lse_s, 0) + at(lse_s, 16) + at(lse_s, 32) + at(lse_s, 48);
+    const float a2 = at(lse_sq, 0) + at(lse_sq, 16) + at(lse_sq, 32) + at(lse_sq, 48);
     if (lane == 0) {
       s_lse[wave][0] = a1;
       s_lse[wave][1] = a2;
