@@ -437,14 +437,15 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 1
 // 4 (l / 16) + l % 4, stored as 8 bytes.
 template <int EPI, int BM, int W>
 __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileInfo& ti,
-                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN]) {
+                                               floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN],
+                                               int wave) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
   constexpr int WTB = C_::WTB, FN = C_::FN, FM = C_::FM, WGN = C_::WGN, WTM = C_::WTM;
   constexpr int WTO = EPI == EPI_SWIGLU ? WTB / 2 : WTB;
   constexpr int FNO = WTO / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15, t = lane & 3;
   const bool shared = ti.g >= p.n_routed;
@@ -493,7 +494,7 @@ __device__ __forceinline__ void dma_store_tile(const GemmParams& p, const TileIn
 // straight from the fragments (16 lanes write 64 contiguous bytes of a row).
 template <int EPI, int BM, int W>
 __device__ __forceinline__ void dma_store_pre(const GemmParams& p, const TileInfo& ti,
-                                              floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN]) {
+                                              floatx4_t (&acc)[dma::Cfg<BM, W>::FM][dma::Cfg<BM, W>::FN], int wave) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
@@ -504,7 +505,7 @@ __device__ __forceinline__ void dma_store_pre(const GemmParams& p, const TileInf
   float* pu = shared ? p.pre_u_s : p.pre_u_r;
   if (!pu) return;
   float* pv = EPI == EPI_SWIGLU ? (shared ? p.pre_v_s : p.pre_v_r) : nullptr;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
   const int q = lane >> 4, c16 = lane & 15;
   const int ew = shared ? ti.gd.widx - p.n_routed : ti.gd.widx;
@@ -832,8 +833,8 @@ __device__ __forceinline__ void dma_tile_body(const GemmParams& p, const TileInf
         *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
-  dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W>(p, ti, acc);
+  dma_store_pre<EPI, BM, W>(p, ti, acc, wave);
+  dma_store_tile<EPI, BM, W>(p, ti, acc, wave);
 }
 
 template <int EPI, int BM, int W, int WF>
@@ -1104,42 +1105,62 @@ __global__ __launch_bounds__(512, 1) void gemm_dma5_kernel(GemmParams p) {
         *reinterpret_cast<floatx4_t*>(dma_part_frag<BM, W>(p.split_part, unit, wave, i, j) + lane * 4) = acc[i][j];
     return;
   }
-  dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W>(p, ti, acc);
+  dma_store_pre<EPI, BM, W>(p, ti, acc, wave);
+  dma_store_tile<EPI, BM, W>(p, ti, acc, wave);
 }
 
-// Fix-up of the k-split tiles: workgroup b takes split tile b, sums its s
-// partial tiles in chunk order and runs the tile epilogue.
+// Fix-up of the k-split tiles: one wave per (split tile, wave of the tile's
+// layout), kFixWaves waves a workgroup, so the r split tiles spread over W r
+// waves on as many CUs instead of one workgroup each. A wave sums its
+// fragments' s partial tiles in chunk order and runs that wave's part of the
+// tile epilogue.
+constexpr int kFixWaves = 4;
 template <int EPI, int BM, int W>
-__global__ __launch_bounds__(64 * W, 1) void gemm_split_fixup_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * kFixWaves) void gemm_split_fixup_kernel(GemmParams p) {
   using namespace dma;
   using C_ = Cfg<BM, W>;
   constexpr int BNO = bno(EPI);
   constexpr int FM = C_::FM, FN = C_::FN;
   const SplitPlan sp = split_plan<BNO>(p, p.K / BK / 2);
-  const int b = blockIdx.x;
+  const int gw = blockIdx.x * kFixWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = gw / W, wave = gw % W;
   if (sp.s == 1 || b >= sp.r) return;
   TileInfo ti;
   tile_from_linear<BM, BNO>(p, sp.full + b, ti);
   if ((p.skip[ti.g >> 5] >> (ti.g & 31)) & 1u) return;  // the other bit width's launch takes this group
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // two chunks in flight: the loads of chunk c + 1 are issued before chunk c
+  // is added (the adds stay in chunk order); the 256-row tile's fragments go
+  // in two halves, so that two chunks of them fit the registers
+  constexpr int FG = FM * FN > 16 ? FM / 2 : FM;  // fragment rows a pass
   floatx4_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i0 = 0; i0 < FM; i0 += FG) {
+    floatx4_t b0[FG][FN], b1[FG][FN];
+    auto load = [&](floatx4_t (&dst)[FG][FN], int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM, W>(p.split_part, b * sp.s, wave, i, j) +
-                                                      lane * 4);
-  for (int c = 1; c < sp.s; ++c) {
+      for (int i = 0; i < FG; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
+          dst[i][j] = *reinterpret_cast<const floatx4_t*>(
+              dma_part_frag<BM, W>(p.split_part, b * sp.s + c, wave, i0 + i, j) + lane * 4);
+    };
+    auto add = [&](const floatx4_t (&src)[FG][FN], bool first) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] += *reinterpret_cast<const floatx4_t*>(dma_part_frag<BM, W>(p.split_part, b * sp.s + c, wave, i, j) +
-                                                         lane * 4);
+      for (int i = 0; i < FG; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i0 + i][j] = first ? src[i][j] : acc[i0 + i][j] + src[i][j];
+    };
+    load(b0, 0);
+    for (int c = 0; c < sp.s; c += 2) {  // s >= 2
+      if (c + 1 < sp.s) load(b1, c + 1);
+      add(b0, c == 0);
+      if (c + 2 < sp.s) load(b0, c + 2);
+      if (c + 1 < sp.s) add(b1, false);
+    }
   }
-  dma_store_pre<EPI, BM, W>(p, ti, acc);
-  dma_store_tile<EPI, BM, W>(p, ti, acc);
+  dma_store_pre<EPI, BM, W>(p, ti, acc, wave);
+  dma_store_tile<EPI, BM, W>(p, ti, acc, wave);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -1272,7 +1293,8 @@ hipError_t run_dma(const GemmParams& p_in, int64_t max_mtiles, hipStream_t s) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // split tiles: r <= kSplitUnits / 2 (each is cut at least in two)
-    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, BM, W>), dim3(kSplitUnits / 2), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, BM, W>), dim3(kSplitUnits / 2 * W / kFixWaves),
+                       dim3(64 * kFixWaves), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -1292,7 +1314,8 @@ hipError_t run_dma5(const GemmParams& p, int64_t max_mtiles, hipStream_t s) {
     if (err != hipSuccess) return err;
     // split tiles: r <= kSplitUnits / 2 (each is cut at least in two); the
     // partial tiles have the fragment layout of dma::Cfg<256, 8>
-    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, 256, 8>), dim3(kSplitUnits / 2), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<EPI, 256, 8>), dim3(kSplitUnits / 2 * 8 / kFixWaves),
+                       dim3(64 * kFixWaves), 0, s, p);
   }
   return hipGetLastError();
 }
