@@ -21,12 +21,92 @@ constexpr int kFrontMaxNT = 4;    // 16-expert column blocks (64 experts)
 constexpr int kFrontWaves = kRouteThreads / 64;
 static_assert(kFrontWaves == 16, "the k range is cut in 16 wave slices");
 
+// One token: after the router GEMM, wave 0 alone routes it and builds the
+// permutation (the general blocks' barriers and block reductions are not
+// needed for one token), then the workgroup writes the FFN group plan. The
+// outputs are those of route_block and perm_rank_block for a block holding
+// only token 0, computed the same way: the token's routing by route_token
+// (its quarters all hold the same logits, so every lane ends with the same
+// selection), statistics from the one token's probabilities and log-sum-exp,
+// the offsets as an exclusive scan of the kept counts over the expert lanes.
+template <int NT>
+__device__ __forceinline__ void front_one(const RouteArgs& ra, const PermuteArgs& pa, const float* logit) {
+  __shared__ int32_t s_off[kPermMaxN + 1];
+  __shared__ double s_fp[16 * kFrontMaxNT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = ra.N, k = ra.k;
+  if (wave == 0) {
+    const int c16 = lane & 15;
+    float lg[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lg[nt] = logit[16 * nt + c16];
+    int sele[8];
+    float pacc[NT], lse;
+    route_token<NT>(ra, 0, lane < 16, lg, c16, nullptr, sele, pacc, lse);
+    // statistics: count, f and P of each expert, then L_aux and z (T = 1)
+    if (lane < 16) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = 16 * nt + c16;
+        if (e >= N) continue;
+        int c = 0;
+        for (int j = 0; j < k; ++j) c += sele[j] == e;
+        finalize_expert(ra, e, static_cast<double>(pacc[nt]), c, s_fp);
+      }
+    }
+    if (lane == 0) finalize_scalars(ra, s_fp, static_cast<double>(lse), static_cast<double>(lse * lse));
+    // permutation: expert e on lane e (N <= 64), kept counts, their
+    // exclusive scan, the token's slots
+    int cnt = 0;
+    for (int j = 0; j < k; ++j) cnt += sele[j] == lane;
+    const int kept = (pa.capacity >= 0 && cnt > pa.capacity) ? static_cast<int>(pa.capacity) : cnt;
+    if (lane < N) {
+      pa.block_base[lane] = 0;
+      pa.kept[lane] = kept;
+    }
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const int off = incl - kept;
+    if (lane < N) {
+      s_off[lane] = off;
+      pa.offsets[lane] = off;
+    }
+    const int total = __shfl(incl, 63);
+    int drop = cnt - kept;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
+    if (lane == 0) {
+      s_off[N] = total;
+      pa.offsets[N] = total;
+      *pa.n_dropped = drop;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = __shfl(off, sele[j]);  // the token is its expert's first row
+      if (lane == 0) {
+        pa.local_rank[j] = 0;
+        const int32_t slot = (pa.capacity < 0 || pa.capacity > 0) ? row : -1;
+        pa.inv_map[j] = slot;
+        if (slot >= 0) pa.perm_token[slot] = 0;
+      }
+    }
+  }
+  __syncthreads();  // the offsets are in LDS
+  if (pa.plan.up) {
+    __shared__ int32_t s_mt[2 * kMaxGroups];
+    plan_groups(s_off, pa.plan, s_mt, tid, kRouteThreads);
+  }
+}
+
 // Router GEMM: wave w takes k [w d/16, (w + 1) d/16) of every token and
 // expert as MFMA 16x16x32 products (tokens as rows, clamped to T - 1; experts
 // 16 nt + c16 as columns), with SB k-steps of loads in flight; the 16 wave
 // partials are then summed in wave order (fixed, so the logits are
 // reproducible bit for bit). Then the routing of the 16-token block and the
-// one-block permutation, as in the general kernels.
+// one-block permutation, as in the general kernels (one token: front_one).
 template <int NT>
 __global__ __launch_bounds__(kRouteThreads) void front_kernel(RouteArgs ra, PermuteArgs pa) {
   __shared__ floatx4_t s_part[kFrontWaves][NT][64];
@@ -83,6 +163,10 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(RouteArgs ra, Perm
     s_logit[t][e] = v;
   }
   __syncthreads();
+  if (T == 1) {
+    front_one<NT>(ra, pa, s_logit[0]);
+    return;
+  }
 
   // routing: token 4 w + q in the lanes of quarter q of wave w (waves 0..3)
   const int64_t t = wave * 4 + q;

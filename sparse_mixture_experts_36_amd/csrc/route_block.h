@@ -91,43 +91,23 @@ __device__ __forceinline__ void token_logits(const RouteArgs& a, const float* pa
   }
 }
 
-// Softmax / top-k / gates / block statistics over 64 tokens, one per
-// quarter-wave (16 waves): lane (q, c16) of wave w holds the logits of token
-// 4w + q for experts 16 nt + c16, so every per-token step is a 16-lane
-// reduction and no wave walks tokens one after another. Logits are the given
-// ones, or the sum of the k-split partial logits (in split order) plus the
-// router bias, which is then also stored as the router output. A launch of one
-// workgroup (T <= 64) also finishes the statistics itself.
-
-// The routing of one block of kRouteTokens tokens, run by all kRouteThreads
-// threads: token t of lane (q, c16) of wave w (t = the block's first token +
-// 4 w + q) arrives with its logits lg[nt] of experts 16 nt + c16. Block b
-// writes its statistics partials, or, when it is the only block (last), the
-// final statistics.
-// With topk_lds, the token's top-k list is also kept there ([t - first][k]).
+// The routing of one token, held by the 16 lanes of a quarter-wave: lane
+// c16 holds the logits lg[nt] of experts 16 nt + c16. Top-k selection (k
+// rounds of a 16-lane arg-max under `better`), softmax over all N (the largest
+// logit is the first selected one), gates in the call's gating mode. When
+// live, the token's top-k list and gates are stored (topk_row: an LDS copy of
+// the list, or null). Every lane of the quarter returns the selected experts;
+// pacc[nt] is its experts' probability (0 when not live), lse the token's
+// log-sum-exp (0 when not live).
 template <int NT>
-__device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool live, const float (&lg)[NT], int b,
-                                            bool last, int32_t* topk_lds = nullptr) {
-  __shared__ int32_t s_cnt[kRouteMaxN];
-  __shared__ float s_P[kRouteWaves][kRouteMaxN];
-  __shared__ float s_lse[kRouteWaves][2];
-  __shared__ double s_fp[kRouteMaxN];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, c16 = lane & 15;
-  (void)q;
+__device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, bool live, const float (&lg)[NT], int c16,
+                                            int32_t* topk_row, int (&sele)[8], float (&pacc)[NT], float& lse_out) {
   const int N = a.N, k = a.k;
-
-  for (int e = tid; e < kRouteMaxN; e += kRouteThreads) s_cnt[e] = 0;
-  __syncthreads();  // s_cnt cleared before any count below
-
-  // selection: k rounds of a 16-lane arg-max under `better`
   uint32_t taken = 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
     if (16 * nt + c16 >= N) taken |= 1u << nt;
   float selv[8];
-  int sele[8];
   for (int j = 0; j < k; ++j) {
     Sel b{-FLT_MAX, 0x7fffffff};
 #pragma unroll
@@ -163,10 +143,9 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool 
   s = row16_sum(s);
   const float inv_s = 1.0f / s;
   const float lse = m + logf(s);
-  float pacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) pacc[nt] = (live && 16 * nt + c16 < N) ? expf(lg[nt] - m) * inv_s : 0.f;
-  const float lse_s = live ? lse : 0.f, lse_sq = live ? lse * lse : 0.f;
+  lse_out = live ? lse : 0.f;
   if (live) {
     float g[8];
     if (a.gating == 0) {
@@ -189,11 +168,50 @@ __device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool 
     for (int j = 0; j < k; ++j)
       if (c16 == j) {
         a.topk_idx[t * k + j] = sele[j];
-        if (topk_lds) topk_lds[(t - static_cast<int64_t>(b) * kRouteTokens) * k + j] = sele[j];
+        if (topk_row) topk_row[j] = sele[j];
         a.topk_w[t * k + j] = g[j];
-        atomicAdd(&s_cnt[sele[j]], 1);
       }
   }
+}
+
+// Softmax / top-k / gates / block statistics over 64 tokens, one per
+// quarter-wave (16 waves): lane (q, c16) of wave w holds the logits of token
+// 4w + q for experts 16 nt + c16, so every per-token step is a 16-lane
+// reduction and no wave walks tokens one after another. Logits are the given
+// ones, or the sum of the k-split partial logits (in split order) plus the
+// router bias, which is then also stored as the router output. A launch of one
+// workgroup (T <= 64) also finishes the statistics itself.
+
+// The routing of one block of kRouteTokens tokens, run by all kRouteThreads
+// threads: token t of lane (q, c16) of wave w (t = the block's first token +
+// 4 w + q) arrives with its logits lg[nt] of experts 16 nt + c16. Block b
+// writes its statistics partials, or, when it is the only block (last), the
+// final statistics.
+// With topk_lds, the token's top-k list is also kept there ([t - first][k]).
+template <int NT>
+__device__ __forceinline__ void route_block(const RouteArgs& a, int64_t t, bool live, const float (&lg)[NT], int b,
+                                            bool last, int32_t* topk_lds = nullptr) {
+  __shared__ int32_t s_cnt[kRouteMaxN];
+  __shared__ float s_P[kRouteWaves][kRouteMaxN];
+  __shared__ float s_lse[kRouteWaves][2];
+  __shared__ double s_fp[kRouteMaxN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  (void)q;
+  const int N = a.N, k = a.k;
+
+  for (int e = tid; e < kRouteMaxN; e += kRouteThreads) s_cnt[e] = 0;
+  __syncthreads();  // s_cnt cleared before any count below
+
+  int sele[8];
+  float pacc[NT], lse;
+  route_token<NT>(a, t, live, lg, c16, topk_lds ? topk_lds + (t - static_cast<int64_t>(b) * kRouteTokens) * k : nullptr,
+                  sele, pacc, lse);
+  if (live)
+    for (int j = 0; j < k; ++j)
+      if (c16 == j) atomicAdd(&s_cnt[sele[j]], 1);
+  const float lse_s = lse, lse_sq = lse * lse;
 
   // ---- block totals, fixed order: the wave's four tokens (xor 16, 32), then waves in order
 #pragma unroll
