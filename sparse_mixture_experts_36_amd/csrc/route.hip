@@ -26,6 +26,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxN = 256;
+// s_waitcnt immediate: vmcnt(n), no wait on expcnt and lgkmcnt
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // Router GEMM over one k range: partial logits of 64 tokens (4 waves x 16) for
 // all experts. Grid (token blocks, k splits). bf16 runs on MFMA with the
@@ -129,6 +131,102 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(RouteArgs a, floa
       }
     }
   }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = 16 * nt + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * q + i;
+      if (t < T && e < N) out[t * N + e] = acc[nt][i];
+    }
+  }
+}
+
+// Router GEMM for prefill-sized calls (bf16): the same products and output
+// layout as router_gemm_kernel, with more loads in flight. k-stages of 64:
+// the router-weight rows of a stage (16 NT experts, padded to RP rows, 128
+// bytes each, 16-byte chunk c of row r at c ^ (r & 7)) go to a ring of NS
+// LDS buffers by global_load_lds, NS - 1 stages ahead; each wave loads its 16
+// tokens' fragments of the same stages into registers, as far ahead. One
+// barrier per stage. Expert rows past N load row N - 1 (computed, never
+// stored). k_len is a multiple of 64 with at least NS - 1 stages.
+template <int NT, int NS>
+__global__ __launch_bounds__(kThreads) void router_gemm_dma_kernel(RouteArgs a, float* part, int k_len) {
+  constexpr int RP = (NT + 1) / 2 * 32;  // weight rows of a stage: 8 per DMA instruction, the same count per wave
+  constexpr int DI = RP / 32;            // DMA instructions per wave and stage
+  constexpr int SB = RP * 128;           // stage bytes
+  __shared__ __attribute__((aligned(16))) char wbuf[NS][SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, c16 = lane & 15;
+  const int N = a.N;
+  const int64_t T = a.T, d = a.d;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens + wave * 16;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * k_len;
+  float* out = part + static_cast<int64_t>(blockIdx.y) * T * N;
+  const int n_st = k_len / 64;
+
+  // DMA sources: instruction i of this wave fills rows 32 i + 8 wave + lane / 8
+  const char* wr = static_cast<const char*>(a.w_router) + k0 * 2;
+  uint32_t woff[DI];
+#pragma unroll
+  for (int i = 0; i < DI; ++i) {
+    const int r = 32 * i + 8 * wave + (lane >> 3);
+    const int e = r < N ? r : N - 1;
+    const int chunk = (lane & 7) ^ (r & 7);
+    woff[i] = static_cast<uint32_t>(e * static_cast<int>(d) * 2 + chunk * 16);
+  }
+  // token fragments: lane (row c16, k-group q) takes k 8 q .. 8 q + 7 of each 32-wide half of a stage
+  int64_t trow = t0 + c16;
+  if (trow > T - 1) trow = T - 1;  // rows past T compute garbage that is never stored
+  const char* xr = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.x) + trow * d + k0 + q * 8);
+  // LDS read offsets of the two 32-wide halves: row 16 nt + c16, logical chunk 4 h + q
+  int rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) rd[h] = c16 * 128 + (((4 * h + q) ^ (c16 & 7)) * 16);
+
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 xf[NS][2];
+#define MOE_RDMA(S, ks)                                                                              \
+  do {                                                                                               \
+    const uint32_t ko_ = static_cast<uint32_t>(ks) * 128;                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < DI; ++i_)                                                \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wr + (woff[i_] + ko_)),            \
+                                         (__attribute__((address_space(3))) void*)(&wbuf[S][(32 * i_ + 8 * wave) * 128]), \
+                                         16, 0, 0);                                                  \
+    _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                                 \
+        xf[S][h_] = *reinterpret_cast<const uint4*>(xr + static_cast<int64_t>(ks) * 128 + h_ * 64); \
+  } while (0)
+  // stage ks in slot S: wait until only the newer NS - 2 stages' loads may
+  // fly, barrier (every wave's DMA of stage ks has landed, and every wave is
+  // done reading slot (ks - 1) mod NS), refill that slot with stage ks + NS - 1
+  // (the last stage again past the end), then the products of stage ks
+#define MOE_RSTAGE(S, ks)                                                                            \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * (DI + 2)));                                      \
+    __builtin_amdgcn_s_waitcnt(0xc07f);                                                              \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    asm volatile("" ::: "memory"); /* no LDS read moves above the barrier */                        \
+    MOE_RDMA(((S) + NS - 1) % NS, min((ks) + NS - 1, n_st - 1));                                      \
+    _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                                 \
+        _Pragma("unroll") for (int nt_ = 0; nt_ < NT; ++nt_) acc[nt_] =                              \
+            mfma16x16x32(xf[S][h_], *reinterpret_cast<const uint4*>(&wbuf[S][nt_ * 2048 + rd[h_]]), acc[nt_]); \
+  } while (0)
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) MOE_RDMA(s0, s0);
+  const int n_round = n_st / NS * NS;
+  for (int ks = 0; ks < n_round; ks += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) MOE_RSTAGE(u, ks + u);
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (n_round + u < n_st) MOE_RSTAGE(u, n_round + u);
+#undef MOE_RSTAGE
+#undef MOE_RDMA
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing refills have landed
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int e = 16 * nt + c16;
@@ -503,15 +601,28 @@ hipError_t launch_nt(const RouteArgs& a, int nb, int splits, hipStream_t s) {
     const int kr = router_kstep(a.T, a.d, a.N);
     const dim3 grid(nb, splits);
     const int k_len = static_cast<int>(a.d / splits);
-    if constexpr (NT <= 4) {  // the 256-wide weight tile fits LDS for at most 64 experts
-      if (kr == 256) hipLaunchKernelGGL((router_gemm_kernel<NT, 256>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+    // prefill sizes, bf16: the LDS-DMA kernel, five stages ahead (three with
+    // more than 160 experts, whose stages are larger)
+    constexpr int NS = (NT + 1) / 2 * 32 <= 160 ? 6 : 4;
+    if (a.T >= 1024 && a.act_dtype == 1 && k_len % 64 == 0 && k_len / 64 >= NS - 1) {
+      hipLaunchKernelGGL((router_gemm_dma_kernel<NT, NS>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      if constexpr (NT <= 4) {  // the 256-wide weight tile fits LDS for at most 64 experts
+        if (kr == 256)
+          hipLaunchKernelGGL((router_gemm_kernel<NT, 256>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+      }
+      if (kr == 256) {
+        if constexpr (NT > 4) return hipErrorInvalidValue;
+      } else if (kr == 128) {
+        hipLaunchKernelGGL((router_gemm_kernel<NT, 128>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+      } else {
+        hipLaunchKernelGGL((router_gemm_kernel<NT, 64>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
+      }
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
-    if (kr == 256) {
-      if constexpr (NT > 4) return hipErrorInvalidValue;
-    } else if (kr == 128) hipLaunchKernelGGL((router_gemm_kernel<NT, 128>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
-    else hipLaunchKernelGGL((router_gemm_kernel<NT, 64>), grid, dim3(kThreads), 0, s, a, a.part_logits, k_len);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
   if (a.ec)
     hipLaunchKernelGGL(route_ec_kernel<NT>, dim3(nb), dim3(kRouteThreads), 0, s, a, a.part_logits, splits);
