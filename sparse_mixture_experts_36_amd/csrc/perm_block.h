@@ -25,15 +25,19 @@ template <int NTH, bool TOPK_LDS = false>
 __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, int nblocks,
                                                 const int32_t* topk_lds = nullptr) {
   __shared__ int32_t s_wcnt[4][kPermMaxN];
+  // per wave and expert: the lanes (tokens) that selected it
+  __shared__ unsigned long long s_mask[4][kPermMaxN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, k = a.k;
   const int64_t t = static_cast<int64_t>(bid) * kPermTokens + wave * 64 + lane;
   const bool live = wave < 4 && t < a.T;
 
-  for (int i = tid; i < 4 * kPermMaxN; i += NTH) (&s_wcnt[0][0])[i] = 0;
+  for (int i = tid; i < 4 * kPermMaxN; i += NTH) {
+    (&s_wcnt[0][0])[i] = 0;
+    (&s_mask[0][0])[i] = 0ull;
+  }
 
   int ex[kPermMaxK], rank[kPermMaxK];
-  uint64_t rem[kPermMaxK];
   int lk[kPermMaxK];  // the LDS lists, read before any use (the addresses are LDS, so no flat loads)
   if constexpr (TOPK_LDS) {
     const auto* tl = (const __attribute__((address_space(3))) int32_t*)(topk_lds);
@@ -49,38 +53,26 @@ __device__ __forceinline__ void perm_rank_block(const PermuteArgs& a, int bid, i
       const int e = TOPK_LDS ? lk[j] : a.topk_idx[t * k + j];
       ex[j] = (e >= 0 && e < N) ? e : -1;  // out-of-range ids are treated as dropped
     }
-    rem[j] = (j < k) ? __ballot(ex[j] >= 0) : 0ull;
   }
   __syncthreads();
 
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (;;) {
-    int j0 = -1;
+  // Rank of pair (token, slot j) among the wave's pairs of its expert: the
+  // lanes below it whose token selected the same expert. Each lane ORs its
+  // bit into the masks of its experts (the OR does not depend on the order),
+  // then counts the set bits below it. The wave's count of an expert is the
+  // population of its mask.
+  if (wave < 4) {
+    const unsigned long long bit = 1ull << lane;
 #pragma unroll
     for (int j = 0; j < kPermMaxK; ++j)
-      if (j0 < 0 && rem[j] != 0ull) j0 = j;
-    if (j0 < 0) break;
-    uint64_t r0 = 0;
+      if (ex[j] >= 0) atomicOr(&s_mask[wave][ex[j]], bit);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's ORs are done
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long below = bit - 1ull;
 #pragma unroll
     for (int j = 0; j < kPermMaxK; ++j)
-      if (j == j0) r0 = rem[j];
-    const int src = __builtin_ctzll(r0);
-    int v = -1;
-#pragma unroll
-    for (int j = 0; j < kPermMaxK; ++j)
-      if (j == j0) v = __builtin_amdgcn_readlane(ex[j], src);  // src is wave-uniform
-    uint64_t m = 0;
-#pragma unroll
-    for (int j = 0; j < kPermMaxK; ++j) {
-      const uint64_t bj = __ballot(ex[j] == v) & rem[j];
-      m |= bj;
-      rem[j] &= ~bj;
-    }
-    const int pos = __popcll(m & below);
-#pragma unroll
-    for (int j = 0; j < kPermMaxK; ++j)
-      if (ex[j] == v) rank[j] = pos;
-    if (lane == 0) s_wcnt[wave][v] = __popcll(m);
+      if (ex[j] >= 0) rank[j] = __popcll(s_mask[wave][ex[j]] & below);
+    for (int e = lane; e < N; e += 64) s_wcnt[wave][e] = __popcll(s_mask[wave][e]);
   }
   __syncthreads();
 

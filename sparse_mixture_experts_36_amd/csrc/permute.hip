@@ -99,18 +99,43 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(PermuteArgs a, 
         }
     }
   }
+  // offsets: exclusive scan of the kept counts by wave 0, lane L owning
+  // experts [4L, 4L + 4) (integer, exact)
   __shared__ int32_t s_off[kMaxN + 1];
-  if (tid == 0) {
-    int32_t off = 0, drop = 0;
-    for (int x = 0; x < N; ++x) {
-      a.offsets[x] = off;
-      s_off[x] = off;
-      off += s_kept[x];
-      drop += s_drop[x];
+  if (tid < 64) {
+    const int lane = tid;
+    int32_t kept4[4], sum = 0, drop = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = 4 * lane + i;
+      kept4[i] = x < N ? s_kept[x] : 0;
+      sum += kept4[i];
+      drop += x < N ? s_drop[x] : 0;
     }
-    a.offsets[N] = off;
-    s_off[N] = off;
-    *a.n_dropped = drop;
+    int32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int32_t off = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = 4 * lane + i;
+      if (x < N) {
+        a.offsets[x] = off;
+        s_off[x] = off;
+      }
+      off += kept4[i];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) drop += __shfl_xor(drop, o);
+    const int32_t total = __shfl(incl, 63);
+    if (lane == 0) {
+      a.offsets[N] = total;
+      s_off[N] = total;
+      *a.n_dropped = drop;
+    }
   }
   if (a.plan.up) {  // the FFN's group plan from the offsets just formed
     __shared__ int32_t s_mt[2 * kMaxGroups];

@@ -63,33 +63,53 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const FfnPla
     s_mt[g] = (u.rows + pl.bm - 1) / pl.bm;
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0, n_active = 0;
-    for (int g = 0; g < G; ++g) {
-      pl.tile_start[g] = acc;
-      acc += s_mt[g];
-      if (s_mt[g] > 0) pl.active[1 + n_active++] = g;
+  // The prefixes, one wave each, 64 groups at a time (a wave scan carried
+  // across the chunks): job 0 the bm-row tile prefix and the active list
+  // (compacted by ballot, in group order), job 1 the tail tiles' prefix,
+  // jobs 2..5 the per-width prefixes (width c = (job - 2) / 2, plan t =
+  // (job - 2) % 2). Integer sums: the same values as a serial loop.
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nthreads >> 6;
+  for (int job = wave; job < 6; job += nwaves) {
+    int32_t* ts = nullptr;
+    int src = 0;            // s_mt offset of the counts summed
+    uint32_t cls = 2u;      // per-width jobs: the width class summed (2: all groups)
+    if (job == 0) {
+      ts = pl.tile_start;
+    } else if (job == 1) {
+      if (pl.bm_t <= 0) continue;
+      ts = pl.tile_start_t;
+      src = G;
+    } else {
+      if (!pl.tile_start_c) continue;
+      cls = static_cast<uint32_t>(job - 2) >> 1;
+      const int t = (job - 2) & 1;
+      if (t == 1 && pl.bm_t <= 0) continue;
+      ts = pl.tile_start_c + (2 * cls + t) * (G + 1);
+      src = t * G;
     }
-    pl.tile_start[G] = acc;
-    pl.active[0] = n_active;
-  } else if (tid == 1 && pl.bm_t > 0) {
-    int32_t acc = 0;
-    for (int g = 0; g < G; ++g) {
-      pl.tile_start_t[g] = acc;
-      acc += s_mt[G + g];
-    }
-    pl.tile_start_t[G] = acc;
-  } else if (pl.tile_start_c && tid >= 2 && tid < 6) {  // per-width prefixes: width c, plan t
-    const uint32_t c = static_cast<uint32_t>(tid - 2) >> 1;
-    const int t = (tid - 2) & 1;
-    if (t == 0 || pl.bm_t > 0) {
-      int32_t* ts = pl.tile_start_c + (2 * c + t) * (G + 1);
-      int32_t acc = 0;
-      for (int g = 0; g < G; ++g) {
-        ts[g] = acc;
-        if (((pl.cls1[g >> 5] >> (g & 31)) & 1u) == c) acc += s_mt[t * G + g];
+    int32_t base = 0, n_active = 0;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+      const int g = g0 + lane;
+      int32_t v = 0;
+      if (g < G && (cls == 2u || ((pl.cls1[g >> 5] >> (g & 31)) & 1u) == cls)) v = s_mt[src + g];
+      int32_t incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
       }
-      ts[G] = acc;
+      if (g < G) ts[g] = base + incl - v;
+      if (job == 0) {
+        const bool act = g < G && s_mt[g] > 0;
+        const uint64_t m = __ballot(act);
+        if (act) pl.active[1 + n_active + __popcll(m & ((1ull << lane) - 1ull))] = g;
+        n_active += __popcll(m);
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      ts[G] = base;
+      if (job == 0) pl.active[0] = n_active;
     }
   }
   __syncthreads();
