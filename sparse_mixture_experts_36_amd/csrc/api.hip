@@ -716,7 +716,14 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const moe_weights*
   if (moe::front_fits(ra, pa)) {  // decode sizes: router GEMM, routing and permutation in one launch
     e = moe::launch_front(ra, pa, stream);
   } else {
-    e = moe::launch_route(ra, stream);
+    // with a scan pass (more than one permutation block) the permutation also
+    // finishes the routing statistics: one launch fewer
+    const bool defer = !is_ec(s) && s.T > moe::kPermTokens;
+    if (defer) {
+      pa.fin = ra;
+      pa.fin_nb = static_cast<int32_t>((s.T + moe::kRouteTokens - 1) / moe::kRouteTokens);
+    }
+    e = moe::launch_route(ra, stream, !defer);
     if (e == hipSuccess) e = moe::launch_permute(pa, stream);
   }
   if (e == hipSuccess) e = moe::launch_grouped_ffn(fa, stream);

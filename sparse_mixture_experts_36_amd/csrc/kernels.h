@@ -44,7 +44,9 @@ constexpr int64_t kEcMaxTokens = 32768;  // expert choice: a column is held by o
 constexpr int kMaxRouteSplits = 16;  // k splits of the router GEMM (partial logit planes)
 int route_splits(int64_t T, int64_t d, int32_t N);  // k splits of the router GEMM
 int router_kstep(int64_t T, int64_t d, int32_t N);  // its k-step (64, 128 or 256)
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// finalize = false: the statistics of more than one routing block are left
+// to the permutation's scan pass (PermuteArgs::fin)
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, bool finalize = true);
 
 // ---------------------------------------------------------------- FFN groups
 // One group = one weight set applied to a contiguous block of rows.
@@ -103,6 +105,10 @@ struct PermuteArgs {
   // took (from per-block counts in ec_part, [ceil(T / 4)] ints of workspace)
   bool ec;
   int32_t* ec_part;
+  // fin_nb > 0: the scan pass (more than one permutation block) also
+  // finalizes the routing statistics of fin_nb routing blocks, with fin
+  RouteArgs fin;
+  int32_t fin_nb;
 };
 constexpr int kPermTokens = 256;  // tokens per permute workgroup
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);

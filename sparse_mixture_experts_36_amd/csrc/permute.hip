@@ -20,6 +20,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "perm_block.h"
+#include "route_block.h"
 #include "plan.h"
 
 namespace moe {
@@ -44,6 +45,11 @@ constexpr int kScanThreads = 1024;
 constexpr int kScanBatch = 16;
 
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(PermuteArgs a, int nb) {
+  static_assert(kScanThreads == kFinThreads, "the routing finalize runs on the scan workgroup");
+  if (a.fin_nb > 0) {  // the routing statistics first
+    route_finalize_block(a.fin, a.fin_nb);
+    __syncthreads();
+  }
   __shared__ int32_t s_seg[kScanThreads];
   __shared__ int32_t s_kept[kMaxN];
   __shared__ int32_t s_drop[kMaxN];

@@ -254,94 +254,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a, const
   route_block<NT>(a, t, live, lg, blockIdx.x, gridDim.x == 1);
 }
 
-// One workgroup of 1024 threads: sums the block partials (fp64) and writes
-// counts, f = counts/(T k), P = sum/T, L_aux = alpha N sum f P, z = mean(lse)^2.
-// Expert e's nb partials are cut into S contiguous segments, one thread each
-// (S <= 1024 / NP, NP the power of two >= N, and at least 16 blocks a segment);
-// a segment is summed in block order with 16 loads in flight, then the
-// segments in order. The lse sums run the same way over up to 64 lanes of
-// wave 0. Every order is fixed.
-constexpr int kFinThreads = 1024;
-constexpr int kFinBatch = 16;
-
-__global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a, int nb) {
-  __shared__ double s_fp[kMaxN];
-  __shared__ double s_segp[kFinThreads];
-  __shared__ int64_t s_segc[kFinThreads];
-  __shared__ double s_lse[2][64];
-  const int tid = threadIdx.x;
-  const int N = a.N;
-  int NP = 1;
-  while (NP < N) NP <<= 1;
-  // at least one full batch of loads per segment
-  const int S = min(kFinThreads / NP, max(1, (nb + kFinBatch - 1) / kFinBatch));
-  const int e = tid % NP, seg = tid / NP;
-  if (!a.ec && e < N && seg < S) {
-    const int b0 = static_cast<int>((static_cast<int64_t>(seg) * nb) / S);
-    const int b1 = static_cast<int>((static_cast<int64_t>(seg + 1) * nb) / S);
-    double p = 0.0;
-    int64_t c = 0;
-    for (int b = b0; b < b1; b += kFinBatch) {
-      float vp[kFinBatch];
-      int32_t vc[kFinBatch];
-#pragma unroll
-      for (int i = 0; i < kFinBatch; ++i)
-        if (b + i < b1) {
-          vp[i] = a.part_P[static_cast<int64_t>(b + i) * N + e];
-          vc[i] = a.part_cnt[static_cast<int64_t>(b + i) * N + e];
-        }
-#pragma unroll
-      for (int i = 0; i < kFinBatch; ++i)
-        if (b + i < b1) {
-          p += static_cast<double>(vp[i]);
-          c += vc[i];
-        }
-    }
-    s_segp[tid] = p;
-    s_segc[tid] = c;
-  }
-  const int SL = min(64, max(1, (nb + kFinBatch - 1) / kFinBatch));  // lse segments
-  if (tid < SL) {  // lse: lane L takes blocks [L nb / SL, (L + 1) nb / SL)
-    const int b0 = (tid * nb) / SL, b1 = ((tid + 1) * nb) / SL;
-    double ls = 0.0, lq = 0.0;
-    for (int b = b0; b < b1; b += kFinBatch) {
-      float v1[kFinBatch], v2[kFinBatch];
-#pragma unroll
-      for (int i = 0; i < kFinBatch; ++i)
-        if (b + i < b1) {
-          v1[i] = a.part_lse[2 * (b + i)];
-          v2[i] = a.part_lse[2 * (b + i) + 1];
-        }
-#pragma unroll
-      for (int i = 0; i < kFinBatch; ++i)
-        if (b + i < b1) {
-          ls += static_cast<double>(v1[i]);
-          lq += static_cast<double>(v2[i]);
-        }
-    }
-    s_lse[0][tid] = ls;
-    s_lse[1][tid] = lq;
-  }
-  __syncthreads();
-  if (!a.ec && tid < N) {
-    double p = 0.0;
-    int64_t c = 0;
-    for (int sg = 0; sg < S; ++sg) {
-      p += s_segp[sg * NP + tid];
-      c += s_segc[sg * NP + tid];
-    }
-    finalize_expert(a, tid, p, c, s_fp);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double ls = 0.0, lq = 0.0;
-    for (int l = 0; l < SL; ++l) {
-      ls += s_lse[0][l];
-      lq += s_lse[1][l];
-    }
-    finalize_scalars(a, s_fp, ls, lq);
-  }
-}
+// One workgroup of 1024 threads: the routing statistics from the block
+// partials (route_finalize_block).
+__global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(RouteArgs a, int nb) { route_finalize_block(a, nb); }
 
 // ---------------------------------------------------------------- expert choice
 // vanos001 "MoE Architecture" / "Router Design", Expert-Choice Router: the
@@ -646,7 +561,7 @@ int route_splits(int64_t T, int64_t d, int32_t N) {
   return s;
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, bool finalize) {
   if (a.T <= 0) return hipSuccess;
   const int nb = static_cast<int>(ceil_div(a.T, kRouteTokens));
   const int nt = static_cast<int>(ceil_div(a.N, 16));
@@ -664,7 +579,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  if (nb > 1) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, a, nb);
+  if (nb > 1 && finalize) hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, a, nb);
   if (a.ec) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
