@@ -157,6 +157,15 @@ REDUCED = {
                                                               capacity_factor=2.0, n_shared=1),
     "front-end-T5-N64-renorm": gen.MIXTRAL_PREFILL.with_(T=5, d=1024, d_ff=512, n_experts=64, top_k=3,
                                                          gating=gen.SOFTMAX_TOPK_RENORM),
+    # one token through the front end: one wave routes it and builds its
+    # statistics and permutation (all three gating modes, 3 and 4 column
+    # blocks, k up to 8, a shared expert, every slot dropped at capacity 0)
+    "front-end-T1-N48-k4-shared": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=256, n_experts=48, top_k=4, n_shared=1),
+    "front-end-T1-N64-k3-renorm": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=512, n_experts=64, top_k=3,
+                                                            gating=gen.SOFTMAX_TOPK_RENORM),
+    "front-end-T1-N64-k8": gen.MIXTRAL_PREFILL.with_(T=1, d=512, d_ff=512, n_experts=64, top_k=8),
+    "front-end-T1-N48-k4-all-dropped": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=256, n_experts=48, top_k=4,
+                                                              capacity_factor=2.0),
 }
 
 

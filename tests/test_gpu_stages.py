@@ -69,7 +69,11 @@ def test_route_given_logits_bit_exact(T, N, k, gating, step):
 
 @pytest.mark.parametrize("T,N,k,dt,zipf", [(300, 8, 2, gen.BF16, None), (1000, 160, 6, gen.BF16, 1.0),
                                            (256, 8, 2, gen.F32, None), (513, 64, 1, gen.BF16, 1.2),
-                                           (70, 256, 8, gen.BF16, None)])
+                                           (70, 256, 8, gen.BF16, None),
+                                           # 1024 tokens or more: the router GEMM on the LDS-DMA ring
+                                           # (6 stages; 4 above 160 experts; 3 column blocks padded)
+                                           (1024, 256, 8, gen.BF16, None), (1536, 48, 4, gen.BF16, 1.0),
+                                           (2048, 160, 6, gen.BF16, 1.0), (1100, 8, 2, gen.BF16, None)])
 def test_router_gemm_and_routing(T, N, k, dt, zipf):
     """GPU logits against the fp64 oracle logits; tokens whose top-k margin is
     well above the logit error must route identically."""
