@@ -73,30 +73,21 @@ __global__ __launch_bounds__(256) void dma_plan_kernel(BGemm p, int32_t* tile_st
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define MOE_L(x) ((__attribute__((address_space(3))) void*)(x))
 
+// The workgroup's tile (group g, row tile mt, column tile nt): consecutive
+// tiles (the row tiles of one column tile) on one XCD. False past the last tile.
 template <bool RK>
-__global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* tile_start) {
-  __shared__ __attribute__((aligned(16))) char A0[kSA];
-  __shared__ __attribute__((aligned(16))) char A1[kSA];
-  __shared__ __attribute__((aligned(16))) char A2[kSA];
-  __shared__ __attribute__((aligned(16))) char A3[kSA];
-  __shared__ __attribute__((aligned(16))) char B0[kSB];
-  __shared__ __attribute__((aligned(16))) char B1[kSB];
-  __shared__ __attribute__((aligned(16))) char B2s[kSB];
-  __shared__ __attribute__((aligned(16))) char B3[kSB];
-
-  // tile: consecutive tiles (the row tiles of one column tile) on one XCD
+__device__ __forceinline__ bool tile_of_block(const BGemm& p, const int32_t* tile_start, int& g, int& mt, int& nt) {
   const int per_xcd = gridDim.x / kXcd;
   const int L = (blockIdx.x % kXcd) * per_xcd + blockIdx.x / kXcd;
   const int ntn = (p.N + kTN - 1) / kTN;
-  int g, mt, nt;
   if (RK || !p.off) {
     const int mtn = ((RK ? p.M : p.rows_all) + kTM - 1) / kTM;
-    if (L >= p.n_groups * mtn * ntn) return;
+    if (L >= p.n_groups * mtn * ntn) return false;
     g = L / (mtn * ntn);
     nt = (L % (mtn * ntn)) / mtn;
     mt = L % mtn;
   } else {
-    if (L >= tile_start[p.n_groups] * ntn) return;
+    if (L >= tile_start[p.n_groups] * ntn) return false;
     int lo = 0, hi = p.n_groups - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -108,6 +99,22 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
     nt = local / mtg;
     mt = local % mtg;
   }
+  return true;
+}
+
+template <bool RK>
+__global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* tile_start) {
+  __shared__ __attribute__((aligned(16))) char A0[kSA];
+  __shared__ __attribute__((aligned(16))) char A1[kSA];
+  __shared__ __attribute__((aligned(16))) char A2[kSA];
+  __shared__ __attribute__((aligned(16))) char A3[kSA];
+  __shared__ __attribute__((aligned(16))) char B0[kSB];
+  __shared__ __attribute__((aligned(16))) char B1[kSB];
+  __shared__ __attribute__((aligned(16))) char B2s[kSB];
+  __shared__ __attribute__((aligned(16))) char B3[kSB];
+
+  int g, mt, nt;
+  if (!tile_of_block<RK>(p, tile_start, g, mt, nt)) return;
   int r0;
   const int rows = group_rows(p, g, r0);
   const int M = RK ? p.M : rows;
@@ -295,6 +302,226 @@ __global__ __launch_bounds__(kNT) void bgemm_dma_kernel(BGemm p, const int32_t* 
       }
     }
 }
+// Rows-M products (dH, dX) with k-stages of 64 in five 32 KB LDS buffers
+// (160 KB): A (routed rows) in a ring of two, filled one stage ahead, B (the
+// weights) in a ring of three, filled two stages ahead. A stage is two 32-k
+// MFMA steps behind one barrier, and each step's fragments are read from LDS
+// while the previous step's MFMAs run.
+//  - A stage: 256 rows x 128 bytes, chunk c of row r at c ^ (r mod 8).
+//  - B stage: 64 k-rows x 256 columns; element (k, 16 jj + 8 x + e) at byte
+//    256 (jj + 16 k2 + 32 (k >> 4)) + 32 rho(k) + 16 x + 2 e, with k2 = bit 2
+//    of k and rho(k) = (k mod 4) + 4 (bit 3 of k). The eight k-rows a
+//    half-wave's transpose read takes (k mod 4 and bit 3 vary, bit 2 and
+//    k >> 4 do not) fill one 256-byte line, all banks once; and a fragment's
+//    column block jj is a whole multiple of 256 bytes away from block 0, so
+//    its reads differ only by immediate offsets (an XOR swizzle costs a
+//    register per fragment and buffer, and those pushed the kernel into
+//    spilling).
+// The rows-K form (dW) stays on bgemm_dma_kernel: on this layout it ran
+// faster for dW2 but slower for dW1 and dW3.
+constexpr int kTK2 = 64;
+constexpr int kS2 = 32768;  // one operand of one stage
+constexpr int kDma2 = 4;    // DMA instructions per wave, operand and stage
+
+__global__ __launch_bounds__(kNT, 1) void bgemm_dma64_kernel(BGemm p, const int32_t* tile_start) {
+  __shared__ __attribute__((aligned(16))) char SA0[kS2];
+  __shared__ __attribute__((aligned(16))) char SA1[kS2];
+  __shared__ __attribute__((aligned(16))) char SB0[kS2];
+  __shared__ __attribute__((aligned(16))) char SB1[kS2];
+  __shared__ __attribute__((aligned(16))) char SB2[kS2];
+
+  int g, mt, nt;
+  if (!tile_of_block<false>(p, tile_start, g, mt, nt)) return;
+  int r0;
+  const int M = group_rows(p, g, r0);
+  const int m0 = mt * kTM, n0 = nt * kTN;
+  if (m0 >= M) return;
+  const int n_st = p.K / kTK2;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, c16 = lane & 15;
+
+  const char* Ab = reinterpret_cast<const char*>(p.A + p.a_gs * g + static_cast<int64_t>(r0 + m0) * p.lda);
+  const char* Bb = reinterpret_cast<const char*>(p.B + p.b_gs * g + n0);
+  const char* B2b = p.B2 ? reinterpret_cast<const char*>(p.B2 + p.b_gs * g + n0) : nullptr;
+  // DMA instruction t of this wave fills bytes [1024 (4 wave + t), + 1024) of
+  // a stage. A: row 32 wave + 8t + l / 8, the global k-chunk that lands at
+  // chunk l mod 8 of the LDS row. B: lane l takes k-row kl (the same for
+  // every t) and 8-column chunk 8t + 2 (l >> 4) + (l mod 2).
+  const int kl = ((lane >> 1) & 3) | ((wave & 1) << 2) | (((lane >> 3) & 1) << 3) | ((wave >> 1) << 4);
+  const int cc0 = 2 * (lane >> 4) + (lane & 1);
+  uint32_t offa[kDma2], offb[kDma2];  // bytes
+#pragma unroll
+  for (int t = 0; t < kDma2; ++t) {
+    const int row = wave * 32 + t * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const int srow = min(row, M - m0 - 1);  // rows past the group: clamped
+    offa[t] = static_cast<uint32_t>(srow * static_cast<int>(p.lda) * 2 + chunk * 16);
+    const int lastc = (min(kTN, p.N - n0) >> 3) - 1;  // columns past N: clamped
+    offb[t] = static_cast<uint32_t>(kl * static_cast<int>(p.ldb) * 2 + min(8 * t + cc0, lastc) * 16);
+  }
+  const int dst = wave * 4096;
+
+  floatx4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // LDS read offsets (bytes). A, step h: row wm 64 + 16 i + c16, chunk
+  // 4h + q. B through transpose reads (see bgemm_dma_kernel): lane (q, c16)
+  // points at k-row 8q + 4hh + c16 / 4 of the step, columns 4 (c16 mod 4) of
+  // the fragment's block; hh = 1 is 4096 bytes on, step 1 16384 bytes on.
+  int rda[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) rda[h] = (wm * 64 + c16) * 128 + (((4 * h + q) ^ (c16 & 7)) << 4);
+  const int rb = 8192 * (q >> 1) + 32 * ((c16 >> 2) | ((q & 1) << 2)) + 16 * ((c16 & 3) >> 1) + 8 * (c16 & 1) +
+                 256 * 8 * wn;  // B fragment j: + 256 j
+
+#define MOE_TR(ADDR) __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(ADDR)))
+#define MOE_DMA_A(S, ks)                                                                             \
+  do {                                                                                               \
+    const uint32_t k0b_ = static_cast<uint32_t>((ks) * kTK2 * 2);                                    \
+    _Pragma("unroll") for (int t_ = 0; t_ < kDma2; ++t_)                                             \
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(Ab + (offa[t_] + k0b_)), MOE_L((S) + dst + t_ * 1024), 16, 0, 0); \
+  } while (0)
+  // piece t of stage ks's B (B2 past k_split)
+#define MOE_DMA_B1(S, ks, t)                                                                         \
+  do {                                                                                               \
+    const int k0_ = (ks) * kTK2;                                                                     \
+    const char* bb_ = (B2b && k0_ >= p.k_split) ? B2b + static_cast<int64_t>(k0_ - p.k_split) * p.ldb * 2 \
+                                                : Bb + static_cast<int64_t>(k0_) * p.ldb * 2;        \
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(bb_ + offb[t]), MOE_L((S) + dst + (t) * 1024), 16, 0, 0); \
+  } while (0)
+#define MOE_READ_B(SB, H, j, OUT)                                                                    \
+  do {                                                                                               \
+    const uint2 l_ = MOE_TR((SB) + (H) * 16384 + rb + 256 * (j));                                   \
+    const uint2 h_ = MOE_TR((SB) + (H) * 16384 + 4096 + rb + 256 * (j));                            \
+    OUT = make_uint4(l_.x, l_.y, h_.x, h_.y);                                                        \
+  } while (0)
+  // One 32-k step: the MFMAs of A fragments AC with the B fragments in bf,
+  // column block by column block. The slot of block j holds its four MFMAs,
+  // the refill of bf[j] with block j of step H of the stage in (SA, SB), for
+  // j < 4 A fragment j of that step (into AN), and with WITH_DMA, for
+  // j < kDma2, piece j of stage DKS's B into DS: one LDS read after each of
+  // the first MFMAs, the DMA after the last. Slots are fenced, so only one
+  // set of B fragments is held.
+#define MOE_PHASE(AC, AN, SA, SB, H, WITH_DMA, DS, DKS)                                              \
+  do {                                                                                               \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) {                                               \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) acc[i_][j_] = mfma16x16x32(AC[i_], bf[j_], acc[i_][j_]); \
+      MOE_READ_B(SB, H, j_, bf[j_]);                                                                 \
+      if (j_ < 4) AN[j_] = *reinterpret_cast<const uint4*>((SA) + j_ * 16 * 128 + rda[H]);          \
+      if (WITH_DMA && j_ < kDma2) MOE_DMA_B1(DS, DKS, j_);                                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+      if (j_ < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+      if (WITH_DMA && j_ < kDma2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                 \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+    }                                                                                                \
+  } while (0)
+  // Stage ks in (SAC, SBC), its first step's A fragments in af0 and B
+  // fragments in bf: run the first step, reading the second's; wait until only
+  // stage ks + 2's B DMA may fly (stage ks + 1 has landed), barrier (every
+  // wave is done with SAC / SBC), refill SAC with stage ks + 2's A and SBC
+  // with stage ks + 3's B (the A DMA first, so that it is older than the B DMA
+  // the next wait leaves in flight), run the second step, reading stage
+  // ks + 1's first.
+#define MOE_STAGE(SAC, SBC, SAN, SBN, ks)                                                            \
+  do {                                                                                               \
+    MOE_PHASE(af0, af1, SAC, SBC, 1, false, SBC, 0);                                                 \
+    __builtin_amdgcn_s_waitcnt(vm_wait(kDma2));                                                      \
+    __builtin_amdgcn_s_waitcnt(kLgkm0);                                                              \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA_A(SAC, min((ks) + 2, n_st - 1));                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_PHASE(af1, af0, SAN, SBN, 0, true, SBC, min((ks) + 3, n_st - 1));                            \
+  } while (0)
+  // a wave whose rows or columns all lie past the tile's: DMA and barriers only
+#define MOE_STAGE_IDLE(SAC, SBC, SAN, SBN, ks)                                                       \
+  do {                                                                                               \
+    __builtin_amdgcn_s_waitcnt(vm_wait(kDma2));                                                      \
+    __builtin_amdgcn_s_barrier();                                                                    \
+    MOE_DMA_A(SAC, min((ks) + 2, n_st - 1));                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    _Pragma("unroll") for (int t_ = 0; t_ < kDma2; ++t_) MOE_DMA_B1(SBC, min((ks) + 3, n_st - 1), t_); \
+  } while (0)
+  // whole rounds of six stages (A buffers cycle by 2, B buffers by 3), then
+  // the 0..5 stages left
+#define MOE_STAGES(STAGE)                                                                            \
+  do {                                                                                               \
+    const int n_round = n_st / 6 * 6;                                                                \
+    for (int ks = 0; ks < n_round; ks += 6) {                                                        \
+      STAGE(SA0, SB0, SA1, SB1, ks);                                                                 \
+      STAGE(SA1, SB1, SA0, SB2, ks + 1);                                                             \
+      STAGE(SA0, SB2, SA1, SB0, ks + 2);                                                             \
+      STAGE(SA1, SB0, SA0, SB1, ks + 3);                                                             \
+      STAGE(SA0, SB1, SA1, SB2, ks + 4);                                                             \
+      STAGE(SA1, SB2, SA0, SB0, ks + 5);                                                             \
+    }                                                                                                \
+    const int left_ = n_st - n_round;                                                                \
+    if (left_ > 0) STAGE(SA0, SB0, SA1, SB1, n_round);                                               \
+    if (left_ > 1) STAGE(SA1, SB1, SA0, SB2, n_round + 1);                                           \
+    if (left_ > 2) STAGE(SA0, SB2, SA1, SB0, n_round + 2);                                           \
+    if (left_ > 3) STAGE(SA1, SB0, SA0, SB1, n_round + 3);                                           \
+    if (left_ > 4) STAGE(SA0, SB1, SA1, SB2, n_round + 4);                                           \
+  } while (0)
+
+  if (n_st > 0) {
+    uint4 af0[4], af1[4], bf[8];
+    MOE_DMA_A(SA0, 0);
+#pragma unroll
+    for (int t = 0; t < kDma2; ++t) MOE_DMA_B1(SB0, 0, t);
+    MOE_DMA_A(SA1, min(1, n_st - 1));
+#pragma unroll
+    for (int t = 0; t < kDma2; ++t) MOE_DMA_B1(SB1, min(1, n_st - 1), t);
+#pragma unroll
+    for (int t = 0; t < kDma2; ++t) MOE_DMA_B1(SB2, min(2, n_st - 1), t);
+    __builtin_amdgcn_s_waitcnt(vm_wait(3 * kDma2));  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    if (wm * 64 < M - m0 && wn * 128 < p.N - n0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af0[i] = *reinterpret_cast<const uint4*>(SA0 + i * 16 * 128 + rda[0]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) MOE_READ_B(SB0, 0, j, bf[j]);
+      MOE_STAGES(MOE_STAGE);
+    } else {
+      MOE_STAGES(MOE_STAGE_IDLE);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));  // the trailing DMAs have landed
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+  }
+#undef MOE_STAGES
+#undef MOE_STAGE_IDLE
+#undef MOE_STAGE
+#undef MOE_PHASE
+#undef MOE_READ_B
+#undef MOE_DMA_B1
+#undef MOE_DMA_A
+#undef MOE_TR
+
+  // lane (q, c16) of fragment (i, j): rows 4q + r, column c16
+  float* C = static_cast<float*>(p.C) + p.c_gs * g + static_cast<int64_t>(r0 + m0) * p.ldc + n0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = wm * 64 + i * 16 + q * 4 + r;
+      if (m >= M - m0) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = wn * 128 + j * 16 + c16;
+        if (n0 + n < p.N) C[static_cast<int64_t>(m) * p.ldc + n] = acc[i][j][r];
+      }
+    }
+}
 #undef MOE_L
 
 }  // namespace
@@ -313,7 +540,10 @@ hipError_t launch_bgemm_dma(const BGemm& p, int32_t* tile_start, hipStream_t s) 
   }
   if (grid <= 0) return hipSuccess;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL(bgemm_dma_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
+  if (p.K % kTK2 == 0 && (!p.B2 || p.k_split % kTK2 == 0))
+    hipLaunchKernelGGL(bgemm_dma64_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
+  else
+    hipLaunchKernelGGL(bgemm_dma_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, p, tile_start);
   return hipGetLastError();
 }
 
