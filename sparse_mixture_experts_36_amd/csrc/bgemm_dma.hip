@@ -84,8 +84,17 @@ __device__ __forceinline__ bool tile_of_block(const BGemm& p, const int32_t* til
     const int mtn = ((RK ? p.M : p.rows_all) + kTM - 1) / kTM;
     if (L >= p.n_groups * mtn * ntn) return false;
     g = L / (mtn * ntn);
-    nt = (L % (mtn * ntn)) / mtn;
-    mt = L % mtn;
+    const int in = L % (mtn * ntn);
+    if (RK && p.M > p.N) {
+      // rows-K with the wider A (dW1, dW3: A = dU or dV, M = d_ff): the column
+      // tiles of one row tile run together and share its A slab, the larger
+      // operand (the B slabs, of X, are re-read from cache)
+      mt = in / ntn;
+      nt = in % ntn;
+    } else {
+      nt = in / mtn;
+      mt = in % mtn;
+    }
   } else {
     if (L >= tile_start[p.n_groups] * ntn) return false;
     int lo = 0, hi = p.n_groups - 1;
