@@ -181,6 +181,73 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(RouteArgs ra, Perm
   perm_rank_block<kRouteThreads, true>(pa, 0, 1, s_topk);
 }
 
+// One token: the router logits by dot products instead of MFMA tiles (a
+// 16-row tile would carry 15 copies of the token and load its row 16 times
+// over; with one workgroup on one CU those redundant loads set the time).
+// The token row goes to LDS once; thread (e, j) takes expert e's slice j of
+// d (kRouteThreads / NP threads an expert, NP the power of two >= N, whole
+// waves an expert), its weights straight from memory. Sums in fixed order:
+// the slice in k order, the 64 lanes by a butterfly, the expert's waves in
+// order. Then front_one.
+constexpr int kOneMaxD = 16384;  // the token row in LDS (32 KB)
+constexpr int kOneMaxSlice = 64;  // weights a thread (eight 16-byte loads)
+
+template <int NT>
+__global__ __launch_bounds__(kRouteThreads) void front1_kernel(RouteArgs ra, PermuteArgs pa) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kOneMaxD];
+  __shared__ float s_wsum[kFrontWaves];
+  __shared__ float s_logit[NT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = ra.N;
+  const int d = static_cast<int>(ra.d);
+  int np = 1;
+  while (np < N) np <<= 1;
+  const int tpe = kRouteThreads / np;  // a multiple of 64
+  const int e = tid / tpe, j = tid % tpe;
+  const int per = d / tpe;  // a multiple of 8, at most kOneMaxSlice
+  uint4 w[kOneMaxSlice / 8];
+  const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ra.w_router) +
+                                                   static_cast<int64_t>(e) * d + j * per);
+#pragma unroll
+  for (int c = 0; c < kOneMaxSlice / 8; ++c)
+    if (e < N && c < per / 8) w[c] = wr[c];
+  const uint4* xg = reinterpret_cast<const uint4*>(ra.x);
+  for (int c = tid; c < d / 8; c += kRouteThreads) reinterpret_cast<uint4*>(s_x)[c] = xg[c];
+  __syncthreads();  // the token row is in LDS
+  float v = 0.f;
+  if (e < N) {
+    const uint4* xs = reinterpret_cast<const uint4*>(s_x + j * per);
+#pragma unroll
+    for (int c = 0; c < kOneMaxSlice / 8; ++c) {
+      if (c >= per / 8) break;
+      const uint4 xv = xs[c];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v = fmaf(bf16_to_f32(static_cast<uint16_t>(xw[h] & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(ww[h] & 0xFFFFu)), v);
+        v = fmaf(bf16_to_f32(static_cast<uint16_t>(xw[h] >> 16)), bf16_to_f32(static_cast<uint16_t>(ww[h] >> 16)), v);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) s_wsum[wave] = v;
+  __syncthreads();
+  if (tid < NT * 16) {
+    float l = 0.f;
+    if (tid < N) {
+      const int wpe = tpe / 64;
+      l = s_wsum[tid * wpe];
+      for (int i = 1; i < wpe; ++i) l += s_wsum[tid * wpe + i];
+      if (ra.b_router) l += ra.b_router[tid];
+      ra.logits[tid] = l;
+    }
+    s_logit[tid] = l;
+  }
+  __syncthreads();
+  front_one<NT>(ra, pa, s_logit);
+}
+
 }  // namespace
 
 bool front_fits(const RouteArgs& ra, const PermuteArgs& pa) {
@@ -191,6 +258,14 @@ bool front_fits(const RouteArgs& ra, const PermuteArgs& pa) {
 
 hipError_t launch_front(const RouteArgs& ra, const PermuteArgs& pa, hipStream_t s) {
   stage_mark(kStageRoute, false, s);
+  int np = 1;
+  while (np < ra.N) np <<= 1;
+  const int64_t tpe = kRouteThreads / np;
+  if (ra.T == 1 && ra.N <= 16 && ra.d <= kOneMaxD && ra.d % (tpe * 8) == 0 && ra.d / tpe <= kOneMaxSlice) {
+    hipLaunchKernelGGL(front1_kernel<1>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa);
+    stage_mark(kStageRoute, true, s);
+    return hipGetLastError();
+  }
   switch ((ra.N + 15) / 16) {
     case 1: hipLaunchKernelGGL(front_kernel<1>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;
     case 2: hipLaunchKernelGGL(front_kernel<2>, dim3(1), dim3(kRouteThreads), 0, s, ra, pa); break;

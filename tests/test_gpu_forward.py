@@ -166,6 +166,15 @@ REDUCED = {
     "front-end-T1-N64-k8": gen.MIXTRAL_PREFILL.with_(T=1, d=512, d_ff=512, n_experts=64, top_k=8),
     "front-end-T1-N48-k4-all-dropped": gen.FINE_GRAINED.with_(T=1, d=512, d_ff=256, n_experts=48, top_k=4,
                                                               capacity_factor=2.0),
+    # one token, at most 16 experts: the router logits by dot products
+    # (1024 / NP threads an expert), then the same one-token routing
+    "front1-T1-N8-k2": gen.MIXTRAL_PREFILL.with_(T=1, d=1024, d_ff=512),
+    "front1-T1-N16-k4-zipf-renorm-shared": gen.FINE_GRAINED.with_(T=1, d=1024, d_ff=256, n_experts=16, top_k=4,
+                                                                  gating=gen.SOFTMAX_TOPK_RENORM, n_shared=1),
+    "front1-T1-N5-k2-cf3": gen.MIXTRAL_PREFILL.with_(T=1, d=2048, d_ff=512, n_experts=5, top_k=2,
+                                                     capacity_factor=3.0),
+    "front1-T1-N2-k1-softmax-topk": gen.MIXTRAL_PREFILL.with_(T=1, d=4096, d_ff=256, n_experts=2, top_k=1,
+                                                              gating=gen.SOFTMAX_TOPK),
 }
 
 
