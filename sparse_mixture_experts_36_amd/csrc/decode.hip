@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int KC = 128;        // k per step
-constexpr int kTStride = 64;   // bf16 weight bytes between MFMA t and t + 1 of a step
 // s_waitcnt immediate for vmcnt(n), the other counters left at their maximum
 constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 // KU: k-steps in flight per wave (a template argument: 1, 2 or 4; 4 when few
@@ -109,11 +108,15 @@ __device__ __forceinline__ uint4 ld_weight16(const char* p) {
 }
 
 // One k-step of a weight row for lane (row, q): 32 weights from byte offset
-// `off` of a wave-uniform base, w[t] holding MFMA t's eight (8 bf16 weights
-// per uint4; e4m3 and int8 codes in .x/.y, int4 codes in .x, decoded to bf16
-// in registers).
+// `off` of a wave-uniform base, w[t] holding MFMA t's eight (e4m3 and int8
+// codes in .x/.y, int4 codes in .x, decoded to bf16 in registers).
+//
+// bf16 rows (256 bytes a step) are read in whole 128-byte lines, so that the
+// loads can carry the nontemporal hint: w[2p] covers line p of rows 0-7 of
+// the 16-row tile and w[2p + 1] line p of rows 8-15 (offsets `off` and
+// `off2`, see line_offsets); wfrag forms MFMA t's operand from them.
 template <int WF>
-__device__ __forceinline__ void load_w(const char* base, uint32_t off, uint4 (&w)[4]) {
+__device__ __forceinline__ void load_w(const char* base, uint32_t off, uint32_t off2, uint4 (&w)[4]) {
   if constexpr (WF == kWE4m3 || WF == kWInt8) {
     const uint4 q0 = *reinterpret_cast<const uint4*>(base + off);
     const uint4 q1 = *reinterpret_cast<const uint4*>(base + (off + 16));
@@ -129,8 +132,34 @@ __device__ __forceinline__ void load_w(const char* base, uint32_t off, uint4 (&w
     w[3] = make_uint4(q0.w, 0, 0, 0);
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[t] = *reinterpret_cast<const uint4*>(base + (off + kTStride * t));
+    for (int l = 0; l < 2; ++l) {
+      w[2 * l] = ld_weight16(base + (off + 128 * l));
+      w[2 * l + 1] = ld_weight16(base + (off2 + 128 * l));
+    }
   }
+}
+
+// Lane offsets of the whole-line bf16 loads of a 16-row tile (rows row0 ..
+// row0 + 15, row pitch ldb_bytes), lane (c16, q): the first load of a line
+// takes row row0 + (c16 & 7), the second row row0 + 8 + (c16 & 7), each at
+// 16-byte chunk q of the line's first half for one half of the lanes and of
+// its second half for the other, so that each load reads 8 whole lines.
+__device__ __forceinline__ void line_offsets(int row0, int ldb_bytes, int c16, int q, uint32_t& off,
+                                             uint32_t& off2) {
+  const int r = row0 + (c16 & 7);
+  off = static_cast<uint32_t>(r * ldb_bytes + 16 * q + (c16 >= 8 ? 64 : 0));
+  off2 = static_cast<uint32_t>((r + 8) * ldb_bytes + 16 * q + (c16 < 8 ? 64 : 0));
+}
+
+// One dword of MFMA operand 2p + hi from the two loads a, b of line p: lane
+// (c16, q) needs row c16, chunk 4 hi + q. For hi = 0 lanes 0-7 of each 16-lane
+// row hold it in a and lanes 8-15 in b; for hi = 1 it sits 8 lanes over, in a
+// for lanes 0-7 and in b for lanes 8-15 (DPP row rotation by 8, the second
+// move writing banks 2-3 only).
+__device__ __forceinline__ uint32_t line_pick(uint32_t a, uint32_t b, bool hi) {
+  if (!hi) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(a), static_cast<int>(b), 0xE4, 0xF, 0xC, false));
+  const int r = __builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x128, 0xF, 0xF, false);  // row_ror:8
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(r, static_cast<int>(b), 0x128, 0xF, 0xC, false));
 }
 
 template <int WF>
@@ -145,6 +174,19 @@ __device__ __forceinline__ uint4 as_bf16(const uint4& w) {
     return int4x8_to_bf16x8_biased(w.x);  // q + 136: the kernels subtract 136 * sum(x)
   } else {
     return w;
+  }
+}
+
+// MFMA t's B operand (bf16) from the loads of load_w.
+template <int WF>
+__device__ __forceinline__ uint4 wfrag(const uint4 (&w)[4], int t) {
+  if constexpr (WF == kWBf16) {
+    const uint4 a = w[2 * (t >> 1)], b = w[2 * (t >> 1) + 1];
+    const bool hi = t & 1;
+    return make_uint4(line_pick(a.x, b.x, hi), line_pick(a.y, b.y, hi), line_pick(a.z, b.z, hi),
+                      line_pick(a.w, b.w, hi));
+  } else {
+    return as_bf16<WF>(w[t]);
   }
 }
 
@@ -211,8 +253,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
   constexpr bool BYTE = WF != kWBf16;  // a byte or half a byte per weight
   // k order inside a 128-wide step (the same for both operands, so any order
   // gives the same sums): bf16 MFMA t takes k [32t, 32t + 32), lane group q
-  // its 8 k at 8q, so the four lanes of a row read 64 contiguous bytes per
-  // load; with e4m3 / int8 codes lane group q takes k [32q, 32q + 32) in two
+  // its 8 k at 8q (the weight loads read whole lines and DPP moves form the
+  // operands, see load_w); with e4m3 / int8 codes lane group q takes k [32q, 32q + 32) in two
   // 16-byte loads (int4: one), MFMA t its 8 k at 8t
   constexpr int QK = BYTE ? 32 : 8;        // k offset of lane group q
   constexpr int AT = BYTE ? 16 : 64;       // A bytes between MFMA t and t + 1
@@ -227,12 +269,17 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
   const char* Bw = (shared ? p.B_s : p.B_r) + eoff;
   const char* B3w = swi ? (shared ? p.B3_s : p.B3_r) + eoff : Bw;
   const char* wbase[FN] = {Bw, swi ? B3w : Bw};
-  uint32_t woff[FN];
+  uint32_t woff[FN], woff2[FN];
   float sw[FN];  // the scale of the lane's weight row in tile j
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int r = swi ? c16 : j * 16 + c16;
-    woff[j] = static_cast<uint32_t>(r * static_cast<int>(p.ldb) * EB) + kbytes<WF>(static_cast<uint32_t>(q * QK));
+    if constexpr (BYTE) {
+      woff[j] = static_cast<uint32_t>(r * static_cast<int>(p.ldb) * EB) + kbytes<WF>(static_cast<uint32_t>(q * QK));
+      woff2[j] = woff[j];
+    } else {
+      line_offsets(r - c16, static_cast<int>(p.ldb) * EB, c16, q, woff[j], woff2[j]);
+    }
     const bool third = swi && j == 1;
     sw[j] = wscale<WF>(p, shared, ew, third ? p.scale_row3 : p.scale_row0, n0 + r, p.scale_col + (third ? 1 : 0));
   }
@@ -246,7 +293,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
     // opaque to the optimiser, so that the first loads' addresses are formed
     // here from base + offset, not hoisted out of the pass loop as 64-bit pointers
 #pragma unroll
-    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(woff[j]));
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(woff[j]), "+v"(woff2[j]));
     const char* Ap = A;
     uint32_t aoff[RB];
 #pragma unroll
@@ -294,7 +341,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
         for (int u = 0; u < KU; ++u) {
           const uint32_t kk = static_cast<uint32_t>((st + u) * KC);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), bw[u][j]);
+          for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), woff2[j] + kbytes<WF>(kk), bw[u][j]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // this wave's token-row DMA has landed (loads complete in issue order)
@@ -314,7 +361,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-              const uint4 b = as_bf16<WF>(bw[u][j][t]);
+              const uint4 b = wfrag<WF>(bw[u][j], t);
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(av[rb], b, acc[rb][j]);
             }
@@ -338,7 +385,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
       for (int u = 0; u < KU; ++u) {
         const uint32_t kk = static_cast<uint32_t>(min(st + u, nsteps - 1) * KC);  // a step past the end re-reads the last one
 #pragma unroll
-        for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), bw[u][j]);
+        for (int j = 0; j < FN; ++j) load_w<WF>(wbase[j], woff[j] + kbytes<WF>(kk), woff2[j] + kbytes<WF>(kk), bw[u][j]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -353,7 +400,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const uint4 b = as_bf16<WF>(bw[u][j][t]);
+            const uint4 b = wfrag<WF>(bw[u][j], t);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) acc[rb][j] = mfma16x16x32(a[u][rb][t], b, acc[rb][j]);
           }
