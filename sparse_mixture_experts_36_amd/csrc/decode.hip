@@ -860,15 +860,17 @@ __global__ __launch_bounds__(kThreads) void gemv_combine_kernel(StreamParams p, 
 }
 
 // k splits for one GEMM: double while the touched experts' blocks give fewer
-// than 1024 waves (four per CU, each with two 8 KB weight loads in flight,
-// which is more than HBM latency times bandwidth needs) and every split keeps
-// at least two 128-wide k-steps. Fewer splits means less partial traffic and,
-// at one split, no reduction pass. Integer weights aim at 4096 waves: a wave
-// then has fewer bytes in flight per k-step and decodes the codes on the
-// vector ALUs, which other waves on the SIMD must cover.
+// than 2048 waves (eight per CU) and every split keeps at least two 128-wide
+// k-steps. Fewer splits means less partial traffic and, at one split, no
+// reduction pass. With ordinary loads 1024 waves had been as fast; with the
+// whole-line nontemporal loads the Mixtral down GEMM (1024 blocks of 32 rows)
+// runs faster split in two (T = 16 step 471 -> 461 us, T = 64 462 -> 454 us),
+// and a target of 4096 waves gained nothing more. Integer weights aim at 4096
+// waves: a wave then has fewer bytes in flight per k-step and decodes the
+// codes on the vector ALUs, which other waves on the SIMD must cover.
 int pick_splits(int64_t K, int64_t blocks_touched, bool intw) {
   const int64_t steps = K / KC;
-  const int64_t target = intw ? 4096 : 1024;
+  const int64_t target = intw ? 4096 : 2048;
   int s = 1;
   while (blocks_touched * s < target && s < 16 && steps % (2 * s) == 0 && steps / (2 * s) >= 2) s *= 2;
   return s;
