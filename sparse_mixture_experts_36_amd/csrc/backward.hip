@@ -110,17 +110,25 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(BwdArgs a) {
   uint16_t* dU = a.dU + r * a.ld_du;
   uint16_t* dV = a.act == 1 ? a.dV + r * a.ld_du : nullptr;
   float dot = 0.f;
-  // four elements a thread and step (d_ff is a multiple of 128: rows stay 16-byte aligned)
+  // four elements a thread and step (d_ff is a multiple of 128: rows stay
+  // 16-byte aligned). dH, U, V and H are read once, each wave load covering
+  // whole lines: the loads carry the nontemporal hint (Mixtral shape 407 ->
+  // 372 us a call).
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   for (int64_t i = 4 * tid; i < f; i += 4 * kThreads) {
-    const float4 hp4 = *reinterpret_cast<const float4*>(dh + i);
-    const float4 u4 = *reinterpret_cast<const float4*>(U + i);
-    const uint2 h2 = *reinterpret_cast<const uint2*>(H + i);
+    const f32x4 hq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dh + i));
+    const f32x4 uq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(U + i));
+    const u32x2 hv = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(H + i));
+    const float4 hp4 = make_float4(hq.x, hq.y, hq.z, hq.w), u4 = make_float4(uq.x, uq.y, uq.z, uq.w);
+    const uint2 h2 = make_uint2(hv.x, hv.y);
     const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
     const uint16_t hb[4] = {static_cast<uint16_t>(h2.x & 0xFFFFu), static_cast<uint16_t>(h2.x >> 16),
                             static_cast<uint16_t>(h2.y & 0xFFFFu), static_cast<uint16_t>(h2.y >> 16)};
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (a.act == 1) {
-      const float4 v4 = *reinterpret_cast<const float4*>(V + i);
+      const f32x4 vq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(V + i));
+      const float4 v4 = make_float4(vq.x, vq.y, vq.z, vq.w);
       v[0] = v4.x; v[1] = v4.y; v[2] = v4.z; v[3] = v4.w;
     }
     uint16_t ou[4], ov[4];

@@ -23,6 +23,15 @@ constexpr int kMaxK = 8;
 // + shared) rows before the first sum, so the dependent chain (inv_map, row,
 // store) of one token overlaps the others'. A token has KS = k + shared slots,
 // at most 8 / TW (12 with TW = 1): the loads stay in registers.
+// A 16-byte load with the nontemporal hint: the rows of y_perm and y_shared
+// are read once, and a wave's loads of one row cover whole lines (fine-grained
+// layer 4.03-4.04 -> 4.00-4.02 ms a call, the others unchanged).
+__device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <bool BF16, int TW>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int KM = TW == 1 ? kMaxK + 4 : 8 / TW;  // slots a token may have
@@ -61,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
           if (row[w][j] >= 0)
-            v[u][w][j] = reinterpret_cast<const uint4*>(j < k ? a.y_perm : a.y_shared)[row[w][j] * nch + c];
+            v[u][w][j] = ld_nt16(reinterpret_cast<const uint4*>(j < k ? a.y_perm : a.y_shared) + (row[w][j] * nch + c));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
