@@ -933,9 +933,16 @@ bool use_gemv(const FfnArgs& a) {
 // NR = 8 weight rows per wave while that still gives 2048 waves, else 4;
 // each burst is 32 KB of one wave's rows (int4: 16 KB, as a segment's
 // activations are four times those of bf16 and would not fit the registers).
+// One token row with bf16 weights always takes NR = 4 with eight 1 KB
+// segments of each row a burst: with the nontemporal loads the Mixtral T = 1
+// FFN (up and down launches by their events) took 125.6-126.1 us with 8 rows x
+// 4 segments, 123.0-123.6 with 4 x 8 (4 x 4 124.1-125.2, 8 x 2 126.3), the
+// whole step within 0.5 us either way; the integer layer's T = 1 step went
+// from 68 to 79 us with it.
 hipError_t run_gemv(const StreamParams& p, int rows, int wf, int64_t slots, hipStream_t s) {
   const bool swi = (p.epi == 1);
-  const int nr = slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4;
+  const bool long_rows = rows == 1 && wf == kWBf16;
+  const int nr = long_rows ? 4 : (slots * p.Nout / (swi ? 4 : 8) >= 2048 ? 8 : 4);
   const int64_t waves = slots * p.Nout / (swi ? nr / 2 : nr);
   if (waves <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(ceil_div(waves, kThreads / 64)));
