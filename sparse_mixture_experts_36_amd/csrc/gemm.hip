@@ -129,7 +129,11 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
 // partial tiles; a fix-up pass sums each tile's chunks in chunk order and
 // applies the epilogue. The result then does not depend on timing.
 constexpr int kSplitUnits = 256;  // partial tiles the workspace holds
-constexpr int kMaxSplit = 8;
+// at most 4 chunks a tile: with 8, the Switch layer's up GEMM (K = 1024, its
+// last round 32 tiles) ran chunks of two k-stages and a fix-up over 33 MB of
+// partials; with 4 the layer took 0.279-0.281 ms against 0.289, the Mixtral
+// and fine-grained layers unchanged
+constexpr int kMaxSplit = 4;
 struct SplitPlan {
   int total, full, r, s;
 };
