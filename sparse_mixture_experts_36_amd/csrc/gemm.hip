@@ -413,12 +413,13 @@ constexpr int BK = 64;      // k per stage
 constexpr int RB = BK * 2;  // row bytes in a stage
 // Cache policy of a weight-row DMA (global_load_lds's aux operand): bit 1 is
 // the nontemporal hint. It is used where no other tile reads the weight
-// tile: a group with one 128-row tile (bf16 rows, whole lines a stage).
-// Measured on the Mixtral layer, whose groups' short tails are such tiles:
-// up and down stages 1.660 -> 1.651 and 0.839 -> 0.825 ms with the hint on
-// every 128-row tile; on the fine-grained layer the same made the down GEMM
-// of its small groups slower (1.543 -> 1.573 ms: groups of two or three row
-// tiles share each weight tile in L2) and its up GEMM faster (2.205 -> 2.177).
+// tile: a group with one 128-row tile (bf16 rows, whole lines a stage; the
+// Mixtral layer's short tails, most small groups of the Switch and
+// fine-grained layers). Measured: Mixtral layer 2.597-2.613 -> 2.559-2.580
+// ms, Switch 0.303-0.305 -> 0.290-0.291 ms, fine-grained unchanged. With the
+// hint on every 128-row tile the fine-grained layer's down GEMM was slower
+// (1.543 -> 1.573 ms): groups of two or three row tiles share each weight
+// tile in L2, and the later tiles found fewer of its lines there.
 constexpr int kAuxNT = 2;
 constexpr int bno(int epi) { return epi == EPI_SWIGLU ? BNB / 2 : BNB; }
 // BM x 256 tile on W waves (2 x W/2): a wave owns BM/2 rows and 512/W weight
