@@ -302,17 +302,62 @@ __global__ __launch_bounds__(kThreads) void sum_parts_kernel(const float* part, 
 
 // dx_t = sum over its kept slots of dX[row] (ascending) + the shared experts'
 // rows + the router term, to bf16.
+// dx of token t: its kept routed rows of dX in slot order, then its shared
+// experts' rows, then the router's term, summed in that order in fp32. Four
+// columns a thread (d is a multiple of 128), the loads of all terms of two
+// column chunks issued before the sums; the rows are read once, in whole lines
+// a wave, with the nontemporal hint (Mixtral shape: 85 -> 58 us a call against
+// one column a thread and the terms loaded one after another). The sums are
+// the same, in the same order.
+constexpr int kDxTerms = 8 + 4 + 1;  // top-k, shared experts, router term
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a, const float* dX, const float* dxr, uint16_t* dx) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int64_t t = blockIdx.x;
-  for (int64_t c = threadIdx.x; c < a.d; c += kThreads) {
-    float s = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int row = a.inv_map[t * a.k + j];
-      if (row >= 0) s += dX[static_cast<int64_t>(row) * a.d + c];
+  const int64_t d = a.d;
+  // element offsets of the terms' rows, in summation order
+  int64_t src[kDxTerms];
+  const float* base[kDxTerms];
+  int n = 0;
+  for (int j = 0; j < a.k; ++j) {
+    const int row = a.inv_map[t * a.k + j];
+    if (row >= 0) {
+      src[n] = static_cast<int64_t>(row) * d;
+      base[n++] = dX;
     }
-    for (int sh = 0; sh < a.S; ++sh) s += dX[(a.cap + static_cast<int64_t>(sh) * a.T + t) * a.d + c];
-    s += dxr[t * a.d + c];
-    dx[t * a.d + c] = f32_to_bf16(s);
+  }
+  for (int sh = 0; sh < a.S; ++sh) {
+    src[n] = (a.cap + static_cast<int64_t>(sh) * a.T + t) * d;
+    base[n++] = dX;
+  }
+  src[n] = t * d;
+  base[n++] = dxr;
+  const int64_t nch = d / 4;
+  for (int64_t c0 = threadIdx.x; c0 < nch; c0 += 2 * kThreads) {
+    f32x4 v[2][kDxTerms];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t c = c0 + u * kThreads;
+#pragma unroll
+      for (int i = 0; i < kDxTerms; ++i)
+        if (i < n && c < nch) v[u][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base[i] + src[i]) + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nch) break;
+      float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDxTerms; ++i)
+        if (i < n) {
+          sx += v[u][i].x;
+          sy += v[u][i].y;
+          sz += v[u][i].z;
+          sw += v[u][i].w;
+        }
+      *reinterpret_cast<uint2*>(dx + t * d + 4 * c) =
+          make_uint2(f32_to_bf16(sx) | (static_cast<uint32_t>(f32_to_bf16(sy)) << 16),
+                     f32_to_bf16(sz) | (static_cast<uint32_t>(f32_to_bf16(sw)) << 16));
+    }
   }
 }
 
