@@ -93,14 +93,16 @@ constexpr int pitch_bytes() { return WF == kWBf16 ? 2 : 1; }
 template <int WF>
 constexpr int loads_per_step() { return WF == kWBf16 ? 4 : (WF == kWInt4 ? 1 : 2); }
 
-// One 16-byte weight load with the nontemporal hint, for the GEMV paths, whose
-// load instructions cover whole 128-byte lines (a wave reads 1 KB of one row).
-// A plain grid-stride read of 2 GiB measured 5.3-5.6 TB/s with ordinary
-// 16-byte loads and 5.6-6.1 TB/s with the hint, at every unroll and grid tried;
-// the Mixtral one-token step went from 134 to 125.6 us. The MFMA streaming
-// kernel keeps ordinary loads: each of its instructions reads 64 bytes of a row
-// and the next one the other half of the line, which with the hint came from
-// memory again (16-token step 512 -> 594 us).
+// One 16-byte weight load with the nontemporal hint, where every load
+// instruction covers whole 128-byte lines: the GEMVs (a wave reads 1 KB of one
+// row) and the streaming kernel's bf16 line loads (load_w). A plain
+// grid-stride read of 2 GiB measured 5.3-5.6 TB/s with ordinary 16-byte loads
+// and 5.6-6.1 TB/s with the hint, at every unroll and grid tried; the Mixtral
+// one-token step went from 134 to 125.6 us. Where an instruction reads only
+// half of each line (the streaming kernel's former loads: 64 bytes of each of
+// 16 rows, the next instruction the other half) the hint made the second
+// request come from memory again (16-token step 512 -> 594 us); the integer
+// codes keep ordinary loads for that reason.
 __device__ __forceinline__ uint4 ld_weight16(const char* p) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -254,8 +256,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, char* abuf0, 
   // k order inside a 128-wide step (the same for both operands, so any order
   // gives the same sums): bf16 MFMA t takes k [32t, 32t + 32), lane group q
   // its 8 k at 8q (the weight loads read whole lines and DPP moves form the
-  // operands, see load_w); with e4m3 / int8 codes lane group q takes k [32q, 32q + 32) in two
-  // 16-byte loads (int4: one), MFMA t its 8 k at 8t
+  // operands, see load_w); with e4m3 / int8 codes lane group q takes k
+  // [32q, 32q + 32) in two 16-byte loads (int4: one), MFMA t its 8 k at 8t
   constexpr int QK = BYTE ? 32 : 8;        // k offset of lane group q
   constexpr int AT = BYTE ? 16 : 64;       // A bytes between MFMA t and t + 1
   const int K = p.K, ks = K / p.splits;
